@@ -1,0 +1,343 @@
+"""CPU oracle for the quantized-KV decode path (ctypes wrapper of liboracle.so).
+
+TEST INFRASTRUCTURE ONLY.  This package may be imported by ``tests/``, by
+``__graft_entry__.smoke()`` and by the CPU-baseline leg of ``bench.py`` -- by
+nothing else.  It never imports the HIP library's package, and the HIP
+library never imports it.  The arithmetic lives in ``kvq_oracle.c``; this file
+only marshals numpy arrays.
+
+Functions mirror the C entry points (see the comments there for the
+definitions and the pages each follows).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_c_f32p = ctypes.POINTER(ctypes.c_float)
+_c_f64p = ctypes.POINTER(ctypes.c_double)
+_c_u8p = ctypes.POINTER(ctypes.c_uint8)
+_c_u16p = ctypes.POINTER(ctypes.c_uint16)
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.ensure_built()
+        L = ctypes.CDLL(path)
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = ctypes.c_int
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_f16_encode.argtypes = [ctypes.c_double]
+        L.oracle_f16_encode.restype = ctypes.c_uint16
+        L.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_decode.restype = ctypes.c_double
+        L.oracle_bf16_encode.argtypes = [ctypes.c_double]
+        L.oracle_bf16_encode.restype = ctypes.c_uint16
+        L.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_decode.restype = ctypes.c_double
+        for name, a, o in [("oracle_e4m3_encode_array", _c_f32p, _c_u8p),
+                           ("oracle_e4m3_decode_array", _c_u8p, _c_f64p),
+                           ("oracle_f16_encode_array", _c_f32p, _c_u16p),
+                           ("oracle_f16_encode_array_f64", _c_f64p, _c_u16p),
+                           ("oracle_f16_decode_array", _c_u16p, _c_f64p),
+                           ("oracle_bf16_encode_array", _c_f32p, _c_u16p),
+                           ("oracle_bf16_encode_array_f64", _c_f64p, _c_u16p)]:
+            f = getattr(L, name)
+            f.argtypes = [a, ctypes.c_int64, o]
+            f.restype = None
+        L.oracle_fwht_f32.argtypes = [_c_f32p, ctypes.c_int]
+        L.oracle_fwht_f32.restype = ctypes.c_int
+        L.oracle_fwht_rows_f32.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int]
+        L.oracle_fwht_rows_f32.restype = ctypes.c_int
+        L.oracle_fwht256_orthonormal.argtypes = [_c_f32p]
+        L.oracle_fwht256_orthonormal.restype = ctypes.c_int
+        L.oracle_encode_fp8.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_f32p]
+        L.oracle_encode_fp8.restype = ctypes.c_int
+        L.oracle_decode_fp8_rows.argtypes = [_c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_f64p]
+        L.oracle_decode_fp8_rows.restype = ctypes.c_int
+        L.oracle_tq4_codebook.argtypes = [_c_f64p, _c_f32p, _c_f32p, ctypes.POINTER(ctypes.c_int)]
+        L.oracle_tq4_codebook.restype = ctypes.c_int
+        L.oracle_quantizer_mse.argtypes = [_c_f64p, _c_f64p]
+        L.oracle_quantizer_mse.restype = ctypes.c_double
+        L.oracle_encode_tq4.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_u8p, _c_f32p]
+        L.oracle_encode_tq4.restype = ctypes.c_int
+        L.oracle_decode_tq4_rows.argtypes = [_c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_f64p]
+        L.oracle_decode_tq4_rows.restype = ctypes.c_int
+        L.oracle_tq4_identity_check.argtypes = [_c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p,
+                                                _c_f64p, _c_f64p]
+        L.oracle_tq4_identity_check.restype = ctypes.c_double
+        L.oracle_decode_attn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         _c_i64p, _c_u8p, _c_f32p, _c_u16p, _c_u8p, _c_f32p, _c_f32p,
+                                         ctypes.c_double, _c_f64p, _c_f64p]
+        L.oracle_decode_attn.restype = ctypes.c_int
+        L.oracle_q4_0_block.argtypes = [_c_f32p, _c_u8p]
+        L.oracle_q4_0_block.restype = None
+        L.oracle_q4_0_block_dequant.argtypes = [_c_u8p, _c_u16p]
+        L.oracle_q4_0_block_dequant.restype = None
+        L.oracle_append_q4_0.argtypes = [_c_u8p, _c_u8p, ctypes.c_int64, _c_i32p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i32p, _c_i64p,
+                                         _c_f32p, _c_f32p, ctypes.c_int]
+        L.oracle_append_q4_0.restype = ctypes.c_int
+        L.oracle_gather_q4_0.argtypes = [_c_u8p, _c_u8p, ctypes.c_int64, _c_i32p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, _c_i64p, _c_u16p, _c_u16p]
+        L.oracle_gather_q4_0.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def set_threads(n=0):
+    """Sets the OpenMP thread count (n > 0); returns the count in force."""
+    return lib().oracle_set_threads(int(n))
+
+
+# ---- formats --------------------------------------------------------------
+
+def e4m3_encode(x):
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().oracle_e4m3_encode_array(_p(x, _c_f32p), x.size, _p(out, _c_u8p))
+    return out
+
+
+def e4m3_decode(c):
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().oracle_e4m3_decode_array(_p(c, _c_u8p), c.size, _p(out, _c_f64p))
+    return out
+
+
+def f16_encode(x):
+    if np.asarray(x).dtype == np.float64:
+        x = _c(x, np.float64)
+        out = np.empty(x.shape, np.uint16)
+        lib().oracle_f16_encode_array_f64(_p(x, _c_f64p), x.size, _p(out, _c_u16p))
+        return out
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_f16_encode_array(_p(x, _c_f32p), x.size, _p(out, _c_u16p))
+    return out
+
+
+def f16_decode(h):
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float64)
+    lib().oracle_f16_decode_array(_p(h, _c_u16p), h.size, _p(out, _c_f64p))
+    return out
+
+
+def bf16_encode(x):
+    if np.asarray(x).dtype == np.float64:
+        x = _c(x, np.float64)
+        out = np.empty(x.shape, np.uint16)
+        lib().oracle_bf16_encode_array_f64(_p(x, _c_f64p), x.size, _p(out, _c_u16p))
+        return out
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_bf16_encode_array(_p(x, _c_f32p), x.size, _p(out, _c_u16p))
+    return out
+
+
+def bf16_decode(b):
+    return np.array([lib().oracle_bf16_decode(int(v)) for v in np.ravel(b)],
+                    np.float64).reshape(np.shape(b))
+
+
+# ---- transforms -----------------------------------------------------------
+
+def fwht(x):
+    """Unnormalized FWHT of each row (last axis, a power of two), fp32."""
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    n = x.shape[-1]
+    rows = x.size // n
+    _check(lib().oracle_fwht_rows_f32(_p(x, _c_f32p), rows, n), "fwht")
+    return x
+
+
+def fwht256_orthonormal(x):
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    assert x.shape[-1] == 256
+    flat = x.reshape(-1, 256)
+    for r in range(flat.shape[0]):
+        row = flat[r]
+        lib().oracle_fwht256_orthonormal(_p(row, _c_f32p))
+    return x
+
+
+# ---- codecs ---------------------------------------------------------------
+
+def encode_fp8(x):
+    x = _c(x, np.float32)
+    n, dim = x.shape
+    codes = np.empty((n, dim), np.uint8)
+    scales = np.empty(n, np.float32)
+    _check(lib().oracle_encode_fp8(_p(x, _c_f32p), n, dim, _p(codes, _c_u8p), _p(scales, _c_f32p)),
+           "encode_fp8")
+    return codes, scales
+
+
+def decode_fp8(codes, scales):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    n, dim = codes.shape
+    out = np.empty((n, dim), np.float64)
+    lib().oracle_decode_fp8_rows(_p(codes, _c_u8p), _p(scales, _c_f32p), n, dim, _p(out, _c_f64p))
+    return out
+
+
+def tq4_codebook():
+    """Returns (levels_exact[16] f64, levels_bf16[16] f32, thresholds[15] f32, iterations)."""
+    le = np.empty(16, np.float64)
+    lb = np.empty(16, np.float32)
+    th = np.empty(15, np.float32)
+    it = ctypes.c_int(0)
+    _check(lib().oracle_tq4_codebook(_p(le, _c_f64p), _p(lb, _c_f32p), _p(th, _c_f32p), ctypes.byref(it)),
+           "tq4_codebook")
+    return le, lb, th, it.value
+
+
+def quantizer_mse(levels, thresholds):
+    lv = _c(levels, np.float64)
+    th = _c(thresholds, np.float64)
+    return lib().oracle_quantizer_mse(_p(lv, _c_f64p), _p(th, _c_f64p))
+
+
+def encode_tq4(x, sign_mask):
+    x = _c(x, np.float32)
+    m = _c(sign_mask, np.uint8)
+    n, dim = x.shape
+    codes = np.empty((n, dim // 2), np.uint8)
+    radii = np.empty(n, np.float32)
+    rc = lib().oracle_encode_tq4(_p(x, _c_f32p), n, dim, _p(m, _c_u8p), _p(codes, _c_u8p), _p(radii, _c_f32p))
+    _check(rc, "encode_tq4")
+    return codes, radii
+
+
+def encode_tq4_rc(x, sign_mask):
+    """Raw return code of the TQ4 encoder (for the refusal tests)."""
+    x = _c(x, np.float32)
+    m = _c(sign_mask, np.uint8)
+    n, dim = x.shape
+    codes = np.empty((n, max(dim // 2, 1)), np.uint8)
+    radii = np.empty(max(n, 1), np.float32)
+    return lib().oracle_encode_tq4(_p(x, _c_f32p), n, dim, _p(m, _c_u8p), _p(codes, _c_u8p), _p(radii, _c_f32p))
+
+
+def decode_tq4(codes, radii, sign_mask):
+    codes = _c(codes, np.uint8)
+    radii = _c(radii, np.float32)
+    m = _c(sign_mask, np.uint8)
+    n = codes.shape[0]
+    dim = codes.shape[1] * 2
+    out = np.empty((n, dim), np.float64)
+    _check(lib().oracle_decode_tq4_rows(_p(codes, _c_u8p), _p(radii, _c_f32p), n, dim, _p(m, _c_u8p),
+                                        _p(out, _c_f64p)), "decode_tq4")
+    return out
+
+
+def tq4_identity_check(codes, radii, sign_mask, q, w):
+    codes = _c(codes, np.uint8)
+    radii = _c(radii, np.float32)
+    m = _c(sign_mask, np.uint8)
+    q = _c(q, np.float64)
+    w = _c(w, np.float64)
+    n = codes.shape[0]
+    dim = codes.shape[1] * 2
+    return lib().oracle_tq4_identity_check(_p(codes, _c_u8p), _p(radii, _c_f32p), n, dim, _p(m, _c_u8p),
+                                           _p(q, _c_f64p), _p(w, _c_f64p))
+
+
+def decode_attn(qmode, seq_offsets, codes, row_scale, k_rope, q_lat, q_rope, sm_scale, sign_mask=None):
+    """fp64 decode attention.  q_lat [S][H][dim], q_rope [S][H][R], k_rope bf16 bits
+    [rows][R].  Returns (out [S][H][dim] f64, lse [S][H] f64)."""
+    offs = _c(seq_offsets, np.int64)
+    codes = _c(codes, np.uint8)
+    rs = _c(row_scale, np.float32)
+    kr = _c(k_rope, np.uint16)
+    ql = _c(q_lat, np.float32)
+    qr = _c(q_rope, np.float32)
+    S, H, dim = ql.shape
+    R = qr.shape[2]
+    m = _c(sign_mask if sign_mask is not None else np.zeros(max(dim // 8, 1), np.uint8), np.uint8)
+    out = np.empty((S, H, dim), np.float64)
+    lse = np.empty((S, H), np.float64)
+    rc = lib().oracle_decode_attn(int(qmode), S, H, dim, R, _p(offs, _c_i64p), _p(codes, _c_u8p),
+                                  _p(rs, _c_f32p), _p(kr, _c_u16p), _p(m, _c_u8p), _p(ql, _c_f32p),
+                                  _p(qr, _c_f32p), float(sm_scale), _p(out, _c_f64p), _p(lse, _c_f64p))
+    _check(rc, "decode_attn")
+    return out, lse
+
+
+# ---- q4_0 paged tier ------------------------------------------------------
+
+def q4_0_block(x32):
+    x = _c(x32, np.float32)
+    assert x.shape == (32,)
+    out = np.empty(18, np.uint8)
+    lib().oracle_q4_0_block(_p(x, _c_f32p), _p(out, _c_u8p))
+    return out
+
+
+def q4_0_block_dequant(blk):
+    b = _c(blk, np.uint8)
+    out = np.empty(32, np.uint16)
+    lib().oracle_q4_0_block_dequant(_p(b, _c_u8p), _p(out, _c_u16p))
+    return out
+
+
+def append_q4_0(k_pool, v_pool, table, page_size, pos0, src_off, k_src, v_src, no_rotate=False):
+    """In place on k_pool/v_pool [n_cells][n_kv_heads][144] u8."""
+    assert k_pool.flags.c_contiguous and v_pool.flags.c_contiguous
+    n_cells, n_kv, rb = k_pool.shape
+    tab = _c(table, np.int32)
+    n_seqs, max_pages = tab.shape
+    p0 = _c(pos0, np.int32)
+    so = _c(src_off, np.int64)
+    ks = _c(k_src, np.float32)
+    vs = _c(v_src, np.float32)
+    head_dim = ks.shape[-1]
+    rc = lib().oracle_append_q4_0(_p(k_pool, _c_u8p), _p(v_pool, _c_u8p), n_cells, _p(tab, _c_i32p), max_pages,
+                                  page_size, n_kv, head_dim, n_seqs, _p(p0, _c_i32p), _p(so, _c_i64p),
+                                  _p(ks, _c_f32p), _p(vs, _c_f32p), 1 if no_rotate else 0)
+    _check(rc, "append_q4_0")
+
+
+def gather_q4_0(k_pool, v_pool, table, page_size, dst_off, head_dim=256, k_dst=None, v_dst=None):
+    n_cells, n_kv, rb = k_pool.shape
+    kp = _c(k_pool, np.uint8)
+    vp = _c(v_pool, np.uint8)
+    tab = _c(table, np.int32)
+    n_seqs, max_pages = tab.shape
+    do = _c(dst_off, np.int64)
+    total = int(do[-1])
+    if k_dst is None:
+        k_dst = np.zeros((total, n_kv, head_dim), np.uint16)
+    if v_dst is None:
+        v_dst = np.zeros((total, n_kv, head_dim), np.uint16)
+    rc = lib().oracle_gather_q4_0(_p(kp, _c_u8p), _p(vp, _c_u8p), n_cells, _p(tab, _c_i32p), max_pages,
+                                  page_size, n_kv, head_dim, n_seqs, _p(do, _c_i64p), _p(k_dst, _c_u16p),
+                                  _p(v_dst, _c_u16p))
+    _check(rc, "gather_q4_0")
+    return k_dst, v_dst

@@ -1,0 +1,196 @@
+"""Benchmark of the quantized-KV decode hot path on one MI355X.
+
+A step is one decode step of the KV8 absorbed-MLA workload (1 sequence,
+T = 32768 cached rows, 128 heads, 512-dim fp8 latent + 64-dim bf16 rope key):
+  1. fp8-encode the step's new latent row into the cache (row T-1),
+  2. decode attention over all T rows: split plan, the split kernel (the
+     dominant kernel, bracketed by HIP events on the launch stream), merge.
+The step cycles through --kv-copies independent caches (16 x 21 MB > the
+256 MB last-level cache) so every step reads its KV from HBM, as consecutive
+layers of a model do.  Inputs are seeded synthetic data, resident in HBM
+before the timed region.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV rows/s + achieved HBM GB/s (% roofline), fp8/TQ4 MLA decode, T=32k"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_flops(T, H):
+    # score K = 512 + 64 and PV N = 512: 2 * H * (576 + 512) per row
+    return 2.0 * H * (576 + 512) * T
+
+
+def decode_bytes(T, qmode):
+    # per row: codes (512 fp8 or 256 nibble bytes) + fp32 scale + 64 bf16 rope
+    return T * ((512 if qmode == 1 else 256) + 4 + 128)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2])
+    ap.add_argument("--kv-copies", type=int, default=16)
+    ap.add_argument("--split-rows", type=int, default=0)
+    ap.add_argument("--precision", type=int, default=0, choices=[0, 1])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode path shards T across GPUs by design, see DESIGN.md, but no multi-GPU run exists)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_kv_cache_row_amd import kvq, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    log(f"device {torch.cuda.get_device_name(0)}")
+    qmode = 1 if args.config == 1 else 2
+    w = workloads.config1() if qmode == 1 else workloads.config2()
+    T, H = w.total_rows, w.n_heads
+    log(f"workload {w.name}: T={T} H={H} copies={args.kv_copies}")
+
+    # ---- device-resident inputs
+    x = torch.from_numpy(w.latent).to(dev)
+    new_rows = torch.from_numpy(workloads.fp8_rows_for_encode(args.steps + args.warmup + 1, seed=77)).to(dev)
+    kr0 = torch.from_numpy(w.k_rope.view(np.int16)).to(dev)
+    offs = torch.from_numpy(w.offsets).to(dev)
+    ql = torch.from_numpy(w.q_lat).to(dev)
+    qr = torch.from_numpy(w.q_rope).to(dev)
+    mask = torch.from_numpy(w.sign_mask).to(dev)
+    cb = 512 if qmode == 1 else 256
+    codes0 = torch.empty((T, cb), dtype=torch.uint8, device=dev)
+    scales0 = torch.empty(T, dtype=torch.float32, device=dev)
+    if qmode == 1:
+        kvq.kvq_encode_fp8(x, codes0, scales0)
+    else:
+        kvq.kvq_encode_tq4(x, mask, codes0, scales0)
+    copies = []
+    for _ in range(args.kv_copies):
+        copies.append((codes0.clone(), scales0.clone(), kr0.clone()))
+    out = torch.empty((1, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, H), dtype=torch.float32, device=dev)
+    argsets = [kvq.attn_args(qmode, args.precision, offs, T, c, s, k, ql, qr, w.sm_scale, out, lse,
+                             sign_mask=mask if qmode == 2 else None, split_rows=args.split_rows)
+               for (c, s, k) in copies]
+    ws = kvq.alloc_workspace(argsets[0])
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c, s, _ = copies[i % len(copies)]
+        a = argsets[i % len(copies)]
+        row = new_rows[i % new_rows.shape[0]: i % new_rows.shape[0] + 1]
+        if qmode == 1:
+            kvq.kvq_encode_fp8(row, c[T - 1:T], s[T - 1:T])
+        else:
+            kvq.kvq_encode_tq4(row, mask, c[T - 1:T], s[T - 1:T])
+        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_PLAN, ws)
+        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_QROT, ws)
+        if ev is not None:
+            ev[0].record()
+        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_SPLITS, ws)
+        if ev is not None:
+            ev[1].record()
+        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_MERGE, ws)
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    rows_per_s = T / (ms_per_step / 1000.0)
+    flops = decode_flops(T, H)
+    nbytes = decode_bytes(T, qmode)
+    tflops = flops / (kern_ms / 1000.0) / 1e12
+    gbps = nbytes / (kern_ms / 1000.0) / 1e9
+    log(f"step {ms_per_step * 1000:.1f} us, split kernel {kern_ms * 1000:.1f} us, {tflops:.1f} TFLOP/s, "
+        f"{gbps:.0f} GB/s")
+
+    # ---- CPU baseline: the oracle on the same decode step
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.set_threads(0)
+        log(f"cpu baseline: oracle, {threads} threads, ~{args.cpu_seconds:.0f} s")
+        c_host = codes0.cpu().numpy()
+        s_host = scales0.cpu().numpy()
+        newrow = new_rows[:1].cpu().numpy()
+        reps = 0
+        t_start = time.perf_counter()
+        while True:
+            if qmode == 1:
+                oracle.encode_fp8(newrow)
+            else:
+                oracle.encode_tq4(newrow, w.sign_mask)
+            oracle.decode_attn(qmode, w.offsets, c_host, s_host, w.k_rope, w.q_lat, w.q_rope, w.sm_scale,
+                               sign_mask=w.sign_mask)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        cpu = {"value": T * reps / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+               "sample": f"{reps} full decode steps of the same workload (1-row encode + {H}-head fp64 "
+                         f"attention over T={T}) in {el:.1f} s"}
+        log(f"cpu baseline {cpu['value']:.3g} rows/s")
+
+    line = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1) latents x lognormal row gain, outlier channels, zero rows)",
+        "config": {"workload": w.name, "seqs": 1, "T": T, "heads": H, "qmode": "fp8" if qmode == 1 else "tq4",
+                   "precision": "mfma-bf16" if args.precision == 0 else "fp32", "kv_copies": args.kv_copies,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "hbm": {"achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+                "bytes_per_launch": nbytes},
+        "kernel_us": kern_ms * 1000.0,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: quantized KV-cache rows and decode attention
+ * over them, native on AMD MI355X (gfx950).
+ *
+ * Conventions (all entry points):
+ *  - Buffer pointers are DEVICE pointers unless the comment says "host".
+ *    Every buffer is owned by the caller; the library keeps no reference to it
+ *    after the call returns and allocates no device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on it and return; no call synchronizes.
+ *  - Arguments are validated before anything is enqueued: a call that returns
+ *    an error has launched nothing.  There is no fallback to another precision
+ *    or to the CPU.
+ *  - Alignment (KVQ_ERR_INVALID_ARG otherwise): fp32 row inputs (x, k_src,
+ *    v_src), code arrays read by the attention, pools, rope keys, outputs of
+ *    the gather and of the attention: 16 bytes; fp8 codes written by the
+ *    encoder: 8 bytes; TQ4 codes: 4 bytes; every other buffer: the natural
+ *    alignment of its element type.
+ *  - NaN and Inf in floating-point inputs are outside the contract.
+ *  - Calls are thread-safe; the library holds only immutable state.
+ *
+ * Sources cited below, by page title and section:
+ *  [KV8]  colibri PR #399 "KV cache quantization: fp8 (KV8) + 4-bit TurboQuant
+ *         (KV_TQ) on CPU, CUDA, and Metal".
+ *  [Q4]   Strata PR #2533 "metal: q4_0 KV cache on the Mac engine".
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+/* ---- status codes ------------------------------------------------------- */
+#define KVQ_OK 0
+#define KVQ_ERR_INVALID_ARG 1 /* null pointer, negative count, misalignment, bad shape    */
+#define KVQ_ERR_UNSUPPORTED 2 /* valid but not provided: non-power-of-two TQ4 width, ...  */
+#define KVQ_ERR_WORKSPACE 3   /* workspace smaller than kvq_decode_attn_workspace_bytes() */
+#define KVQ_ERR_LAUNCH 4      /* the HIP runtime reported an error at launch             */
+
+/* ---- modes ---------------------------------------------------------------- */
+#define KVQ_QMODE_FP8 1      /* e4m3 codes [rows][dim] + fp32 scale per row           */
+#define KVQ_QMODE_TQ4 2      /* 4-bit codebook indices [rows][dim/2] + fp32 radius    */
+#define KVQ_PREC_MFMA_BF16 0 /* bf16 matrix-core contractions, fp32 softmax/scales   */
+#define KVQ_PREC_FP32 1      /* fp32 vector arithmetic throughout (check path)        */
+#define KVQ_Q4_NO_ROTATE 1u  /* append: rows are already in the rotated domain        */
+
+/* ABI version of the loaded library (KVQ_ABI_VERSION at build time). */
+int kvq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* kvq_status_string(int status);
+
+/* Bytes per stored row: KVQ_QMODE_FP8 -> dim + 4 (codes + scale),
+ * KVQ_QMODE_TQ4 -> dim/2 + 4 (nibbles + radius).  Returns -1 for an unknown
+ * mode or a dim the encoders refuse.  Host only. */
+int64_t kvq_row_bytes(int qmode, int dim);
+
+/* The 4-bit codec's codebook ([KV8] "Why rotated-int4 for the 4-bit tier":
+ * a fixed 16-level Lloyd-Max quantizer for N(0,1)).  levels: host float[16],
+ * ascending, each a bfloat16 value; thresholds: host float[15], the exact
+ * midpoints of neighbouring levels.  Either may be NULL.  Host only. */
+int kvq_tq4_codebook(float* levels, float* thresholds);
+
+/* ---- a1: fp8 e4m3 per-row encoder ([KV8] Summary, commit 1) -------------
+ * For each row r of x (fp32 [n_rows][dim], row-major):
+ *   amax = max_i |x_i|,  scales[r] = fl32(amax / 448),
+ *   codes[r][i] = e4m3(fl32(x_i / scales[r])), round to nearest even on the
+ *   OCP e4m3 grid, |value| saturated to 448; the NaN code is never written.
+ *   An all-zero row gets scales[r] = 0 and all codes 0x00.
+ * Decode: x_hat = e4m3_value(code) * scale.
+ * codes: u8 [n_rows][dim]; scales: fp32 [n_rows].
+ * dim: a multiple of 8, 8 <= dim <= 2048.  n_rows == 0 is a no-op. */
+int kvq_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* codes, float* scales,
+                   void* stream);
+
+/* ---- a2: TQ4 row encoder ([KV8] Why rotated-int4; refusal of
+ * non-power-of-two widths in the 85852e2 rebase note) ----------------------
+ * For each row x (fp32 [n_rows][dim]):
+ *   z_i = -x_i if bit i of sign_mask is set (bit i = byte i/8, bit i%8), else x_i;
+ *   w = FWHT(z), unnormalized, stages h = 1, 2, 4, ... with (a, b) -> (a+b, a-b);
+ *   radii[r] = sqrt(sum_i x_i^2), the sum a pairwise tree over i (fp32);
+ *   idx_i = #{k : w_i > fl32(t_k * radii[r])}, t_k the codebook thresholds;
+ *   codes[r][j] = idx_{2j} | idx_{2j+1} << 4.
+ * Decode: y_i = level[idx_i] * r / sqrt(dim); x_hat = D H y / sqrt(dim).
+ * sign_mask: u8 [dim/8]; codes: u8 [n_rows][dim/2]; radii: fp32 [n_rows].
+ * dim: a power of two, 8 <= dim <= 512 (KVQ_ERR_UNSUPPORTED otherwise). */
+int kvq_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
+                   uint8_t* codes, float* radii, void* stream);
+
+/* ---- a9/a10: q4_0 paged tier ([Q4]) ---------------------------------------
+ * Pools: u8 [n_cells][n_kv_heads][144]; each 144-byte head-row is 8 blocks of
+ * 18 bytes: binary16 scale d (little-endian) then 16 nibble bytes,
+ * byte 2+j = q_j | q_{j+16} << 4.  Position p of sequence s lives in cell
+ * block_table[s][p / page_size] * page_size + p % page_size. */
+typedef struct kvq_q4_cache {
+    uint8_t* k_pool;            /* device, [n_cells][n_kv_heads][144]            */
+    uint8_t* v_pool;            /* device, [n_cells][n_kv_heads][144]            */
+    const int32_t* block_table; /* device, [n_seqs][max_pages] physical page ids */
+    int64_t n_cells;            /* cells in each pool (a multiple of page_size)  */
+    int32_t max_pages;          /* columns of block_table                        */
+    int32_t page_size;          /* cells per page, >= 1                          */
+    int32_t n_kv_heads;         /* >= 1                                          */
+    int32_t head_dim;           /* must be 256                                   */
+} kvq_q4_cache;
+
+/* Append new K and V rows ([Q4] first commit: kv_append_q4 single-step and
+ * batch paths).  For sequence s the new rows are src_off[s] .. src_off[s+1]-1
+ * of k_src/v_src (fp32 [total_new][n_kv_heads][256]); row i of s goes to
+ * position pos0[s] + i.  Each head-row is rotated by FWHT-256 x 1/16 (skipped
+ * with KVQ_Q4_NO_ROTATE) and quantized in blocks of 32:
+ *   mval = element of largest |x| (a tie goes to the larger signed value,
+ *          +0 over -0);  d = mval / -8;  id = d != 0 ? 1/d : 0;
+ *   q_j  = min(15, max(0, trunc(fma(x_j, id, 8.5))))  (NaN -> 0);
+ *   the scale is stored as binary16(d), round to nearest even.
+ * pos0: device int32 [n_seqs]; src_off: device int64 [n_seqs+1], ascending,
+ * src_off[0] = 0, src_off[n_seqs] = total_new (host).  Rows whose page is
+ * outside block_table's columns, whose table entry is negative, or whose cell
+ * is outside the pool are not written (never an out-of-bounds store).
+ * Appends of the same cell in one call race; callers do not do that. */
+int kvq_append_q4_0(const kvq_q4_cache* cache, int n_seqs, const int32_t* pos0,
+                    const int64_t* src_off, int64_t total_new, const float* k_src,
+                    const float* v_src, uint32_t flags, void* stream);
+
+/* Gather positions 0 .. len_s-1 of every sequence (len_s = dst_off[s+1] -
+ * dst_off[s]) to binary16 rows in the rotated domain ([Q4] kv_gather_q4 and
+ * the QSA_KV_Q4 commit: dequant (nibble - 8) * f32(d)):
+ *   out_j = binary16_rne((q_j - 8) * f32(d)).
+ * dst_off: device int64 [n_seqs+1] (dst_off[n_seqs] = total_rows, host);
+ * k_dst/v_dst: binary16 bits [total_rows][n_kv_heads][256].  Rows whose cell is
+ * invalid (as for append) are left untouched. */
+int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_off,
+                    int64_t total_rows, uint16_t* k_dst, uint16_t* v_dst, void* stream);
+
+/* ---- a3..a8: absorbed-MLA decode attention over quantized rows ------------
+ * ([KV8] commit 6: fused decode with a 3-way qmode, score a_score8 and context
+ * a_clat8 over fp8 rows; commit 2: split-T kernels; "Ready for review": the
+ * native 4-bit consumer rotates q once per head, dots the codes through the
+ * codebook and un-rotates the weighted sum.)
+ * For sequence s (rows seq_offsets[s] .. seq_offsets[s+1]-1) and head h:
+ *   x_hat_t = the decoded latent row (fp8: e4m3(code)*scale; TQ4: see above);
+ *   s_t = sm_scale * (q_lat[s,h] . x_hat_t + q_rope[s,h] . k_rope_t);
+ *   out[s,h] = sum_t softmax(s)_t x_hat_t;  lse[s,h] = log sum_t exp(s_t).
+ * The latent rows are not reconstructed: fp8 codes are converted exactly to
+ * bf16 and the per-row scale is applied in fp32; TQ4 uses the rotated query
+ * R q and un-rotates the merged output (R = H D / sqrt(dim)).
+ * A sequence with no rows gets out = 0 and lse = -Inf.
+ * Tolerance against an fp64 evaluation on the same codes:
+ *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA_BF16), <= 1e-5 (KVQ_PREC_FP32). */
+typedef struct kvq_attn_args {
+    int32_t qmode;              /* KVQ_QMODE_FP8 or KVQ_QMODE_TQ4                 */
+    int32_t precision;          /* KVQ_PREC_MFMA_BF16 or KVQ_PREC_FP32            */
+    int32_t n_seqs;             /* >= 1                                           */
+    int32_t n_heads;            /* 1 .. 256                                       */
+    int32_t dim_lat;            /* must be 512                                    */
+    int32_t dim_rope;           /* must be 64                                     */
+    int32_t split_rows;         /* rows per work item; 0 = automatic              */
+    int32_t reserved0;          /* must be 0                                      */
+    int64_t total_rows;         /* host copy of seq_offsets[n_seqs]               */
+    const int64_t* seq_offsets; /* device int64 [n_seqs+1], ascending, [0] = 0    */
+    const uint8_t* codes;       /* device, fp8 [rows][512] or TQ4 [rows][256]     */
+    const float* row_scale;     /* device fp32 [rows]: fp8 scale or TQ4 radius    */
+    const uint16_t* k_rope;     /* device bf16 bits [rows][64]                    */
+    const uint8_t* sign_mask;   /* device u8 [64] (TQ4 only, else ignored)        */
+    const float* q_lat;         /* device fp32 [n_seqs][n_heads][512]             */
+    const float* q_rope;        /* device fp32 [n_seqs][n_heads][64]              */
+    float* out;                 /* device fp32 [n_seqs][n_heads][512]             */
+    float* lse;                 /* device fp32 [n_seqs][n_heads], or NULL         */
+    float sm_scale;             /* softmax scale, finite                          */
+    int32_t reserved1;          /* must be 0                                      */
+} kvq_attn_args;
+
+/* Device workspace bytes kvq_decode_attn needs for these arguments (partial
+ * softmax states of the T-splits and the split plan); depends on qmode,
+ * precision, n_seqs, n_heads, total_rows and split_rows only.  Host only;
+ * returns -1 for arguments kvq_decode_attn would refuse. */
+int64_t kvq_decode_attn_workspace_bytes(const kvq_attn_args* a);
+
+/* Runs decode attention.  workspace: device, >= the queried size, 256-byte
+ * aligned, contents need not be initialised; the call overwrites it.  Two
+ * calls that share a workspace must be ordered (same stream). */
+int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, void* stream);
+
+/* One stage of kvq_decode_attn; running stages 0..3 in order on one stream is
+ * exactly kvq_decode_attn.  Stage 0 (split plan) depends only on seq_offsets,
+ * total_rows, split_rows, n_heads and precision, so callers whose layers share
+ * the sequence lengths may run it once and stages 1..3 per layer; running a
+ * stage also gives profilers and timers one kernel per call:
+ *   KVQ_STAGE_PLAN   per-sequence T-split prefix into the workspace;
+ *   KVQ_STAGE_QROT   TQ4: the rotated query R q into the workspace (no-op for fp8);
+ *   KVQ_STAGE_SPLITS the attention over every T-split (partial softmax states);
+ *   KVQ_STAGE_MERGE  merge of the splits (+ TQ4 un-rotation) into out / lse. */
+#define KVQ_STAGE_PLAN 0
+#define KVQ_STAGE_QROT 1
+#define KVQ_STAGE_SPLITS 2
+#define KVQ_STAGE_MERGE 3
+int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, int64_t ws_bytes,
+                          void* stream);
+
+/* ---- conformance probe -------------------------------------------------------
+ * Element-wise conversions exactly as the kernels perform them, so a caller
+ * can check them against the format definitions (for instance over every
+ * fp32 bit pattern):
+ *   KVQ_CVT_F32_TO_E4M3   fp32 -> e4m3 byte, round to nearest even, |v| saturated
+ *                         to 448 (the fp8 encoder's step after the division);
+ *   KVQ_CVT_E4M3_TO_BF16  e4m3 byte -> bf16 bits, exact (the attention's dequant;
+ *                         S.1111.111 reads as +0, [KV8] HIP portability note);
+ *   KVQ_CVT_F32_TO_F16    fp32 -> binary16 bits, round to nearest even (the q4_0
+ *                         scale and gather outputs);
+ *   KVQ_CVT_F32_TO_BF16   fp32 -> bf16 bits, round to nearest even (the query
+ *                         and probability operands of the matrix-core path).
+ * in/out: device arrays of n elements of the source/destination type. */
+#define KVQ_CVT_F32_TO_E4M3 1
+#define KVQ_CVT_E4M3_TO_BF16 2
+#define KVQ_CVT_F32_TO_F16 3
+#define KVQ_CVT_F32_TO_BF16 4
+int kvq_convert(int kind, const void* in, int64_t n, void* out, void* stream);
+
+/* ---- binding support ------------------------------------------------------
+ * Layout of the argument structs, so a foreign-language binding can check its
+ * mirror: which = 0 -> kvq_attn_args, 1 -> kvq_q4_cache; out[0] = sizeof, then
+ * the offsetof of every field in declaration order.  Returns the number of
+ * values written (at most n), or -1 for an unknown struct.  Host only. */
+int kvq_struct_layout(int which, int64_t* out, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

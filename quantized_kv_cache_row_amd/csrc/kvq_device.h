@@ -1,0 +1,127 @@
+// kvq_device.h -- device helpers of the HIP library: format conversions and
+// wave-level primitives for gfx950 (wave64).
+//
+// Every conversion is written from its format definition:
+//  - OCP FP8 E4M3 ("e4m3fn"): bias 7, 3 mantissa bits, largest finite 448,
+//    S.1111.111 is NaN; the pages read that code back as 0 (colibri PR #399,
+//    HIP portability rebase note);
+//  - IEEE 754 binary16 and bfloat16 (the upper half of a binary32), both
+//    rounded to nearest, ties to even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define KVQ_WAVE 64
+
+namespace kvq {
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// fp32 -> e4m3 code, round to nearest even, |v| saturated to 448 (0x7E).
+// NaN input is outside the contract.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+    uint32_t b = f2u(v);
+    uint32_t sign = (b >> 24) & 0x80u;
+    uint32_t a = b & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {            // |v| >= 448
+        code = 0x7Eu;
+    } else if (a >= 0x3C800000u) {     // |v| >= 2^-6: normal e4m3
+        // round the fp32 significand to 3 bits at bit 20, ties to even
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);  // rebias exponent 127 -> 7
+    } else {                           // subnormal e4m3: multiples of 2^-9
+        float s = u2f(a) * 512.0f;     // exact: |v| * 2^9 < 8
+        float t = s + 8388608.0f;      // 2^23: rounds to an integer, ties to even
+        code = f2u(t) - 0x4B000000u;   // 0..8 (8 is the smallest normal, 0x08)
+    }
+    return sign | code;
+}
+
+// e4m3 code -> fp32, exact.  S.1111.111 -> +0.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float mag = (e == 0u) ? (float)m * 0.001953125f                      // M * 2^-9
+                          : u2f(((c & 0x7Fu) << 20) + (120u << 23));      // (1 + M/8) 2^(E-7)
+    if ((c & 0x7Fu) == 0x7Fu) return 0.0f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; overflow -> Inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t b = f2u(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// e4m3 code -> bf16 bits, exact (3 mantissa bits fit in 7).
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) { return f2u(e4m3_to_f32(c)) >> 16; }
+
+// fp32 -> binary16 bits, round to nearest even, subnormals kept, |v| >= 65520 -> Inf.
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+    uint32_t b = f2u(f);
+    uint32_t sign = (b >> 16) & 0x8000u;
+    uint32_t a = b & 0x7FFFFFFFu;
+    uint32_t h;
+    if (a > 0x7F800000u) {
+        h = 0x7E00u;                                   // NaN
+    } else if (a >= 0x477FF000u) {
+        h = 0x7C00u;                                   // overflow threshold 65520
+    } else if (a >= 0x38800000u) {                     // >= 2^-14: normal binary16
+        uint32_t r = a - 0x38000000u;                  // rebias exponent 127 -> 15
+        r = r + 0xFFFu + ((r >> 13) & 1u);
+        h = r >> 13;
+    } else {                                           // subnormal: multiples of 2^-24
+        float s = u2f(a) * 16777216.0f;                // exact, < 1024
+        float t = s + 8388608.0f;                      // round to integer, ties to even
+        h = f2u(t) - 0x4B000000u;                      // 0..1024
+    }
+    return sign | h;
+}
+
+// binary16 bits -> fp32, exact.
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    uint32_t sign = (h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+    float mag;
+    if (e == 0u) mag = (float)m * 5.9604644775390625e-8f;           // M * 2^-24
+    else if (e == 31u) mag = u2f(0x7F800000u | (m << 13));
+    else mag = u2f(((e + 112u) << 23) | (m << 13));
+    return u2f(f2u(mag) | sign);
+}
+
+// ---- wave primitives -------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, KVQ_WAVE); }
+__device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
+    return (uint32_t)__shfl_xor((int)v, m, KVQ_WAVE);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+    return v;
+}
+
+// Cross-lane FWHT stage with partner lane^m: the lower lane keeps a + b, the
+// upper lane keeps a - b, where a is the lower lane's value and b the upper's.
+__device__ __forceinline__ float fwht_xlane(float v, int lane, int m) {
+    float o = shfl_xor_f(v, m);
+    return (lane & m) ? (o - v) : (v + o);
+}
+
+// Largest-value selection on the key (|x|, x) with +0 above -0: the key is
+// order-preserving as an unsigned integer.
+__device__ __forceinline__ uint32_t absval_key(float x) {
+    uint32_t b = f2u(x);
+    return ((b & 0x7FFFFFFFu) << 1) | ((b >> 31) ^ 1u);
+}
+
+}  // namespace kvq

@@ -1,0 +1,98 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, its host-only calls answer, struct layouts match the binding,
+its codebook equals the oracle's (independently derived), and invalid
+arguments are refused before anything touches a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_kv_cache_row_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = kvq.lib()
+    names = _declared()
+    assert set(names) == set(kvq.exported_symbols()), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_host_calls():
+    assert kvq.kvq_abi_version() == 1
+    assert kvq.kvq_status_string(0) == "ok"
+    assert "workspace" in kvq.kvq_status_string(3)
+    assert kvq.kvq_status_string(99) == "unknown status"
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_FP8, 512) == 516
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ4, 512) == 260
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ4, 384) == -1
+    assert kvq.kvq_row_bytes(7, 512) == -1
+
+
+def test_struct_layouts_match_binding():
+    for which in (0, 1):
+        assert kvq.kvq_struct_layout(which) == kvq.binding_layout(which)
+
+
+def test_codebook_equals_oracle():
+    lv, th = kvq.kvq_tq4_codebook()
+    _, olv, oth, _ = oracle.tq4_codebook()
+    np.testing.assert_array_equal(np.array(lv, np.float32), olv)
+    np.testing.assert_array_equal(np.array(th, np.float32), oth)
+
+
+def test_refusals_without_launch():
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    # fp8: bad widths / counts
+    assert L.kvq_encode_fp8(None, 4, 7, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_encode_fp8(None, -1, 512, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_encode_fp8(None, 4, 4096, None, None, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert L.kvq_encode_fp8(None, 4, 512, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_encode_fp8(None, 0, 512, None, None, None) == kvq.KVQ_OK  # empty is a no-op
+    assert L.kvq_encode_fp8(P(8), 4, 512, P(16), P(16), None) == kvq.KVQ_ERR_INVALID_ARG  # misaligned
+    # TQ4: non-power-of-two widths are refused, as the pages require
+    for dim in (384, 500, 576, 1024):
+        assert L.kvq_encode_tq4(P(16), 4, dim, P(16), P(16), P(16), None) == kvq.KVQ_ERR_UNSUPPORTED
+    # attention
+    a = kvq.KvqAttnArgs()
+    assert L.kvq_decode_attn(ctypes.byref(a), None, 0, None) == kvq.KVQ_ERR_UNSUPPORTED  # qmode 0
+    a.qmode, a.precision, a.n_seqs, a.n_heads, a.dim_lat, a.dim_rope = 1, 0, 1, 128, 512, 64
+    assert L.kvq_decode_attn(ctypes.byref(a), None, 0, None) == kvq.KVQ_ERR_INVALID_ARG  # null pointers
+    a.seq_offsets = a.q_lat = a.q_rope = a.out = a.codes = a.row_scale = a.k_rope = 256
+    a.total_rows, a.sm_scale = 32768, 0.0417
+    need = L.kvq_decode_attn_workspace_bytes(ctypes.byref(a))
+    assert need > 0
+    assert L.kvq_decode_attn(ctypes.byref(a), P(256), need - 1, None) == kvq.KVQ_ERR_WORKSPACE
+    a.dim_lat = 576
+    assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_UNSUPPORTED
+    a.dim_lat, a.split_rows = 512, 33
+    assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    a.split_rows, a.qmode = 0, 2  # TQ4 without a sign mask
+    assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    # q4_0
+    c = kvq.KvqQ4Cache(256, 256, 256, 64, 1, 64, 8, 128)
+    assert L.kvq_append_q4_0(ctypes.byref(c), 1, P(256), P(256), 1, P(256), P(256), 0, None) == \
+        kvq.KVQ_ERR_UNSUPPORTED  # head_dim 128
+    c.head_dim = 256
+    assert L.kvq_append_q4_0(ctypes.byref(c), 1, P(256), P(256), 1, P(256), P(256), 4, None) == \
+        kvq.KVQ_ERR_INVALID_ARG  # unknown flag
+    assert L.kvq_gather_q4_0(None, 1, P(256), 1, P(256), P(256), None) == kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_convert(9, P(256), 4, P(256), None) == kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_binding_has_no_cpu_path():
+    import torch
+    x = torch.zeros(4, 512)
+    with pytest.raises(ValueError, match="device tensor"):
+        kvq.kvq_encode_fp8(x, torch.zeros(4, 512, dtype=torch.uint8), torch.zeros(4))

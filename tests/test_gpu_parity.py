@@ -1,0 +1,350 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Encoders, conversions and the q4_0 tier must match bit for bit; decode
+attention must match the oracle's fp64 evaluation on the same codes within
+max|err| / max|ref| <= 2e-3 (bf16 matrix cores) or <= 1e-5 (fp32 check path).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_kv_cache_row_amd import kvq, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {kvq.KVQ_PREC_MFMA_BF16: 2e-3, kvq.KVQ_PREC_FP32: 1e-5}
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def _t(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def _np(t, dtype=None):
+    a = t.cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def gpu_encode_fp8(x):
+    xt = _t(x.astype(np.float32))
+    n, d = x.shape
+    c = torch.empty((n, d), dtype=torch.uint8, device=DEV)
+    s = torch.empty(n, dtype=torch.float32, device=DEV)
+    kvq.kvq_encode_fp8(xt, c, s)
+    return c, s
+
+
+def gpu_encode_tq4(x, mask):
+    xt = _t(x.astype(np.float32))
+    n, d = x.shape
+    c = torch.empty((n, d // 2), dtype=torch.uint8, device=DEV)
+    r = torch.empty(n, dtype=torch.float32, device=DEV)
+    kvq.kvq_encode_tq4(xt, _t(mask), c, r)
+    return c, r
+
+
+def gpu_attn(w, codes, scales, precision, split_rows=0, q_lat=None, q_rope=None, heads=None):
+    q_lat = w.q_lat if q_lat is None else q_lat
+    q_rope = w.q_rope if q_rope is None else q_rope
+    out = torch.empty(q_lat.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q_lat.shape[:2], dtype=torch.float32, device=DEV)
+    args = kvq.attn_args(w.qmode, precision, _t(w.offsets), w.total_rows, codes, scales, _t(w.k_rope),
+                         _t(q_lat), _t(q_rope), w.sm_scale, out, lse,
+                         sign_mask=_t(w.sign_mask) if w.qmode == 2 else None, split_rows=split_rows)
+    ws = kvq.alloc_workspace(args)
+    kvq.kvq_decode_attn(args, ws)
+    torch.cuda.synchronize()
+    return _np(out).astype(np.float64), _np(lse).astype(np.float64)
+
+
+def rel_err(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+# ---- conversions ----------------------------------------------------------------------
+
+def _near(v):
+    v = np.asarray(v, np.float32)
+    a = np.concatenate([v, np.nextafter(v, np.float32(np.inf)), np.nextafter(v, np.float32(-np.inf))])
+    return np.concatenate([a, -a])
+
+
+def _convert(kind, x, out_dtype):
+    src = _t(x)
+    dst = torch.empty(x.shape, dtype=out_dtype, device=DEV)
+    kvq.kvq_convert(kind, src, dst)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy()
+
+
+def test_convert_e4m3_bf16_f16_against_oracle():
+    _say("conversions")
+    pos = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    rnd = bits.view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    x = np.concatenate([_near(mids), _near(pos.astype(np.float32)), rnd, np.array([448, 500, 1e30], np.float32)])
+    got = _convert(kvq.KVQ_CVT_F32_TO_E4M3, x, torch.uint8)
+    np.testing.assert_array_equal(got, oracle.e4m3_encode(x))
+    codes = np.array([c for c in range(256)], np.uint8)
+    got = _convert(kvq.KVQ_CVT_E4M3_TO_BF16, codes, torch.int16).view(np.uint16)
+    np.testing.assert_array_equal(oracle.bf16_decode(got), oracle.e4m3_decode(codes))
+    h = np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    hm = ((h[:-1] + h[1:]) / 2).astype(np.float32)
+    x = np.concatenate([_near(hm), rnd])
+    got = _convert(kvq.KVQ_CVT_F32_TO_F16, x, torch.int16).view(np.uint16)
+    np.testing.assert_array_equal(got, oracle.f16_encode(x))
+    got = _convert(kvq.KVQ_CVT_F32_TO_BF16, rnd, torch.int16).view(np.uint16)
+    np.testing.assert_array_equal(got, oracle.bf16_encode(rnd))
+
+
+# ---- encoders -----------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["config0", "config1", "random-dims", "zeros-extremes"])
+def test_fp8_encoder_bit_exact(case):
+    _say(f"fp8 encoder {case}")
+    rng = np.random.default_rng(5)
+    if case == "config0":
+        xs = [workloads.config0().latent]
+    elif case == "config1":
+        xs = [workloads.fp8_rows_for_encode(32768)]
+    elif case == "random-dims":
+        xs = [(rng.standard_normal((37, d)) * 10 ** rng.uniform(-5, 5, (37, 1))).astype(np.float32)
+              for d in (8, 72, 520, 1024, 2048)]
+    else:
+        x = rng.standard_normal((9, 512)).astype(np.float32)
+        x[0] = 0
+        x[1] = 0
+        x[1, 5] = -1e-38
+        x[2] *= 1e30
+        x[3] *= 1e-30
+        x[4, :] = 448.0
+        x[5, 7] = 3e38
+        xs = [x]
+    for x in xs:
+        c, s = gpu_encode_fp8(x)
+        rc, rs = oracle.encode_fp8(x)
+        np.testing.assert_array_equal(_np(s).view(np.uint32), rs.view(np.uint32))
+        np.testing.assert_array_equal(_np(c), rc)
+
+
+@pytest.mark.parametrize("case", ["config2-cache", "config2-new", "dims"])
+def test_tq4_encoder_bit_exact(case):
+    _say(f"tq4 encoder {case}")
+    w = workloads.config2(T=1024) if case != "config2-cache" else workloads.config2()
+    if case == "config2-cache":
+        xs = [(w.latent, w.sign_mask)]
+    elif case == "config2-new":
+        xs = [(workloads.config2_new_rows(8192), w.sign_mask)]
+    else:
+        rng = np.random.default_rng(3)
+        xs = []
+        for d in (8, 16, 64, 256, 512):
+            x = rng.standard_normal((33, d)).astype(np.float32) * rng.lognormal(0, 1, (33, 1)).astype(np.float32)
+            x[3] = 0
+            xs.append((x, rng.integers(0, 256, d // 8, dtype=np.uint8)))
+    for x, m in xs:
+        c, r = gpu_encode_tq4(x, m)
+        rc, rr = oracle.encode_tq4(x, m)
+        np.testing.assert_array_equal(_np(r).view(np.uint32), rr.view(np.uint32))
+        np.testing.assert_array_equal(_np(c), rc)
+
+
+# ---- decode attention --------------------------------------------------------------------
+
+def _encode_cache(w):
+    if w.qmode == 1:
+        return gpu_encode_fp8(w.latent)
+    return gpu_encode_tq4(w.latent, w.sign_mask)
+
+
+_REF = {}
+
+
+def _oracle_ref(w, c, s, ql, qr, key):
+    """fp64 oracle on the GPU-produced codes, cached per (workload, query) key."""
+    k = (w.name, key)
+    if k not in _REF:
+        _REF.clear()
+        _REF[k] = oracle.decode_attn(w.qmode, w.offsets, _np(c), _np(s), w.k_rope, ql, qr, w.sm_scale,
+                                     sign_mask=w.sign_mask)
+    return _REF[k]
+
+
+def _check_attn(w, c, s, precision, split_rows=0, q_lat=None, q_rope=None, tol=None, label=""):
+    got, glse = gpu_attn(w, c, s, precision, split_rows, q_lat, q_rope)
+    ql = w.q_lat if q_lat is None else q_lat
+    qr = w.q_rope if q_rope is None else q_rope
+    ref, rlse = _oracle_ref(w, c, s, ql, qr, (label, q_lat is None))
+    e = rel_err(got, ref)
+    tol = TOL[precision] if tol is None else tol
+    _say(f"  {label} prec={precision} split={split_rows}: max|err|/max|ref| = {e:.3e} (tol {tol})")
+    assert e <= tol, (label, e)
+    fin = np.isfinite(rlse)
+    assert np.all(np.isneginf(glse[~fin]))
+    assert np.max(np.abs(glse[fin] - rlse[fin])) <= 50 * tol * max(1.0, np.max(np.abs(rlse[fin])))
+    return got
+
+
+@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32])
+def test_attn_config0_and_split_invariance(precision):
+    _say(f"attn config0 precision={precision}")
+    w = workloads.config0()
+    c, s = _encode_cache(w)
+    outs = [_check_attn(w, c, s, precision, sr, label="config0") for sr in (0, 256, 128, 64, 32)]
+    for o in outs[1:]:
+        assert rel_err(o, outs[0]) <= 2 * TOL[precision]
+
+
+@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32])
+def test_attn_full_T32768(qmode, precision):
+    _say(f"attn T=32768 H=128 qmode={qmode} precision={precision}")
+    w = workloads.config1() if qmode == 1 else workloads.config2()
+    c, s = _encode_cache(w)
+    _check_attn(w, c, s, precision, label=w.name)
+    if precision == kvq.KVQ_PREC_MFMA_BF16:  # a few explicit split sizes
+        for sr in (32768, 4096, 4704):
+            _check_attn(w, c, s, precision, sr, label=w.name)
+
+
+@pytest.mark.parametrize("qmode", [1, 2])
+def test_attn_peaked_softmax(qmode):
+    _say(f"attn peaked qmode={qmode}")
+    w = workloads.config2(T=3000) if qmode == 2 else workloads.config1(T=3000)
+    c, s = _encode_cache(w)
+    ql = (w.q_lat * 50).astype(np.float32)
+    qr = (w.q_rope * 50).astype(np.float32)
+    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+        _check_attn(w, c, s, prec, q_lat=ql, q_rope=qr, label="peaked")
+        _check_attn(w, c, s, prec, split_rows=96, q_lat=ql, q_rope=qr, label="peaked-split96")
+
+
+def test_attn_ragged_edges():
+    _say("attn ragged edges")
+    w = workloads.DecodeWorkload("edges", 77, [1, 0, 33, 100, 257, 5], 20, qmode=1)
+    c, s = _encode_cache(w)
+    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+        for sr in (0, 32, 64):
+            got = _check_attn(w, c, s, prec, sr, label="edges")
+            assert np.all(got[1] == 0)  # empty sequence
+    w2 = workloads.DecodeWorkload("edges-tq4", 78, [1, 40, 0, 129], 16, qmode=2)
+    c2, s2 = _encode_cache(w2)
+    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+        _check_attn(w2, c2, s2, prec, 32, label="edges-tq4")
+
+
+def test_attn_ragged_config3_sampled_heads():
+    _say("attn config3 (ragged, 33 sequences) sampled heads")
+    w = workloads.config3()
+    c, s = _encode_cache(w)
+    got, glse = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA_BF16)
+    heads = np.array([0, 37, 127])
+    ref, rlse = oracle.decode_attn(1, w.offsets, _np(c), _np(s), w.k_rope, w.q_lat[:, heads], w.q_rope[:, heads],
+                                   w.sm_scale)
+    e = rel_err(got[:, heads], ref)
+    _say(f"  config3 heads {list(heads)}: {e:.3e}")
+    assert e <= 2e-3
+
+
+def test_attn_scaled_config3_all_heads():
+    _say("attn config3/16 all heads")
+    w = workloads.config3(scale=16)
+    c, s = _encode_cache(w)
+    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+        _check_attn(w, c, s, prec, label=w.name)
+
+
+def test_attn_deterministic():
+    _say("attn determinism")
+    w = workloads.config1(T=5000)
+    c, s = _encode_cache(w)
+    a, la = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA_BF16)
+    b, lb = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA_BF16)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+# ---- q4_0 ----------------------------------------------------------------------------
+
+def _q4_gpu(w, kp, vp):
+    return kvq.q4_cache(kp, vp, _t(w.table), 64)
+
+
+def _run_q4(w, with_prefill=True):
+    kp = torch.zeros((w.n_cells, 8, 144), dtype=torch.uint8, device=DEV)
+    vp = torch.zeros_like(kp)
+    cache = _q4_gpu(w, kp, vp)
+    okp, ovp = w.empty_pools()
+    if with_prefill:
+        kvq.kvq_append_q4_0(cache, _t(w.pos0_prefill), _t(w.prefill_off), int(w.prefill_off[-1]),
+                            _t(w.k_prefill), _t(w.v_prefill))
+        oracle.append_q4_0(okp, ovp, w.table, 64, w.pos0_prefill, w.prefill_off, w.k_prefill, w.v_prefill)
+    kvq.kvq_append_q4_0(cache, _t(w.pos0_append), _t(w.append_off), int(w.append_off[-1]),
+                        _t(w.k_append), _t(w.v_append))
+    oracle.append_q4_0(okp, ovp, w.table, 64, w.pos0_append, w.append_off, w.k_append, w.v_append)
+    torch.cuda.synchronize()
+    return cache, kp, vp, okp, ovp
+
+
+@pytest.mark.parametrize("scale", [8, 1])
+def test_q4_append_gather_bit_exact(scale):
+    _say(f"q4_0 append+gather scale={scale}")
+    w = workloads.Q4Workload(scale=scale)
+    cache, kp, vp, okp, ovp = _run_q4(w)
+    np.testing.assert_array_equal(_np(kp), okp)
+    np.testing.assert_array_equal(_np(vp), ovp)
+    total = int(w.final_off[-1])
+    kd = torch.zeros((total, 8, 256), dtype=torch.int16, device=DEV)
+    vd = torch.zeros_like(kd)
+    kvq.kvq_gather_q4_0(cache, _t(w.final_off), total, kd, vd)
+    torch.cuda.synchronize()
+    if scale == 1:  # the oracle's gather is slow: compare three sequences
+        sel = [0, 7, 15]
+        for s in sel:
+            lo, hi = w.final_off[s], w.final_off[s + 1]
+            off = np.array([0, hi - lo], np.int64)
+            rk, rv = oracle.gather_q4_0(okp, ovp, w.table[s:s + 1], 64, off)
+            np.testing.assert_array_equal(_np(kd)[lo:hi].view(np.uint16), rk)
+            np.testing.assert_array_equal(_np(vd)[lo:hi].view(np.uint16), rv)
+    else:
+        rk, rv = oracle.gather_q4_0(okp, ovp, w.table, 64, w.final_off)
+        np.testing.assert_array_equal(_np(kd).view(np.uint16), rk)
+        np.testing.assert_array_equal(_np(vd).view(np.uint16), rv)
+
+
+def test_q4_no_rotate_fixtures_and_invalid_pages():
+    _say("q4_0 fixtures")
+    fx = workloads.q4_tie_fixtures()  # blocks of 32 in the rotated domain
+    n_blocks = fx.shape[0]
+    rows = np.zeros((1, 8, 256), np.float32)
+    flat = rows.reshape(-1)
+    flat[:n_blocks * 32] = fx.reshape(-1)
+    table = np.array([[2, -1]], np.int32)
+    kp = torch.zeros((3 * 64, 8, 144), dtype=torch.uint8, device=DEV)
+    vp = torch.zeros_like(kp)
+    cache = kvq.q4_cache(kp, vp, _t(table), 64)
+    pos0 = np.array([5], np.int32)
+    off = np.array([0, 1], np.int64)
+    kvq.kvq_append_q4_0(cache, _t(pos0), _t(off), 1, _t(rows), _t(rows), flags=kvq.KVQ_Q4_NO_ROTATE)
+    okp = np.zeros((3 * 64, 8, 144), np.uint8)
+    ovp = okp.copy()
+    oracle.append_q4_0(okp, ovp, table, 64, pos0, off, rows, rows, no_rotate=True)
+    np.testing.assert_array_equal(_np(kp), okp)
+    # a position whose page entry is -1 and one beyond the table: nothing written
+    kvq.kvq_append_q4_0(cache, _t(np.array([64], np.int32)), _t(off), 1, _t(rows), _t(rows))
+    kvq.kvq_append_q4_0(cache, _t(np.array([200], np.int32)), _t(off), 1, _t(rows), _t(rows))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(kp), okp)

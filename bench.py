@@ -177,10 +177,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
         "data": "synthetic (seeded; N(0,1) latents x lognormal row gain, outlier channels, zero rows)",
         "config": {"workload": w.name, "seqs": 1, "T": T, "heads": H, "qmode": "fp8" if qmode == 1 else "tq4",
-                   "precision": "mfma-bf16" if args.precision == 0 else "fp32", "kv_copies": args.kv_copies,
+                   "precision": "mfma-fp16" if args.precision == 0 else "fp32", "kv_copies": args.kv_copies,
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},

@@ -45,7 +45,7 @@ extern "C" {
 /* ---- modes ---------------------------------------------------------------- */
 #define KVQ_QMODE_FP8 1      /* e4m3 codes [rows][dim] + fp32 scale per row           */
 #define KVQ_QMODE_TQ4 2      /* 4-bit codebook indices [rows][dim/2] + fp32 radius    */
-#define KVQ_PREC_MFMA_BF16 0 /* bf16 matrix-core contractions, fp32 softmax/scales   */
+#define KVQ_PREC_MFMA 0      /* 16-bit matrix-core contractions, fp32 softmax/scales */
 #define KVQ_PREC_FP32 1      /* fp32 vector arithmetic throughout (check path)        */
 #define KVQ_Q4_NO_ROTATE 1u  /* append: rows are already in the rotated domain        */
 
@@ -150,10 +150,15 @@ int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_of
  * R q and un-rotates the merged output (R = H D / sqrt(dim)).
  * A sequence with no rows gets out = 0 and lse = -Inf.
  * Tolerance against an fp64 evaluation on the same codes:
- *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA_BF16), <= 1e-5 (KVQ_PREC_FP32). */
+ *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA), <= 1e-5 (KVQ_PREC_FP32).
+ * KVQ_PREC_MFMA operands: latent codes in fp16 (exact for every e4m3 value and
+ * codebook level); the latent query scaled per head by a power of two and
+ * split into two fp16 terms; the rope query split into two bf16 terms (k_rope
+ * is bf16); the probabilities p * rho_t scaled per T-split by a power of two
+ * and rounded to fp16; fp32 accumulation, softmax and per-row scales. */
 typedef struct kvq_attn_args {
     int32_t qmode;              /* KVQ_QMODE_FP8 or KVQ_QMODE_TQ4                 */
-    int32_t precision;          /* KVQ_PREC_MFMA_BF16 or KVQ_PREC_FP32            */
+    int32_t precision;          /* KVQ_PREC_MFMA or KVQ_PREC_FP32                 */
     int32_t n_seqs;             /* >= 1                                           */
     int32_t n_heads;            /* 1 .. 256                                       */
     int32_t dim_lat;            /* must be 512                                    */
@@ -211,13 +216,19 @@ int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, in
  *                         S.1111.111 reads as +0, [KV8] HIP portability note);
  *   KVQ_CVT_F32_TO_F16    fp32 -> binary16 bits, round to nearest even (the q4_0
  *                         scale and gather outputs);
- *   KVQ_CVT_F32_TO_BF16   fp32 -> bf16 bits, round to nearest even (the query
- *                         and probability operands of the matrix-core path).
+ *   KVQ_CVT_F32_TO_BF16   fp32 -> bf16 bits, round to nearest even (the rope
+ *                         query terms of the matrix-core path);
+ *   KVQ_CVT_E4M3_TO_F16   e4m3 byte -> binary16 bits with the instruction the
+ *                         matrix-core path uses (v_cvt_scalef32_pk_f16_fp8, scale
+ *                         1): exact for the 254 finite codes; the two NaN codes,
+ *                         which kvq_encode_fp8 never writes, are outside the
+ *                         attention's contract.
  * in/out: device arrays of n elements of the source/destination type. */
 #define KVQ_CVT_F32_TO_E4M3 1
 #define KVQ_CVT_E4M3_TO_BF16 2
 #define KVQ_CVT_F32_TO_F16 3
 #define KVQ_CVT_F32_TO_BF16 4
+#define KVQ_CVT_E4M3_TO_F16 5
 int kvq_convert(int kind, const void* in, int64_t n, void* out, void* stream);
 
 /* ---- binding support ------------------------------------------------------

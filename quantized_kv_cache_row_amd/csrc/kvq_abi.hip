@@ -49,7 +49,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUN
 int check_attn(const kvq_attn_args* a) {
     if (!a) return KVQ_ERR_INVALID_ARG;
     if (a->qmode != KVQ_QMODE_FP8 && a->qmode != KVQ_QMODE_TQ4) return KVQ_ERR_UNSUPPORTED;
-    if (a->precision != KVQ_PREC_MFMA_BF16 && a->precision != KVQ_PREC_FP32) return KVQ_ERR_UNSUPPORTED;
+    if (a->precision != KVQ_PREC_MFMA && a->precision != KVQ_PREC_FP32) return KVQ_ERR_UNSUPPORTED;
     if (a->dim_lat != 512 || a->dim_rope != 64) return KVQ_ERR_UNSUPPORTED;
     if (a->n_seqs < 1 || a->n_heads < 1 || a->total_rows < 0 || a->split_rows < 0) return KVQ_ERR_INVALID_ARG;
     if (a->n_heads > 256) return KVQ_ERR_UNSUPPORTED;
@@ -173,7 +173,7 @@ int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, in
 }
 
 int kvq_convert(int kind, const void* in, int64_t n, void* out, void* stream) {
-    if (kind < KVQ_CVT_F32_TO_E4M3 || kind > KVQ_CVT_F32_TO_BF16) return KVQ_ERR_UNSUPPORTED;
+    if (kind < KVQ_CVT_F32_TO_E4M3 || kind > KVQ_CVT_E4M3_TO_F16) return KVQ_ERR_UNSUPPORTED;
     if (n < 0) return KVQ_ERR_INVALID_ARG;
     if (n == 0) return KVQ_OK;
     if (!in || !out || !aligned(in, 4) || !aligned(out, 4)) return KVQ_ERR_INVALID_ARG;

@@ -22,10 +22,10 @@
 //   4. k_merge    -- one wave per (sequence, head): combine the splits,
 //                    TQ4 un-rotation, write out / lse.
 //
-// Matrix-core path: the tile's codes are converted exactly to bf16 in LDS (row
-// major for the score, transposed for PV); per wave v_mfma_f32_16x16x32_bf16
-// computes S^T = X q^T (16 rows x 16 heads, K = 576 in 18 steps) with the
-// latent and rope parts in separate accumulators so rho_t is applied in fp32;
+// Matrix-core path: the tile's codes are converted exactly to fp16 in LDS (row
+// major for the score, transposed for PV); per wave 16x16x32 MFMAs compute
+// S^T = X q^T (16 rows x 16 heads, K = 512 latent + 64 rope) with the latent
+// and rope parts in separate accumulators so rho_t is applied in fp32;
 // the probabilities come out of the score accumulators in exactly the layout
 // the PV step needs as its B operand (the PV contraction's K order is a
 // permutation of the tile's rows), and O^T = X^T P'^T accumulates 512 x 16 in
@@ -334,20 +334,56 @@ __global__ __launch_bounds__(256) void k_attn_f32(kvq_attn_args a, Plan p, const
     }
 }
 
-// ---- 3b. bf16 matrix-core path ------------------------------------------------------------
+// ---- 3b. matrix-core path ---------------------------------------------------------------------
+// Operand precision (chosen by measurement: bf16 query and probabilities cost
+// 2e-3 .. 1.5e-2 of the output on these workloads, whose outputs are
+// near-cancelling averages):
+//  - latent codes: fp16, exact (every e4m3 value and every bf16 codebook level);
+//  - latent query: per head scaled by a power of two (max |q| in [256, 512)),
+//    then split q = hi + lo in fp16 (22-bit significand), two MFMA chains;
+//  - rope: k_rope is bf16; the rope query is split hi + lo in bf16;
+//  - probabilities p * rho_t: times a per-split power of two rs (max rho * rs in
+//    [0.5, 1)), then fp16;
+//  - accumulation fp32; the power-of-two scales are undone exactly in fp32.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int XS_STRIDE = DL + DR + 8;  // bf16 per row-major tile row (padded)
-constexpr int XT_STRIDE = MF_TILE + 8;  // bf16 per transposed tile row (padded)
+constexpr int XS_STRIDE = DL + DR + 8;  // halfwords per row-major tile row (padded)
+constexpr int XT_STRIDE = MF_TILE + 8;  // halfwords per transposed tile row (padded)
 
+__device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) { return f16_bits(lo) | (f16_bits(hi) << 16); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-__device__ __forceinline__ uint32_t tq4_bf16(uint32_t idx) { return c_tq4_level[idx] >> 16; }
+// e4m3 byte pair (bits 0..15 of w when HI is false, 16..31 otherwise) -> two fp16, exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+    const f16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// TQ4 nibble -> fp16 bits of the codebook level (exact).
+__device__ __forceinline__ uint32_t tq4_f16(uint32_t idx) { return f16_bits(u2f(c_tq4_level[idx])); }
+
+// Power of two 2^k with max_abs * 2^k in [lo_target, 2 lo_target); 1 if max_abs == 0.
+__device__ __forceinline__ float pow2_scale_for(float max_abs, int log2_target) {
+    if (!(max_abs > 0.0f)) return 1.0f;
+    int e = (int)((f2u(max_abs) >> 23) & 255u) - 127;  // floor(log2) for normal values
+    if (e < -126) e = -126;
+    int k = log2_target - e;
+    if (k > 127) k = 127;
+    if (k < -126) k = -126;
+    return u2f((uint32_t)(k + 127) << 23);
+}
 
 // Workgroup = (chunk, head group of 16 * nw heads), nw = blockDim.x / 64 waves,
 // wave w owns heads h0 + 16 w .. +15.  Tiles of 32 rows.
@@ -356,6 +392,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
     __shared__ __align__(16) uint16_t xs[MF_TILE][XS_STRIDE];
     __shared__ __align__(16) uint16_t xt[DL][XT_STRIDE];
     __shared__ float rho_s[MF_TILE];
+    __shared__ float red_s[4];
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -369,21 +406,58 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
     const int h0 = blockIdx.y * p.heads_per_group + wave * MF_WAVE_HEADS;
     const int head = h0 + n;
     const bool head_ok = head < a.n_heads;
+    const float rho_mul = QMODE == KVQ_QMODE_TQ4 ? INV_SQRT_DL : 1.0f;
 
-    // query operand (B of the score): lane (g, n) holds q[head][32 ks + 8 g .. + 7]
-    uint4 qb[18];
-    {
-        const float* ql = qsrc + ((int64_t)s * a.n_heads + (head_ok ? head : 0)) * DL;
-        const float* qr = a.q_rope + ((int64_t)s * a.n_heads + (head_ok ? head : 0)) * DR;
+    // ---- per-split probability scale rs from the largest row scale
+    float rmax = 0.0f;
+    for (int64_t t = r0 + tid; t < r1; t += nthreads) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
+    rmax = wave_max(rmax);
+    if (lane == 0) red_s[wave] = rmax;
+    __syncthreads();
+    rmax = red_s[0];
+    for (int i = 1; i < nthreads / 64; i++) rmax = fmaxf(rmax, red_s[i]);
+    const float rs = pow2_scale_for(rmax * rho_mul, -1);  // max rho * rs in [0.5, 1)
+
+    // ---- query operands: lane (g, n) holds q[head][32 ks + 8 g .. + 7]
+    const float* ql = qsrc + ((int64_t)s * a.n_heads + (head_ok ? head : 0)) * DL;
+    const float* qr = a.q_rope + ((int64_t)s * a.n_heads + (head_ok ? head : 0)) * DR;
+    float qmax = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 18; ks++) {
-            const float* src = ks < 16 ? ql + 32 * ks + 8 * g : qr + 32 * (ks - 16) + 8 * g;
-            float f[8];
+    for (int ks = 0; ks < 16; ks++)
 #pragma unroll
-            for (int i = 0; i < 8; i++) f[i] = head_ok ? src[i] : 0.0f;
-            qb[ks] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                                pack_bf16x2(f[6], f[7]));
+        for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, head_ok ? fabsf(ql[32 * ks + 8 * g + i]) : 0.0f);
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+    const float qs = pow2_scale_for(qmax, 8);  // max |q| * qs in [256, 512)
+    const float qinv = 1.0f / qs;              // exact
+    uint4 qh[16], qlo[16], rh[2], rl[2];
+#pragma unroll
+    for (int ks = 0; ks < 16; ks++) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float f0 = head_ok ? ql[32 * ks + 8 * g + 2 * i] * qs : 0.0f;
+            const float f1 = head_ok ? ql[32 * ks + 8 * g + 2 * i + 1] * qs : 0.0f;
+            const float h0f = (float)(_Float16)f0, h1f = (float)(_Float16)f1;
+            hw[i] = pack_f16x2(h0f, h1f);
+            lw[i] = pack_f16x2(f0 - h0f, f1 - h1f);
         }
+        qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        qlo[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float f0 = head_ok ? qr[32 * ks + 8 * g + 2 * i] : 0.0f;
+            const float f1 = head_ok ? qr[32 * ks + 8 * g + 2 * i + 1] : 0.0f;
+            const float b0 = u2f(f32_to_bf16_rne(f0) << 16), b1 = u2f(f32_to_bf16_rne(f1) << 16);
+            hw[i] = pack_bf16x2(b0, b1);
+            lw[i] = pack_bf16x2(f0 - b0, f1 - b1);
+        }
+        rh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        rl[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
     f32x4_t acc_o[32];
@@ -394,9 +468,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
 
     for (int64_t t0 = r0; t0 < r1; t0 += MF_TILE) {
         const int nt = (int)min((int64_t)MF_TILE, r1 - t0);
-        // ---- stage the tile: codes -> bf16 (row-major xs and transposed xt), rope, rho
+        // ---- stage the tile: codes -> fp16 (row-major xs and transposed xt), rope, rho
         if (QMODE == KVQ_QMODE_FP8) {
-            // 32 rows x 512 codes: 16-byte units, 32 per row
             for (int u = tid; u < MF_TILE * 32; u += nthreads) {
                 const int row = u >> 5, col = (u & 31) * 16;
                 uint4 raw = make_uint4(0, 0, 0, 0);
@@ -405,10 +478,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
                 uint32_t o[8];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const uint32_t b0 = e4m3_to_bf16(w[i] & 0xFF), b1 = e4m3_to_bf16((w[i] >> 8) & 0xFF);
-                    const uint32_t b2 = e4m3_to_bf16((w[i] >> 16) & 0xFF), b3 = e4m3_to_bf16(w[i] >> 24);
-                    o[2 * i] = b0 | (b1 << 16);
-                    o[2 * i + 1] = b2 | (b3 << 16);
+                    o[2 * i] = e4m3x2_to_f16x2<false>(w[i]);
+                    o[2 * i + 1] = e4m3x2_to_f16x2<true>(w[i]);
                 }
                 *reinterpret_cast<uint4*>(&xs[row][col]) = make_uint4(o[0], o[1], o[2], o[3]);
                 *reinterpret_cast<uint4*>(&xs[row][col + 8]) = make_uint4(o[4], o[5], o[6], o[7]);
@@ -419,7 +490,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
                 }
             }
         } else {
-            // 32 rows x 256 code bytes: 16-byte units (32 elements), 16 per row
             for (int u = tid; u < MF_TILE * 16; u += nthreads) {
                 const int row = u >> 4, col = (u & 15) * 32;
                 uint4 raw = make_uint4(0, 0, 0, 0);
@@ -431,7 +501,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
 #pragma unroll
                     for (int k = 0; k < 4; k++) {
                         const uint32_t byte = (w[i] >> (8 * k)) & 0xFF;
-                        o[4 * i + k] = tq4_bf16(byte & 15u) | (tq4_bf16(byte >> 4) << 16);
+                        o[4 * i + k] = tq4_f16(byte & 15u) | (tq4_f16(byte >> 4) << 16);
                     }
                 if (row >= nt) {
 #pragma unroll
@@ -448,21 +518,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
                 }
             }
         }
-        // rope: 32 rows x 64 bf16 = 8 units of 16 bytes per row
-        for (int u = tid; u < MF_TILE * 8; u += nthreads) {
+        for (int u = tid; u < MF_TILE * 8; u += nthreads) {  // rope (bf16), 8 units of 16 bytes per row
             const int row = u >> 3, col = (u & 7) * 8;
             uint4 raw = make_uint4(0, 0, 0, 0);
             if (row < nt) raw = *reinterpret_cast<const uint4*>(a.k_rope + (t0 + row) * DR + col);
             *reinterpret_cast<uint4*>(&xs[row][DL + col]) = raw;
         }
-        for (int u = tid; u < MF_TILE; u += nthreads) {
-            float r = u < nt ? a.row_scale[t0 + u] : 0.0f;
-            if (QMODE == KVQ_QMODE_TQ4) r *= INV_SQRT_DL;
-            rho_s[u] = r;
-        }
+        for (int u = tid; u < MF_TILE; u += nthreads) rho_s[u] = u < nt ? a.row_scale[t0 + u] * rho_mul : 0.0f;
         __syncthreads();
 
-        // ---- scores S^T (rows x heads): two 16-row blocks
+        // ---- scores S^T (rows x heads), two 16-row blocks
         f32x4_t sl[2], sr[2];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
@@ -471,13 +536,15 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
             const uint16_t* xrow = &xs[16 * rb + n][8 * g];
 #pragma unroll
             for (int ks = 0; ks < 16; ks++) {
-                const uint4 av = *reinterpret_cast<const uint4*>(xrow + 32 * ks);
-                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(qb[ks]), sl[rb], 0, 0, 0);
+                const f16x8_t av = as_f16x8(*reinterpret_cast<const uint4*>(xrow + 32 * ks));
+                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_f16x8(qh[ks]), sl[rb], 0, 0, 0);
+                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_f16x8(qlo[ks]), sl[rb], 0, 0, 0);
             }
 #pragma unroll
-            for (int ks = 16; ks < 18; ks++) {
-                const uint4 av = *reinterpret_cast<const uint4*>(xrow + 32 * ks);
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(qb[ks]), sr[rb], 0, 0, 0);
+            for (int ks = 0; ks < 2; ks++) {
+                const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(xrow + DL + 32 * ks));
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(rh[ks]), sr[rb], 0, 0, 0);
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(rl[ks]), sr[rb], 0, 0, 0);
             }
         }
         // lane (g, n): rows 16 rb + 4 g + r of head n
@@ -489,7 +556,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
             for (int r = 0; r < 4; r++) {
                 const int t = 16 * rb + 4 * g + r;
                 rr[rb][r] = rho_s[t];
-                const float v = t < nt ? c2 * (rr[rb][r] * sl[rb][r] + sr[rb][r]) : -INFINITY;
+                const float v = t < nt ? c2 * (rr[rb][r] * (sl[rb][r] * qinv) + sr[rb][r]) : -INFINITY;
                 sc[rb][r] = v;
                 tmax = fmaxf(tmax, v);
             }
@@ -506,35 +573,36 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
             for (int r = 0; r < 4; r++) {
                 const float pv = (sc[rb][r] == -INFINITY) ? 0.0f : exp2f(sc[rb][r] - m_new);
                 psum += pv;
-                pw[r] = pv * rr[rb][r];
+                pw[r] = pv * (rr[rb][r] * rs);
             }
-            pb[2 * rb] = pack_bf16x2(pw[0], pw[1]);
-            pb[2 * rb + 1] = pack_bf16x2(pw[2], pw[3]);
+            pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
+            pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
         }
         l_part = l_part * alpha + psum;
         m_run = m_new;
         // PV B operand: k-slots 8 g + j <-> rows {4g..4g+3, 16+4g..16+4g+3}
-        const bf16x8_t bop = as_bf16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
+        const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
 #pragma unroll
         for (int mb = 0; mb < 32; mb++) {
             const uint16_t* col = &xt[16 * mb + n][0];
             const uint2 lo = *reinterpret_cast<const uint2*>(col + 4 * g);
             const uint2 hi = *reinterpret_cast<const uint2*>(col + 16 + 4 * g);
-            const bf16x8_t aop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            const f16x8_t aop = as_f16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
             acc_o[mb] = acc_o[mb] * alpha;
-            acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc_o[mb], 0, 0, 0);
+            acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[mb], 0, 0, 0);
         }
         __syncthreads();
     }
-    // ---- partials: lane (g, n) holds O[head n][16 mb + 4 g + r]
+    // ---- partials: lane (g, n) holds O[head n][16 mb + 4 g + r] * rs
     l_part += __shfl_xor(l_part, 16, 64);
     l_part += __shfl_xor(l_part, 32, 64);
+    const float rsinv = 1.0f / rs;  // exact
     if (head_ok) {
         float* dst = p.part_o + (c * a.n_heads + head) * DL + 4 * g;
 #pragma unroll
         for (int mb = 0; mb < 32; mb++)
-            *reinterpret_cast<float4*>(dst + 16 * mb) = make_float4(acc_o[mb][0], acc_o[mb][1], acc_o[mb][2],
-                                                                    acc_o[mb][3]);
+            *reinterpret_cast<float4*>(dst + 16 * mb) =
+                make_float4(acc_o[mb][0] * rsinv, acc_o[mb][1] * rsinv, acc_o[mb][2] * rsinv, acc_o[mb][3] * rsinv);
         if (g == 0) {
             p.part_m[c * a.n_heads + head] = m_run;  // log2 units
             p.part_l[c * a.n_heads + head] = l_part;

@@ -91,6 +91,27 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return u2f(f2u(mag) | sign);
 }
 
+// Correctly rounded fp32 square root of a finite x >= 0.  v_sqrt_f32 alone is
+// not correctly rounded; its estimate is moved to the representable value
+// whose rounding interval contains sqrt(x), decided exactly in double: the
+// midpoints of neighbouring floats have at most 25 significant bits, so their
+// squares are exact in double.
+__device__ __forceinline__ float sqrt_rn(float x) {
+    if (!(x > 0.0f) || x > 3.4e38f) return x == 0.0f ? x : __builtin_sqrtf(x);
+    float y = __builtin_sqrtf(x);
+    const double xd = (double)x;
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+        const float up = u2f(f2u(y) + 1u);
+        const double mid_hi = 0.5 * ((double)y + (double)up);
+        if (mid_hi * mid_hi < xd) { y = up; continue; }
+        const float dn = u2f(f2u(y) - 1u);
+        const double mid_lo = 0.5 * ((double)y + (double)dn);
+        if (mid_lo * mid_lo > xd) y = dn;
+    }
+    return y;
+}
+
 // ---- wave primitives -------------------------------------------------------
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, KVQ_WAVE); }

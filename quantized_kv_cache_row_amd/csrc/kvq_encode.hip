@@ -107,7 +107,7 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4(const float
     for (int i = 0; i < 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
     float r2 = sq[0] + sq[1];
     for (int m = 1; m < L; m <<= 1) r2 = r2 + shfl_xor_f(r2, m);  // a + b == b + a exactly
-    const float rad = __fsqrt_rn(r2);
+    const float rad = sqrt_rn(r2);
     // random signs: byte j of the mask covers elements 8j .. 8j+7
     const uint32_t sm = valid ? sign_mask[j] : 0u;
 #pragma unroll
@@ -158,6 +158,12 @@ __global__ void k_convert(int kind, const void* __restrict__ in, int64_t n, void
             case KVQ_CVT_F32_TO_F16:
                 ((uint16_t*)out)[i] = (uint16_t)f32_to_f16_rne(((const float*)in)[i]);
                 break;
+            case KVQ_CVT_E4M3_TO_F16: {
+                typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+                const f16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(((const uint8_t*)in)[i], 1.0f, false);
+                ((uint16_t*)out)[i] = __builtin_bit_cast(uint16_t, h[0]);
+                break;
+            }
             default:
                 ((uint16_t*)out)[i] = (uint16_t)f32_to_bf16_rne(((const float*)in)[i]);
                 break;

@@ -15,10 +15,10 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 KVQ_ABI_VERSION = 1
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = 0, 1, 2, 3, 4
 KVQ_QMODE_FP8, KVQ_QMODE_TQ4 = 1, 2
-KVQ_PREC_MFMA_BF16, KVQ_PREC_FP32 = 0, 1
+KVQ_PREC_MFMA, KVQ_PREC_FP32 = 0, 1
 KVQ_Q4_NO_ROTATE = 1
 KVQ_STAGE_PLAN, KVQ_STAGE_QROT, KVQ_STAGE_SPLITS, KVQ_STAGE_MERGE = 0, 1, 2, 3
-KVQ_CVT_F32_TO_E4M3, KVQ_CVT_E4M3_TO_BF16, KVQ_CVT_F32_TO_F16, KVQ_CVT_F32_TO_BF16 = 1, 2, 3, 4
+KVQ_CVT_F32_TO_E4M3, KVQ_CVT_E4M3_TO_BF16, KVQ_CVT_F32_TO_F16, KVQ_CVT_F32_TO_BF16, KVQ_CVT_E4M3_TO_F16 = 1, 2, 3, 4, 5
 
 
 class KvqError(RuntimeError):
@@ -171,10 +171,13 @@ def kvq_encode_tq4(x, sign_mask, codes, radii, stream=None):
 
 
 def q4_cache(k_pool, v_pool, block_table, page_size, head_dim=256):
+    """The cache descriptor; it keeps the tensors it points to alive."""
     n_cells, n_kv, rb = k_pool.shape
-    return KvqQ4Cache(_ptr(k_pool, torch.uint8, "k_pool"), _ptr(v_pool, torch.uint8, "v_pool"),
-                      _ptr(block_table, torch.int32, "block_table"), n_cells, block_table.shape[1],
-                      page_size, n_kv, head_dim)
+    c = KvqQ4Cache(_ptr(k_pool, torch.uint8, "k_pool"), _ptr(v_pool, torch.uint8, "v_pool"),
+                   _ptr(block_table, torch.int32, "block_table"), n_cells, block_table.shape[1],
+                   page_size, n_kv, head_dim)
+    c._keep = (k_pool, v_pool, block_table)
+    return c
 
 
 def kvq_append_q4_0(cache, pos0, src_off, total_new, k_src, v_src, flags=0, stream=None):
@@ -197,8 +200,9 @@ def kvq_gather_q4_0(cache, dst_off, total_rows, k_dst, v_dst, stream=None):
 
 def attn_args(qmode, precision, seq_offsets, total_rows, codes, row_scale, k_rope, q_lat, q_rope, sm_scale, out,
               lse=None, sign_mask=None, split_rows=0):
+    """The argument struct; it keeps the tensors it points to alive."""
     n_seqs, n_heads, dim_lat = q_lat.shape
-    return KvqAttnArgs(
+    a = KvqAttnArgs(
         qmode, precision, n_seqs, n_heads, dim_lat, q_rope.shape[2], split_rows, 0, int(total_rows),
         _ptr(seq_offsets, torch.int64, "seq_offsets"), _ptr(codes, torch.uint8, "codes"),
         _ptr(row_scale, torch.float32, "row_scale"), _ptr(k_rope, (torch.uint16, torch.int16, torch.bfloat16),
@@ -206,6 +210,8 @@ def attn_args(qmode, precision, seq_offsets, total_rows, codes, row_scale, k_rop
         _ptr(sign_mask, torch.uint8, "sign_mask"), _ptr(q_lat, torch.float32, "q_lat"),
         _ptr(q_rope, torch.float32, "q_rope"), _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), float(sm_scale), 0)
+    a._keep = (seq_offsets, codes, row_scale, k_rope, sign_mask, q_lat, q_rope, out, lse)
+    return a
 
 
 def kvq_decode_attn_workspace_bytes(args):

@@ -15,7 +15,7 @@ from quantized_kv_cache_row_amd import kvq, workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = {kvq.KVQ_PREC_MFMA_BF16: 2e-3, kvq.KVQ_PREC_FP32: 1e-5}
+TOL = {kvq.KVQ_PREC_MFMA: 2e-3, kvq.KVQ_PREC_FP32: 1e-5}
 DEV = "cuda"
 
 
@@ -108,6 +108,11 @@ def test_convert_e4m3_bf16_f16_against_oracle():
     np.testing.assert_array_equal(got, oracle.f16_encode(x))
     got = _convert(kvq.KVQ_CVT_F32_TO_BF16, rnd, torch.int16).view(np.uint16)
     np.testing.assert_array_equal(got, oracle.bf16_encode(rnd))
+    # the matrix-core path's hardware e4m3 -> fp16 conversion: exact on the 254 finite codes
+    fin = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    got = _convert(kvq.KVQ_CVT_E4M3_TO_F16, fin, torch.int16).view(np.uint16)
+    np.testing.assert_array_equal(oracle.f16_decode(got), oracle.e4m3_decode(fin))
+    np.testing.assert_array_equal(np.signbit(oracle.f16_decode(got)), np.signbit(oracle.e4m3_decode(fin)))
 
 
 # ---- encoders -----------------------------------------------------------------------
@@ -198,7 +203,7 @@ def _check_attn(w, c, s, precision, split_rows=0, q_lat=None, q_rope=None, tol=N
     return got
 
 
-@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32])
+@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_attn_config0_and_split_invariance(precision):
     _say(f"attn config0 precision={precision}")
     w = workloads.config0()
@@ -209,13 +214,13 @@ def test_attn_config0_and_split_invariance(precision):
 
 
 @pytest.mark.parametrize("qmode", [1, 2])
-@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32])
+@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_attn_full_T32768(qmode, precision):
     _say(f"attn T=32768 H=128 qmode={qmode} precision={precision}")
     w = workloads.config1() if qmode == 1 else workloads.config2()
     c, s = _encode_cache(w)
     _check_attn(w, c, s, precision, label=w.name)
-    if precision == kvq.KVQ_PREC_MFMA_BF16:  # a few explicit split sizes
+    if precision == kvq.KVQ_PREC_MFMA:  # a few explicit split sizes
         for sr in (32768, 4096, 4704):
             _check_attn(w, c, s, precision, sr, label=w.name)
 
@@ -227,7 +232,7 @@ def test_attn_peaked_softmax(qmode):
     c, s = _encode_cache(w)
     ql = (w.q_lat * 50).astype(np.float32)
     qr = (w.q_rope * 50).astype(np.float32)
-    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+    for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         _check_attn(w, c, s, prec, q_lat=ql, q_rope=qr, label="peaked")
         _check_attn(w, c, s, prec, split_rows=96, q_lat=ql, q_rope=qr, label="peaked-split96")
 
@@ -236,13 +241,13 @@ def test_attn_ragged_edges():
     _say("attn ragged edges")
     w = workloads.DecodeWorkload("edges", 77, [1, 0, 33, 100, 257, 5], 20, qmode=1)
     c, s = _encode_cache(w)
-    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+    for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         for sr in (0, 32, 64):
             got = _check_attn(w, c, s, prec, sr, label="edges")
             assert np.all(got[1] == 0)  # empty sequence
     w2 = workloads.DecodeWorkload("edges-tq4", 78, [1, 40, 0, 129], 16, qmode=2)
     c2, s2 = _encode_cache(w2)
-    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+    for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         _check_attn(w2, c2, s2, prec, 32, label="edges-tq4")
 
 
@@ -250,7 +255,7 @@ def test_attn_ragged_config3_sampled_heads():
     _say("attn config3 (ragged, 33 sequences) sampled heads")
     w = workloads.config3()
     c, s = _encode_cache(w)
-    got, glse = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA_BF16)
+    got, glse = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)
     heads = np.array([0, 37, 127])
     ref, rlse = oracle.decode_attn(1, w.offsets, _np(c), _np(s), w.k_rope, w.q_lat[:, heads], w.q_rope[:, heads],
                                    w.sm_scale)
@@ -263,7 +268,7 @@ def test_attn_scaled_config3_all_heads():
     _say("attn config3/16 all heads")
     w = workloads.config3(scale=16)
     c, s = _encode_cache(w)
-    for prec in (kvq.KVQ_PREC_MFMA_BF16, kvq.KVQ_PREC_FP32):
+    for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         _check_attn(w, c, s, prec, label=w.name)
 
 
@@ -271,8 +276,8 @@ def test_attn_deterministic():
     _say("attn determinism")
     w = workloads.config1(T=5000)
     c, s = _encode_cache(w)
-    a, la = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA_BF16)
-    b, lb = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA_BF16)
+    a, la = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)
+    b, lb = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
 

@@ -108,7 +108,7 @@ def main():
         else:
             kvq.kvq_encode_tq4(row, mask, c[T - 1:T], s[T - 1:T])
         kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_PLAN, ws)
-        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_QROT, ws)
+        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_QPREP, ws)
         if ev is not None:
             ev[0].record()
         kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_SPLITS, ws)

@@ -196,11 +196,12 @@ int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, v
  * the sequence lengths may run it once and stages 1..3 per layer; running a
  * stage also gives profilers and timers one kernel per call:
  *   KVQ_STAGE_PLAN   per-sequence T-split prefix into the workspace;
- *   KVQ_STAGE_QROT   TQ4: the rotated query R q into the workspace (no-op for fp8);
+ *   KVQ_STAGE_QPREP  the query operands into the workspace (TQ4: rotated by R;
+ *                    matrix-core path: scaled and split into 16-bit terms);
  *   KVQ_STAGE_SPLITS the attention over every T-split (partial softmax states);
  *   KVQ_STAGE_MERGE  merge of the splits (+ TQ4 un-rotation) into out / lse. */
 #define KVQ_STAGE_PLAN 0
-#define KVQ_STAGE_QROT 1
+#define KVQ_STAGE_QPREP 1
 #define KVQ_STAGE_SPLITS 2
 #define KVQ_STAGE_MERGE 3
 int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, int64_t ws_bytes,

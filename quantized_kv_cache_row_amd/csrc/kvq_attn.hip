@@ -15,21 +15,11 @@
 // un-rotated by R^T after the merge).  The latent rows are never rebuilt.
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
-//   1. k_plan     -- per-sequence split counts -> prefix (ragged batches);
-//   2. k_qrot     -- TQ4 only: q~ = H D q / sqrt(512) per (sequence, head);
-//   3. k_attn_*   -- one workgroup per (T-split, head group): online softmax
-//                    over the split's rows, partial (m, l, O) to the workspace;
-//   4. k_merge    -- one wave per (sequence, head): combine the splits,
-//                    TQ4 un-rotation, write out / lse.
-//
-// Matrix-core path: the tile's codes are converted exactly to fp16 in LDS (row
-// major for the score, transposed for PV); per wave 16x16x32 MFMAs compute
-// S^T = X q^T (16 rows x 16 heads, K = 512 latent + 64 rope) with the latent
-// and rope parts in separate accumulators so rho_t is applied in fp32;
-// the probabilities come out of the score accumulators in exactly the layout
-// the PV step needs as its B operand (the PV contraction's K order is a
-// permutation of the tile's rows), and O^T = X^T P'^T accumulates 512 x 16 in
-// 32 accumulator blocks.
+//   0. k_plan       -- per-sequence T-split counts -> prefix (ragged batches);
+//   1. k_qprep /    -- matrix-core path: the query operands (TQ4: rotated), scaled
+//      k_qrot          and split into 16-bit terms; fp32 path, TQ4: R q in fp32;
+//   2. k_attn_*     -- online softmax over every T-split, partial (m, l, O);
+//   3. k_merge      -- combine the splits, TQ4 un-rotation, write out / lse.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_codebook.inc"
@@ -46,9 +36,22 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float INV_SQRT_DL = 0.044194173824159216f;  // 1 / sqrt(512)
 
+constexpr int F32_HEADS = 8;      // fp32 path: heads per workgroup
+constexpr int MF_HEADS = 16;      // matrix-core path: heads per workgroup (one MFMA N block)
+constexpr int MF_WAVES = 4;       // matrix-core path: waves per workgroup, splitting the rows
+constexpr int MF_TILE = 32;       // rows per wave tile
+constexpr int QPACK_U4 = 144;     // uint4 per packed query (hi 64, lo 64, rope hi 8, rope lo 8)
+constexpr int QP_LO8 = 64;        // fp8 path: lo term as 64 x 8 e4m3 bytes (uint2 units from here)
+constexpr int QP_LO16 = 64;       // TQ4 path: lo term as 64 x 8 fp16
+constexpr int QP_RH = 128, QP_RL = 136;
+constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators are rescaled
+
 struct Plan {
     int64_t* chunk_prefix;  // [n_seqs + 1]
-    float* q_rot;           // [n_seqs][H][512] (TQ4) or nullptr
+    float* q_rot;           // fp32 path, TQ4: [n_seqs][H][512]
+    uint4* q_pack;          // matrix-core path: [n_seqs][H padded to 16][QPACK_U4]
+    float* q_inv;           // matrix-core path: [n_seqs][H padded to 16]
     float* part_m;          // [max_chunks][H]
     float* part_l;          // [max_chunks][H]
     float* part_o;          // [max_chunks][H][512]
@@ -56,41 +59,34 @@ struct Plan {
     int split_rows;
     int heads_per_group;
     int n_groups;
+    int heads_padded;
+    int64_t chunks_per_xcd; // matrix-core grid: chunk c runs on XCD c % 8, all its head groups together
 };
 
 // ---- workspace plan ------------------------------------------------------------
 
-constexpr int F32_HEADS = 8;
-constexpr int MF_WAVE_HEADS = 16;
-constexpr int MF_TILE = 32;
-
 int auto_split_rows(const kvq_attn_args& a) {
     if (a.precision == KVQ_PREC_FP32) return 512;
-    // about one workgroup per compute unit across all sequences and head groups
-    const int heads_per_group = MF_WAVE_HEADS * ((a.n_heads + MF_WAVE_HEADS - 1) / MF_WAVE_HEADS > 4
-                                                     ? 4
-                                                     : (a.n_heads + MF_WAVE_HEADS - 1) / MF_WAVE_HEADS);
-    const int64_t groups = (a.n_heads + heads_per_group - 1) / heads_per_group;
-    const int64_t target_chunks = 512 / groups;
-    int64_t split = (a.total_rows + target_chunks - 1) / (target_chunks > 0 ? target_chunks : 1);
-    split = (split + MF_TILE - 1) / MF_TILE * MF_TILE;
-    if (split < 128) split = 128;
-    if (split > (1 << 20)) split = 1 << 20;
+    // Large splits keep the partial states small next to the KV bytes they
+    // summarize (a partial is 128 heads x 2 KB per split); about two
+    // workgroups per compute unit over all splits and head groups.
+    const int64_t groups = (a.n_heads + MF_HEADS - 1) / MF_HEADS;
+    int64_t split = (a.total_rows * groups + 511) / 512;
+    if (split < 1024) split = 1024;
+    split = (split + MF_WAVES * MF_TILE - 1) / (MF_WAVES * MF_TILE) * (MF_WAVES * MF_TILE);
+    if (split > (1 << 24)) split = 1 << 24;
     return (int)split;
 }
 
-Plan make_plan(const kvq_attn_args& a, void* ws) {
+Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     Plan p{};
     p.split_rows = a.split_rows > 0 ? a.split_rows : auto_split_rows(a);
-    if (a.precision == KVQ_PREC_FP32) {
-        p.heads_per_group = F32_HEADS;
-    } else {
-        int nw = (a.n_heads + MF_WAVE_HEADS - 1) / MF_WAVE_HEADS;
-        if (nw > 4) nw = 4;
-        p.heads_per_group = nw * MF_WAVE_HEADS;
-    }
+    const bool f32 = a.precision == KVQ_PREC_FP32;
+    p.heads_per_group = f32 ? F32_HEADS : MF_HEADS;
     p.n_groups = (a.n_heads + p.heads_per_group - 1) / p.heads_per_group;
+    p.heads_padded = p.n_groups * p.heads_per_group;
     p.max_chunks = (int64_t)a.n_seqs + a.total_rows / p.split_rows + 1;
+    p.chunks_per_xcd = (p.max_chunks + N_XCD - 1) / N_XCD;
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
     int64_t off = 0;
     char* base = (char*)ws;
@@ -99,27 +95,27 @@ Plan make_plan(const kvq_attn_args& a, void* ws) {
         off = align(off + bytes);
         return q;
     };
+    const int64_t rows_q = (int64_t)a.n_seqs * p.heads_padded;
     p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
-    p.q_rot = a.qmode == KVQ_QMODE_TQ4 ? (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL) : nullptr;
+    if (f32 && a.qmode == KVQ_QMODE_TQ4) p.q_rot = (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
+    if (!f32) {
+        p.q_pack = (uint4*)take(sizeof(uint4) * rows_q * QPACK_U4);
+        p.q_inv = (float*)take(sizeof(float) * rows_q);
+    }
     p.part_m = (float*)take(sizeof(float) * p.max_chunks * a.n_heads);
     p.part_l = (float*)take(sizeof(float) * p.max_chunks * a.n_heads);
     p.part_o = (float*)take(sizeof(float) * p.max_chunks * a.n_heads * DL);
+    if (bytes_out) *bytes_out = off;
     return p;
 }
 
 int64_t plan_bytes(const kvq_attn_args& a) {
-    Plan p = make_plan(a, nullptr);
-    int64_t total = 0;
-    auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
-    total += align(sizeof(int64_t) * (a.n_seqs + 1));
-    if (a.qmode == KVQ_QMODE_TQ4) total += align(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
-    total += align(sizeof(float) * p.max_chunks * a.n_heads);
-    total += align(sizeof(float) * p.max_chunks * a.n_heads);
-    total += align(sizeof(float) * p.max_chunks * a.n_heads * DL);
-    return total;
+    int64_t n = 0;
+    make_plan(a, nullptr, &n);
+    return n;
 }
 
-// ---- 1. plan -----------------------------------------------------------------------
+// ---- 0. plan -----------------------------------------------------------------------
 // chunk_prefix[s] = sum_{s' < s} max(1, ceil(T_s' / split)); one workgroup.
 __global__ __launch_bounds__(256) void k_plan(const int64_t* __restrict__ seq_offsets, int n_seqs, int split,
                                              int64_t total_rows, int64_t* __restrict__ chunk_prefix) {
@@ -158,7 +154,7 @@ __device__ __forceinline__ int find_chunk_seq(const int64_t* __restrict__ cp, in
     return lo;
 }
 
-// ---- 2. TQ4 query rotation ----------------------------------------------------------
+// ---- 1a. TQ4 query rotation (fp32 path) ----------------------------------------------------------
 // One wave per (sequence, head): q~ = H (D q) / sqrt(512), 8 consecutive per lane.
 __global__ __launch_bounds__(256) void k_qrot(const float* __restrict__ q, const uint8_t* __restrict__ sign_mask,
                                              int64_t n_rows, float* __restrict__ q_rot) {
@@ -196,7 +192,7 @@ __device__ __forceinline__ float code_value(const uint8_t* __restrict__ row, int
     return u2f(c_tq4_level[(i & 1) ? (b >> 4) : (b & 15u)]);
 }
 
-// ---- 3a. fp32 check path ----------------------------------------------------------------
+// ---- 2a. fp32 check path ----------------------------------------------------------------
 // Workgroup = (chunk, group of 8 heads), 256 threads.  Tiles of 256 rows: one
 // row per thread for the scores, then thread (head = tid/32, 16 dims) for PV.
 template <int QMODE>
@@ -334,13 +330,15 @@ __global__ __launch_bounds__(256) void k_attn_f32(kvq_attn_args a, Plan p, const
     }
 }
 
-// ---- 3b. matrix-core path ---------------------------------------------------------------------
+// ---- matrix-core path ------------------------------------------------------------------------
 // Operand precision (chosen by measurement: bf16 query and probabilities cost
 // 2e-3 .. 1.5e-2 of the output on these workloads, whose outputs are
 // near-cancelling averages):
 //  - latent codes: fp16, exact (every e4m3 value and every bf16 codebook level);
 //  - latent query: per head scaled by a power of two (max |q| in [256, 512)),
-//    then split q = hi + lo in fp16 (22-bit significand), two MFMA chains;
+//    then split q = hi + lo, hi in fp16; lo (at most 2^-12 of q) in fp16 for
+//    TQ4, and for fp8 rows as e4m3 bytes x 2^10 applied by fp8 matrix cores
+//    to the raw codes (lo's own 2^-4 rounding leaves q good to ~2^-16);
 //  - rope: k_rope is bf16; the rope query is split hi + lo in bf16;
 //  - probabilities p * rho_t: times a per-split power of two rs (max rho * rs in
 //    [0.5, 1)), then fp16;
@@ -349,9 +347,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-constexpr int XS_STRIDE = DL + DR + 8;  // halfwords per row-major tile row (padded)
-constexpr int XT_STRIDE = MF_TILE + 8;  // halfwords per transposed tile row (padded)
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -364,17 +360,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// e4m3 byte pair (bits 0..15 of w when HI is false, 16..31 otherwise) -> two fp16, exact.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
-    const f16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-// TQ4 nibble -> fp16 bits of the codebook level (exact).
-__device__ __forceinline__ uint32_t tq4_f16(uint32_t idx) { return f16_bits(u2f(c_tq4_level[idx])); }
-
-// Power of two 2^k with max_abs * 2^k in [lo_target, 2 lo_target); 1 if max_abs == 0.
+// Power of two 2^k with max_abs * 2^k in [2^log2_target, 2^(log2_target+1)); 1 if max_abs == 0.
 __device__ __forceinline__ float pow2_scale_for(float max_abs, int log2_target) {
     if (!(max_abs > 0.0f)) return 1.0f;
     int e = (int)((f2u(max_abs) >> 23) & 255u) - 127;  // floor(log2) for normal values
@@ -385,185 +371,286 @@ __device__ __forceinline__ float pow2_scale_for(float max_abs, int log2_target) 
     return u2f((uint32_t)(k + 127) << 23);
 }
 
-// Workgroup = (chunk, head group of 16 * nw heads), nw = blockDim.x / 64 waves,
-// wave w owns heads h0 + 16 w .. +15.  Tiles of 32 rows.
+// Query operand layout, per lane group g (MFMA k-slot 8 g .. 8 g + 7 of each
+// k-step ks), following the row bytes each lane loads:
+//   fp8: lane g loads 16 code bytes at 64 j + 16 g -> k-steps 2 j, 2 j + 1
+//        cover latent dims 64 j + 16 g + 8 hh + e  (ks = 2 j + hh);
+//   TQ4: lane g loads 16 nibble bytes at 64 j + 16 g -> k-steps 4 j .. 4 j + 3
+//        cover latent dims 128 j + 32 g + 8 hh + e (ks = 4 j + hh);
+//   rope: k-step ks' in {0, 1} covers rope dims 32 ks' + 8 g + e.
+// One packed query (uint4 units): [0,64) hi (index 16 g + ks); lo: fp8 --
+// 64 e4m3 uint2 (x 2^10) at QP_LO8, TQ4 -- 64 fp16 uint4 at QP_LO16; rope hi
+// (index 2 g + ks') at QP_RH, rope lo at QP_RL.
 template <int QMODE>
-__global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, const float* __restrict__ qsrc) {
-    __shared__ __align__(16) uint16_t xs[MF_TILE][XS_STRIDE];
-    __shared__ __align__(16) uint16_t xt[DL][XT_STRIDE];
-    __shared__ float rho_s[MF_TILE];
-    __shared__ float red_s[4];
+__global__ __launch_bounds__(256) void k_qprep(kvq_attn_args a, Plan p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + h
+    if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
+    const int s = (int)(row / p.heads_padded), h = (int)(row % p.heads_padded);
+    const bool valid = h < a.n_heads;
+    const float* src = a.q_lat + ((int64_t)s * a.n_heads + (valid ? h : 0)) * DL + 8 * lane;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = valid ? src[i] : 0.0f;
+    if (QMODE == KVQ_QMODE_TQ4) {  // q~ = H D q / sqrt(512)
+        const uint32_t sm = a.sign_mask[lane];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if ((sm >> i) & 1u) v[i] = -v[i];
+#pragma unroll
+        for (int hh = 1; hh < 8; hh <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (!(i & hh)) {
+                    const float x = v[i], y = v[i + hh];
+                    v[i] = x + y;
+                    v[i + hh] = x - y;
+                }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, m);
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] *= INV_SQRT_DL;
+    }
+    float qmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, fabsf(v[i]));
+    qmax = wave_max(qmax);
+    const float qs = pow2_scale_for(qmax, 8);  // max |q| * qs in [256, 512)
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float f0 = v[2 * i] * qs, f1 = v[2 * i + 1] * qs;
+        const float h0 = (float)(_Float16)f0, h1 = (float)(_Float16)f1;
+        hw[i] = pack_f16x2(h0, h1);
+        lw[i] = pack_f16x2(f0 - h0, f1 - h1);
+    }
+    int g, ks;
+    if (QMODE == KVQ_QMODE_FP8) { g = (lane & 7) >> 1; ks = 2 * (lane >> 3) + (lane & 1); }
+    else { g = (lane & 15) >> 2; ks = 4 * (lane >> 4) + (lane & 3); }
+    uint4* dst = p.q_pack + row * QPACK_U4;
+    dst[16 * g + ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    if (QMODE == KVQ_QMODE_FP8) {
+        // lo term as e4m3 bytes, times 2^10, for fp8 matrix cores on the raw codes
+        uint32_t b[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float f = v[i] * qs;
+            const float lo = (f - (float)(_Float16)f) * 1024.0f;
+            b[i >> 2] |= e4m3_rne(lo) << (8 * (i & 3));
+        }
+        reinterpret_cast<uint2*>(dst + QP_LO8)[16 * g + ks] = make_uint2(b[0], b[1]);
+    } else {
+        dst[QP_LO16 + 16 * g + ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    if (lane < 8) {  // rope dims 8 lane .. + 7: k-step lane / 4, lane group lane % 4
+        const float* r = a.q_rope + ((int64_t)s * a.n_heads + (valid ? h : 0)) * DR + 8 * lane;
+        uint32_t rh[4], rl[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float f0 = valid ? r[2 * i] : 0.0f, f1 = valid ? r[2 * i + 1] : 0.0f;
+            const float b0 = u2f(f32_to_bf16_rne(f0) << 16), b1 = u2f(f32_to_bf16_rne(f1) << 16);
+            rh[i] = pack_bf16x2(b0, b1);
+            rl[i] = pack_bf16x2(f0 - b0, f1 - b1);
+        }
+        const int gg = lane & 3, kk = lane >> 2;
+        dst[QP_RH + 2 * gg + kk] = make_uint4(rh[0], rh[1], rh[2], rh[3]);
+        dst[QP_RL + 2 * gg + kk] = make_uint4(rl[0], rl[1], rl[2], rl[3]);
+    }
+    if (lane == 0) p.q_inv[row] = 1.0f / qs;  // exact
+}
+
+// Two e4m3 codes (byte pair HI of w) -> two fp16, exact (hardware conversion, scale 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+    const f16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint4 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
+    return make_uint4(e4m3x2_to_f16x2<false>(w0), e4m3x2_to_f16x2<true>(w0), e4m3x2_to_f16x2<false>(w1),
+                      e4m3x2_to_f16x2<true>(w1));
+}
+
+// Byte tables of the fp16 bits of the 8 positive codebook levels (index 8 + m).
+struct Tq4Lut {
+    uint32_t lo03, lo47, hi03, hi47;
+};
+
+__device__ __forceinline__ Tq4Lut make_tq4_lut() {
+    Tq4Lut t{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        const uint32_t h = f16_bits(u2f(c_tq4_level[8 + m]));  // exact: 8 significant bits
+        const uint32_t lo = h & 0xFF, hi = h >> 8;
+        if (m < 4) { t.lo03 |= lo << (8 * m); t.hi03 |= hi << (8 * m); }
+        else { t.lo47 |= lo << (8 * (m - 4)); t.hi47 |= hi << (8 * (m - 4)); }
+    }
+    return t;
+}
+
+// 8 nibble indices (element k = nibble k of x) -> 8 fp16 codebook levels.  The
+// codebook is symmetric: index i >= 8 is +level[i], index i < 8 is
+// -level[15 - i]; the magnitude comes from a byte table lookup (v_perm).
+__device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
+    const uint32_t neg = ((x >> 3) & 0x11111111u) ^ 0x11111111u;  // 1 where index < 8
+    const uint32_t m = (x & 0x77777777u) ^ (neg * 7u);                // magnitude index
+    const uint32_t me = m & 0x0F0F0F0Fu, mo = (m >> 4) & 0x0F0F0F0Fu;  // elements 0,2,4,6 / 1,3,5,7
+    const uint32_t lo_e = __builtin_amdgcn_perm(t.lo47, t.lo03, me);
+    const uint32_t lo_o = __builtin_amdgcn_perm(t.lo47, t.lo03, mo);
+    const uint32_t hi_e = __builtin_amdgcn_perm(t.hi47, t.hi03, me) | ((neg & 0x01010101u) << 7);
+    const uint32_t hi_o = __builtin_amdgcn_perm(t.hi47, t.hi03, mo) | (((neg >> 4) & 0x01010101u) << 7);
+    const uint32_t ae = __builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u);  // e0 | e2 << 16
+    const uint32_t ao = __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u);  // o0 | o2 << 16
+    const uint32_t be = __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u);  // e4 | e6 << 16
+    const uint32_t bo = __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u);  // o4 | o6 << 16
+    return make_uint4(__builtin_amdgcn_perm(ao, ae, 0x05040100u), __builtin_amdgcn_perm(ao, ae, 0x07060302u),
+                      __builtin_amdgcn_perm(bo, be, 0x05040100u), __builtin_amdgcn_perm(bo, be, 0x07060302u));
+}
+
+constexpr int XS = DL + 16;  // halfwords per LDS tile row: rows 32 bytes apart modulo 128
+
+// Split kernel.  Work item = (T-chunk, group of 16 heads); the items are dealt
+// to XCDs in contiguous runs so the head groups of a chunk share one L2.  The
+// 4 waves of a workgroup take consecutive quarters of the chunk (tiles of 32
+// rows) for the same 16 heads, each with a private LDS tile:
+//   score:  S^T (16 rows x 16 heads) += X(rows, k) q^T -- X straight from the
+//           loaded codes (converted in registers), q hi and lo;
+//   PV:     O^T (16 dims x 16 heads) += X^T P'^T -- X^T from the row-major LDS
+//           tile via ds_read_b64_tr_b16 (lane (g, p) gets rows 4 g .. 4 g + 3 and
+//           16 + 4 g .. + 3 of column p, the k order the score accumulators
+//           already hold P in).
+// The waves' (m, l, O) are merged in LDS; one partial per (chunk, head).
+template <int QMODE>
+__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma(kvq_attn_args a, Plan p) {
+    __shared__ __align__(16) uint16_t tile[MF_WAVES][MF_TILE][XS];
+    __shared__ float red_s[MF_WAVES];
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, n = lane & 15;
-    const int64_t c = blockIdx.x;
+    // workgroups are dealt round-robin to the XCDs: chunk c goes to XCD c % 8 and
+    // its head groups are consecutive there, so they share that XCD's L2
+    const int64_t local = blockIdx.x / N_XCD;
+    const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
+    const int hg = (int)(local % p.n_groups);
     if (c >= p.chunk_prefix[a.n_seqs]) return;
     const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
     const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
     const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
     const int64_t r1 = min(seq_hi, r0 + (int64_t)p.split_rows);
-    const int h0 = blockIdx.y * p.heads_per_group + wave * MF_WAVE_HEADS;
-    const int head = h0 + n;
-    const bool head_ok = head < a.n_heads;
+    const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
+    const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
+    const int head = hg * MF_HEADS + n;  // may exceed n_heads (padded query is zero)
     const float rho_mul = QMODE == KVQ_QMODE_TQ4 ? INV_SQRT_DL : 1.0f;
+    constexpr int CB = QMODE == KVQ_QMODE_FP8 ? DL : DL / 2;  // code bytes per row
 
-    // ---- per-split probability scale rs from the largest row scale
+    // ---- per-split probability scale rs from the largest row scale of the chunk
     float rmax = 0.0f;
-    for (int64_t t = r0 + tid; t < r1; t += nthreads) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
+    for (int64_t t = r0 + tid; t < r1; t += MF_WAVES * 64) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
     rmax = wave_max(rmax);
     if (lane == 0) red_s[wave] = rmax;
     __syncthreads();
-    rmax = red_s[0];
-    for (int i = 1; i < nthreads / 64; i++) rmax = fmaxf(rmax, red_s[i]);
+    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
     const float rs = pow2_scale_for(rmax * rho_mul, -1);  // max rho * rs in [0.5, 1)
 
-    // ---- query operands: lane (g, n) holds q[head][32 ks + 8 g .. + 7]
-    const float* ql = qsrc + ((int64_t)s * a.n_heads + (head_ok ? head : 0)) * DL;
-    const float* qr = a.q_rope + ((int64_t)s * a.n_heads + (head_ok ? head : 0)) * DR;
-    float qmax = 0.0f;
+    // ---- query operands
+    const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
+    uint4 qh[16], ql[16], rh[2], rl[2];
 #pragma unroll
-    for (int ks = 0; ks < 16; ks++)
-#pragma unroll
-        for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, head_ok ? fabsf(ql[32 * ks + 8 * g + i]) : 0.0f);
-    qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
-    qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-    const float qs = pow2_scale_for(qmax, 8);  // max |q| * qs in [256, 512)
-    const float qinv = 1.0f / qs;              // exact
-    uint4 qh[16], qlo[16], rh[2], rl[2];
-#pragma unroll
-    for (int ks = 0; ks < 16; ks++) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float f0 = head_ok ? ql[32 * ks + 8 * g + 2 * i] * qs : 0.0f;
-            const float f1 = head_ok ? ql[32 * ks + 8 * g + 2 * i + 1] * qs : 0.0f;
-            const float h0f = (float)(_Float16)f0, h1f = (float)(_Float16)f1;
-            hw[i] = pack_f16x2(h0f, h1f);
-            lw[i] = pack_f16x2(f0 - h0f, f1 - h1f);
-        }
-        qh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        qlo[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    for (int k = 0; k < 16; k++) {
+        qh[k] = qp[16 * g + k];
+        ql[k] = qp[QP_LO16 + 16 * g + k];
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float f0 = head_ok ? qr[32 * ks + 8 * g + 2 * i] : 0.0f;
-            const float f1 = head_ok ? qr[32 * ks + 8 * g + 2 * i + 1] : 0.0f;
-            const float b0 = u2f(f32_to_bf16_rne(f0) << 16), b1 = u2f(f32_to_bf16_rne(f1) << 16);
-            hw[i] = pack_bf16x2(b0, b1);
-            lw[i] = pack_bf16x2(f0 - b0, f1 - b1);
-        }
-        rh[ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        rl[ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    for (int k = 0; k < 2; k++) {
+        rh[k] = qp[QP_RH + 2 * g + k];
+        rl[k] = qp[QP_RL + 2 * g + k];
     }
+    const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
+    Tq4Lut lut{};
+    if (QMODE == KVQ_QMODE_TQ4) lut = make_tq4_lut();
+
     const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
     f32x4_t acc_o[32];
 #pragma unroll
     for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_part = 0.0f;
-    const int cb = QMODE == KVQ_QMODE_FP8 ? DL : DL / 2;
+    uint16_t(*xs)[XS] = tile[wave];
 
-    for (int64_t t0 = r0; t0 < r1; t0 += MF_TILE) {
-        const int nt = (int)min((int64_t)MF_TILE, r1 - t0);
-        // ---- stage the tile: codes -> fp16 (row-major xs and transposed xt), rope, rho
-        if (QMODE == KVQ_QMODE_FP8) {
-            for (int u = tid; u < MF_TILE * 32; u += nthreads) {
-                const int row = u >> 5, col = (u & 31) * 16;
-                uint4 raw = make_uint4(0, 0, 0, 0);
-                if (row < nt) raw = *reinterpret_cast<const uint4*>(a.codes + (t0 + row) * cb + col);
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-                uint32_t o[8];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    o[2 * i] = e4m3x2_to_f16x2<false>(w[i]);
-                    o[2 * i + 1] = e4m3x2_to_f16x2<true>(w[i]);
-                }
-                *reinterpret_cast<uint4*>(&xs[row][col]) = make_uint4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<uint4*>(&xs[row][col + 8]) = make_uint4(o[4], o[5], o[6], o[7]);
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    xt[col + 2 * i][row] = (uint16_t)(o[i] & 0xFFFF);
-                    xt[col + 2 * i + 1][row] = (uint16_t)(o[i] >> 16);
-                }
-            }
-        } else {
-            for (int u = tid; u < MF_TILE * 16; u += nthreads) {
-                const int row = u >> 4, col = (u & 15) * 32;
-                uint4 raw = make_uint4(0, 0, 0, 0);
-                if (row < nt) raw = *reinterpret_cast<const uint4*>(a.codes + (t0 + row) * cb + col / 2);
-                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-                uint32_t o[16];
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-#pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        const uint32_t byte = (w[i] >> (8 * k)) & 0xFF;
-                        o[4 * i + k] = tq4_f16(byte & 15u) | (tq4_f16(byte >> 4) << 16);
-                    }
-                if (row >= nt) {
-#pragma unroll
-                    for (int i = 0; i < 16; i++) o[i] = 0;
-                }
-#pragma unroll
-                for (int q = 0; q < 4; q++)
-                    *reinterpret_cast<uint4*>(&xs[row][col + 8 * q]) =
-                        make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-#pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    xt[col + 2 * i][row] = (uint16_t)(o[i] & 0xFFFF);
-                    xt[col + 2 * i + 1][row] = (uint16_t)(o[i] >> 16);
-                }
-            }
-        }
-        for (int u = tid; u < MF_TILE * 8; u += nthreads) {  // rope (bf16), 8 units of 16 bytes per row
-            const int row = u >> 3, col = (u & 7) * 8;
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if (row < nt) raw = *reinterpret_cast<const uint4*>(a.k_rope + (t0 + row) * DR + col);
-            *reinterpret_cast<uint4*>(&xs[row][DL + col]) = raw;
-        }
-        for (int u = tid; u < MF_TILE; u += nthreads) rho_s[u] = u < nt ? a.row_scale[t0 + u] * rho_mul : 0.0f;
-        __syncthreads();
-
-        // ---- scores S^T (rows x heads), two 16-row blocks
+    for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+        // ---- scores S^T (rows x heads), two 16-row blocks; rows >= nt are zero
         f32x4_t sl[2], sr[2];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
+            const int row = 16 * rb + n;
+            const bool rok = row < nt;
+            const uint8_t* crow = a.codes + (t0 + (rok ? row : 0)) * CB + 16 * g;
+            const uint16_t* krow = a.k_rope + (t0 + (rok ? row : 0)) * DR + 8 * g;
+            uint4 raw[8];
+#pragma unroll
+            for (int j = 0; j < CB / 64; j++)
+                raw[j] = rok ? *reinterpret_cast<const uint4*>(crow + 64 * j) : make_uint4(0, 0, 0, 0);
+            uint4 kr[2];
+#pragma unroll
+            for (int k = 0; k < 2; k++) kr[k] = rok ? *reinterpret_cast<const uint4*>(krow + 32 * k) : make_uint4(0, 0, 0, 0);
             sl[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             sr[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint16_t* xrow = &xs[16 * rb + n][8 * g];
+            if (QMODE == KVQ_QMODE_FP8) {
 #pragma unroll
-            for (int ks = 0; ks < 16; ks++) {
-                const f16x8_t av = as_f16x8(*reinterpret_cast<const uint4*>(xrow + 32 * ks));
-                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_f16x8(qh[ks]), sl[rb], 0, 0, 0);
-                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, as_f16x8(qlo[ks]), sl[rb], 0, 0, 0);
+                for (int j = 0; j < 8; j++) {
+                    const uint4 x0 = e4m3x8_to_f16x8(raw[j].x, raw[j].y);
+                    const uint4 x1 = e4m3x8_to_f16x8(raw[j].z, raw[j].w);
+                    *reinterpret_cast<uint4*>(&xs[row][64 * j + 16 * g]) = x0;
+                    *reinterpret_cast<uint4*>(&xs[row][64 * j + 16 * g + 8]) = x1;
+                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x0), as_f16x8(qh[2 * j]), sl[rb], 0, 0, 0);
+                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x0), as_f16x8(ql[2 * j]), sl[rb], 0, 0, 0);
+                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x1), as_f16x8(qh[2 * j + 1]), sl[rb], 0, 0, 0);
+                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x1), as_f16x8(ql[2 * j + 1]), sl[rb], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+                    for (int hh = 0; hh < 4; hh++) {
+                        const uint4 xv = tq4x8_to_f16x8(w[hh], lut);
+                        *reinterpret_cast<uint4*>(&xs[row][128 * j + 32 * g + 8 * hh]) = xv;
+                        sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xv), as_f16x8(qh[4 * j + hh]), sl[rb], 0, 0, 0);
+                        sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xv), as_f16x8(ql[4 * j + hh]), sl[rb], 0, 0, 0);
+                    }
+                }
             }
 #pragma unroll
-            for (int ks = 0; ks < 2; ks++) {
-                const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(xrow + DL + 32 * ks));
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(rh[ks]), sr[rb], 0, 0, 0);
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, as_bf16x8(rl[ks]), sr[rb], 0, 0, 0);
+            for (int k = 0; k < 2; k++) {
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
             }
         }
         // lane (g, n): rows 16 rb + 4 g + r of head n
         float sc[2][4], rr[2][4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++)
+        for (int rb = 0; rb < 2; rb++) {
+            const int tb = 16 * rb + 4 * g;
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int t = 16 * rb + 4 * g + r;
-                rr[rb][r] = rho_s[t];
-                const float v = t < nt ? c2 * (rr[rb][r] * (sl[rb][r] * qinv) + sr[rb][r]) : -INFINITY;
+                const bool ok = tb + r < nt;
+                rr[rb][r] = ok ? a.row_scale[t0 + tb + r] * rho_mul : 0.0f;
+                const float v = ok ? c2 * (rr[rb][r] * (sl[rb][r] * qinv) + sr[rb][r]) : -INFINITY;
                 sc[rb][r] = v;
                 tmax = fmaxf(tmax, v);
             }
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2f(m_run - m_new);
+        // lazy rescaling: keep a stale running max unless this tile exceeds it by
+        // more than 2^8 (then p <= 256 stays exact enough in fp32 / fp16)
+        const bool bump = tmax > m_run + LAZY_LOG2;
+        const float m_new = bump ? tmax : m_run;
+        const float alpha = bump ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new)) : 1.0f;
+        const bool any_bump = __any(bump);
         float psum = 0.0f;
         uint32_t pb[4];
 #pragma unroll
@@ -580,91 +667,443 @@ __global__ __launch_bounds__(256) void k_attn_mfma(kvq_attn_args a, Plan p, cons
         }
         l_part = l_part * alpha + psum;
         m_run = m_new;
-        // PV B operand: k-slots 8 g + j <-> rows {4g..4g+3, 16+4g..16+4g+3}
+        if (any_bump) {
+#pragma unroll
+            for (int mb = 0; mb < 32; mb++) acc_o[mb] = acc_o[mb] * alpha;
+        }
         const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
+        // the tile rows written above are read back transposed by other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- PV: source lane (g, n) points at row t0' + n / 4, column 16 mb + 4 (n % 4)
+        const int trow = 4 * g + (n >> 2), tcol = 4 * (n & 3);
 #pragma unroll
         for (int mb = 0; mb < 32; mb++) {
-            const uint16_t* col = &xt[16 * mb + n][0];
-            const uint2 lo = *reinterpret_cast<const uint2*>(col + 4 * g);
-            const uint2 hi = *reinterpret_cast<const uint2*>(col + 16 + 4 * g);
-            const f16x8_t aop = as_f16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-            acc_o[mb] = acc_o[mb] * alpha;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)&xs[trow][16 * mb + tcol]);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)&xs[16 + trow][16 * mb + tcol]);
+            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+            const f16x8_t aop = as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
             acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[mb], 0, 0, 0);
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // ---- partials: lane (g, n) holds O[head n][16 mb + 4 g + r] * rs
+    // ---- merge the waves' states in LDS (each wave's tile holds its own state)
     l_part += __shfl_xor(l_part, 16, 64);
     l_part += __shfl_xor(l_part, 32, 64);
-    const float rsinv = 1.0f / rs;  // exact
-    if (head_ok) {
-        float* dst = p.part_o + (c * a.n_heads + head) * DL + 4 * g;
+    constexpr int OS = DL + 4;  // floats per stored head row (banks shifted per row)
+    float* st = reinterpret_cast<float*>(&tile[wave][0][0]);  // [16][OS] O, then m[16], l[16]
+    __syncthreads();  // every wave is done reading its tile
 #pragma unroll
-        for (int mb = 0; mb < 32; mb++)
-            *reinterpret_cast<float4*>(dst + 16 * mb) =
-                make_float4(acc_o[mb][0] * rsinv, acc_o[mb][1] * rsinv, acc_o[mb][2] * rsinv, acc_o[mb][3] * rsinv);
-        if (g == 0) {
-            p.part_m[c * a.n_heads + head] = m_run;  // log2 units
-            p.part_l[c * a.n_heads + head] = l_part;
+    for (int mb = 0; mb < 32; mb++)
+        *reinterpret_cast<float4*>(st + n * OS + 16 * mb + 4 * g) =
+            make_float4(acc_o[mb][0], acc_o[mb][1], acc_o[mb][2], acc_o[mb][3]);
+    if (g == 0) {
+        st[MF_HEADS * OS + n] = m_run;
+        st[MF_HEADS * OS + MF_HEADS + n] = l_part;
+    }
+    __syncthreads();
+    {
+        const int hh = tid >> 4;             // head within the group
+        const int d0 = (tid & 15) * 32;      // 32 dims per thread
+        float mw[MF_WAVES], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MF_WAVES; w++) {
+            mw[w] = reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + hh];
+            M = fmaxf(M, mw[w]);
+        }
+        float sw[MF_WAVES], L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MF_WAVES; w++) {
+            sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
+            L += sw[w] * reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + MF_HEADS + hh];
+        }
+        const int h = hg * MF_HEADS + hh;
+        if (h < a.n_heads) {
+            float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
+            const float rsinv = 1.0f / rs;  // exact
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                for (int w = 0; w < MF_WAVES; w++) {
+                    const float4 v =
+                        *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&tile[w][0][0]) + hh * OS + d0 + 4 * q);
+                    o.x += sw[w] * v.x; o.y += sw[w] * v.y; o.z += sw[w] * v.z; o.w += sw[w] * v.w;
+                }
+                o.x *= rsinv; o.y *= rsinv; o.z *= rsinv; o.w *= rsinv;
+                *reinterpret_cast<float4*>(dst + 4 * q) = o;
+            }
+            if ((tid & 15) == 0) {
+                p.part_m[c * a.n_heads + h] = M;  // log2 units
+                p.part_l[c * a.n_heads + h] = L;
+            }
         }
     }
 }
 
-// ---- 4. merge --------------------------------------------------------------------------------
-// One wave per (sequence, head); lane holds dims 8 lane .. 8 lane + 7.
+// fp8 split kernel (raw-tile variant).  Same work items and wave split as
+// k_attn_mfma, but every wave streams its rows' raw e4m3 codes into a
+// double-buffered LDS tile with global_load_lds (no register staging, the next
+// tile's load overlaps this tile's math).  Tile row r keeps its 16-byte chunk c
+// at position c ^ r, so both read patterns below spread over all banks:
+//   score: lane (g, n) of row block rb reads tile row 8 (n / 4) + 4 rb + n % 4,
+//          chunks 4 j + g (16 codes -> two fp16 k-steps);  the accumulator row
+//          order then matches the transposed read;
+//   PV:    ds_read_b64_tr_b8: source lane (g, q) points at row 8 g + q / 2,
+//          byte column 16 mb + 8 (q % 2); lane (g, p) receives the 8 codes of
+//          rows 8 g .. 8 g + 7 in column 16 mb + p, converted to fp16 in
+//          registers -- k-slots (g, j) = row 8 g + j, as the probabilities.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+constexpr int RAW_ROW = DL;                   // bytes per raw fp8 tile row
+constexpr int RAW_TILE = MF_TILE * RAW_ROW;   // 16 KB
+
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
+    __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
+    __shared__ __align__(16) uint8_t rope_s[MF_WAVES][MF_TILE * DR * 2];  // rope keys (bf16)
+    __shared__ __align__(16) float rho_s[MF_WAVES][2][64];             // row scales
+    __shared__ float red_s[MF_WAVES];
+    __shared__ float ml_s[MF_WAVES][2][MF_HEADS];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, n = lane & 15;
+    // workgroups are dealt round-robin to the XCDs: chunk c goes to XCD c % 8 and
+    // its head groups are consecutive there, so they share that XCD's L2
+    const int64_t local = blockIdx.x / N_XCD;
+    const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
+    const int hg = (int)(local % p.n_groups);
+    if (c >= p.chunk_prefix[a.n_seqs]) return;
+    const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
+    const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
+    const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
+    const int64_t r1 = min(seq_hi, r0 + (int64_t)p.split_rows);
+    const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
+    const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
+    const int head = hg * MF_HEADS + n;
+
+    // DMA loaders (global -> LDS, no registers); rows past the end re-read row t0,
+    // which holds valid codes and is masked later.
+    auto load_codes = [&](int64_t t0, int buf) {  // 16 x 1 KB: rows 2 i, 2 i + 1
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+        const int rsub = lane >> 5, pos = lane & 31;
+#pragma unroll
+        for (int i = 0; i < MF_TILE / 2; i++) {
+            const int r = 2 * i + rsub;
+            const uint8_t* src = a.codes + (t0 + (r < nt ? r : 0)) * RAW_ROW + 16 * (pos ^ r);
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (__attribute__((address_space(3))) void*)&raw[wave][buf][i * 1024],
+                                             16, 0, 0);
+        }
+    };
+    auto load_rope = [&](int64_t t0) {  // 4 x 1 KB: rows 8 i .. 8 i + 7, row-major
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+#pragma unroll
+        for (int i = 0; i < MF_TILE / 8; i++) {
+            const int r = 8 * i + (lane >> 3);
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k_rope + (t0 + (r < nt ? r : 0)) * DR) + 16 * (lane & 7);
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (__attribute__((address_space(3))) void*)&rope_s[wave][i * 1024],
+                                             16, 0, 0);
+        }
+    };
+    auto load_rho = [&](int64_t t0, int buf) {  // 64 x 4 bytes: row scales of rows 0 .. 31 (and copies)
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+        const int r = lane & 31;
+        __builtin_amdgcn_global_load_lds((const void*)(a.row_scale + t0 + (r < nt ? r : 0)),
+                                         (__attribute__((address_space(3))) void*)&rho_s[wave][buf][0], 4, 0, 0);
+    };
+    auto tile_row = [](int rb, int nn) { return 8 * (nn >> 2) + 4 * rb + (nn & 3); };
+
+    if (w0 < w1) {
+        load_codes(w0, 0);
+        load_rope(w0);
+        load_rho(w0, 0);
+    }
+
+    // ---- per-split probability scale rs from the largest row scale of the chunk
+    float rmax = 0.0f;
+    for (int64_t t = r0 + tid; t < r1; t += MF_WAVES * 64) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
+    rmax = wave_max(rmax);
+    if (lane == 0) red_s[wave] = rmax;
+    __syncthreads();
+    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+    const float rs = pow2_scale_for(rmax, -1);  // max rho * rs in [0.5, 1)
+
+    // ---- query operands
+    const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
+    uint4 qh[16], rh[2], rl[2];
+    uint2 ql8[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+        qh[k] = qp[16 * g + k];
+        ql8[k] = reinterpret_cast<const uint2*>(qp + QP_LO8)[16 * g + k];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        rh[k] = qp[QP_RH + 2 * g + k];
+        rl[k] = qp[QP_RL + 2 * g + k];
+    }
+    const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
+    const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
+
+    f32x4_t acc_o[32];
+#pragma unroll
+    for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_part = 0.0f;
+    int buf = 0;
+
+    for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+        vm_wait_all();  // this tile's codes, rope keys and scales are in LDS
+        const bool more = t0 + MF_TILE < w1;
+        // rope operands and row scales to registers, then the rope buffer is free
+        uint4 kr[2][2];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int k = 0; k < 2; k++)
+                kr[rb][k] = *reinterpret_cast<const uint4*>(&rope_s[wave][tile_row(rb, n) * DR * 2 + 16 * g + 64 * k]);
+        const float4 rho0 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g]);
+        const float4 rho1 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g + 4]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): those reads are done before the buffers refill
+        if (more) {
+            load_codes(t0 + MF_TILE, buf ^ 1);
+            load_rope(t0 + MF_TILE);
+            load_rho(t0 + MF_TILE, buf ^ 1);
+        }
+        const uint8_t* tb = raw[wave][buf];
+        // ---- scores
+        f32x4_t sl[2], sr[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const int r = tile_row(rb, n);
+            sl[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            sr[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t s8 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};  // lo term, x 2^10
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint4 rw = *reinterpret_cast<const uint4*>(tb + r * RAW_ROW + 16 * ((4 * j + g) ^ r));
+                const uint4 x0 = e4m3x8_to_f16x8(rw.x, rw.y);
+                const uint4 x1 = e4m3x8_to_f16x8(rw.z, rw.w);
+                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x0), as_f16x8(qh[2 * j]), sl[rb], 0, 0, 0);
+                s8 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                    (long)(((uint64_t)rw.y << 32) | rw.x), (long)(((uint64_t)ql8[2 * j].y << 32) | ql8[2 * j].x), s8, 0, 0, 0);
+                sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x1), as_f16x8(qh[2 * j + 1]), sl[rb], 0, 0, 0);
+                s8 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+                    (long)(((uint64_t)rw.w << 32) | rw.z), (long)(((uint64_t)ql8[2 * j + 1].y << 32) | ql8[2 * j + 1].x), s8,
+                    0, 0, 0);
+                if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            sl[rb] = sl[rb] + s8 * 0.0009765625f;  // 2^-10
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
+            }
+        }
+        // lane (g, n): accumulator register r of block rb = tile row 8 g + 4 rb + r
+        float sc[2][4], rr[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const float4 rq = rb ? rho1 : rho0;
+            const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const bool ok = 8 * g + 4 * rb + r < nt;
+                rr[rb][r] = ok ? rv[r] : 0.0f;
+                const float v = ok ? c2 * (rv[r] * (sl[rb][r] * qinv) + sr[rb][r]) : -INFINITY;
+                sc[rb][r] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // lazy rescaling: keep a stale running max unless this tile exceeds it by
+        // more than 2^8 (then p <= 256 stays exact enough in fp32 / fp16)
+        const bool bump = tmax > m_run + LAZY_LOG2;
+        const float m_new = bump ? tmax : m_run;
+        const float alpha = bump ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new)) : 1.0f;
+        const bool any_bump = __any(bump);
+        float psum = 0.0f;
+        uint32_t pb[4];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            float pw[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float pv = (sc[rb][r] == -INFINITY) ? 0.0f : exp2f(sc[rb][r] - m_new);
+                psum += pv;
+                pw[r] = pv * (rr[rb][r] * rs);
+            }
+            pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
+            pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
+        }
+        l_part = l_part * alpha + psum;
+        m_run = m_new;
+        if (any_bump) {
+#pragma unroll
+            for (int mb = 0; mb < 32; mb++) acc_o[mb] = acc_o[mb] * alpha;
+        }
+        const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
+        // ---- PV
+        const int trow = 8 * g + (n >> 1), thalf = 8 * (n & 1);
+        const uint8_t* trbase = tb + trow * RAW_ROW + thalf;
+#pragma unroll
+        for (int mb = 0; mb < 32; mb++) {
+            const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2_t*)(trbase + 16 * (mb ^ trow)));
+            const uint4 aop = e4m3x8_to_f16x8((uint32_t)v[0], (uint32_t)v[1]);
+            acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(aop), bop, acc_o[mb], 0, 0, 0);
+            if ((mb & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        buf ^= 1;
+    }
+    // ---- merge the waves' states in LDS (each wave reuses its own raw buffers)
+    l_part += __shfl_xor(l_part, 16, 64);
+    l_part += __shfl_xor(l_part, 32, 64);
+    float* st = reinterpret_cast<float*>(&raw[wave][0][0]);  // [16][512] O
+    __syncthreads();  // every wave is done with its tiles
+    // float4 slot f of head row hh is stored at slot f ^ hh (spreads the 16 rows over the banks)
+#pragma unroll
+    for (int mb = 0; mb < 32; mb++)
+        *reinterpret_cast<float4*>(st + n * DL + 4 * ((4 * mb + g) ^ n)) =
+            make_float4(acc_o[mb][0], acc_o[mb][1], acc_o[mb][2], acc_o[mb][3]);
+    if (g == 0) {
+        ml_s[wave][0][n] = m_run;
+        ml_s[wave][1][n] = l_part;
+    }
+    __syncthreads();
+    {
+        const int hh = tid >> 4;             // head within the group
+        const int d0 = (tid & 15) * 32;      // 32 dims per thread
+        float mw[MF_WAVES], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MF_WAVES; w++) {
+            mw[w] = ml_s[w][0][hh];
+            M = fmaxf(M, mw[w]);
+        }
+        float sw[MF_WAVES], L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MF_WAVES; w++) {
+            sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
+            L += sw[w] * ml_s[w][1][hh];
+        }
+        const int h = hg * MF_HEADS + hh;
+        if (h < a.n_heads) {
+            float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
+            const float rsinv = 1.0f / rs;  // exact
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                for (int w = 0; w < MF_WAVES; w++) {
+                    const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&raw[w][0][0]) +
+                                                                      hh * DL + 4 * (((d0 >> 2) + q) ^ hh));
+                    o.x += sw[w] * v.x; o.y += sw[w] * v.y; o.z += sw[w] * v.z; o.w += sw[w] * v.w;
+                }
+                o.x *= rsinv; o.y *= rsinv; o.z *= rsinv; o.w *= rsinv;
+                *reinterpret_cast<float4*>(dst + 4 * q) = o;
+            }
+            if ((tid & 15) == 0) {
+                p.part_m[c * a.n_heads + h] = M;  // log2 units
+                p.part_l[c * a.n_heads + h] = L;
+            }
+        }
+    }
+}
+
+// ---- 3. merge --------------------------------------------------------------------------------
+// One workgroup (256 threads) per (sequence, head): two halves of 128 threads
+// take alternate splits, 4 dims per thread; then TQ4 un-rotation by one wave.
 template <bool TQ4, bool LOG2>
 __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= (int64_t)a.n_seqs * a.n_heads) return;
+    __shared__ float red[256];
+    __shared__ __align__(16) float vec[DL];
+    const int tid = threadIdx.x;
+    const int64_t item = blockIdx.x;
     const int s = (int)(item / a.n_heads), h = (int)(item % a.n_heads);
     const int64_t c0 = min(p.chunk_prefix[s], p.max_chunks), c1 = min(p.chunk_prefix[s + 1], p.max_chunks);
     float M = -INFINITY;
-    for (int64_t c = c0 + lane; c < c1; c += 64) M = fmaxf(M, p.part_m[c * a.n_heads + h]);
-    M = wave_max(M);
+    for (int64_t c = c0 + tid; c < c1; c += 256) M = fmaxf(M, p.part_m[c * a.n_heads + h]);
+    red[tid] = M;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+        __syncthreads();
+    }
+    M = red[0];
+    __syncthreads();
     float L = 0.0f;
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) o[i] = 0.0f;
+    for (int64_t c = c0 + tid; c < c1; c += 256) {
+        const float mc = p.part_m[c * a.n_heads + h];
+        const float w = (mc == -INFINITY) ? 0.0f : (LOG2 ? exp2f(mc - M) : expf(mc - M));
+        L += w * p.part_l[c * a.n_heads + h];
+    }
+    red[tid] = L;
+    __syncthreads();
+    for (int o = 128; o >= 1; o >>= 1) {
+        if (tid < o) red[tid] += red[tid + o];
+        __syncthreads();
+    }
+    L = red[0];
+    const int half = tid >> 7, col = (tid & 127) * 4;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (M != -INFINITY) {
-        for (int64_t c = c0; c < c1; c++) {
+        for (int64_t c = c0 + half; c < c1; c += 2) {
             const float mc = p.part_m[c * a.n_heads + h];
             const float w = (mc == -INFINITY) ? 0.0f : (LOG2 ? exp2f(mc - M) : expf(mc - M));
-            L += w * p.part_l[c * a.n_heads + h];
-            const float4* src = reinterpret_cast<const float4*>(p.part_o + (c * a.n_heads + h) * DL + 8 * lane);
-            const float4 u = src[0], v = src[1];
-            o[0] += w * u.x; o[1] += w * u.y; o[2] += w * u.z; o[3] += w * u.w;
-            o[4] += w * v.x; o[5] += w * v.y; o[6] += w * v.z; o[7] += w * v.w;
+            const float4 v = *reinterpret_cast<const float4*>(p.part_o + (c * a.n_heads + h) * DL + col);
+            o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
         }
     }
+    if (half == 1) *reinterpret_cast<float4*>(&vec[col]) = o;
+    __syncthreads();
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if (half == 0) {
+        const float4 u = *reinterpret_cast<const float4*>(&vec[col]);
+        o = make_float4((o.x + u.x) * inv, (o.y + u.y) * inv, (o.z + u.z) * inv, (o.w + u.w) * inv);
+        if (TQ4) *reinterpret_cast<float4*>(&vec[col]) = o;
+        else *reinterpret_cast<float4*>(a.out + item * DL + col) = o;
+    }
+    if (TQ4) {
+        __syncthreads();
+        if (tid < 64) {  // o = D H o~ / sqrt(512), 8 consecutive per lane
+            const int lane = tid;
+            float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) o[i] *= inv;
-    if (TQ4) {  // o = D H o~ / sqrt(512)
+            for (int i = 0; i < 8; i++) v[i] = vec[8 * lane + i];
 #pragma unroll
-        for (int hh = 1; hh < 8; hh <<= 1)
+            for (int hh = 1; hh < 8; hh <<= 1)
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                if (!(i & hh)) {
-                    const float x = o[i], y = o[i + hh];
-                    o[i] = x + y;
-                    o[i + hh] = x - y;
-                }
+                for (int i = 0; i < 8; i++)
+                    if (!(i & hh)) {
+                        const float x = v[i], y = v[i + hh];
+                        v[i] = x + y;
+                        v[i + hh] = x - y;
+                    }
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1)
+            for (int m = 1; m < 64; m <<= 1)
 #pragma unroll
-            for (int i = 0; i < 8; i++) o[i] = fwht_xlane(o[i], lane, m);
-        const uint32_t sm = a.sign_mask[lane];
+                for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, m);
+            const uint32_t sm = a.sign_mask[lane];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            o[i] *= INV_SQRT_DL;
-            if ((sm >> i) & 1u) o[i] = -o[i];
+            for (int i = 0; i < 8; i++) {
+                v[i] *= INV_SQRT_DL;
+                if ((sm >> i) & 1u) v[i] = -v[i];
+            }
+            float4* dst = reinterpret_cast<float4*>(a.out + item * DL + 8 * lane);
+            dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+            dst[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
     }
-    float4* dst = reinterpret_cast<float4*>(a.out + item * DL + 8 * lane);
-    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-    if (a.lse && lane == 0) {
+    if (a.lse && tid == 0) {
         float v;
         if (!(L > 0.0f)) v = -INFINITY;
         else v = LOG2 ? (M + log2f(L)) * LN2 : M + logf(L);
@@ -677,46 +1116,48 @@ __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
 int64_t attn_workspace_bytes(const kvq_attn_args& a) { return plan_bytes(a); }
 
 hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws, hipStream_t st) {
-    Plan p = make_plan(a, ws);
-    const float* qsrc = a.qmode == KVQ_QMODE_TQ4 ? p.q_rot : a.q_lat;
+    Plan p = make_plan(a, ws, nullptr);
+    const bool f32 = a.precision == KVQ_PREC_FP32;
+    const bool tq4 = a.qmode == KVQ_QMODE_TQ4;
     switch (stage) {
         case KVQ_STAGE_PLAN:
             hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a.seq_offsets, a.n_seqs, p.split_rows, a.total_rows,
                                p.chunk_prefix);
             break;
-        case KVQ_STAGE_QROT:
-            if (a.qmode == KVQ_QMODE_TQ4) {
-                const int64_t rows = (int64_t)a.n_seqs * a.n_heads;
-                hipLaunchKernelGGL(k_qrot, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.q_lat, a.sign_mask,
-                                   rows, p.q_rot);
-            }
-            break;
-        case KVQ_STAGE_SPLITS: {
-            const dim3 grid((unsigned)p.max_chunks, (unsigned)p.n_groups);
-            if (a.precision == KVQ_PREC_FP32) {
-                if (a.qmode == KVQ_QMODE_FP8)
-                    hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p, qsrc);
-                else
-                    hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_TQ4>, grid, dim3(256), 0, st, a, p, qsrc);
+        case KVQ_STAGE_QPREP:
+            if (f32) {
+                if (tq4) {
+                    const int64_t rows = (int64_t)a.n_seqs * a.n_heads;
+                    hipLaunchKernelGGL(k_qrot, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.q_lat,
+                                       a.sign_mask, rows, p.q_rot);
+                }
             } else {
-                const dim3 block(p.heads_per_group / MF_WAVE_HEADS * 64);
-                if (a.qmode == KVQ_QMODE_FP8)
-                    hipLaunchKernelGGL(k_attn_mfma<KVQ_QMODE_FP8>, grid, block, 0, st, a, p, qsrc);
-                else
-                    hipLaunchKernelGGL(k_attn_mfma<KVQ_QMODE_TQ4>, grid, block, 0, st, a, p, qsrc);
+                const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
+                const dim3 grid((unsigned)((rows + 3) / 4));
+                if (tq4) hipLaunchKernelGGL(k_qprep<KVQ_QMODE_TQ4>, grid, dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL(k_qprep<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p);
             }
             break;
-        }
+        case KVQ_STAGE_SPLITS:
+            if (f32) {
+                const dim3 grid((unsigned)p.max_chunks, (unsigned)p.n_groups);
+                const float* qsrc = tq4 ? p.q_rot : a.q_lat;
+                if (tq4) hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_TQ4>, grid, dim3(256), 0, st, a, p, qsrc);
+                else hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p, qsrc);
+            } else {
+                const dim3 grid((unsigned)(p.chunks_per_xcd * N_XCD * p.n_groups));
+                if (tq4) hipLaunchKernelGGL(k_attn_mfma<KVQ_QMODE_TQ4>, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+                else hipLaunchKernelGGL(k_attn_mfma_fp8, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+            }
+            break;
         default: {
-            const int64_t items = (int64_t)a.n_seqs * a.n_heads;
-            const dim3 mgrid((unsigned)((items + 3) / 4));
-            const bool log2dom = a.precision != KVQ_PREC_FP32;
-            if (a.qmode == KVQ_QMODE_TQ4) {
-                if (log2dom) hipLaunchKernelGGL((k_merge<true, true>), mgrid, dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<true, false>), mgrid, dim3(256), 0, st, a, p);
+            const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads));
+            if (tq4) {
+                if (!f32) hipLaunchKernelGGL((k_merge<true, true>), grid, dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<true, false>), grid, dim3(256), 0, st, a, p);
             } else {
-                if (log2dom) hipLaunchKernelGGL((k_merge<false, true>), mgrid, dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<false, false>), mgrid, dim3(256), 0, st, a, p);
+                if (!f32) hipLaunchKernelGGL((k_merge<false, true>), grid, dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<false, false>), grid, dim3(256), 0, st, a, p);
             }
             break;
         }

@@ -3,12 +3,18 @@
 A step is one decode step of the KV8 absorbed-MLA workload (1 sequence,
 T = 32768 cached rows, 128 heads, 512-dim fp8 latent + 64-dim bf16 rope key):
   1. fp8-encode the step's new latent row into the cache (row T-1),
-  2. decode attention over all T rows: split plan, the split kernel (the
-     dominant kernel, bracketed by HIP events on the launch stream), merge.
-The step cycles through --kv-copies independent caches (16 x 21 MB > the
-256 MB last-level cache) so every step reads its KV from HBM, as consecutive
-layers of a model do.  Inputs are seeded synthetic data, resident in HBM
-before the timed region.
+  2. decode attention over all T rows: split plan + query preparation, the
+     split kernel (the dominant kernel), the merge.
+Each step is captured once as a HIP graph and replayed, as a serving loop
+does, so the step time is GPU time rather than Python launch overhead.  The
+steps cycle through --kv-copies independent caches (16 x 21 MB > the 256 MB
+last-level cache) so every step reads its KV from HBM, as consecutive layers
+of a model do.  Inputs are seeded synthetic data, resident in HBM before the
+timed region.
+
+The split kernel's average duration is timed with HIP events on the launch
+stream around graphs of back-to-back split launches (one per cache copy), so
+no host gap falls inside the bracket.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -75,7 +81,7 @@ def main():
 
     # ---- device-resident inputs
     x = torch.from_numpy(w.latent).to(dev)
-    new_rows = torch.from_numpy(workloads.fp8_rows_for_encode(args.steps + args.warmup + 1, seed=77)).to(dev)
+    new_rows = torch.from_numpy(workloads.fp8_rows_for_encode(args.kv_copies, seed=77)).to(dev)
     kr0 = torch.from_numpy(w.k_rope.view(np.int16)).to(dev)
     offs = torch.from_numpy(w.offsets).to(dev)
     ql = torch.from_numpy(w.q_lat).to(dev)
@@ -99,45 +105,80 @@ def main():
     ws = kvq.alloc_workspace(argsets[0])
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
-        c, s, _ = copies[i % len(copies)]
-        a = argsets[i % len(copies)]
-        row = new_rows[i % new_rows.shape[0]: i % new_rows.shape[0] + 1]
-        if qmode == 1:
-            kvq.kvq_encode_fp8(row, c[T - 1:T], s[T - 1:T])
+    def step(c, stage=None):
+        codes_c, scales_c, _ = copies[c]
+        a = argsets[c]
+        if stage is None:
+            row = new_rows[c:c + 1]
+            if qmode == 1:
+                kvq.kvq_encode_fp8(row, codes_c[T - 1:T], scales_c[T - 1:T])
+            else:
+                kvq.kvq_encode_tq4(row, mask, codes_c[T - 1:T], scales_c[T - 1:T])
+            for st in (kvq.KVQ_STAGE_PLAN, kvq.KVQ_STAGE_QPREP, kvq.KVQ_STAGE_SPLITS, kvq.KVQ_STAGE_MERGE):
+                kvq.kvq_decode_attn_stage(a, st, ws)
         else:
-            kvq.kvq_encode_tq4(row, mask, c[T - 1:T], s[T - 1:T])
-        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_PLAN, ws)
-        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_QPREP, ws)
-        if ev is not None:
-            ev[0].record()
-        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_SPLITS, ws)
-        if ev is not None:
-            ev[1].record()
-        kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_MERGE, ws)
+            kvq.kvq_decode_attn_stage(a, stage, ws)
+
+    n_copies = len(copies)
+    # eager reference of one step per copy, then capture
+    for c in range(n_copies):
+        step(c)
+    torch.cuda.synchronize()
+    eager_out = [None] * n_copies
+    for c in range(n_copies):
+        step(c)
+        torch.cuda.synchronize()
+        eager_out[c] = out.clone()
+    side = torch.cuda.Stream()
+    step_graphs = []
+    for c in range(n_copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(c)
+        step_graphs.append(g)
+    split_graph = torch.cuda.CUDAGraph()  # one split launch per copy, back to back
+    with torch.cuda.graph(split_graph, stream=side):
+        for c in range(n_copies):
+            step(c, kvq.KVQ_STAGE_SPLITS)
+    torch.cuda.synchronize()
+    for rep in range(2):  # replays reproduce the eager results exactly
+        for c in (0, n_copies - 1):
+            out.zero_()
+            step_graphs[c].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager_out[c]), f"graph replay {rep} of copy {c} differs from the eager step"
 
     log(f"warmup {args.warmup}")
     for i in range(args.warmup):
-        step(i)
+        step_graphs[i % n_copies].replay()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step_graphs[(args.warmup + i) % n_copies].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+
+    # split kernel: HIP events around back-to-back launches on the replay stream
+    reps = max(1, args.steps // n_copies)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    split_graph.replay()
+    e0.record(stream)
+    for _ in range(reps):
+        split_graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = e0.elapsed_time(e1) / (reps * n_copies)
     rows_per_s = T / (ms_per_step / 1000.0)
     flops = decode_flops(T, H)
     nbytes = decode_bytes(T, qmode)
     tflops = flops / (kern_ms / 1000.0) / 1e12
     gbps = nbytes / (kern_ms / 1000.0) / 1e9
-    log(f"step {ms_per_step * 1000:.1f} us, split kernel {kern_ms * 1000:.1f} us, {tflops:.1f} TFLOP/s, "
-        f"{gbps:.0f} GB/s")
+    log(f"step {ms_per_step * 1000:.1f} us, split kernel {kern_ms * 1000:.1f} us ({reps * n_copies} launches), "
+        f"{tflops:.1f} TFLOP/s, {gbps:.0f} GB/s")
 
     # ---- CPU baseline: the oracle on the same decode step
     cpu = None

@@ -84,7 +84,12 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     p.heads_per_group = f32 ? F32_HEADS : MF_HEADS;
     p.n_groups = (a.n_heads + p.heads_per_group - 1) / p.heads_per_group;
     p.heads_padded = p.n_groups * p.heads_per_group;
-    p.max_chunks = (int64_t)a.n_seqs + a.total_rows / p.split_rows + 1;
+    // sum_s max(1, ceil(T_s / split)) over T_s summing to at most total_rows is at
+    // most floor(total / split) + n_seqs, and at most ceil(total / split) + n_seqs - 1
+    // unless every sequence is empty
+    p.max_chunks = std::max<int64_t>(a.n_seqs, std::min<int64_t>(a.total_rows / p.split_rows + a.n_seqs,
+                                                                  (a.total_rows + p.split_rows - 1) / p.split_rows +
+                                                                      a.n_seqs - 1));
     p.chunks_per_xcd = (p.max_chunks + N_XCD - 1) / N_XCD;
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
     int64_t off = 0;
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(kvq_attn_args a, Plan p, const
     __shared__ float red_s[F32_HEADS][2];
     const int tid = threadIdx.x;
     const int64_t c = blockIdx.x;
-    if (c >= p.chunk_prefix[a.n_seqs]) return;
+    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
     const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
     const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
     const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
@@ -520,7 +525,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma(kvq_attn_args a, Pl
     const int64_t local = blockIdx.x / N_XCD;
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
-    if (c >= p.chunk_prefix[a.n_seqs]) return;
+    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
     const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
     const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
     const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
@@ -735,36 +740,80 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma(kvq_attn_args a, Pl
 // fp8 split kernel (raw-tile variant).  Same work items and wave split as
 // k_attn_mfma, but every wave streams its rows' raw e4m3 codes into a
 // double-buffered LDS tile with global_load_lds (no register staging, the next
-// tile's load overlaps this tile's math).  Tile row r keeps its 16-byte chunk c
-// at position c ^ r, so both read patterns below spread over all banks:
+// tile's load overlaps this tile's math).
+//
+// Tile layout, chunk-major: 16-byte chunk c of tile row r sits at
+//   1024 (c / 2) + 512 (c % 2) + 16 sigma(r),
+// sigma(r) = r ^ (bit3(r) << 2) ^ (bit4(r) << 3) (a bijection of 0..31).  One
+// DMA instruction fills one 1 KB block -- chunks 2 i, 2 i + 1 of all 32 rows,
+// lane l loading row sigma^-1(l % 32) -- so each lane's source offset is the same
+// for all 16 instructions, and every LDS read below is a per-lane base plus a
+// compile-time offset:
 //   score: lane (g, n) of row block rb reads tile row 8 (n / 4) + 4 rb + n % 4,
-//          chunks 4 j + g (16 codes -> two fp16 k-steps);  the accumulator row
+//          chunks 4 j + g (16 codes -> two fp16 k-steps) at
+//          512 g + 16 sigma(row) + 2048 j; sigma spreads the 8 or 16 rows a
+//          read serves at once over distinct bank groups.  The accumulator row
 //          order then matches the transposed read;
 //   PV:    ds_read_b64_tr_b8: source lane (g, q) points at row 8 g + q / 2,
-//          byte column 16 mb + 8 (q % 2); lane (g, p) receives the 8 codes of
-//          rows 8 g .. 8 g + 7 in column 16 mb + p, converted to fp16 in
-//          registers -- k-slots (g, j) = row 8 g + j, as the probabilities.
+//          byte 8 (q % 2) of chunk mb (512 contiguous bytes per read); lane
+//          (g, p) receives the 8 codes of rows 8 g .. 8 g + 7 in column
+//          16 mb + p, converted to fp16 in registers -- k-slots (g, j) = row
+//          8 g + j, as the probabilities.
+// The rope keys (8 chunks per row) use the same layout in 4 blocks.
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 constexpr int RAW_ROW = DL;                   // bytes per raw fp8 tile row
 constexpr int RAW_TILE = MF_TILE * RAW_ROW;   // 16 KB
 
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// LDS DMA (global_load_lds: each lane's bytes land at the wave-uniform LDS
+// base in M0 + lane * size) issued from inline assembly.  The compiler does not
+// see these LDS writes, so it adds no wait of its own before the LDS reads that
+// follow -- with the builtin it waits for every outstanding DMA, the next
+// tile's included, before the first read of the current tile.  The kernel
+// waits explicitly (vmcnt) before it reads what a DMA wrote, and finishes its
+// reads of a buffer (lgkmcnt) before a DMA refills it.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Scalar base + per-lane 32-bit offset form.  The global address is
+// sbase + voff; the LDS address is M0 + 16 (or 4) * lane.  The compiler's
+// hazard recognizer does not look inside the assembly, so each block starts
+// with 5 wait states: a VALU write of an SGPR (v_readlane / v_readfirstlane,
+// e.g. an SGPR reloaded from a spill lane) needs 5 before a VMEM instruction
+// reads that SGPR as its base, and an SALU write of M0 needs 1 before LDS DMA.
+// With fewer, the load can use a stale base register and fault.
+__device__ __forceinline__ void dma_lds_b128(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+                 : "memory");
+}
+__device__ __forceinline__ void dma_lds_b32(const void* sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+                 : "memory");
+}
+__device__ __forceinline__ int tile_sigma(int r) { return r ^ (((r >> 3) & 1) << 2) ^ (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int tile_sigma_inv(int q) {
+    return q ^ (((q >> 4) & 1) << 3) ^ ((((q >> 3) ^ (q >> 4)) & 1) << 2);
+}
+
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
     __shared__ __align__(16) uint8_t rope_s[MF_WAVES][MF_TILE * DR * 2];  // rope keys (bf16)
     __shared__ __align__(16) float rho_s[MF_WAVES][2][64];             // row scales
-    __shared__ float red_s[MF_WAVES];
-    __shared__ float ml_s[MF_WAVES][2][MF_HEADS];
+    __shared__ float ml_s[MF_WAVES][3][MF_HEADS];
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, n = lane & 15;
     // workgroups are dealt round-robin to the XCDs: chunk c goes to XCD c % 8 and
     // its head groups are consecutive there, so they share that XCD's L2
     const int64_t local = blockIdx.x / N_XCD;
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
-    if (c >= p.chunk_prefix[a.n_seqs]) return;
+    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
     const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
     const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
     const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
@@ -773,53 +822,35 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
     const int head = hg * MF_HEADS + n;
 
-    // DMA loaders (global -> LDS, no registers); rows past the end re-read row t0,
-    // which holds valid codes and is masked later.
-    auto load_codes = [&](int64_t t0, int buf) {  // 16 x 1 KB: rows 2 i, 2 i + 1
+    // DMA loaders (global -> LDS, no registers).  Lane l fills slot l % 32 of
+    // half l / 32 of each chunk pair, so it loads tile row sigma^-1(l % 32);
+    // rows past the end of the wave's range re-read row t0, which holds valid
+    // data and is masked later.
+    const int dma_row = tile_sigma_inv(lane & 31), dma_half = lane >> 5;
+    const uint32_t lds_codes = lds_offset(&raw[wave][0][0]);
+    const uint32_t lds_rope = lds_offset(&rope_s[wave][0]);
+    const uint32_t lds_rho = lds_offset(&rho_s[wave][0][0]);
+    auto load_tile = [&](int64_t t0, int buf) {
         const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        const int rsub = lane >> 5, pos = lane & 31;
+        const uint32_t rowc = dma_row < nt ? (uint32_t)dma_row : 0u;
+        const uint32_t voff_c = rowc * RAW_ROW + 16u * dma_half;
+        const uint32_t voff_r = rowc * (DR * 2) + 16u * dma_half;
+        const uint32_t voff_s = (uint32_t)((lane & 31) < nt ? (lane & 31) : 0) * 4u;
+        const uint8_t* cb = a.codes + t0 * RAW_ROW;
+        const uint8_t* rb = reinterpret_cast<const uint8_t*>(a.k_rope + t0 * DR);
+        const uint32_t lc = __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE);
+        const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_rho + 256u * buf);
 #pragma unroll
-        for (int i = 0; i < MF_TILE / 2; i++) {
-            const int r = 2 * i + rsub;
-            const uint8_t* src = a.codes + (t0 + (r < nt ? r : 0)) * RAW_ROW + 16 * (pos ^ r);
-            __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (__attribute__((address_space(3))) void*)&raw[wave][buf][i * 1024],
-                                             16, 0, 0);
-        }
-    };
-    auto load_rope = [&](int64_t t0) {  // 4 x 1 KB: rows 8 i .. 8 i + 7, row-major
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+        for (int i = 0; i < MF_TILE / 2; i++) dma_lds_b128(cb + 32 * i, voff_c, lc + 1024u * i);
 #pragma unroll
-        for (int i = 0; i < MF_TILE / 8; i++) {
-            const int r = 8 * i + (lane >> 3);
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k_rope + (t0 + (r < nt ? r : 0)) * DR) + 16 * (lane & 7);
-            __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (__attribute__((address_space(3))) void*)&rope_s[wave][i * 1024],
-                                             16, 0, 0);
-        }
-    };
-    auto load_rho = [&](int64_t t0, int buf) {  // 64 x 4 bytes: row scales of rows 0 .. 31 (and copies)
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        const int r = lane & 31;
-        __builtin_amdgcn_global_load_lds((const void*)(a.row_scale + t0 + (r < nt ? r : 0)),
-                                         (__attribute__((address_space(3))) void*)&rho_s[wave][buf][0], 4, 0, 0);
+        for (int i = 0; i < DR * 2 / 32; i++) dma_lds_b128(rb + 32 * i, voff_r, lds_rope + 1024u * i);
+        dma_lds_b32(a.row_scale + t0, voff_s, ls);
     };
     auto tile_row = [](int rb, int nn) { return 8 * (nn >> 2) + 4 * rb + (nn & 3); };
-
-    if (w0 < w1) {
-        load_codes(w0, 0);
-        load_rope(w0);
-        load_rho(w0, 0);
-    }
-
-    // ---- per-split probability scale rs from the largest row scale of the chunk
-    float rmax = 0.0f;
-    for (int64_t t = r0 + tid; t < r1; t += MF_WAVES * 64) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
-    rmax = wave_max(rmax);
-    if (lane == 0) red_s[wave] = rmax;
-    __syncthreads();
-    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-    const float rs = pow2_scale_for(rmax, -1);  // max rho * rs in [0.5, 1)
+    // per-lane LDS read offsets (bytes within a tile)
+    const uint32_t rd_a = 512u * g + 16u * tile_sigma(tile_row(0, n));  // row block 0 (score, rope)
+    const uint32_t rd_b = 512u * g + 16u * tile_sigma(tile_row(1, n));  // row block 1
+    const uint32_t rd_t = 16u * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
 
     // ---- query operands
     const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
@@ -834,12 +865,25 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
     const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
 
+    // Softmax with a fixed reference per wave and head: p = 2^(s - m_run), with
+    // m_run the first tile's maximum, and probabilities enter the matrix cores
+    // as fp16 p * rho * rsc with rsc a power of two (rho * rsc in [0.5, 1) for
+    // the first tile's largest row scale).  A later tile may exceed them by 2^8
+    // (scores) and 2^4 (row scales), so p * rho * rsc <= 2^12.  A tile beyond
+    // that raises the references and the wave starts its rows again: the
+    // accumulators are never rescaled inside the loop (they stay in the matrix
+    // cores' registers), and for all but adversarial score sequences the first
+    // pass is the only one.
     f32x4_t acc_o[32];
+    float m_run = -INFINITY, l_part = 0.0f;
+    float rsc = 0.0f;  // 0 until a row with a nonzero scale
+    for (;;) {
 #pragma unroll
     for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_part = 0.0f;
+    l_part = 0.0f;
     int buf = 0;
-
+    bool again = false;
+    if (w0 < w1) load_tile(w0, 0);
     for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
         const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
         vm_wait_all();  // this tile's codes, rope keys and scales are in LDS
@@ -850,32 +894,25 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
             for (int k = 0; k < 2; k++)
-                kr[rb][k] = *reinterpret_cast<const uint4*>(&rope_s[wave][tile_row(rb, n) * DR * 2 + 16 * g + 64 * k]);
+                kr[rb][k] = *reinterpret_cast<const uint4*>(&rope_s[wave][(rb ? rd_b : rd_a) + 2048 * k]);
         const float4 rho0 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g]);
         const float4 rho1 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g + 4]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): those reads are done before the buffers refill
-        if (more) {
-            load_codes(t0 + MF_TILE, buf ^ 1);
-            load_rope(t0 + MF_TILE);
-            load_rho(t0 + MF_TILE, buf ^ 1);
-        }
+        if (more) load_tile(t0 + MF_TILE, buf ^ 1);
         const uint8_t* tb = raw[wave][buf];
         // ---- scores: both row blocks together, the reads one k-chunk ahead
-        const int ra = tile_row(0, n), rbr = tile_row(1, n);
-        const uint8_t* pa = tb + ra * RAW_ROW;
-        const uint8_t* pbp = tb + rbr * RAW_ROW;
-        auto chunk = [&](const uint8_t* base, int r, int j) {
-            return *reinterpret_cast<const uint4*>(base + 16 * ((4 * j + g) ^ r));
-        };
+        const uint8_t* pa = tb + rd_a;
+        const uint8_t* pbp = tb + rd_b;
+        auto chunk = [&](const uint8_t* base, int j) { return *reinterpret_cast<const uint4*>(base + 2048 * j); };
         f32x4_t sl[2], sr[2];
         sl[0] = sl[1] = sr[0] = sr[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        uint4 na = chunk(pa, ra, 0), nb = chunk(pbp, rbr, 0);
+        uint4 na = chunk(pa, 0), nb = chunk(pbp, 0);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const uint4 ca = na, cbv = nb;
             if (j < 7) {
-                na = chunk(pa, ra, j + 1);
-                nb = chunk(pbp, rbr, j + 1);
+                na = chunk(pa, j + 1);
+                nb = chunk(pbp, j + 1);
             }
             __builtin_amdgcn_sched_barrier(0);  // the look-ahead reads issue before this chunk's math
             const uint4 a0 = e4m3x8_to_f16x8(ca.x, ca.y), a1 = e4m3x8_to_f16x8(ca.z, ca.w);
@@ -911,12 +948,23 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // lazy rescaling: keep a stale running max unless this tile exceeds it by
-        // more than 2^8 (then p <= 256 stays exact enough in fp32 / fp16)
-        const bool bump = tmax > m_run + LAZY_LOG2;
-        const float m_new = bump ? tmax : m_run;
-        const float alpha = bump ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new)) : 1.0f;
-        const bool any_bump = __any(bump);
+        float rmx = 0.0f;  // largest |rho| of the tile, over the whole wave
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) rmx = fmaxf(rmx, fabsf(rr[rb][r]));
+        rmx = fmaxf(rmx, __shfl_xor(rmx, 16, 64));
+        rmx = fmaxf(rmx, __shfl_xor(rmx, 32, 64));
+        if (m_run == -INFINITY) m_run = tmax;                         // first tile: every row valid
+        if (rsc == 0.0f && rmx > 0.0f) rsc = pow2_scale_for(rmx, -1);  // wave-uniform
+        const bool over = tmax > m_run + LAZY_LOG2;
+        if (__any(over) || rmx * rsc > 16.0f) {
+            // raise the references past this tile and start the rows again
+            m_run = fmaxf(m_run, tmax);
+            if (rmx * rsc > 16.0f) rsc = pow2_scale_for(rmx, -1);
+            again = true;
+            break;
+        }
         float psum = 0.0f;
         uint32_t pb[4];
 #pragma unroll
@@ -924,26 +972,19 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             float pw[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float pv = (sc[rb][r] == -INFINITY) ? 0.0f : exp2f(sc[rb][r] - m_new);
+                const float pv = (sc[rb][r] == -INFINITY) ? 0.0f : exp2f(sc[rb][r] - m_run);
                 psum += pv;
-                pw[r] = pv * (rr[rb][r] * rs);
+                pw[r] = pv * (rr[rb][r] * rsc);
             }
             pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
             pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
         }
-        l_part = l_part * alpha + psum;
-        m_run = m_new;
-        if (any_bump) {
-#pragma unroll
-            for (int mb = 0; mb < 32; mb++) acc_o[mb] = acc_o[mb] * alpha;
-        }
+        l_part += psum;
         const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
         // ---- PV: groups of 8 column blocks, the next group's reads in flight
-        const int trow = 8 * g + (n >> 1), thalf = 8 * (n & 1);
-        const uint8_t* trbase = tb + trow * RAW_ROW + thalf;
+        const uint8_t* trbase = tb + rd_t;
         auto trd = [&](int mb) {
-            return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2_t*)(trbase + 16 * (mb ^ trow)));
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(trbase + 512 * mb));
         };
         i32x2_t nv[8];
 #pragma unroll
@@ -968,6 +1009,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
         buf ^= 1;
     }
+    if (!again) break;
+    vm_wait_all();  // the next tile's DMA may still be landing: drain it before the rows restart
+    }
     // ---- merge the waves' states in LDS (each wave reuses its own raw buffers)
     l_part += __shfl_xor(l_part, 16, 64);
     l_part += __shfl_xor(l_part, 32, 64);
@@ -981,6 +1025,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     if (g == 0) {
         ml_s[wave][0][n] = m_run;
         ml_s[wave][1][n] = l_part;
+        ml_s[wave][2][n] = rsc;
     }
     __syncthreads();
     {
@@ -992,16 +1037,17 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             mw[w] = ml_s[w][0][hh];
             M = fmaxf(M, mw[w]);
         }
-        float sw[MF_WAVES], L = 0.0f;
+        float sw[MF_WAVES], so[MF_WAVES], L = 0.0f;
 #pragma unroll
         for (int w = 0; w < MF_WAVES; w++) {
             sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
             L += sw[w] * ml_s[w][1][hh];
+            const float rw = ml_s[w][2][hh];
+            so[w] = rw > 0.0f ? sw[w] / rw : 0.0f;  // 1 / rsc is exact
         }
         const int h = hg * MF_HEADS + hh;
         if (h < a.n_heads) {
             float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
-            const float rsinv = 1.0f / rs;  // exact
 #pragma unroll
             for (int q = 0; q < 8; q++) {
                 float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -1009,9 +1055,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 for (int w = 0; w < MF_WAVES; w++) {
                     const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&raw[w][0][0]) +
                                                                       hh * DL + 4 * (((d0 >> 2) + q) ^ hh));
-                    o.x += sw[w] * v.x; o.y += sw[w] * v.y; o.z += sw[w] * v.z; o.w += sw[w] * v.w;
+                    o.x += so[w] * v.x; o.y += so[w] * v.y; o.z += so[w] * v.z; o.w += so[w] * v.w;
                 }
-                o.x *= rsinv; o.y *= rsinv; o.z *= rsinv; o.w *= rsinv;
                 *reinterpret_cast<float4*>(dst + 4 * q) = o;
             }
             if ((tid & 15) == 0) {

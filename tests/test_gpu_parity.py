@@ -180,7 +180,7 @@ _REF = {}
 
 def _oracle_ref(w, c, s, ql, qr, key):
     """fp64 oracle on the GPU-produced codes, cached per (workload, query) key."""
-    k = (w.name, key)
+    k = (w.name, w.qmode, w.total_rows, w.n_heads, key)
     if k not in _REF:
         _REF.clear()
         _REF[k] = oracle.decode_attn(w.qmode, w.offsets, _np(c), _np(s), w.k_rope, ql, qr, w.sm_scale,
@@ -235,6 +235,27 @@ def test_attn_peaked_softmax(qmode):
     for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         _check_attn(w, c, s, prec, q_lat=ql, q_rope=qr, label="peaked")
         _check_attn(w, c, s, prec, split_rows=96, q_lat=ql, q_rope=qr, label="peaked-split96")
+
+
+@pytest.mark.parametrize("qmode", [1, 2])
+def test_attn_rising_scores_and_scales(qmode):
+    """Scores that climb along the rows (a sawtooth of period 512 in one rope
+    dimension) and row gains that double every 256 rows: the split kernels'
+    first-tile softmax and row-scale references are exceeded again and again."""
+    _say(f"attn rising scores/scales qmode={qmode}")
+    w = workloads.DecodeWorkload(f"rising-q{qmode}", 4242, [4096], 16, qmode=qmode, sign_seed=4243)
+    t = np.arange(w.total_rows, dtype=np.float64)
+    w.latent = (w.latent * (2.0 ** (t / 256.0))[:, None]).astype(np.float32)
+    rope = np.random.default_rng(4244).standard_normal((w.total_rows, 64)).astype(np.float32)
+    rope[:, 0] = ((t % 512) * 0.02).astype(np.float32)
+    w.k_rope = workloads.to_bf16_bits(rope)
+    ql = (w.q_lat * 1e-2).astype(np.float32)
+    qr = w.q_rope.copy()
+    qr[..., 0] = 400.0
+    c, s = _encode_cache(w)
+    for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
+        for sr in (0, 4096, 96):
+            _check_attn(w, c, s, prec, sr, q_lat=ql, q_rope=qr, label="rising")
 
 
 def test_attn_ragged_edges():

@@ -742,27 +742,31 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma(kvq_attn_args a, Pl
 // double-buffered LDS tile with global_load_lds (no register staging, the next
 // tile's load overlaps this tile's math).
 //
-// Tile layout, chunk-major: 16-byte chunk c of tile row r sits at
-//   1024 (c / 2) + 512 (c % 2) + 16 sigma(r),
-// sigma(r) = r ^ (bit3(r) << 2) ^ (bit4(r) << 3) (a bijection of 0..31).  One
-// DMA instruction fills one 1 KB block -- chunks 2 i, 2 i + 1 of all 32 rows,
-// lane l loading row sigma^-1(l % 32) -- so each lane's source offset is the same
-// for all 16 instructions, and every LDS read below is a per-lane base plus a
-// compile-time offset:
+// Tile layout, row-major with one 16-byte pad per row: chunk c (16 codes) of
+// tile row r sits in 16-byte slot 33 sigma(r) + c, where
+// sigma(r) = r ^ (bit3(r) << 2) ^ (bit4(r) << 3) is a bijection of 0..31.
+// The DMA fills 64 consecutive slots per instruction (17 per tile, rows stay
+// contiguous in global memory); each lane's source offset for instruction i
+// is computed once per wave.  Every LDS read below is then a per-lane base
+// plus a compile-time offset, and the 33-slot stride with sigma puts the rows
+// one read serves on distinct bank groups:
 //   score: lane (g, n) of row block rb reads tile row 8 (n / 4) + 4 rb + n % 4,
 //          chunks 4 j + g (16 codes -> two fp16 k-steps) at
-//          512 g + 16 sigma(row) + 2048 j; sigma spreads the 8 or 16 rows a
-//          read serves at once over distinct bank groups.  The accumulator row
-//          order then matches the transposed read;
+//          16 (33 sigma(row) + g) + 64 j; the accumulator row order then
+//          matches the transposed read;
 //   PV:    ds_read_b64_tr_b8: source lane (g, q) points at row 8 g + q / 2,
-//          byte 8 (q % 2) of chunk mb (512 contiguous bytes per read); lane
-//          (g, p) receives the 8 codes of rows 8 g .. 8 g + 7 in column
-//          16 mb + p, converted to fp16 in registers -- k-slots (g, j) = row
-//          8 g + j, as the probabilities.
-// The rope keys (8 chunks per row) use the same layout in 4 blocks.
+//          byte 8 (q % 2) of chunk mb; lane (g, p) receives the 8 codes of
+//          rows 8 g .. 8 g + 7 in column 16 mb + p, converted to fp16 in
+//          registers -- k-slots (g, j) = row 8 g + j, as the probabilities.
+// The rope keys (8 chunks per row) use 9-slot rows: slot 9 sigma(r) + c.
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
-constexpr int RAW_ROW = DL;                   // bytes per raw fp8 tile row
-constexpr int RAW_TILE = MF_TILE * RAW_ROW;   // 16 KB
+constexpr int RAW_ROW = DL;                   // bytes per raw fp8 code row
+constexpr int RAW_SLOTS = 33;                 // 16-byte slots per padded tile row
+constexpr int RAW_DMA = 17;                   // DMA instructions per code tile (1056 slots, 64 per instruction)
+constexpr int RAW_TILE = RAW_DMA * 64 * 16;   // 17408 bytes
+constexpr int ROPE_SLOTS = 9;
+constexpr int ROPE_DMA = 5;                   // 288 slots
+constexpr int ROPE_TILE = ROPE_DMA * 64 * 16; // 5120 bytes
 
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -802,7 +806,7 @@ __device__ __forceinline__ int tile_sigma_inv(int q) {
 
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
-    __shared__ __align__(16) uint8_t rope_s[MF_WAVES][MF_TILE * DR * 2];  // rope keys (bf16)
+    __shared__ __align__(16) uint8_t rope_s[MF_WAVES][ROPE_TILE];      // rope keys (bf16)
     __shared__ __align__(16) float rho_s[MF_WAVES][2][64];             // row scales
     __shared__ float ml_s[MF_WAVES][3][MF_HEADS];
     const int tid = threadIdx.x;
@@ -822,35 +826,59 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
     const int head = hg * MF_HEADS + n;
 
-    // DMA loaders (global -> LDS, no registers).  Lane l fills slot l % 32 of
-    // half l / 32 of each chunk pair, so it loads tile row sigma^-1(l % 32);
-    // rows past the end of the wave's range re-read row t0, which holds valid
-    // data and is masked later.
-    const int dma_row = tile_sigma_inv(lane & 31), dma_half = lane >> 5;
+    // DMA loaders (global -> LDS, no registers).  Lane l of instruction i fills
+    // slot 64 i + l: row sigma^-1(slot / 33), chunk slot % 33 (the pad slot and
+    // the slots past the tile re-read chunk 0 of that row, or of row 0).  The
+    // offsets are fixed per lane; in a tile shorter than 32 rows the rows past
+    // its end re-read row 0, which is masked later.
+    uint32_t voff_c[RAW_DMA], voff_r[ROPE_DMA];
+#pragma unroll
+    for (int i = 0; i < RAW_DMA; i++) {
+        const int q = 64 * i + lane;
+        const int k = q / RAW_SLOTS, ch = q % RAW_SLOTS;
+        const int r = k < MF_TILE ? tile_sigma_inv(k) : 0;
+        voff_c[i] = (uint32_t)(r * RAW_ROW + 16 * (ch < 32 && k < MF_TILE ? ch : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < ROPE_DMA; i++) {
+        const int q = 64 * i + lane;
+        const int k = q / ROPE_SLOTS, ch = q % ROPE_SLOTS;
+        const int r = k < MF_TILE ? tile_sigma_inv(k) : 0;
+        voff_r[i] = (uint32_t)(r * DR * 2 + 16 * (ch < 8 && k < MF_TILE ? ch : 0));
+    }
     const uint32_t lds_codes = lds_offset(&raw[wave][0][0]);
     const uint32_t lds_rope = lds_offset(&rope_s[wave][0]);
     const uint32_t lds_rho = lds_offset(&rho_s[wave][0][0]);
     auto load_tile = [&](int64_t t0, int buf) {
         const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        const uint32_t rowc = dma_row < nt ? (uint32_t)dma_row : 0u;
-        const uint32_t voff_c = rowc * RAW_ROW + 16u * dma_half;
-        const uint32_t voff_r = rowc * (DR * 2) + 16u * dma_half;
-        const uint32_t voff_s = (uint32_t)((lane & 31) < nt ? (lane & 31) : 0) * 4u;
         const uint8_t* cb = a.codes + t0 * RAW_ROW;
         const uint8_t* rb = reinterpret_cast<const uint8_t*>(a.k_rope + t0 * DR);
         const uint32_t lc = __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE);
         const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_rho + 256u * buf);
+        const uint32_t voff_s = (uint32_t)((lane & 31) < nt ? (lane & 31) : 0) * 4u;
+        if (nt == MF_TILE) {
 #pragma unroll
-        for (int i = 0; i < MF_TILE / 2; i++) dma_lds_b128(cb + 32 * i, voff_c, lc + 1024u * i);
+            for (int i = 0; i < RAW_DMA; i++) dma_lds_b128(cb, voff_c[i], lc + 1024u * i);
 #pragma unroll
-        for (int i = 0; i < DR * 2 / 32; i++) dma_lds_b128(rb + 32 * i, voff_r, lds_rope + 1024u * i);
+            for (int i = 0; i < ROPE_DMA; i++) dma_lds_b128(rb, voff_r[i], lds_rope + 1024u * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RAW_DMA; i++)
+                dma_lds_b128(cb, (int)(voff_c[i] / RAW_ROW) < nt ? voff_c[i] : voff_c[i] % RAW_ROW, lc + 1024u * i);
+#pragma unroll
+            for (int i = 0; i < ROPE_DMA; i++)
+                dma_lds_b128(rb, (int)(voff_r[i] / (DR * 2)) < nt ? voff_r[i] : voff_r[i] % (DR * 2),
+                             lds_rope + 1024u * i);
+        }
         dma_lds_b32(a.row_scale + t0, voff_s, ls);
     };
     auto tile_row = [](int rb, int nn) { return 8 * (nn >> 2) + 4 * rb + (nn & 3); };
     // per-lane LDS read offsets (bytes within a tile)
-    const uint32_t rd_a = 512u * g + 16u * tile_sigma(tile_row(0, n));  // row block 0 (score, rope)
-    const uint32_t rd_b = 512u * g + 16u * tile_sigma(tile_row(1, n));  // row block 1
-    const uint32_t rd_t = 16u * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
+    const uint32_t rd_a = 16u * (RAW_SLOTS * tile_sigma(tile_row(0, n)) + g);   // score, row block 0
+    const uint32_t rd_b = 16u * (RAW_SLOTS * tile_sigma(tile_row(1, n)) + g);   // score, row block 1
+    const uint32_t rp_a = 16u * (ROPE_SLOTS * tile_sigma(tile_row(0, n)) + g);  // rope, row block 0
+    const uint32_t rp_b = 16u * (ROPE_SLOTS * tile_sigma(tile_row(1, n)) + g);  // rope, row block 1
+    const uint32_t rd_t = 16u * RAW_SLOTS * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
 
     // ---- query operands
     const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
@@ -894,7 +922,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
             for (int k = 0; k < 2; k++)
-                kr[rb][k] = *reinterpret_cast<const uint4*>(&rope_s[wave][(rb ? rd_b : rd_a) + 2048 * k]);
+                kr[rb][k] = *reinterpret_cast<const uint4*>(&rope_s[wave][(rb ? rp_b : rp_a) + 64 * k]);
         const float4 rho0 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g]);
         const float4 rho1 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g + 4]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): those reads are done before the buffers refill
@@ -903,7 +931,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         // ---- scores: both row blocks together, the reads one k-chunk ahead
         const uint8_t* pa = tb + rd_a;
         const uint8_t* pbp = tb + rd_b;
-        auto chunk = [&](const uint8_t* base, int j) { return *reinterpret_cast<const uint4*>(base + 2048 * j); };
+        auto chunk = [&](const uint8_t* base, int j) { return *reinterpret_cast<const uint4*>(base + 64 * j); };
         f32x4_t sl[2], sr[2];
         sl[0] = sl[1] = sr[0] = sr[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         uint4 na = chunk(pa, 0), nb = chunk(pbp, 0);
@@ -984,7 +1012,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         // ---- PV: groups of 8 column blocks, the next group's reads in flight
         const uint8_t* trbase = tb + rd_t;
         auto trd = [&](int mb) {
-            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(trbase + 512 * mb));
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(trbase + 16 * mb));
         };
         i32x2_t nv[8];
 #pragma unroll

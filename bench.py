@@ -114,7 +114,7 @@ def main():
                 kvq.kvq_encode_fp8(row, codes_c[T - 1:T], scales_c[T - 1:T])
             else:
                 kvq.kvq_encode_tq4(row, mask, codes_c[T - 1:T], scales_c[T - 1:T])
-            for st in (kvq.KVQ_STAGE_PLAN, kvq.KVQ_STAGE_QPREP, kvq.KVQ_STAGE_SPLITS, kvq.KVQ_STAGE_MERGE):
+            for st in (kvq.KVQ_STAGE_PREP, kvq.KVQ_STAGE_SPLITS, kvq.KVQ_STAGE_MERGE):
                 kvq.kvq_decode_attn_stage(a, st, ws)
         else:
             kvq.kvq_decode_attn_stage(a, stage, ws)

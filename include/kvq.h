@@ -153,9 +153,10 @@ int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_of
  *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA), <= 1e-5 (KVQ_PREC_FP32).
  * KVQ_PREC_MFMA operands: latent codes in fp16 (exact for every e4m3 value and
  * codebook level); the latent query scaled per head by a power of two and
- * split into two fp16 terms; the rope query split into two bf16 terms (k_rope
- * is bf16); the probabilities p * rho_t scaled per T-split by a power of two
- * and rounded to fp16; fp32 accumulation, softmax and per-row scales. */
+ * rounded to fp16 (TQ4: split into two fp16 terms); the rope query split into
+ * two bf16 terms (k_rope is bf16); the probabilities p * rho_t scaled by a
+ * power of two per work item and rounded to fp16; fp32 accumulation, softmax
+ * and per-row scales. */
 typedef struct kvq_attn_args {
     int32_t qmode;              /* KVQ_QMODE_FP8 or KVQ_QMODE_TQ4                 */
     int32_t precision;          /* KVQ_PREC_MFMA or KVQ_PREC_FP32                 */
@@ -190,20 +191,18 @@ int64_t kvq_decode_attn_workspace_bytes(const kvq_attn_args* a);
  * calls that share a workspace must be ordered (same stream). */
 int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, void* stream);
 
-/* One stage of kvq_decode_attn; running stages 0..3 in order on one stream is
- * exactly kvq_decode_attn.  Stage 0 (split plan) depends only on seq_offsets,
- * total_rows, split_rows, n_heads and precision, so callers whose layers share
- * the sequence lengths may run it once and stages 1..3 per layer; running a
- * stage also gives profilers and timers one kernel per call:
- *   KVQ_STAGE_PLAN   per-sequence T-split prefix into the workspace;
- *   KVQ_STAGE_QPREP  the query operands into the workspace (TQ4: rotated by R;
- *                    matrix-core path: scaled and split into 16-bit terms);
+/* One stage of kvq_decode_attn; running stages 0..2 in order on one stream is
+ * exactly kvq_decode_attn.  Running a stage gives profilers and timers one
+ * stage per call:
+ *   KVQ_STAGE_PREP   the per-sequence T-split prefix and the query operands in
+ *                    the workspace (TQ4: rotated by R); the fp8 matrix-core
+ *                    path does both inside its split kernel and launches
+ *                    nothing here;
  *   KVQ_STAGE_SPLITS the attention over every T-split (partial softmax states);
  *   KVQ_STAGE_MERGE  merge of the splits (+ TQ4 un-rotation) into out / lse. */
-#define KVQ_STAGE_PLAN 0
-#define KVQ_STAGE_QPREP 1
-#define KVQ_STAGE_SPLITS 2
-#define KVQ_STAGE_MERGE 3
+#define KVQ_STAGE_PREP 0
+#define KVQ_STAGE_SPLITS 1
+#define KVQ_STAGE_MERGE 2
 int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, int64_t ws_bytes,
                           void* stream);
 

@@ -165,7 +165,7 @@ int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, v
 int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, int64_t ws_bytes, void* stream) {
     int rc = check_attn(a);
     if (rc != KVQ_OK) return rc;
-    if (stage < KVQ_STAGE_PLAN || stage > KVQ_STAGE_MERGE) return KVQ_ERR_INVALID_ARG;
+    if (stage < KVQ_STAGE_PREP || stage > KVQ_STAGE_MERGE) return KVQ_ERR_INVALID_ARG;
     const int64_t need = kvq::attn_workspace_bytes(*a);
     if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;

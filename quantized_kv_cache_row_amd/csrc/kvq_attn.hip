@@ -809,6 +809,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     __shared__ __align__(16) uint8_t rope_s[MF_WAVES][ROPE_TILE];      // rope keys (bf16)
     __shared__ __align__(16) float rho_s[MF_WAVES][2][64];             // row scales
     __shared__ float ml_s[MF_WAVES][3][MF_HEADS];
+    __shared__ int64_t plan_s[3];  // this chunk's first row, end row, sequence (-1: none)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, n = lane & 15;
@@ -817,14 +818,101 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int64_t local = blockIdx.x / N_XCD;
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
-    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
-    const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
-    const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
-    const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
-    const int64_t r1 = min(seq_hi, r0 + (int64_t)p.split_rows);
+    if (c >= p.max_chunks) return;
+    const int head = hg * MF_HEADS + n;
+    // ---- the split plan, in-kernel: wave 0 scans max(1, ceil(T_s / split)) over
+    // the sequences, 64 at a time, and finds the one holding chunk c; the
+    // workgroup of chunk 0, head group 0 also stores the prefix for the merge.
+    const bool writer = blockIdx.x == 0;
+    if (wave == 0) {
+        const int64_t split = p.split_rows;
+        int64_t run = 0;
+        if (lane == 0) plan_s[2] = -1;
+        for (int base = 0; base < a.n_seqs; base += 64) {
+            const int sq = base + lane;
+            int64_t cnt = 0, lo = 0, hi = 0;
+            if (sq < a.n_seqs) {
+                lo = max(a.seq_offsets[sq], (int64_t)0);
+                hi = min(a.seq_offsets[sq + 1], a.total_rows);
+                cnt = hi > lo ? (hi - lo + split - 1) / split : 1;
+            }
+            int64_t incl = cnt;  // inclusive scan over the wave
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int64_t v = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += v;
+            }
+            const int64_t excl = run + incl - cnt;
+            const bool mine = sq < a.n_seqs && c >= excl && c < excl + cnt;  // one lane over all passes
+            if (sq < a.n_seqs && writer) p.chunk_prefix[sq] = excl;
+            if (mine) {
+                const int64_t r0c = lo + (c - excl) * split;
+                plan_s[0] = r0c;
+                plan_s[1] = min(hi, r0c + split);
+                plan_s[2] = sq;
+            }
+            run += __shfl(incl, 63, 64);
+            if (!writer && __any(mine)) break;
+        }
+        if (writer && lane == 0) p.chunk_prefix[a.n_seqs] = run;
+    }
+
+    // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
+    // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
+    // two qs (max |q| * qs in [256, 512)) and rounded to fp16; the rope dims
+    // 32 ks' + 8 g + e as a bf16 hi + lo pair.
+    uint4 qh[16], rh[2], rl[2];
+    float qinv;
+    {
+        __syncthreads();  // plan_s
+        const int sq = (int)plan_s[2];
+        const bool hv = head < a.n_heads && sq >= 0;
+        const float* ql = a.q_lat + ((int64_t)(sq < 0 ? 0 : sq) * a.n_heads + (hv ? head : 0)) * DL;
+        const float* qr = a.q_rope + ((int64_t)(sq < 0 ? 0 : sq) * a.n_heads + (hv ? head : 0)) * DR;
+        float4 v[32], w[4];
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++) {
+            const float* src = ql + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
+            v[2 * ks] = hv ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[2 * ks + 1] = hv ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const float* src = qr + 32 * k + 8 * g;
+            w[2 * k] = hv ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+            w[2 * k + 1] = hv ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float qmax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; k++)
+            qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+        const float qs = pow2_scale_for(qmax, 8);
+        qinv = 1.0f / qs;  // exact
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++) {
+            const float4 x = v[2 * ks], y = v[2 * ks + 1];
+            qh[ks] = make_uint4(pack_f16x2(x.x * qs, x.y * qs), pack_f16x2(x.z * qs, x.w * qs),
+                                pack_f16x2(y.x * qs, y.y * qs), pack_f16x2(y.z * qs, y.w * qs));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const float f[8] = {w[2 * k].x, w[2 * k].y, w[2 * k].z, w[2 * k].w,
+                                w[2 * k + 1].x, w[2 * k + 1].y, w[2 * k + 1].z, w[2 * k + 1].w};
+            float b[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) b[e] = u2f(f32_to_bf16_rne(f[e]) << 16);
+            rh[k] = make_uint4(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]),
+                               pack_bf16x2(b[6], b[7]));
+            rl[k] = make_uint4(pack_bf16x2(f[0] - b[0], f[1] - b[1]), pack_bf16x2(f[2] - b[2], f[3] - b[3]),
+                               pack_bf16x2(f[4] - b[4], f[5] - b[5]), pack_bf16x2(f[6] - b[6], f[7] - b[7]));
+        }
+    }
+    if (plan_s[2] < 0) return;  // no such chunk (workgroup-uniform)
+    const int64_t r0 = plan_s[0], r1 = plan_s[1];
     const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
     const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
-    const int head = hg * MF_HEADS + n;
 
     // DMA loaders (global -> LDS, no registers).  Lane l of instruction i fills
     // slot 64 i + l: row sigma^-1(slot / 33), chunk slot % 33 (the pad slot and
@@ -880,17 +968,6 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const uint32_t rp_b = 16u * (ROPE_SLOTS * tile_sigma(tile_row(1, n)) + g);  // rope, row block 1
     const uint32_t rd_t = 16u * RAW_SLOTS * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
 
-    // ---- query operands
-    const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
-    uint4 qh[16], rh[2], rl[2];
-#pragma unroll
-    for (int k = 0; k < 16; k++) qh[k] = qp[16 * g + k];
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        rh[k] = qp[QP_RH + 2 * g + k];
-        rl[k] = qp[QP_RL + 2 * g + k];
-    }
-    const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
     const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
 
     // Softmax with a fixed reference per wave and head: p = 2^(s - m_run), with
@@ -1096,57 +1173,82 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 }
 
 // ---- 3. merge --------------------------------------------------------------------------------
-// One workgroup (256 threads) per (sequence, head): two halves of 128 threads
-// take alternate splits, 4 dims per thread; then TQ4 un-rotation by one wave.
+// NDH workgroups per (sequence, head), each over DL / NDH output dims (TQ4: the
+// whole row, which the un-rotation needs).  A thread owns one float4 column and
+// every NGRP-th split; it merges its splits online (running max, rescaled sums),
+// then the NGRP groups are combined through LDS.
 template <bool TQ4, bool LOG2>
 __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
-    __shared__ float red[256];
+    constexpr int NDH = TQ4 ? 1 : 2;
+    constexpr int DW = DL / NDH;       // dims per workgroup
+    constexpr int COLS = DW / 4;       // float4 columns
+    constexpr int NGRP = 256 / COLS;   // split groups
+    __shared__ __align__(16) float4 o_s[NGRP][COLS];
+    __shared__ float m_s[NGRP], l_s[NGRP];
     __shared__ __align__(16) float vec[DL];
     const int tid = threadIdx.x;
-    const int64_t item = blockIdx.x;
+    const int64_t item = blockIdx.x / NDH;
+    const int part = (int)(blockIdx.x % NDH);
     const int s = (int)(item / a.n_heads), h = (int)(item % a.n_heads);
     const int64_t c0 = min(p.chunk_prefix[s], p.max_chunks), c1 = min(p.chunk_prefix[s + 1], p.max_chunks);
-    float M = -INFINITY;
-    for (int64_t c = c0 + tid; c < c1; c += 256) M = fmaxf(M, p.part_m[c * a.n_heads + h]);
-    red[tid] = M;
-    __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
-        if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-        __syncthreads();
-    }
-    M = red[0];
-    __syncthreads();
-    float L = 0.0f;
-    for (int64_t c = c0 + tid; c < c1; c += 256) {
-        const float mc = p.part_m[c * a.n_heads + h];
-        const float w = (mc == -INFINITY) ? 0.0f : (LOG2 ? exp2f(mc - M) : expf(mc - M));
-        L += w * p.part_l[c * a.n_heads + h];
-    }
-    red[tid] = L;
-    __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
-        if (tid < o) red[tid] += red[tid + o];
-        __syncthreads();
-    }
-    L = red[0];
-    const int half = tid >> 7, col = (tid & 127) * 4;
+    const int col = tid % COLS, grp = tid / COLS;
+    auto ex = [](float x) { return LOG2 ? exp2f(x) : expf(x); };
+    float m = -INFINITY, l = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (M != -INFINITY) {
-        for (int64_t c = c0 + half; c < c1; c += 2) {
-            const float mc = p.part_m[c * a.n_heads + h];
-            const float w = (mc == -INFINITY) ? 0.0f : (LOG2 ? exp2f(mc - M) : expf(mc - M));
-            const float4 v = *reinterpret_cast<const float4*>(p.part_o + (c * a.n_heads + h) * DL + col);
-            o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
+    // batches of 4 splits: all loads first (no branch between them), then the
+    // online update with selects
+    for (int64_t cb = c0 + grp; cb < c1; cb += 4 * NGRP) {
+        float mc[4], lc[4];
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t c = cb + u * NGRP;
+            const int64_t ch = (c < c1 ? c : cb) * a.n_heads + h;
+            mc[u] = p.part_m[ch];
+            lc[u] = p.part_l[ch];
+            v[u] = *reinterpret_cast<const float4*>(p.part_o + ch * DL + part * DW + 4 * col);
+            if (c >= c1) mc[u] = -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const float mn = fmaxf(m, mc[u]);
+            const float sc = m == -INFINITY ? 0.0f : ex(m - mn);
+            const float w = mc[u] == -INFINITY ? 0.0f : ex(mc[u] - mn);
+            o.x = o.x * sc + w * v[u].x;
+            o.y = o.y * sc + w * v[u].y;
+            o.z = o.z * sc + w * v[u].z;
+            o.w = o.w * sc + w * v[u].w;
+            l = l * sc + w * lc[u];
+            m = mn;
         }
     }
-    if (half == 1) *reinterpret_cast<float4*>(&vec[col]) = o;
+    o_s[grp][col] = o;
+    if (col == 0) {
+        m_s[grp] = m;
+        l_s[grp] = l;
+    }
     __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NGRP; k++) M = fmaxf(M, m_s[k]);
+    float L = 0.0f;
+    float wg[NGRP];
+#pragma unroll
+    for (int k = 0; k < NGRP; k++) {
+        wg[k] = m_s[k] == -INFINITY ? 0.0f : ex(m_s[k] - M);
+        L += wg[k] * l_s[k];
+    }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    if (half == 0) {
-        const float4 u = *reinterpret_cast<const float4*>(&vec[col]);
-        o = make_float4((o.x + u.x) * inv, (o.y + u.y) * inv, (o.z + u.z) * inv, (o.w + u.w) * inv);
-        if (TQ4) *reinterpret_cast<float4*>(&vec[col]) = o;
-        else *reinterpret_cast<float4*>(a.out + item * DL + col) = o;
+    if (grp == 0) {
+        float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int k = 0; k < NGRP; k++) {
+            const float4 u = o_s[k][col];
+            r.x += wg[k] * u.x; r.y += wg[k] * u.y; r.z += wg[k] * u.z; r.w += wg[k] * u.w;
+        }
+        r = make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+        if (TQ4) *reinterpret_cast<float4*>(&vec[4 * col]) = r;
+        else *reinterpret_cast<float4*>(a.out + item * DL + part * DW + 4 * col) = r;
     }
     if (TQ4) {
         __syncthreads();
@@ -1165,9 +1267,9 @@ __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
                         v[i + hh] = x - y;
                     }
 #pragma unroll
-            for (int m = 1; m < 64; m <<= 1)
+            for (int mm = 1; mm < 64; mm <<= 1)
 #pragma unroll
-                for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, m);
+                for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, mm);
             const uint32_t sm = a.sign_mask[lane];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
@@ -1179,7 +1281,7 @@ __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
             dst[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
     }
-    if (a.lse && tid == 0) {
+    if (a.lse && part == 0 && tid == 0) {
         float v;
         if (!(L > 0.0f)) v = -INFINITY;
         else v = LOG2 ? (M + log2f(L)) * LN2 : M + logf(L);
@@ -1196,11 +1298,11 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
     const bool f32 = a.precision == KVQ_PREC_FP32;
     const bool tq4 = a.qmode == KVQ_QMODE_TQ4;
     switch (stage) {
-        case KVQ_STAGE_PLAN:
+        case KVQ_STAGE_PREP:
+            // the fp8 matrix-core split kernel plans and prepares its query itself
+            if (!f32 && !tq4) break;
             hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a.seq_offsets, a.n_seqs, p.split_rows, a.total_rows,
                                p.chunk_prefix);
-            break;
-        case KVQ_STAGE_QPREP:
             if (f32) {
                 if (tq4) {
                     const int64_t rows = (int64_t)a.n_seqs * a.n_heads;
@@ -1209,9 +1311,7 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
                 }
             } else {
                 const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
-                const dim3 grid((unsigned)((rows + 3) / 4));
-                if (tq4) hipLaunchKernelGGL(k_qprep<KVQ_QMODE_TQ4>, grid, dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL(k_qprep<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p);
+                hipLaunchKernelGGL(k_qprep<KVQ_QMODE_TQ4>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
             }
             break;
         case KVQ_STAGE_SPLITS:
@@ -1227,13 +1327,13 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
             }
             break;
         default: {
-            const dim3 grid((unsigned)((int64_t)a.n_seqs * a.n_heads));
+            const int64_t items = (int64_t)a.n_seqs * a.n_heads;
             if (tq4) {
-                if (!f32) hipLaunchKernelGGL((k_merge<true, true>), grid, dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<true, false>), grid, dim3(256), 0, st, a, p);
+                if (!f32) hipLaunchKernelGGL((k_merge<true, true>), dim3((unsigned)items), dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<true, false>), dim3((unsigned)items), dim3(256), 0, st, a, p);
             } else {
-                if (!f32) hipLaunchKernelGGL((k_merge<false, true>), grid, dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<false, false>), grid, dim3(256), 0, st, a, p);
+                if (!f32) hipLaunchKernelGGL((k_merge<false, true>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<false, false>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
             }
             break;
         }
@@ -1243,7 +1343,7 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
 
 hipError_t launch_decode_attn(const kvq_attn_args& a, void* ws, int64_t ws_bytes, hipStream_t st) {
     (void)ws_bytes;
-    for (int stage = KVQ_STAGE_PLAN; stage <= KVQ_STAGE_MERGE; stage++) {
+    for (int stage = KVQ_STAGE_PREP; stage <= KVQ_STAGE_MERGE; stage++) {
         const hipError_t e = launch_decode_attn_stage(a, stage, ws, st);
         if (e != hipSuccess) return e;
     }

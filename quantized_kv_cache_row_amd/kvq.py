@@ -17,7 +17,7 @@ KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAU
 KVQ_QMODE_FP8, KVQ_QMODE_TQ4 = 1, 2
 KVQ_PREC_MFMA, KVQ_PREC_FP32 = 0, 1
 KVQ_Q4_NO_ROTATE = 1
-KVQ_STAGE_PLAN, KVQ_STAGE_QPREP, KVQ_STAGE_SPLITS, KVQ_STAGE_MERGE = 0, 1, 2, 3
+KVQ_STAGE_PREP, KVQ_STAGE_SPLITS, KVQ_STAGE_MERGE = 0, 1, 2
 KVQ_CVT_F32_TO_E4M3, KVQ_CVT_E4M3_TO_BF16, KVQ_CVT_F32_TO_F16, KVQ_CVT_F32_TO_BF16, KVQ_CVT_E4M3_TO_F16 = 1, 2, 3, 4, 5
 
 

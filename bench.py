@@ -49,22 +49,65 @@ def decode_bytes(T, qmode):
     return T * ((512 if qmode == 1 else 256) + 4 + 128)
 
 
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fp8_T32768_hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "quantized_kv_cache_row_amd", "csrc", "kvq_attn.hip")
+
+
+def copy_calibration():
+    import torch
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 10}), flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per split-kernel launch from the committed counter summary:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled by
+    what the same counter reads for a plain copy of known size.  None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if kv.get("source_sha256") != sha:
+        return None
+    fetch = float(kv["fetch_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_fetch_kib_per_dispatch"])
+    write = float(kv["write_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_write_kib_per_dispatch"])
+    return fetch + write
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2])
+    ap.add_argument("--qmode", default="fp8", choices=["fp8", "tq4"])
     ap.add_argument("--kv-copies", type=int, default=16)
     ap.add_argument("--split-rows", type=int, default=0)
     ap.add_argument("--precision", type=int, default=0, choices=[0, 1])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 10 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the decode path shards T across GPUs by design, see DESIGN.md, but no multi-GPU run exists)",
-              file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (decode attention would "
+              f"shard the cached rows across GPUs and all-gather the partial softmax states; no multi-GPU "
+              f"path is built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -74,8 +117,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     log(f"device {torch.cuda.get_device_name(0)}")
-    qmode = 1 if args.config == 1 else 2
-    w = workloads.config1() if qmode == 1 else workloads.config2()
+    qmode = 1 if args.qmode == "fp8" else 2
+    w = workloads.kv8_decode() if qmode == 1 else workloads.tq4_decode()
     T, H = w.total_rows, w.n_heads
     log(f"workload {w.name}: T={T} H={H} copies={args.kv_copies}")
 
@@ -224,7 +267,8 @@ def main():
                    "precision": "mfma-fp16" if args.precision == 0 else "fp32", "kv_copies": args.kv_copies,
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic() if (qmode == 1 and args.precision == 0) else None},
         "hbm": {"achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
                 "bytes_per_launch": nbytes},
         "kernel_us": kern_ms * 1000.0,

@@ -30,7 +30,7 @@
  *         [cell][kv head][144], dequant (nibble - 8) * f32(d)), and the k4
  *         commit (four consecutive k share one nibble side of a block).
  *
- * Readings of points the pages leave open are listed in the design doc and at each
+ * Readings of points the pages leave open are stated at each
  * function below.
  */
 #include <math.h>

@@ -89,29 +89,29 @@ class DecodeWorkload:
         self.sm_scale = SM_SCALE
 
 
-def config0():
+def tiny_fp8_decode():
     """Tiny MLA decode, fp8: 1 sequence, T = 256, 16 heads (seed 1000)."""
     return DecodeWorkload("tiny-fp8-T256-H16", 1000, [256], 16, qmode=1)
 
 
-def config1(T=32768):
+def kv8_decode(T=32768):
     """KV8 absorbed-MLA decode: batch 1, 128 heads, T = 32768 (seed 1001)."""
     return DecodeWorkload(f"kv8-mla-decode-T{T}-H128", 1001, [T], 128, qmode=1)
 
 
-def config2(T=32768):
-    """TQ4 decode, same latents as config 1 (seed 1001), signs from seed 1002."""
+def tq4_decode(T=32768):
+    """TQ4 decode, the same latents as the KV8 decode (seed 1001), signs from seed 1002."""
     return DecodeWorkload(f"tq4-mla-decode-T{T}-H128", 1001, [T], 128, qmode=2, sign_seed=1002)
 
 
-def config2_new_rows(n=8192, dim=DIM_LAT):
+def tq4_encode_rows(n=8192, dim=DIM_LAT):
     """The 8192 new rows of the TQ4 encode-throughput pass (seed 1002)."""
     st = streams(1002)
     x, _ = latent_rows(st[S_GAIN], st[S_NEW], n, np.arange(1, n + 1, dtype=np.int64), dim)
     return x
 
 
-def config3_lengths(scale=1):
+def ragged_lengths(scale=1):
     st = streams(1003)
     L = st[S_LENGTHS].integers(1024, 16384 + 1, size=32).astype(np.int64)
     L = np.concatenate([L, [131072]])
@@ -120,12 +120,12 @@ def config3_lengths(scale=1):
     return L
 
 
-def config3(scale=1):
+def ragged_kv8_decode(scale=1):
     """Ragged long-context KV8 decode: 32 sequences, T ~ U[1024, 16384], plus one
     sequence of 131072 (last); 128 heads (seed 1003).  scale > 1 shrinks every
     length by that factor (parity-test sizes)."""
     return DecodeWorkload(f"ragged-kv8-33seq{'' if scale == 1 else f'-div{scale}'}", 1003,
-                          config3_lengths(scale), 128, qmode=1)
+                          ragged_lengths(scale), 128, qmode=1)
 
 
 def fp8_rows_for_encode(n, seed=1001, dim=DIM_LAT):

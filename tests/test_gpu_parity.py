@@ -117,13 +117,13 @@ def test_convert_e4m3_bf16_f16_against_oracle():
 
 # ---- encoders -----------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", ["config0", "config1", "random-dims", "zeros-extremes"])
+@pytest.mark.parametrize("case", ["tiny_fp8_decode", "kv8_decode", "random-dims", "zeros-extremes"])
 def test_fp8_encoder_bit_exact(case):
     _say(f"fp8 encoder {case}")
     rng = np.random.default_rng(5)
-    if case == "config0":
-        xs = [workloads.config0().latent]
-    elif case == "config1":
+    if case == "tiny_fp8_decode":
+        xs = [workloads.tiny_fp8_decode().latent]
+    elif case == "kv8_decode":
         xs = [workloads.fp8_rows_for_encode(32768)]
     elif case == "random-dims":
         xs = [(rng.standard_normal((37, d)) * 10 ** rng.uniform(-5, 5, (37, 1))).astype(np.float32)
@@ -145,14 +145,14 @@ def test_fp8_encoder_bit_exact(case):
         np.testing.assert_array_equal(_np(c), rc)
 
 
-@pytest.mark.parametrize("case", ["config2-cache", "config2-new", "dims"])
+@pytest.mark.parametrize("case", ["tq4_decode-cache", "tq4_decode-new", "dims"])
 def test_tq4_encoder_bit_exact(case):
     _say(f"tq4 encoder {case}")
-    w = workloads.config2(T=1024) if case != "config2-cache" else workloads.config2()
-    if case == "config2-cache":
+    w = workloads.tq4_decode(T=1024) if case != "tq4_decode-cache" else workloads.tq4_decode()
+    if case == "tq4_decode-cache":
         xs = [(w.latent, w.sign_mask)]
-    elif case == "config2-new":
-        xs = [(workloads.config2_new_rows(8192), w.sign_mask)]
+    elif case == "tq4_decode-new":
+        xs = [(workloads.tq4_encode_rows(8192), w.sign_mask)]
     else:
         rng = np.random.default_rng(3)
         xs = []
@@ -204,11 +204,11 @@ def _check_attn(w, c, s, precision, split_rows=0, q_lat=None, q_rope=None, tol=N
 
 
 @pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
-def test_attn_config0_and_split_invariance(precision):
-    _say(f"attn config0 precision={precision}")
-    w = workloads.config0()
+def test_attn_tiny_and_split_invariance(precision):
+    _say(f"attn tiny_fp8_decode precision={precision}")
+    w = workloads.tiny_fp8_decode()
     c, s = _encode_cache(w)
-    outs = [_check_attn(w, c, s, precision, sr, label="config0") for sr in (0, 256, 128, 64, 32)]
+    outs = [_check_attn(w, c, s, precision, sr, label="tiny_fp8_decode") for sr in (0, 256, 128, 64, 32)]
     for o in outs[1:]:
         assert rel_err(o, outs[0]) <= 2 * TOL[precision]
 
@@ -217,7 +217,7 @@ def test_attn_config0_and_split_invariance(precision):
 @pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_attn_full_T32768(qmode, precision):
     _say(f"attn T=32768 H=128 qmode={qmode} precision={precision}")
-    w = workloads.config1() if qmode == 1 else workloads.config2()
+    w = workloads.kv8_decode() if qmode == 1 else workloads.tq4_decode()
     c, s = _encode_cache(w)
     _check_attn(w, c, s, precision, label=w.name)
     if precision == kvq.KVQ_PREC_MFMA:  # a few explicit split sizes
@@ -228,7 +228,7 @@ def test_attn_full_T32768(qmode, precision):
 @pytest.mark.parametrize("qmode", [1, 2])
 def test_attn_peaked_softmax(qmode):
     _say(f"attn peaked qmode={qmode}")
-    w = workloads.config2(T=3000) if qmode == 2 else workloads.config1(T=3000)
+    w = workloads.tq4_decode(T=3000) if qmode == 2 else workloads.kv8_decode(T=3000)
     c, s = _encode_cache(w)
     ql = (w.q_lat * 50).astype(np.float32)
     qr = (w.q_rope * 50).astype(np.float32)
@@ -272,22 +272,22 @@ def test_attn_ragged_edges():
         _check_attn(w2, c2, s2, prec, 32, label="edges-tq4")
 
 
-def test_attn_ragged_config3_sampled_heads():
-    _say("attn config3 (ragged, 33 sequences) sampled heads")
-    w = workloads.config3()
+def test_attn_ragged_sampled_heads():
+    _say("attn ragged_kv8_decode (ragged, 33 sequences) sampled heads")
+    w = workloads.ragged_kv8_decode()
     c, s = _encode_cache(w)
     got, glse = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)
     heads = np.array([0, 37, 127])
     ref, rlse = oracle.decode_attn(1, w.offsets, _np(c), _np(s), w.k_rope, w.q_lat[:, heads], w.q_rope[:, heads],
                                    w.sm_scale)
     e = rel_err(got[:, heads], ref)
-    _say(f"  config3 heads {list(heads)}: {e:.3e}")
+    _say(f"  ragged_kv8_decode heads {list(heads)}: {e:.3e}")
     assert e <= 2e-3
 
 
-def test_attn_scaled_config3_all_heads():
-    _say("attn config3/16 all heads")
-    w = workloads.config3(scale=16)
+def test_attn_ragged_div16_all_heads():
+    _say("attn ragged_kv8_decode/16 all heads")
+    w = workloads.ragged_kv8_decode(scale=16)
     c, s = _encode_cache(w)
     for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         _check_attn(w, c, s, prec, label=w.name)
@@ -295,7 +295,7 @@ def test_attn_scaled_config3_all_heads():
 
 def test_attn_deterministic():
     _say("attn determinism")
-    w = workloads.config1(T=5000)
+    w = workloads.kv8_decode(T=5000)
     c, s = _encode_cache(w)
     a, la = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)
     b, lb = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)

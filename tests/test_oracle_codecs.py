@@ -71,8 +71,8 @@ def _torch_fp8_rows(x):
     return c, s
 
 
-def test_fp8_encoder_matches_torch_on_config0():
-    w = workloads.config0()
+def test_fp8_encoder_matches_torch_on_tiny_workload():
+    w = workloads.tiny_fp8_decode()
     codes, scales = oracle.encode_fp8(w.latent)
     ref_c, ref_s = _torch_fp8_rows(w.latent)
     np.testing.assert_array_equal(scales.view(np.uint32), ref_s.view(np.uint32))
@@ -110,7 +110,7 @@ def test_fp8_scale_one_is_plain_e4m3():
 
 
 def test_fp8_roundtrip_error_bounds():
-    w = workloads.config0()
+    w = workloads.tiny_fp8_decode()
     codes, scales = oracle.encode_fp8(w.latent)
     xh = oracle.decode_fp8(codes, scales)
     x = w.latent.astype(np.float64)
@@ -221,7 +221,7 @@ def test_tq4_distortion_near_page_figure():
 
 
 def test_tq4_radius_invariant_and_rotation_identity():
-    w = workloads.config0()
+    w = workloads.tiny_fp8_decode()
     x = w.latent[:64]
     mask = _mask()
     codes, radii = oracle.encode_tq4(x, mask)

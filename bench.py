@@ -5,11 +5,12 @@ T = 32768 cached rows, 128 heads, 512-dim fp8 latent + 64-dim bf16 rope key):
   1. fp8-encode the step's new latent row into the cache (row T-1),
   2. decode attention over all T rows: split plan + query preparation, the
      split kernel (the dominant kernel), the merge.
-Each step is captured once as a HIP graph and replayed, as a serving loop
-does, so the step time is GPU time rather than Python launch overhead.  The
-steps cycle through --kv-copies independent caches (16 x 21 MB > the 256 MB
-last-level cache) so every step reads its KV from HBM, as consecutive layers
-of a model do.  Inputs are seeded synthetic data, resident in HBM before the
+The steps cycle through --kv-copies independent caches (16 x 21 MB > the
+256 MB last-level cache) so every step reads its KV from HBM, as consecutive
+layers of a model do; one step per cache, in order, is captured as one HIP
+graph and replayed, as a serving loop replays a captured forward pass, so the
+step time is GPU time rather than launch overhead (leftover steps replay
+single-step graphs).  Inputs are seeded synthetic data, resident in HBM before the
 timed region.
 
 The split kernel's average duration is timed with HIP events on the launch
@@ -179,6 +180,10 @@ def main():
         with torch.cuda.graph(g, stream=side):
             step(c)
         step_graphs.append(g)
+    round_graph = torch.cuda.CUDAGraph()  # one step per copy, in order: consecutive layers of a model
+    with torch.cuda.graph(round_graph, stream=side):
+        for c in range(n_copies):
+            step(c)
     split_graph = torch.cuda.CUDAGraph()  # one split launch per copy, back to back
     with torch.cuda.graph(split_graph, stream=side):
         for c in range(n_copies):
@@ -190,16 +195,24 @@ def main():
             step_graphs[c].replay()
             torch.cuda.synchronize()
             assert torch.equal(out, eager_out[c]), f"graph replay {rep} of copy {c} differs from the eager step"
+        out.zero_()
+        round_graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out[n_copies - 1]), f"round replay {rep} differs from the eager steps"
+
+    def run_steps(k):
+        for _ in range(k // n_copies):
+            round_graph.replay()
+        for c in range(k % n_copies):
+            step_graphs[c].replay()
 
     log(f"warmup {args.warmup}")
-    for i in range(args.warmup):
-        step_graphs[i % n_copies].replay()
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step_graphs[(args.warmup + i) % n_copies].replay()
+    run_steps(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1000.0 / args.steps

@@ -799,6 +799,14 @@ __device__ __forceinline__ void dma_lds_b32(const void* sbase, uint32_t voff, ui
                  : "v"(voff), "s"(sbase), "{m0}"(lds_base)
                  : "memory");
 }
+// max over the four lanes n, n ^ 16, n ^ 32, n ^ 48 (gfx950 lane-swap
+// instructions: each pairs a lane with the one 16 or 32 lanes away).
+__device__ __forceinline__ float max_xor16_xor32(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ int tile_sigma(int r) { return r ^ (((r >> 3) & 1) << 2) ^ (((r >> 4) & 1) << 3); }
 __device__ __forceinline__ int tile_sigma_inv(int q) {
     return q ^ (((q >> 4) & 1) << 3) ^ ((((q >> 3) ^ (q >> 4)) & 1) << 2);
@@ -860,7 +868,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
     // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
     // two qs (max |q| * qs in [256, 512)) and rounded to fp16; the rope dims
-    // 32 ks' + 8 g + e as a bf16 hi + lo pair.
+    // 32 ks' + 8 g + e, times sm_scale * log2(e), as a bf16 hi + lo pair.
     uint4 qh[16], rh[2], rl[2];
     float qinv;
     {
@@ -898,8 +906,10 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
 #pragma unroll
         for (int k = 0; k < 2; k++) {
-            const float f[8] = {w[2 * k].x, w[2 * k].y, w[2 * k].z, w[2 * k].w,
-                                w[2 * k + 1].x, w[2 * k + 1].y, w[2 * k + 1].z, w[2 * k + 1].w};
+            const float c2r = a.sm_scale * LOG2E;  // rope scores come out in log2 units
+            const float f[8] = {w[2 * k].x * c2r, w[2 * k].y * c2r, w[2 * k].z * c2r, w[2 * k].w * c2r,
+                                w[2 * k + 1].x * c2r, w[2 * k + 1].y * c2r, w[2 * k + 1].z * c2r,
+                                w[2 * k + 1].w * c2r};
             float b[8];
 #pragma unroll
             for (int e = 0; e < 8; e++) b[e] = u2f(f32_to_bf16_rne(f[e]) << 16);
@@ -968,7 +978,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const uint32_t rp_b = 16u * (ROPE_SLOTS * tile_sigma(tile_row(1, n)) + g);  // rope, row block 1
     const uint32_t rd_t = 16u * RAW_SLOTS * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
 
-    const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
+    const float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
 
     // Softmax with a fixed reference per wave and head: p = 2^(s - m_run), with
     // m_run the first tile's maximum, and probabilities enter the matrix cores
@@ -1036,30 +1046,25 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
             }
         // lane (g, n): accumulator register r of block rb = tile row 8 g + 4 rb + r
+        const bool full = nt == MF_TILE;  // wave-uniform
         float sc[2][4], rr[2][4];
-        float tmax = -INFINITY;
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
             const float4 rq = rb ? rho1 : rho0;
             const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const bool ok = 8 * g + 4 * rb + r < nt;
+                const bool ok = full || 8 * g + 4 * rb + r < nt;
                 rr[rb][r] = ok ? rv[r] : 0.0f;
-                const float v = ok ? c2 * (rv[r] * (sl[rb][r] * qinv) + sr[rb][r]) : -INFINITY;
-                sc[rb][r] = v;
-                tmax = fmaxf(tmax, v);
+                sc[rb][r] = ok ? fmaf(rv[r] * k1, sl[rb][r], sr[rb][r]) : -INFINITY;
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        float rmx = 0.0f;  // largest |rho| of the tile, over the whole wave
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) rmx = fmaxf(rmx, fabsf(rr[rb][r]));
-        rmx = fmaxf(rmx, __shfl_xor(rmx, 16, 64));
-        rmx = fmaxf(rmx, __shfl_xor(rmx, 32, 64));
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        tmax = max_xor16_xor32(tmax);
+        float rmx = fmaxf(fmaxf(fmaxf(fabsf(rr[0][0]), fabsf(rr[0][1])), fmaxf(fabsf(rr[0][2]), fabsf(rr[0][3]))),
+                          fmaxf(fmaxf(fabsf(rr[1][0]), fabsf(rr[1][1])), fmaxf(fabsf(rr[1][2]), fabsf(rr[1][3]))));
+        rmx = max_xor16_xor32(rmx);  // largest |rho| of the tile, over the whole wave
         if (m_run == -INFINITY) m_run = tmax;                         // first tile: every row valid
         if (rsc == 0.0f && rmx > 0.0f) rsc = pow2_scale_for(rmx, -1);  // wave-uniform
         const bool over = tmax > m_run + LAZY_LOG2;
@@ -1077,7 +1082,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             float pw[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float pv = (sc[rb][r] == -INFINITY) ? 0.0f : exp2f(sc[rb][r] - m_run);
+                // v_exp_f32: masked rows (score -inf) give 0; m_run is finite after the first tile
+                const float pv = __builtin_amdgcn_exp2f(sc[rb][r] - m_run);
                 psum += pv;
                 pw[r] = pv * (rr[rb][r] * rsc);
             }

@@ -88,6 +88,155 @@ def measured_traffic():
     return fetch + write
 
 
+def gpu_latents(torch, n_rows, seed, lengths=None, dim=512):
+    """Seeded synthetic latents generated on the device, with the recipe of
+    quantized_kv_cache_row_amd/workloads.py (N(0,1) x lognormal(0, 0.5) row
+    gain, channels 7 and 300 x20, rows 0 and 100 of every sequence zero) --
+    the same distribution, not the same stream (for sizes where host
+    generation would dominate the run)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn((n_rows, dim), generator=g, device="cuda")
+    x *= torch.exp(0.5 * torch.randn((n_rows, 1), generator=g, device="cuda"))
+    x[:, 7] *= 20.0
+    x[:, 300] *= 20.0
+    if lengths is not None:
+        starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+        zero = np.concatenate([starts + z for z in (0, 100)])
+        zero = zero[zero < n_rows]
+        x[torch.from_numpy(zero).cuda()] = 0.0
+    return x
+
+
+def time_graph(torch, fn, reps):
+    """Average duration (ms) of fn() over reps back-to-back launches captured
+    in one HIP graph, by HIP events on the replay stream."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_other_rows(torch, kvq, workloads, x_kv8):
+    """The other hot-path rows, each on its own workload: encoders, TQ4
+    decode, the ragged long-context decode, q4_0 append and gather.  Inputs
+    resident on the device; HIP events around graphs of back-to-back
+    launches.  Rates are algorithmic bytes (or flops) over kernel time."""
+    res = {}
+    dev = "cuda"
+    PEAK_T = PEAK_BF16_TFLOPS
+
+    def hbm(name, nbytes, ms, extra=None):
+        gbps = nbytes / (ms / 1000.0) / 1e9
+        d = {"us": ms * 1000.0, "GB/s": gbps, "frac_hbm": gbps / PEAK_HBM_GBPS, "bytes": nbytes}
+        d.update(extra or {})
+        res[name] = d
+        log(f"{name}: {ms * 1000:.1f} us, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+
+    # a1: fp8 encode of the 32768-row cache
+    N = x_kv8.shape[0]
+    c8 = torch.empty((N, 512), dtype=torch.uint8, device=dev)
+    s8 = torch.empty(N, dtype=torch.float32, device=dev)
+    ms = time_graph(torch, lambda: kvq.kvq_encode_fp8(x_kv8, c8, s8), 20)
+    hbm("fp8_encode_32768", N * (2048 + 516), ms, {"rows/s": N / (ms / 1000.0)})
+    # a2: TQ4 encode, the 8192-row pass and a 262144-row asymptote
+    mask = torch.from_numpy(workloads.tq4_decode(T=256).sign_mask).to(dev)
+    x8k = torch.from_numpy(workloads.tq4_encode_rows(8192)).to(dev)
+    for n, xs in ((8192, x8k), (262144, gpu_latents(torch, 262144, 5))):
+        ct = torch.empty((n, 256), dtype=torch.uint8, device=dev)
+        rt = torch.empty(n, dtype=torch.float32, device=dev)
+        ms = time_graph(torch, lambda: kvq.kvq_encode_tq4(xs, mask, ct, rt), 20)
+        hbm(f"tq4_encode_{n}", n * (2048 + 260) + 64, ms, {"rows/s": n / (ms / 1000.0)})
+    del x8k
+
+    def decode(name, qmode, x, lengths, n_heads, seed, copies):
+        T = x.shape[0]
+        offs = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)).to(dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        S = len(lengths)
+        ql = torch.randn((S, n_heads, 512), generator=g, device=dev) / math.sqrt(576.0)
+        qr = torch.randn((S, n_heads, 64), generator=g, device=dev) / math.sqrt(576.0)
+        kr = torch.randn((T, 64), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+        cb = 512 if qmode == 1 else 256
+        sets = []
+        for _ in range(copies):
+            codes = torch.empty((T, cb), dtype=torch.uint8, device=dev)
+            sc = torch.empty(T, dtype=torch.float32, device=dev)
+            if qmode == 1:
+                kvq.kvq_encode_fp8(x, codes, sc)
+            else:
+                kvq.kvq_encode_tq4(x, mask, codes, sc)
+            sets.append((codes, sc, kr.clone() if copies > 1 else kr))
+        out = torch.empty((S, n_heads, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((S, n_heads), dtype=torch.float32, device=dev)
+        argsets = [kvq.attn_args(qmode, 0, offs, T, c, s_, k, ql, qr, workloads.SM_SCALE, out, lse,
+                                 sign_mask=mask if qmode == 2 else None) for (c, s_, k) in sets]
+        ws = kvq.alloc_workspace(argsets[0])
+        it = [0]
+
+        def full():
+            a = argsets[it[0] % copies]
+            it[0] += 1
+            kvq.kvq_decode_attn(a, ws)
+
+        def splits():
+            a = argsets[it[0] % copies]
+            it[0] += 1
+            kvq.kvq_decode_attn_stage(a, kvq.KVQ_STAGE_SPLITS, ws)
+
+        kvq.kvq_decode_attn_stage(argsets[0], kvq.KVQ_STAGE_PREP, ws)
+        ms_full = time_graph(torch, full, 2 * copies)
+        ms_split = time_graph(torch, splits, 2 * copies)
+        flops = 2.0 * n_heads * (576 + 512) * T
+        nbytes = T * (cb + 4 + 128)
+        tf = flops / (ms_split / 1000.0) / 1e12
+        res[name] = {"us_per_call": ms_full * 1000.0, "rows/s": T / (ms_full / 1000.0), "split_us": ms_split * 1000.0,
+                     "TFLOP/s": tf, "frac_mfma": tf / PEAK_T, "GB/s": nbytes / (ms_split / 1000.0) / 1e9,
+                     "rows": T, "seqs": S}
+        log(f"{name}: attention call {ms_full * 1000:.1f} us ({T / (ms_full / 1000.0):.3g} rows/s), split kernel "
+            f"{ms_split * 1000:.1f} us, {tf:.0f} TFLOP/s ({100 * tf / PEAK_T:.1f}% of MFMA)")
+
+    # a2 + a3-a8 on TQ4 rows: T = 32768, 128 heads, 16 copies
+    decode("tq4_decode_T32768_H128", 2, x_kv8, [x_kv8.shape[0]], 128, 1002, 16)
+    # ragged long-context fp8 decode: 32 sequences U[1024, 16384] + one of 131072
+    L = workloads.ragged_lengths()
+    xr = gpu_latents(torch, int(L.sum()), 1003, lengths=L)
+    decode("ragged_kv8_decode_33seq", 1, xr, L, 128, 1003, 1)
+    del xr
+    torch.cuda.empty_cache()
+
+    # a9 / a10: q4_0 bulk append of the 16 prefills, then the gather of everything
+    q = workloads.Q4Workload()
+    tok = int(q.prefill_off[-1])
+    kp = torch.zeros((q.n_cells, 8, 144), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    cache = kvq.q4_cache(kp, vp, torch.from_numpy(q.table).to(dev), 64)
+    ks = torch.from_numpy(q.k_prefill).to(dev)
+    vs = torch.from_numpy(q.v_prefill).to(dev)
+    pos0 = torch.from_numpy(q.pos0_prefill).to(dev)
+    off = torch.from_numpy(q.prefill_off).to(dev)
+    ms = time_graph(torch, lambda: kvq.kvq_append_q4_0(cache, pos0, off, tok, ks, vs), 5)
+    hbm("q4_0_append_bulk", tok * 8 * 2 * (1024 + 144), ms, {"tokens": tok})
+    del ks, vs
+    kd = torch.empty((tok, 8, 256), dtype=torch.int16, device=dev)
+    vd = torch.empty_like(kd)
+    ms = time_graph(torch, lambda: kvq.kvq_gather_q4_0(cache, off, tok, kd, vd), 5)
+    hbm("q4_0_gather", tok * 8 * 2 * (144 + 512), ms, {"tokens": tok})
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +248,8 @@ def main():
     ap.add_argument("--precision", type=int, default=0, choices=[0, 1])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-rows", action="store_true",
+                    help="skip the encoders, TQ4 decode, ragged decode and q4_0 measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 10 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -236,6 +387,10 @@ def main():
     log(f"step {ms_per_step * 1000:.1f} us, split kernel {kern_ms * 1000:.1f} us ({reps * n_copies} launches), "
         f"{tflops:.1f} TFLOP/s, {gbps:.0f} GB/s")
 
+    other = None
+    if not args.no_other_rows and qmode == 1 and args.precision == 0:
+        other = measure_other_rows(torch, kvq, workloads, x)
+
     # ---- CPU baseline: the oracle on the same decode step
     cpu = None
     if not args.no_cpu_baseline:
@@ -286,6 +441,7 @@ def main():
                 "bytes_per_launch": nbytes},
         "kernel_us": kern_ms * 1000.0,
         "cpu_baseline": cpu,
+        "other_rows": other,
     }
     print(json.dumps(line), flush=True)
 

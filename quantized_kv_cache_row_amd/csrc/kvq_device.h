@@ -138,6 +138,43 @@ __device__ __forceinline__ float fwht_xlane(float v, int lane, int m) {
     return (lane & m) ? (o - v) : (v + o);
 }
 
+// The value of lane ^ M, for a compile-time M, without the LDS crossbar:
+// DPP quad permutations (M = 1, 2), two row shifts and a select (M = 4), a row
+// rotation (M = 8), the gfx950 16- and 32-lane swaps (M = 16, 32).
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+    const int x = __float_as_int(v);
+    int r;
+    if constexpr (M == 1) {
+        r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm [1, 0, 3, 2]
+    } else if constexpr (M == 2) {
+        r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm [2, 3, 0, 1]
+    } else if constexpr (M == 4) {
+        const int up = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0xF, false);  // row_shl:4, lane i <- i + 4
+        const int dn = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, false);  // row_shr:4, lane i <- i - 4
+        r = (lane & 4) ? dn : up;
+    } else if constexpr (M == 8) {
+        r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+        r = (int)((lane & 16) ? p[0] : p[1]);
+    } else {
+        static_assert(M == 32, "xor_lane: M must be 1, 2, 4, 8, 16 or 32");
+        const auto p = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+        r = (int)((lane & 32) ? p[0] : p[1]);
+    }
+    return __int_as_float(r);
+}
+
+// FWHT stage with partner lane ^ M (as fwht_xlane, M a compile-time constant).
+// The lower lane keeps a + b, the upper b' = a - b; both as one fma with the
+// exact product (+-1) * v, so the sum is rounded once, as an add or subtract.
+template <int M>
+__device__ __forceinline__ float fwht_xlane_c(float v, int lane) {
+    const float o = xor_lane<M>(v, lane);
+    return __builtin_fmaf((lane & M) ? -1.0f : 1.0f, v, o);
+}
+
 // Largest-value selection on the key (|x|, x) with +0 above -0: the key is
 // order-preserving as an unsigned integer.
 __device__ __forceinline__ uint32_t absval_key(float x) {

@@ -12,6 +12,7 @@
 // stored as one 8-byte (fp8) or 4-byte (TQ4) store per lane, so every wave
 // instruction touches one contiguous span.
 #include <cstring>
+#include <type_traits>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -85,62 +86,107 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4(const float
     const int lane = threadIdx.x & (KVQ_WAVE - 1);
     const int j = lane & (L - 1);                      // lane within the row
     const int64_t rows_per_wave = KVQ_WAVE / L;
-    const int64_t row = ((int64_t)blockIdx.x * ENC_WAVES + (threadIdx.x >> 6)) * rows_per_wave + lane / L;
-    const bool valid = row < n_rows;
-    float v[8], sq[8];
-    if (valid) {
-        const float* xr = x + row * dim + 8 * j;
-        const float4 a = *reinterpret_cast<const float4*>(xr);
-        const float4 b = *reinterpret_cast<const float4*>(xr + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
+    // grid-stride over groups of rows_per_wave rows; the next group's inputs
+    // are loaded while this one is encoded
+    const int64_t stride = (int64_t)gridDim.x * ENC_WAVES * rows_per_wave;
+    const int64_t first = ((int64_t)blockIdx.x * ENC_WAVES + (threadIdx.x >> 6)) * rows_per_wave;
+    const uint32_t sm = sign_mask[j];  // byte j of the mask covers elements 8j .. 8j+7
+    auto load = [&](int64_t row, float (&v)[8]) {
+        if (row < n_rows) {
+            const float* xr = x + row * dim + 8 * j;
+            const float4 a = *reinterpret_cast<const float4*>(xr);
+            const float4 b = *reinterpret_cast<const float4*>(xr + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = 0.0f;
-    }
-    // radius^2: pairwise tree, leaves fl(x_i * x_i)
+            for (int i = 0; i < 8; i++) v[i] = 0.0f;
+        }
+    };
+    float nv[8];
+    load(first + lane / L, nv);
+    for (int64_t base = first; base < n_rows; base += stride) {
+        const int64_t row = base + lane / L;
+        const bool valid = row < n_rows;
+        float v[8], sq[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) sq[i] = v[i] * v[i];
+        for (int i = 0; i < 8; i++) v[i] = nv[i];
+        load(base + stride + lane / L, nv);
+        // radius^2: pairwise tree, leaves fl(x_i * x_i)
 #pragma unroll
-    for (int i = 0; i < 4; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
+        for (int i = 0; i < 8; i++) sq[i] = v[i] * v[i];
 #pragma unroll
-    for (int i = 0; i < 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
-    float r2 = sq[0] + sq[1];
-    for (int m = 1; m < L; m <<= 1) r2 = r2 + shfl_xor_f(r2, m);  // a + b == b + a exactly
-    const float rad = sqrt_rn(r2);
-    // random signs: byte j of the mask covers elements 8j .. 8j+7
-    const uint32_t sm = valid ? sign_mask[j] : 0u;
+        for (int i = 0; i < 4; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-        if ((sm >> i) & 1u) v[i] = -v[i];
-    // FWHT, unnormalized
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
+        for (int i = 0; i < 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
+        float r2 = sq[0] + sq[1];
+        // a + b == b + a exactly, so every lane of the row ends with the same sum
+        if (L > 1) r2 = r2 + xor_lane<1>(r2, lane);
+        if (L > 2) r2 = r2 + xor_lane<2>(r2, lane);
+        if (L > 4) r2 = r2 + xor_lane<4>(r2, lane);
+        if (L > 8) r2 = r2 + xor_lane<8>(r2, lane);
+        if (L > 16) r2 = r2 + xor_lane<16>(r2, lane);
+        if (L > 32) r2 = r2 + xor_lane<32>(r2, lane);
+        const float rad = sqrt_rn(r2);
+        // random signs
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            if (!(i & h)) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-    for (int m = 1; m < L; m <<= 1)
+            if ((sm >> i) & 1u) v[i] = -v[i];
+        // FWHT, unnormalized
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, m);
-    // bucketize against fl(t_k * r): idx = #{k : w > T_k}
-    float T[15];
+        for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-    for (int k = 0; k < 15; k++) T[k] = u2f(c_tq4_thresh[k]) * rad;
-    uint32_t packed = 0;
+            for (int i = 0; i < 8; i++)
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+        auto stage = [&](auto mc) {
+            constexpr int M = decltype(mc)::value;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        uint32_t idx = 0;
+            for (int i = 0; i < 8; i++) v[i] = fwht_xlane_c<M>(v[i], lane);
+        };
+        if (L == 64) {  // dim 512: all six lane stages, no per-stage branch
+            stage(std::integral_constant<int, 1>{});
+            stage(std::integral_constant<int, 2>{});
+            stage(std::integral_constant<int, 4>{});
+            stage(std::integral_constant<int, 8>{});
+            stage(std::integral_constant<int, 16>{});
+            stage(std::integral_constant<int, 32>{});
+        } else {
+            if (L > 1) stage(std::integral_constant<int, 1>{});
+            if (L > 2) stage(std::integral_constant<int, 2>{});
+            if (L > 4) stage(std::integral_constant<int, 4>{});
+            if (L > 8) stage(std::integral_constant<int, 8>{});
+            if (L > 16) stage(std::integral_constant<int, 16>{});
+            if (L > 32) stage(std::integral_constant<int, 32>{});
+        }
+        // bucketize against fl(t_k * r): idx = #{k : w > T_k}
+        float T[15];
 #pragma unroll
-        for (int k = 0; k < 15; k++) idx += (v[i] > T[k]) ? 1u : 0u;
-        packed |= idx << (4 * i);
-    }
-    if (valid) {
-        *reinterpret_cast<uint32_t*>(codes + row * (dim >> 1) + 4 * j) = packed;
-        if (j == 0) radii[row] = rad;
+        for (int k = 0; k < 15; k++) T[k] = u2f(c_tq4_thresh[k]) * rad;
+        // T is ascending, so #{k : w > T_k} is found by a branch-free binary search:
+        // four comparisons against T_7, then T_3 / T_11, then T_1 / T_5 / T_9 /
+        // T_13, then the even-indexed threshold below the interval found so far.
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float w = v[i];
+            const bool b3 = w > T[7];
+            const bool b2 = w > (b3 ? T[11] : T[3]);
+            const float t1 = b3 ? (b2 ? T[13] : T[9]) : (b2 ? T[5] : T[1]);
+            const bool b1 = w > t1;
+            const float e3 = b1 ? T[14] : T[12], e2 = b1 ? T[10] : T[8];
+            const float e1 = b1 ? T[6] : T[4], e0 = b1 ? T[2] : T[0];
+            const float t0 = b3 ? (b2 ? e3 : e2) : (b2 ? e1 : e0);
+            const uint32_t idx = (b3 ? 8u : 0u) + (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + ((w > t0) ? 1u : 0u);
+            packed |= idx << (4 * i);
+        }
+        if (valid) {
+            *reinterpret_cast<uint32_t*>(codes + row * (dim >> 1) + 4 * j) = packed;
+            if (j == 0) radii[row] = rad;
+        }
     }
 }
 
@@ -201,7 +247,9 @@ hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int dim, const uint
     if (n_rows == 0) return hipSuccess;
     const int64_t rows_per_wave = KVQ_WAVE / (dim / 8);
     const int64_t waves = (n_rows + rows_per_wave - 1) / rows_per_wave;
-    const dim3 grid((unsigned)((waves + ENC_WAVES - 1) / ENC_WAVES)), block(ENC_WAVES * KVQ_WAVE);
+    int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;
+    if (wgs > 4096) wgs = 4096;  // 16 waves per CU; the kernel strides over the rest
+    const dim3 grid((unsigned)wgs), block(ENC_WAVES * KVQ_WAVE);
     hipLaunchKernelGGL(k_encode_tq4, grid, block, 0, st, x, n_rows, dim, sign_mask, codes, radii);
     return hipGetLastError();
 }

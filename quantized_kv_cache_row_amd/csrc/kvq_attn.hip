@@ -40,9 +40,8 @@ constexpr int F32_HEADS = 8;      // fp32 path: heads per workgroup
 constexpr int MF_HEADS = 16;      // matrix-core path: heads per workgroup (one MFMA N block)
 constexpr int MF_WAVES = 4;       // matrix-core path: waves per workgroup, splitting the rows
 constexpr int MF_TILE = 32;       // rows per wave tile
-constexpr int QPACK_U4 = 144;     // uint4 per packed query (hi 64, lo 64, rope hi 8, rope lo 8)
-constexpr int QP_LO16 = 64;       // TQ4 path: lo term as 64 x 8 fp16
-constexpr int QP_RH = 128, QP_RL = 136;
+constexpr int QPACK_U4 = 80;      // uint4 per packed query (fp16 latent 64, rope hi 8, rope lo 8)
+constexpr int QP_RH = 64, QP_RL = 72;
 constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators are rescaled
 
@@ -382,8 +381,9 @@ __device__ __forceinline__ float pow2_scale_for(float max_abs, int log2_target) 
 //   TQ4: lane g loads 16 nibble bytes at 64 j + 16 g -> k-steps 4 j .. 4 j + 3
 //        cover latent dims 128 j + 32 g + 8 hh + e (ks = 4 j + hh);
 //   rope: k-step ks' in {0, 1} covers rope dims 32 ks' + 8 g + e.
-// One packed query (uint4 units): [0,64) hi (index 16 g + ks); TQ4 only: the
-// lo term at QP_LO16; rope hi (index 2 g + ks') at QP_RH, rope lo at QP_RL.
+// One packed query (uint4 units): [0,64) fp16 q * qs (index 16 g + ks; TQ4:
+// within each 8 dims in the decoder's order 0 2 4 6 1 3 5 7); rope hi (index
+// 2 g + ks') at QP_RH, rope lo at QP_RL.
 template <int QMODE>
 __global__ __launch_bounds__(256) void k_qprep(kvq_attn_args a, Plan p) {
     const int lane = threadIdx.x & 63;
@@ -421,20 +421,17 @@ __global__ __launch_bounds__(256) void k_qprep(kvq_attn_args a, Plan p) {
     for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, fabsf(v[i]));
     qmax = wave_max(qmax);
     const float qs = pow2_scale_for(qmax, 8);  // max |q| * qs in [256, 512)
-    uint32_t hw[4], lw[4];
+    // TQ4: the decoder's order within each 8 dims, 0 2 4 6 1 3 5 7
+    constexpr int ord[2][8] = {{0, 1, 2, 3, 4, 5, 6, 7}, {0, 2, 4, 6, 1, 3, 5, 7}};
+    const int* o = ord[QMODE == KVQ_QMODE_TQ4 ? 1 : 0];
+    uint32_t hw[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float f0 = v[2 * i] * qs, f1 = v[2 * i + 1] * qs;
-        const float h0 = (float)(_Float16)f0, h1 = (float)(_Float16)f1;
-        hw[i] = pack_f16x2(h0, h1);
-        lw[i] = pack_f16x2(f0 - h0, f1 - h1);
-    }
+    for (int i = 0; i < 4; i++) hw[i] = pack_f16x2(v[o[2 * i]] * qs, v[o[2 * i + 1]] * qs);
     int g, ks;
     if (QMODE == KVQ_QMODE_FP8) { g = (lane & 7) >> 1; ks = 2 * (lane >> 3) + (lane & 1); }
     else { g = (lane & 15) >> 2; ks = 4 * (lane >> 4) + (lane & 3); }
     uint4* dst = p.q_pack + row * QPACK_U4;
     dst[16 * g + ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    if (QMODE == KVQ_QMODE_TQ4) dst[QP_LO16 + 16 * g + ks] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     if (lane < 8) {  // rope dims 8 lane .. + 7: k-step lane / 4, lane group lane % 4
         const float* r = a.q_rope + ((int64_t)s * a.n_heads + (valid ? h : 0)) * DR + 8 * lane;
         uint32_t rh[4], rl[4];
@@ -481,9 +478,10 @@ __device__ __forceinline__ Tq4Lut make_tq4_lut() {
     return t;
 }
 
-// 8 nibble indices (element k = nibble k of x) -> 8 fp16 codebook levels.  The
-// codebook is symmetric: index i >= 8 is +level[i], index i < 8 is
-// -level[15 - i]; the magnitude comes from a byte table lookup (v_perm).
+// 8 nibble indices (element k = nibble k of x) -> 8 fp16 codebook levels, in
+// the order 0 2 4 6 1 3 5 7.  The codebook is symmetric: index i >= 8 is
+// +level[i], index i < 8 is -level[15 - i]; the magnitude comes from a byte
+// table lookup (v_perm).
 __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
     const uint32_t neg = ((x >> 3) & 0x11111111u) ^ 0x11111111u;  // 1 where index < 8
     const uint32_t m = (x & 0x77777777u) ^ (neg * 7u);                // magnitude index
@@ -492,250 +490,13 @@ __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
     const uint32_t lo_o = __builtin_amdgcn_perm(t.lo47, t.lo03, mo);
     const uint32_t hi_e = __builtin_amdgcn_perm(t.hi47, t.hi03, me) | ((neg & 0x01010101u) << 7);
     const uint32_t hi_o = __builtin_amdgcn_perm(t.hi47, t.hi03, mo) | (((neg >> 4) & 0x01010101u) << 7);
-    const uint32_t ae = __builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u);  // e0 | e2 << 16
-    const uint32_t ao = __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u);  // o0 | o2 << 16
-    const uint32_t be = __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u);  // e4 | e6 << 16
-    const uint32_t bo = __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u);  // o4 | o6 << 16
-    return make_uint4(__builtin_amdgcn_perm(ao, ae, 0x05040100u), __builtin_amdgcn_perm(ao, ae, 0x07060302u),
-                      __builtin_amdgcn_perm(bo, be, 0x05040100u), __builtin_amdgcn_perm(bo, be, 0x07060302u));
+    return make_uint4(__builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u),   // elements 0, 2
+                      __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u),   // 4, 6
+                      __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u),   // 1, 3
+                      __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u));  // 5, 7
 }
 
 constexpr int XS = DL + 16;  // halfwords per LDS tile row: rows 32 bytes apart modulo 128
-
-// Split kernel.  Work item = (T-chunk, group of 16 heads); the items are dealt
-// to XCDs in contiguous runs so the head groups of a chunk share one L2.  The
-// 4 waves of a workgroup take consecutive quarters of the chunk (tiles of 32
-// rows) for the same 16 heads, each with a private LDS tile:
-//   score:  S^T (16 rows x 16 heads) += X(rows, k) q^T -- X straight from the
-//           loaded codes (converted in registers), q hi and lo;
-//   PV:     O^T (16 dims x 16 heads) += X^T P'^T -- X^T from the row-major LDS
-//           tile via ds_read_b64_tr_b16 (lane (g, p) gets rows 4 g .. 4 g + 3 and
-//           16 + 4 g .. + 3 of column p, the k order the score accumulators
-//           already hold P in).
-// The waves' (m, l, O) are merged in LDS; one partial per (chunk, head).
-template <int QMODE>
-__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma(kvq_attn_args a, Plan p) {
-    __shared__ __align__(16) uint16_t tile[MF_WAVES][MF_TILE][XS];
-    __shared__ float red_s[MF_WAVES];
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int g = lane >> 4, n = lane & 15;
-    // workgroups are dealt round-robin to the XCDs: chunk c goes to XCD c % 8 and
-    // its head groups are consecutive there, so they share that XCD's L2
-    const int64_t local = blockIdx.x / N_XCD;
-    const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
-    const int hg = (int)(local % p.n_groups);
-    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
-    const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
-    const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
-    const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
-    const int64_t r1 = min(seq_hi, r0 + (int64_t)p.split_rows);
-    const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
-    const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
-    const int head = hg * MF_HEADS + n;  // may exceed n_heads (padded query is zero)
-    const float rho_mul = QMODE == KVQ_QMODE_TQ4 ? INV_SQRT_DL : 1.0f;
-    constexpr int CB = QMODE == KVQ_QMODE_FP8 ? DL : DL / 2;  // code bytes per row
-
-    // ---- per-split probability scale rs from the largest row scale of the chunk
-    float rmax = 0.0f;
-    for (int64_t t = r0 + tid; t < r1; t += MF_WAVES * 64) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
-    rmax = wave_max(rmax);
-    if (lane == 0) red_s[wave] = rmax;
-    __syncthreads();
-    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-    const float rs = pow2_scale_for(rmax * rho_mul, -1);  // max rho * rs in [0.5, 1)
-
-    // ---- query operands
-    const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
-    uint4 qh[16], ql[16], rh[2], rl[2];
-#pragma unroll
-    for (int k = 0; k < 16; k++) {
-        qh[k] = qp[16 * g + k];
-        ql[k] = qp[QP_LO16 + 16 * g + k];
-    }
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        rh[k] = qp[QP_RH + 2 * g + k];
-        rl[k] = qp[QP_RL + 2 * g + k];
-    }
-    const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
-    Tq4Lut lut{};
-    if (QMODE == KVQ_QMODE_TQ4) lut = make_tq4_lut();
-
-    const float c2 = a.sm_scale * LOG2E;  // scores in log2 units
-    f32x4_t acc_o[32];
-#pragma unroll
-    for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_part = 0.0f;
-    uint16_t(*xs)[XS] = tile[wave];
-
-    for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        // ---- scores S^T (rows x heads), two 16-row blocks; rows >= nt are zero
-        f32x4_t sl[2], sr[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const int row = 16 * rb + n;
-            const bool rok = row < nt;
-            const uint8_t* crow = a.codes + (t0 + (rok ? row : 0)) * CB + 16 * g;
-            const uint16_t* krow = a.k_rope + (t0 + (rok ? row : 0)) * DR + 8 * g;
-            uint4 raw[8];
-#pragma unroll
-            for (int j = 0; j < CB / 64; j++)
-                raw[j] = rok ? *reinterpret_cast<const uint4*>(crow + 64 * j) : make_uint4(0, 0, 0, 0);
-            uint4 kr[2];
-#pragma unroll
-            for (int k = 0; k < 2; k++) kr[k] = rok ? *reinterpret_cast<const uint4*>(krow + 32 * k) : make_uint4(0, 0, 0, 0);
-            sl[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            sr[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            if (QMODE == KVQ_QMODE_FP8) {
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const uint4 x0 = e4m3x8_to_f16x8(raw[j].x, raw[j].y);
-                    const uint4 x1 = e4m3x8_to_f16x8(raw[j].z, raw[j].w);
-                    *reinterpret_cast<uint4*>(&xs[row][64 * j + 16 * g]) = x0;
-                    *reinterpret_cast<uint4*>(&xs[row][64 * j + 16 * g + 8]) = x1;
-                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x0), as_f16x8(qh[2 * j]), sl[rb], 0, 0, 0);
-                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x0), as_f16x8(ql[2 * j]), sl[rb], 0, 0, 0);
-                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x1), as_f16x8(qh[2 * j + 1]), sl[rb], 0, 0, 0);
-                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(x1), as_f16x8(ql[2 * j + 1]), sl[rb], 0, 0, 0);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-                    for (int hh = 0; hh < 4; hh++) {
-                        const uint4 xv = tq4x8_to_f16x8(w[hh], lut);
-                        *reinterpret_cast<uint4*>(&xs[row][128 * j + 32 * g + 8 * hh]) = xv;
-                        sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xv), as_f16x8(qh[4 * j + hh]), sl[rb], 0, 0, 0);
-                        sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xv), as_f16x8(ql[4 * j + hh]), sl[rb], 0, 0, 0);
-                    }
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < 2; k++) {
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
-            }
-        }
-        // lane (g, n): rows 16 rb + 4 g + r of head n
-        float sc[2][4], rr[2][4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const int tb = 16 * rb + 4 * g;
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const bool ok = tb + r < nt;
-                rr[rb][r] = ok ? a.row_scale[t0 + tb + r] * rho_mul : 0.0f;
-                const float v = ok ? c2 * (rr[rb][r] * (sl[rb][r] * qinv) + sr[rb][r]) : -INFINITY;
-                sc[rb][r] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // lazy rescaling: keep a stale running max unless this tile exceeds it by
-        // more than 2^8 (then p <= 256 stays exact enough in fp32 / fp16)
-        const bool bump = tmax > m_run + LAZY_LOG2;
-        const float m_new = bump ? tmax : m_run;
-        const float alpha = bump ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new)) : 1.0f;
-        const bool any_bump = __any(bump);
-        float psum = 0.0f;
-        uint32_t pb[4];
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            float pw[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float pv = (sc[rb][r] == -INFINITY) ? 0.0f : exp2f(sc[rb][r] - m_new);
-                psum += pv;
-                pw[r] = pv * (rr[rb][r] * rs);
-            }
-            pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
-            pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
-        }
-        l_part = l_part * alpha + psum;
-        m_run = m_new;
-        if (any_bump) {
-#pragma unroll
-            for (int mb = 0; mb < 32; mb++) acc_o[mb] = acc_o[mb] * alpha;
-        }
-        const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
-        // the tile rows written above are read back transposed by other lanes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- PV: source lane (g, n) points at row t0' + n / 4, column 16 mb + 4 (n % 4)
-        const int trow = 4 * g + (n >> 2), tcol = 4 * (n & 3);
-#pragma unroll
-        for (int mb = 0; mb < 32; mb++) {
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)&xs[trow][16 * mb + tcol]);
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)&xs[16 + trow][16 * mb + tcol]);
-            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-            const f16x8_t aop = as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-            acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[mb], 0, 0, 0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    // ---- merge the waves' states in LDS (each wave's tile holds its own state)
-    l_part += __shfl_xor(l_part, 16, 64);
-    l_part += __shfl_xor(l_part, 32, 64);
-    constexpr int OS = DL + 4;  // floats per stored head row (banks shifted per row)
-    float* st = reinterpret_cast<float*>(&tile[wave][0][0]);  // [16][OS] O, then m[16], l[16]
-    __syncthreads();  // every wave is done reading its tile
-#pragma unroll
-    for (int mb = 0; mb < 32; mb++)
-        *reinterpret_cast<float4*>(st + n * OS + 16 * mb + 4 * g) =
-            make_float4(acc_o[mb][0], acc_o[mb][1], acc_o[mb][2], acc_o[mb][3]);
-    if (g == 0) {
-        st[MF_HEADS * OS + n] = m_run;
-        st[MF_HEADS * OS + MF_HEADS + n] = l_part;
-    }
-    __syncthreads();
-    {
-        const int hh = tid >> 4;             // head within the group
-        const int d0 = (tid & 15) * 32;      // 32 dims per thread
-        float mw[MF_WAVES], M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < MF_WAVES; w++) {
-            mw[w] = reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + hh];
-            M = fmaxf(M, mw[w]);
-        }
-        float sw[MF_WAVES], L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < MF_WAVES; w++) {
-            sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
-            L += sw[w] * reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + MF_HEADS + hh];
-        }
-        const int h = hg * MF_HEADS + hh;
-        if (h < a.n_heads) {
-            float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
-            const float rsinv = 1.0f / rs;  // exact
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-                for (int w = 0; w < MF_WAVES; w++) {
-                    const float4 v =
-                        *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&tile[w][0][0]) + hh * OS + d0 + 4 * q);
-                    o.x += sw[w] * v.x; o.y += sw[w] * v.y; o.z += sw[w] * v.z; o.w += sw[w] * v.w;
-                }
-                o.x *= rsinv; o.y *= rsinv; o.z *= rsinv; o.w *= rsinv;
-                *reinterpret_cast<float4*>(dst + 4 * q) = o;
-            }
-            if ((tid & 15) == 0) {
-                p.part_m[c * a.n_heads + h] = M;  // log2 units
-                p.part_l[c * a.n_heads + h] = L;
-            }
-        }
-    }
-}
 
 // fp8 split kernel (raw-tile variant).  Same work items and wave split as
 // k_attn_mfma, but every wave streams its rows' raw e4m3 codes into a
@@ -1178,6 +939,252 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     }
 }
 
+// TQ4 split kernel.  Work item = (T-chunk, group of 16 heads); the items are
+// dealt to XCDs in contiguous runs so the head groups of a chunk share one L2.
+// The 4 waves of a workgroup take consecutive quarters of the chunk (tiles of
+// 32 rows) for the same 16 heads, each with a private LDS tile:
+//   score:  S^T (16 rows x 16 heads) += X(rows, k) q^T -- X decoded from the
+//           nibbles in registers (the next tile's codes are loaded while this
+//           one is processed) and written to the LDS tile as fp16;
+//   PV:     O^T (16 dims x 16 heads) += X^T P'^T -- X^T from the row-major LDS
+//           tile via ds_read_b64_tr_b16 (lane (g, p) gets rows 4 g .. 4 g + 3 and
+//           16 + 4 g .. + 3 of column p, the k order the score accumulators
+//           already hold P in).
+// Within each 8 dims the decoder emits the order 0 2 4 6 1 3 5 7 (fewer byte
+// permutes); the packed query follows it, and the output dims are put back
+// in order when the accumulators are stored.  Softmax: fixed per-wave
+// reference as in the fp8 kernel (a tile more than 2^8 above it raises the
+// reference and the wave starts its rows again), probabilities times
+// rho * rs with rs from the chunk's largest radius, so the accumulators are
+// never rescaled inside the loop.  The waves' (m, l, O) are merged in LDS; one
+// partial per (chunk, head).
+__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a, Plan p) {
+    __shared__ __align__(16) uint16_t tile[MF_WAVES][MF_TILE][XS];
+    __shared__ float red_s[MF_WAVES];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int64_t local = blockIdx.x / N_XCD;
+    const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
+    const int hg = (int)(local % p.n_groups);
+    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
+    const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
+    const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
+    const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
+    const int64_t r1 = min(seq_hi, r0 + (int64_t)p.split_rows);
+    const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
+    const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
+    const int head = hg * MF_HEADS + n;  // may exceed n_heads (padded query is zero)
+    constexpr int CB = DL / 2;           // code bytes per row
+
+    // ---- per-split probability scale rs from the largest row scale of the chunk
+    float rmax = 0.0f;
+    for (int64_t t = r0 + tid; t < r1; t += MF_WAVES * 64) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
+    rmax = wave_max(rmax);
+    if (lane == 0) red_s[wave] = rmax;
+    __syncthreads();
+    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+    const float rs = pow2_scale_for(rmax * INV_SQRT_DL, -1);  // max rho * rs in [0.5, 1)
+
+    // ---- query operands (rotated, one fp16 term scaled by a power of two)
+    const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
+    uint4 qh[16], rh[2], rl[2];
+#pragma unroll
+    for (int k = 0; k < 16; k++) qh[k] = qp[16 * g + k];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        rh[k] = qp[QP_RH + 2 * g + k];
+        rl[k] = qp[QP_RL + 2 * g + k];
+    }
+    const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
+    const Tq4Lut lut = make_tq4_lut();
+    const float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
+    const float c2 = a.sm_scale * LOG2E;         // rope scores (the rope query is unscaled)
+    uint16_t(*xs)[XS] = tile[wave];
+
+    // next-tile registers: lane (g, n) loads row 16 rb + n (codes at 64 j + 16 g,
+    // rope at 8 g + 32 k) and the scales of rows 16 rb + 4 g .. + 3.  Every load
+    // is issued (rows past the tile re-read its last row, masked in the
+    // softmax): a guarded load would be a branch with a wait for all loads.
+    uint4 nraw[2][4], nkr[2][2];
+    float nrho[2][4];
+    auto load_tile = [&](int64_t t0) __attribute__((always_inline)) {
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const int row = min(16 * rb + n, nt - 1);
+            const uint8_t* crow = a.codes + (t0 + row) * CB + 16 * g;
+            const uint16_t* krow = a.k_rope + (t0 + row) * DR + 8 * g;
+#pragma unroll
+            for (int j = 0; j < 4; j++) nraw[rb][j] = *reinterpret_cast<const uint4*>(crow + 64 * j);
+#pragma unroll
+            for (int k = 0; k < 2; k++) nkr[rb][k] = *reinterpret_cast<const uint4*>(krow + 32 * k);
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                nrho[rb][r] = a.row_scale[t0 + min(16 * rb + 4 * g + r, nt - 1)] * INV_SQRT_DL;
+        }
+    };
+
+    f32x4_t acc_o[32];
+    float m_run = -INFINITY, l_part = 0.0f;
+    for (;;) {
+#pragma unroll
+    for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    l_part = 0.0f;
+    bool again = false;
+    if (w0 < w1) load_tile(w0);
+    for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
+        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
+        uint4 raw[2][4], kr[2][2];
+        float rr[2][4];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) raw[rb][j] = nraw[rb][j];
+#pragma unroll
+            for (int k = 0; k < 2; k++) kr[rb][k] = nkr[rb][k];
+#pragma unroll
+            for (int r = 0; r < 4; r++) rr[rb][r] = nrho[rb][r];
+        }
+        if (t0 + MF_TILE < w1) load_tile(t0 + MF_TILE);
+        // ---- decode to fp16 (LDS tile row 16 rb + n) and the scores S^T
+        f32x4_t sl[2], sr[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const int row = 16 * rb + n;
+            sl[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            sr[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint32_t w[4] = {raw[rb][j].x, raw[rb][j].y, raw[rb][j].z, raw[rb][j].w};
+#pragma unroll
+                for (int hh = 0; hh < 4; hh++) {
+                    const uint4 xv = tq4x8_to_f16x8(w[hh], lut);
+                    *reinterpret_cast<uint4*>(&xs[row][128 * j + 32 * g + 8 * hh]) = xv;
+                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xv), as_f16x8(qh[4 * j + hh]), sl[rb], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
+                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
+            }
+        }
+        // ---- softmax: lane (g, n) holds rows 16 rb + 4 g + r of head n
+        float sc[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const bool ok = 16 * rb + 4 * g + r < nt;
+                if (!ok) rr[rb][r] = 0.0f;
+                const float v = ok ? fmaf(rr[rb][r] * k1, sl[rb][r], c2 * sr[rb][r]) : -INFINITY;
+                sc[rb][r] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        tmax = max_xor16_xor32(tmax);
+        if (m_run == -INFINITY) m_run = tmax;  // first tile: row 0 is valid
+        if (__any(tmax > m_run + LAZY_LOG2)) {
+            // raise the reference past this tile and start the rows again
+            m_run = fmaxf(m_run, tmax);
+            again = true;
+            break;
+        }
+        float psum = 0.0f;
+        uint32_t pb[4];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            float pw[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float pv = __builtin_amdgcn_exp2f(sc[rb][r] - m_run);  // masked rows: 0
+                psum += pv;
+                pw[r] = pv * (rr[rb][r] * rs);
+            }
+            pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
+            pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
+        }
+        l_part += psum;
+        const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
+        // the tile rows written above are read back transposed by other lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // ---- PV: source lane (g, n) points at row t0' + n / 4, column 16 mb + 4 (n % 4)
+        const int trow = 4 * g + (n >> 2), tcol = 4 * (n & 3);
+#pragma unroll
+        for (int mb = 0; mb < 32; mb++) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)&xs[trow][16 * mb + tcol]);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)&xs[16 + trow][16 * mb + tcol]);
+            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+            const f16x8_t aop = as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+            acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[mb], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (!again) break;
+    }
+    // ---- merge the waves' states in LDS (each wave's tile holds its own state)
+    l_part += __shfl_xor(l_part, 16, 64);
+    l_part += __shfl_xor(l_part, 32, 64);
+    constexpr int OS = DL + 4;  // floats per stored head row (banks shifted per row)
+    float* st = reinterpret_cast<float*>(&tile[wave][0][0]);  // [16][OS] O, then m[16], l[16]
+    __syncthreads();  // every wave is done reading its tile
+    // accumulator element r of block mb is tile column 16 mb + 4 g + r, which
+    // holds dim 16 mb + 8 (g / 2) + g % 2 + 2 r
+#pragma unroll
+    for (int mb = 0; mb < 32; mb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) st[n * OS + 16 * mb + 8 * (g >> 1) + (g & 1) + 2 * r] = acc_o[mb][r];
+    if (g == 0) {
+        st[MF_HEADS * OS + n] = m_run;
+        st[MF_HEADS * OS + MF_HEADS + n] = l_part;
+    }
+    __syncthreads();
+    {
+        const int hh = tid >> 4;             // head within the group
+        const int d0 = (tid & 15) * 32;      // 32 dims per thread
+        float mw[MF_WAVES], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MF_WAVES; w++) {
+            mw[w] = reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + hh];
+            M = fmaxf(M, mw[w]);
+        }
+        float sw[MF_WAVES], L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < MF_WAVES; w++) {
+            sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
+            L += sw[w] * reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + MF_HEADS + hh];
+        }
+        const int h = hg * MF_HEADS + hh;
+        if (h < a.n_heads) {
+            float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
+            const float rsinv = 1.0f / rs;  // exact
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                for (int w = 0; w < MF_WAVES; w++) {
+                    const float4 v =
+                        *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&tile[w][0][0]) + hh * OS + d0 + 4 * q);
+                    o.x += sw[w] * v.x; o.y += sw[w] * v.y; o.z += sw[w] * v.z; o.w += sw[w] * v.w;
+                }
+                o.x *= rsinv; o.y *= rsinv; o.z *= rsinv; o.w *= rsinv;
+                *reinterpret_cast<float4*>(dst + 4 * q) = o;
+            }
+            if ((tid & 15) == 0) {
+                p.part_m[c * a.n_heads + h] = M;  // log2 units
+                p.part_l[c * a.n_heads + h] = L;
+            }
+        }
+    }
+}
+
 // ---- 3. merge --------------------------------------------------------------------------------
 // NDH workgroups per (sequence, head), each over DL / NDH output dims (TQ4: the
 // whole row, which the un-rotation needs).  A thread owns one float4 column and
@@ -1328,7 +1335,7 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
                 else hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p, qsrc);
             } else {
                 const dim3 grid((unsigned)(p.chunks_per_xcd * N_XCD * p.n_groups));
-                if (tq4) hipLaunchKernelGGL(k_attn_mfma<KVQ_QMODE_TQ4>, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+                if (tq4) hipLaunchKernelGGL(k_attn_mfma_tq4, grid, dim3(MF_WAVES * 64), 0, st, a, p);
                 else hipLaunchKernelGGL(k_attn_mfma_fp8, grid, dim3(MF_WAVES * 64), 0, st, a, p);
             }
             break;

@@ -15,11 +15,13 @@
 // un-rotated by R^T after the merge).  The latent rows are never rebuilt.
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
-//   0. k_plan       -- per-sequence T-split counts -> prefix (ragged batches);
-//   1. k_qprep /    -- matrix-core path: the query operands (TQ4: rotated), scaled
-//      k_qrot          and split into 16-bit terms; fp32 path, TQ4: R q in fp32;
-//   2. k_attn_*     -- online softmax over every T-split, partial (m, l, O);
-//   3. k_merge      -- combine the splits, TQ4 un-rotation, write out / lse.
+//   prep  -- fp32 check path: k_plan (per-sequence T-split counts -> prefix)
+//            and, TQ4, k_qrot (R q in fp32); matrix-core path, TQ4:
+//            k_qprep_tq4 (R q as fp16 operands).  The matrix-core split
+//            kernels plan their chunk themselves, the fp8 one also prepares
+//            its query;
+//   split -- k_attn_*: online softmax over every T-split, partial (m, l, O);
+//   merge -- k_merge: combine the splits, TQ4 un-rotation, write out / lse.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_codebook.inc"
@@ -40,7 +42,8 @@ constexpr int F32_HEADS = 8;      // fp32 path: heads per workgroup
 constexpr int MF_HEADS = 16;      // matrix-core path: heads per workgroup (one MFMA N block)
 constexpr int MF_WAVES = 4;       // matrix-core path: waves per workgroup, splitting the rows
 constexpr int MF_TILE = 32;       // rows per wave tile
-constexpr int QPACK_U4 = 80;      // uint4 per packed query (fp16 latent 64, rope hi 8, rope lo 8)
+constexpr int TQ4_HEADS = 64;    // TQ4 matrix-core path: heads per workgroup (4 waves x 16)
+constexpr int QPACK_U4 = 80;      // TQ4: uint4 per prepared query (fp16 latent 64, rope hi 8, rope lo 8)
 constexpr int QP_RH = 64, QP_RL = 72;
 constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators are rescaled
@@ -48,8 +51,8 @@ constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators a
 struct Plan {
     int64_t* chunk_prefix;  // [n_seqs + 1]
     float* q_rot;           // fp32 path, TQ4: [n_seqs][H][512]
-    uint4* q_pack;          // matrix-core path: [n_seqs][H padded to 16][QPACK_U4]
-    float* q_inv;           // matrix-core path: [n_seqs][H padded to 16]
+    uint4* q_pack;          // matrix-core path, TQ4: [n_seqs][H padded to 64][QPACK_U4]
+    float* q_inv;           // matrix-core path, TQ4: [n_seqs][H padded to 64]
     float* part_m;          // [max_chunks][H]
     float* part_l;          // [max_chunks][H]
     float* part_o;          // [max_chunks][H][512]
@@ -65,6 +68,16 @@ struct Plan {
 
 int auto_split_rows(const kvq_attn_args& a) {
     if (a.precision == KVQ_PREC_FP32) return 512;
+    if (a.qmode == KVQ_QMODE_TQ4) {
+        // one workgroup per compute unit over all splits and groups of 64 heads,
+        // whole tiles, at least 8 tiles per split
+        const int64_t groups = (a.n_heads + TQ4_HEADS - 1) / TQ4_HEADS;
+        int64_t split = (a.total_rows * groups + 255) / 256;
+        if (split < 8 * MF_TILE) split = 8 * MF_TILE;
+        split = (split + MF_TILE - 1) / MF_TILE * MF_TILE;
+        if (split > (1 << 24)) split = 1 << 24;
+        return (int)split;
+    }
     // Large splits keep the partial states small next to the KV bytes they
     // summarize (a partial is 128 heads x 2 KB per split); about two
     // workgroups per compute unit over all splits and head groups.
@@ -80,7 +93,7 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     Plan p{};
     p.split_rows = a.split_rows > 0 ? a.split_rows : auto_split_rows(a);
     const bool f32 = a.precision == KVQ_PREC_FP32;
-    p.heads_per_group = f32 ? F32_HEADS : MF_HEADS;
+    p.heads_per_group = f32 ? F32_HEADS : (a.qmode == KVQ_QMODE_TQ4 ? TQ4_HEADS : MF_HEADS);
     p.n_groups = (a.n_heads + p.heads_per_group - 1) / p.heads_per_group;
     p.heads_padded = p.n_groups * p.heads_per_group;
     // sum_s max(1, ceil(T_s / split)) over T_s summing to at most total_rows is at
@@ -98,10 +111,10 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
         off = align(off + bytes);
         return q;
     };
-    const int64_t rows_q = (int64_t)a.n_seqs * p.heads_padded;
     p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
     if (f32 && a.qmode == KVQ_QMODE_TQ4) p.q_rot = (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
-    if (!f32) {
+    if (!f32 && a.qmode == KVQ_QMODE_TQ4) {
+        const int64_t rows_q = (int64_t)a.n_seqs * p.heads_padded;
         p.q_pack = (uint4*)take(sizeof(uint4) * rows_q * QPACK_U4);
         p.q_inv = (float*)take(sizeof(float) * rows_q);
     }
@@ -374,81 +387,6 @@ __device__ __forceinline__ float pow2_scale_for(float max_abs, int log2_target) 
     return u2f((uint32_t)(k + 127) << 23);
 }
 
-// Query operand layout, per lane group g (MFMA k-slot 8 g .. 8 g + 7 of each
-// k-step ks), following the row bytes each lane loads:
-//   fp8: lane g loads 16 code bytes at 64 j + 16 g -> k-steps 2 j, 2 j + 1
-//        cover latent dims 64 j + 16 g + 8 hh + e  (ks = 2 j + hh);
-//   TQ4: lane g loads 16 nibble bytes at 64 j + 16 g -> k-steps 4 j .. 4 j + 3
-//        cover latent dims 128 j + 32 g + 8 hh + e (ks = 4 j + hh);
-//   rope: k-step ks' in {0, 1} covers rope dims 32 ks' + 8 g + e.
-// One packed query (uint4 units): [0,64) fp16 q * qs (index 16 g + ks; TQ4:
-// within each 8 dims in the decoder's order 0 2 4 6 1 3 5 7); rope hi (index
-// 2 g + ks') at QP_RH, rope lo at QP_RL.
-template <int QMODE>
-__global__ __launch_bounds__(256) void k_qprep(kvq_attn_args a, Plan p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + h
-    if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
-    const int s = (int)(row / p.heads_padded), h = (int)(row % p.heads_padded);
-    const bool valid = h < a.n_heads;
-    const float* src = a.q_lat + ((int64_t)s * a.n_heads + (valid ? h : 0)) * DL + 8 * lane;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = valid ? src[i] : 0.0f;
-    if (QMODE == KVQ_QMODE_TQ4) {  // q~ = H D q / sqrt(512)
-        const uint32_t sm = a.sign_mask[lane];
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            if ((sm >> i) & 1u) v[i] = -v[i];
-#pragma unroll
-        for (int hh = 1; hh < 8; hh <<= 1)
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                if (!(i & hh)) {
-                    const float x = v[i], y = v[i + hh];
-                    v[i] = x + y;
-                    v[i + hh] = x - y;
-                }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1)
-#pragma unroll
-            for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, m);
-#pragma unroll
-        for (int i = 0; i < 8; i++) v[i] *= INV_SQRT_DL;
-    }
-    float qmax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) qmax = fmaxf(qmax, fabsf(v[i]));
-    qmax = wave_max(qmax);
-    const float qs = pow2_scale_for(qmax, 8);  // max |q| * qs in [256, 512)
-    // TQ4: the decoder's order within each 8 dims, 0 2 4 6 1 3 5 7
-    constexpr int ord[2][8] = {{0, 1, 2, 3, 4, 5, 6, 7}, {0, 2, 4, 6, 1, 3, 5, 7}};
-    const int* o = ord[QMODE == KVQ_QMODE_TQ4 ? 1 : 0];
-    uint32_t hw[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) hw[i] = pack_f16x2(v[o[2 * i]] * qs, v[o[2 * i + 1]] * qs);
-    int g, ks;
-    if (QMODE == KVQ_QMODE_FP8) { g = (lane & 7) >> 1; ks = 2 * (lane >> 3) + (lane & 1); }
-    else { g = (lane & 15) >> 2; ks = 4 * (lane >> 4) + (lane & 3); }
-    uint4* dst = p.q_pack + row * QPACK_U4;
-    dst[16 * g + ks] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    if (lane < 8) {  // rope dims 8 lane .. + 7: k-step lane / 4, lane group lane % 4
-        const float* r = a.q_rope + ((int64_t)s * a.n_heads + (valid ? h : 0)) * DR + 8 * lane;
-        uint32_t rh[4], rl[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float f0 = valid ? r[2 * i] : 0.0f, f1 = valid ? r[2 * i + 1] : 0.0f;
-            const float b0 = u2f(f32_to_bf16_rne(f0) << 16), b1 = u2f(f32_to_bf16_rne(f1) << 16);
-            rh[i] = pack_bf16x2(b0, b1);
-            rl[i] = pack_bf16x2(f0 - b0, f1 - b1);
-        }
-        const int gg = lane & 3, kk = lane >> 2;
-        dst[QP_RH + 2 * gg + kk] = make_uint4(rh[0], rh[1], rh[2], rh[3]);
-        dst[QP_RL + 2 * gg + kk] = make_uint4(rl[0], rl[1], rl[2], rl[3]);
-    }
-    if (lane == 0) p.q_inv[row] = 1.0f / qs;  // exact
-}
-
 // Two e4m3 codes (byte pair HI of w) -> two fp16, exact (hardware conversion, scale 1).
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
@@ -478,10 +416,9 @@ __device__ __forceinline__ Tq4Lut make_tq4_lut() {
     return t;
 }
 
-// 8 nibble indices (element k = nibble k of x) -> 8 fp16 codebook levels, in
-// the order 0 2 4 6 1 3 5 7.  The codebook is symmetric: index i >= 8 is
-// +level[i], index i < 8 is -level[15 - i]; the magnitude comes from a byte
-// table lookup (v_perm).
+// 8 nibble indices (element k = nibble k of x) -> 8 fp16 codebook levels.  The
+// codebook is symmetric: index i >= 8 is +level[i], index i < 8 is
+// -level[15 - i]; the magnitude comes from a byte table lookup (v_perm).
 __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
     const uint32_t neg = ((x >> 3) & 0x11111111u) ^ 0x11111111u;  // 1 where index < 8
     const uint32_t m = (x & 0x77777777u) ^ (neg * 7u);                // magnitude index
@@ -490,13 +427,14 @@ __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
     const uint32_t lo_o = __builtin_amdgcn_perm(t.lo47, t.lo03, mo);
     const uint32_t hi_e = __builtin_amdgcn_perm(t.hi47, t.hi03, me) | ((neg & 0x01010101u) << 7);
     const uint32_t hi_o = __builtin_amdgcn_perm(t.hi47, t.hi03, mo) | (((neg >> 4) & 0x01010101u) << 7);
-    return make_uint4(__builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u),   // elements 0, 2
-                      __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u),   // 4, 6
-                      __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u),   // 1, 3
-                      __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u));  // 5, 7
+    const uint32_t ae = __builtin_amdgcn_perm(hi_e, lo_e, 0x05010400u);  // e0 | e2 << 16
+    const uint32_t ao = __builtin_amdgcn_perm(hi_o, lo_o, 0x05010400u);  // o0 | o2 << 16
+    const uint32_t be = __builtin_amdgcn_perm(hi_e, lo_e, 0x07030602u);  // e4 | e6 << 16
+    const uint32_t bo = __builtin_amdgcn_perm(hi_o, lo_o, 0x07030602u);  // o4 | o6 << 16
+    return make_uint4(__builtin_amdgcn_perm(ao, ae, 0x05040100u), __builtin_amdgcn_perm(ao, ae, 0x07060302u),
+                      __builtin_amdgcn_perm(bo, be, 0x05040100u), __builtin_amdgcn_perm(bo, be, 0x07060302u));
 }
 
-constexpr int XS = DL + 16;  // halfwords per LDS tile row: rows 32 bytes apart modulo 128
 
 // fp8 split kernel (raw-tile variant).  Same work items and wave split as
 // k_attn_mfma, but every wave streams its rows' raw e4m3 codes into a
@@ -530,6 +468,11 @@ constexpr int ROPE_DMA = 5;                   // 288 slots
 constexpr int ROPE_TILE = ROPE_DMA * 64 * 16; // 5120 bytes
 
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Workgroup barrier after this wave's LDS accesses have completed.  Unlike
+// __syncthreads it does not wait for outstanding global loads (loads of later
+// tiles stay in flight); the assembly is a compiler memory barrier as well.
+__device__ __forceinline__ void wg_barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // LDS DMA (global_load_lds: each lane's bytes land at the wave-uniform LDS
 // base in M0 + lane * size) issued from inline assembly.  The compiler does not
@@ -573,6 +516,46 @@ __device__ __forceinline__ int tile_sigma_inv(int q) {
     return q ^ (((q >> 4) & 1) << 3) ^ ((((q >> 3) ^ (q >> 4)) & 1) << 2);
 }
 
+// The split plan, in-kernel (matrix-core paths), run by one wave: it scans
+// max(1, ceil(T_s / split)) over the sequences, 64 at a time, and finds the
+// one holding chunk c: plan_s = {first row, end row, sequence}, sequence -1
+// if there is no such chunk.  The workgroup with blockIdx 0 also stores the
+// prefix (chunk_prefix) for the merge.
+__device__ __forceinline__ void plan_chunk(const kvq_attn_args& a, const Plan& p, int64_t c, int64_t* plan_s,
+                                           int lane) {
+    const bool writer = blockIdx.x == 0;
+    const int64_t split = p.split_rows;
+    int64_t run = 0;
+    if (lane == 0) plan_s[2] = -1;
+    for (int base = 0; base < a.n_seqs; base += 64) {
+        const int sq = base + lane;
+        int64_t cnt = 0, lo = 0, hi = 0;
+        if (sq < a.n_seqs) {
+            lo = max(a.seq_offsets[sq], (int64_t)0);
+            hi = min(a.seq_offsets[sq + 1], a.total_rows);
+            cnt = hi > lo ? (hi - lo + split - 1) / split : 1;
+        }
+        int64_t incl = cnt;  // inclusive scan over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        const int64_t excl = run + incl - cnt;
+        const bool mine = sq < a.n_seqs && c >= excl && c < excl + cnt;  // one lane over all passes
+        if (sq < a.n_seqs && writer) p.chunk_prefix[sq] = excl;
+        if (mine) {
+            const int64_t r0c = lo + (c - excl) * split;
+            plan_s[0] = r0c;
+            plan_s[1] = min(hi, r0c + split);
+            plan_s[2] = sq;
+        }
+        run += __shfl(incl, 63, 64);
+        if (!writer && __any(mine)) break;
+    }
+    if (writer && lane == 0) p.chunk_prefix[a.n_seqs] = run;
+}
+
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
     __shared__ __align__(16) uint8_t rope_s[MF_WAVES][ROPE_TILE];      // rope keys (bf16)
@@ -589,42 +572,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int hg = (int)(local % p.n_groups);
     if (c >= p.max_chunks) return;
     const int head = hg * MF_HEADS + n;
-    // ---- the split plan, in-kernel: wave 0 scans max(1, ceil(T_s / split)) over
-    // the sequences, 64 at a time, and finds the one holding chunk c; the
-    // workgroup of chunk 0, head group 0 also stores the prefix for the merge.
-    const bool writer = blockIdx.x == 0;
-    if (wave == 0) {
-        const int64_t split = p.split_rows;
-        int64_t run = 0;
-        if (lane == 0) plan_s[2] = -1;
-        for (int base = 0; base < a.n_seqs; base += 64) {
-            const int sq = base + lane;
-            int64_t cnt = 0, lo = 0, hi = 0;
-            if (sq < a.n_seqs) {
-                lo = max(a.seq_offsets[sq], (int64_t)0);
-                hi = min(a.seq_offsets[sq + 1], a.total_rows);
-                cnt = hi > lo ? (hi - lo + split - 1) / split : 1;
-            }
-            int64_t incl = cnt;  // inclusive scan over the wave
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int64_t v = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += v;
-            }
-            const int64_t excl = run + incl - cnt;
-            const bool mine = sq < a.n_seqs && c >= excl && c < excl + cnt;  // one lane over all passes
-            if (sq < a.n_seqs && writer) p.chunk_prefix[sq] = excl;
-            if (mine) {
-                const int64_t r0c = lo + (c - excl) * split;
-                plan_s[0] = r0c;
-                plan_s[1] = min(hi, r0c + split);
-                plan_s[2] = sq;
-            }
-            run += __shfl(incl, 63, 64);
-            if (!writer && __any(mine)) break;
-        }
-        if (writer && lane == 0) p.chunk_prefix[a.n_seqs] = run;
-    }
+    if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
 
     // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
     // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
@@ -902,7 +850,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     __syncthreads();
     {
         const int hh = tid >> 4;             // head within the group
-        const int d0 = (tid & 15) * 32;      // 32 dims per thread
+        const int f0 = tid & 15;             // float4 columns f0 + 16 q: each store covers 256 contiguous bytes
         float mw[MF_WAVES], M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < MF_WAVES; w++) {
@@ -919,17 +867,18 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
         const int h = hg * MF_HEADS + hh;
         if (h < a.n_heads) {
-            float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
+            float* dst = p.part_o + (c * a.n_heads + h) * DL;
 #pragma unroll
             for (int q = 0; q < 8; q++) {
+                const int f = f0 + 16 * q;
                 float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
                 for (int w = 0; w < MF_WAVES; w++) {
                     const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&raw[w][0][0]) +
-                                                                      hh * DL + 4 * (((d0 >> 2) + q) ^ hh));
+                                                                      hh * DL + 4 * (f ^ hh));
                     o.x += so[w] * v.x; o.y += so[w] * v.y; o.z += so[w] * v.z; o.w += so[w] * v.w;
                 }
-                *reinterpret_cast<float4*>(dst + 4 * q) = o;
+                *reinterpret_cast<float4*>(dst + 4 * f) = o;
             }
             if ((tid & 15) == 0) {
                 p.part_m[c * a.n_heads + h] = M;  // log2 units
@@ -939,55 +888,158 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     }
 }
 
-// TQ4 split kernel.  Work item = (T-chunk, group of 16 heads); the items are
-// dealt to XCDs in contiguous runs so the head groups of a chunk share one L2.
-// The 4 waves of a workgroup take consecutive quarters of the chunk (tiles of
-// 32 rows) for the same 16 heads, each with a private LDS tile:
-//   score:  S^T (16 rows x 16 heads) += X(rows, k) q^T -- X decoded from the
-//           nibbles in registers (the next tile's codes are loaded while this
-//           one is processed) and written to the LDS tile as fp16;
-//   PV:     O^T (16 dims x 16 heads) += X^T P'^T -- X^T from the row-major LDS
-//           tile via ds_read_b64_tr_b16 (lane (g, p) gets rows 4 g .. 4 g + 3 and
-//           16 + 4 g .. + 3 of column p, the k order the score accumulators
-//           already hold P in).
-// Within each 8 dims the decoder emits the order 0 2 4 6 1 3 5 7 (fewer byte
-// permutes); the packed query follows it, and the output dims are put back
-// in order when the accumulators are stored.  Softmax: fixed per-wave
-// reference as in the fp8 kernel (a tile more than 2^8 above it raises the
-// reference and the wave starts its rows again), probabilities times
-// rho * rs with rs from the chunk's largest radius, so the accumulators are
-// never rescaled inside the loop.  The waves' (m, l, O) are merged in LDS; one
-// partial per (chunk, head).
+// TQ4 query preparation: q~ = H D q / sqrt(512) for every (sequence, head),
+// scaled by a power of two qs (max |q~| * qs in [256, 512)) and rounded to
+// fp16, in the split kernel's operand layout: uint4 16 g + ks holds dims
+// 32 ks + 8 g .. + 7; the rope query (times sm_scale * log2(e)) as bf16 hi
+// (uint4 QP_RH + 2 g + k) and lo (QP_RL + 2 g + k) terms of dims 32 k + 8 g ..
+// + 7; 1 / qs in q_inv.  One wave per (sequence, head); lane l rotates dims
+// 8 l .. 8 l + 7 (three butterfly stages in registers, six across lanes).
+__global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + h
+    if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
+    const int s = (int)(row / p.heads_padded), h = (int)(row % p.heads_padded);
+    const bool valid = h < a.n_heads;
+    // unconditional loads (a clamped head; a guarded load would wait for every load in flight)
+    const float* src = a.q_lat + ((int64_t)s * a.n_heads + min(h, a.n_heads - 1)) * DL + 8 * lane;
+    const float4 x0 = *reinterpret_cast<const float4*>(src), x1 = *reinterpret_cast<const float4*>(src + 4);
+    const float* r = a.q_rope + ((int64_t)s * a.n_heads + min(h, a.n_heads - 1)) * DR + 8 * (lane & 7);
+    const float4 y0 = *reinterpret_cast<const float4*>(r), y1 = *reinterpret_cast<const float4*>(r + 4);
+    float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = valid ? v[i] : 0.0f;
+    const uint32_t sm = a.sign_mask[lane];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        if ((sm >> i) & 1u) v[i] = -v[i];
+#pragma unroll
+    for (int hh = 1; hh < 8; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            if (!(i & hh)) {
+                const float x = v[i], y = v[i + hh];
+                v[i] = x + y;
+                v[i + hh] = x - y;
+            }
+    // across lanes: DPP and lane-swap butterflies
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        float x = v[i];
+        x = fwht_xlane_c<1>(x, lane);
+        x = fwht_xlane_c<2>(x, lane);
+        x = fwht_xlane_c<4>(x, lane);
+        x = fwht_xlane_c<8>(x, lane);
+        x = fwht_xlane_c<16>(x, lane);
+        v[i] = fwht_xlane_c<32>(x, lane);
+    }
+    float qmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        v[i] *= INV_SQRT_DL;
+        qmax = fmaxf(qmax, fabsf(v[i]));
+    }
+    qmax = wave_max(qmax);
+    const float qs = pow2_scale_for(qmax, 8);
+    uint4* dst = p.q_pack + row * QPACK_U4;
+    dst[16 * (lane & 3) + (lane >> 2)] = make_uint4(pack_f16x2(v[0] * qs, v[1] * qs), pack_f16x2(v[2] * qs, v[3] * qs),
+                                                    pack_f16x2(v[4] * qs, v[5] * qs), pack_f16x2(v[6] * qs, v[7] * qs));
+    if (lane < 8) {  // rope dims 8 lane .. + 7: k-step lane / 4, lane group lane % 4
+        const float c2r = valid ? a.sm_scale * LOG2E : 0.0f;
+        const float rv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        uint32_t rh[4], rl[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float f0 = rv[2 * i] * c2r, f1 = rv[2 * i + 1] * c2r;
+            const float b0 = u2f(f32_to_bf16_rne(f0) << 16), b1 = u2f(f32_to_bf16_rne(f1) << 16);
+            rh[i] = pack_bf16x2(b0, b1);
+            rl[i] = pack_bf16x2(f0 - b0, f1 - b1);
+        }
+        dst[QP_RH + 2 * (lane & 3) + (lane >> 2)] = make_uint4(rh[0], rh[1], rh[2], rh[3]);
+        dst[QP_RL + 2 * (lane & 3) + (lane >> 2)] = make_uint4(rl[0], rl[1], rl[2], rl[3]);
+    }
+    if (lane == 0) p.q_inv[row] = 1.0f / qs;  // exact
+}
+
+// TQ4 split kernel.  Work item = (T-chunk, group of 64 heads); the items are
+// dealt to XCDs in contiguous runs so the head groups of a chunk share one
+// L2.  All 4 waves of a workgroup step through the chunk's tiles (32 rows)
+// together, wave w for heads 16 w .. 16 w + 15: the nibble codes of a tile
+// are decoded once per workgroup -- each wave decodes 8 rows into a shared,
+// double-buffered fp16 LDS tile (rope keys and row scales next to it) -- and
+// every wave then reads the whole tile:
+//   score:  S^T (16 rows x 16 heads) += X(rows, k) q~^T, X from the tile
+//           (lane (g, n): row 16 rb + n, dims 32 ks + 8 g .. + 7);
+//   PV:     O^T (16 dims x 16 heads) += X^T P'^T, X^T via ds_read_b64_tr_b16
+//           (lane (g, p) gets rows 4 g .. 4 g + 3 and 16 + 4 g .. + 3 of column
+//           p, the k order the score accumulators hold P in).
+// One barrier per tile.  While a wave multiplies tile t it decodes tile t + 1
+// (its codes were loaded one tile earlier).  Softmax: fixed per-wave
+// reference (first tile's max) and probabilities times rho * rs with rs from
+// the chunk's largest radius; a tile more than 2^8 above the reference raises
+// it, and the workgroup (which shares the tiles) starts its rows again.  One
+// partial per (chunk, head), written by the wave that owns the head.
+constexpr int XT = DL + 8;                // halfwords per fp16 tile row (rows 4 banks apart)
+constexpr int KT = DR + 8;                // halfwords per rope tile row
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a, Plan p) {
-    __shared__ __align__(16) uint16_t tile[MF_WAVES][MF_TILE][XS];
+    __shared__ __align__(16) uint16_t xt[2][MF_TILE][XT];  // decoded latent rows, fp16
+    __shared__ __align__(16) uint16_t kt[2][MF_TILE][KT];  // rope keys, bf16
+    __shared__ __align__(16) float rho_s[2][MF_TILE];      // radius / sqrt(512)
     __shared__ float red_s[MF_WAVES];
+    __shared__ int flag_s[2][MF_WAVES];
+    __shared__ int64_t plan_s[3];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, n = lane & 15;
     const int64_t local = blockIdx.x / N_XCD;
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
-    if (c >= p.max_chunks || c >= p.chunk_prefix[a.n_seqs]) return;
-    const int s = find_chunk_seq(p.chunk_prefix, a.n_seqs, c);
-    const int64_t seq_lo = max(a.seq_offsets[s], (int64_t)0), seq_hi = min(a.seq_offsets[s + 1], a.total_rows);
-    const int64_t r0 = seq_lo + (c - p.chunk_prefix[s]) * p.split_rows;
-    const int64_t r1 = min(seq_hi, r0 + (int64_t)p.split_rows);
-    const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
-    const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
-    const int head = hg * MF_HEADS + n;  // may exceed n_heads (padded query is zero)
-    constexpr int CB = DL / 2;           // code bytes per row
+    if (c >= p.max_chunks) return;
+    const int head = hg * TQ4_HEADS + MF_HEADS * wave + n;  // may exceed n_heads (its query is zero)
+    constexpr int CB = DL / 2;                                 // code bytes per row
+    if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
+    __syncthreads();  // plan_s
+    const int sq = (int)plan_s[2];
+    if (sq < 0) return;  // no such chunk (workgroup-uniform)
+    const int64_t r0 = plan_s[0], r1 = plan_s[1];
+    const int ntiles = (int)((r1 - r0 + MF_TILE - 1) / MF_TILE);
 
-    // ---- per-split probability scale rs from the largest row scale of the chunk
+    // decode share of this wave: tile row 8 wave + lane / 8, code bytes
+    // 32 (lane % 8) .. + 31 (dims 64 (lane % 8) .. + 63), rope bytes 16 (lane % 8)
+    const int drow = 8 * wave + (lane >> 3), dq = lane & 7;
+    uint4 ca[2], cr;  // codes and rope of the tile to decode next
+    float cs;         // its row scale
+    auto load_share = [&](int t) __attribute__((always_inline)) {
+        const int64_t t0 = r0 + (int64_t)MF_TILE * t;
+        const int64_t row = t0 + min(drow, (int)(r1 - t0) - 1);  // rows past the chunk re-read its last row
+        const uint8_t* cp = a.codes + row * CB + 32 * dq;
+        ca[0] = *reinterpret_cast<const uint4*>(cp);
+        ca[1] = *reinterpret_cast<const uint4*>(cp + 16);
+        cr = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 8 * dq);
+        cs = a.row_scale[row] * INV_SQRT_DL;
+    };
+    const Tq4Lut lut = make_tq4_lut();
+    auto decode_share = [&](int buf) __attribute__((always_inline)) {
+        const uint32_t w[8] = {ca[0].x, ca[0].y, ca[0].z, ca[0].w, ca[1].x, ca[1].y, ca[1].z, ca[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            *reinterpret_cast<uint4*>(&xt[buf][drow][64 * dq + 8 * i]) = tq4x8_to_f16x8(w[i], lut);
+        *reinterpret_cast<uint4*>(&kt[buf][drow][8 * dq]) = cr;
+        rho_s[buf][drow] = cs;  // the 8 lanes of a row store the same value
+    };
+    if (ntiles > 0) load_share(0);
+
+    // ---- the chunk's largest row scale (four loads in flight per thread)
     float rmax = 0.0f;
-    for (int64_t t = r0 + tid; t < r1; t += MF_WAVES * 64) rmax = fmaxf(rmax, fabsf(a.row_scale[t]));
-    rmax = wave_max(rmax);
-    if (lane == 0) red_s[wave] = rmax;
-    __syncthreads();
-    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-    const float rs = pow2_scale_for(rmax * INV_SQRT_DL, -1);  // max rho * rs in [0.5, 1)
-
-    // ---- query operands (rotated, one fp16 term scaled by a power of two)
-    const uint4* qp = p.q_pack + ((int64_t)s * p.heads_padded + head) * QPACK_U4;
+    for (int64_t t = r0 + tid; t < r1; t += 4 * MF_WAVES * 64) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(t + u * MF_WAVES * 64, r1 - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; u++) rmax = fmaxf(rmax, fabsf(x[u]));
+    }
+    // ---- query operands (prepared once per sequence and head)
+    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + head) * QPACK_U4;
     uint4 qh[16], rh[2], rl[2];
 #pragma unroll
     for (int k = 0; k < 16; k++) qh[k] = qp[16 * g + k];
@@ -996,101 +1048,96 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
         rh[k] = qp[QP_RH + 2 * g + k];
         rl[k] = qp[QP_RL + 2 * g + k];
     }
-    const float qinv = p.q_inv[(int64_t)s * p.heads_padded + head];
-    const Tq4Lut lut = make_tq4_lut();
-    const float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
-    const float c2 = a.sm_scale * LOG2E;         // rope scores (the rope query is unscaled)
-    uint16_t(*xs)[XS] = tile[wave];
+    const float k1 = a.sm_scale * LOG2E * p.q_inv[(int64_t)sq * p.heads_padded + head];
+    rmax = wave_max(rmax);
+    if (lane == 0) red_s[wave] = rmax;
+    __syncthreads();
+    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+    const float rs = pow2_scale_for(rmax * INV_SQRT_DL, -1);  // max rho * rs in [0.5, 1)
 
-    // next-tile registers: lane (g, n) loads row 16 rb + n (codes at 64 j + 16 g,
-    // rope at 8 g + 32 k) and the scales of rows 16 rb + 4 g .. + 3.  Every load
-    // is issued (rows past the tile re-read its last row, masked in the
-    // softmax): a guarded load would be a branch with a wait for all loads.
-    uint4 nraw[2][4], nkr[2][2];
-    float nrho[2][4];
-    auto load_tile = [&](int64_t t0) __attribute__((always_inline)) {
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const int row = min(16 * rb + n, nt - 1);
-            const uint8_t* crow = a.codes + (t0 + row) * CB + 16 * g;
-            const uint16_t* krow = a.k_rope + (t0 + row) * DR + 8 * g;
-#pragma unroll
-            for (int j = 0; j < 4; j++) nraw[rb][j] = *reinterpret_cast<const uint4*>(crow + 64 * j);
-#pragma unroll
-            for (int k = 0; k < 2; k++) nkr[rb][k] = *reinterpret_cast<const uint4*>(krow + 32 * k);
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-                nrho[rb][r] = a.row_scale[t0 + min(16 * rb + 4 * g + r, nt - 1)] * INV_SQRT_DL;
-        }
-    };
-
+    // per-lane LDS addresses: score row 16 rb + n, dims 8 g + 32 ks; PV source
+    // lane (g, n) at row 4 g + n / 4, column 4 (n % 4) (+ 16 mb, + 16 rows)
+    const int trow = 4 * g + (n >> 2), tcol = 4 * (n & 3);
     f32x4_t acc_o[32];
     float m_run = -INFINITY, l_part = 0.0f;
+    bool over = false;
+    // one vote + barrier per tile: every wave reports whether its last tile was
+    // out of range (any such vote restarts the workgroup); the barrier also
+    // publishes the tile decoded since the last one
+    auto vote = [&](int t) __attribute__((always_inline)) {
+        flag_s[t & 1][wave] = over ? 1 : 0;  // every lane stores the same value
+        wg_barrier_lds();
+        const int4 f = *reinterpret_cast<const int4*>(&flag_s[t & 1][0]);
+        return (f.x | f.y | f.z | f.w) != 0;  // workgroup-uniform
+    };
     for (;;) {
 #pragma unroll
     for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     l_part = 0.0f;
-    bool again = false;
-    if (w0 < w1) load_tile(w0);
-    for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        uint4 raw[2][4], kr[2][2];
-        float rr[2][4];
+    if (ntiles > 0) {
+        decode_share(0);  // its codes were loaded above (or at the restart)
+        load_share(min(1, ntiles - 1));
+    }
+    bool again = vote(0);
+    if (!again && ntiles > 0) {
+    int t = 0;
+    do {
+        const int buf = t & 1;
+        const int nt = (int)min((int64_t)MF_TILE, r1 - (r0 + (int64_t)MF_TILE * t));
+        // ---- scores S^T (two row blocks) from the tile: four independent
+        // accumulator chains (row block x even / odd k-step), reads one step ahead
+        f32x4_t sl[2], sr[2], sx[2];
+        sl[0] = sl[1] = sr[0] = sr[1] = sx[0] = sx[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            const uint16_t* xa = &xt[buf][n][8 * g];
+            const uint16_t* xb = &xt[buf][16 + n][8 * g];
+            f16x8_t na = *reinterpret_cast<const f16x8_t*>(xa), nb = *reinterpret_cast<const f16x8_t*>(xb);
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) raw[rb][j] = nraw[rb][j];
-#pragma unroll
-            for (int k = 0; k < 2; k++) kr[rb][k] = nkr[rb][k];
-#pragma unroll
-            for (int r = 0; r < 4; r++) rr[rb][r] = nrho[rb][r];
-        }
-        if (t0 + MF_TILE < w1) load_tile(t0 + MF_TILE);
-        // ---- decode to fp16 (LDS tile row 16 rb + n) and the scores S^T
-        f32x4_t sl[2], sr[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const int row = 16 * rb + n;
-            sl[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            sr[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const uint32_t w[4] = {raw[rb][j].x, raw[rb][j].y, raw[rb][j].z, raw[rb][j].w};
-#pragma unroll
-                for (int hh = 0; hh < 4; hh++) {
-                    const uint4 xv = tq4x8_to_f16x8(w[hh], lut);
-                    *reinterpret_cast<uint4*>(&xs[row][128 * j + 32 * g + 8 * hh]) = xv;
-                    sl[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xv), as_f16x8(qh[4 * j + hh]), sl[rb], 0, 0, 0);
+            for (int ks = 0; ks < 16; ks++) {
+                const f16x8_t ca2 = na, cb2 = nb;
+                if (ks < 15) {
+                    na = *reinterpret_cast<const f16x8_t*>(xa + 32 * (ks + 1));
+                    nb = *reinterpret_cast<const f16x8_t*>(xb + 32 * (ks + 1));
                 }
+                f32x4_t& s0 = (ks & 1) ? sx[0] : sl[0];
+                f32x4_t& s1 = (ks & 1) ? sx[1] : sl[1];
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qh[ks]), s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qh[ks]), s1, 0, 0, 0);
             }
 #pragma unroll
-            for (int k = 0; k < 2; k++) {
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
+            for (int rb = 0; rb < 2; rb++) {
+                const uint16_t* kr = &kt[buf][16 * rb + n][8 * g];
+#pragma unroll
+                for (int k = 0; k < 2; k++) {
+                    const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kr + 32 * k);
+                    sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
+                    sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
+                }
+                sl[rb] += sx[rb];
             }
         }
-        // ---- softmax: lane (g, n) holds rows 16 rb + 4 g + r of head n
-        float sc[2][4];
+        // ---- softmax: lane (g, n) holds rows 16 rb + 4 g + r of head n (no branches)
+        float sc[2][4], rr[2][4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++)
+        for (int rb = 0; rb < 2; rb++) {
+            const float4 rq = *reinterpret_cast<const float4*>(&rho_s[buf][16 * rb + 4 * g]);
+            const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const bool ok = 16 * rb + 4 * g + r < nt;
-                if (!ok) rr[rb][r] = 0.0f;
-                const float v = ok ? fmaf(rr[rb][r] * k1, sl[rb][r], c2 * sr[rb][r]) : -INFINITY;
-                sc[rb][r] = v;
-                tmax = fmaxf(tmax, v);
+                rr[rb][r] = ok ? rv[r] : 0.0f;
+                sc[rb][r] = ok ? fmaf(rv[r] * k1, sl[rb][r], sr[rb][r]) : -INFINITY;
+                tmax = fmaxf(tmax, sc[rb][r]);
             }
-        tmax = max_xor16_xor32(tmax);
-        if (m_run == -INFINITY) m_run = tmax;  // first tile: row 0 is valid
-        if (__any(tmax > m_run + LAZY_LOG2)) {
-            // raise the reference past this tile and start the rows again
-            m_run = fmaxf(m_run, tmax);
-            again = true;
-            break;
         }
+        tmax = max_xor16_xor32(tmax);
+        m_run = m_run == -INFINITY ? tmax : m_run;  // first tile: row 0 is valid
+        // a tile more than 2^8 above the reference raises it; the workgroup
+        // restarts at the next vote
+        const bool ov = __any(tmax > m_run + LAZY_LOG2);
+        m_run = ov ? fmaxf(m_run, tmax) : m_run;
+        over = over || ov;
         float psum = 0.0f;
         uint32_t pb[4];
 #pragma unroll
@@ -1107,81 +1154,68 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
         }
         l_part += psum;
         const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
-        // the tile rows written above are read back transposed by other lanes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // ---- PV: source lane (g, n) points at row t0' + n / 4, column 16 mb + 4 (n % 4)
-        const int trow = 4 * g + (n >> 2), tcol = 4 * (n & 3);
+        // ---- the next tile's share (after the last tile: the last one again,
+        // into the free buffer), then the loads of the one after
+        decode_share(buf ^ 1);
+        load_share(min(t + 2, ntiles - 1));
+        // ---- PV from the tile, the transposed reads four column blocks ahead
+        auto pv_read = [&](int mb) __attribute__((always_inline)) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)&xt[buf][trow][16 * mb + tcol]);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)&xt[buf][16 + trow][16 * mb + tcol]);
+            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+            return as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+        };
+        f16x8_t pvq[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) pvq[i] = pv_read(i);
 #pragma unroll
         for (int mb = 0; mb < 32; mb++) {
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)&xs[trow][16 * mb + tcol]);
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)&xs[16 + trow][16 * mb + tcol]);
-            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-            const f16x8_t aop = as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+            const f16x8_t aop = pvq[mb & 3];
+            if (mb + 4 < 32) pvq[mb & 3] = pv_read(mb + 4);
             acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[mb], 0, 0, 0);
+        }
+        t++;
+        again = vote(t);
+    } while (!again && t < ntiles);
+    }
+    if (!again) break;
+    over = false;
+    if (ntiles > 0) load_share(0);
+    }
+    // ---- the partials of this wave's heads, staged in LDS (the tiles are free
+    // after the last vote) half a row at a time and stored as whole rows
+    l_part += __shfl_xor(l_part, 16, 64);
+    l_part += __shfl_xor(l_part, 32, 64);
+    if (g == 0 && head < a.n_heads) {
+        p.part_m[c * a.n_heads + head] = m_run;  // log2 units
+        p.part_l[c * a.n_heads + head] = l_part;
+    }
+    constexpr int SR = DL / 2 + 4;  // floats per staged half row
+    static_assert(sizeof(xt) >= MF_WAVES * MF_HEADS * SR * sizeof(float), "staging fits in the tiles");
+    float* stg = reinterpret_cast<float*>(&xt[0][0][0]) + wave * (MF_HEADS * SR);
+    const float so = 1.0f / rs;  // exact (a power of two)
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+#pragma unroll
+        for (int mb = 0; mb < 16; mb++) {
+            const f32x4_t v = acc_o[16 * hf + mb];
+            *reinterpret_cast<float4*>(stg + n * SR + 16 * mb + 4 * g) = make_float4(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    if (!again) break;
-    }
-    // ---- merge the waves' states in LDS (each wave's tile holds its own state)
-    l_part += __shfl_xor(l_part, 16, 64);
-    l_part += __shfl_xor(l_part, 32, 64);
-    constexpr int OS = DL + 4;  // floats per stored head row (banks shifted per row)
-    float* st = reinterpret_cast<float*>(&tile[wave][0][0]);  // [16][OS] O, then m[16], l[16]
-    __syncthreads();  // every wave is done reading its tile
-    // accumulator element r of block mb is tile column 16 mb + 4 g + r, which
-    // holds dim 16 mb + 8 (g / 2) + g % 2 + 2 r
 #pragma unroll
-    for (int mb = 0; mb < 32; mb++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) st[n * OS + 16 * mb + 8 * (g >> 1) + (g & 1) + 2 * r] = acc_o[mb][r];
-    if (g == 0) {
-        st[MF_HEADS * OS + n] = m_run;
-        st[MF_HEADS * OS + MF_HEADS + n] = l_part;
-    }
-    __syncthreads();
-    {
-        const int hh = tid >> 4;             // head within the group
-        const int d0 = (tid & 15) * 32;      // 32 dims per thread
-        float mw[MF_WAVES], M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < MF_WAVES; w++) {
-            mw[w] = reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + hh];
-            M = fmaxf(M, mw[w]);
+        for (int k = 0; k < MF_HEADS; k++) {
+            const int h = hg * TQ4_HEADS + MF_HEADS * wave + k;
+            if (h < a.n_heads)
+                *reinterpret_cast<float4*>(p.part_o + (c * a.n_heads + h) * DL + DL / 2 * hf + 4 * lane) =
+                    *reinterpret_cast<const float4*>(stg + k * SR + 4 * lane);
         }
-        float sw[MF_WAVES], L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < MF_WAVES; w++) {
-            sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
-            L += sw[w] * reinterpret_cast<const float*>(&tile[w][0][0])[MF_HEADS * OS + MF_HEADS + hh];
-        }
-        const int h = hg * MF_HEADS + hh;
-        if (h < a.n_heads) {
-            float* dst = p.part_o + (c * a.n_heads + h) * DL + d0;
-            const float rsinv = 1.0f / rs;  // exact
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-                for (int w = 0; w < MF_WAVES; w++) {
-                    const float4 v =
-                        *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&tile[w][0][0]) + hh * OS + d0 + 4 * q);
-                    o.x += sw[w] * v.x; o.y += sw[w] * v.y; o.z += sw[w] * v.z; o.w += sw[w] * v.w;
-                }
-                o.x *= rsinv; o.y *= rsinv; o.z *= rsinv; o.w *= rsinv;
-                *reinterpret_cast<float4*>(dst + 4 * q) = o;
-            }
-            if ((tid & 15) == 0) {
-                p.part_m[c * a.n_heads + h] = M;  // log2 units
-                p.part_l[c * a.n_heads + h] = L;
-            }
-        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -1191,11 +1225,13 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
 // every NGRP-th split; it merges its splits online (running max, rescaled sums),
 // then the NGRP groups are combined through LDS.
 template <bool TQ4, bool LOG2>
-__global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
+__global__ __launch_bounds__(TQ4 ? 1024 : 256) void k_merge(kvq_attn_args a, Plan p) {
+    constexpr int NT = TQ4 ? 1024 : 256;  // threads (TQ4: one workgroup per head, more split groups)
     constexpr int NDH = TQ4 ? 1 : 2;
     constexpr int DW = DL / NDH;       // dims per workgroup
     constexpr int COLS = DW / 4;       // float4 columns
-    constexpr int NGRP = 256 / COLS;   // split groups
+    constexpr int NGRP = NT / COLS;    // split groups
+    constexpr int U = 8;               // splits in flight per thread
     __shared__ __align__(16) float4 o_s[NGRP][COLS];
     __shared__ float m_s[NGRP], l_s[NGRP];
     __shared__ __align__(16) float vec[DL];
@@ -1208,13 +1244,13 @@ __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
     auto ex = [](float x) { return LOG2 ? exp2f(x) : expf(x); };
     float m = -INFINITY, l = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    // batches of 4 splits: all loads first (no branch between them), then the
+    // batches of U splits: all loads first (no branch between them), then the
     // online update with selects
-    for (int64_t cb = c0 + grp; cb < c1; cb += 4 * NGRP) {
-        float mc[4], lc[4];
-        float4 v[4];
+    for (int64_t cb = c0 + grp; cb < c1; cb += U * NGRP) {
+        float mc[U], lc[U];
+        float4 v[U];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < U; u++) {
             const int64_t c = cb + u * NGRP;
             const int64_t ch = (c < c1 ? c : cb) * a.n_heads + h;
             mc[u] = p.part_m[ch];
@@ -1223,7 +1259,7 @@ __global__ __launch_bounds__(256) void k_merge(kvq_attn_args a, Plan p) {
             if (c >= c1) mc[u] = -INFINITY;
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < U; u++) {
             const float mn = fmaxf(m, mc[u]);
             const float sc = m == -INFINITY ? 0.0f : ex(m - mn);
             const float w = mc[u] == -INFINITY ? 0.0f : ex(mc[u] - mn);
@@ -1312,19 +1348,21 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
     const bool tq4 = a.qmode == KVQ_QMODE_TQ4;
     switch (stage) {
         case KVQ_STAGE_PREP:
-            // the fp8 matrix-core split kernel plans and prepares its query itself
-            if (!f32 && !tq4) break;
+            // the matrix-core split kernels plan their chunk themselves; the fp8 one
+            // also prepares its query, TQ4 rotates it here once per head
+            if (!f32) {
+                if (tq4) {
+                    const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
+                    hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
+                }
+                break;
+            }
             hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a.seq_offsets, a.n_seqs, p.split_rows, a.total_rows,
                                p.chunk_prefix);
-            if (f32) {
-                if (tq4) {
-                    const int64_t rows = (int64_t)a.n_seqs * a.n_heads;
-                    hipLaunchKernelGGL(k_qrot, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.q_lat,
-                                       a.sign_mask, rows, p.q_rot);
-                }
-            } else {
-                const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
-                hipLaunchKernelGGL(k_qprep<KVQ_QMODE_TQ4>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
+            if (tq4) {
+                const int64_t rows = (int64_t)a.n_seqs * a.n_heads;
+                hipLaunchKernelGGL(k_qrot, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.q_lat, a.sign_mask,
+                                   rows, p.q_rot);
             }
             break;
         case KVQ_STAGE_SPLITS:
@@ -1342,8 +1380,8 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
         default: {
             const int64_t items = (int64_t)a.n_seqs * a.n_heads;
             if (tq4) {
-                if (!f32) hipLaunchKernelGGL((k_merge<true, true>), dim3((unsigned)items), dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<true, false>), dim3((unsigned)items), dim3(256), 0, st, a, p);
+                if (!f32) hipLaunchKernelGGL((k_merge<true, true>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<true, false>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
             } else {
                 if (!f32) hipLaunchKernelGGL((k_merge<false, true>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
                 else hipLaunchKernelGGL((k_merge<false, false>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);

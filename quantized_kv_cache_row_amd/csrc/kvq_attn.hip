@@ -1224,9 +1224,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
 // whole row, which the un-rotation needs).  A thread owns one float4 column and
 // every NGRP-th split; it merges its splits online (running max, rescaled sums),
 // then the NGRP groups are combined through LDS.
-template <bool TQ4, bool LOG2>
-__global__ __launch_bounds__(TQ4 ? 1024 : 256) void k_merge(kvq_attn_args a, Plan p) {
-    constexpr int NT = TQ4 ? 1024 : 256;  // threads (TQ4: one workgroup per head, more split groups)
+template <bool TQ4, bool LOG2, int NT>
+__global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
     constexpr int NDH = TQ4 ? 1 : 2;
     constexpr int DW = DL / NDH;       // dims per workgroup
     constexpr int COLS = DW / 4;       // float4 columns
@@ -1379,12 +1378,16 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
             break;
         default: {
             const int64_t items = (int64_t)a.n_seqs * a.n_heads;
+            // more split groups per workgroup when there are many splits per sequence
+            const bool wide = p.max_chunks >= 16 * (int64_t)a.n_seqs;
             if (tq4) {
-                if (!f32) hipLaunchKernelGGL((k_merge<true, true>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<true, false>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
+                if (!f32 && wide) hipLaunchKernelGGL((k_merge<true, true, 1024>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
+                else if (!f32) hipLaunchKernelGGL((k_merge<true, true, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<true, false, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);
             } else {
-                if (!f32) hipLaunchKernelGGL((k_merge<false, true>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL((k_merge<false, false>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
+                if (!f32 && wide) hipLaunchKernelGGL((k_merge<false, true, 512>), dim3((unsigned)(2 * items)), dim3(512), 0, st, a, p);
+                else if (!f32) hipLaunchKernelGGL((k_merge<false, true, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL((k_merge<false, false, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
             }
             break;
         }

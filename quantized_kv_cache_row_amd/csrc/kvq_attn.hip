@@ -574,60 +574,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int head = hg * MF_HEADS + n;
     if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
 
-    // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
-    // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
-    // two qs (max |q| * qs in [256, 512)) and rounded to fp16; the rope dims
-    // 32 ks' + 8 g + e, times sm_scale * log2(e), as a bf16 hi + lo pair.
-    uint4 qh[16], rh[2], rl[2];
-    float qinv;
-    {
-        __syncthreads();  // plan_s
-        const int sq = (int)plan_s[2];
-        const bool hv = head < a.n_heads && sq >= 0;
-        const float* ql = a.q_lat + ((int64_t)(sq < 0 ? 0 : sq) * a.n_heads + (hv ? head : 0)) * DL;
-        const float* qr = a.q_rope + ((int64_t)(sq < 0 ? 0 : sq) * a.n_heads + (hv ? head : 0)) * DR;
-        float4 v[32], w[4];
-#pragma unroll
-        for (int ks = 0; ks < 16; ks++) {
-            const float* src = ql + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
-            v[2 * ks] = hv ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
-            v[2 * ks + 1] = hv ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const float* src = qr + 32 * k + 8 * g;
-            w[2 * k] = hv ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
-            w[2 * k + 1] = hv ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        float qmax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 32; k++)
-            qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
-        qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
-        qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-        const float qs = pow2_scale_for(qmax, 8);
-        qinv = 1.0f / qs;  // exact
-#pragma unroll
-        for (int ks = 0; ks < 16; ks++) {
-            const float4 x = v[2 * ks], y = v[2 * ks + 1];
-            qh[ks] = make_uint4(pack_f16x2(x.x * qs, x.y * qs), pack_f16x2(x.z * qs, x.w * qs),
-                                pack_f16x2(y.x * qs, y.y * qs), pack_f16x2(y.z * qs, y.w * qs));
-        }
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const float c2r = a.sm_scale * LOG2E;  // rope scores come out in log2 units
-            const float f[8] = {w[2 * k].x * c2r, w[2 * k].y * c2r, w[2 * k].z * c2r, w[2 * k].w * c2r,
-                                w[2 * k + 1].x * c2r, w[2 * k + 1].y * c2r, w[2 * k + 1].z * c2r,
-                                w[2 * k + 1].w * c2r};
-            float b[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) b[e] = u2f(f32_to_bf16_rne(f[e]) << 16);
-            rh[k] = make_uint4(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]),
-                               pack_bf16x2(b[6], b[7]));
-            rl[k] = make_uint4(pack_bf16x2(f[0] - b[0], f[1] - b[1]), pack_bf16x2(f[2] - b[2], f[3] - b[3]),
-                               pack_bf16x2(f[4] - b[4], f[5] - b[5]), pack_bf16x2(f[6] - b[6], f[7] - b[7]));
-        }
-    }
+    __syncthreads();  // plan_s
     if (plan_s[2] < 0) return;  // no such chunk (workgroup-uniform)
     const int64_t r0 = plan_s[0], r1 = plan_s[1];
     const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
@@ -636,8 +583,11 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // DMA loaders (global -> LDS, no registers).  Lane l of instruction i fills
     // slot 64 i + l: row sigma^-1(slot / 33), chunk slot % 33 (the pad slot and
     // the slots past the tile re-read chunk 0 of that row, or of row 0).  The
-    // offsets are fixed per lane; in a tile shorter than 32 rows the rows past
-    // its end re-read row 0, which is masked later.
+    // offsets are fixed per lane.  Rows past the wave's end are loaded too (and
+    // masked later) while they lie inside the arrays; past the arrays' end a
+    // lane loads their last 16 bytes instead.  Instruction k of a tile
+    // (0..22: codes, rope, scales) is issued on its own, so the issue can be
+    // spread over the score steps.
     uint32_t voff_c[RAW_DMA], voff_r[ROPE_DMA];
 #pragma unroll
     for (int i = 0; i < RAW_DMA; i++) {
@@ -656,29 +606,80 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const uint32_t lds_codes = lds_offset(&raw[wave][0][0]);
     const uint32_t lds_rope = lds_offset(&rope_s[wave][0]);
     const uint32_t lds_rho = lds_offset(&rho_s[wave][0][0]);
-    auto load_tile = [&](int64_t t0, int buf) {
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        const uint8_t* cb = a.codes + t0 * RAW_ROW;
-        const uint8_t* rb = reinterpret_cast<const uint8_t*>(a.k_rope + t0 * DR);
-        const uint32_t lc = __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE);
-        const uint32_t ls = __builtin_amdgcn_readfirstlane(lds_rho + 256u * buf);
-        const uint32_t voff_s = (uint32_t)((lane & 31) < nt ? (lane & 31) : 0) * 4u;
-        if (nt == MF_TILE) {
-#pragma unroll
-            for (int i = 0; i < RAW_DMA; i++) dma_lds_b128(cb, voff_c[i], lc + 1024u * i);
-#pragma unroll
-            for (int i = 0; i < ROPE_DMA; i++) dma_lds_b128(rb, voff_r[i], lds_rope + 1024u * i);
+    constexpr int NDMA = RAW_DMA + ROPE_DMA + 1;
+    auto dma_one = [&](int k, int64_t t0, int buf) __attribute__((always_inline)) {
+        const int lim = (int)min((int64_t)MF_TILE, a.total_rows - t0);  // rows inside the arrays
+        if (k < RAW_DMA) {
+            dma_lds_b128(a.codes + t0 * RAW_ROW, min(voff_c[k], (uint32_t)lim * RAW_ROW - 16u),
+                         __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE + 1024u * k));
+        } else if (k < RAW_DMA + ROPE_DMA) {
+            dma_lds_b128(reinterpret_cast<const uint8_t*>(a.k_rope + t0 * DR),
+                         min(voff_r[k - RAW_DMA], (uint32_t)lim * (DR * 2) - 16u), lds_rope + 1024u * (k - RAW_DMA));
         } else {
-#pragma unroll
-            for (int i = 0; i < RAW_DMA; i++)
-                dma_lds_b128(cb, (int)(voff_c[i] / RAW_ROW) < nt ? voff_c[i] : voff_c[i] % RAW_ROW, lc + 1024u * i);
-#pragma unroll
-            for (int i = 0; i < ROPE_DMA; i++)
-                dma_lds_b128(rb, (int)(voff_r[i] / (DR * 2)) < nt ? voff_r[i] : voff_r[i] % (DR * 2),
-                             lds_rope + 1024u * i);
+            const uint32_t voff_s = (uint32_t)((lane & 31) < lim ? (lane & 31) : 0) * 4u;
+            dma_lds_b32(a.row_scale + t0, voff_s, __builtin_amdgcn_readfirstlane(lds_rho + 256u * buf));
         }
-        dma_lds_b32(a.row_scale + t0, voff_s, ls);
     };
+    auto load_tile = [&](int64_t t0, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NDMA; k++) dma_one(k, t0, buf);
+    };
+    if (w0 < w1) load_tile(w0, 0);  // the first tile's loads overlap the query preparation
+
+    // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
+    // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
+    // two qs (max |q| * qs in [256, 512)) and rounded to fp16; the rope dims
+    // 32 ks' + 8 g + e, times sm_scale * log2(e), as a bf16 hi + lo pair.
+    uint4 qh[16], rh[2], rl[2];
+    float qinv;
+    {
+        // unconditional loads (clamped head): a guarded load would wait for every load in flight
+        const int sq = (int)plan_s[2];
+        const bool hv = head < a.n_heads;
+        const float* ql = a.q_lat + ((int64_t)sq * a.n_heads + min(head, a.n_heads - 1)) * DL;
+        const float* qr = a.q_rope + ((int64_t)sq * a.n_heads + min(head, a.n_heads - 1)) * DR;
+        float4 v[32], w[4];
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++) {
+            const float* src = ql + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
+            v[2 * ks] = *reinterpret_cast<const float4*>(src);
+            v[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 4);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const float* src = qr + 32 * k + 8 * g;
+            w[2 * k] = *reinterpret_cast<const float4*>(src);
+            w[2 * k + 1] = *reinterpret_cast<const float4*>(src + 4);
+        }
+        float qmax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; k++)
+            qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+        qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+        const float qs = hv ? pow2_scale_for(qmax, 8) : 0.0f;  // absent heads: a zero query
+        qinv = hv ? 1.0f / qs : 0.0f;                           // exact
+#pragma unroll
+        for (int ks = 0; ks < 16; ks++) {
+            const float4 x = v[2 * ks], y = v[2 * ks + 1];
+            qh[ks] = make_uint4(pack_f16x2(x.x * qs, x.y * qs), pack_f16x2(x.z * qs, x.w * qs),
+                                pack_f16x2(y.x * qs, y.y * qs), pack_f16x2(y.z * qs, y.w * qs));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const float c2r = hv ? a.sm_scale * LOG2E : 0.0f;  // rope scores come out in log2 units
+            const float f[8] = {w[2 * k].x * c2r, w[2 * k].y * c2r, w[2 * k].z * c2r, w[2 * k].w * c2r,
+                                w[2 * k + 1].x * c2r, w[2 * k + 1].y * c2r, w[2 * k + 1].z * c2r,
+                                w[2 * k + 1].w * c2r};
+            float b[8];
+#pragma unroll
+            for (int e = 0; e < 8; e++) b[e] = u2f(f32_to_bf16_rne(f[e]) << 16);
+            rh[k] = make_uint4(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]),
+                               pack_bf16x2(b[6], b[7]));
+            rl[k] = make_uint4(pack_bf16x2(f[0] - b[0], f[1] - b[1]), pack_bf16x2(f[2] - b[2], f[3] - b[3]),
+                               pack_bf16x2(f[4] - b[4], f[5] - b[5]), pack_bf16x2(f[6] - b[6], f[7] - b[7]));
+        }
+    }
     auto tile_row = [](int rb, int nn) { return 8 * (nn >> 2) + 4 * rb + (nn & 3); };
     // per-lane LDS read offsets (bytes within a tile)
     const uint32_t rd_a = 16u * (RAW_SLOTS * tile_sigma(tile_row(0, n)) + g);   // score, row block 0
@@ -701,13 +702,15 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     f32x4_t acc_o[32];
     float m_run = -INFINITY, l_part = 0.0f;
     float rsc = 0.0f;  // 0 until a row with a nonzero scale
+    bool restarted = false;
     for (;;) {
 #pragma unroll
     for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     l_part = 0.0f;
     int buf = 0;
     bool again = false;
-    if (w0 < w1) load_tile(w0, 0);
+    if (restarted && w0 < w1) load_tile(w0, 0);
+    restarted = true;
     for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
         const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
         vm_wait_all();  // this tile's codes, rope keys and scales are in LDS
@@ -722,7 +725,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         const float4 rho0 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g]);
         const float4 rho1 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g + 4]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): those reads are done before the buffers refill
-        if (more) load_tile(t0 + MF_TILE, buf ^ 1);
+        // the next tile's DMA, three instructions per score step (after the last
+        // tile: this tile again, into the free buffer)
+        const int64_t tn = more ? t0 + MF_TILE : t0;
         const uint8_t* tb = raw[wave][buf];
         // ---- scores: both row blocks together, the reads one k-chunk ahead
         const uint8_t* pa = tb + rd_a;
@@ -738,6 +743,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 na = chunk(pa, j + 1);
                 nb = chunk(pbp, j + 1);
             }
+#pragma unroll
+            for (int k = 3 * j; k < 3 * j + 3; k++)
+                if (k < NDMA) dma_one(k, tn, buf ^ 1);
             __builtin_amdgcn_sched_barrier(0);  // the look-ahead reads issue before this chunk's math
             const uint4 a0 = e4m3x8_to_f16x8(ca.x, ca.y), a1 = e4m3x8_to_f16x8(ca.z, ca.w);
             const uint4 b0 = e4m3x8_to_f16x8(cbv.x, cbv.y), b1 = e4m3x8_to_f16x8(cbv.z, cbv.w);
@@ -754,6 +762,14 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
                 sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
             }
+        // the first PV operands are read now: their latency hides behind the softmax
+        const uint8_t* trbase = tb + rd_t;
+        auto trd = [&](int mb) __attribute__((always_inline)) {
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(trbase + 16 * mb));
+        };
+        i32x2_t nv[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) nv[i] = trd(i);
         // lane (g, n): accumulator register r of block rb = tile row 8 g + 4 rb + r
         const bool full = nt == MF_TILE;  // wave-uniform
         float sc[2][4], rr[2][4];
@@ -802,13 +818,6 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         l_part += psum;
         const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
         // ---- PV: groups of 8 column blocks, the next group's reads in flight
-        const uint8_t* trbase = tb + rd_t;
-        auto trd = [&](int mb) {
-            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(trbase + 16 * mb));
-        };
-        i32x2_t nv[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) nv[i] = trd(i);
 #pragma unroll
         for (int grp = 0; grp < 4; grp++) {
             i32x2_t cv[8];
@@ -829,8 +838,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
         buf ^= 1;
     }
+    vm_wait_all();  // the next tile's DMA may still be landing: drain it (restart or epilogue)
     if (!again) break;
-    vm_wait_all();  // the next tile's DMA may still be landing: drain it before the rows restart
     }
     // ---- merge the waves' states in LDS (each wave reuses its own raw buffers)
     l_part += __shfl_xor(l_part, 16, 64);

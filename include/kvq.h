@@ -152,11 +152,10 @@ int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_of
  * Tolerance against an fp64 evaluation on the same codes:
  *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA), <= 1e-5 (KVQ_PREC_FP32).
  * KVQ_PREC_MFMA operands: latent codes in fp16 (exact for every e4m3 value and
- * codebook level); the latent query scaled per head by a power of two and
- * rounded to fp16 (TQ4: split into two fp16 terms); the rope query split into
- * two bf16 terms (k_rope is bf16); the probabilities p * rho_t scaled by a
- * power of two per work item and rounded to fp16; fp32 accumulation, softmax
- * and per-row scales. */
+ * codebook level); the latent query (TQ4: R q) scaled per head by a power of
+ * two and rounded to fp16; the rope query split into two bf16 terms (k_rope is
+ * bf16); the probabilities p * rho_t scaled by a power of two per work item
+ * and rounded to fp16; fp32 accumulation, softmax and per-row scales. */
 typedef struct kvq_attn_args {
     int32_t qmode;              /* KVQ_QMODE_FP8 or KVQ_QMODE_TQ4                 */
     int32_t precision;          /* KVQ_PREC_MFMA or KVQ_PREC_FP32                 */
@@ -194,10 +193,11 @@ int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, v
 /* One stage of kvq_decode_attn; running stages 0..2 in order on one stream is
  * exactly kvq_decode_attn.  Running a stage gives profilers and timers one
  * stage per call:
- *   KVQ_STAGE_PREP   the per-sequence T-split prefix and the query operands in
- *                    the workspace (TQ4: rotated by R); the fp8 matrix-core
- *                    path does both inside its split kernel and launches
- *                    nothing here;
+ *   KVQ_STAGE_PREP   KVQ_PREC_FP32: the per-sequence T-split prefix and, TQ4,
+ *                    R q in the workspace; KVQ_PREC_MFMA, TQ4: the rotated
+ *                    fp16 query operands; KVQ_PREC_MFMA, fp8: nothing (the
+ *                    matrix-core split kernels plan their T-split themselves,
+ *                    the fp8 one also prepares its query);
  *   KVQ_STAGE_SPLITS the attention over every T-split (partial softmax states);
  *   KVQ_STAGE_MERGE  merge of the splits (+ TQ4 un-rotation) into out / lse. */
 #define KVQ_STAGE_PREP 0

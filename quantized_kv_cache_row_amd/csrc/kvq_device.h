@@ -175,6 +175,35 @@ __device__ __forceinline__ float fwht_xlane_c(float v, int lane) {
     return __builtin_fmaf((lane & M) ? -1.0f : 1.0f, v, o);
 }
 
+// ---- DPP helpers (lane patterns inside a 16-lane row) -----------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    // every source lane of the patterns below exists, so bound_ctrl never applies; the form
+    // with an old value of 0 lets the compiler fold the move into the add that uses it
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// y[i0 + e] += c * (y[i0 + e] of the partner lane), e = 0..7, as v_fmac_f32_dpp (the
+// compiler does not fold a DPP move into an fma whose addend is tied to the result).
+// A DPP read of a VGPR needs 2 wait states after a VALU write of it; the block
+// provides them up front (inside it, no instruction reads what the one before wrote).
+#define KVQ_FMAC_DPP_X8(PAT, y, i0, c)                                                     \
+    asm("s_nop 1\n\t"                                                                     \
+        "v_fmac_f32_dpp %0, %0, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %1, %1, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %2, %2, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %3, %3, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %4, %4, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %5, %5, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %6, %6, %8 " PAT " row_mask:0xf bank_mask:0xf\n\t"                \
+        "v_fmac_f32_dpp %7, %7, %8 " PAT " row_mask:0xf bank_mask:0xf"                      \
+        : "+v"(y[(i0) + 0]), "+v"(y[(i0) + 1]), "+v"(y[(i0) + 2]), "+v"(y[(i0) + 3]),       \
+          "+v"(y[(i0) + 4]), "+v"(y[(i0) + 5]), "+v"(y[(i0) + 6]), "+v"(y[(i0) + 7])        \
+        : "v"(c))
+constexpr int DPP_XOR1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int DPP_XOR7 = 0x141;  // row_half_mirror: lane i <- 7 - i within 8
+constexpr int DPP_XOR8 = 0x128;  // row_ror:8 within a 16-lane row
+
 // Largest-value selection on the key (|x|, x) with +0 above -0: the key is
 // order-preserving as an unsigned integer.
 __device__ __forceinline__ uint32_t absval_key(float x) {

@@ -7,10 +7,11 @@
 //      a Walsh-Hadamard rotation, one radius per row and indices into a fixed
 //      16-level Lloyd-Max codebook scaled by radius / sqrt(n).
 //
-// Both kernels are bandwidth kernels: one wave per row (fp8) or dim/8 lanes per
-// row (TQ4), 8 consecutive fp32 per lane loaded as two 16-byte loads, codes
-// stored as one 8-byte (fp8) or 4-byte (TQ4) store per lane, so every wave
-// instruction touches one contiguous span.
+// fp8: one wave per row, 8 consecutive fp32 per lane loaded as two 16-byte
+// loads, codes stored as one 8-byte store per lane, so every wave instruction
+// touches one contiguous span.  TQ4: a general kernel (dim/8 lanes per row) and
+// one for dim 512 that spends half the vector instructions per row (the TQ4
+// encoder is bound by the vector ALU, not by HBM).
 #include <cstring>
 #include <type_traits>
 
@@ -190,6 +191,194 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4(const float
     }
 }
 
+// ---- TQ4, dim 512 --------------------------------------------------------------
+// The same result as k_encode_tq4 with fewer vector instructions per row
+// (the general kernel spends about 500 per 512-wide row, so it is bound by the
+// vector ALU rather than by HBM):
+//  - 16 lanes per row, 4 rows per wave.  Lane u of a row holds column
+//    q = u ^ 3 bit2(u), i.e. the 32 elements p = j + 4 q + 64 k (j = 0..3,
+//    k = 0..7), loaded as eight 16-byte loads (load k covers 256 contiguous
+//    bytes per row).  FWHT stages in the definition's order: h = 1, 2 in
+//    registers (bits of j), h = 4, 8, 16, 32 across lanes (bits of q: partner
+//    lane u ^ 1, u ^ 2, u ^ 7, u ^ 8, each a single DPP pattern inside a 16-lane
+//    row), h = 64, 128, 256 in registers (bits of k).
+//  - Each cross-lane stage is one fma with the partner's value as the DPP
+//    operand: y + c * y_partner with c = +1 in the lower lane and -1 in the
+//    upper.  The upper lane then holds -(a - b) instead of a - b (the sum is
+//    rounded once either way, and rounding to nearest is symmetric), so after
+//    the four stages lane q holds (-1)^popcount(q) times the transform; that
+//    sign is put back in the bucketing step.
+//  - Bucketing uses the codebook's symmetry (t_{14-k} = -t_k, t_7 = 0, hence
+//    T_{14-k} = -T_k exactly): for w > 0, idx = 8 + #{k >= 8 : w > T_k}; for
+//    w <= 0, idx = 7 - #{k >= 8 : |w| >= T_k}.  Both counts are one 3-level
+//    search over the 7 positive thresholds on integer keys (the bits of |w|,
+//    plus 1 for w <= 0, which turns >= into >); the bits of nonnegative floats
+//    order like the values.  A row whose radius is not finite takes the
+//    defining comparisons against all 15 thresholds instead.
+constexpr int D512_ROWS = 4;  // rows per wave
+
+
+__global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const float* __restrict__ x,
+                                                                          int64_t n_rows,
+                                                                          const uint8_t* __restrict__ sign_mask,
+                                                                          uint8_t* __restrict__ codes,
+                                                                          float* __restrict__ radii) {
+    constexpr int D = 512;
+    const int lane = threadIdx.x & (KVQ_WAVE - 1);
+    const int slot = lane >> 4, u = lane & 15;
+    const int q = u ^ (((u >> 2) & 1) * 3);
+    // sign flip of element (j, k): bit j + 4 (q & 1) of mask byte 8 k + q / 2, gathered
+    // into bit 4 k + j of one word
+    uint32_t sbits = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        sbits |= (((uint32_t)sign_mask[8 * k + (q >> 1)] >> (4 * (q & 1))) & 15u) << (4 * k);
+    const float c0 = (q & 1) ? -1.0f : 1.0f, c1 = (q & 2) ? -1.0f : 1.0f;
+    const float c2 = (q & 4) ? -1.0f : 1.0f, c3 = (q & 8) ? -1.0f : 1.0f;
+    const uint32_t lane_sign = (uint32_t)(__builtin_popcount(q) & 1) << 31;
+    // value classes (v_cmp_class bits) of y where w = (-1)^popcount(q) y is <= 0:
+    // -inf, -normal, -denormal, -0, +0, or their mirror images
+    const int nonpos_class = lane_sign ? 0x3E0 : 0x07C;
+    const bool qodd = q & 1;
+    const uint32_t sel_lo = qodd ? 0x01000504u : 0x05040100u;  // own 16 bits low (even q) or high (odd q)
+    const uint32_t sel_hi = qodd ? 0x03020706u : 0x07060302u;
+
+    const int64_t stride = (int64_t)gridDim.x * ENC_WAVES * D512_ROWS;
+    const int64_t first = ((int64_t)blockIdx.x * ENC_WAVES + (threadIdx.x >> 6)) * D512_ROWS;
+    // clamped rows: no load waits on a lane condition; a row slot past the end works on a
+    // copy of the last row
+    auto load = [&](int64_t base, float4 (&v)[8]) __attribute__((always_inline)) {
+        const int64_t row = min(base + slot, n_rows - 1);
+        const float* xr = x + row * D + 4 * q;
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = *reinterpret_cast<const float4*>(xr + 64 * k);
+    };
+    // No prefetch: at 4 rows per wave and about 1100 vector instructions per
+    // iteration, the other resident waves cover a wave's load latency.
+    for (int64_t base = first; base < n_rows; base += stride) {
+        float v[32];
+        {
+            float4 nv[8];
+            load(base, nv);
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                v[4 * k + 0] = nv[k].x; v[4 * k + 1] = nv[k].y; v[4 * k + 2] = nv[k].z; v[4 * k + 3] = nv[k].w;
+            }
+        }
+        const int64_t row = base + slot;  // rows past the end hold a copy of the last row
+        // radius^2: the pairwise tree over p (bits 0, 1 here, 2..5 across lanes, 6..8 here)
+        float s2[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float a0 = v[4 * k] * v[4 * k], a1 = v[4 * k + 1] * v[4 * k + 1];
+            const float a2 = v[4 * k + 2] * v[4 * k + 2], a3 = v[4 * k + 3] * v[4 * k + 3];
+            s2[k] = (a0 + a1) + (a2 + a3);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; k++) s2[k] = s2[k] + dpp_f32<DPP_XOR1>(s2[k]);  // a + b == b + a: both lanes agree
+#pragma unroll
+        for (int k = 0; k < 8; k++) s2[k] = s2[k] + dpp_f32<DPP_XOR2>(s2[k]);
+#pragma unroll
+        for (int k = 0; k < 8; k++) s2[k] = s2[k] + dpp_f32<DPP_XOR7>(s2[k]);
+#pragma unroll
+        for (int k = 0; k < 8; k++) s2[k] = s2[k] + dpp_f32<DPP_XOR8>(s2[k]);
+        const float r2 = ((s2[0] + s2[1]) + (s2[2] + s2[3])) + ((s2[4] + s2[5]) + (s2[6] + s2[7]));
+        const float rad = sqrt_rn(r2);
+        // random signs, then the transform
+        uint32_t sb = sbits;
+        asm("" : "+v"(sb));  // opaque per iteration: the 32 masks are not hoisted into 32 registers
+#pragma unroll
+        for (int i = 0; i < 32; i++)  // bit i rotated to bit 31, xor-ed into the sign
+            v[i] = u2f(f2u(v[i]) ^ (__builtin_amdgcn_alignbit(sb, sb, (i + 1) & 31) & 0x80000000u));
+#pragma unroll
+        for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < 32; i++)
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+#pragma unroll
+        for (int i = 0; i < 32; i += 8) KVQ_FMAC_DPP_X8("quad_perm:[1,0,3,2]", v, i, c0);
+#pragma unroll
+        for (int i = 0; i < 32; i += 8) KVQ_FMAC_DPP_X8("quad_perm:[2,3,0,1]", v, i, c1);
+#pragma unroll
+        for (int i = 0; i < 32; i += 8) KVQ_FMAC_DPP_X8("row_half_mirror", v, i, c2);
+#pragma unroll
+        for (int i = 0; i < 32; i += 8) KVQ_FMAC_DPP_X8("row_ror:8", v, i, c3);
+#pragma unroll
+        for (int h = 4; h < 32; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < 32; i++)
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+        // bucketing; nibble of element (j, k) -> bit 4 j + 16 bit1(k) of word P[2 (k & 1) + k / 4]
+        uint32_t tb[7];
+#pragma unroll
+        for (int i = 0; i < 7; i++) tb[i] = f2u(u2f(c_tq4_thresh[8 + i]) * rad);
+        uint32_t P[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float y = v[4 * k + j];
+                const bool neg = __builtin_amdgcn_classf(y, nonpos_class);  // w = +-y <= 0
+                const uint32_t key = (f2u(y) & 0x7FFFFFFFu) + (neg ? 1u : 0u);
+                const bool b2 = key > tb[3];
+                const bool b1 = key > (b2 ? tb[5] : tb[1]);
+                const uint32_t ta = b2 ? tb[6] : tb[2], tc = b2 ? tb[4] : tb[0];
+                const bool b0 = key > (b1 ? ta : tc);
+                // idx = 8 + m (w > 0) or 7 - m (w <= 0), m = 4 b2 + 2 b1 + b0: the bits of 7 - m are
+                // those of m flipped, so idx = 8 (w > 0) + the three bits, each xor neg
+                uint32_t idx = neg ? 0u : 1u;
+                idx = 2u * idx + ((b2 != neg) ? 1u : 0u);
+                idx = 2u * idx + ((b1 != neg) ? 1u : 0u);
+                idx = 2u * idx + ((b0 != neg) ? 1u : 0u);
+                P[2 * (k & 1) + (k >> 2)] |= idx << (4 * j + 16 * ((k >> 1) & 1));
+            }
+        if (__builtin_amdgcn_ballot_w64(!(r2 <= 3.40282347e38f)) != 0 && !(r2 <= 3.40282347e38f)) {
+            // radius inf or NaN (wave-uniform test first: the common path has no select of it;
+            // the empty volatile block keeps the compiler from evaluating this path speculatively)
+            asm volatile("" ::: "memory");
+            float T[15];
+#pragma unroll
+            for (int k = 0; k < 15; k++) T[k] = u2f(c_tq4_thresh[k]) * rad;
+#pragma unroll
+            for (int i = 0; i < 4; i++) P[i] = 0u;
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float w = u2f(f2u(v[4 * k + j]) ^ lane_sign);
+                    uint32_t idx = 0;
+#pragma unroll
+                    for (int t = 0; t < 15; t++) idx += (w > T[t]) ? 1u : 0u;
+                    P[2 * (k & 1) + (k >> 2)] |= idx << (4 * j + 16 * ((k >> 1) & 1));
+                }
+        }
+        // lanes q and q ^ 1 (lane u ^ 1) own the two halves of each 4-byte word at
+        // byte 32 k + 2 (q & ~1): the even lane assembles even k, the odd lane odd k
+        const uint32_t send0 = qodd ? P[0] : P[2], send1 = qodd ? P[1] : P[3];
+        const uint32_t keep0 = qodd ? P[2] : P[0], keep1 = qodd ? P[3] : P[1];
+        const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)send0, DPP_XOR1, 0xF, 0xF, false);
+        const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)send1, DPP_XOR1, 0xF, 0xF, false);
+        // Unconditional stores (no branch): a row slot past the end loaded the last row
+        // and writes that row's bytes again (identical values), and all 16 lanes of a
+        // row store its radius.
+        const int64_t srow = min(row, n_rows - 1);
+        uint8_t* cr = codes + srow * (D / 2) + 2 * (q & 14) + 32 * (qodd ? 1 : 0);
+        *reinterpret_cast<uint32_t*>(cr) = __builtin_amdgcn_perm(r0, keep0, sel_lo);        // k = 0 / 1
+        *reinterpret_cast<uint32_t*>(cr + 64) = __builtin_amdgcn_perm(r0, keep0, sel_hi);   // k = 2 / 3
+        *reinterpret_cast<uint32_t*>(cr + 128) = __builtin_amdgcn_perm(r1, keep1, sel_lo);  // k = 4 / 5
+        *reinterpret_cast<uint32_t*>(cr + 192) = __builtin_amdgcn_perm(r1, keep1, sel_hi);  // k = 6 / 7
+        radii[srow] = rad;
+    }
+}
+
 // ---- conversion probe ---------------------------------------------------------
 __global__ void k_convert(int kind, const void* __restrict__ in, int64_t n, void* __restrict__ out) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -245,6 +434,14 @@ hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* c
 hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
                              uint8_t* codes, float* radii, hipStream_t st) {
     if (n_rows == 0) return hipSuccess;
+    if (dim == 512) {
+        const int64_t waves = (n_rows + D512_ROWS - 1) / D512_ROWS;
+        int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;
+        if (wgs > 1280) wgs = 1280;  // the resident count (5 per CU at 86 VGPRs); the kernel strides
+        hipLaunchKernelGGL(k_encode_tq4_d512, dim3((unsigned)wgs), dim3(ENC_WAVES * KVQ_WAVE), 0, st, x, n_rows,
+                           sign_mask, codes, radii);
+        return hipGetLastError();
+    }
     const int64_t rows_per_wave = KVQ_WAVE / (dim / 8);
     const int64_t waves = (n_rows + rows_per_wave - 1) / rows_per_wave;
     int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;

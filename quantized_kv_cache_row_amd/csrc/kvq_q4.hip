@@ -20,28 +20,53 @@ constexpr int Q4_WAVES = 4;
 constexpr int Q4_ROWS_PER_BLOCK = Q4_WAVES * 4;  // head-rows per workgroup
 constexpr int Q4_ROW_BYTES = 144;
 
-// Sequence owning item `r` of a segmented range: the s with off[s] <= r < off[s+1].
-__device__ __forceinline__ int find_seq(const int64_t* __restrict__ off, int n_seqs, int64_t r) {
-    int lo = 0, hi = n_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= r) lo = mid; else hi = mid - 1;
+// Sequence owning item `r` of a segmented range: the largest s with off[s] <= r
+// (off non-decreasing, off[0] <= r).  The 16 lanes of a head-row search together,
+// 16-ary: each step loads the first offset of 16 equal sub-ranges of the remaining
+// range (one load per lane, all in flight at once) and keeps the last sub-range
+// whose first offset is <= r -- ceil(log16(n_seqs)) dependent loads where a binary
+// search takes log2(n_seqs).  Every lane of the wave calls it (the step count is
+// uniform); `lane16` is the lane within the head-row's group, `shift` the group's
+// first lane in the wave.
+__device__ __forceinline__ int find_seq16(const int64_t* __restrict__ off, int n_seqs, int64_t r, int lane16,
+                                          int shift) {
+    int steps = 0;
+    for (int64_t span = 1; span < n_seqs; span *= 16) steps++;
+    int lo = 0, n = n_seqs;  // invariant: the answer lies in [lo, lo + n) and off[lo] <= r
+    for (int it = 0; it < steps; it++) {
+        const int step = (n + 15) / 16;
+        const int first = lo + lane16 * step;
+        const int64_t o = off[min(first, n_seqs - 1)];  // unconditional (clamped) load
+        const bool ok = lane16 * step < n && o <= r;     // true for a prefix of the sub-ranges
+        const int cnt = max(1, __builtin_popcount((uint32_t)(__ballot(ok) >> shift) & 0xFFFFu));
+        lo += (cnt - 1) * step;
+        n = min(step, n - (cnt - 1) * step);
     }
     return lo;
 }
 
-__device__ __forceinline__ int64_t cell_of(const kvq_q4_cache& c, int s, int64_t pos) {
-    if (pos < 0) return -1;
-    const int64_t page = pos / c.page_size;
-    if (page >= c.max_pages) return -1;
-    const int64_t phys = c.block_table[(int64_t)s * c.max_pages + page];
-    if (phys < 0) return -1;
-    const int64_t cell = phys * c.page_size + pos % c.page_size;
-    return cell < c.n_cells ? cell : -1;
+// log2 of the head count and of the page size when they are powers of two, else
+// -1 (set by the host).  A 64-bit division is a long instruction sequence on the
+// GPU; with a power of two it is a shift (the branch is uniform).
+struct Q4Shifts {
+    int kv, page;
+};
+__device__ __forceinline__ int64_t div_by(int64_t x, int64_t d, int sh) { return sh >= 0 ? (x >> sh) : x / d; }
+__device__ __forceinline__ int64_t mod_by(int64_t x, int64_t d, int sh) { return sh >= 0 ? (x & (d - 1)) : x % d; }
+
+// Pool cell of position `pos` of sequence s through the page table, -1 if it has
+// none.  Branch-free: the table load is unconditional (clamped index).
+__device__ __forceinline__ int64_t cell_of(const kvq_q4_cache& c, const Q4Shifts& sh, int s, int64_t pos) {
+    const int64_t p = pos >= 0 ? pos : 0;
+    const int64_t page = div_by(p, c.page_size, sh.page);
+    const bool in_table = pos >= 0 && page < c.max_pages;
+    const int64_t phys = c.block_table[(int64_t)s * c.max_pages + (in_table ? page : 0)];
+    const int64_t cell = phys * c.page_size + mod_by(p, c.page_size, sh.page);
+    return (in_table && phys >= 0 && cell < c.n_cells) ? cell : -1;
 }
 
 // grid.x: groups of Q4_ROWS_PER_BLOCK head-rows of one plane; grid.y: plane (0 = K, 1 = V).
-__global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cache c, int n_seqs,
+__global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cache c, Q4Shifts sh, int n_seqs,
                                                                     const int32_t* __restrict__ pos0,
                                                                     const int64_t* __restrict__ src_off,
                                                                     int64_t total_new,
@@ -55,23 +80,27 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
     const int64_t hr = (int64_t)blockIdx.x * Q4_ROWS_PER_BLOCK + slot;  // head-row = r * n_kv + h
     const int64_t n_hr = total_new * c.n_kv_heads;
     const bool valid = hr < n_hr;
-    const int64_t r = valid ? hr / c.n_kv_heads : 0;
-    const int h = valid ? (int)(hr % c.n_kv_heads) : 0;
-    int64_t cell = -1;
+    // past the end: work on the last head-row (clamped, so no load waits on a lane
+    // condition), store nothing
+    const int64_t hrc = valid ? hr : n_hr - 1;
+    const int64_t r = div_by(hrc, c.n_kv_heads, sh.kv);
+    const int h = (int)mod_by(hrc, c.n_kv_heads, sh.kv);
+    // Lane `lane` of the head-row holds column q = lane ^ 3 bit2(lane): elements
+    // 16 q .. 16 q + 15.  The FWHT partners of element-index bits 4..7 (bits 0..3
+    // of q) are then lanes lane ^ 1, ^ 2, ^ 7, ^ 8 -- one DPP pattern each.
+    const int q = lane ^ (((lane >> 2) & 1) * 3);
     float v[16];
-    if (valid) {
-        const int s = find_seq(src_off, n_seqs, r);
-        cell = cell_of(c, s, (int64_t)pos0[s] + (r - src_off[s]));
-        const float* src = (plane ? v_src : k_src) + hr * 256 + lane * 16;
+    {
+        const float* src = (plane ? v_src : k_src) + hrc * 256 + q * 16;  // independent of the lookup
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const float4 a = *reinterpret_cast<const float4*>(src + 4 * q);
             v[4 * q + 0] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = 0.0f;
     }
+    const int s = find_seq16(src_off, n_seqs, r, lane, threadIdx.x & 48);
+    int64_t cell = cell_of(c, sh, s, (int64_t)pos0[s] + (r - src_off[s]));
+    if (!valid) cell = -1;
     if (rotate) {
 #pragma unroll
         for (int hh = 1; hh < 16; hh <<= 1)
@@ -82,46 +111,56 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
                     v[i] = a + b;
                     v[i + hh] = a - b;
                 }
+        // Cross-lane stages h = 16 .. 128: y + c * y_partner, c = +1 in the lower
+        // lane and -1 in the upper (one fma, rounded once like a + b or b - a), so
+        // the upper lane holds the negated butterfly output; lane q ends with
+        // (-1)^popcount(q) times the transform, and the x 1/16 scale (exact)
+        // carries that sign back.
+        const float c0 = (q & 1) ? -1.0f : 1.0f, c1 = (q & 2) ? -1.0f : 1.0f;
+        const float c2 = (q & 4) ? -1.0f : 1.0f, c3 = (q & 8) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1)
+        for (int i = 0; i < 16; i += 8) KVQ_FMAC_DPP_X8("quad_perm:[1,0,3,2]", v, i, c0);
 #pragma unroll
-            for (int i = 0; i < 16; i++) v[i] = fwht_xlane(v[i], threadIdx.x, m);
+        for (int i = 0; i < 16; i += 8) KVQ_FMAC_DPP_X8("quad_perm:[2,3,0,1]", v, i, c1);
 #pragma unroll
-        for (int i = 0; i < 16; i++) v[i] = v[i] * 0.0625f;
+        for (int i = 0; i < 16; i += 8) KVQ_FMAC_DPP_X8("row_half_mirror", v, i, c2);
+#pragma unroll
+        for (int i = 0; i < 16; i += 8) KVQ_FMAC_DPP_X8("row_ror:8", v, i, c3);
+        const float sc = (__builtin_popcount(q) & 1) ? -0.0625f : 0.0625f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) v[i] = v[i] * sc;
     }
-    // block b = lane / 2: mval = element with the largest key (|x|, x), +0 over -0
-    uint32_t best = absval_key(v[0]);
-    float mval = v[0];
+    // block b = q / 2 (lanes q, q ^ 1): mval = element with the largest key
+    // (|x|, x), +0 over -0.  key = bits of x with the sign flipped, rotated left
+    // by one: magnitude << 1 | (sign ^ 1).
+    uint32_t best = 0;
 #pragma unroll
-    for (int i = 1; i < 16; i++) {
-        const uint32_t k = absval_key(v[i]);
-        if (k > best) { best = k; mval = v[i]; }
+    for (int i = 0; i < 16; i++) {
+        const uint32_t b = f2u(v[i]) ^ 0x80000000u;
+        best = max(best, __builtin_amdgcn_alignbit(b, b, 31));
     }
-    {
-        const uint32_t ob = shfl_xor_u(best, 1);
-        const float om = shfl_xor_f(mval, 1);
-        if (ob > best) { best = ob; mval = om; }
-    }
+    best = max(best, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)best, DPP_XOR1, 0xF, 0xF, true));
+    const float mval = u2f((best >> 1) | ((~best & 1u) << 31));
     const float d = mval / -8.0f;
     const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
-    uint32_t q[16];
+    uint32_t qn[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const float t = __builtin_fmaf(v[i], id, 8.5f);
-        q[i] = !(t >= 0.0f) ? 0u : (t >= 15.0f ? 15u : (uint32_t)(int)t);
+        qn[i] = !(t >= 0.0f) ? 0u : (t >= 15.0f ? 15u : (uint32_t)(int)t);
     }
     // lane 2b holds block elements 0..15, lane 2b+1 elements 16..31.
     // byte j = q_j | q_{j+16} << 4: the even lane forms bytes 0..7, the odd lane 8..15.
     uint32_t mine_lo = 0, mine_hi = 0;  // nibbles of elements 0..7 and 8..15 of this lane
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        mine_lo |= q[i] << (4 * i);
-        mine_hi |= q[8 + i] << (4 * i);
+        mine_lo |= qn[i] << (4 * i);
+        mine_hi |= qn[8 + i] << (4 * i);
     }
-    const bool odd = lane & 1;
+    const bool odd = q & 1;
     // the even lane needs the odd lane's 0..7, the odd lane needs the even lane's 8..15
     const uint32_t give = odd ? mine_lo : mine_hi;
-    const uint32_t got = shfl_xor_u(give, 1);
+    const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)give, DPP_XOR1, 0xF, 0xF, false);
     const uint32_t low_nib = odd ? got : mine_lo;    // q_j for the 8 bytes this lane forms
     const uint32_t high_nib = odd ? mine_hi : got;   // q_{j+16}
     uint32_t w0 = 0, w1 = 0;
@@ -131,7 +170,7 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
         w1 |= (((low_nib >> (4 * (i + 4))) & 15u) | (((high_nib >> (4 * (i + 4))) & 15u) << 4)) << (8 * i);
     }
     uint8_t* row = stage[slot];
-    const int blk = (lane >> 1) * 18;
+    const int blk = (q >> 1) * 18;
     uint16_t* row16 = reinterpret_cast<uint16_t*>(row);  // every field starts at an even offset
     if (!odd) row16[blk / 2] = (uint16_t)f32_to_f16_rne(d);
     const int qo = (blk + 2 + (odd ? 8 : 0)) / 2;
@@ -147,10 +186,18 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
     }
 }
 
+// fp32 -> binary16 bits by v_cvt_f16_f32 (round to nearest even).  The value is
+// made opaque first: otherwise the compiler fuses the product that feeds it into
+// v_fma_mix with a +0 addend, which turns a -0 product into +0.
+__device__ __forceinline__ uint32_t f16_bits_hw(float f) {
+    asm("" : "+v"(f));
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // One 16-lane group per destination head-row: nine 16-byte loads of the
 // 144-byte head-row into LDS, then each lane dequantizes 16 elements (half of
 // one block) and stores 32 bytes of binary16.
-__global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cache c, int n_seqs,
+__global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cache c, Q4Shifts sh, int n_seqs,
                                                                     const int64_t* __restrict__ dst_off,
                                                                     int64_t total_rows, uint16_t* __restrict__ k_dst,
                                                                     uint16_t* __restrict__ v_dst) {
@@ -159,15 +206,14 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cach
     const int lane = threadIdx.x & 15;
     const int slot = threadIdx.x >> 4;
     const int64_t hr = (int64_t)blockIdx.x * Q4_ROWS_PER_BLOCK + slot;  // = R * n_kv + h
-    const bool valid = hr < total_rows * c.n_kv_heads;
-    int64_t cell = -1;
-    int h = 0;
-    if (valid) {
-        const int64_t R = hr / c.n_kv_heads;
-        h = (int)(hr % c.n_kv_heads);
-        const int s = find_seq(dst_off, n_seqs, R);
-        cell = cell_of(c, s, R - dst_off[s]);
-    }
+    const int64_t n_hr = total_rows * c.n_kv_heads;
+    const bool valid = hr < n_hr;
+    const int64_t hrc = valid ? hr : n_hr - 1;  // clamped: the lookup runs in every lane
+    const int64_t R = div_by(hrc, c.n_kv_heads, sh.kv);
+    const int h = (int)mod_by(hrc, c.n_kv_heads, sh.kv);
+    const int s = find_seq16(dst_off, n_seqs, R, lane, threadIdx.x & 48);
+    int64_t cell = cell_of(c, sh, s, R - dst_off[s]);
+    if (!valid) cell = -1;
     const uint8_t* pool = plane ? c.v_pool : c.k_pool;
     if (cell >= 0 && lane < 9)
         reinterpret_cast<uint4*>(stage[slot])[lane] =
@@ -185,14 +231,23 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cach
         const uint32_t two = row16[blk / 2 + 1 + i];  // qs bytes 2i, 2i+1
         const int q0 = (int)((two >> shift) & 15u);
         const int q1 = (int)((two >> (8 + shift)) & 15u);
-        const uint32_t h0 = f32_to_f16_rne((float)(q0 - 8) * d);
-        const uint32_t h1 = f32_to_f16_rne((float)(q1 - 8) * d);
+        // (q - 8) d is exact in fp32; the hardware conversion rounds it to nearest even
+        const uint32_t h0 = f16_bits_hw((float)(q0 - 8) * d);
+        const uint32_t h1 = f16_bits_hw((float)(q1 - 8) * d);
         out[i] = h0 | (h1 << 16);
     }
     uint16_t* dst = (plane ? v_dst : k_dst) + hr * 256 + lane * 16;
     reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
     reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
+
+int log2_if_pow2(int64_t v) {
+    if (v <= 0 || (v & (v - 1)) != 0) return -1;
+    int k = 0;
+    while ((int64_t(1) << k) < v) k++;
+    return k;
+}
+Q4Shifts shifts_of(const kvq_q4_cache& c) { return Q4Shifts{log2_if_pow2(c.n_kv_heads), log2_if_pow2(c.page_size)}; }
 
 }  // namespace
 
@@ -202,7 +257,7 @@ hipError_t launch_append_q4_0(const kvq_q4_cache& c, int n_seqs, const int32_t* 
     const int64_t n_hr = total_new * c.n_kv_heads;
     if (n_hr == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_hr + Q4_ROWS_PER_BLOCK - 1) / Q4_ROWS_PER_BLOCK), 2), block(Q4_WAVES * KVQ_WAVE);
-    hipLaunchKernelGGL(k_append_q4_0, grid, block, 0, st, c, n_seqs, pos0, src_off, total_new, k_src, v_src,
+    hipLaunchKernelGGL(k_append_q4_0, grid, block, 0, st, c, shifts_of(c), n_seqs, pos0, src_off, total_new, k_src, v_src,
                        rotate ? 1 : 0);
     return hipGetLastError();
 }
@@ -212,7 +267,7 @@ hipError_t launch_gather_q4_0(const kvq_q4_cache& c, int n_seqs, const int64_t* 
     const int64_t n_hr = total_rows * c.n_kv_heads;
     if (n_hr == 0) return hipSuccess;
     const dim3 grid((unsigned)((n_hr + Q4_ROWS_PER_BLOCK - 1) / Q4_ROWS_PER_BLOCK), 2), block(Q4_WAVES * KVQ_WAVE);
-    hipLaunchKernelGGL(k_gather_q4_0, grid, block, 0, st, c, n_seqs, dst_off, total_rows, k_dst, v_dst);
+    hipLaunchKernelGGL(k_gather_q4_0, grid, block, 0, st, c, shifts_of(c), n_seqs, dst_off, total_rows, k_dst, v_dst);
     return hipGetLastError();
 }
 

@@ -145,7 +145,7 @@ def test_fp8_encoder_bit_exact(case):
         np.testing.assert_array_equal(_np(c), rc)
 
 
-@pytest.mark.parametrize("case", ["tq4_decode-cache", "tq4_decode-new", "dims"])
+@pytest.mark.parametrize("case", ["tq4_decode-cache", "tq4_decode-new", "dims", "extremes"])
 def test_tq4_encoder_bit_exact(case):
     _say(f"tq4 encoder {case}")
     w = workloads.tq4_decode(T=1024) if case != "tq4_decode-cache" else workloads.tq4_decode()
@@ -153,6 +153,29 @@ def test_tq4_encoder_bit_exact(case):
         xs = [(w.latent, w.sign_mask)]
     elif case == "tq4_decode-new":
         xs = [(workloads.tq4_encode_rows(8192), w.sign_mask)]
+    elif case == "extremes":
+        # zero, constant and one-hot rows (exact cancellations give +0 and -0 in the
+        # transform), a squared norm that overflows, denormal rows, inf and NaN; 25 rows,
+        # so the last group of four rows is ragged
+        rng = np.random.default_rng(11)
+        x = rng.standard_normal((25, 512)).astype(np.float32)
+        x[0] = 0
+        x[1] *= 1e20
+        x[2] *= 1e-30
+        x[3] *= 1e-41
+        x[4, 5] = np.inf
+        x[5, 9] = np.nan
+        x[6] = 0
+        x[6, 3] = 1.0
+        x[7] = 1.0
+        x[8, 100] = -np.inf
+        x[9] *= 3e19
+        x[10] = 0
+        x[10, 0] = -0.0
+        x[11] = np.float32(1e-45)
+        x[12, ::2] = 0
+        x[13] = np.float32(2.0) ** -126
+        xs = [(x, w.sign_mask)]
     else:
         rng = np.random.default_rng(3)
         xs = []
@@ -349,6 +372,50 @@ def test_q4_append_gather_bit_exact(scale):
         rk, rv = oracle.gather_q4_0(okp, ovp, w.table, 64, w.final_off)
         np.testing.assert_array_equal(_np(kd).view(np.uint16), rk)
         np.testing.assert_array_equal(_np(vd).view(np.uint16), rv)
+
+
+def test_q4_non_pow2_page_and_heads():
+    """Page size 48, 3 KV heads and 21 sequences (one empty): the index arithmetic
+    takes the division path (powers of two take shifts) and the sequence search
+    takes two 16-ary steps."""
+    _say("q4_0 page 48, 3 heads, 21 sequences")
+    rng = np.random.default_rng(21)
+    n_kv, page, n_seqs = 3, 48, 21
+    lens = rng.integers(1, 200, n_seqs)
+    lens[4] = 0
+    pages_per = (lens + page - 1) // page
+    max_pages = int(pages_per.max())
+    n_pages = int(pages_per.sum())
+    perm = rng.permutation(n_pages).astype(np.int32)
+    table = np.full((n_seqs, max_pages), -1, np.int32)
+    k = 0
+    for s in range(n_seqs):
+        for p in range(int(pages_per[s])):
+            table[s, p] = perm[k]
+            k += 1
+    n_cells = n_pages * page
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total = int(off[-1])
+    ks = (rng.standard_normal((total, n_kv, 256)) * 3).astype(np.float32)
+    vs = rng.standard_normal((total, n_kv, 256)).astype(np.float32)
+    pos0 = np.zeros(n_seqs, np.int32)
+    kp = torch.zeros((n_cells, n_kv, 144), dtype=torch.uint8, device=DEV)
+    vp = torch.zeros_like(kp)
+    cache = kvq.q4_cache(kp, vp, _t(table), page)
+    kvq.kvq_append_q4_0(cache, _t(pos0), _t(off), total, _t(ks), _t(vs))
+    okp = np.zeros((n_cells, n_kv, 144), np.uint8)
+    ovp = np.zeros_like(okp)
+    oracle.append_q4_0(okp, ovp, table, page, pos0, off, ks, vs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(kp), okp)
+    np.testing.assert_array_equal(_np(vp), ovp)
+    kd = torch.zeros((total, n_kv, 256), dtype=torch.int16, device=DEV)
+    vd = torch.zeros_like(kd)
+    kvq.kvq_gather_q4_0(cache, _t(off), total, kd, vd)
+    torch.cuda.synchronize()
+    rk, rv = oracle.gather_q4_0(okp, ovp, table, page, off)
+    np.testing.assert_array_equal(_np(kd).view(np.uint16), rk)
+    np.testing.assert_array_equal(_np(vd).view(np.uint16), rv)
 
 
 def test_q4_no_rotate_fixtures_and_invalid_pages():

@@ -21,28 +21,36 @@ constexpr int Q4_ROWS_PER_BLOCK = Q4_WAVES * 4;  // head-rows per workgroup
 constexpr int Q4_ROW_BYTES = 144;
 
 // Sequence owning item `r` of a segmented range: the largest s with off[s] <= r
-// (off non-decreasing, off[0] <= r).  The 16 lanes of a head-row search together,
-// 16-ary: each step loads the first offset of 16 equal sub-ranges of the remaining
-// range (one load per lane, all in flight at once) and keeps the last sub-range
-// whose first offset is <= r -- ceil(log16(n_seqs)) dependent loads where a binary
-// search takes log2(n_seqs).  Every lane of the wave calls it (the step count is
-// uniform); `lane16` is the lane within the head-row's group, `shift` the group's
-// first lane in the wave.
-__device__ __forceinline__ int find_seq16(const int64_t* __restrict__ off, int n_seqs, int64_t r, int lane16,
-                                          int shift) {
+// (off non-decreasing, off[0] <= r), and off[s].  The 16 lanes of a head-row
+// search together, 16-ary: each step loads the first offset of 16 equal
+// sub-ranges of the remaining range (one load per lane, all in flight at once)
+// and keeps the last sub-range whose first offset is <= r -- ceil(log16(n_seqs))
+// dependent loads where a binary search takes log2(n_seqs).  The last step has
+// sub-ranges of one sequence, so off[s] is the value the winning lane loaded.
+// Every lane of the wave calls it (the step count is uniform); `lane16` is the
+// lane within the head-row's group, `shift` the group's first lane in the wave.
+struct SeqHit {
+    int s;
+    int64_t start;  // off[s]
+};
+__device__ __forceinline__ SeqHit find_seq16(const int64_t* __restrict__ off, int n_seqs, int64_t r, int lane16,
+                                             int shift) {
     int steps = 0;
     for (int64_t span = 1; span < n_seqs; span *= 16) steps++;
+    if (steps == 0) return SeqHit{0, off[0]};
     int lo = 0, n = n_seqs;  // invariant: the answer lies in [lo, lo + n) and off[lo] <= r
+    int64_t o = 0;
+    int cnt = 1;
     for (int it = 0; it < steps; it++) {
         const int step = (n + 15) / 16;
         const int first = lo + lane16 * step;
-        const int64_t o = off[min(first, n_seqs - 1)];  // unconditional (clamped) load
-        const bool ok = lane16 * step < n && o <= r;     // true for a prefix of the sub-ranges
-        const int cnt = max(1, __builtin_popcount((uint32_t)(__ballot(ok) >> shift) & 0xFFFFu));
+        o = off[min(first, n_seqs - 1)];              // unconditional (clamped) load
+        const bool ok = lane16 * step < n && o <= r;  // true for a prefix of the sub-ranges
+        cnt = max(1, __builtin_popcount((uint32_t)(__ballot(ok) >> shift) & 0xFFFFu));
         lo += (cnt - 1) * step;
         n = min(step, n - (cnt - 1) * step);
     }
-    return lo;
+    return SeqHit{lo, __shfl(o, shift + cnt - 1, 64)};
 }
 
 // log2 of the head count and of the page size when they are powers of two, else
@@ -98,8 +106,8 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
             v[4 * q + 0] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
         }
     }
-    const int s = find_seq16(src_off, n_seqs, r, lane, threadIdx.x & 48);
-    int64_t cell = cell_of(c, sh, s, (int64_t)pos0[s] + (r - src_off[s]));
+    const SeqHit hit = find_seq16(src_off, n_seqs, r, lane, threadIdx.x & 48);
+    int64_t cell = cell_of(c, sh, hit.s, (int64_t)pos0[hit.s] + (r - hit.start));
     if (!valid) cell = -1;
     if (rotate) {
 #pragma unroll
@@ -194,51 +202,66 @@ __device__ __forceinline__ uint32_t f16_bits_hw(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// One 16-lane group per destination head-row: nine 16-byte loads of the
-// 144-byte head-row into LDS, then each lane dequantizes 16 elements (half of
-// one block) and stores 32 bytes of binary16.
+// One 16-lane group per destination head-row, four head-row groups per workgroup
+// (64 head-rows): the lookups of all four come first, so their dependent loads
+// (offsets, page table, pool) overlap instead of running one chain per group.
+// Nine 16-byte loads bring a 144-byte head-row to LDS; then each lane
+// dequantizes 16 elements (half of one block) and stores 32 bytes of binary16.
+constexpr int G_SUB = 4;  // head-row groups per gather workgroup
+
 __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cache c, Q4Shifts sh, int n_seqs,
                                                                     const int64_t* __restrict__ dst_off,
                                                                     int64_t total_rows, uint16_t* __restrict__ k_dst,
                                                                     uint16_t* __restrict__ v_dst) {
-    __shared__ __align__(16) uint8_t stage[Q4_ROWS_PER_BLOCK][Q4_ROW_BYTES];
+    __shared__ __align__(16) uint8_t stage[G_SUB][Q4_ROWS_PER_BLOCK][Q4_ROW_BYTES];
     const int plane = blockIdx.y;
     const int lane = threadIdx.x & 15;
     const int slot = threadIdx.x >> 4;
-    const int64_t hr = (int64_t)blockIdx.x * Q4_ROWS_PER_BLOCK + slot;  // = R * n_kv + h
     const int64_t n_hr = total_rows * c.n_kv_heads;
-    const bool valid = hr < n_hr;
-    const int64_t hrc = valid ? hr : n_hr - 1;  // clamped: the lookup runs in every lane
-    const int64_t R = div_by(hrc, c.n_kv_heads, sh.kv);
-    const int h = (int)mod_by(hrc, c.n_kv_heads, sh.kv);
-    const int s = find_seq16(dst_off, n_seqs, R, lane, threadIdx.x & 48);
-    int64_t cell = cell_of(c, sh, s, R - dst_off[s]);
-    if (!valid) cell = -1;
     const uint8_t* pool = plane ? c.v_pool : c.k_pool;
-    if (cell >= 0 && lane < 9)
-        reinterpret_cast<uint4*>(stage[slot])[lane] =
-            reinterpret_cast<const uint4*>(pool + (cell * c.n_kv_heads + h) * Q4_ROW_BYTES)[lane];
-    __syncthreads();
-    if (cell < 0) return;
-    const uint8_t* row = stage[slot];
-    const int blk = (lane >> 1) * 18;
-    const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row);
-    const float d = f16_to_f32(row16[blk / 2]);
-    const int shift = (lane & 1) ? 4 : 0;  // even lane: low nibbles (elements 0..15), odd: high (16..31)
-    uint32_t out[8];
+    int64_t hr[G_SUB], cell[G_SUB];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const uint32_t two = row16[blk / 2 + 1 + i];  // qs bytes 2i, 2i+1
-        const int q0 = (int)((two >> shift) & 15u);
-        const int q1 = (int)((two >> (8 + shift)) & 15u);
-        // (q - 8) d is exact in fp32; the hardware conversion rounds it to nearest even
-        const uint32_t h0 = f16_bits_hw((float)(q0 - 8) * d);
-        const uint32_t h1 = f16_bits_hw((float)(q1 - 8) * d);
-        out[i] = h0 | (h1 << 16);
+    for (int g = 0; g < G_SUB; g++) {
+        hr[g] = ((int64_t)blockIdx.x * G_SUB + g) * Q4_ROWS_PER_BLOCK + slot;  // = R * n_kv + h
+        const bool valid = hr[g] < n_hr;
+        const int64_t hrc = valid ? hr[g] : n_hr - 1;  // clamped: the lookup runs in every lane
+        const int64_t R = div_by(hrc, c.n_kv_heads, sh.kv);
+        const SeqHit hit = find_seq16(dst_off, n_seqs, R, lane, threadIdx.x & 48);
+        const int64_t cl = cell_of(c, sh, hit.s, R - hit.start);
+        // pool row of (cell, head); -1: no cell (a position outside the table or the pool)
+        cell[g] = (valid && cl >= 0) ? cl * c.n_kv_heads + mod_by(hrc, c.n_kv_heads, sh.kv) : -1;
     }
-    uint16_t* dst = (plane ? v_dst : k_dst) + hr * 256 + lane * 16;
-    reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    uint4 raw[G_SUB];
+#pragma unroll
+    for (int g = 0; g < G_SUB; g++)  // unconditional: no cell reads row 0, lanes 9..15 re-read chunk 8
+        raw[g] = reinterpret_cast<const uint4*>(pool + max(cell[g], (int64_t)0) * Q4_ROW_BYTES)[min(lane, 8)];
+#pragma unroll
+    for (int g = 0; g < G_SUB; g++)
+        if (lane < 9) reinterpret_cast<uint4*>(stage[g][slot])[lane] = raw[g];
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G_SUB; g++) {
+        if (cell[g] < 0) continue;
+        const uint8_t* row = stage[g][slot];
+        const int blk = (lane >> 1) * 18;
+        const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row);
+        const float d = f16_to_f32(row16[blk / 2]);
+        const int shift = (lane & 1) ? 4 : 0;  // even lane: low nibbles (elements 0..15), odd: high (16..31)
+        uint32_t out[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t two = row16[blk / 2 + 1 + i];  // qs bytes 2i, 2i+1
+            const int q0 = (int)((two >> shift) & 15u);
+            const int q1 = (int)((two >> (8 + shift)) & 15u);
+            // (q - 8) d is exact in fp32; the hardware conversion rounds it to nearest even
+            const uint32_t h0 = f16_bits_hw((float)(q0 - 8) * d);
+            const uint32_t h1 = f16_bits_hw((float)(q1 - 8) * d);
+            out[i] = h0 | (h1 << 16);
+        }
+        uint16_t* dst = (plane ? v_dst : k_dst) + hr[g] * 256 + lane * 16;
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    }
 }
 
 int log2_if_pow2(int64_t v) {
@@ -266,7 +289,9 @@ hipError_t launch_gather_q4_0(const kvq_q4_cache& c, int n_seqs, const int64_t* 
                               int64_t total_rows, uint16_t* k_dst, uint16_t* v_dst, hipStream_t st) {
     const int64_t n_hr = total_rows * c.n_kv_heads;
     if (n_hr == 0) return hipSuccess;
-    const dim3 grid((unsigned)((n_hr + Q4_ROWS_PER_BLOCK - 1) / Q4_ROWS_PER_BLOCK), 2), block(Q4_WAVES * KVQ_WAVE);
+    if (c.n_cells == 0) return hipSuccess;  // no cell: nothing is written
+    constexpr int64_t per_wg = (int64_t)G_SUB * Q4_ROWS_PER_BLOCK;
+    const dim3 grid((unsigned)((n_hr + per_wg - 1) / per_wg), 2), block(Q4_WAVES * KVQ_WAVE);
     hipLaunchKernelGGL(k_gather_q4_0, grid, block, 0, st, c, shifts_of(c), n_seqs, dst_off, total_rows, k_dst, v_dst);
     return hipGetLastError();
 }

@@ -211,11 +211,12 @@ int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, in
  * can check them against the format definitions (for instance over every
  * fp32 bit pattern):
  *   KVQ_CVT_F32_TO_E4M3   fp32 -> e4m3 byte, round to nearest even, |v| saturated
- *                         to 448 (the fp8 encoder's step after the division);
+ *                         to 448 (the fp8 encoder's step after the division:
+ *                         v_med3_f32, then v_cvt_scalef32_pk_fp8_f32, scale 1);
  *   KVQ_CVT_E4M3_TO_BF16  e4m3 byte -> bf16 bits, exact (the attention's dequant;
  *                         S.1111.111 reads as +0, [KV8] HIP portability note);
  *   KVQ_CVT_F32_TO_F16    fp32 -> binary16 bits, round to nearest even (the q4_0
- *                         scale and gather outputs);
+ *                         scale and gather outputs: v_cvt_f16_f32);
  *   KVQ_CVT_F32_TO_BF16   fp32 -> bf16 bits, round to nearest even (the rope
  *                         query terms of the matrix-core path);
  *   KVQ_CVT_E4M3_TO_F16   e4m3 byte -> binary16 bits with the instruction the

@@ -19,25 +19,17 @@ namespace kvq {
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 
-// fp32 -> e4m3 code, round to nearest even, |v| saturated to 448 (0x7E).
-// NaN input is outside the contract.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-    uint32_t b = f2u(v);
-    uint32_t sign = (b >> 24) & 0x80u;
-    uint32_t a = b & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E00000u) {            // |v| >= 448
-        code = 0x7Eu;
-    } else if (a >= 0x3C800000u) {     // |v| >= 2^-6: normal e4m3
-        // round the fp32 significand to 3 bits at bit 20, ties to even
-        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        code = (r >> 20) - (120u << 3);  // rebias exponent 127 -> 7
-    } else {                           // subnormal e4m3: multiples of 2^-9
-        float s = u2f(a) * 512.0f;     // exact: |v| * 2^9 < 8
-        float t = s + 8388608.0f;      // 2^23: rounds to an integer, ties to even
-        code = f2u(t) - 0x4B000000u;   // 0..8 (8 is the smallest normal, 0x08)
-    }
-    return sign | code;
+// Two fp32 -> two e4m3 codes (byte 0: a, byte 1: b): |v| saturated to 448,
+// then the hardware conversion on the OCP e4m3 grid, round to nearest even
+// (the conversion probe checks it against the format definition on every
+// code, every midpoint between codes and their neighbouring floats).  NaN
+// input is outside the contract.
+__device__ __forceinline__ uint32_t e4m3x2_rne(float a, float b) {
+    typedef short s16x2_t __attribute__((ext_vector_type(2)));
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    const s16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, a, b, 1.0f, false);
+    return (uint32_t)(uint16_t)r[0];
 }
 
 // e4m3 code -> fp32, exact.  S.1111.111 -> +0.
@@ -58,26 +50,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // e4m3 code -> bf16 bits, exact (3 mantissa bits fit in 7).
 __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) { return f2u(e4m3_to_f32(c)) >> 16; }
 
-// fp32 -> binary16 bits, round to nearest even, subnormals kept, |v| >= 65520 -> Inf.
+// fp32 -> binary16 bits, round to nearest even (overflow to inf, subnormal
+// results kept), by v_cvt_f16_f32 (the conversion probe checks it against the
+// format definition on every binary16 midpoint and its neighbours).  The value
+// is made opaque first: otherwise the compiler fuses a product feeding it into
+// v_fma_mix with a +0 addend, which turns a -0 product into +0.
 __device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
-    uint32_t b = f2u(f);
-    uint32_t sign = (b >> 16) & 0x8000u;
-    uint32_t a = b & 0x7FFFFFFFu;
-    uint32_t h;
-    if (a > 0x7F800000u) {
-        h = 0x7E00u;                                   // NaN
-    } else if (a >= 0x477FF000u) {
-        h = 0x7C00u;                                   // overflow threshold 65520
-    } else if (a >= 0x38800000u) {                     // >= 2^-14: normal binary16
-        uint32_t r = a - 0x38000000u;                  // rebias exponent 127 -> 15
-        r = r + 0xFFFu + ((r >> 13) & 1u);
-        h = r >> 13;
-    } else {                                           // subnormal: multiples of 2^-24
-        float s = u2f(a) * 16777216.0f;                // exact, < 1024
-        float t = s + 8388608.0f;                      // round to integer, ties to even
-        h = f2u(t) - 0x4B000000u;                      // 0..1024
-    }
-    return sign | h;
+    asm("" : "+v"(f));
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
 // binary16 bits -> fp32, exact.

@@ -56,18 +56,30 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float
     }
     amax = wave_max(amax);
     const float s = (amax == 0.0f) ? 0.0f : amax / 448.0f;  // correctly rounded division
+    // x / s, correctly rounded: for amax >= 2^-90 from the correctly rounded
+    // reciprocal r = 1/s with one fma correction, q = q0 + (x - q0 s) r with
+    // q0 = x r (Markstein's theorem; the residual x - q0 s is exact in an fma).
+    // Smaller rows, where 1/s can overflow, divide.  Wave-uniform branch.
+    const bool recip = amax >= 0x1p-90f;
+    const float r = recip ? 1.0f / s : 0.0f;
     uint8_t* cr = codes + row * dim;
 #pragma unroll
     for (int it = 0; it < ITER; it++) {
         const int base = it * 512 + lane * 8;
         if (base < dim) {
-            uint32_t lo = 0, hi = 0;
-            if (s != 0.0f) {
+            float qv[8];
+            if (recip) {
 #pragma unroll
-                for (int j = 0; j < 4; j++) lo |= e4m3_rne(v[it][j] / s) << (8 * j);
+                for (int j = 0; j < 8; j++) {
+                    const float q0 = v[it][j] * r;
+                    qv[j] = __builtin_fmaf(__builtin_fmaf(-q0, s, v[it][j]), r, q0);
+                }
+            } else {
 #pragma unroll
-                for (int j = 0; j < 4; j++) hi |= e4m3_rne(v[it][4 + j] / s) << (8 * j);
+                for (int j = 0; j < 8; j++) qv[j] = (s != 0.0f) ? v[it][j] / s : 0.0f;
             }
+            const uint32_t lo = e4m3x2_rne(qv[0], qv[1]) | (e4m3x2_rne(qv[2], qv[3]) << 16);
+            const uint32_t hi = e4m3x2_rne(qv[4], qv[5]) | (e4m3x2_rne(qv[6], qv[7]) << 16);
             *reinterpret_cast<uint2*>(cr + base) = make_uint2(lo, hi);
         }
     }
@@ -385,7 +397,7 @@ __global__ void k_convert(int kind, const void* __restrict__ in, int64_t n, void
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         switch (kind) {
             case KVQ_CVT_F32_TO_E4M3:
-                ((uint8_t*)out)[i] = (uint8_t)e4m3_rne(((const float*)in)[i]);
+                ((uint8_t*)out)[i] = (uint8_t)(e4m3x2_rne(((const float*)in)[i], 0.0f) & 0xFFu);
                 break;
             case KVQ_CVT_E4M3_TO_BF16:
                 ((uint16_t*)out)[i] = (uint16_t)e4m3_to_bf16(((const uint8_t*)in)[i]);

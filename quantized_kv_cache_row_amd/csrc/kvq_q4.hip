@@ -194,14 +194,6 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
     }
 }
 
-// fp32 -> binary16 bits by v_cvt_f16_f32 (round to nearest even).  The value is
-// made opaque first: otherwise the compiler fuses the product that feeds it into
-// v_fma_mix with a +0 addend, which turns a -0 product into +0.
-__device__ __forceinline__ uint32_t f16_bits_hw(float f) {
-    asm("" : "+v"(f));
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
 // One 16-lane group per destination head-row, four head-row groups per workgroup
 // (64 head-rows): the lookups of all four come first, so their dependent loads
 // (offsets, page table, pool) overlap instead of running one chain per group.
@@ -254,8 +246,8 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cach
             const int q0 = (int)((two >> shift) & 15u);
             const int q1 = (int)((two >> (8 + shift)) & 15u);
             // (q - 8) d is exact in fp32; the hardware conversion rounds it to nearest even
-            const uint32_t h0 = f16_bits_hw((float)(q0 - 8) * d);
-            const uint32_t h1 = f16_bits_hw((float)(q1 - 8) * d);
+            const uint32_t h0 = f32_to_f16_rne((float)(q0 - 8) * d);
+            const uint32_t h1 = f32_to_f16_rne((float)(q1 - 8) * d);
             out[i] = h0 | (h1 << 16);
         }
         uint16_t* dst = (plane ? v_dst : k_dst) + hr[g] * 256 + lane * 16;

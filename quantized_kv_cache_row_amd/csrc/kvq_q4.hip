@@ -155,7 +155,11 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_append_q4_0(kvq_q4_cach
 #pragma unroll
     for (int i = 0; i < 16; i++) {
         const float t = __builtin_fmaf(v[i], id, 8.5f);
-        qn[i] = !(t >= 0.0f) ? 0u : (t >= 15.0f ? 15u : (uint32_t)(int)t);
+        // v_cvt_u32_f32 truncates toward zero, gives 0 for negatives and NaN and
+        // saturates above; the min caps at 15
+        uint32_t u;
+        asm("v_cvt_u32_f32 %0, %1" : "=v"(u) : "v"(t));
+        qn[i] = min(u, 15u);
     }
     // lane 2b holds block elements 0..15, lane 2b+1 elements 16..31.
     // byte j = q_j | q_{j+16} << 4: the even lane forms bytes 0..7, the odd lane 8..15.

@@ -425,6 +425,15 @@ def test_q4_no_rotate_fixtures_and_invalid_pages():
     rows = np.zeros((1, 8, 256), np.float32)
     flat = rows.reshape(-1)
     flat[:n_blocks * 32] = fx.reshape(-1)
+    # blocks with an infinite element (head 1): the scale is -inf or +inf, 1/d is a
+    # signed zero, so fma(x, id, 8.5) is 8.5 for finite x and NaN for the infinite one
+    # (code 0 by the NaN rule)
+    rng = np.random.default_rng(4)
+    inf_blocks = rng.standard_normal((3, 32)).astype(np.float32)
+    inf_blocks[0, 5] = np.inf
+    inf_blocks[1, 17] = -np.inf
+    inf_blocks[2, 3], inf_blocks[2, 30] = -np.inf, np.inf
+    flat[256:256 + 96] = inf_blocks.reshape(-1)
     table = np.array([[2, -1]], np.int32)
     kp = torch.zeros((3 * 64, 8, 144), dtype=torch.uint8, device=DEV)
     vp = torch.zeros_like(kp)

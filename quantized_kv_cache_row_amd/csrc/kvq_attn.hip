@@ -632,6 +632,19 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // 32 ks' + 8 g + e, times sm_scale * log2(e), as a bf16 hi + lo pair.
     uint4 qh[16], rh[2], rl[2];
     float qinv;
+    // the largest |row scale| of this wave's rows sets the probabilities' power-of-two
+    // scale rsc (loads clamped to the wave's range, issued with the query's)
+    float rsc;
+    {
+        float rmw = 0.0f;
+        if (w0 < w1) {  // wave-uniform
+            const int iters = (int)((w1 - w0 + 63) / 64);
+#pragma unroll 4
+            for (int k = 0; k < iters; k++)
+                rmw = fmaxf(rmw, fabsf(a.row_scale[min(w0 + lane + 64 * (int64_t)k, w1 - 1)]));
+        }
+        rsc = pow2_scale_for(wave_max(rmw), -1);  // rho * rsc < 1 for every row; 1 if all are 0
+    }
     {
         // unconditional loads (clamped head): a guarded load would wait for every load in flight
         const int sq = (int)plan_s[2];
@@ -692,16 +705,14 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 
     // Softmax with a fixed reference per wave and head: p = 2^(s - m_run), with
     // m_run the first tile's maximum, and probabilities enter the matrix cores
-    // as fp16 p * rho * rsc with rsc a power of two (rho * rsc in [0.5, 1) for
-    // the first tile's largest row scale).  A later tile may exceed them by 2^8
-    // (scores) and 2^4 (row scales), so p * rho * rsc <= 2^12.  A tile beyond
-    // that raises the references and the wave starts its rows again: the
+    // as fp16 p * rho * rsc (rho * rsc < 1 for all of the wave's rows).  A later
+    // tile may exceed the reference by 2^8, so p * rho * rsc <= 2^8.  A tile
+    // beyond that raises the reference and the wave starts its rows again: the
     // accumulators are never rescaled inside the loop (they stay in the matrix
     // cores' registers), and for all but adversarial score sequences the first
     // pass is the only one.
     f32x4_t acc_o[32];
     float m_run = -INFINITY, l_part = 0.0f;
-    float rsc = 0.0f;  // 0 until a row with a nonzero scale
     bool restarted = false;
     for (;;) {
 #pragma unroll
@@ -735,24 +746,37 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         auto chunk = [&](const uint8_t* base, int j) { return *reinterpret_cast<const uint4*>(base + 64 * j); };
         f32x4_t sl[2], sr[2];
         sl[0] = sl[1] = sr[0] = sr[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        uint4 na = chunk(pa, 0), nb = chunk(pbp, 0);
+        // the reads run two k-chunks ahead and the conversions one, so a step's
+        // matrix-core work and the next step's conversions are independent
+        uint4 ca = chunk(pa, 0), cbv = chunk(pbp, 0);
+        uint4 na = chunk(pa, 1), nb = chunk(pbp, 1);
+        uint4 a0 = e4m3x8_to_f16x8(ca.x, ca.y), a1 = e4m3x8_to_f16x8(ca.z, ca.w);
+        uint4 b0 = e4m3x8_to_f16x8(cbv.x, cbv.y), b1 = e4m3x8_to_f16x8(cbv.z, cbv.w);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            const uint4 ca = na, cbv = nb;
+            const uint4 ua0 = a0, ua1 = a1, ub0 = b0, ub1 = b1;
             if (j < 7) {
-                na = chunk(pa, j + 1);
-                nb = chunk(pbp, j + 1);
+                ca = na;
+                cbv = nb;
+                if (j < 6) {
+                    na = chunk(pa, j + 2);
+                    nb = chunk(pbp, j + 2);
+                }
             }
 #pragma unroll
             for (int k = 3 * j; k < 3 * j + 3; k++)
                 if (k < NDMA) dma_one(k, tn, buf ^ 1);
             __builtin_amdgcn_sched_barrier(0);  // the look-ahead reads issue before this chunk's math
-            const uint4 a0 = e4m3x8_to_f16x8(ca.x, ca.y), a1 = e4m3x8_to_f16x8(ca.z, ca.w);
-            const uint4 b0 = e4m3x8_to_f16x8(cbv.x, cbv.y), b1 = e4m3x8_to_f16x8(cbv.z, cbv.w);
-            sl[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a0), as_f16x8(qh[2 * j]), sl[0], 0, 0, 0);
-            sl[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(b0), as_f16x8(qh[2 * j]), sl[1], 0, 0, 0);
-            sl[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a1), as_f16x8(qh[2 * j + 1]), sl[0], 0, 0, 0);
-            sl[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(b1), as_f16x8(qh[2 * j + 1]), sl[1], 0, 0, 0);
+            if (j < 7) {
+                a0 = e4m3x8_to_f16x8(ca.x, ca.y);
+                a1 = e4m3x8_to_f16x8(ca.z, ca.w);
+                b0 = e4m3x8_to_f16x8(cbv.x, cbv.y);
+                b1 = e4m3x8_to_f16x8(cbv.z, cbv.w);
+            }
+            sl[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ua0), as_f16x8(qh[2 * j]), sl[0], 0, 0, 0);
+            sl[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ub0), as_f16x8(qh[2 * j]), sl[1], 0, 0, 0);
+            sl[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ua1), as_f16x8(qh[2 * j + 1]), sl[0], 0, 0, 0);
+            sl[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ub1), as_f16x8(qh[2 * j + 1]), sl[1], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -787,17 +811,20 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                            fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
         tmax = max_xor16_xor32(tmax);
-        float rmx = fmaxf(fmaxf(fmaxf(fabsf(rr[0][0]), fabsf(rr[0][1])), fmaxf(fabsf(rr[0][2]), fabsf(rr[0][3]))),
-                          fmaxf(fmaxf(fabsf(rr[1][0]), fabsf(rr[1][1])), fmaxf(fabsf(rr[1][2]), fabsf(rr[1][3]))));
-        rmx = max_xor16_xor32(rmx);  // largest |rho| of the tile, over the whole wave
-        if (m_run == -INFINITY) m_run = tmax;                         // first tile: every row valid
-        if (rsc == 0.0f && rmx > 0.0f) rsc = pow2_scale_for(rmx, -1);  // wave-uniform
+        // the first column group's PV operands are converted now (independent of
+        // the softmax, so they fill its latency), and the second group's reads issued
+        uint4 pv0[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) pv0[i] = e4m3x8_to_f16x8((uint32_t)nv[i][0], (uint32_t)nv[i][1]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) nv[i] = trd(8 + i);
+        if (m_run == -INFINITY) m_run = tmax;  // first tile: every row valid
         const bool over = tmax > m_run + LAZY_LOG2;
-        if (__any(over) || rmx * rsc > 16.0f) {
-            // raise the references past this tile and start the rows again
+        if (__any(over)) {
+            // raise the reference past this tile and start the rows again
             m_run = fmaxf(m_run, tmax);
-            if (rmx * rsc > 16.0f) rsc = pow2_scale_for(rmx, -1);
             again = true;
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): no LDS read pending when the buffers refill
             break;
         }
         float psum = 0.0f;
@@ -819,7 +846,11 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
         // ---- PV: groups of 8 column blocks, the next group's reads in flight
 #pragma unroll
-        for (int grp = 0; grp < 4; grp++) {
+        for (int i = 0; i < 8; i++)
+            acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pv0[i]), bop, acc_o[i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int grp = 1; grp < 4; grp++) {
             i32x2_t cv[8];
 #pragma unroll
             for (int i = 0; i < 8; i++) cv[i] = nv[i];

@@ -572,11 +572,30 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int hg = (int)(local % p.n_groups);
     if (c >= p.max_chunks) return;
     const int head = hg * MF_HEADS + n;
-    if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
-
-    __syncthreads();  // plan_s
-    if (plan_s[2] < 0) return;  // no such chunk (workgroup-uniform)
-    const int64_t r0 = plan_s[0], r1 = plan_s[1];
+    int64_t r0, r1;
+    int sq;
+    if (a.n_seqs == 1) {
+        // one sequence holds rows 0 .. total_rows - 1 (seq_offsets[0] = 0 and
+        // seq_offsets[1] = total_rows by the interface): chunk c starts at row
+        // c * split, with no loads and no barrier
+        const int64_t split = p.split_rows;
+        const int64_t nch = max((int64_t)1, (a.total_rows + split - 1) / split);
+        if (c >= nch) return;  // workgroup-uniform
+        r0 = c * split;
+        r1 = min(a.total_rows, r0 + split);
+        sq = 0;
+        if (blockIdx.x == 0 && tid == 0) {
+            p.chunk_prefix[0] = 0;
+            p.chunk_prefix[1] = nch;
+        }
+    } else {
+        if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
+        __syncthreads();  // plan_s
+        if (plan_s[2] < 0) return;  // no such chunk (workgroup-uniform)
+        r0 = plan_s[0];
+        r1 = plan_s[1];
+        sq = (int)plan_s[2];
+    }
     const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
     const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
 
@@ -624,7 +643,6 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 #pragma unroll
         for (int k = 0; k < NDMA; k++) dma_one(k, t0, buf);
     };
-    if (w0 < w1) load_tile(w0, 0);  // the first tile's loads overlap the query preparation
 
     // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
     // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
@@ -636,33 +654,72 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // scale rsc (loads clamped to the wave's range, issued with the query's)
     float rsc;
     {
+        // The group's 16 query heads are loaded once per workgroup: wave w loads
+        // heads 4 w .. 4 w + 3 (fp32) into its second code buffer, which is free
+        // until the first tile's next-tile DMA (after the barrier at the end of
+        // this block).  Head k's latent row sits at QS_ROW * (k % 4) + 64 * (k / 4)
+        // and its rope row at QS_ROPE + QS_RROW * (k % 4) + 64 * (k / 4) of
+        // raw[k / 4][1]: the 16-byte row pads and the 64-byte skew put the 16 heads
+        // one read serves on distinct bank groups.  These loads and the row-scale
+        // loads are the only ones waited for; the first tile's DMA is issued after
+        // them (a wait on the load counter would otherwise wait for the whole DMA
+        // burst), so its latency overlaps the query conversion.
+        constexpr int QS_ROW = DL * 4 + 16, QS_ROPE = 8448, QS_RROW = DR * 4 + 16;
+        static_assert(QS_ROPE >= 3 * QS_ROW + 192 + DL * 4 && QS_ROPE % 256 == 0 &&
+                          QS_ROPE + 3 * QS_RROW + 192 + DR * 4 <= RAW_TILE, "query staging fits a code buffer");
+        const bool hv = head < a.n_heads;
         float rmw = 0.0f;
-        if (w0 < w1) {  // wave-uniform
-            const int iters = (int)((w1 - w0 + 63) / 64);
-#pragma unroll 4
-            for (int k = 0; k < iters; k++)
-                rmw = fmaxf(rmw, fabsf(a.row_scale[min(w0 + lane + 64 * (int64_t)k, w1 - 1)]));
+        {
+            // unconditional loads (clamped heads): a guarded load would wait for every load in flight
+            const int hq = hg * MF_HEADS + 4 * wave;  // first head of this wave's quarter
+            float4 sv[9];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int f = 64 * i + lane;  // float4 f % 128 of head f / 128
+                const int hh = min(hq + (f >> 7), a.n_heads - 1);
+                sv[i] = *reinterpret_cast<const float4*>(a.q_lat + ((int64_t)sq * a.n_heads + hh) * DL + 4 * (f & 127));
+            }
+            {
+                const int hh = min(hq + (lane >> 4), a.n_heads - 1);
+                sv[8] = *reinterpret_cast<const float4*>(a.q_rope + ((int64_t)sq * a.n_heads + hh) * DR + 4 * (lane & 15));
+            }
+            // the first 256 of the wave's row scales, unconditionally (clamped; with no
+            // rows at all the loads read the query instead and are discarded)
+            const float* rsp = a.total_rows > 0 ? a.row_scale : a.q_lat;
+            const int64_t rlast = w1 > w0 ? w1 - 1 : 0;
+            float rs4[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) rs4[u] = rsp[min(w0 + lane + 64 * u, rlast)];
+            // (used before the stores, so the compiler issues them ahead of the stores' waits)
+            rmw = w0 < w1 ? fmaxf(fmaxf(fabsf(rs4[0]), fabsf(rs4[1])), fmaxf(fabsf(rs4[2]), fabsf(rs4[3]))) : 0.0f;
+            uint8_t* const qst = &raw[wave][1][0];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int f = 64 * i + lane;
+                *reinterpret_cast<float4*>(qst + QS_ROW * (f >> 7) + 64 * wave + 16 * (f & 127)) = sv[i];
+            }
+            *reinterpret_cast<float4*>(qst + QS_ROPE + QS_RROW * (lane >> 4) + 64 * wave + 16 * (lane & 15)) = sv[8];
+            // the rest of a quarter longer than 256 rows
+            for (int64_t t = w0 + 256 + lane; t < w1; t += 64) rmw = fmaxf(rmw, fabsf(a.row_scale[t]));
         }
         rsc = pow2_scale_for(wave_max(rmw), -1);  // rho * rsc < 1 for every row; 1 if all are 0
-    }
-    {
-        // unconditional loads (clamped head): a guarded load would wait for every load in flight
-        const int sq = (int)plan_s[2];
-        const bool hv = head < a.n_heads;
-        const float* ql = a.q_lat + ((int64_t)sq * a.n_heads + min(head, a.n_heads - 1)) * DL;
-        const float* qr = a.q_rope + ((int64_t)sq * a.n_heads + min(head, a.n_heads - 1)) * DR;
+        if (w0 < w1) load_tile(w0, 0);
+        wg_barrier_lds();  // every quarter is in LDS (the DMA stays in flight)
+        // lane (g, n): head n's dims 64 j + 16 g + 8 hh + e and rope dims 32 k + 8 g + e
+        const uint8_t* const hrow = &raw[n >> 2][1][0] + QS_ROW * (n & 3) + 64 * (n >> 2);
+        const uint8_t* const rrow = &raw[n >> 2][1][0] + QS_ROPE + QS_RROW * (n & 3) + 64 * (n >> 2);
         float4 v[32], w[4];
 #pragma unroll
         for (int ks = 0; ks < 16; ks++) {
-            const float* src = ql + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1);
+            const uint8_t* src = hrow + 4 * (64 * (ks >> 1) + 16 * g + 8 * (ks & 1));
             v[2 * ks] = *reinterpret_cast<const float4*>(src);
-            v[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 4);
+            v[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 16);
         }
 #pragma unroll
         for (int k = 0; k < 2; k++) {
-            const float* src = qr + 32 * k + 8 * g;
+            const uint8_t* src = rrow + 4 * (32 * k + 8 * g);
             w[2 * k] = *reinterpret_cast<const float4*>(src);
-            w[2 * k + 1] = *reinterpret_cast<const float4*>(src + 4);
+            w[2 * k + 1] = *reinterpret_cast<const float4*>(src + 16);
         }
         float qmax = 0.0f;
 #pragma unroll
@@ -692,6 +749,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             rl[k] = make_uint4(pack_bf16x2(f[0] - b[0], f[1] - b[1]), pack_bf16x2(f[2] - b[2], f[3] - b[3]),
                                pack_bf16x2(f[4] - b[4], f[5] - b[5]), pack_bf16x2(f[6] - b[6], f[7] - b[7]));
         }
+        wg_barrier_lds();  // every wave has read the staged query before the second buffers refill
     }
     auto tile_row = [](int rb, int nn) { return 8 * (nn >> 2) + 4 * rb + (nn & 3); };
     // per-lane LDS read offsets (bytes within a tile)

@@ -626,8 +626,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const uint32_t lds_rope = lds_offset(&rope_s[wave][0]);
     const uint32_t lds_rho = lds_offset(&rho_s[wave][0][0]);
     constexpr int NDMA = RAW_DMA + ROPE_DMA + 1;
-    auto dma_one = [&](int k, int64_t t0, int buf) __attribute__((always_inline)) {
-        const int lim = (int)min((int64_t)MF_TILE, a.total_rows - t0);  // rows inside the arrays
+    auto dma_one = [&](int k, int64_t t0, int buf, int lim) __attribute__((always_inline)) {
+        // lim: rows of the tile inside the arrays (offsets are clamped to them)
         if (k < RAW_DMA) {
             dma_lds_b128(a.codes + t0 * RAW_ROW, min(voff_c[k], (uint32_t)lim * RAW_ROW - 16u),
                          __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE + 1024u * k));
@@ -640,8 +640,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
     };
     auto load_tile = [&](int64_t t0, int buf) __attribute__((always_inline)) {
+        const int lim = (int)min((int64_t)MF_TILE, a.total_rows - t0);
 #pragma unroll
-        for (int k = 0; k < NDMA; k++) dma_one(k, t0, buf);
+        for (int k = 0; k < NDMA; k++) dma_one(k, t0, buf, lim);
     };
 
     // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
@@ -654,57 +655,61 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // scale rsc (loads clamped to the wave's range, issued with the query's)
     float rsc;
     {
-        // The group's 16 query heads are loaded once per workgroup: wave w loads
-        // heads 4 w .. 4 w + 3 (fp32) into its second code buffer, which is free
-        // until the first tile's next-tile DMA (after the barrier at the end of
-        // this block).  Head k's latent row sits at QS_ROW * (k % 4) + 64 * (k / 4)
-        // and its rope row at QS_ROPE + QS_RROW * (k % 4) + 64 * (k / 4) of
-        // raw[k / 4][1]: the 16-byte row pads and the 64-byte skew put the 16 heads
-        // one read serves on distinct bank groups.  These loads and the row-scale
-        // loads are the only ones waited for; the first tile's DMA is issued after
-        // them (a wait on the load counter would otherwise wait for the whole DMA
-        // burst), so its latency overlaps the query conversion.
-        constexpr int QS_ROW = DL * 4 + 16, QS_ROPE = 8448, QS_RROW = DR * 4 + 16;
+        // The group's 16 query heads are loaded once per workgroup: wave w brings
+        // heads 4 w .. 4 w + 3 (fp32) and the first 256 of its rows' scales by DMA
+        // into its second code buffer, which is free until the first tile's
+        // next-tile DMA (after the barrier at the end of this block).  Head k's
+        // latent row sits at QS_ROW * (k % 4) + 64 * (k / 4) of raw[k / 4][1] (the
+        // 16-byte row pads and the 64-byte skew put the 16 heads one read serves on
+        // distinct bank groups), its rope row at QS_ROPE + QS_RROW * (k % 4) +
+        // 64 * (k / 4), the scales at QS_RS.  The first tile's DMA goes out right
+        // after, and the wait below covers only the staging DMAs, so the three
+        // latencies overlap.
+        constexpr int QS_ROW = DL * 4 + 16, QS_ROPE = 8448, QS_RROW = DR * 4, QS_RS = 9728;
         static_assert(QS_ROPE >= 3 * QS_ROW + 192 + DL * 4 && QS_ROPE % 256 == 0 &&
-                          QS_ROPE + 3 * QS_RROW + 192 + DR * 4 <= RAW_TILE, "query staging fits a code buffer");
+                          QS_RS >= QS_ROPE + 192 + 4 * QS_RROW && QS_RS + 1024 <= RAW_TILE,
+                      "query staging fits a code buffer");
         const bool hv = head < a.n_heads;
-        float rmw = 0.0f;
+        uint8_t* const qst = &raw[wave][1][0];
+        const uint32_t lqs = __builtin_amdgcn_readfirstlane(lds_offset(qst));
         {
-            // unconditional loads (clamped heads): a guarded load would wait for every load in flight
-            const int hq = hg * MF_HEADS + 4 * wave;  // first head of this wave's quarter
-            float4 sv[9];
+            const int hq = hg * MF_HEADS + 4 * wave;  // first head of this wave's quarter (clamped below)
+            const float* qb = a.q_lat + (int64_t)sq * a.n_heads * DL;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                const int f = 64 * i + lane;  // float4 f % 128 of head f / 128
-                const int hh = min(hq + (f >> 7), a.n_heads - 1);
-                sv[i] = *reinterpret_cast<const float4*>(a.q_lat + ((int64_t)sq * a.n_heads + hh) * DL + 4 * (f & 127));
+                const int hi = min(hq + (i >> 1), a.n_heads - 1);
+                dma_lds_b128(qb + (int64_t)hi * DL, 1024u * (i & 1) + 16u * lane,
+                             lqs + QS_ROW * (i >> 1) + 64 * wave + 1024 * (i & 1));
             }
-            {
-                const int hh = min(hq + (lane >> 4), a.n_heads - 1);
-                sv[8] = *reinterpret_cast<const float4*>(a.q_rope + ((int64_t)sq * a.n_heads + hh) * DR + 4 * (lane & 15));
-            }
-            // the first 256 of the wave's row scales, unconditionally (clamped; with no
-            // rows at all the loads read the query instead and are discarded)
+            const int hr = min(hq + (lane >> 4), a.n_heads - 1);
+            dma_lds_b128(a.q_rope + (int64_t)sq * a.n_heads * DR, (uint32_t)hr * (DR * 4) + 16u * (lane & 15),
+                         lqs + QS_ROPE + 64 * wave);
+            // the row scales: clamped to the wave's rows; with no rows the loads read
+            // the query instead (always present) and are discarded
             const float* rsp = a.total_rows > 0 ? a.row_scale : a.q_lat;
-            const int64_t rlast = w1 > w0 ? w1 - 1 : 0;
-            float rs4[4];
+            const int64_t rb = w0 < w1 ? w0 : 0;
+            const int rl = w0 < w1 ? (int)min((int64_t)255, w1 - 1 - w0) : 0;
 #pragma unroll
-            for (int u = 0; u < 4; u++) rs4[u] = rsp[min(w0 + lane + 64 * u, rlast)];
-            // (used before the stores, so the compiler issues them ahead of the stores' waits)
-            rmw = w0 < w1 ? fmaxf(fmaxf(fabsf(rs4[0]), fabsf(rs4[1])), fmaxf(fabsf(rs4[2]), fabsf(rs4[3]))) : 0.0f;
-            uint8_t* const qst = &raw[wave][1][0];
+            for (int u = 0; u < 4; u++)
+                dma_lds_b32(rsp + rb, 4u * (uint32_t)min(64 * u + lane, rl), lqs + QS_RS + 256 * u);
+        }
+        if (w0 < w1) {  // wave-uniform
+            load_tile(w0, 0);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | 7 | (16 << 10));  // vmcnt(23): the staging DMAs have landed
+        } else {
+            vm_wait_all();
+        }
+        static_assert(NDMA == 23, "the wait above counts the first tile's DMA instructions");
+        wg_barrier_lds();  // every quarter is in LDS (the first tile's DMA stays in flight)
+        float rmw = 0.0f;
+        if (w0 < w1) {  // wave-uniform
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int f = 64 * i + lane;
-                *reinterpret_cast<float4*>(qst + QS_ROW * (f >> 7) + 64 * wave + 16 * (f & 127)) = sv[i];
-            }
-            *reinterpret_cast<float4*>(qst + QS_ROPE + QS_RROW * (lane >> 4) + 64 * wave + 16 * (lane & 15)) = sv[8];
+            for (int u = 0; u < 4; u++)
+                rmw = fmaxf(rmw, fabsf(*reinterpret_cast<const float*>(qst + QS_RS + 256 * u + 4 * lane)));
             // the rest of a quarter longer than 256 rows
             for (int64_t t = w0 + 256 + lane; t < w1; t += 64) rmw = fmaxf(rmw, fabsf(a.row_scale[t]));
         }
         rsc = pow2_scale_for(wave_max(rmw), -1);  // rho * rsc < 1 for every row; 1 if all are 0
-        if (w0 < w1) load_tile(w0, 0);
-        wg_barrier_lds();  // every quarter is in LDS (the DMA stays in flight)
         // lane (g, n): head n's dims 64 j + 16 g + 8 hh + e and rope dims 32 k + 8 g + e
         const uint8_t* const hrow = &raw[n >> 2][1][0] + QS_ROW * (n & 3) + 64 * (n >> 2);
         const uint8_t* const rrow = &raw[n >> 2][1][0] + QS_ROPE + QS_RROW * (n & 3) + 64 * (n >> 2);
@@ -797,6 +802,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         // the next tile's DMA, three instructions per score step (after the last
         // tile: this tile again, into the free buffer)
         const int64_t tn = more ? t0 + MF_TILE : t0;
+        // after the last tile the reload only has to be harmless: one row, from the cache
+        const int limn = more ? (int)min((int64_t)MF_TILE, a.total_rows - tn) : 1;
         const uint8_t* tb = raw[wave][buf];
         // ---- scores: both row blocks together, the reads one k-chunk ahead
         const uint8_t* pa = tb + rd_a;
@@ -823,7 +830,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             }
 #pragma unroll
             for (int k = 3 * j; k < 3 * j + 3; k++)
-                if (k < NDMA) dma_one(k, tn, buf ^ 1);
+                if (k < NDMA) dma_one(k, tn, buf ^ 1, limn);
             __builtin_amdgcn_sched_barrier(0);  // the look-ahead reads issue before this chunk's math
             if (j < 7) {
                 a0 = e4m3x8_to_f16x8(ca.x, ca.y);

@@ -556,6 +556,34 @@ __device__ __forceinline__ void plan_chunk(const kvq_attn_args& a, const Plan& p
     if (writer && lane == 0) p.chunk_prefix[a.n_seqs] = run;
 }
 
+// This workgroup's chunk c: rows [r0, r1) of sequence sq; false if there is
+// no such chunk (workgroup-uniform).  One sequence holds rows 0 .. total_rows - 1
+// (seq_offsets[0] = 0 and seq_offsets[1] = total_rows by the interface), so its
+// chunks need no loads and no barrier; otherwise wave 0 scans the offsets.
+__device__ __forceinline__ bool locate_chunk(const kvq_attn_args& a, const Plan& p, int64_t c, int64_t* plan_s,
+                                             int wave, int lane, int64_t& r0, int64_t& r1, int& sq) {
+    if (a.n_seqs == 1) {
+        const int64_t split = p.split_rows;
+        const int64_t nch = max((int64_t)1, (a.total_rows + split - 1) / split);
+        if (c >= nch) return false;
+        r0 = c * split;
+        r1 = min(a.total_rows, r0 + split);
+        sq = 0;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            p.chunk_prefix[0] = 0;
+            p.chunk_prefix[1] = nch;
+        }
+        return true;
+    }
+    if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
+    __syncthreads();  // plan_s
+    if (plan_s[2] < 0) return false;
+    r0 = plan_s[0];
+    r1 = plan_s[1];
+    sq = (int)plan_s[2];
+    return true;
+}
+
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
     __shared__ __align__(16) uint8_t rope_s[MF_WAVES][ROPE_TILE];      // rope keys (bf16)
@@ -574,28 +602,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const int head = hg * MF_HEADS + n;
     int64_t r0, r1;
     int sq;
-    if (a.n_seqs == 1) {
-        // one sequence holds rows 0 .. total_rows - 1 (seq_offsets[0] = 0 and
-        // seq_offsets[1] = total_rows by the interface): chunk c starts at row
-        // c * split, with no loads and no barrier
-        const int64_t split = p.split_rows;
-        const int64_t nch = max((int64_t)1, (a.total_rows + split - 1) / split);
-        if (c >= nch) return;  // workgroup-uniform
-        r0 = c * split;
-        r1 = min(a.total_rows, r0 + split);
-        sq = 0;
-        if (blockIdx.x == 0 && tid == 0) {
-            p.chunk_prefix[0] = 0;
-            p.chunk_prefix[1] = nch;
-        }
-    } else {
-        if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
-        __syncthreads();  // plan_s
-        if (plan_s[2] < 0) return;  // no such chunk (workgroup-uniform)
-        r0 = plan_s[0];
-        r1 = plan_s[1];
-        sq = (int)plan_s[2];
-    }
+    if (!locate_chunk(a, p, c, plan_s, wave, lane, r0, r1, sq)) return;  // workgroup-uniform
     const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
     const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
 
@@ -1102,18 +1109,16 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
     if (c >= p.max_chunks) return;
     const int head = hg * TQ4_HEADS + MF_HEADS * wave + n;  // may exceed n_heads (its query is zero)
     constexpr int CB = DL / 2;                                 // code bytes per row
-    if (wave == 0) plan_chunk(a, p, c, plan_s, lane);
-    __syncthreads();  // plan_s
-    const int sq = (int)plan_s[2];
-    if (sq < 0) return;  // no such chunk (workgroup-uniform)
-    const int64_t r0 = plan_s[0], r1 = plan_s[1];
+    int64_t r0, r1;
+    int sq;
+    if (!locate_chunk(a, p, c, plan_s, wave, lane, r0, r1, sq)) return;  // workgroup-uniform
     const int ntiles = (int)((r1 - r0 + MF_TILE - 1) / MF_TILE);
 
     // decode share of this wave: tile row 8 wave + lane / 8, code bytes
     // 32 (lane % 8) .. + 31 (dims 64 (lane % 8) .. + 63), rope bytes 16 (lane % 8)
     const int drow = 8 * wave + (lane >> 3), dq = lane & 7;
     uint4 ca[2], cr;  // codes and rope of the tile to decode next
-    float cs;         // its row scale
+    float cs;         // its row radius (scaled by 1 / sqrt(512) when it is stored)
     auto load_share = [&](int t) __attribute__((always_inline)) {
         const int64_t t0 = r0 + (int64_t)MF_TILE * t;
         const int64_t row = t0 + min(drow, (int)(r1 - t0) - 1);  // rows past the chunk re-read its last row
@@ -1121,7 +1126,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
         ca[0] = *reinterpret_cast<const uint4*>(cp);
         ca[1] = *reinterpret_cast<const uint4*>(cp + 16);
         cr = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 8 * dq);
-        cs = a.row_scale[row] * INV_SQRT_DL;
+        cs = a.row_scale[row];
     };
     const Tq4Lut lut = make_tq4_lut();
     auto decode_share = [&](int buf) __attribute__((always_inline)) {
@@ -1130,8 +1135,21 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
         for (int i = 0; i < 8; i++)
             *reinterpret_cast<uint4*>(&xt[buf][drow][64 * dq + 8 * i]) = tq4x8_to_f16x8(w[i], lut);
         *reinterpret_cast<uint4*>(&kt[buf][drow][8 * dq]) = cr;
-        rho_s[buf][drow] = cs;  // the 8 lanes of a row store the same value
+        rho_s[buf][drow] = cs * INV_SQRT_DL;  // the 8 lanes of a row store the same value
     };
+    // ---- query operands (prepared once per sequence and head), loaded first: the
+    // row-scale loop below waits for its loads, and with them for these
+    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + head) * QPACK_U4;
+    uint4 qh[16], rh[2], rl[2];
+#pragma unroll
+    for (int k = 0; k < 16; k++) qh[k] = qp[16 * g + k];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        rh[k] = qp[QP_RH + 2 * g + k];
+        rl[k] = qp[QP_RL + 2 * g + k];
+    }
+    const float k1 = a.sm_scale * LOG2E * p.q_inv[(int64_t)sq * p.heads_padded + head];
+
     if (ntiles > 0) load_share(0);
 
     // ---- the chunk's largest row scale (four loads in flight per thread)
@@ -1143,17 +1161,6 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
 #pragma unroll
         for (int u = 0; u < 4; u++) rmax = fmaxf(rmax, fabsf(x[u]));
     }
-    // ---- query operands (prepared once per sequence and head)
-    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + head) * QPACK_U4;
-    uint4 qh[16], rh[2], rl[2];
-#pragma unroll
-    for (int k = 0; k < 16; k++) qh[k] = qp[16 * g + k];
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        rh[k] = qp[QP_RH + 2 * g + k];
-        rl[k] = qp[QP_RL + 2 * g + k];
-    }
-    const float k1 = a.sm_scale * LOG2E * p.q_inv[(int64_t)sq * p.heads_padded + head];
     rmax = wave_max(rmax);
     if (lane == 0) red_s[wave] = rmax;
     __syncthreads();

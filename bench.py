@@ -217,6 +217,34 @@ def measure_other_rows(torch, kvq, workloads, x_kv8):
     del xr
     torch.cuda.empty_cache()
 
+    # sparse (DSA-style) decode: a 32768-row fp8 cache, 16 queries x 2048 selected rows, 128 heads;
+    # the selected rows are gathered into the workspace, then the dense kernels run
+    w = workloads.dsa_sparse_decode()
+    xs = torch.from_numpy(w.latent).to(dev)
+    cs = torch.empty((w.cache_rows, 512), dtype=torch.uint8, device=dev)
+    ss = torch.empty(w.cache_rows, dtype=torch.float32, device=dev)
+    kvq.kvq_encode_fp8(xs, cs, ss)
+    krs = torch.from_numpy(w.k_rope.view(np.int16)).to(dev)
+    idx = torch.from_numpy(w.row_index).to(dev)
+    outs = torch.empty((w.n_seqs, w.n_heads, 512), dtype=torch.float32, device=dev)
+    lses = torch.empty((w.n_seqs, w.n_heads), dtype=torch.float32, device=dev)
+    sa = kvq.attn_args(1, 0, torch.from_numpy(w.offsets).to(dev), w.total_rows, cs, ss, krs,
+                       torch.from_numpy(w.q_lat).to(dev), torch.from_numpy(w.q_rope).to(dev), w.sm_scale, outs, lses)
+    sws = kvq.alloc_workspace_sparse(sa)
+    ms_sp = time_graph(torch, lambda: kvq.kvq_decode_attn_sparse(sa, idx, w.cache_rows, sws), 16)
+    gc = torch.empty((w.total_rows, 512), dtype=torch.uint8, device=dev)
+    gs = torch.empty(w.total_rows, dtype=torch.float32, device=dev)
+    gr = torch.empty((w.total_rows, 64), dtype=torch.int16, device=dev)
+    ms_g = time_graph(torch, lambda: kvq.kvq_gather_rows(1, cs, ss, krs, idx, gc, gs, gr), 16)
+    n = w.total_rows
+    res["dsa_sparse_decode_T32768_q16_k2048"] = {
+        "us_per_call": ms_sp * 1000.0, "rows/s": n / (ms_sp / 1000.0), "gather_us": ms_g * 1000.0,
+        "gather_GB/s": n * (8 + 2 * 644) / (ms_g / 1000.0) / 1e9, "rows": n, "queries": w.n_seqs}
+    log(f"dsa_sparse_decode_T32768_q16_k2048: call {ms_sp * 1000:.1f} us ({n / (ms_sp / 1000.0):.3g} rows/s), "
+        f"gather {ms_g * 1000:.1f} us ({n * (8 + 2 * 644) / (ms_g / 1000.0) / 1e9:.0f} GB/s)")
+    del xs, cs, ss, krs, idx, sws, gc, gs, gr
+    torch.cuda.empty_cache()
+
     # a9 / a10: q4_0 bulk append of the 16 prefills, then the gather of everything
     q = workloads.Q4Workload()
     tok = int(q.prefill_off[-1])

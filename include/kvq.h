@@ -206,6 +206,42 @@ int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, v
 int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, int64_t ws_bytes,
                           void* stream);
 
+/* ---- sparse (DSA-style) decode ----------------------------------------------
+ * [KV8] commit list, item 2 ("split-T kernels, DSA-aware gather"), and the
+ * rebase note on the DSA gather: a top-k selection picks the cache rows a
+ * query attends to.  The selected rows are gathered by absolute row index into
+ * a compact buffer, and the dense decode kernels consume that buffer.
+ *
+ * kvq_gather_rows copies rows row_index[0 .. n_index) of a quantized cache
+ * (codes, row_scale, k_rope: cache_rows rows; code bytes per row: 512 for
+ * KVQ_QMODE_FP8, 256 for KVQ_QMODE_TQ4) unchanged to row i of codes_out,
+ * scale_out and rope_out.
+ *  - row_index: device int64.  An index outside [0, cache_rows) is clamped
+ *    to the nearest valid row (0 or cache_rows - 1), so the call never reads
+ *    outside the cache.
+ *  - All buffers are device memory.  codes, k_rope, codes_out and rope_out
+ *    must be 16-byte aligned.
+ *  - n_index = 0 launches nothing. */
+int kvq_gather_rows(int qmode, const uint8_t* codes, const float* row_scale, const uint16_t* k_rope,
+                    int64_t cache_rows, const int64_t* row_index, int64_t n_index, uint8_t* codes_out,
+                    float* scale_out, uint16_t* rope_out, void* stream);
+
+/* kvq_decode_attn_sparse: decode attention of sequence s over the cache rows
+ * row_index[seq_offsets[s] .. seq_offsets[s+1]).
+ *  - a->seq_offsets partitions the index list, and a->total_rows = n_index is
+ *    its host copy of seq_offsets[n_seqs].
+ *  - a->codes, a->row_scale and a->k_rope describe the whole cache of
+ *    cache_rows rows.
+ *  - The result equals kvq_decode_attn over the gathered rows: the call gathers
+ *    them into the workspace (kvq_gather_rows), then runs the same kernels.
+ *  - A repeated index counts once per occurrence.
+ *  - The workspace is device memory, 256-byte aligned, of at least
+ *    kvq_decode_attn_sparse_workspace_bytes(a) bytes.  That function returns
+ *    -1 for arguments the call would refuse. */
+int64_t kvq_decode_attn_sparse_workspace_bytes(const kvq_attn_args* a);
+int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int64_t cache_rows, void* workspace,
+                           int64_t ws_bytes, void* stream);
+
 /* ---- conformance probe -------------------------------------------------------
  * Element-wise conversions exactly as the kernels perform them, so a caller
  * can check them against the format definitions (for instance over every

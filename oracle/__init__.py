@@ -290,6 +290,19 @@ def decode_attn(qmode, seq_offsets, codes, row_scale, k_rope, q_lat, q_rope, sm_
     return out, lse
 
 
+def decode_attn_sparse(qmode, index_offsets, row_index, codes, row_scale, k_rope, q_lat, q_rope, sm_scale,
+                       sign_mask=None):
+    """Sparse (DSA-style) decode attention, fp64: query s attends over the cache
+    rows row_index[index_offsets[s]:index_offsets[s+1]], a row listed twice
+    counting twice ([KV8] commit list item 2, the DSA-aware gather, and the
+    rebase note on the DSA gather: the selected rows are staged into a compact
+    buffer for the dense kernel).  By that definition it is decode_attn over the
+    listed rows in list order; the selection is numpy indexing."""
+    idx = np.asarray(row_index, np.int64)
+    return decode_attn(qmode, index_offsets, np.asarray(codes)[idx], np.asarray(row_scale)[idx],
+                       np.asarray(k_rope)[idx], q_lat, q_rope, sm_scale, sign_mask)
+
+
 # ---- q4_0 paged tier ------------------------------------------------------
 
 def q4_0_block(x32):

@@ -172,6 +172,43 @@ int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, in
     return launch_status(kvq::launch_decode_attn_stage(*a, stage, workspace, as_stream(stream)));
 }
 
+int kvq_gather_rows(int qmode, const uint8_t* codes, const float* row_scale, const uint16_t* k_rope,
+                    int64_t cache_rows, const int64_t* row_index, int64_t n_index, uint8_t* codes_out,
+                    float* scale_out, uint16_t* rope_out, void* stream) {
+    if (qmode != KVQ_QMODE_FP8 && qmode != KVQ_QMODE_TQ4) return KVQ_ERR_UNSUPPORTED;
+    if (n_index < 0 || cache_rows < 0) return KVQ_ERR_INVALID_ARG;
+    if (n_index == 0) return KVQ_OK;
+    if (cache_rows < 1 || !codes || !row_scale || !k_rope || !row_index || !codes_out || !scale_out || !rope_out)
+        return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(k_rope) || !aligned16(codes_out) || !aligned16(rope_out) ||
+        !aligned(row_scale, 4) || !aligned(scale_out, 4) || !aligned(row_index, 8))
+        return KVQ_ERR_INVALID_ARG;
+    if (n_index > ((int64_t)1 << 33)) return KVQ_ERR_UNSUPPORTED;  // grid of n_index / 4 workgroups
+    const int cb = qmode == KVQ_QMODE_TQ4 ? 256 : 512;
+    return launch_status(kvq::launch_gather_rows(cb, codes, row_scale, k_rope, cache_rows, row_index, n_index,
+                                                 codes_out, scale_out, rope_out, as_stream(stream)));
+}
+
+int64_t kvq_decode_attn_sparse_workspace_bytes(const kvq_attn_args* a) {
+    if (check_attn(a) != KVQ_OK) return -1;
+    if (a->total_rows > ((int64_t)1 << 33)) return -1;
+    return kvq::attn_sparse_workspace_bytes(*a);
+}
+
+int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int64_t cache_rows, void* workspace,
+                           int64_t ws_bytes, void* stream) {
+    int rc = check_attn(a);
+    if (rc != KVQ_OK) return rc;
+    if (a->total_rows > ((int64_t)1 << 33)) return KVQ_ERR_UNSUPPORTED;
+    if (cache_rows < 0) return KVQ_ERR_INVALID_ARG;
+    if (a->total_rows > 0 && (cache_rows < 1 || !row_index || !aligned(row_index, 8))) return KVQ_ERR_INVALID_ARG;
+    const int64_t need = kvq::attn_sparse_workspace_bytes(*a);
+    if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
+    return launch_status(
+        kvq::launch_decode_attn_sparse(*a, row_index, cache_rows, workspace, ws_bytes, as_stream(stream)));
+}
+
 int kvq_convert(int kind, const void* in, int64_t n, void* out, void* stream) {
     if (kind < KVQ_CVT_F32_TO_E4M3 || kind > KVQ_CVT_E4M3_TO_F16) return KVQ_ERR_UNSUPPORTED;
     if (n < 0) return KVQ_ERR_INVALID_ARG;

@@ -71,6 +71,9 @@ def lib():
             "kvq_decode_attn": ([ctypes.POINTER(KvqAttnArgs), vp, i64, vp], i32),
             "kvq_decode_attn_stage": ([ctypes.POINTER(KvqAttnArgs), i32, vp, i64, vp], i32),
             "kvq_convert": ([i32, vp, i64, vp, vp], i32),
+            "kvq_gather_rows": ([i32, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp], i32),
+            "kvq_decode_attn_sparse_workspace_bytes": ([ctypes.POINTER(KvqAttnArgs)], i64),
+            "kvq_decode_attn_sparse": ([ctypes.POINTER(KvqAttnArgs), vp, i64, vp, i64, vp], i32),
             "kvq_struct_layout": ([i32, ctypes.POINTER(ctypes.c_int64), i32], i32),
         }
         for name, (args, res) in sig.items():
@@ -84,7 +87,8 @@ def lib():
 def exported_symbols():
     return ["kvq_abi_version", "kvq_status_string", "kvq_row_bytes", "kvq_tq4_codebook", "kvq_encode_fp8",
             "kvq_encode_tq4", "kvq_append_q4_0", "kvq_gather_q4_0", "kvq_decode_attn_workspace_bytes",
-            "kvq_decode_attn", "kvq_decode_attn_stage", "kvq_convert", "kvq_struct_layout"]
+            "kvq_decode_attn", "kvq_decode_attn_stage", "kvq_gather_rows", "kvq_decode_attn_sparse_workspace_bytes",
+            "kvq_decode_attn_sparse", "kvq_convert", "kvq_struct_layout"]
 
 
 # ---- host-only entry points -----------------------------------------------------
@@ -232,6 +236,38 @@ def kvq_decode_attn_stage(args, stage, workspace, stream=None):
     _check("kvq_decode_attn_stage", lib().kvq_decode_attn_stage(ctypes.byref(args), int(stage),
                                                                 _ptr(workspace, torch.uint8, "workspace"),
                                                                 workspace.numel(), _stream(stream)))
+
+
+def kvq_gather_rows(qmode, codes, row_scale, k_rope, row_index, codes_out, scale_out, rope_out, stream=None):
+    """Rows row_index of the cache (codes [rows][512 or 256], row_scale [rows],
+    k_rope [rows][64] bf16 bits) copied to row i of the outputs."""
+    _check("kvq_gather_rows", lib().kvq_gather_rows(
+        int(qmode), _ptr(codes, torch.uint8, "codes"), _ptr(row_scale, torch.float32, "row_scale"),
+        _ptr(k_rope, (torch.uint16, torch.int16, torch.bfloat16), "k_rope"), codes.shape[0],
+        _ptr(row_index, torch.int64, "row_index"), row_index.numel(), _ptr(codes_out, torch.uint8, "codes_out"),
+        _ptr(scale_out, torch.float32, "scale_out"),
+        _ptr(rope_out, (torch.uint16, torch.int16, torch.bfloat16), "rope_out"), _stream(stream)))
+
+
+def kvq_decode_attn_sparse_workspace_bytes(args):
+    n = lib().kvq_decode_attn_sparse_workspace_bytes(ctypes.byref(args))
+    if n < 0:
+        raise KvqError("kvq_decode_attn_sparse_workspace_bytes", KVQ_ERR_INVALID_ARG)
+    return n
+
+
+def kvq_decode_attn_sparse(args, row_index, cache_rows, workspace, stream=None):
+    """args: KvqAttnArgs whose seq_offsets partition row_index (total_rows =
+    row_index.numel()) and whose codes / row_scale / k_rope are the whole cache of
+    cache_rows rows; workspace: at least kvq_decode_attn_sparse_workspace_bytes(args)."""
+    _check("kvq_decode_attn_sparse", lib().kvq_decode_attn_sparse(
+        ctypes.byref(args), _ptr(row_index, torch.int64, "row_index"), int(cache_rows),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def alloc_workspace_sparse(args, device="cuda"):
+    n = kvq_decode_attn_sparse_workspace_bytes(args)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def kvq_convert(kind, src, dst, stream=None):

@@ -89,6 +89,46 @@ class DecodeWorkload:
         self.sm_scale = SM_SCALE
 
 
+class SparseDecodeWorkload:
+    """DSA-style sparse decode: a cache of T rows (the recipe above, local rows 0
+    and 100 zero) and len(ks) query rows (sequences), query s attending over ks[s]
+    cache rows drawn uniformly without replacement and listed in ascending
+    order (the index lists come from the page-permutation substream)."""
+
+    def __init__(self, name, seed, T, ks, n_heads, qmode=1, sign_seed=None):
+        self.name = name
+        self.seed = seed
+        self.qmode = qmode
+        st = streams(seed)
+        self.cache_rows = int(T)
+        self.latent, zero = latent_rows(st[S_GAIN], st[S_LATENT], T, np.arange(T, dtype=np.int64))
+        rope = st[S_ROPE].standard_normal((T, DIM_ROPE), dtype=np.float32)
+        rope[zero] = 0.0
+        self.k_rope = to_bf16_bits(rope)
+        self.ks = np.asarray(ks, np.int64)
+        self.n_seqs = len(self.ks)
+        self.n_heads = n_heads
+        inv = np.float32(1.0 / math.sqrt(DIM_LAT + DIM_ROPE))
+        self.q_lat = st[S_QLAT].standard_normal((self.n_seqs, n_heads, DIM_LAT), dtype=np.float32) * inv
+        self.q_rope = st[S_QROPE].standard_normal((self.n_seqs, n_heads, DIM_ROPE), dtype=np.float32) * inv
+        rng = st[S_PERM]
+        self.row_index = np.concatenate(
+            [np.sort(rng.choice(T, size=int(k), replace=False)) for k in self.ks]).astype(np.int64)
+        self.offsets = np.zeros(self.n_seqs + 1, np.int64)
+        self.offsets[1:] = np.cumsum(self.ks)
+        self.total_rows = int(self.offsets[-1])
+        ss = streams(sign_seed)[S_SIGNS] if sign_seed is not None else st[S_SIGNS]
+        self.sign_mask = ss.integers(0, 256, size=DIM_LAT // 8, dtype=np.uint8)
+        self.sm_scale = SM_SCALE
+
+
+def dsa_sparse_decode(T=32768, n_q=16, k=2048, qmode=1):
+    """Sparse decode over a T-row cache: n_q queries, each over k selected rows
+    (top-k style), 128 heads (seed 1005)."""
+    return SparseDecodeWorkload(f"dsa-sparse-decode-T{T}-q{n_q}-k{k}-H128", 1005, T, [k] * n_q, 128, qmode=qmode,
+                                sign_seed=1002 if qmode == 2 else None)
+
+
 def tiny_fp8_decode():
     """Tiny MLA decode, fp8: 1 sequence, T = 256, 16 heads (seed 1000)."""
     return DecodeWorkload("tiny-fp8-T256-H16", 1000, [256], 16, qmode=1)

@@ -1,0 +1,165 @@
+"""GPU parity of the sparse (DSA-style) decode, through the C ABI.
+
+The row gather must match numpy indexing bit for bit (clamping included).
+Sparse attention must match the oracle, on the same codes, within
+max|err| / max|ref| <= 2e-3 (matrix cores) or <= 1e-5 (fp32 check path).
+It must also equal, bit for bit, the dense kernels run over a gathered copy
+of the rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_kv_cache_row_amd import kvq, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {kvq.KVQ_PREC_MFMA: 2e-3, kvq.KVQ_PREC_FP32: 1e-5}
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def _t(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def _np(t, dtype=None):
+    a = t.cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def rel_err(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def _encode(w):
+    x = _t(w.latent)
+    cb = 512 if w.qmode == 1 else 256
+    codes = torch.empty((w.cache_rows, cb), dtype=torch.uint8, device=DEV)
+    scales = torch.empty(w.cache_rows, dtype=torch.float32, device=DEV)
+    if w.qmode == 1:
+        kvq.kvq_encode_fp8(x, codes, scales)
+    else:
+        kvq.kvq_encode_tq4(x, _t(w.sign_mask), codes, scales)
+    return codes, scales
+
+
+def _args(w, precision, offsets, n, codes, scales, k_rope, split_rows=0):
+    out = torch.empty((w.n_seqs, w.n_heads, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.n_seqs, w.n_heads), dtype=torch.float32, device=DEV)
+    a = kvq.attn_args(w.qmode, precision, _t(offsets), n, codes, scales, k_rope, _t(w.q_lat), _t(w.q_rope),
+                      w.sm_scale, out, lse, sign_mask=_t(w.sign_mask) if w.qmode == 2 else None, split_rows=split_rows)
+    return a, out, lse
+
+
+def _sparse(w, precision, codes, scales, offsets, row_index, split_rows=0):
+    a, out, lse = _args(w, precision, offsets, len(row_index), codes, scales, _t(w.k_rope), split_rows)
+    ws = kvq.alloc_workspace_sparse(a)
+    kvq.kvq_decode_attn_sparse(a, _t(np.asarray(row_index, np.int64)), w.cache_rows, ws)
+    torch.cuda.synchronize()
+    return _np(out).astype(np.float64), _np(lse).astype(np.float64)
+
+
+def _oracle(w, codes, scales, offsets, row_index):
+    return oracle.decode_attn_sparse(w.qmode, np.asarray(offsets, np.int64), np.asarray(row_index, np.int64),
+                                     _np(codes), _np(scales), w.k_rope, w.q_lat, w.q_rope, w.sm_scale,
+                                     sign_mask=w.sign_mask if w.qmode == 2 else None)
+
+
+@pytest.mark.parametrize("qmode", [1, 2])
+def test_gather_rows_bit_exact(qmode):
+    _say(f"gather rows qmode={qmode}")
+    rng = np.random.default_rng(11)
+    T, cb = 1000, (512 if qmode == 1 else 256)
+    codes = rng.integers(0, 256, (T, cb), dtype=np.uint8)
+    sc = rng.standard_normal(T).astype(np.float32)
+    kr = rng.integers(0, 65536, (T, 64), dtype=np.uint16)
+    # duplicates, both ends, descending runs, and two indices outside the cache
+    idx = np.concatenate([[0, T - 1, T - 1, 5, -7, T + 3], np.arange(T - 1, 0, -3), rng.integers(0, T, 501)])
+    idx = idx.astype(np.int64)
+    n = len(idx)
+    co = torch.empty((n, cb), dtype=torch.uint8, device=DEV)
+    so = torch.empty(n, dtype=torch.float32, device=DEV)
+    ro = torch.empty((n, 64), dtype=torch.int16, device=DEV)
+    kvq.kvq_gather_rows(qmode, _t(codes), _t(sc), _t(kr), _t(idx), co, so, ro)
+    torch.cuda.synchronize()
+    ref = np.clip(idx, 0, T - 1)  # indices outside the cache clamp to the nearest row
+    assert np.array_equal(_np(co), codes[ref])
+    assert np.array_equal(_np(so).view(np.uint32), sc[ref].view(np.uint32))
+    assert np.array_equal(_np(ro, np.uint16), kr[ref])
+
+
+@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
+def test_sparse_attn_vs_oracle(qmode, precision):
+    _say(f"sparse attention qmode={qmode} precision={precision}")
+    w = workloads.SparseDecodeWorkload("sparse-small", 1005, 4096, [1, 37, 300, 2048], 16, qmode=qmode,
+                                       sign_seed=1002 if qmode == 2 else None)
+    codes, scales = _encode(w)
+    got, glse = _sparse(w, precision, codes, scales, w.offsets, w.row_index)
+    ref, rlse = _oracle(w, codes, scales, w.offsets, w.row_index)
+    err = rel_err(got, ref)
+    assert err <= TOL[precision], f"max|err|/max|ref| = {err:.3e}"
+    assert np.max(np.abs(glse - rlse)) <= 1e-3
+
+
+def test_sparse_edge_lists():
+    _say("sparse attention: duplicates, unsorted lists, last row, split sweep")
+    w = workloads.SparseDecodeWorkload("sparse-edges", 1005, 4096, [1, 1, 1], 16)
+    rng = np.random.default_rng(5)
+    T = w.cache_rows
+    lists = [np.array([T - 1, T - 1, T - 1, 0]), np.arange(T - 1, -1, -7), rng.integers(0, T, 333)]
+    idx = np.concatenate(lists).astype(np.int64)
+    offs = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int64)
+    codes, scales = _encode(w)
+    ref, _ = _oracle(w, codes, scales, offs, idx)
+    for split in (0, 32, 96):
+        got, _ = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, offs, idx, split_rows=split)
+        err = rel_err(got, ref)
+        assert err <= TOL[kvq.KVQ_PREC_MFMA], f"split {split}: {err:.3e}"
+
+
+def test_sparse_equals_dense_on_gathered_copy():
+    _say("sparse attention == dense attention over a gathered copy")
+    w = workloads.SparseDecodeWorkload("sparse-vs-dense", 1005, 4096, [100, 700, 2048], 32)
+    codes, scales = _encode(w)
+    got, glse = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, w.offsets, w.row_index)
+    ix = torch.from_numpy(w.row_index).to(DEV)
+    a, out, lse = _args(w, kvq.KVQ_PREC_MFMA, w.offsets, len(w.row_index), codes[ix].contiguous(),
+                        scales[ix].contiguous(), _t(w.k_rope[w.row_index]))
+    kvq.kvq_decode_attn(a, kvq.alloc_workspace(a))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(out).astype(np.float64), got) and np.array_equal(_np(lse).astype(np.float64), glse)
+
+
+def test_sparse_full_size():
+    _say("sparse attention, the measured workload: T=32768 cache, 16 queries x 2048 rows, 128 heads")
+    w = workloads.dsa_sparse_decode()
+    codes, scales = _encode(w)
+    got, _ = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, w.offsets, w.row_index)
+    ref, _ = _oracle(w, codes, scales, w.offsets, w.row_index)
+    err = rel_err(got, ref)
+    assert err <= TOL[kvq.KVQ_PREC_MFMA], f"max|err|/max|ref| = {err:.3e}"
+
+
+def test_sparse_refusals():
+    _say("sparse attention: argument checks")
+    w = workloads.SparseDecodeWorkload("sparse-refuse", 1005, 256, [8], 16)
+    codes, scales = _encode(w)
+    a, _, _ = _args(w, kvq.KVQ_PREC_MFMA, w.offsets, 8, codes, scales, _t(w.k_rope))
+    ws = kvq.alloc_workspace_sparse(a)
+    with pytest.raises(kvq.KvqError) as e:  # a workspace one byte short
+        kvq.kvq_decode_attn_sparse(a, _t(w.row_index), w.cache_rows, ws[: kvq.kvq_decode_attn_sparse_workspace_bytes(a) - 1])
+    assert e.value.status == kvq.KVQ_ERR_WORKSPACE
+    with pytest.raises(kvq.KvqError) as e:  # an empty cache with a non-empty list
+        kvq.kvq_decode_attn_sparse(a, _t(w.row_index), 0, ws)
+    assert e.value.status == kvq.KVQ_ERR_INVALID_ARG

@@ -238,25 +238,29 @@ __global__ __launch_bounds__(Q4_WAVES * KVQ_WAVE) void k_gather_q4_0(kvq_q4_cach
 #pragma unroll
     for (int g = 0; g < G_SUB; g++) {
         if (cell[g] < 0) continue;
-        const uint8_t* row = stage[g][slot];
-        const int blk = (lane >> 1) * 18;
-        const uint16_t* row16 = reinterpret_cast<const uint16_t*>(row);
-        const float d = f16_to_f32(row16[blk / 2]);
-        const int shift = (lane & 1) ? 4 : 0;  // even lane: low nibbles (elements 0..15), odd: high (16..31)
-        uint32_t out[8];
+        const uint16_t* row16 = reinterpret_cast<const uint16_t*>(stage[g][slot]);
+        uint16_t* dst = (plane ? v_dst : k_dst) + hr[g] * 256;
+        // lane l writes elements 8 l .. 8 l + 7 and 128 + 8 l .. + 7: each of the
+        // two stores covers 256 contiguous bytes of the row across the 16 lanes
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const uint32_t two = row16[blk / 2 + 1 + i];  // qs bytes 2i, 2i+1
-            const int q0 = (int)((two >> shift) & 15u);
-            const int q1 = (int)((two >> (8 + shift)) & 15u);
-            // (q - 8) d is exact in fp32; the hardware conversion rounds it to nearest even
-            const uint32_t h0 = f32_to_f16_rne((float)(q0 - 8) * d);
-            const uint32_t h1 = f32_to_f16_rne((float)(q1 - 8) * d);
-            out[i] = h0 | (h1 << 16);
+        for (int part = 0; part < 2; part++) {
+            const int e0 = 128 * part + 8 * lane;          // first element: block e0 / 32
+            const int blk = (e0 >> 5) * 18, pos = e0 & 31;  // 8 positions of one nibble side
+            const float d = f16_to_f32(row16[blk / 2]);
+            const int shift = pos >= 16 ? 4 : 0;            // elements 16..31 of a block: high nibbles
+            const uint8_t* qs = stage[g][slot] + blk + 2 + (pos & 15);
+            uint32_t out[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int q0 = (int)((qs[2 * i] >> shift) & 15u), q1 = (int)((qs[2 * i + 1] >> shift) & 15u);
+                // (q - 8) d is exact in fp32; the hardware conversion rounds it to nearest even
+                out[i] = f32_to_f16_rne((float)(q0 - 8) * d) | (f32_to_f16_rne((float)(q1 - 8) * d) << 16);
+            }
+            __builtin_nontemporal_store(make_uint4(out[0], out[1], out[2], out[3]).x, reinterpret_cast<uint32_t*>(dst + e0));
+            __builtin_nontemporal_store(make_uint4(out[0], out[1], out[2], out[3]).y, reinterpret_cast<uint32_t*>(dst + e0) + 1);
+            __builtin_nontemporal_store(make_uint4(out[0], out[1], out[2], out[3]).z, reinterpret_cast<uint32_t*>(dst + e0) + 2);
+            __builtin_nontemporal_store(make_uint4(out[0], out[1], out[2], out[3]).w, reinterpret_cast<uint32_t*>(dst + e0) + 3);
         }
-        uint16_t* dst = (plane ? v_dst : k_dst) + hr[g] * 256 + lane * 16;
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
     }
 }
 

@@ -29,6 +29,8 @@ constexpr int ENC_WAVES = 4;  // waves per workgroup
 
 // ---- fp8 -------------------------------------------------------------------
 // One wave per row; ITER chunks of 512 elements (8 per lane).
+typedef float f32x4v __attribute__((ext_vector_type(4)));  // a native vector (non-temporal loads)
+
 template <int ITER>
 __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float* __restrict__ x, int64_t n_rows,
                                                                      int dim, uint8_t* __restrict__ codes,
@@ -37,19 +39,23 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float
     const int64_t row = (int64_t)blockIdx.x * ENC_WAVES + (threadIdx.x >> 6);
     if (row >= n_rows) return;  // whole wave exits together
     const float* xr = x + row * dim;
+    // lane l holds elements 4 l .. 4 l + 3 and 256 + 4 l .. + 3 of each 512-element
+    // span, so every load covers 1 KB of the row contiguously (the steps below are
+    // element-wise; the maximum does not depend on the order)
     float v[ITER][8];
     float amax = 0.0f;
 #pragma unroll
     for (int it = 0; it < ITER; it++) {
-        const int base = it * 512 + lane * 8;
-        if (base < dim) {
-            const float4 a = *reinterpret_cast<const float4*>(xr + base);
-            const float4 b = *reinterpret_cast<const float4*>(xr + base + 4);
-            v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
-            v[it][4] = b.x; v[it][5] = b.y; v[it][6] = b.z; v[it][7] = b.w;
-        } else {
 #pragma unroll
-            for (int j = 0; j < 8; j++) v[it][j] = 0.0f;
+        for (int hf = 0; hf < 2; hf++) {
+            const int base = it * 512 + 256 * hf + lane * 4;  // dim is a multiple of 8: all four or none
+            if (base < dim) {
+                const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(xr + base));
+                v[it][4 * hf + 0] = a[0]; v[it][4 * hf + 1] = a[1]; v[it][4 * hf + 2] = a[2]; v[it][4 * hf + 3] = a[3];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[it][4 * hf + j] = 0.0f;
+            }
         }
 #pragma unroll
         for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(v[it][j]));
@@ -65,22 +71,24 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float
     uint8_t* cr = codes + row * dim;
 #pragma unroll
     for (int it = 0; it < ITER; it++) {
-        const int base = it * 512 + lane * 8;
-        if (base < dim) {
-            float qv[8];
-            if (recip) {
 #pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const float q0 = v[it][j] * r;
-                    qv[j] = __builtin_fmaf(__builtin_fmaf(-q0, s, v[it][j]), r, q0);
+        for (int hf = 0; hf < 2; hf++) {
+            const int base = it * 512 + 256 * hf + lane * 4;
+            if (base < dim) {
+                float qv[4];
+                if (recip) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float q0 = v[it][4 * hf + j] * r;
+                        qv[j] = __builtin_fmaf(__builtin_fmaf(-q0, s, v[it][4 * hf + j]), r, q0);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) qv[j] = (s != 0.0f) ? v[it][4 * hf + j] / s : 0.0f;
                 }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; j++) qv[j] = (s != 0.0f) ? v[it][j] / s : 0.0f;
+                const uint32_t w = e4m3x2_rne(qv[0], qv[1]) | (e4m3x2_rne(qv[2], qv[3]) << 16);
+                __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(cr + base));
             }
-            const uint32_t lo = e4m3x2_rne(qv[0], qv[1]) | (e4m3x2_rne(qv[2], qv[3]) << 16);
-            const uint32_t hi = e4m3x2_rne(qv[4], qv[5]) | (e4m3x2_rne(qv[6], qv[7]) << 16);
-            *reinterpret_cast<uint2*>(cr + base) = make_uint2(lo, hi);
         }
     }
     if (lane == 0) scales[row] = s;

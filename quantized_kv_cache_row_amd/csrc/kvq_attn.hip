@@ -1490,14 +1490,18 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
             break;
         default: {
             const int64_t items = (int64_t)a.n_seqs * a.n_heads;
-            // more split groups per workgroup when there are many splits per sequence
+            // more split groups per workgroup when there are many splits per sequence,
+            // a single one (one thread per float4 column) when there are few
             const bool wide = p.max_chunks >= 16 * (int64_t)a.n_seqs;
+            const bool narrow = p.max_chunks <= 4 * (int64_t)a.n_seqs;
             if (tq4) {
                 if (!f32 && wide) hipLaunchKernelGGL((k_merge<true, true, 1024>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
+                else if (!f32 && narrow) hipLaunchKernelGGL((k_merge<true, true, 128>), dim3((unsigned)items), dim3(128), 0, st, a, p);
                 else if (!f32) hipLaunchKernelGGL((k_merge<true, true, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);
                 else hipLaunchKernelGGL((k_merge<true, false, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);
             } else {
                 if (!f32 && wide) hipLaunchKernelGGL((k_merge<false, true, 512>), dim3((unsigned)(2 * items)), dim3(512), 0, st, a, p);
+                else if (!f32 && narrow) hipLaunchKernelGGL((k_merge<false, true, 64>), dim3((unsigned)(2 * items)), dim3(64), 0, st, a, p);
                 else if (!f32) hipLaunchKernelGGL((k_merge<false, true, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
                 else hipLaunchKernelGGL((k_merge<false, false, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
             }

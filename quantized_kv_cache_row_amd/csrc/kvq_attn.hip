@@ -457,15 +457,12 @@ __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
 //          byte 8 (q % 2) of chunk mb; lane (g, p) receives the 8 codes of
 //          rows 8 g .. 8 g + 7 in column 16 mb + p, converted to fp16 in
 //          registers -- k-slots (g, j) = row 8 g + j, as the probabilities.
-// The rope keys (8 chunks per row) use 9-slot rows: slot 9 sigma(r) + c.
+// The rope keys do not go through LDS: each lane loads its score rows' keys.
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 constexpr int RAW_ROW = DL;                   // bytes per raw fp8 code row
 constexpr int RAW_SLOTS = 33;                 // 16-byte slots per padded tile row
 constexpr int RAW_DMA = 17;                   // DMA instructions per code tile (1056 slots, 64 per instruction)
 constexpr int RAW_TILE = RAW_DMA * 64 * 16;   // 17408 bytes
-constexpr int ROPE_SLOTS = 9;
-constexpr int ROPE_DMA = 5;                   // 288 slots
-constexpr int ROPE_TILE = ROPE_DMA * 64 * 16; // 5120 bytes
 
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -586,7 +583,6 @@ __device__ __forceinline__ bool locate_chunk(const kvq_attn_args& a, const Plan&
 
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
-    __shared__ __align__(16) uint8_t rope_s[MF_WAVES][ROPE_TILE];      // rope keys (bf16)
     __shared__ __align__(16) float rho_s[MF_WAVES][2][64];             // row scales
     __shared__ float ml_s[MF_WAVES][3][MF_HEADS];
     __shared__ int64_t plan_s[3];  // this chunk's first row, end row, sequence (-1: none)
@@ -612,9 +608,9 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // offsets are fixed per lane.  Rows past the wave's end are loaded too (and
     // masked later) while they lie inside the arrays; past the arrays' end a
     // lane loads their last 16 bytes instead.  Instruction k of a tile
-    // (0..22: codes, rope, scales) is issued on its own, so the issue can be
-    // spread over the score steps.
-    uint32_t voff_c[RAW_DMA], voff_r[ROPE_DMA];
+    // (0..17: codes, scales) is issued on its own, so the issue can be spread
+    // over the score steps.  The rope keys go straight to registers (load_rope).
+    uint32_t voff_c[RAW_DMA];
 #pragma unroll
     for (int i = 0; i < RAW_DMA; i++) {
         const int q = 64 * i + lane;
@@ -622,25 +618,14 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         const int r = k < MF_TILE ? tile_sigma_inv(k) : 0;
         voff_c[i] = (uint32_t)(r * RAW_ROW + 16 * (ch < 32 && k < MF_TILE ? ch : 0));
     }
-#pragma unroll
-    for (int i = 0; i < ROPE_DMA; i++) {
-        const int q = 64 * i + lane;
-        const int k = q / ROPE_SLOTS, ch = q % ROPE_SLOTS;
-        const int r = k < MF_TILE ? tile_sigma_inv(k) : 0;
-        voff_r[i] = (uint32_t)(r * DR * 2 + 16 * (ch < 8 && k < MF_TILE ? ch : 0));
-    }
     const uint32_t lds_codes = lds_offset(&raw[wave][0][0]);
-    const uint32_t lds_rope = lds_offset(&rope_s[wave][0]);
     const uint32_t lds_rho = lds_offset(&rho_s[wave][0][0]);
-    constexpr int NDMA = RAW_DMA + ROPE_DMA + 1;
+    constexpr int NDMA = RAW_DMA + 1;
     auto dma_one = [&](int k, int64_t t0, int buf, int lim) __attribute__((always_inline)) {
         // lim: rows of the tile inside the arrays (offsets are clamped to them)
         if (k < RAW_DMA) {
             dma_lds_b128(a.codes + t0 * RAW_ROW, min(voff_c[k], (uint32_t)lim * RAW_ROW - 16u),
                          __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE + 1024u * k));
-        } else if (k < RAW_DMA + ROPE_DMA) {
-            dma_lds_b128(reinterpret_cast<const uint8_t*>(a.k_rope + t0 * DR),
-                         min(voff_r[k - RAW_DMA], (uint32_t)lim * (DR * 2) - 16u), lds_rope + 1024u * (k - RAW_DMA));
         } else {
             const uint32_t voff_s = (uint32_t)((lane & 31) < lim ? (lane & 31) : 0) * 4u;
             dma_lds_b32(a.row_scale + t0, voff_s, __builtin_amdgcn_readfirstlane(lds_rho + 256u * buf));
@@ -650,6 +635,19 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         const int lim = (int)min((int64_t)MF_TILE, a.total_rows - t0);
 #pragma unroll
         for (int k = 0; k < NDMA; k++) dma_one(k, t0, buf, lim);
+    };
+    // The rope keys of a tile, straight into registers one tile ahead: lane (g, n)
+    // takes the score rows 8 (n / 4) + 4 rb + n % 4 (rb = 0, 1), dims 32 k + 8 g
+    // .. + 7 (16-byte aligned), clamped to the arrays; unconditional loads.
+    uint4 krn[2][2];
+    auto load_rope = [&](int64_t t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const int64_t row = min(t0 + 8 * (n >> 2) + 4 * rb + (n & 3), a.total_rows - 1);
+#pragma unroll
+            for (int k = 0; k < 2; k++)
+                krn[rb][k] = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 32 * k + 8 * g);
+        }
     };
 
     // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
@@ -702,11 +700,12 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         }
         if (w0 < w1) {  // wave-uniform
             load_tile(w0, 0);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | 7 | (16 << 10));  // vmcnt(23): the staging DMAs have landed
+            load_rope(w0);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | 6 | (16 << 10));  // vmcnt(22): the staging DMAs have landed
         } else {
             vm_wait_all();
         }
-        static_assert(NDMA == 23, "the wait above counts the first tile's DMA instructions");
+        static_assert(NDMA == 18, "the wait above counts the first tile's 18 DMAs and 4 rope loads");
         wg_barrier_lds();  // every quarter is in LDS (the first tile's DMA stays in flight)
         float rmw = 0.0f;
         if (w0 < w1) {  // wave-uniform
@@ -767,8 +766,6 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // per-lane LDS read offsets (bytes within a tile)
     const uint32_t rd_a = 16u * (RAW_SLOTS * tile_sigma(tile_row(0, n)) + g);   // score, row block 0
     const uint32_t rd_b = 16u * (RAW_SLOTS * tile_sigma(tile_row(1, n)) + g);   // score, row block 1
-    const uint32_t rp_a = 16u * (ROPE_SLOTS * tile_sigma(tile_row(0, n)) + g);  // rope, row block 0
-    const uint32_t rp_b = 16u * (ROPE_SLOTS * tile_sigma(tile_row(1, n)) + g);  // rope, row block 1
     const uint32_t rd_t = 16u * RAW_SLOTS * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
 
     const float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
@@ -790,19 +787,20 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     l_part = 0.0f;
     int buf = 0;
     bool again = false;
-    if (restarted && w0 < w1) load_tile(w0, 0);
+    if (restarted && w0 < w1) {
+        load_tile(w0, 0);
+        load_rope(w0);
+    }
     restarted = true;
     for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
         const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        vm_wait_all();  // this tile's codes, rope keys and scales are in LDS
+        vm_wait_all();  // this tile's codes and scales are in LDS, its rope keys in registers
         const bool more = t0 + MF_TILE < w1;
-        // rope operands and row scales to registers, then the rope buffer is free
         uint4 kr[2][2];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-            for (int k = 0; k < 2; k++)
-                kr[rb][k] = *reinterpret_cast<const uint4*>(&rope_s[wave][(rb ? rp_b : rp_a) + 64 * k]);
+            for (int k = 0; k < 2; k++) kr[rb][k] = krn[rb][k];
         const float4 rho0 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g]);
         const float4 rho1 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g + 4]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): those reads are done before the buffers refill
@@ -811,6 +809,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         const int64_t tn = more ? t0 + MF_TILE : t0;
         // after the last tile the reload only has to be harmless: one row, from the cache
         const int limn = more ? (int)min((int64_t)MF_TILE, a.total_rows - tn) : 1;
+        load_rope(tn);  // the next tile's rope keys (after the last tile: this tile's again)
         const uint8_t* tb = raw[wave][buf];
         // ---- scores: both row blocks together, the reads one k-chunk ahead
         const uint8_t* pa = tb + rd_a;

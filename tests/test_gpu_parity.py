@@ -236,6 +236,20 @@ def test_attn_tiny_and_split_invariance(precision):
         assert rel_err(o, outs[0]) <= 2 * TOL[precision]
 
 
+@pytest.mark.parametrize("n_heads", [5, 20])
+@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
+def test_attn_head_counts(n_heads, qmode, precision):
+    """Head counts that leave part of a head group empty: 5 heads (one partial
+    group) and 20 (a full group of 16 and a partial one; one partial 64-head
+    group for TQ4).  Two sequences of 700 and 333 rows."""
+    _say(f"attn head count {n_heads} qmode={qmode} precision={precision}")
+    w = workloads.DecodeWorkload(f"heads{n_heads}", 1006, [700, 333], n_heads, qmode=qmode,
+                                 sign_seed=1002 if qmode == 2 else None)
+    c, s = _encode_cache(w)
+    _check_attn(w, c, s, precision, label=f"heads{n_heads}")
+
+
 @pytest.mark.parametrize("qmode", [1, 2])
 @pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_attn_full_T32768(qmode, precision):

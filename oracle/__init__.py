@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY.  This package may be imported by ``tests/``, by
 ``__graft_entry__.smoke()`` and by the CPU-baseline leg of ``bench.py`` -- by
 nothing else.  It never imports the HIP library's package, and the HIP
 library never imports it.  The arithmetic lives in ``kvq_oracle.c``; this file
-only marshals numpy arrays.
+only marshals numpy arrays, except for two compositions written in numpy
+(fp64): the sparse decode (a row selection in front of ``decode_attn``) and
+the fused decode attention over the q4_0 pools (``decode_attn_q4_0``).
 
 Functions mirror the C entry points (see the comments there for the
 definitions and the pages each follows).
@@ -354,3 +356,73 @@ def gather_q4_0(k_pool, v_pool, table, page_size, dst_off, head_dim=256, k_dst=N
                                   _p(v_dst, _c_u16p))
     _check(rc, "gather_q4_0")
     return k_dst, v_dst
+
+
+def q4_0_rows_f64(rows):
+    """Dequantize q4_0 head-rows u8 [..., 144] to fp64 [..., 256] in the rotated
+    domain, exactly as the fused decode reads them ([Q4], QSA_KV_Q4 commit:
+    every block is (nibble - 8) * f32(d), no rounding to binary16): block b is
+    bytes 18b .. 18b+17, a little-endian binary16 scale d then 16 bytes whose
+    low nibbles are elements 0..15 and high nibbles elements 16..31."""
+    r = np.ascontiguousarray(rows, np.uint8)
+    lead = r.shape[:-1]
+    blk = r.reshape(-1, 8, 18)
+    d = blk[:, :, 0:2].copy().view("<f2")[:, :, 0].astype(np.float64)
+    nib = blk[:, :, 2:18]
+    codes = np.concatenate([nib & 15, nib >> 4], axis=2).astype(np.float64)
+    return ((codes - 8.0) * d[:, :, None]).reshape(lead + (256,))
+
+
+def decode_attn_q4_0(k_pool, v_pool, table, page_size, len_off, q, sm_scale):
+    """Fused decode attention over the q4_0 pools, fp64 ([Q4], QSA_KV_Q4 commit:
+    the query rows pass through the orthonormal 256-point FWHT, the pools are
+    dequantized per block, softmax and the weighted sum of V rows run in the
+    rotated domain, and the merged row o / L is rotated back with the same
+    self-inverse transform; the sigmoid gate that follows in the pages' model is
+    not part of it).
+
+    k_pool, v_pool: u8 [n_cells][n_kv][144]; table: int32 [n_seqs][max_pages];
+    len_off: int64 [n_seqs + 1], sequence s attends positions
+    0 .. len_off[s+1] - len_off[s] - 1; q: fp32 [n_seqs][n_q][256], n_q a
+    multiple of n_kv, query head h reading kv head h // (n_q / n_kv).
+    Positions whose cell does not exist (page column past the table, negative
+    entry, cell past the pool) take no part.  Returns (out [n_seqs][n_q][256],
+    lse [n_seqs][n_q]) in fp64; a sequence with no positions gives 0 and -inf.
+    The FWHT is the Sylvester-ordered Hadamard matrix over 16 (scipy's
+    ``hadamard``, a library primitive), the same order as the append's."""
+    from scipy.linalg import hadamard
+    kp = np.asarray(k_pool, np.uint8)
+    vp = np.asarray(v_pool, np.uint8)
+    tab = np.asarray(table, np.int32)
+    offs = np.asarray(len_off, np.int64)
+    qq = np.asarray(q, np.float32).astype(np.float64)
+    n_cells, n_kv, _ = kp.shape
+    n_seqs, n_q, dim = qq.shape
+    assert dim == 256 and n_q % n_kv == 0
+    group = n_q // n_kv
+    hm = hadamard(256).astype(np.float64) / 16.0
+    q_rot = qq @ hm
+    out = np.zeros((n_seqs, n_q, 256), np.float64)
+    lse = np.full((n_seqs, n_q), -np.inf, np.float64)
+    for s in range(n_seqs):
+        n = int(offs[s + 1] - offs[s])
+        pos = np.arange(max(n, 0), dtype=np.int64)
+        col = pos // page_size
+        ok = col < tab.shape[1]
+        page = np.where(ok, tab[s, np.minimum(col, tab.shape[1] - 1)], -1).astype(np.int64)
+        cell = page * page_size + pos % page_size
+        ok &= (page >= 0) & (cell < n_cells)
+        cell = cell[ok]
+        if cell.size == 0:
+            continue
+        for g in range(n_kv):
+            kd = q4_0_rows_f64(kp[cell, g])
+            vd = q4_0_rows_f64(vp[cell, g])
+            for h in range(g * group, (g + 1) * group):
+                sc = float(sm_scale) * (kd @ q_rot[s, h])
+                m = sc.max()
+                w = np.exp(sc - m)
+                den = w.sum()
+                out[s, h] = hm @ ((w @ vd) / den)
+                lse[s, h] = m + np.log(den)
+    return out, lse

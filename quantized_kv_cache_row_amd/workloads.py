@@ -21,6 +21,8 @@ Workload recipe (the decode workloads of the MLA pages: 512-dim latent plus a
   [512, 8192] snapped down to 56 mod 64, a random permutation of all physical
   pages, amplitude classes 1e-3 / 1 / 40 cycled by (token + head) mod 3, every
   token index divisible by 97 all zero.
+* fused q4_0 decode: 4 query heads per KV head (32 query heads), queries
+  ~ N(0, 1) / 16 (unrotated), softmax scale 1 / 16, over the prefill pools.
 """
 import math
 
@@ -180,6 +182,8 @@ Q4_HEAD_DIM = 256
 Q4_KV_HEADS = 8
 Q4_PAGE = 64
 Q4_ROW_BYTES = 144
+Q4_GROUP = 4                 # query heads per KV head in the fused q4_0 decode
+Q4_SM_SCALE = 1.0 / 16.0     # 1 / sqrt(head_dim)
 
 
 class Q4Workload:
@@ -254,3 +258,9 @@ def q4_tie_fixtures():
     for a in (1e-3, 1.0, 40.0):
         blocks.append((rng.standard_normal(32) * a).astype(np.float32))
     return np.stack(blocks)
+
+
+def q4_queries(seed, n_seqs, n_q_heads=Q4_KV_HEADS * Q4_GROUP, dim=Q4_HEAD_DIM):
+    """Unrotated decode queries for the fused q4_0 attention, ~ N(0, 1) / 16."""
+    rng = streams(seed)[S_QLAT]
+    return (rng.standard_normal((n_seqs, n_q_heads, dim), dtype=np.float32) / np.float32(16.0)).astype(np.float32)

@@ -242,6 +242,54 @@ int64_t kvq_decode_attn_sparse_workspace_bytes(const kvq_attn_args* a);
 int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int64_t cache_rows, void* workspace,
                            int64_t ws_bytes, void* stream);
 
+/* ---- fused decode attention over the q4_0 pools ([Q4], QSA_KV_Q4 commit) ---
+ * The decode attention of the paged q4_0 tier, read straight from the pools:
+ * for sequence s and query head h (KV head g = h / G, G = n_q_heads /
+ * n_kv_heads, so query heads g*G .. g*G+G-1 share KV head g):
+ *   q~      = FWHT256(q[s,h]) / 16 (the append's rotation; orthonormal);
+ *   x_t     = (nibble - 8) * f32(d) for every block of the K and V head-rows
+ *             of position t (fp32, exact: no rounding to binary16);
+ *   s_t     = sm_scale * (q~ . k_t);  p = softmax(s) over the positions;
+ *   out     = FWHT256(sum_t p_t v_t) / 16 (rotated back), lse = log sum exp s_t.
+ * Sequence s attends positions 0 .. len_off[s+1] - len_off[s] - 1 through
+ * cache.block_table (cell = table[s][pos / page_size] * page_size + pos %
+ * page_size); positions whose page column is past max_pages, whose table entry
+ * is negative or whose cell is past n_cells take no part.  A sequence with no
+ * position gets out = 0 and lse = -Inf.  The sigmoid gate that follows in the
+ * pages' model is the caller's.
+ * Arithmetic: fp32 throughout (scores as d * (sum nibble * q~ - 8 * sum q~)
+ * per block, sm_scale * log2(e) folded into q~, exp2); tolerance against an
+ * fp64 evaluation on the same pool bytes: max|err| / max|ref| <= 1e-4. */
+typedef struct kvq_q4_attn_args {
+    int32_t n_seqs;             /* >= 1                                              */
+    int32_t n_q_heads;          /* n_kv_heads * G with G in {1, 2, 4, 8, 16}          */
+    int32_t split_rows;         /* positions per work item: 0 = automatic, else a
+                                   multiple of 256 up to 2^24                         */
+    int32_t reserved0;          /* must be 0                                         */
+    int64_t total_rows;         /* host copy of len_off[n_seqs]                      */
+    const int64_t* len_off;     /* device int64 [n_seqs+1], non-decreasing, [0] = 0  */
+    const float* q;             /* device fp32 [n_seqs][n_q_heads][256], unrotated   */
+    float* out;                 /* device fp32 [n_seqs][n_q_heads][256]              */
+    float* lse;                 /* device fp32 [n_seqs][n_q_heads], or NULL          */
+    float sm_scale;             /* softmax scale, finite                             */
+    int32_t reserved1;          /* must be 0                                         */
+} kvq_q4_attn_args;
+
+/* Device workspace bytes for kvq_decode_attn_q4_0 (rotated queries, the T-split
+ * prefix and the partial softmax states); depends on n_kv_heads, n_seqs,
+ * n_q_heads, total_rows and split_rows only.  Host only; -1 for arguments the
+ * call would refuse. */
+int64_t kvq_decode_attn_q4_0_workspace_bytes(const kvq_q4_cache* cache, const kvq_q4_attn_args* a);
+
+/* Runs the fused decode attention on `stream` (three launches: query rotation
+ * and split plan, split kernel, merge and rotation back).  workspace: device,
+ * 256-byte aligned, >= the queried size (KVQ_ERR_WORKSPACE otherwise); two
+ * calls sharing it must be ordered.  q and out 16-byte aligned, len_off 8-byte
+ * aligned; pools as for kvq_append_q4_0.  KVQ_ERR_UNSUPPORTED for a head ratio
+ * other than 1, 2, 4, 8 or 16 or head_dim != 256. */
+int kvq_decode_attn_q4_0(const kvq_q4_cache* cache, const kvq_q4_attn_args* a, void* workspace,
+                         int64_t ws_bytes, void* stream);
+
 /* ---- conformance probe -------------------------------------------------------
  * Element-wise conversions exactly as the kernels perform them, so a caller
  * can check them against the format definitions (for instance over every
@@ -270,7 +318,8 @@ int kvq_convert(int kind, const void* in, int64_t n, void* out, void* stream);
 
 /* ---- binding support ------------------------------------------------------
  * Layout of the argument structs, so a foreign-language binding can check its
- * mirror: which = 0 -> kvq_attn_args, 1 -> kvq_q4_cache; out[0] = sizeof, then
+ * mirror: which = 0 -> kvq_attn_args, 1 -> kvq_q4_cache, 2 -> kvq_q4_attn_args;
+ * out[0] = sizeof, then
  * the offsetof of every field in declaration order.  Returns the number of
  * values written (at most n), or -1 for an unknown struct.  Host only. */
 int kvq_struct_layout(int which, int64_t* out, int n);

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["kvq_abi.hip", "kvq_encode.hip", "kvq_q4.hip", "kvq_attn.hip", "kvq_sparse.hip"]
+SOURCES = ["kvq_abi.hip", "kvq_encode.hip", "kvq_q4.hip", "kvq_attn.hip", "kvq_sparse.hip", "kvq_q4attn.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-ffp-contract=off",

@@ -73,6 +73,23 @@ int check_q4(const kvq_q4_cache* c) {
     return KVQ_OK;
 }
 
+int check_q4_attn(const kvq_q4_cache* c, const kvq_q4_attn_args* a) {
+    int rc = check_q4(c);
+    if (rc != KVQ_OK) return rc;
+    if (!a) return KVQ_ERR_INVALID_ARG;
+    if (a->n_seqs < 1 || a->n_q_heads < 1 || a->total_rows < 0 || a->split_rows < 0) return KVQ_ERR_INVALID_ARG;
+    if (a->n_q_heads % c->n_kv_heads != 0) return KVQ_ERR_UNSUPPORTED;
+    const int g = a->n_q_heads / c->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return KVQ_ERR_UNSUPPORTED;
+    if (a->reserved0 != 0 || a->reserved1 != 0) return KVQ_ERR_INVALID_ARG;
+    if (a->split_rows > 0 && (a->split_rows % 256 != 0 || a->split_rows > (1 << 24))) return KVQ_ERR_INVALID_ARG;
+    if (!a->len_off || !a->q || !a->out) return KVQ_ERR_INVALID_ARG;
+    if (!aligned(a->len_off, 8) || !aligned16(a->q) || !aligned16(a->out) || !aligned(a->lse, 4))
+        return KVQ_ERR_INVALID_ARG;
+    if (!(a->sm_scale == a->sm_scale) || a->sm_scale > 3.0e38f || a->sm_scale < -3.0e38f) return KVQ_ERR_INVALID_ARG;
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,6 +163,21 @@ int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_of
         return KVQ_ERR_INVALID_ARG;
     return launch_status(
         kvq::launch_gather_q4_0(*cache, n_seqs, dst_off, total_rows, k_dst, v_dst, as_stream(stream)));
+}
+
+int64_t kvq_decode_attn_q4_0_workspace_bytes(const kvq_q4_cache* cache, const kvq_q4_attn_args* a) {
+    if (check_q4_attn(cache, a) != KVQ_OK) return -1;
+    return kvq::q4_attn_workspace_bytes(*cache, *a);
+}
+
+int kvq_decode_attn_q4_0(const kvq_q4_cache* cache, const kvq_q4_attn_args* a, void* workspace, int64_t ws_bytes,
+                         void* stream) {
+    int rc = check_q4_attn(cache, a);
+    if (rc != KVQ_OK) return rc;
+    const int64_t need = kvq::q4_attn_workspace_bytes(*cache, *a);
+    if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
+    return launch_status(kvq::launch_decode_attn_q4_0(*cache, *a, workspace, as_stream(stream)));
 }
 
 int64_t kvq_decode_attn_workspace_bytes(const kvq_attn_args* a) {
@@ -252,6 +284,19 @@ int kvq_struct_layout(int which, int64_t* out, int n) {
         v[k++] = offsetof(kvq_q4_cache, page_size);
         v[k++] = offsetof(kvq_q4_cache, n_kv_heads);
         v[k++] = offsetof(kvq_q4_cache, head_dim);
+    } else if (which == 2) {
+        v[k++] = sizeof(kvq_q4_attn_args);
+        v[k++] = offsetof(kvq_q4_attn_args, n_seqs);
+        v[k++] = offsetof(kvq_q4_attn_args, n_q_heads);
+        v[k++] = offsetof(kvq_q4_attn_args, split_rows);
+        v[k++] = offsetof(kvq_q4_attn_args, reserved0);
+        v[k++] = offsetof(kvq_q4_attn_args, total_rows);
+        v[k++] = offsetof(kvq_q4_attn_args, len_off);
+        v[k++] = offsetof(kvq_q4_attn_args, q);
+        v[k++] = offsetof(kvq_q4_attn_args, out);
+        v[k++] = offsetof(kvq_q4_attn_args, lse);
+        v[k++] = offsetof(kvq_q4_attn_args, sm_scale);
+        v[k++] = offsetof(kvq_q4_attn_args, reserved1);
     } else {
         return -1;
     }

@@ -47,6 +47,15 @@ class KvqQ4Cache(ctypes.Structure):
     ]
 
 
+class KvqQ4AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("n_seqs", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("split_rows", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("total_rows", ctypes.c_int64), ("len_off", ctypes.c_void_p),
+        ("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("sm_scale", ctypes.c_float), ("reserved1", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -75,6 +84,9 @@ def lib():
             "kvq_decode_attn_sparse_workspace_bytes": ([ctypes.POINTER(KvqAttnArgs)], i64),
             "kvq_decode_attn_sparse": ([ctypes.POINTER(KvqAttnArgs), vp, i64, vp, i64, vp], i32),
             "kvq_struct_layout": ([i32, ctypes.POINTER(ctypes.c_int64), i32], i32),
+            "kvq_decode_attn_q4_0_workspace_bytes": ([ctypes.POINTER(KvqQ4Cache), ctypes.POINTER(KvqQ4AttnArgs)],
+                                                     i64),
+            "kvq_decode_attn_q4_0": ([ctypes.POINTER(KvqQ4Cache), ctypes.POINTER(KvqQ4AttnArgs), vp, i64, vp], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -88,7 +100,8 @@ def exported_symbols():
     return ["kvq_abi_version", "kvq_status_string", "kvq_row_bytes", "kvq_tq4_codebook", "kvq_encode_fp8",
             "kvq_encode_tq4", "kvq_append_q4_0", "kvq_gather_q4_0", "kvq_decode_attn_workspace_bytes",
             "kvq_decode_attn", "kvq_decode_attn_stage", "kvq_gather_rows", "kvq_decode_attn_sparse_workspace_bytes",
-            "kvq_decode_attn_sparse", "kvq_convert", "kvq_struct_layout"]
+            "kvq_decode_attn_sparse", "kvq_convert", "kvq_struct_layout", "kvq_decode_attn_q4_0_workspace_bytes",
+            "kvq_decode_attn_q4_0"]
 
 
 # ---- host-only entry points -----------------------------------------------------
@@ -122,7 +135,7 @@ def kvq_struct_layout(which):
 
 
 def binding_layout(which):
-    S = KvqAttnArgs if which == 0 else KvqQ4Cache
+    S = (KvqAttnArgs, KvqQ4Cache, KvqQ4AttnArgs)[which]
     return [ctypes.sizeof(S)] + [getattr(S, f).offset for f, _ in S._fields_]
 
 
@@ -278,3 +291,33 @@ def kvq_convert(kind, src, dst, stream=None):
 def alloc_workspace(args, device="cuda"):
     n = kvq_decode_attn_workspace_bytes(args)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+# ---- fused decode attention over the q4_0 pools -------------------------------------
+
+def q4_attn_args(len_off, total_rows, q, out, lse=None, sm_scale=1.0 / 16.0, split_rows=0):
+    """Arguments of kvq_decode_attn_q4_0; q / out fp32 [n_seqs][n_q_heads][256]."""
+    n_seqs, n_q, _ = q.shape
+    a = KvqQ4AttnArgs(n_seqs, n_q, int(split_rows), 0, int(total_rows), _ptr(len_off, torch.int64, "len_off"),
+                      _ptr(q, torch.float32, "q"), _ptr(out, torch.float32, "out"),
+                      _ptr(lse, torch.float32, "lse") if lse is not None else None, float(sm_scale), 0)
+    a._keep = (len_off, q, out, lse)
+    return a
+
+
+def kvq_decode_attn_q4_0_workspace_bytes(cache, args):
+    n = lib().kvq_decode_attn_q4_0_workspace_bytes(ctypes.byref(cache), ctypes.byref(args))
+    if n < 0:
+        raise KvqError("kvq_decode_attn_q4_0_workspace_bytes", KVQ_ERR_INVALID_ARG)
+    return n
+
+
+def alloc_workspace_q4(cache, args, device="cuda"):
+    n = kvq_decode_attn_q4_0_workspace_bytes(cache, args)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def kvq_decode_attn_q4_0(cache, args, workspace, stream=None):
+    _check("kvq_decode_attn_q4_0", lib().kvq_decode_attn_q4_0(
+        ctypes.byref(cache), ctypes.byref(args), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))

@@ -40,7 +40,7 @@ def test_host_calls():
 
 
 def test_struct_layouts_match_binding():
-    for which in (0, 1):
+    for which in (0, 1, 2):
         assert kvq.kvq_struct_layout(which) == kvq.binding_layout(which)
 
 

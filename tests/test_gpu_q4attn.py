@@ -1,0 +1,153 @@
+"""GPU parity of the fused decode attention over the q4_0 pools, through the C ABI.
+
+Pools are written by the oracle's append on the CPU and the same bytes are
+uploaded, so both sides read identical blocks.  The HIP result must match the
+oracle's fp64 evaluation within max|err| / max|ref| <= 1e-4 per query head
+row set (fp32 arithmetic over 256-term dots, two 256-point rotations and a
+softmax: a few 1e-6 relative in practice), and lse within 1e-4 * max(1, |lse|).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_kv_cache_row_amd import kvq, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+DEV = "cuda"
+SM = workloads.Q4_SM_SCALE
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def _pools(n_seqs, lmin, lmax, seed=1004):
+    w = workloads.Q4Workload(seed=seed, n_seqs=n_seqs, lmin=lmin, lmax=lmax)
+    kp, vp = w.empty_pools()
+    oracle.append_q4_0(kp, vp, w.table, 64, w.pos0_prefill, w.prefill_off, w.k_prefill, w.v_prefill)
+    return w, kp, vp
+
+
+def _run(kp, vp, table, len_off, q, split_rows=0, with_lse=True):
+    kpd = torch.from_numpy(kp).to(DEV)
+    vpd = torch.from_numpy(vp).to(DEV)
+    tab = torch.from_numpy(np.ascontiguousarray(table, np.int32)).to(DEV)
+    cache = kvq.q4_cache(kpd, vpd, tab, 64)
+    off = torch.from_numpy(np.ascontiguousarray(len_off, np.int64)).to(DEV)
+    qd = torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(DEV)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV) if with_lse else None
+    a = kvq.q4_attn_args(off, int(len_off[-1]), qd, out, lse, SM, split_rows)
+    ws = kvq.alloc_workspace_q4(cache, a)
+    kvq.kvq_decode_attn_q4_0(cache, a, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse.cpu().numpy() if with_lse else None)
+
+
+def _check(out, lse, ref_o, ref_l, label):
+    assert np.all(np.isfinite(out)), label
+    for s in range(ref_o.shape[0]):
+        if np.all(np.isneginf(ref_l[s])):
+            assert np.all(out[s] == 0), label
+            if lse is not None:
+                assert np.all(np.isneginf(lse[s])), label
+            continue
+        e = np.max(np.abs(out[s] - ref_o[s])) / max(np.max(np.abs(ref_o[s])), 1e-30)
+        assert e <= TOL, f"{label} seq {s}: rel err {e:.3e}"
+        if lse is not None:
+            d = np.max(np.abs(lse[s] - ref_l[s]) / np.maximum(1.0, np.abs(ref_l[s])))
+            assert d <= TOL, f"{label} seq {s}: lse err {d:.3e}"
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+def test_q4_attn_head_groups(group):
+    _say(f"q4 attn group {group}")
+    w, kp, vp = _pools(4, 100, 700)
+    q = workloads.q4_queries(1007, w.n_seqs, n_q_heads=8 * group)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, w.table, 64, w.prefill_off, q, SM)
+    out, lse = _run(kp, vp, w.table, w.prefill_off, q)
+    _check(out, lse, ref_o, ref_l, f"group {group}")
+
+
+@pytest.mark.parametrize("split_rows", [256, 512, 1024])
+def test_q4_attn_split_sweep(split_rows):
+    _say(f"q4 attn split {split_rows}")
+    w, kp, vp = _pools(5, 60, 1500, seed=1010)
+    q = workloads.q4_queries(1008, w.n_seqs)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, w.table, 64, w.prefill_off, q, SM)
+    out, lse = _run(kp, vp, w.table, w.prefill_off, q, split_rows=split_rows)
+    _check(out, lse, ref_o, ref_l, f"split {split_rows}")
+    out2, none = _run(kp, vp, w.table, w.prefill_off, q, split_rows=split_rows, with_lse=False)
+    np.testing.assert_array_equal(out2, out)
+
+
+def test_q4_attn_missing_cells_empty_and_overlong_sequences():
+    _say("q4 attn missing cells / empty / overlong")
+    w, kp, vp = _pools(4, 300, 900, seed=1011)
+    q = workloads.q4_queries(1009, w.n_seqs)
+    table = w.table.copy()
+    table[0, 2] = -1                       # one missing page inside sequence 0
+    table[1, 1:] = -1                      # sequence 1 keeps its first page only
+    lens = np.diff(w.prefill_off).copy()
+    lens[2] = 0                            # an empty sequence
+    lens[3] = table.shape[1] * 64 + 300    # longer than the table holds
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, table, 64, off, q, SM)
+    for split in (0, 256):
+        out, lse = _run(kp, vp, table, off, q, split_rows=split)
+        _check(out, lse, ref_o, ref_l, f"edge split {split}")
+
+
+def test_q4_attn_single_position_and_all_missing():
+    _say("q4 attn one position / all missing")
+    w, kp, vp = _pools(3, 100, 200, seed=1012)
+    q = workloads.q4_queries(1010, w.n_seqs)
+    table = w.table.copy()
+    table[2, :] = -1
+    off = np.array([0, 1, 1 + 65, 1 + 65 + 100], np.int64)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, table, 64, off, q, SM)
+    out, lse = _run(kp, vp, table, off, q)
+    _check(out, lse, ref_o, ref_l, "one position")
+
+
+def test_q4_attn_full_size():
+    """The paged-pool workload: 16 sequences of 504 .. 8184 positions (56 mod
+    64), 8 KV heads x 256, page 64, permuted pages, 32 query heads."""
+    _say("q4 attn full size")
+    w, kp, vp = _pools(16, 512, 8192)
+    q = workloads.q4_queries(1007, w.n_seqs)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, w.table, 64, w.prefill_off, q, SM)
+    out, lse = _run(kp, vp, w.table, w.prefill_off, q)
+    _check(out, lse, ref_o, ref_l, "full size")
+
+
+def test_q4_attn_refusals():
+    _say("q4 attn refusals")
+    w, kp, vp = _pools(2, 100, 200, seed=1013)
+    kpd = torch.from_numpy(kp).to(DEV)
+    vpd = torch.from_numpy(vp).to(DEV)
+    tab = torch.from_numpy(w.table).to(DEV)
+    cache = kvq.q4_cache(kpd, vpd, tab, 64)
+    off = torch.from_numpy(w.prefill_off).to(DEV)
+    n = int(w.prefill_off[-1])
+    q3 = torch.zeros((2, 24, 256), dtype=torch.float32, device=DEV)
+    o3 = torch.zeros_like(q3)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn_q4_0_workspace_bytes(cache, kvq.q4_attn_args(off, n, q3, o3))
+    q = torch.zeros((2, 32, 256), dtype=torch.float32, device=DEV)
+    o = torch.zeros_like(q)
+    a = kvq.q4_attn_args(off, n, q, o)
+    need = kvq.kvq_decode_attn_q4_0_workspace_bytes(cache, a)
+    short = torch.empty(need - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn_q4_0(cache, a, short)
+    assert e.value.status == kvq.KVQ_ERR_WORKSPACE
+    bad = kvq.q4_attn_args(off, n, q, o, split_rows=100)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_decode_attn_q4_0(cache, bad, torch.empty(need, dtype=torch.uint8, device=DEV))
+    assert e.value.status == kvq.KVQ_ERR_INVALID_ARG

@@ -262,6 +262,26 @@ def measure_other_rows(torch, kvq, workloads, x_kv8):
     vd = torch.empty_like(kd)
     ms = time_graph(torch, lambda: kvq.kvq_gather_q4_0(cache, off, tok, kd, vd), 5)
     hbm("q4_0_gather", tok * 8 * 2 * (144 + 512), ms, {"tokens": tok})
+    del kd, vd
+    # fused decode attention over the same pools: 32 query heads over the 8 KV heads, one
+    # query per sequence; three copies of the pools (3 x 131 MB) rotate past the 256 MB MALL
+    qq = torch.from_numpy(workloads.q4_queries(1007, q.n_seqs)).to(dev)
+    oq = torch.empty_like(qq)
+    lq = torch.empty(qq.shape[:2], dtype=torch.float32, device=dev)
+    tab = torch.from_numpy(q.table).to(dev)
+    caches = [cache] + [kvq.q4_cache(kp.clone(), vp.clone(), tab, 64) for _ in range(2)]
+    qa = kvq.q4_attn_args(off, tok, qq, oq, lq, workloads.Q4_SM_SCALE)
+    qws = kvq.alloc_workspace_q4(cache, qa)
+    it = [0]
+
+    def q4_call():
+        kvq.kvq_decode_attn_q4_0(caches[it[0] % 3], qa, qws)
+        it[0] += 1
+
+    ms = time_graph(torch, q4_call, 6)
+    kv_bytes = tok * 8 * 2 * 144
+    hbm("q4_0_decode_attn_g4", kv_bytes, ms, {"tokens": tok, "q_heads": 32, "kv_heads": 8,
+                                               "tokens/s": tok / (ms / 1000.0)})
     return res
 
 

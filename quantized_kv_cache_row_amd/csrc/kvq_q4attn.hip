@@ -24,10 +24,12 @@
 //     elements with q~ broadcast from LDS, then d * (sum - 8 * sum_j q~_j), so
 //     each element costs one byte-to-float conversion and G fmas;
 //   * online softmax in the log2 domain per query head;
-//   * values, lane = 4 output elements (the two bytes of one block that hold
-//     elements 2k, 2k+1, 2k+16, 2k+17): the tile's V head-rows sit in the
-//     wave's LDS slice, p from LDS; O += (p d) * nibble and a per-block
-//     correction sum of p d (the -8 term) applied once at the end.
+//   * values: the tile's V head-rows go to the wave's LDS slice regrouped so
+//     that every read is aligned (nibble bytes of block b at 16b, scales at
+//     128); a lane owns 8 output elements (4 nibble bytes of one block) over
+//     the positions of one parity, O += (p d) * nibble with p from LDS, plus a
+//     per-head correction sum of p d (the -8 term) applied once at the end;
+//     the two parities are added across the wave halves.
 // Nothing here is a dense contraction big enough for the matrix cores at
 // G <= 16 query heads per KV head without a transposed V operand; the kernel
 // is bound by VALU issue (about 5 * G + 8 instructions per element and
@@ -61,8 +63,8 @@ struct Q4Plan {
 };
 
 int q4_auto_split(const kvq_q4_attn_args& a, int n_kv) {
-    // about three workgroups per compute unit over all splits and KV heads
-    int64_t split = (a.total_rows * n_kv + 767) / 768;
+    // about four workgroups per compute unit over all splits and KV heads
+    int64_t split = (a.total_rows * n_kv + 1023) / 1024;
     if (split < 256) split = 256;
     split = (split + QA_TILE * QA_WAVES - 1) / (QA_TILE * QA_WAVES) * (QA_TILE * QA_WAVES);
     if (split > (1 << 24)) split = 1 << 24;
@@ -242,6 +244,29 @@ __device__ __forceinline__ void qk_block(const uint32_t (&k)[36], const Q4AttnSh
     for (int h = 0; h < G; h++) sc[h] = __builtin_fmaf(d, __builtin_fmaf(-8.0f, sh.qb[h][B], acc[h]), sc[h]);
 }
 
+// A V head-row into the wave's LDS slice, blocks regrouped so that every read
+// is aligned: bytes 16b .. 16b+15 = the nibble bytes of block b, bytes 128 +
+// 2b = its binary16 scale.
+template <int B>
+__device__ __forceinline__ void stage_v_block(const uint32_t (&r)[36], uint8_t* dst) {
+    *reinterpret_cast<uint4*>(dst + 16 * B) = make_uint4(row_dw<18 * B + 2>(r), row_dw<18 * B + 6>(r),
+                                                          row_dw<18 * B + 10>(r), row_dw<18 * B + 14>(r));
+}
+__device__ __forceinline__ void stage_v_row(const uint32_t (&r)[36], uint8_t* dst) {
+    stage_v_block<0>(r, dst);
+    stage_v_block<1>(r, dst);
+    stage_v_block<2>(r, dst);
+    stage_v_block<3>(r, dst);
+    stage_v_block<4>(r, dst);
+    stage_v_block<5>(r, dst);
+    stage_v_block<6>(r, dst);
+    stage_v_block<7>(r, dst);
+    auto sc2 = [&](uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); };
+    *reinterpret_cast<uint4*>(dst + 128) =
+        make_uint4(sc2(row_dw<0>(r), row_dw<18>(r)), sc2(row_dw<36>(r), row_dw<54>(r)),
+                   sc2(row_dw<72>(r), row_dw<90>(r)), sc2(row_dw<108>(r), row_dw<126>(r)));
+}
+
 template <int G>
 __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q4_attn_args a, Q4Plan p) {
     __shared__ __align__(16) Q4AttnShared<G> sh;
@@ -306,14 +331,14 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
         return ok;
     };
 
-    float m[G], lp[G], o[G][4], cs[G];
+    float m[G], lp[G], o[G][8], cs[G];
 #pragma unroll
     for (int h = 0; h < G; h++) {
         m[h] = -INFINITY;
         lp[h] = 0.0f;
         cs[h] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[h][e] = 0.0f;
+        for (int e = 0; e < 8; e++) o[h][e] = 0.0f;
     }
     const bool any_cells = c.n_cells > 0;
     uint4 kn[9], vn[9];
@@ -321,18 +346,23 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
     for (int i = 0; i < 9; i++) kn[i] = vn[i] = make_uint4(0, 0, 0, 0);  // no cells: every row reads as zeros
     bool okn = false;
     if (w0 < w1 && any_cells) okn = load_rows(w0, kn, vn);
-    const int vb = lane >> 3, vk2 = (lane & 7) * 2;  // value lane: block, first byte
+    // value lane: positions of parity vh, block vb, nibble bytes 4 vk .. 4 vk + 3
+    const int vh = lane >> 5, vb = (lane & 31) >> 2, vk = lane & 3;
     for (int64_t t0 = w0; t0 < w1; t0 += QA_TILE) {
         const int nt = (int)min((int64_t)QA_TILE, w1 - t0);
-        uint32_t k[36];
+        uint32_t k[36], vw[36];
 #pragma unroll
         for (int i = 0; i < 9; i++) {
             k[4 * i] = kn[i].x;
             k[4 * i + 1] = kn[i].y;
             k[4 * i + 2] = kn[i].z;
             k[4 * i + 3] = kn[i].w;
-            reinterpret_cast<uint4*>(&sh.v[wave][lane][0])[i] = vn[i];
+            vw[4 * i] = vn[i].x;
+            vw[4 * i + 1] = vn[i].y;
+            vw[4 * i + 2] = vn[i].z;
+            vw[4 * i + 3] = vn[i].w;
         }
+        stage_v_row(vw, &sh.v[wave][lane][0]);
         const bool ok = okn;
         if (t0 + QA_TILE < w1 && any_cells) okn = load_rows(t0 + QA_TILE, kn, vn);
 
@@ -370,27 +400,40 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
             lp[h] = __builtin_fmaf(lp[h], alpha, pv);
             cs[h] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 4; e++) o[h][e] *= alpha;
+            for (int e = 0; e < 8; e++) o[h][e] *= alpha;
             sh.pr[wave][lane][h] = pv;
         }
 
-        // values, lane = elements 32 vb + vk2 + {0, 1, 16, 17}
-        for (int t = 0; t < nt; t++) {
+        // values: lane = elements 32 vb + 4 vk + {0..3} and 32 vb + 16 + 4 vk + {0..3} over the
+        // positions of parity vh (rows past nt are zero with p = 0, so the pair loop may read one)
+#pragma unroll 4
+        for (int tt = 0; tt < nt; tt += 2) {
+            const int t = tt + vh;
             const uint8_t* vrow = &sh.v[wave][t][0];
-            const uint32_t nb = *reinterpret_cast<const uint16_t*>(vrow + 18 * vb + 2 + vk2);
-            const float d = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vrow + 18 * vb));
-            const float n0 = (float)(nb & 15u), n1 = (float)((nb >> 8) & 15u);
-            const float n2 = (float)((nb >> 4) & 15u), n3 = (float)(nb >> 12);
+            const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 16 * vb + 4 * vk);
+            const float d = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vrow + 128 + 2 * vb));
+            const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+            float n[8];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                n[e] = (float)((lo >> (8 * e)) & 0xFFu);
+                n[4 + e] = (float)((hi >> (8 * e)) & 0xFFu);
+            }
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float wgt = sh.pr[wave][t][h] * d;
-                o[h][0] = __builtin_fmaf(wgt, n0, o[h][0]);
-                o[h][1] = __builtin_fmaf(wgt, n1, o[h][1]);
-                o[h][2] = __builtin_fmaf(wgt, n2, o[h][2]);
-                o[h][3] = __builtin_fmaf(wgt, n3, o[h][3]);
+#pragma unroll
+                for (int e = 0; e < 8; e++) o[h][e] = __builtin_fmaf(wgt, n[e], o[h][e]);
                 cs[h] += wgt;
             }
         }
+    }
+    // the two position parities
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[h][e] += xor_lane<32>(o[h][e], lane);
+        cs[h] += xor_lane<32>(cs[h], lane);
     }
 
     // wave states -> LDS, then combine the four waves per query head
@@ -407,16 +450,19 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
     constexpr int HB = (int)(sizeof(sh.v) / (sizeof(float) * QA_WAVES * QA_HD));  // heads that fit per pass
     constexpr int HPASS = G <= 8 ? G : 8;                                          // heads per exchange pass
     static_assert(HPASS <= HB && G % HPASS == 0, "exchange buffer");
-    const int e0 = 32 * vb + vk2;
+    const int e0 = 32 * vb + 4 * vk;
     for (int hb = 0; hb < G; hb += HPASS) {
+        if (vh == 0) {
 #pragma unroll
-        for (int hh = 0; hh < HPASS; hh++) {
-            const int h = hb + hh;
-            float* dst = ob + ((int64_t)wave * HPASS + hh) * QA_HD;
-            dst[e0] = __builtin_fmaf(-8.0f, cs[h], o[h][0]);
-            dst[e0 + 1] = __builtin_fmaf(-8.0f, cs[h], o[h][1]);
-            dst[e0 + 16] = __builtin_fmaf(-8.0f, cs[h], o[h][2]);
-            dst[e0 + 17] = __builtin_fmaf(-8.0f, cs[h], o[h][3]);
+            for (int hh = 0; hh < HPASS; hh++) {
+                const int h = hb + hh;
+                float* dst = ob + ((int64_t)wave * HPASS + hh) * QA_HD;
+                const float c8 = -8.0f * cs[h];
+                *reinterpret_cast<float4*>(dst + e0) =
+                    make_float4(o[h][0] + c8, o[h][1] + c8, o[h][2] + c8, o[h][3] + c8);
+                *reinterpret_cast<float4*>(dst + e0 + 16) =
+                    make_float4(o[h][4] + c8, o[h][5] + c8, o[h][6] + c8, o[h][7] + c8);
+            }
         }
         __syncthreads();
         for (int hh = 0; hh < HPASS; hh++) {

@@ -495,21 +495,45 @@ __global__ __launch_bounds__(256) void k_q4_merge(kvq_q4_attn_args a, Q4Plan p) 
     if (row >= (int64_t)a.n_seqs * a.n_q_heads) return;
     const int s = (int)(row / a.n_q_heads);
     const int hq = (int)(row % a.n_q_heads);
-    const int64_t c0 = p.chunk_prefix[s], c1 = p.chunk_prefix[s + 1];
+    const int64_t c0 = p.chunk_prefix[s], nc = p.chunk_prefix[s + 1] - c0;
+    // the splits' maxima and sums one split per lane (64 at a time), then the
+    // partial rows with the weights broadcast from their lanes; the row loads
+    // do not depend on each other
     float mx = -INFINITY;
-    for (int64_t cc = c0; cc < c1; cc++) mx = fmaxf(mx, p.part_m[cc * a.n_q_heads + hq]);
+    for (int64_t b0 = 0; b0 < nc; b0 += 64) {
+        const int64_t j = b0 + lane;
+        mx = fmaxf(mx, wave_max(j < nc ? p.part_m[(c0 + j) * a.n_q_heads + hq] : -INFINITY));
+    }
     float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float L = 0.0f;
     if (mx != -INFINITY) {
-        for (int64_t cc = c0; cc < c1; cc++) {
-            const int64_t prow = cc * a.n_q_heads + hq;
-            const float f = exp2f(p.part_m[prow] - mx);
-            L = __builtin_fmaf(p.part_l[prow], f, L);
-            const float4 ov = reinterpret_cast<const float4*>(p.part_o + prow * QA_HD)[lane];
-            x[0] = __builtin_fmaf(ov.x, f, x[0]);
-            x[1] = __builtin_fmaf(ov.y, f, x[1]);
-            x[2] = __builtin_fmaf(ov.z, f, x[2]);
-            x[3] = __builtin_fmaf(ov.w, f, x[3]);
+        for (int64_t b0 = 0; b0 < nc; b0 += 64) {
+            const int64_t j = b0 + lane;
+            float f = 0.0f, lj = 0.0f;
+            if (j < nc) {
+                f = exp2f(p.part_m[(c0 + j) * a.n_q_heads + hq] - mx);
+                lj = p.part_l[(c0 + j) * a.n_q_heads + hq];
+            }
+            L += wave_sum(lj * f);
+            const int n = (int)min((int64_t)64, nc - b0);
+            const float4* po = reinterpret_cast<const float4*>(p.part_o + ((c0 + b0) * a.n_q_heads + hq) * QA_HD) + lane;
+            const int64_t stride = (int64_t)a.n_q_heads * (QA_HD / 4);  // float4s between splits
+            auto acc = [&](float fu, const float4& ov) {
+                x[0] = __builtin_fmaf(ov.x, fu, x[0]);
+                x[1] = __builtin_fmaf(ov.y, fu, x[1]);
+                x[2] = __builtin_fmaf(ov.z, fu, x[2]);
+                x[3] = __builtin_fmaf(ov.w, fu, x[3]);
+            };
+            int u = 0;
+            for (; u + 4 <= n; u += 4) {
+                const float4 o0 = po[u * stride], o1 = po[(u + 1) * stride];
+                const float4 o2 = po[(u + 2) * stride], o3 = po[(u + 3) * stride];
+                acc(__shfl(f, u, 64), o0);
+                acc(__shfl(f, u + 1, 64), o1);
+                acc(__shfl(f, u + 2, 64), o2);
+                acc(__shfl(f, u + 3, 64), o3);
+            }
+            for (; u < n; u++) acc(__shfl(f, u, 64), po[u * stride]);
         }
         const float inv = 1.0f / L;
 #pragma unroll

@@ -151,3 +151,39 @@ def test_q4_attn_refusals():
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_decode_attn_q4_0(cache, bad, torch.empty(need, dtype=torch.uint8, device=DEV))
     assert e.value.status == kvq.KVQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("page_size,n_kv,group", [(48, 2, 8), (16, 3, 2), (1, 1, 16)])
+def test_q4_attn_other_pages_and_kv_heads(page_size, n_kv, group):
+    """Page sizes that are not powers of two (48), tiny pages (1), 1-3 KV heads."""
+    _say(f"q4 attn page {page_size} kv {n_kv} group {group}")
+    rng = np.random.default_rng(1014 + page_size)
+    lens = np.array([0, 37, 300, 1100], np.int64)
+    pages = (lens + page_size - 1) // page_size
+    max_pages = int(pages.max())
+    perm = rng.permutation(int(pages.sum())).astype(np.int32)
+    table = np.full((len(lens), max_pages), -1, np.int32)
+    k = 0
+    for s, n in enumerate(pages):
+        table[s, :n] = perm[k:k + n]
+        k += n
+    n_cells = int(pages.sum()) * page_size
+    kp = np.zeros((n_cells, n_kv, 144), np.uint8)
+    vp = np.zeros_like(kp)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    total = int(off[-1])
+    ks = (rng.standard_normal((total, n_kv, 256)) * rng.choice([0.01, 1.0, 30.0], (total, n_kv, 1))).astype(np.float32)
+    vs = rng.standard_normal((total, n_kv, 256)).astype(np.float32)
+    oracle.append_q4_0(kp, vp, table, page_size, np.zeros(len(lens), np.int32), off, ks, vs)
+    q = (rng.standard_normal((len(lens), n_kv * group, 256)) / 16).astype(np.float32)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, table, page_size, off, q, SM)
+    kpd = torch.from_numpy(kp).to(DEV)
+    vpd = torch.from_numpy(vp).to(DEV)
+    cache = kvq.q4_cache(kpd, vpd, torch.from_numpy(table).to(DEV), page_size)
+    qd = torch.from_numpy(q).to(DEV)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device=DEV)
+    a = kvq.q4_attn_args(torch.from_numpy(off).to(DEV), total, qd, out, lse, SM, 256)
+    kvq.kvq_decode_attn_q4_0(cache, a, kvq.alloc_workspace_q4(cache, a))
+    torch.cuda.synchronize()
+    _check(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"page {page_size} kv {n_kv}")

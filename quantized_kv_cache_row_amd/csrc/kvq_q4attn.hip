@@ -30,10 +30,12 @@
 //     the positions of one parity, O += (p d) * nibble with p from LDS, plus a
 //     per-head correction sum of p d (the -8 term) applied once at the end;
 //     the two parities are added across the wave halves.
-// Nothing here is a dense contraction big enough for the matrix cores at
-// G <= 16 query heads per KV head without a transposed V operand; the kernel
-// is bound by VALU issue (about 5 * G + 8 instructions per element and
-// position over K and V), see the roofline in the design notes.
+// The arithmetic stays on the vector ALU: about 9 * G + 12 wave64
+// instructions per position and KV head (scores 4 * G + 5.6, values
+// 5 * G + 6.5), which at G = 4 query heads per KV head outweighs the 288 HBM
+// bytes of the two head-rows; the matrix cores (a K = 32 step per block for
+// the scores, a V operand transposed through LDS for the values) are the way
+// past that bound.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 

@@ -89,6 +89,24 @@ def test_refusals_without_launch():
         kvq.KVQ_ERR_INVALID_ARG  # unknown flag
     assert L.kvq_gather_q4_0(None, 1, P(256), 1, P(256), P(256), None) == kvq.KVQ_ERR_INVALID_ARG
     assert L.kvq_convert(9, P(256), 4, P(256), None) == kvq.KVQ_ERR_UNSUPPORTED
+    # fused q4_0 decode
+    qa = kvq.KvqQ4AttnArgs(2, 32, 0, 0, 1000, 256, 256, 256, None, 0.0625, 0)
+    need = L.kvq_decode_attn_q4_0_workspace_bytes(ctypes.byref(c), ctypes.byref(qa))
+    assert need > 0
+    assert L.kvq_decode_attn_q4_0(ctypes.byref(c), ctypes.byref(qa), P(256), need - 1, None) == kvq.KVQ_ERR_WORKSPACE
+    assert L.kvq_decode_attn_q4_0(ctypes.byref(c), ctypes.byref(qa), P(264), need, None) == \
+        kvq.KVQ_ERR_INVALID_ARG  # workspace not 256-byte aligned
+    for n_q in (24, 4, 8 * 32):  # ratios 3, 1/2, 32
+        qa.n_q_heads = n_q
+        assert L.kvq_decode_attn_q4_0_workspace_bytes(ctypes.byref(c), ctypes.byref(qa)) == -1
+        assert L.kvq_decode_attn_q4_0(ctypes.byref(c), ctypes.byref(qa), P(256), need, None) == \
+            kvq.KVQ_ERR_UNSUPPORTED
+    qa.n_q_heads, qa.split_rows = 32, 300  # not a multiple of 256
+    assert L.kvq_decode_attn_q4_0(ctypes.byref(c), ctypes.byref(qa), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    qa.split_rows, qa.q = 0, 260  # misaligned query
+    assert L.kvq_decode_attn_q4_0(ctypes.byref(c), ctypes.byref(qa), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    qa.q, qa.sm_scale = 256, float("nan")
+    assert L.kvq_decode_attn_q4_0(ctypes.byref(c), ctypes.byref(qa), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
 
 
 def test_binding_has_no_cpu_path():

@@ -48,6 +48,11 @@ constexpr int QA_TILE = 64;   // positions per wave tile (one per lane)
 constexpr int QA_HD = 256;    // head_dim
 constexpr int QA_RB = 144;    // bytes per head-row: 8 blocks of 18
 constexpr int QA_NXCD = 8;
+// Query heads per workgroup at most: larger groups split over workgroups that
+// read the same head-rows (neighbouring items, so from the same L2).  Eight
+// heads per workgroup fill all 256 registers and took 1.5 x the time of two
+// workgroups of four.
+constexpr int QA_GMAX = 4;
 constexpr float QA_LOG2E = 1.4426950408889634f;
 constexpr float QA_LN2 = 0.6931471805599453f;
 
@@ -59,9 +64,10 @@ struct Q4Plan {
     float* part_l;          // [max_chunks][n_q]
     float* part_o;          // [max_chunks][n_q][256] (rotated domain, unnormalized)
     int64_t max_chunks;
-    int64_t items_per_xcd;  // attn grid: item (chunk * n_kv + kv head) runs on XCD item / items_per_xcd
+    int64_t items_per_xcd;  // attn grid: item ((chunk * n_kv + kv head) * sub + part) runs on XCD item / items_per_xcd
     int split;
     int group;              // query heads per KV head
+    int sub;                // workgroups per (split, KV head): each takes group / sub query heads
 };
 
 int q4_auto_split(const kvq_q4_attn_args& a, int n_kv) {
@@ -77,10 +83,11 @@ Q4Plan q4_make_plan(const kvq_q4_cache& c, const kvq_q4_attn_args& a, void* ws, 
     Q4Plan p{};
     p.split = a.split_rows > 0 ? a.split_rows : q4_auto_split(a, c.n_kv_heads);
     p.group = a.n_q_heads / c.n_kv_heads;
+    p.sub = p.group > QA_GMAX ? p.group / QA_GMAX : 1;
     // sum_s max(1, ceil(len_s / split)), as for the latent decode's T-split
     p.max_chunks = std::max<int64_t>(a.n_seqs, std::min<int64_t>(a.total_rows / p.split + a.n_seqs,
                                                                   (a.total_rows + p.split - 1) / p.split + a.n_seqs - 1));
-    p.items_per_xcd = (p.max_chunks * c.n_kv_heads + QA_NXCD - 1) / QA_NXCD;
+    p.items_per_xcd = (p.max_chunks * c.n_kv_heads * p.sub + QA_NXCD - 1) / QA_NXCD;
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
     int64_t off = 0;
     char* base = (char*)ws;
@@ -274,11 +281,12 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
     __shared__ __align__(16) Q4AttnShared<G> sh;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t n_items = p.max_chunks * c.n_kv_heads;
+    const int64_t n_items = p.max_chunks * c.n_kv_heads * p.sub;
     const int64_t item = (int64_t)(blockIdx.x % QA_NXCD) * p.items_per_xcd + blockIdx.x / QA_NXCD;
     if (item >= n_items) return;
-    const int64_t ch = item / c.n_kv_heads;
-    const int g = (int)(item % c.n_kv_heads);
+    const int64_t ch = item / ((int64_t)c.n_kv_heads * p.sub);
+    const int rem = (int)(item % ((int64_t)c.n_kv_heads * p.sub));
+    const int g = rem / p.sub, part = rem % p.sub;
     const int64_t nch = p.chunk_prefix[a.n_seqs];
     if (ch >= nch) return;
     int s;
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
     const int64_t len = seq_len(a.len_off, s);
     const int64_t r0 = (ch - p.chunk_prefix[s]) * p.split;
     const int64_t r1 = min(len, r0 + p.split);
-    const int hq0 = g * G;
+    const int hq0 = g * p.group + part * G;
     const int64_t qrow0 = (int64_t)s * a.n_q_heads + hq0;
 
     // rotated queries of the G heads and their block sums
@@ -570,9 +578,9 @@ hipError_t launch_decode_attn_q4_0(const kvq_q4_cache& c, const kvq_q4_attn_args
     switch (p.group) {
         case 1: e = launch_attn_g<1>(c, a, p, st); break;
         case 2: e = launch_attn_g<2>(c, a, p, st); break;
-        case 4: e = launch_attn_g<4>(c, a, p, st); break;
-        case 8: e = launch_attn_g<8>(c, a, p, st); break;
-        case 16: e = launch_attn_g<16>(c, a, p, st); break;
+        case 4:
+        case 8:
+        case 16: e = launch_attn_g<QA_GMAX>(c, a, p, st); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

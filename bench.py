@@ -282,6 +282,14 @@ def measure_other_rows(torch, kvq, workloads, x_kv8):
     kv_bytes = tok * 8 * 2 * 144
     hbm("q4_0_decode_attn_g4", kv_bytes, ms, {"tokens": tok, "q_heads": 32, "kv_heads": 8,
                                                "tokens/s": tok / (ms / 1000.0)})
+    # the same pools read by 64 query heads (8 per KV head)
+    q8 = torch.from_numpy(workloads.q4_queries(1007, q.n_seqs, n_q_heads=64)).to(dev)
+    o8 = torch.empty_like(q8)
+    qa = kvq.q4_attn_args(off, tok, q8, o8, None, workloads.Q4_SM_SCALE)
+    qws = kvq.alloc_workspace_q4(cache, qa)
+    ms = time_graph(torch, q4_call, 6)
+    hbm("q4_0_decode_attn_g8", kv_bytes, ms, {"tokens": tok, "q_heads": 64, "kv_heads": 8,
+                                               "tokens/s": tok / (ms / 1000.0)})
     return res
 
 

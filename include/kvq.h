@@ -45,7 +45,14 @@ extern "C" {
 /* ---- modes ---------------------------------------------------------------- */
 #define KVQ_QMODE_FP8 1      /* e4m3 codes [rows][dim] + fp32 scale per row           */
 #define KVQ_QMODE_TQ4 2      /* 4-bit codebook indices [rows][dim/2] + fp32 radius    */
-#define KVQ_PREC_MFMA 0      /* 16-bit matrix-core contractions, fp32 softmax/scales */
+/* KVQ_PREC_MFMA: 16-bit matrix-core contractions with fp32 accumulation,
+ * softmax and per-row scales.  [KV8]'s matrix-core wording names bf16
+ * operands; it is read as "16-bit operands, fp32 accumulation", and the
+ * latent codes and query are fp16 (exact for every e4m3 code and codebook
+ * level, 3 more mantissa bits than bf16 for the query and probabilities, the
+ * range handled by power-of-two scaling), the rope term bf16 (k_rope is
+ * stored bf16) with a two-term bf16 query.  Hence the name: not _BF16. */
+#define KVQ_PREC_MFMA 0
 #define KVQ_PREC_FP32 1      /* fp32 vector arithmetic throughout (check path)        */
 #define KVQ_Q4_NO_ROTATE 1u  /* append: rows are already in the rotated domain        */
 
@@ -145,9 +152,10 @@ int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_of
  *   x_hat_t = the decoded latent row (fp8: e4m3(code)*scale; TQ4: see above);
  *   s_t = sm_scale * (q_lat[s,h] . x_hat_t + q_rope[s,h] . k_rope_t);
  *   out[s,h] = sum_t softmax(s)_t x_hat_t;  lse[s,h] = log sum_t exp(s_t).
- * The latent rows are not reconstructed: fp8 codes are converted exactly to
- * bf16 and the per-row scale is applied in fp32; TQ4 uses the rotated query
- * R q and un-rotates the merged output (R = H D / sqrt(dim)).
+ * The latent rows are not reconstructed: fp8 codes (and TQ4 codebook levels)
+ * are converted exactly to fp16 matrix-core operands (KVQ_PREC_MFMA) or to
+ * fp32 (KVQ_PREC_FP32), and the per-row scale is applied in fp32; TQ4 uses
+ * the rotated query R q and un-rotates the merged output (R = H D / sqrt(dim)).
  * A sequence with no rows gets out = 0 and lse = -Inf.
  * Tolerance against an fp64 evaluation on the same codes:
  *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA), <= 1e-5 (KVQ_PREC_FP32).
@@ -251,7 +259,9 @@ int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int
  *             of position t (fp32, exact: no rounding to binary16);
  *   s_t     = sm_scale * (q~ . k_t);  p = softmax(s) over the positions;
  *   out     = FWHT256(sum_t p_t v_t) / 16 (rotated back), lse = log sum exp s_t.
- * Sequence s attends positions 0 .. len_off[s+1] - len_off[s] - 1 through
+ * Sequence s attends positions 0 .. n_s - 1, n_s = min(len_off[s+1], total_rows)
+ * - max(len_off[s], 0) (the device offsets are clamped to the host total, so
+ * a stale device copy never makes the call read past its workspace), through
  * cache.block_table (cell = table[s][pos / page_size] * page_size + pos %
  * page_size); positions whose page column is past max_pages, whose table entry
  * is negative or whose cell is past n_cells take no part.  A sequence with no
@@ -259,7 +269,7 @@ int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int
  * pages' model is the caller's.
  * Arithmetic: fp32 throughout (scores as d * (sum nibble * q~ - 8 * sum q~)
  * per block, sm_scale * log2(e) folded into q~, exp2); tolerance against an
- * fp64 evaluation on the same pool bytes: max|err| / max|ref| <= 1e-4. */
+ * fp64 evaluation on the same pool bytes: max|err| / max|ref| <= 1e-5. */
 typedef struct kvq_q4_attn_args {
     int32_t n_seqs;             /* >= 1                                              */
     int32_t n_q_heads;          /* n_kv_heads * G with G in {1, 2, 4, 8, 16}          */

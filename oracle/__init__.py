@@ -78,6 +78,9 @@ def lib():
         L.oracle_tq4_identity_check.argtypes = [_c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p,
                                                 _c_f64p, _c_f64p]
         L.oracle_tq4_identity_check.restype = ctypes.c_double
+        L.oracle_tq4_identity_check_planted.argtypes = [_c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p,
+                                                        _c_f64p, _c_f64p, ctypes.c_int]
+        L.oracle_tq4_identity_check_planted.restype = ctypes.c_double
         L.oracle_decode_attn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          _c_i64p, _c_u8p, _c_f32p, _c_u16p, _c_u8p, _c_f32p, _c_f32p,
                                          ctypes.c_double, _c_f64p, _c_f64p]
@@ -259,7 +262,9 @@ def decode_tq4(codes, radii, sign_mask):
     return out
 
 
-def tq4_identity_check(codes, radii, sign_mask, q, w):
+def tq4_identity_check(codes, radii, sign_mask, q, w, plant=0):
+    """Largest relative discrepancy of the two rotation identities; plant > 0
+    plants a known mistake in the check (tests of the check's sensitivity)."""
     codes = _c(codes, np.uint8)
     radii = _c(radii, np.float32)
     m = _c(sign_mask, np.uint8)
@@ -267,6 +272,9 @@ def tq4_identity_check(codes, radii, sign_mask, q, w):
     w = _c(w, np.float64)
     n = codes.shape[0]
     dim = codes.shape[1] * 2
+    if plant:
+        return lib().oracle_tq4_identity_check_planted(_p(codes, _c_u8p), _p(radii, _c_f32p), n, dim,
+                                                       _p(m, _c_u8p), _p(q, _c_f64p), _p(w, _c_f64p), int(plant))
     return lib().oracle_tq4_identity_check(_p(codes, _c_u8p), _p(radii, _c_f32p), n, dim, _p(m, _c_u8p),
                                            _p(q, _c_f64p), _p(w, _c_f64p))
 

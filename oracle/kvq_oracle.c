@@ -457,9 +457,15 @@ int oracle_decode_tq4_rows(const uint8_t* codes, const float* radii, int64_t n_r
  *   q . x_hat_t        == (R q) . y_t
  *   sum_t w_t x_hat_t  == R^T (sum_t w_t y_t)
  * Both sides are formed in double; returns the largest relative discrepancy
- * (against the magnitude of the terms) over all rows and coordinates. */
-double oracle_tq4_identity_check(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
-                                 const uint8_t* sign_mask, const double* q, const double* w) {
+ * (against the magnitude of the terms) over all rows and coordinates.
+ *
+ * `plant` exists only so that a test can show the check is sensitive: 0 is the
+ * definition; 1 leaves the query unrotated (R q := q); 2 drops the signs from
+ * the query rotation (R q := H q / sqrt(n)); 3 drops the signs from the
+ * un-rotation (R^T v := H v / sqrt(n)); 4 leaves the weighted sum unrotated
+ * (R^T v := v).  Each planted mistake must show up as a large discrepancy. */
+static double tq4_identity_check_planted(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
+                                         const uint8_t* sign_mask, const double* q, const double* w, int plant) {
     if (!is_pow2(dim) || dim < 2) return -1.0;
     float lv[16];
     oracle_tq4_codebook(NULL, lv, NULL, NULL);
@@ -472,9 +478,11 @@ double oracle_tq4_identity_check(const uint8_t* codes, const float* radii, int64
     double* sxa = (double*)calloc((size_t)dim, sizeof(double));
     double worst = 0.0;
     /* R q = H D q / sqrt(n) */
-    for (int i = 0; i < dim; i++) rq[i] = sign_bit(sign_mask, i) ? -q[i] : q[i];
-    fwht_f64(rq, dim);
-    for (int i = 0; i < dim; i++) rq[i] /= rs;
+    for (int i = 0; i < dim; i++) rq[i] = (sign_bit(sign_mask, i) && plant != 2) ? -q[i] : q[i];
+    if (plant != 1) {
+        fwht_f64(rq, dim);
+        for (int i = 0; i < dim; i++) rq[i] /= rs;
+    }
     for (int64_t r = 0; r < n_rows; r++) {
         decode_tq4_rows_with(lv, codes + r * (dim / 2), radii + r, 1, dim, sign_mask, xh);
         const uint8_t* cr = codes + r * (dim / 2);
@@ -499,9 +507,9 @@ double oracle_tq4_identity_check(const uint8_t* codes, const float* radii, int64
         }
     }
     /* R^T sy = D H sy / sqrt(n) */
-    fwht_f64(sy, dim);
+    if (plant != 4) fwht_f64(sy, dim);
     for (int i = 0; i < dim; i++) {
-        double v = (sign_bit(sign_mask, i) ? -sy[i] : sy[i]) / rs;
+        double v = plant == 4 ? sy[i] : ((sign_bit(sign_mask, i) && plant != 3) ? -sy[i] : sy[i]) / rs;
         if (sxa[i] > 0) {
             double e = fabs(v - sx[i]) / sxa[i];
             if (e > worst) worst = e;
@@ -509,6 +517,17 @@ double oracle_tq4_identity_check(const uint8_t* codes, const float* radii, int64
     }
     free(xh); free(y); free(rq); free(sx); free(sy); free(sxa);
     return worst;
+}
+
+double oracle_tq4_identity_check(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
+                                 const uint8_t* sign_mask, const double* q, const double* w) {
+    return tq4_identity_check_planted(codes, radii, n_rows, dim, sign_mask, q, w, 0);
+}
+
+/* The same check with a planted mistake (see above); tests only. */
+double oracle_tq4_identity_check_planted(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
+                                         const uint8_t* sign_mask, const double* q, const double* w, int plant) {
+    return tq4_identity_check_planted(codes, radii, n_rows, dim, sign_mask, q, w, plant);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -28,8 +28,10 @@
 //     that every read is aligned (nibble bytes of block b at 16b, scales at
 //     128); a lane owns 8 output elements (4 nibble bytes of one block) over
 //     the positions of one parity, O += (p d) * nibble with p from LDS, plus a
-//     per-head correction sum of p d (the -8 term) applied once at the end;
-//     the two parities are added across the wave halves.
+//     per-head sum of p d for the -8 term, folded into O at the end of every
+//     tile (so the offset codes' large, nearly cancelling sums never span more
+//     than one tile's 32 positions per lane); the two parities are added
+//     across the wave halves.
 // The arithmetic stays on the vector ALU: about 9 * G + 12 wave64
 // instructions per position and KV head (scores 4 * G + 5.6, values
 // 5 * G + 6.5), which at G = 4 query heads per KV head outweighs the 288 HBM
@@ -107,9 +109,12 @@ Q4Plan q4_make_plan(const kvq_q4_cache& c, const kvq_q4_attn_args& a, void* ws, 
     return p;
 }
 
-__device__ __forceinline__ int64_t seq_len(const int64_t* __restrict__ off, int s) {
-    const int64_t n = off[s + 1] - off[s];
-    return n > 0 ? n : 0;
+// Positions of sequence s.  The offsets are clamped to [0, total] (total =
+// the host copy of off[n_seqs]), as the latent decode clamps its rows, so the
+// split count built from them never exceeds what the workspace was sized for.
+__device__ __forceinline__ int64_t seq_len(const int64_t* __restrict__ off, int s, int64_t total) {
+    const int64_t lo = max(off[s], (int64_t)0), hi = min(off[s + 1], total);
+    return hi > lo ? hi - lo : 0;
 }
 
 // Orthonormal FWHT-256 of a row held 4 consecutive values per lane (lane l has
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
         const int s0 = tid * per, s1 = min(a.n_seqs, s0 + per);
         int64_t local = 0;
         for (int s = s0; s < s1; s++) {
-            const int64_t n = seq_len(a.len_off, s);
+            const int64_t n = seq_len(a.len_off, s, a.total_rows);
             local += n > 0 ? (n + p.split - 1) / p.split : 1;
         }
         part[tid] = local;
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
         int64_t run = tid > 0 ? part[tid - 1] : 0;
         for (int s = s0; s < s1; s++) {
             p.chunk_prefix[s] = run;
-            const int64_t n = seq_len(a.len_off, s);
+            const int64_t n = seq_len(a.len_off, s, a.total_rows);
             run += n > 0 ? (n + p.split - 1) / p.split : 1;
         }
         if (tid == 255) p.chunk_prefix[a.n_seqs] = part[255];
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
         }
         s = lo;
     }
-    const int64_t len = seq_len(a.len_off, s);
+    const int64_t len = seq_len(a.len_off, s, a.total_rows);
     const int64_t r0 = (ch - p.chunk_prefix[s]) * p.split;
     const int64_t r1 = min(len, r0 + p.split);
     const int hq0 = g * p.group + part * G;
@@ -341,12 +346,11 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
         return ok;
     };
 
-    float m[G], lp[G], o[G][8], cs[G];
+    float m[G], lp[G], o[G][8];
 #pragma unroll
     for (int h = 0; h < G; h++) {
         m[h] = -INFINITY;
         lp[h] = 0.0f;
-        cs[h] = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; e++) o[h][e] = 0.0f;
     }
@@ -408,14 +412,17 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
             }
             m[h] = mn;
             lp[h] = __builtin_fmaf(lp[h], alpha, pv);
-            cs[h] *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; e++) o[h][e] *= alpha;
             sh.pr[wave][lane][h] = pv;
         }
 
         // values: lane = elements 32 vb + 4 vk + {0..3} and 32 vb + 16 + 4 vk + {0..3} over the
-        // positions of parity vh (rows past nt are zero with p = 0, so the pair loop may read one)
+        // positions of parity vh (rows past nt are zero with p = 0, so the pair loop may read one);
+        // cs = this tile's sum of p d, the weight of the -8 offset, folded in below
+        float cs[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) cs[h] = 0.0f;
 #pragma unroll 4
         for (int tt = 0; tt < nt; tt += 2) {
             const int t = tt + vh;
@@ -437,14 +444,17 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
                 cs[h] += wgt;
             }
         }
+        // sum p d (nibble - 8) = sum p d nibble - 8 sum p d, once per tile
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[h][e] = __builtin_fmaf(-8.0f, cs[h], o[h][e]);
     }
     // the two position parities
 #pragma unroll
-    for (int h = 0; h < G; h++) {
+    for (int h = 0; h < G; h++)
 #pragma unroll
         for (int e = 0; e < 8; e++) o[h][e] += xor_lane<32>(o[h][e], lane);
-        cs[h] += xor_lane<32>(cs[h], lane);
-    }
 
     // wave states -> LDS, then combine the four waves per query head
 #pragma unroll
@@ -467,11 +477,8 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
             for (int hh = 0; hh < HPASS; hh++) {
                 const int h = hb + hh;
                 float* dst = ob + ((int64_t)wave * HPASS + hh) * QA_HD;
-                const float c8 = -8.0f * cs[h];
-                *reinterpret_cast<float4*>(dst + e0) =
-                    make_float4(o[h][0] + c8, o[h][1] + c8, o[h][2] + c8, o[h][3] + c8);
-                *reinterpret_cast<float4*>(dst + e0 + 16) =
-                    make_float4(o[h][4] + c8, o[h][5] + c8, o[h][6] + c8, o[h][7] + c8);
+                *reinterpret_cast<float4*>(dst + e0) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+                *reinterpret_cast<float4*>(dst + e0 + 16) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
             }
         }
         __syncthreads();
@@ -505,7 +512,9 @@ __global__ __launch_bounds__(256) void k_q4_merge(kvq_q4_attn_args a, Q4Plan p) 
     if (row >= (int64_t)a.n_seqs * a.n_q_heads) return;
     const int s = (int)(row / a.n_q_heads);
     const int hq = (int)(row % a.n_q_heads);
-    const int64_t c0 = p.chunk_prefix[s], nc = p.chunk_prefix[s + 1] - c0;
+    // clamped to the workspace's splits (the prefix is built from device offsets)
+    const int64_t c0 = min(p.chunk_prefix[s], p.max_chunks);
+    const int64_t nc = max(min(p.chunk_prefix[s + 1], p.max_chunks) - c0, (int64_t)0);
     // the splits' maxima and sums one split per lane (64 at a time), then the
     // partial rows with the weights broadcast from their lanes; the row loads
     // do not depend on each other

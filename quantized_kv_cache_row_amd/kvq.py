@@ -168,6 +168,15 @@ def _ptr(t, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, shape, name):
+    """Raises ValueError unless tensor t has this shape (None entries match any size)."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        raise ValueError(f"{name}: shape {got}, expected {tuple('*' if w is None else w for w in shape)}")
+
+
 # ---- device entry points --------------------------------------------------------
 
 def kvq_encode_fp8(x, codes, scales, stream=None):
@@ -189,7 +198,10 @@ def kvq_encode_tq4(x, sign_mask, codes, radii, stream=None):
 
 def q4_cache(k_pool, v_pool, block_table, page_size, head_dim=256):
     """The cache descriptor; it keeps the tensors it points to alive."""
+    _shape(k_pool, (None, None, 144), "k_pool")
     n_cells, n_kv, rb = k_pool.shape
+    _shape(v_pool, (n_cells, n_kv, 144), "v_pool")
+    _shape(block_table, (None, None), "block_table")
     c = KvqQ4Cache(_ptr(k_pool, torch.uint8, "k_pool"), _ptr(v_pool, torch.uint8, "v_pool"),
                    _ptr(block_table, torch.int32, "block_table"), n_cells, block_table.shape[1],
                    page_size, n_kv, head_dim)
@@ -218,7 +230,17 @@ def kvq_gather_q4_0(cache, dst_off, total_rows, k_dst, v_dst, stream=None):
 def attn_args(qmode, precision, seq_offsets, total_rows, codes, row_scale, k_rope, q_lat, q_rope, sm_scale, out,
               lse=None, sign_mask=None, split_rows=0):
     """The argument struct; it keeps the tensors it points to alive."""
+    _shape(q_lat, (None, None, None), "q_lat")
     n_seqs, n_heads, dim_lat = q_lat.shape
+    _shape(q_rope, (n_seqs, n_heads, None), "q_rope")
+    _shape(out, (n_seqs, n_heads, dim_lat), "out")
+    _shape(lse, (n_seqs, n_heads), "lse")
+    _shape(seq_offsets, (n_seqs + 1,), "seq_offsets")
+    _shape(codes, (None, dim_lat if qmode == KVQ_QMODE_FP8 else dim_lat // 2), "codes")
+    rows = codes.shape[0]
+    _shape(row_scale, (rows,), "row_scale")
+    _shape(k_rope, (rows, q_rope.shape[2]), "k_rope")
+    _shape(sign_mask, (dim_lat // 8,), "sign_mask")
     a = KvqAttnArgs(
         qmode, precision, n_seqs, n_heads, dim_lat, q_rope.shape[2], split_rows, 0, int(total_rows),
         _ptr(seq_offsets, torch.int64, "seq_offsets"), _ptr(codes, torch.uint8, "codes"),
@@ -241,11 +263,20 @@ def kvq_decode_attn_workspace_bytes(args):
 def kvq_decode_attn(args, workspace, stream=None):
     """args: KvqAttnArgs (see attn_args); workspace: a device uint8 tensor of at
     least kvq_decode_attn_workspace_bytes(args) bytes."""
+    _cache_rows_cover(args)
     _check("kvq_decode_attn", lib().kvq_decode_attn(ctypes.byref(args), _ptr(workspace, torch.uint8, "workspace"),
                                                     workspace.numel(), _stream(stream)))
 
 
+def _cache_rows_cover(args):
+    """The dense decode reads rows 0 .. total_rows - 1 of the code arrays."""
+    codes = args._keep[1]
+    if codes is not None and codes.shape[0] < args.total_rows:
+        raise ValueError(f"codes: {codes.shape[0]} rows, fewer than total_rows = {args.total_rows}")
+
+
 def kvq_decode_attn_stage(args, stage, workspace, stream=None):
+    _cache_rows_cover(args)
     _check("kvq_decode_attn_stage", lib().kvq_decode_attn_stage(ctypes.byref(args), int(stage),
                                                                 _ptr(workspace, torch.uint8, "workspace"),
                                                                 workspace.numel(), _stream(stream)))
@@ -297,7 +328,11 @@ def alloc_workspace(args, device="cuda"):
 
 def q4_attn_args(len_off, total_rows, q, out, lse=None, sm_scale=1.0 / 16.0, split_rows=0):
     """Arguments of kvq_decode_attn_q4_0; q / out fp32 [n_seqs][n_q_heads][256]."""
+    _shape(q, (None, None, 256), "q")
     n_seqs, n_q, _ = q.shape
+    _shape(out, (n_seqs, n_q, 256), "out")
+    _shape(lse, (n_seqs, n_q), "lse")
+    _shape(len_off, (n_seqs + 1,), "len_off")
     a = KvqQ4AttnArgs(n_seqs, n_q, int(split_rows), 0, int(total_rows), _ptr(len_off, torch.int64, "len_off"),
                       _ptr(q, torch.float32, "q"), _ptr(out, torch.float32, "out"),
                       _ptr(lse, torch.float32, "lse") if lse is not None else None, float(sm_scale), 0)

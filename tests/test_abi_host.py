@@ -114,3 +114,44 @@ def test_binding_has_no_cpu_path():
     x = torch.zeros(4, 512)
     with pytest.raises(ValueError, match="device tensor"):
         kvq.kvq_encode_fp8(x, torch.zeros(4, 512, dtype=torch.uint8), torch.zeros(4))
+
+
+def test_binding_refuses_mis_shaped_tensors():
+    """The wrappers check shapes before any pointer reaches the C ABI (which
+    cannot see a tensor's extent); these raise before the device check."""
+    import torch
+    u8, f32, i32, i64 = torch.uint8, torch.float32, torch.int32, torch.int64
+    kp = torch.zeros(64, 8, 144, dtype=u8)
+    tab = torch.zeros(1, 1, dtype=i32)
+    with pytest.raises(ValueError, match="k_pool"):
+        kvq.q4_cache(torch.zeros(64, 8, 128, dtype=u8), kp, tab, 64)
+    with pytest.raises(ValueError, match="v_pool"):
+        kvq.q4_cache(kp, torch.zeros(64, 4, 144, dtype=u8), tab, 64)
+    with pytest.raises(ValueError, match="block_table"):
+        kvq.q4_cache(kp, kp, torch.zeros(4, dtype=i32), 64)
+    off = torch.zeros(3, dtype=i64)
+    q = torch.zeros(2, 32, 256)
+    with pytest.raises(ValueError, match="q:"):
+        kvq.q4_attn_args(off, 10, torch.zeros(2, 32, 128), q)
+    with pytest.raises(ValueError, match="out"):
+        kvq.q4_attn_args(off, 10, q, torch.zeros(2, 16, 256))
+    with pytest.raises(ValueError, match="lse"):
+        kvq.q4_attn_args(off, 10, q, q, torch.zeros(2, 16))
+    with pytest.raises(ValueError, match="len_off"):
+        kvq.q4_attn_args(torch.zeros(2, dtype=i64), 10, q, q)
+    ql, qr = torch.zeros(1, 128, 512), torch.zeros(1, 128, 64)
+    codes, sc, kr = torch.zeros(100, 512, dtype=u8), torch.zeros(100), torch.zeros(100, 64, dtype=torch.int16)
+    off1 = torch.zeros(2, dtype=i64)
+    with pytest.raises(ValueError, match="codes"):
+        kvq.attn_args(1, 0, off1, 100, torch.zeros(100, 256, dtype=u8), sc, kr, ql, qr, 0.04, ql)
+    with pytest.raises(ValueError, match="row_scale"):
+        kvq.attn_args(1, 0, off1, 100, codes, torch.zeros(99), kr, ql, qr, 0.04, ql)
+    with pytest.raises(ValueError, match="k_rope"):
+        kvq.attn_args(1, 0, off1, 100, codes, sc, torch.zeros(100, 32, dtype=torch.int16), ql, qr, 0.04, ql)
+    with pytest.raises(ValueError, match="out"):
+        kvq.attn_args(1, 0, off1, 100, codes, sc, kr, ql, qr, 0.04, torch.zeros(1, 64, 512))
+    with pytest.raises(ValueError, match="seq_offsets"):
+        kvq.attn_args(1, 0, torch.zeros(3, dtype=i64), 100, codes, sc, kr, ql, qr, 0.04, ql)
+    with pytest.raises(ValueError, match="sign_mask"):
+        kvq.attn_args(2, 0, off1, 100, torch.zeros(100, 256, dtype=u8), sc, kr, ql, qr, 0.04, ql,
+                      sign_mask=torch.zeros(32, dtype=u8))

@@ -222,7 +222,10 @@ def _check_attn(w, c, s, precision, split_rows=0, q_lat=None, q_rope=None, tol=N
     assert e <= tol, (label, e)
     fin = np.isfinite(rlse)
     assert np.all(np.isneginf(glse[~fin]))
-    assert np.max(np.abs(glse[fin] - rlse[fin])) <= 50 * tol * max(1.0, np.max(np.abs(rlse[fin])))
+    if np.any(fin):  # lse per (sequence, head), relative to max(1, |lse|), at the same tolerance
+        el = float(np.max(np.abs(glse[fin] - rlse[fin]) / np.maximum(1.0, np.abs(rlse[fin]))))
+        _say(f"  {label} lse: max|err|/max(1,|lse|) = {el:.3e}")
+        assert el <= tol, (label, "lse", el)
     return got
 
 
@@ -309,17 +312,14 @@ def test_attn_ragged_edges():
         _check_attn(w2, c2, s2, prec, 32, label="edges-tq4")
 
 
-def test_attn_ragged_sampled_heads():
-    _say("attn ragged_kv8_decode (ragged, 33 sequences) sampled heads")
+def test_attn_ragged_full_size_all_heads():
+    """The ragged long-context workload at full size (32 sequences of 1024 ..
+    16384 rows and one of 131072, 128 heads) on every head, in the launch
+    configuration the benchmark times (automatic split)."""
+    _say("attn ragged_kv8_decode (ragged, 33 sequences) all 128 heads")
     w = workloads.ragged_kv8_decode()
     c, s = _encode_cache(w)
-    got, glse = gpu_attn(w, c, s, kvq.KVQ_PREC_MFMA)
-    heads = np.array([0, 37, 127])
-    ref, rlse = oracle.decode_attn(1, w.offsets, _np(c), _np(s), w.k_rope, w.q_lat[:, heads], w.q_rope[:, heads],
-                                   w.sm_scale)
-    e = rel_err(got[:, heads], ref)
-    _say(f"  ragged_kv8_decode heads {list(heads)}: {e:.3e}")
-    assert e <= 2e-3
+    _check_attn(w, c, s, kvq.KVQ_PREC_MFMA, label=w.name)
 
 
 def test_attn_ragged_div16_all_heads():

@@ -2,9 +2,10 @@
 
 Pools are written by the oracle's append on the CPU and the same bytes are
 uploaded, so both sides read identical blocks.  The HIP result must match the
-oracle's fp64 evaluation within max|err| / max|ref| <= 1e-4 per query head
-row set (fp32 arithmetic over 256-term dots, two 256-point rotations and a
-softmax: a few 1e-6 relative in practice), and lse within 1e-4 * max(1, |lse|).
+oracle's fp64 evaluation within max|err| / max|ref| <= 1e-5 per sequence
+(fp32 arithmetic over 256-term dots, two 256-point rotations and a softmax: a
+few 1e-6 relative in practice; the pages report 1.9-2.7e-7 for their fp32
+attention and merge), and lse within 1e-5 * max(1, |lse|).
 """
 import sys
 
@@ -17,7 +18,7 @@ from quantized_kv_cache_row_amd import kvq, workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-4
+TOL = 1e-5
 DEV = "cuda"
 SM = workloads.Q4_SM_SCALE
 
@@ -187,3 +188,31 @@ def test_q4_attn_other_pages_and_kv_heads(page_size, n_kv, group):
     kvq.kvq_decode_attn_q4_0(cache, a, kvq.alloc_workspace_q4(cache, a))
     torch.cuda.synchronize()
     _check(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"page {page_size} kv {n_kv}")
+
+
+@pytest.mark.parametrize("split_rows", [65536, 0])
+def test_q4_attn_long_flat_sequence(split_rows):
+    """One sequence of 65536 positions under a zero query (every score 0, so
+    the softmax is flat and every position weighs the same), one KV head and
+    four query heads, at one split of the whole sequence and at the automatic
+    split.  The value sum then adds 8192 positions per lane per parity; the
+    offset nibbles' -8 term must not leave an error that grows with that."""
+    _say(f"q4 attn long flat sequence split {split_rows}")
+    rng = np.random.default_rng(1015)
+    n = 65536
+    page = 64
+    n_pages = n // page
+    table = rng.permutation(n_pages).astype(np.int32)[None, :]
+    kp = rng.integers(0, 256, (n, 1, 144), dtype=np.uint8)
+    vp = rng.integers(0, 256, (n, 1, 144), dtype=np.uint8)
+    for pool in (kp, vp):  # finite binary16 scales, both signs, magnitudes 0.25 .. 4
+        d = (rng.uniform(0.25, 4.0, (n, 1, 8)) * rng.choice([-1.0, 1.0], (n, 1, 8))).astype(np.float16)
+        b = d.view(np.uint16)
+        for blk in range(8):
+            pool[:, :, 18 * blk] = (b[:, :, blk] & 0xFF).astype(np.uint8)
+            pool[:, :, 18 * blk + 1] = (b[:, :, blk] >> 8).astype(np.uint8)
+    off = np.array([0, n], np.int64)
+    q = np.zeros((1, 4, 256), np.float32)
+    ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, table, page, off, q, SM)
+    out, lse = _run(kp, vp, table, off, q, split_rows=split_rows)
+    _check(out, lse, ref_o, ref_l, f"long flat split {split_rows}")

@@ -234,6 +234,20 @@ def test_tq4_radius_invariant_and_rotation_identity():
     q = rng.standard_normal(512)
     wts = rng.uniform(0, 1, 64)
     assert oracle.tq4_identity_check(codes, radii, mask, q, wts) < 1e-12
+    # the check must see a mistake on either side: an unrotated query, a rotation
+    # without its signs, an un-rotation without its signs, an unrotated sum
+    for plant in (1, 2, 3, 4):
+        assert oracle.tq4_identity_check(codes, radii, mask, q, wts, plant=plant) > 1e-3, plant
+    # and the identity itself, outside the check: q . x_hat against (R q) . y with
+    # R = H D / sqrt(n) from scipy's Sylvester matrix and y read from the codebook
+    from scipy.linalg import hadamard
+    _, lv, _, _ = oracle.tq4_codebook()
+    d = np.where(np.unpackbits(mask, bitorder="little")[:512] == 1, -1.0, 1.0)
+    R = hadamard(512) * d[None, :] / np.sqrt(512.0)
+    idx = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], 512)
+    y = lv.astype(np.float64)[idx] * radii.astype(np.float64)[:, None] / np.sqrt(512.0)
+    np.testing.assert_allclose(xh @ q, y @ (R @ q), rtol=0, atol=1e-9 * np.max(np.abs(xh @ q)))
+    np.testing.assert_allclose(wts @ xh, R.T @ (wts @ y), rtol=0, atol=1e-9 * np.max(np.abs(wts @ xh)))
 
 
 def test_tq4_inert_rows_and_refusal():

@@ -41,6 +41,7 @@ extern "C" {
 #define KVQ_ERR_UNSUPPORTED 2 /* valid but not provided: non-power-of-two TQ4 width, ...  */
 #define KVQ_ERR_WORKSPACE 3   /* workspace smaller than kvq_decode_attn_workspace_bytes() */
 #define KVQ_ERR_LAUNCH 4      /* the HIP runtime reported an error at launch             */
+#define KVQ_ERR_TOO_LARGE 5   /* needs more than KVQ_NOALLOC_SCRATCH_BYTES of workspace   */
 
 /* ---- modes ---------------------------------------------------------------- */
 #define KVQ_QMODE_FP8 1      /* e4m3 codes [rows][dim] + fp32 scale per row           */
@@ -197,6 +198,25 @@ int64_t kvq_decode_attn_workspace_bytes(const kvq_attn_args* a);
  * aligned, contents need not be initialised; the call overwrites it.  Two
  * calls that share a workspace must be ordered (same stream). */
 int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, void* stream);
+
+/* ---- decode attention without allocation ----------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, kernels, results and errors as kvq_decode_attn,
+ * but the workspace is a static array inside the library, one per GPU, of
+ * KVQ_NOALLOC_SCRATCH_BYTES bytes, held until the process ends (each GPU the
+ * library runs on gets its own copy at its own address, looked up on the first
+ * call on that device).  The call allocates nothing.
+ *  - KVQ_ERR_TOO_LARGE when kvq_decode_attn_workspace_bytes(a) exceeds the
+ *    scratch (32 MiB covers, e.g., one 32768-row sequence or 400k rows over 33
+ *    sequences with 128 heads; the T-split partial states dominate).
+ *  - `stream` must belong to the current device.
+ *  - Every call on one GPU shares that GPU's scratch and leaves it holding the
+ *    last call's contents (nothing in it must start at zero).  Calls that may
+ *    overlap on one GPU (different streams, or threads without ordering) race
+ *    and give wrong results: order them on one stream. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int kvq_decode_attn_noalloc(const kvq_attn_args* a, void* stream);
 
 /* One stage of kvq_decode_attn; running stages 0..2 in order on one stream is
  * exactly kvq_decode_attn.  Running a stage gives profilers and timers one

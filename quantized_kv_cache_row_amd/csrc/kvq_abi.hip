@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 // Layouts the bindings mirror; a same-size reorder would otherwise go unnoticed.
@@ -90,6 +92,30 @@ int check_q4_attn(const kvq_q4_cache* c, const kvq_q4_attn_args* a) {
     return KVQ_OK;
 }
 
+// ---- static scratch of kvq_decode_attn_noalloc ----------------------------------
+// The workspace of the no-allocation entry point: one array per GPU the library
+// runs on, held until the process ends.  Its name is only a host-side handle;
+// kernels get its device address, looked up once per device with that device
+// current and kept below.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of this device's scratch array (nullptr if it cannot be had).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +129,9 @@ const char* kvq_status_string(int status) {
         case KVQ_ERR_UNSUPPORTED: return "unsupported (mode, width or size not provided by this library)";
         case KVQ_ERR_WORKSPACE: return "workspace smaller than kvq_decode_attn_workspace_bytes()";
         case KVQ_ERR_LAUNCH: return "HIP launch failed";
+        case KVQ_ERR_TOO_LARGE:
+            return "the call needs more workspace than the static scratch of the no-allocation entry point "
+                   "(KVQ_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -192,6 +221,16 @@ int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, v
     if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
     return launch_status(kvq::launch_decode_attn(*a, workspace, ws_bytes, as_stream(stream)));
+}
+
+int kvq_decode_attn_noalloc(const kvq_attn_args* a, void* stream) {
+    int rc = check_attn(a);
+    if (rc != KVQ_OK) return rc;
+    const int64_t need = kvq::attn_workspace_bytes(*a);
+    if (need > (int64_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_TOO_LARGE;
+    void* ws = scratch_for_current_device();
+    if (!ws) return KVQ_ERR_LAUNCH;
+    return launch_status(kvq::launch_decode_attn(*a, ws, need, as_stream(stream)));
 }
 
 int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, int64_t ws_bytes, void* stream) {

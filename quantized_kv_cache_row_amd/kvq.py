@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_ABI_VERSION = 1
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = 0, 1, 2, 3, 4
+KVQ_ERR_TOO_LARGE = 5
+KVQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 KVQ_QMODE_FP8, KVQ_QMODE_TQ4 = 1, 2
 KVQ_PREC_MFMA, KVQ_PREC_FP32 = 0, 1
 KVQ_Q4_NO_ROTATE = 1
@@ -79,6 +81,7 @@ def lib():
             "kvq_decode_attn_workspace_bytes": ([ctypes.POINTER(KvqAttnArgs)], i64),
             "kvq_decode_attn": ([ctypes.POINTER(KvqAttnArgs), vp, i64, vp], i32),
             "kvq_decode_attn_stage": ([ctypes.POINTER(KvqAttnArgs), i32, vp, i64, vp], i32),
+            "kvq_decode_attn_noalloc": ([ctypes.POINTER(KvqAttnArgs), vp], i32),
             "kvq_convert": ([i32, vp, i64, vp, vp], i32),
             "kvq_gather_rows": ([i32, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp], i32),
             "kvq_decode_attn_sparse_workspace_bytes": ([ctypes.POINTER(KvqAttnArgs)], i64),
@@ -101,7 +104,7 @@ def exported_symbols():
             "kvq_encode_tq4", "kvq_append_q4_0", "kvq_gather_q4_0", "kvq_decode_attn_workspace_bytes",
             "kvq_decode_attn", "kvq_decode_attn_stage", "kvq_gather_rows", "kvq_decode_attn_sparse_workspace_bytes",
             "kvq_decode_attn_sparse", "kvq_convert", "kvq_struct_layout", "kvq_decode_attn_q4_0_workspace_bytes",
-            "kvq_decode_attn_q4_0"]
+            "kvq_decode_attn_q4_0", "kvq_decode_attn_noalloc"]
 
 
 # ---- host-only entry points -----------------------------------------------------
@@ -273,6 +276,13 @@ def _cache_rows_cover(args):
     codes = args._keep[1]
     if codes is not None and codes.shape[0] < args.total_rows:
         raise ValueError(f"codes: {codes.shape[0]} rows, fewer than total_rows = {args.total_rows}")
+
+
+def kvq_decode_attn_noalloc(args, stream=None):
+    """kvq_decode_attn with the library's static per-GPU scratch as its workspace
+    (no allocation; calls on one GPU must be ordered)."""
+    _cache_rows_cover(args)
+    _check("kvq_decode_attn_noalloc", lib().kvq_decode_attn_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def kvq_decode_attn_stage(args, stage, workspace, stream=None):

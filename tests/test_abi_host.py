@@ -80,6 +80,13 @@ def test_refusals_without_launch():
     assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
     a.split_rows, a.qmode = 0, 2  # TQ4 without a sign mask
     assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_decode_attn_noalloc(ctypes.byref(a), None) == kvq.KVQ_ERR_INVALID_ARG
+    # the no-allocation entry point refuses work beyond its static scratch before any HIP call
+    a.qmode, a.total_rows, a.split_rows = 1, 1 << 22, 1024
+    assert L.kvq_decode_attn_workspace_bytes(ctypes.byref(a)) > kvq.KVQ_NOALLOC_SCRATCH_BYTES
+    assert L.kvq_decode_attn_noalloc(ctypes.byref(a), None) == kvq.KVQ_ERR_TOO_LARGE
+    assert "scratch" in kvq.kvq_status_string(kvq.KVQ_ERR_TOO_LARGE)
+    a.total_rows, a.split_rows = 32768, 0
     # q4_0
     c = kvq.KvqQ4Cache(256, 256, 256, 64, 1, 64, 8, 128)
     assert L.kvq_append_q4_0(ctypes.byref(c), 1, P(256), P(256), 1, P(256), P(256), 0, None) == \

@@ -45,14 +45,16 @@ constexpr int MF_TILE = 32;       // rows per wave tile
 constexpr int TQ4_HEADS = 64;    // TQ4 matrix-core path: heads per workgroup (4 waves x 16)
 constexpr int QPACK_U4 = 80;      // TQ4: uint4 per prepared query (fp16 latent 64, rope hi 8, rope lo 8)
 constexpr int QP_RH = 64, QP_RL = 72;
+constexpr int F8_HEADS = 32;      // fp8 matrix-core path: heads per workgroup (one 32x32 MFMA N block)
+constexpr int F8_TILE = 128;      // fp8 matrix-core path: rows per workgroup tile (32 per wave)
 constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators are rescaled
 
 struct Plan {
     int64_t* chunk_prefix;  // [n_seqs + 1]
     float* q_rot;           // fp32 path, TQ4: [n_seqs][H][512]
-    uint4* q_pack;          // matrix-core path, TQ4: [n_seqs][H padded to 64][QPACK_U4]
-    float* q_inv;           // matrix-core path, TQ4: [n_seqs][H padded to 64]
+    uint4* q_pack;          // matrix-core paths: [n_seqs][H padded][QPACK_U4] (fp8: in operand order per group)
+    float* q_inv;           // matrix-core paths: [n_seqs][H padded]
     float* part_m;          // [max_chunks][H]
     float* part_l;          // [max_chunks][H]
     float* part_o;          // [max_chunks][H][512]
@@ -78,13 +80,14 @@ int auto_split_rows(const kvq_attn_args& a) {
         if (split > (1 << 24)) split = 1 << 24;
         return (int)split;
     }
-    // Large splits keep the partial states small next to the KV bytes they
-    // summarize (a partial is 128 heads x 2 KB per split); about two
-    // workgroups per compute unit over all splits and head groups.
-    const int64_t groups = (a.n_heads + MF_HEADS - 1) / MF_HEADS;
-    int64_t split = (a.total_rows * groups + 511) / 512;
-    if (split < 1024) split = 1024;
-    split = (split + MF_WAVES * MF_TILE - 1) / (MF_WAVES * MF_TILE) * (MF_WAVES * MF_TILE);
+    // fp8: about one workgroup per compute unit over all splits and groups of
+    // 32 heads, whole 128-row tiles, at least two tiles per split; large splits
+    // keep the partial states (32 heads x 2 KB per split and group) below the
+    // KV bytes they summarize.
+    const int64_t groups = (a.n_heads + F8_HEADS - 1) / F8_HEADS;
+    int64_t split = (a.total_rows * groups + 255) / 256;
+    if (split < 2 * F8_TILE) split = 2 * F8_TILE;
+    split = (split + F8_TILE - 1) / F8_TILE * F8_TILE;
     if (split > (1 << 24)) split = 1 << 24;
     return (int)split;
 }
@@ -93,7 +96,7 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     Plan p{};
     p.split_rows = a.split_rows > 0 ? a.split_rows : auto_split_rows(a);
     const bool f32 = a.precision == KVQ_PREC_FP32;
-    p.heads_per_group = f32 ? F32_HEADS : (a.qmode == KVQ_QMODE_TQ4 ? TQ4_HEADS : MF_HEADS);
+    p.heads_per_group = f32 ? F32_HEADS : (a.qmode == KVQ_QMODE_TQ4 ? TQ4_HEADS : F8_HEADS);
     p.n_groups = (a.n_heads + p.heads_per_group - 1) / p.heads_per_group;
     p.heads_padded = p.n_groups * p.heads_per_group;
     // sum_s max(1, ceil(T_s / split)) over T_s summing to at most total_rows is at
@@ -113,14 +116,16 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     };
     p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
     if (f32 && a.qmode == KVQ_QMODE_TQ4) p.q_rot = (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
-    if (!f32 && a.qmode == KVQ_QMODE_TQ4) {
+    if (!f32) {  // matrix-core paths: the prepared query operands
         const int64_t rows_q = (int64_t)a.n_seqs * p.heads_padded;
         p.q_pack = (uint4*)take(sizeof(uint4) * rows_q * QPACK_U4);
         p.q_inv = (float*)take(sizeof(float) * rows_q);
     }
     p.part_m = (float*)take(sizeof(float) * p.max_chunks * a.n_heads);
     p.part_l = (float*)take(sizeof(float) * p.max_chunks * a.n_heads);
-    p.part_o = (float*)take(sizeof(float) * p.max_chunks * a.n_heads * DL);
+    // (fp8 matrix-core partials are stored per group of 32 heads, the last one padded)
+    const int64_t ph = (!f32 && a.qmode == KVQ_QMODE_FP8) ? p.heads_padded : a.n_heads;
+    p.part_o = (float*)take(sizeof(float) * p.max_chunks * ph * DL);
     if (bytes_out) *bytes_out = off;
     return p;
 }
@@ -436,33 +441,7 @@ __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
 }
 
 
-// fp8 split kernel (raw-tile variant).  Same work items and wave split as
-// k_attn_mfma, but every wave streams its rows' raw e4m3 codes into a
-// double-buffered LDS tile with global_load_lds (no register staging, the next
-// tile's load overlaps this tile's math).
-//
-// Tile layout, row-major with one 16-byte pad per row: chunk c (16 codes) of
-// tile row r sits in 16-byte slot 33 sigma(r) + c, where
-// sigma(r) = r ^ (bit3(r) << 2) ^ (bit4(r) << 3) is a bijection of 0..31.
-// The DMA fills 64 consecutive slots per instruction (17 per tile, rows stay
-// contiguous in global memory); each lane's source offset for instruction i
-// is computed once per wave.  Every LDS read below is then a per-lane base
-// plus a compile-time offset, and the 33-slot stride with sigma puts the rows
-// one read serves on distinct bank groups:
-//   score: lane (g, n) of row block rb reads tile row 8 (n / 4) + 4 rb + n % 4,
-//          chunks 4 j + g (16 codes -> two fp16 k-steps) at
-//          16 (33 sigma(row) + g) + 64 j; the accumulator row order then
-//          matches the transposed read;
-//   PV:    ds_read_b64_tr_b8: source lane (g, q) points at row 8 g + q / 2,
-//          byte 8 (q % 2) of chunk mb; lane (g, p) receives the 8 codes of
-//          rows 8 g .. 8 g + 7 in column 16 mb + p, converted to fp16 in
-//          registers -- k-slots (g, j) = row 8 g + j, as the probabilities.
-// The rope keys do not go through LDS: each lane loads its score rows' keys.
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
-constexpr int RAW_ROW = DL;                   // bytes per raw fp8 code row
-constexpr int RAW_SLOTS = 33;                 // 16-byte slots per padded tile row
-constexpr int RAW_DMA = 17;                   // DMA instructions per code tile (1056 slots, 64 per instruction)
-constexpr int RAW_TILE = RAW_DMA * 64 * 16;   // 17408 bytes
 
 __device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -507,10 +486,6 @@ __device__ __forceinline__ float max_xor16_xor32(float v) {
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ int tile_sigma(int r) { return r ^ (((r >> 3) & 1) << 2) ^ (((r >> 4) & 1) << 3); }
-__device__ __forceinline__ int tile_sigma_inv(int q) {
-    return q ^ (((q >> 4) & 1) << 3) ^ ((((q >> 3) ^ (q >> 4)) & 1) << 2);
 }
 
 // The split plan, in-kernel (matrix-core paths), run by one wave: it scans
@@ -581,420 +556,370 @@ __device__ __forceinline__ bool locate_chunk(const kvq_attn_args& a, const Plan&
     return true;
 }
 
+// fp8 query preparation: for every (sequence, head) the latent query scaled by
+// a power of two qs (max |q| qs in [256, 512)) and rounded to fp16, the rope
+// query times sm_scale log2(e) as bf16 hi + lo terms, and 1 / qs.  Stored per
+// (sequence, group of 32 heads) in the split kernel's operand order, so that a
+// wave's load of one operand register set is 1 KB contiguous: uint4
+// ((i * 2 + j) * 2 + h) * 32 + n holds head n's latent dims 32 i + 16 h + 8 j
+// .. + 7 (i < 16, j < 2, h < 2); uint4 2048 + (((i * 2 + j) * 2 + t) * 2 + h) *
+// 32 + n its rope dims 32 i + 16 h + 8 j .. + 7, term t (0: hi, 1: lo; i < 2).
+// One wave per (sequence, head); lane l converts dims 8 l .. 8 l + 7.
+__global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + head
+    if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
+    const int s = (int)(row / p.heads_padded), hd = (int)(row % p.heads_padded);
+    const bool hv = hd < a.n_heads;
+    const int64_t qrow = (int64_t)s * a.n_heads + min(hd, a.n_heads - 1);  // absent heads: a zero query
+    const float4 x0 = *reinterpret_cast<const float4*>(a.q_lat + qrow * DL + 8 * lane);
+    const float4 x1 = *reinterpret_cast<const float4*>(a.q_lat + qrow * DL + 8 * lane + 4);
+    const float4 y0 = *reinterpret_cast<const float4*>(a.q_rope + qrow * DR + 8 * (lane & 7));
+    const float4 y1 = *reinterpret_cast<const float4*>(a.q_rope + qrow * DR + 8 * (lane & 7) + 4);
+    float qmax = fmaxf(fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))),
+                       fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
+    qmax = wave_max(qmax);
+    const float qs = hv ? pow2_scale_for(qmax, 8) : 0.0f;
+    uint4* dst = p.q_pack + ((int64_t)s * p.heads_padded + (hd & ~(F8_HEADS - 1))) * QPACK_U4;
+    const int n = hd & (F8_HEADS - 1);
+    const int i = lane >> 2, h = (lane >> 1) & 1, j = lane & 1;
+    dst[((i * 2 + j) * 2 + h) * F8_HEADS + n] =
+        make_uint4(pack_f16x2(x0.x * qs, x0.y * qs), pack_f16x2(x0.z * qs, x0.w * qs),
+                   pack_f16x2(x1.x * qs, x1.y * qs), pack_f16x2(x1.z * qs, x1.w * qs));
+    if (lane < 8) {
+        const float cr = hv ? a.sm_scale * LOG2E : 0.0f;
+        const float f[8] = {y0.x * cr, y0.y * cr, y0.z * cr, y0.w * cr, y1.x * cr, y1.y * cr, y1.z * cr, y1.w * cr};
+        float b[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) b[e] = u2f(f32_to_bf16_rne(f[e]) << 16);
+        dst[2048 + (((i * 2 + j) * 2 + 0) * 2 + h) * F8_HEADS + n] =
+            make_uint4(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]), pack_bf16x2(b[6], b[7]));
+        dst[2048 + (((i * 2 + j) * 2 + 1) * 2 + h) * F8_HEADS + n] =
+            make_uint4(pack_bf16x2(f[0] - b[0], f[1] - b[1]), pack_bf16x2(f[2] - b[2], f[3] - b[3]),
+                       pack_bf16x2(f[4] - b[4], f[5] - b[5]), pack_bf16x2(f[6] - b[6], f[7] - b[7]));
+    }
+    if (lane == 0) p.q_inv[row] = hv ? 1.0f / qs : 0.0f;  // exact
+}
+
+// fp8 split kernel.  Work item = (T-chunk, group of 32 heads); the 32 heads
+// are the N dimension of v_mfma_f32_32x32x16_f16, so every e4m3 code converted
+// to fp16 serves 32 heads.  The chunk is walked in tiles of 128 rows; within a
+// tile the four waves split the work two ways:
+//   score  wave w takes rows 32 w .. 32 w + 31 of the tile and all 32 heads:
+//          S (32 rows x 32 heads) = codes (rows x k) . q~ (k x heads) on the
+//          f16 matrix cores (latent, fp16 codes and query) and on the bf16 ones
+//          (rope, bf16 keys and a two-term bf16 query);
+//   PV     wave w takes output dims 128 w .. 128 w + 127 over all 128 rows:
+//          O^T (dims x heads) += V^T (dims x rows) . P^T (rows x heads), with
+//          V^T read transposed from the raw tile (ds_read_b64_tr_b8) and P^T
+//          from LDS, where the score waves leave it as fp16 p * rho * rsc.
+// So no wave's output overlaps another's, and nothing is merged across waves
+// at the end.  Each wave streams its score rows' raw codes into the tile by
+// LDS DMA (double-buffered); rope keys go straight to registers one tile ahead.
+//
+// Lane layouts (checked on the device): for v_mfma_f32_32x32x16, lane l holds
+// A[m = l % 32][k = 8 (l / 32) + e] and B[k = 8 (l / 32) + e][n = l % 32]
+// (e = 0..7), and D[m][n] sits in lane n + 32 ((m / 4) % 2), register
+// 4 (m / 8) + m % 4.  The contraction index is free to relabel: in k-step j of
+// pair i = j / 2, lane half h holds the latent dims 32 i + 16 h + 8 (j % 2) + e,
+// the 16 contiguous code bytes of one 16-byte chunk.
+//
+// Tile layout: wave w's 32 rows at w * 16 KB of the buffer, row r at 512 r,
+// 16-byte chunk c stored at chunk c ^ (r % 16), which puts the rows any read
+// below serves on distinct banks (checked on the CPU).
+//
+// Softmax: one reference per head for the whole workgroup (the first tile's
+// maximum, agreed through LDS at a barrier every tile); probabilities are
+// 2^(s - m) <= 2^8, times rho * rsc (rsc a power of two with max rho * rsc < 1
+// over the chunk), rounded to fp16.  A tile whose maximum exceeds the reference
+// by more than 2^8 raises it and the workgroup starts its rows again: the
+// accumulators are never rescaled inside the loop.
+constexpr int F8_WROWS = 32;                    // score rows per wave
+constexpr int F8_WBYTES = F8_WROWS * DL;        // one wave's rows in a code buffer: 16 KB
+constexpr int F8_BUF = MF_WAVES * F8_WBYTES;    // a code buffer: 64 KB
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct F8Smem {
+    uint8_t code[2][F8_BUF];               // raw e4m3 rows
+    uint4 p[8][2][F8_HEADS];               // P^T per k-step of 16 rows: [step][lane half][head] x 8 fp16
+    float rho[2][MF_WAVES][64];            // each wave's row scales (lanes 32..63 hold copies)
+    float xch[MF_WAVES][F8_HEADS];         // per-wave values per head: tile maxima, then sums
+    float red[MF_WAVES];
+};
+static_assert(sizeof(F8Smem) <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ f32x16_t mfma32_f16(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32_bf16(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
-    __shared__ __align__(16) uint8_t raw[MF_WAVES][2][RAW_TILE];     // codes, double-buffered
-    __shared__ __align__(16) float rho_s[MF_WAVES][2][64];             // row scales
-    __shared__ float ml_s[MF_WAVES][3][MF_HEADS];
-    __shared__ int64_t plan_s[3];  // this chunk's first row, end row, sequence (-1: none)
+    __shared__ __align__(16) F8Smem sm;
+    __shared__ int64_t plan_s[3];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int g = lane >> 4, n = lane & 15;
-    // workgroups are dealt round-robin to the XCDs: chunk c goes to XCD c % 8 and
-    // its head groups are consecutive there, so they share that XCD's L2
+    const int h = lane >> 5, n = lane & 31;  // lane half, head (and score row) within the group
     const int64_t local = blockIdx.x / N_XCD;
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
     if (c >= p.max_chunks) return;
-    const int head = hg * MF_HEADS + n;
     int64_t r0, r1;
     int sq;
     if (!locate_chunk(a, p, c, plan_s, wave, lane, r0, r1, sq)) return;  // workgroup-uniform
-    const int64_t quarter = ((r1 - r0 + MF_WAVES - 1) / MF_WAVES + MF_TILE - 1) / MF_TILE * MF_TILE;
-    const int64_t w0 = min(r1, r0 + wave * quarter), w1 = min(r1, w0 + quarter);
+    const int ntiles = (int)((r1 - r0 + F8_TILE - 1) / F8_TILE);
+    const int head = hg * F8_HEADS + n;
 
-    // DMA loaders (global -> LDS, no registers).  Lane l of instruction i fills
-    // slot 64 i + l: row sigma^-1(slot / 33), chunk slot % 33 (the pad slot and
-    // the slots past the tile re-read chunk 0 of that row, or of row 0).  The
-    // offsets are fixed per lane.  Rows past the wave's end are loaded too (and
-    // masked later) while they lie inside the arrays; past the arrays' end a
-    // lane loads their last 16 bytes instead.  Instruction k of a tile
-    // (0..17: codes, scales) is issued on its own, so the issue can be spread
-    // over the score steps.  The rope keys go straight to registers (load_rope).
-    uint32_t voff_c[RAW_DMA];
-#pragma unroll
-    for (int i = 0; i < RAW_DMA; i++) {
-        const int q = 64 * i + lane;
-        const int k = q / RAW_SLOTS, ch = q % RAW_SLOTS;
-        const int r = k < MF_TILE ? tile_sigma_inv(k) : 0;
-        voff_c[i] = (uint32_t)(r * RAW_ROW + 16 * (ch < 32 && k < MF_TILE ? ch : 0));
-    }
-    const uint32_t lds_codes = lds_offset(&raw[wave][0][0]);
-    const uint32_t lds_rho = lds_offset(&rho_s[wave][0][0]);
-    constexpr int NDMA = RAW_DMA + 1;
-    auto dma_one = [&](int k, int64_t t0, int buf, int lim) __attribute__((always_inline)) {
-        // lim: rows of the tile inside the arrays (offsets are clamped to them)
-        if (k < RAW_DMA) {
-            dma_lds_b128(a.codes + t0 * RAW_ROW, min(voff_c[k], (uint32_t)lim * RAW_ROW - 16u),
-                         __builtin_amdgcn_readfirstlane(lds_codes + (uint32_t)buf * RAW_TILE + 1024u * k));
+    // ---- loaders.  The DMA of a tile brings this wave's 32 score rows: instruction
+    // k (0..15) fills LDS chunks 64 k .. 64 k + 63 of the wave's 16 KB, lane l the
+    // chunk of row 2 k + l / 32 stored at l % 32, i.e. global chunk (l % 32) ^ (row % 16);
+    // instruction 16 brings the 32 row scales.  Rows past the arrays re-read the last
+    // row (offsets clamped); rows past the chunk are loaded and masked later.
+    const uint32_t dma_c = (uint32_t)((lane & 31) ^ h);  // (l % 32) ^ (row % 16) = dma_c ^ (2 k % 16)
+    const uint32_t lds_code0 = lds_offset(&sm.code[0][0]) + (uint32_t)wave * F8_WBYTES;
+    const uint32_t lds_rho0 = lds_offset(&sm.rho[0][0][0]) + (uint32_t)wave * 256u;
+    auto dma_one = [&](int k, int64_t tw, int buf) __attribute__((always_inline)) {
+        // tw: first row of this wave's block; the base row and the offsets stay inside the arrays
+        const int64_t b = min(tw, a.total_rows - 1);
+        const uint32_t lim = (uint32_t)(a.total_rows - b);  // rows from b to the end, >= 1
+        if (k < 16) {
+            const uint32_t voff = (uint32_t)(2 * k + h) * 512u + ((dma_c ^ (uint32_t)((2 * k) & 15)) << 4);
+            dma_lds_b128(a.codes + b * DL, min(voff, lim * 512u - 16u),
+                         __builtin_amdgcn_readfirstlane(lds_code0 + (uint32_t)buf * F8_BUF + 1024u * k));
         } else {
-            const uint32_t voff_s = (uint32_t)((lane & 31) < lim ? (lane & 31) : 0) * 4u;
-            dma_lds_b32(a.row_scale + t0, voff_s, __builtin_amdgcn_readfirstlane(lds_rho + 256u * buf));
+            dma_lds_b32(a.row_scale + b, 4u * min((uint32_t)(lane & 31), lim - 1u),
+                        __builtin_amdgcn_readfirstlane(lds_rho0 + (uint32_t)buf * (MF_WAVES * 256u)));
         }
     };
-    auto load_tile = [&](int64_t t0, int buf) __attribute__((always_inline)) {
-        const int lim = (int)min((int64_t)MF_TILE, a.total_rows - t0);
+    // rope keys of this wave's score rows: lane (h, n) takes row n, dims 32 i + 16 h .. + 15 (i = 0, 1)
+    uint4 kr[2][2];
+    auto load_rope = [&](int64_t tw) __attribute__((always_inline)) {
+        const int64_t row = min(tw + n, a.total_rows - 1);
 #pragma unroll
-        for (int k = 0; k < NDMA; k++) dma_one(k, t0, buf, lim);
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                kr[i][j] = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 32 * i + 16 * h + 8 * j);
     };
-    // The rope keys of a tile, straight into registers one tile ahead: lane (g, n)
-    // takes the score rows 8 (n / 4) + 4 rb + n % 4 (rb = 0, 1), dims 32 k + 8 g
-    // .. + 7 (16-byte aligned), clamped to the arrays; unconditional loads.
-    uint4 krn[2][2];
-    auto load_rope = [&](int64_t t0) __attribute__((always_inline)) {
+    if (ntiles > 0) {  // workgroup-uniform
+        const int64_t tw = r0 + F8_WROWS * wave;
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const int64_t row = min(t0 + 8 * (n >> 2) + 4 * rb + (n & 3), a.total_rows - 1);
-#pragma unroll
-            for (int k = 0; k < 2; k++)
-                krn[rb][k] = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 32 * k + 8 * g);
-        }
-    };
+        for (int k = 0; k < 17; k++) dma_one(k, tw, 0);
+        load_rope(tw);
+    }
 
-    // ---- query operands, in-kernel: lane (g, n) holds head n's latent dims
-    // 64 j + 16 g + 8 hh + e as k-step 2 j + hh (e = 0..7), scaled by a power of
-    // two qs (max |q| * qs in [256, 512)) and rounded to fp16; the rope dims
-    // 32 ks' + 8 g + e, times sm_scale * log2(e), as a bf16 hi + lo pair.
-    uint4 qh[16], rh[2], rl[2];
-    float qinv;
-    // the largest |row scale| of this wave's rows sets the probabilities' power-of-two
-    // scale rsc (loads clamped to the wave's range, issued with the query's)
-    float rsc;
+    // ---- query operands, prepared once per (sequence, head) by k_qprep_fp8 in this
+    // kernel's operand order (40 KB per group of 32 heads).  Every wave needs all of
+    // them, so they are brought into the second code buffer once per workgroup by
+    // LDS DMA (each wave 10 of the 40 KB-sized instructions) and read from there.
     {
-        // The group's 16 query heads are loaded once per workgroup: wave w brings
-        // heads 4 w .. 4 w + 3 (fp32) and the first 256 of its rows' scales by DMA
-        // into its second code buffer, which is free until the first tile's
-        // next-tile DMA (after the barrier at the end of this block).  Head k's
-        // latent row sits at QS_ROW * (k % 4) + 64 * (k / 4) of raw[k / 4][1] (the
-        // 16-byte row pads and the 64-byte skew put the 16 heads one read serves on
-        // distinct bank groups), its rope row at QS_ROPE + QS_RROW * (k % 4) +
-        // 64 * (k / 4), the scales at QS_RS.  The first tile's DMA goes out right
-        // after, and the wait below covers only the staging DMAs, so the three
-        // latencies overlap.
-        constexpr int QS_ROW = DL * 4 + 16, QS_ROPE = 8448, QS_RROW = DR * 4, QS_RS = 9728;
-        static_assert(QS_ROPE >= 3 * QS_ROW + 192 + DL * 4 && QS_ROPE % 256 == 0 &&
-                          QS_RS >= QS_ROPE + 192 + 4 * QS_RROW && QS_RS + 1024 <= RAW_TILE,
-                      "query staging fits a code buffer");
-        const bool hv = head < a.n_heads;
-        uint8_t* const qst = &raw[wave][1][0];
-        const uint32_t lqs = __builtin_amdgcn_readfirstlane(lds_offset(qst));
-        {
-            const int hq = hg * MF_HEADS + 4 * wave;  // first head of this wave's quarter (clamped below)
-            const float* qb = a.q_lat + (int64_t)sq * a.n_heads * DL;
+        const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + hg * F8_HEADS) * QPACK_U4;
+        const uint32_t lq = __builtin_amdgcn_readfirstlane(lds_offset(&sm.code[1][0]));
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int hi = min(hq + (i >> 1), a.n_heads - 1);
-                dma_lds_b128(qb + (int64_t)hi * DL, 1024u * (i & 1) + 16u * lane,
-                             lqs + QS_ROW * (i >> 1) + 64 * wave + 1024 * (i & 1));
-            }
-            const int hr = min(hq + (lane >> 4), a.n_heads - 1);
-            dma_lds_b128(a.q_rope + (int64_t)sq * a.n_heads * DR, (uint32_t)hr * (DR * 4) + 16u * (lane & 15),
-                         lqs + QS_ROPE + 64 * wave);
-            // the row scales: clamped to the wave's rows; with no rows the loads read
-            // the query instead (always present) and are discarded
-            const float* rsp = a.total_rows > 0 ? a.row_scale : a.q_lat;
-            const int64_t rb = w0 < w1 ? w0 : 0;
-            const int rl = w0 < w1 ? (int)min((int64_t)255, w1 - 1 - w0) : 0;
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                dma_lds_b32(rsp + rb, 4u * (uint32_t)min(64 * u + lane, rl), lqs + QS_RS + 256 * u);
+        for (int k = 0; k < 10; k++) {
+            const int blk = 10 * wave + k;  // 1 KB block of the 40 KB pack
+            dma_lds_b128(qp + 64 * blk, 16u * lane, lq + 1024u * blk);
         }
-        if (w0 < w1) {  // wave-uniform
-            load_tile(w0, 0);
-            load_rope(w0);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | 6 | (16 << 10));  // vmcnt(22): the staging DMAs have landed
-        } else {
-            vm_wait_all();
-        }
-        static_assert(NDMA == 18, "the wait above counts the first tile's 18 DMAs and 4 rope loads");
-        wg_barrier_lds();  // every quarter is in LDS (the first tile's DMA stays in flight)
-        float rmw = 0.0f;
-        if (w0 < w1) {  // wave-uniform
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-                rmw = fmaxf(rmw, fabsf(*reinterpret_cast<const float*>(qst + QS_RS + 256 * u + 4 * lane)));
-            // the rest of a quarter longer than 256 rows
-            for (int64_t t = w0 + 256 + lane; t < w1; t += 64) rmw = fmaxf(rmw, fabsf(a.row_scale[t]));
-        }
-        rsc = pow2_scale_for(wave_max(rmw), -1);  // rho * rsc < 1 for every row; 1 if all are 0
-        // lane (g, n): head n's dims 64 j + 16 g + 8 hh + e and rope dims 32 k + 8 g + e
-        const uint8_t* const hrow = &raw[n >> 2][1][0] + QS_ROW * (n & 3) + 64 * (n >> 2);
-        const uint8_t* const rrow = &raw[n >> 2][1][0] + QS_ROPE + QS_RROW * (n & 3) + 64 * (n >> 2);
-        float4 v[32], w[4];
-#pragma unroll
-        for (int ks = 0; ks < 16; ks++) {
-            const uint8_t* src = hrow + 4 * (64 * (ks >> 1) + 16 * g + 8 * (ks & 1));
-            v[2 * ks] = *reinterpret_cast<const float4*>(src);
-            v[2 * ks + 1] = *reinterpret_cast<const float4*>(src + 16);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const uint8_t* src = rrow + 4 * (32 * k + 8 * g);
-            w[2 * k] = *reinterpret_cast<const float4*>(src);
-            w[2 * k + 1] = *reinterpret_cast<const float4*>(src + 16);
-        }
-        float qmax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 32; k++)
-            qmax = fmaxf(qmax, fmaxf(fmaxf(fabsf(v[k].x), fabsf(v[k].y)), fmaxf(fabsf(v[k].z), fabsf(v[k].w))));
-        qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
-        qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
-        const float qs = hv ? pow2_scale_for(qmax, 8) : 0.0f;  // absent heads: a zero query
-        qinv = hv ? 1.0f / qs : 0.0f;                           // exact
-#pragma unroll
-        for (int ks = 0; ks < 16; ks++) {
-            const float4 x = v[2 * ks], y = v[2 * ks + 1];
-            qh[ks] = make_uint4(pack_f16x2(x.x * qs, x.y * qs), pack_f16x2(x.z * qs, x.w * qs),
-                                pack_f16x2(y.x * qs, y.y * qs), pack_f16x2(y.z * qs, y.w * qs));
-        }
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const float c2r = hv ? a.sm_scale * LOG2E : 0.0f;  // rope scores come out in log2 units
-            const float f[8] = {w[2 * k].x * c2r, w[2 * k].y * c2r, w[2 * k].z * c2r, w[2 * k].w * c2r,
-                                w[2 * k + 1].x * c2r, w[2 * k + 1].y * c2r, w[2 * k + 1].z * c2r,
-                                w[2 * k + 1].w * c2r};
-            float b[8];
-#pragma unroll
-            for (int e = 0; e < 8; e++) b[e] = u2f(f32_to_bf16_rne(f[e]) << 16);
-            rh[k] = make_uint4(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]), pack_bf16x2(b[4], b[5]),
-                               pack_bf16x2(b[6], b[7]));
-            rl[k] = make_uint4(pack_bf16x2(f[0] - b[0], f[1] - b[1]), pack_bf16x2(f[2] - b[2], f[3] - b[3]),
-                               pack_bf16x2(f[4] - b[4], f[5] - b[5]), pack_bf16x2(f[6] - b[6], f[7] - b[7]));
-        }
-        wg_barrier_lds();  // every wave has read the staged query before the second buffers refill
     }
-    auto tile_row = [](int rb, int nn) { return 8 * (nn >> 2) + 4 * rb + (nn & 3); };
-    // per-lane LDS read offsets (bytes within a tile)
-    const uint32_t rd_a = 16u * (RAW_SLOTS * tile_sigma(tile_row(0, n)) + g);   // score, row block 0
-    const uint32_t rd_b = 16u * (RAW_SLOTS * tile_sigma(tile_row(1, n)) + g);   // score, row block 1
-    const uint32_t rd_t = 16u * RAW_SLOTS * tile_sigma(8 * g + (n >> 1)) + 8u * (n & 1);  // PV transposed reads
+    const float qinv = p.q_inv[(int64_t)sq * p.heads_padded + head];
+    // ---- rsc from the chunk's largest row scale (four loads in flight per thread)
+    float rm = 0.0f;
+    for (int64_t t = r0 + tid; t < r1; t += 4 * MF_WAVES * 64) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(t + u * MF_WAVES * 64, r1 - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; u++) rm = fmaxf(rm, fabsf(x[u]));
+    }
+    rm = wave_max(rm);
+    if (lane == 0) sm.red[wave] = rm;
 
+    vm_wait_all();     // this wave's share of the pack (and the loads before it) has landed
+    wg_barrier_lds();  // every wave's share, and the row-scale maxima, are visible
+    uint4 qh[16][2], rh[2][2], rl[2][2];
+    {
+        const uint4* q4 = reinterpret_cast<const uint4*>(&sm.code[1][0]) + lane;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) qh[i][j] = q4[(i * 2 + j) * 64];
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                rh[i][j] = q4[2048 + ((i * 2 + j) * 2 + 0) * 64];
+                rl[i][j] = q4[2048 + ((i * 2 + j) * 2 + 1) * 64];
+            }
+    }
     const float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
+    const float rsc = pow2_scale_for(fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3])), -1);
 
-    // Softmax with a fixed reference per wave and head: p = 2^(s - m_run), with
-    // m_run the first tile's maximum, and probabilities enter the matrix cores
-    // as fp16 p * rho * rsc (rho * rsc < 1 for all of the wave's rows).  A later
-    // tile may exceed the reference by 2^8, so p * rho * rsc <= 2^8.  A tile
-    // beyond that raises the reference and the wave starts its rows again: the
-    // accumulators are never rescaled inside the loop (they stay in the matrix
-    // cores' registers), and for all but adversarial score sequences the first
-    // pass is the only one.
-    f32x4_t acc_o[32];
-    float m_run = -INFINITY, l_part = 0.0f;
-    bool restarted = false;
+    // ---- per-lane LDS addresses
+    // score: row n of this wave's block, global chunk 2 i + h stored at (2 i + h) ^ (n % 16)
+    const uint32_t sc_row = (uint32_t)wave * F8_WBYTES + (uint32_t)n * 512u;
+    const uint32_t sc_x = (uint32_t)(n & 15);
+    // PV: lane l in 16-lane group (h, mh), q = l % 16: row R = 8 (e / 4) + 4 h + e % 4 of
+    // a 16-row k-step (e = q / 2), bytes 8 (q % 2) of global chunk 8 w + 2 b + mh
+    const int q16 = lane & 15, e8 = q16 >> 1, mh = (lane >> 4) & 1;
+    const uint32_t pv_r = (uint32_t)(8 * (e8 >> 2) + 4 * h + (e8 & 3));
+    uint32_t pv_addr[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+        pv_addr[b] = pv_r * 512u + (((uint32_t)(8 * wave + 2 * b + mh) ^ pv_r) << 4) + 8u * (uint32_t)(q16 & 1);
+
+    f32x16_t acc_o[4];
+    float m_ref = -INFINITY;  // per head (lane n), identical in every wave
+    float l_part = 0.0f;
     for (;;) {
 #pragma unroll
-    for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < 4; b++) acc_o[b] = f32x16_t{};
     l_part = 0.0f;
-    int buf = 0;
     bool again = false;
-    if (restarted && w0 < w1) {
-        load_tile(w0, 0);
-        load_rope(w0);
-    }
-    restarted = true;
-    for (int64_t t0 = w0; t0 < w1; t0 += MF_TILE) {
-        const int nt = (int)min((int64_t)MF_TILE, w1 - t0);
-        vm_wait_all();  // this tile's codes and scales are in LDS, its rope keys in registers
-        const bool more = t0 + MF_TILE < w1;
-        uint4 kr[2][2];
+    for (int t = 0; t < ntiles; t++) {
+        const int buf = t & 1;
+        const int64_t tw = r0 + (int64_t)F8_TILE * t + F8_WROWS * wave;  // this wave's first score row
+        vm_wait_all();  // this wave's rows, row scales and rope keys of the tile have landed
+        // ---- scores: rope first (its keys are then free for the next tile's), latent on two chains
+        f32x16_t s_r = f32x16_t{}, s_a = f32x16_t{}, s_b = f32x16_t{};
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int k = 0; k < 2; k++) kr[rb][k] = krn[rb][k];
-        const float4 rho0 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g]);
-        const float4 rho1 = *reinterpret_cast<const float4*>(&rho_s[wave][buf][8 * g + 4]);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): those reads are done before the buffers refill
-        // the next tile's DMA, three instructions per score step (after the last
-        // tile: this tile again, into the free buffer)
-        const int64_t tn = more ? t0 + MF_TILE : t0;
-        // after the last tile the reload only has to be harmless: one row, from the cache
-        const int limn = more ? (int)min((int64_t)MF_TILE, a.total_rows - tn) : 1;
-        load_rope(tn);  // the next tile's rope keys (after the last tile: this tile's again)
-        const uint8_t* tb = raw[wave][buf];
-        // ---- scores: both row blocks together, the reads one k-chunk ahead
-        const uint8_t* pa = tb + rd_a;
-        const uint8_t* pbp = tb + rd_b;
-        auto chunk = [&](const uint8_t* base, int j) { return *reinterpret_cast<const uint4*>(base + 64 * j); };
-        f32x4_t sl[2], sr[2];
-        sl[0] = sl[1] = sr[0] = sr[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        // the reads run two k-chunks ahead and the conversions one, so a step's
-        // matrix-core work and the next step's conversions are independent
-        uint4 ca = chunk(pa, 0), cbv = chunk(pbp, 0);
-        uint4 na = chunk(pa, 1), nb = chunk(pbp, 1);
-        uint4 a0 = e4m3x8_to_f16x8(ca.x, ca.y), a1 = e4m3x8_to_f16x8(ca.z, ca.w);
-        uint4 b0 = e4m3x8_to_f16x8(cbv.x, cbv.y), b1 = e4m3x8_to_f16x8(cbv.z, cbv.w);
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint4 ua0 = a0, ua1 = a1, ub0 = b0, ub1 = b1;
-            if (j < 7) {
-                ca = na;
-                cbv = nb;
-                if (j < 6) {
-                    na = chunk(pa, j + 2);
-                    nb = chunk(pbp, j + 2);
-                }
+            for (int j = 0; j < 2; j++) {
+                s_r = mfma32_bf16(kr[i][j], rh[i][j], s_r);
+                s_r = mfma32_bf16(kr[i][j], rl[i][j], s_r);
             }
+        const bool more = t + 1 < ntiles;  // workgroup-uniform
+        if (more) load_rope(tw + F8_TILE);
+        const uint8_t* cw = &sm.code[buf][0] + sc_row;
+        auto chunk = [&](int i) {
+            return *reinterpret_cast<const uint4*>(cw + ((((uint32_t)(2 * i + h)) ^ sc_x) << 4));
+        };
+        uint4 nx = chunk(0), nx2 = chunk(1);
 #pragma unroll
-            for (int k = 3 * j; k < 3 * j + 3; k++)
-                if (k < NDMA) dma_one(k, tn, buf ^ 1, limn);
-            __builtin_amdgcn_sched_barrier(0);  // the look-ahead reads issue before this chunk's math
-            if (j < 7) {
-                a0 = e4m3x8_to_f16x8(ca.x, ca.y);
-                a1 = e4m3x8_to_f16x8(ca.z, ca.w);
-                b0 = e4m3x8_to_f16x8(cbv.x, cbv.y);
-                b1 = e4m3x8_to_f16x8(cbv.z, cbv.w);
-            }
-            sl[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ua0), as_f16x8(qh[2 * j]), sl[0], 0, 0, 0);
-            sl[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ub0), as_f16x8(qh[2 * j]), sl[1], 0, 0, 0);
-            sl[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ua1), as_f16x8(qh[2 * j + 1]), sl[0], 0, 0, 0);
-            sl[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ub1), as_f16x8(qh[2 * j + 1]), sl[1], 0, 0, 0);
+        for (int i = 0; i < 16; i++) {
+            const uint4 cur = nx;
+            nx = nx2;
+            if (i < 14) nx2 = chunk(i + 2);
+            __builtin_amdgcn_sched_barrier(0);  // the look-ahead read issues before this chunk's math
+            const uint4 a0 = make_uint4(e4m3x2_to_f16x2<false>(cur.x), e4m3x2_to_f16x2<true>(cur.x),
+                                        e4m3x2_to_f16x2<false>(cur.y), e4m3x2_to_f16x2<true>(cur.y));
+            const uint4 a1 = make_uint4(e4m3x2_to_f16x2<false>(cur.z), e4m3x2_to_f16x2<true>(cur.z),
+                                        e4m3x2_to_f16x2<false>(cur.w), e4m3x2_to_f16x2<true>(cur.w));
+            f32x16_t& s = (i & 1) ? s_b : s_a;
+            s = mfma32_f16(a0, qh[i][0], s);
+            s = mfma32_f16(a1, qh[i][1], s);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // ---- softmax: lane (h, n) holds rows 8 (r / 4) + 4 h + r % 4 of head n
+        const int nvw = (int)min((int64_t)F8_WROWS, r1 - tw);  // valid rows of this wave's block (may be <= 0)
+        float sc[16], rr[16];
+        float tmax = -INFINITY;
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-            for (int k = 0; k < 2; k++) {
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
-                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[rb][k]), as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
-            }
-        // the first PV operands are read now: their latency hides behind the softmax
-        const uint8_t* trbase = tb + rd_t;
-        auto trd = [&](int mb) __attribute__((always_inline)) {
-            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(trbase + 16 * mb));
-        };
-        i32x2_t nv[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) nv[i] = trd(i);
-        // lane (g, n): accumulator register r of block rb = tile row 8 g + 4 rb + r
-        const bool full = nt == MF_TILE;  // wave-uniform
-        float sc[2][4], rr[2][4];
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const float4 rq = rb ? rho1 : rho0;
+        for (int j = 0; j < 4; j++) {
+            const float4 rq = *reinterpret_cast<const float4*>(&sm.rho[buf][wave][8 * j + 4 * h]);
             const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const bool ok = full || 8 * g + 4 * rb + r < nt;
-                rr[rb][r] = ok ? rv[r] : 0.0f;
-                sc[rb][r] = ok ? fmaf(rv[r] * k1, sl[rb][r], sr[rb][r]) : -INFINITY;
+            for (int u = 0; u < 4; u++) {
+                const int r = 4 * j + u;
+                const bool ok = 8 * j + 4 * h + u < nvw;
+                rr[r] = ok ? rv[u] : 0.0f;
+                sc[r] = ok ? fmaf(rv[u] * k1, s_a[r] + s_b[r], s_r[r]) : -INFINITY;
+                tmax = fmaxf(tmax, sc[r]);
             }
         }
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                           fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        tmax = max_xor16_xor32(tmax);
-        // the first column group's PV operands are converted now (independent of
-        // the softmax, so they fill its latency), and the second group's reads issued
-        uint4 pv0[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) pv0[i] = e4m3x8_to_f16x8((uint32_t)nv[i][0], (uint32_t)nv[i][1]);
-#pragma unroll
-        for (int i = 0; i < 8; i++) nv[i] = trd(8 + i);
-        if (m_run == -INFINITY) m_run = tmax;  // first tile: every row valid
-        const bool over = tmax > m_run + LAZY_LOG2;
-        if (__any(over)) {
-            // raise the reference past this tile and start the rows again
-            m_run = fmaxf(m_run, tmax);
+        tmax = fmaxf(tmax, xor_lane<32>(tmax, lane));
+        if (h == 0) sm.xch[wave][n] = tmax;
+        wg_barrier_lds();  // B1: every wave's tile maxima
+        const float mt = fmaxf(fmaxf(sm.xch[0][n], sm.xch[1][n]), fmaxf(sm.xch[2][n], sm.xch[3][n]));
+        m_ref = m_ref == -INFINITY ? mt : m_ref;  // first tile: the workgroup's maximum (finite)
+        if (__any(mt > m_ref + LAZY_LOG2)) {  // workgroup-uniform: every wave sees the same maxima
+            m_ref = fmaxf(m_ref, mt);
             again = true;
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): no LDS read pending when the buffers refill
             break;
         }
         float psum = 0.0f;
-        uint32_t pb[4];
+        uint32_t pk[8];
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            float pw[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                // v_exp_f32: masked rows (score -inf) give 0; m_run is finite after the first tile
-                const float pv = __builtin_amdgcn_exp2f(sc[rb][r] - m_run);
-                psum += pv;
-                pw[r] = pv * (rr[rb][r] * rsc);
-            }
-            pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
-            pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(sc[r] - m_ref), p1 = __builtin_amdgcn_exp2f(sc[r + 1] - m_ref);
+            psum += p0 + p1;
+            pk[r / 2] = pack_f16x2(p0 * (rr[r] * rsc), p1 * (rr[r + 1] * rsc));
         }
         l_part += psum;
-        const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
-        // ---- PV: groups of 8 column blocks, the next group's reads in flight
+        // (one buffer: the previous tile's PV read it, and every wave is past that PV at B1)
+        sm.p[2 * wave][h][n] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        sm.p[2 * wave + 1][h][n] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        wg_barrier_lds();  // B2: P of every row and every wave's rows of the tile are in LDS
+        // ---- PV over the tile's 8 k-steps, each step's reads issued during the one
+        // before; the next tile's DMA goes out between the steps
+        const uint8_t* vb = &sm.code[buf][0];
+        auto pv_read = [&](int J, int b) __attribute__((always_inline)) {
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(
+                vb + (J >> 1) * F8_WBYTES + (J & 1) * 16 * 512 + pv_addr[b]));
+        };
+        uint4 bp = sm.p[0][h][n];
+        i32x2_t tv[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(pv0[i]), bop, acc_o[i], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int b = 0; b < 4; b++) tv[b] = pv_read(0, b);
 #pragma unroll
-        for (int grp = 1; grp < 4; grp++) {
-            i32x2_t cv[8];
+        for (int J = 0; J < 8; J++) {
+            const uint4 cbp = bp;
+            i32x2_t cv[4];
 #pragma unroll
-            for (int i = 0; i < 8; i++) cv[i] = nv[i];
-            if (grp < 3) {
+            for (int b = 0; b < 4; b++) cv[b] = tv[b];
+            if (J < 7) {
+                bp = sm.p[J + 1][h][n];
 #pragma unroll
-                for (int i = 0; i < 8; i++) nv[i] = trd(8 * grp + 8 + i);
+                for (int b = 0; b < 4; b++) tv[b] = pv_read(J + 1, b);
             }
-            __builtin_amdgcn_sched_barrier(0);  // the next group's reads issue before this group's math
+            __builtin_amdgcn_sched_barrier(0);  // the next step's reads issue before this step's math
+            if (more) {
+                dma_one(2 * J, tw + F8_TILE, buf ^ 1);
+                dma_one(2 * J + 1, tw + F8_TILE, buf ^ 1);
+                if (J == 7) dma_one(16, tw + F8_TILE, buf ^ 1);
+            }
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const uint4 aop = e4m3x8_to_f16x8((uint32_t)cv[i][0], (uint32_t)cv[i][1]);
-                acc_o[8 * grp + i] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(aop), bop, acc_o[8 * grp + i], 0, 0, 0);
+            for (int b = 0; b < 4; b++) {
+                const uint4 av = e4m3x8_to_f16x8((uint32_t)cv[b][0], (uint32_t)cv[b][1]);
+                acc_o[b] = mfma32_f16(av, cbp, acc_o[b]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        buf ^= 1;
     }
-    vm_wait_all();  // the next tile's DMA may still be landing: drain it (restart or epilogue)
+    vm_wait_all();  // DMA and rope loads in flight (restart or epilogue)
     if (!again) break;
-    }
-    // ---- merge the waves' states in LDS (each wave reuses its own raw buffers)
-    l_part += __shfl_xor(l_part, 16, 64);
-    l_part += __shfl_xor(l_part, 32, 64);
-    float* st = reinterpret_cast<float*>(&raw[wave][0][0]);  // [16][512] O
-    __syncthreads();  // every wave is done with its tiles
-    // float4 slot f of head row hh is stored at slot f ^ hh (spreads the 16 rows over the banks)
+    __syncthreads();  // every wave has read the tile maxima before they are written again
+    if (ntiles > 0) {  // start the rows again with the raised reference
+        const int64_t tw = r0 + F8_WROWS * wave;
 #pragma unroll
-    for (int mb = 0; mb < 32; mb++)
-        *reinterpret_cast<float4*>(st + n * DL + 4 * ((4 * mb + g) ^ n)) =
-            make_float4(acc_o[mb][0], acc_o[mb][1], acc_o[mb][2], acc_o[mb][3]);
-    if (g == 0) {
-        ml_s[wave][0][n] = m_run;
-        ml_s[wave][1][n] = l_part;
-        ml_s[wave][2][n] = rsc;
+        for (int k = 0; k < 17; k++) dma_one(k, tw, 0);
+        load_rope(tw);
     }
+    }
+
+    // ---- epilogue: l per head over the waves, then each wave's dims of every head
+    float lt = l_part + xor_lane<32>(l_part, lane);
+    __syncthreads();  // every wave is done with xch
+    if (h == 0) sm.xch[wave][n] = lt;
     __syncthreads();
+    const float L = (sm.xch[0][n] + sm.xch[1][n]) + (sm.xch[2][n] + sm.xch[3][n]);
     {
-        const int hh = tid >> 4;             // head within the group
-        const int f0 = tid & 15;             // float4 columns f0 + 16 q: each store covers 256 contiguous bytes
-        float mw[MF_WAVES], M = -INFINITY;
+        // partial O of this (chunk, group) in the matrix cores' lane order: float4
+        // ((w * 4 + b) * 4 + j) * 64 + lane holds head n = lane % 32, dims 128 w + 32 b +
+        // 8 j + 4 (lane / 32) .. + 3 (k_merge_f8 reads it in the same order)
+        const float so = 1.0f / rsc;  // exact (a power of two)
+        float4* dst = reinterpret_cast<float4*>(p.part_o) + (c * p.n_groups + hg) * (int64_t)(F8_HEADS * DL / 4) +
+                      wave * 16 * 64 + lane;
 #pragma unroll
-        for (int w = 0; w < MF_WAVES; w++) {
-            mw[w] = ml_s[w][0][hh];
-            M = fmaxf(M, mw[w]);
-        }
-        float sw[MF_WAVES], so[MF_WAVES], L = 0.0f;
+        for (int b = 0; b < 4; b++)
 #pragma unroll
-        for (int w = 0; w < MF_WAVES; w++) {
-            sw[w] = (mw[w] == -INFINITY) ? 0.0f : exp2f(mw[w] - M);
-            L += sw[w] * ml_s[w][1][hh];
-            const float rw = ml_s[w][2][hh];
-            so[w] = rw > 0.0f ? sw[w] / rw : 0.0f;  // 1 / rsc is exact
-        }
-        const int h = hg * MF_HEADS + hh;
-        if (h < a.n_heads) {
-            float* dst = p.part_o + (c * a.n_heads + h) * DL;
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const int f = f0 + 16 * q;
-                float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-                for (int w = 0; w < MF_WAVES; w++) {
-                    const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&raw[w][0][0]) +
-                                                                      hh * DL + 4 * (f ^ hh));
-                    o.x += so[w] * v.x; o.y += so[w] * v.y; o.z += so[w] * v.z; o.w += so[w] * v.w;
-                }
-                *reinterpret_cast<float4*>(dst + 4 * f) = o;
-            }
-            if ((tid & 15) == 0) {
-                p.part_m[c * a.n_heads + h] = M;  // log2 units
-                p.part_l[c * a.n_heads + h] = L;
-            }
+            for (int j = 0; j < 4; j++)
+                dst[(b * 4 + j) * 64] = make_float4(acc_o[b][4 * j] * so, acc_o[b][4 * j + 1] * so,
+                                                    acc_o[b][4 * j + 2] * so, acc_o[b][4 * j + 3] * so);
+        if (wave == 0 && h == 0 && head < a.n_heads) {
+            p.part_m[c * a.n_heads + head] = m_ref;  // log2 units
+            p.part_l[c * a.n_heads + head] = L;
         }
     }
 }
@@ -1448,6 +1373,79 @@ __global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
     }
 }
 
+// Merge of the fp8 matrix-core partials (stored in the split kernel's lane order,
+// see its epilogue).  Workgroup = (sequence, group of 32 heads, 32-dim block
+// (w, b, j) of the output): 64 threads (h, n) own head n's dims 128 w + 32 b +
+// 8 j + 4 h .. + 3, so the threads of a chunk group read 1 KB contiguous per
+// split; NG chunk groups take every NG-th split, U loads in flight each, merged
+// online (running max, rescaled sums), then combined through LDS.
+template <int NG>
+__global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
+    constexpr int U = 8;
+    __shared__ __align__(16) float4 o_s[NG][64];
+    __shared__ float m_s[NG][64], l_s[NG][64];
+    const int tid = threadIdx.x, grp = tid >> 6, l = tid & 63, n = l & 31, h = l >> 5;
+    const int64_t item = blockIdx.x;
+    const int wbj = (int)(item & 63);  // (w * 4 + b) * 4 + j
+    const int64_t sg = item >> 6;
+    const int g = (int)(sg % p.n_groups), s = (int)(sg / p.n_groups);
+    const int head = g * F8_HEADS + n;
+    const int hc = min(head, a.n_heads - 1);  // a padded head reads a real one's m, l and is not written
+    const int64_t c0 = min(p.chunk_prefix[s], p.max_chunks), c1 = min(p.chunk_prefix[s + 1], p.max_chunks);
+    const float4* src = reinterpret_cast<const float4*>(p.part_o) + g * (int64_t)(F8_HEADS * DL / 4) + wbj * 64 + l;
+    const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
+    float m = -INFINITY, lsum = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int64_t cb = c0 + grp; cb < c1; cb += U * NG) {
+        float mc[U], lc[U];
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t cc = cb + u * NG;
+            const int64_t ch = cc < c1 ? cc : cb;
+            mc[u] = p.part_m[ch * a.n_heads + hc];
+            lc[u] = p.part_l[ch * a.n_heads + hc];
+            v[u] = src[ch * cstride];
+            if (cc >= c1) mc[u] = -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const float mn = fmaxf(m, mc[u]);
+            const float sc = m == -INFINITY ? 0.0f : exp2f(m - mn);
+            const float w = mc[u] == -INFINITY ? 0.0f : exp2f(mc[u] - mn);
+            o.x = o.x * sc + w * v[u].x;
+            o.y = o.y * sc + w * v[u].y;
+            o.z = o.z * sc + w * v[u].z;
+            o.w = o.w * sc + w * v[u].w;
+            lsum = lsum * sc + w * lc[u];
+            m = mn;
+        }
+    }
+    o_s[grp][l] = o;
+    m_s[grp][l] = m;
+    l_s[grp][l] = lsum;
+    __syncthreads();
+    if (grp != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NG; k++) M = fmaxf(M, m_s[k][l]);
+    float L = 0.0f;
+    float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int k = 0; k < NG; k++) {
+        const float wk = m_s[k][l] == -INFINITY ? 0.0f : exp2f(m_s[k][l] - M);
+        L += wk * l_s[k][l];
+        const float4 u = o_s[k][l];
+        r.x += wk * u.x; r.y += wk * u.y; r.z += wk * u.z; r.w += wk * u.w;
+    }
+    if (head >= a.n_heads) return;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const int w = wbj >> 4, b = (wbj >> 2) & 3, j = wbj & 3;
+    *reinterpret_cast<float4*>(a.out + ((int64_t)s * a.n_heads + head) * DL + 128 * w + 32 * b + 8 * j + 4 * h) =
+        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    if (a.lse && wbj == 0 && h == 0) a.lse[(int64_t)s * a.n_heads + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -INFINITY;
+}
+
 }  // namespace
 
 int64_t attn_workspace_bytes(const kvq_attn_args& a) { return plan_bytes(a); }
@@ -1458,13 +1456,12 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
     const bool tq4 = a.qmode == KVQ_QMODE_TQ4;
     switch (stage) {
         case KVQ_STAGE_PREP:
-            // the matrix-core split kernels plan their chunk themselves; the fp8 one
-            // also prepares its query, TQ4 rotates it here once per head
+            // the matrix-core split kernels plan their chunk themselves; their
+            // query operands are prepared here once per head (TQ4: rotated)
             if (!f32) {
-                if (tq4) {
-                    const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
-                    hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
-                }
+                const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
+                if (tq4) hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
+                else hipLaunchKernelGGL(k_qprep_fp8, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
                 break;
             }
             hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a.seq_offsets, a.n_seqs, p.split_rows, a.total_rows,
@@ -1499,9 +1496,10 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
                 else if (!f32) hipLaunchKernelGGL((k_merge<true, true, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);
                 else hipLaunchKernelGGL((k_merge<true, false, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);
             } else {
-                if (!f32 && wide) hipLaunchKernelGGL((k_merge<false, true, 512>), dim3((unsigned)(2 * items)), dim3(512), 0, st, a, p);
-                else if (!f32 && narrow) hipLaunchKernelGGL((k_merge<false, true, 64>), dim3((unsigned)(2 * items)), dim3(64), 0, st, a, p);
-                else if (!f32) hipLaunchKernelGGL((k_merge<false, true, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
+                const int64_t f8_items = (int64_t)a.n_seqs * p.n_groups * 64;  // (sequence, group, 32-dim block)
+                if (!f32 && wide) hipLaunchKernelGGL((k_merge_f8<8>), dim3((unsigned)f8_items), dim3(512), 0, st, a, p);
+                else if (!f32 && narrow) hipLaunchKernelGGL((k_merge_f8<1>), dim3((unsigned)f8_items), dim3(64), 0, st, a, p);
+                else if (!f32) hipLaunchKernelGGL((k_merge_f8<2>), dim3((unsigned)f8_items), dim3(128), 0, st, a, p);
                 else hipLaunchKernelGGL((k_merge<false, false, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
             }
             break;

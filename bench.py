@@ -128,14 +128,19 @@ def time_graph(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def measure_other_rows(torch, kvq, workloads, x_kv8):
+ROWS = ("encode", "tq4", "ragged", "sparse", "q4", "q4attn")
+
+
+def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
     """The other hot-path rows, each on its own workload: encoders, TQ4
-    decode, the ragged long-context decode, q4_0 append and gather.  Inputs
-    resident on the device; HIP events around graphs of back-to-back
-    launches.  Rates are algorithmic bytes (or flops) over kernel time."""
+    decode, the ragged long-context decode, the sparse decode, q4_0 append and
+    gather, the fused q4_0 decode.  Inputs resident on the device; HIP events
+    around graphs of back-to-back launches.  Rates are algorithmic bytes (or
+    flops) over kernel time.  only: one of ROWS (the others are skipped)."""
     res = {}
     dev = "cuda"
     PEAK_T = PEAK_BF16_TFLOPS
+    want = (lambda r: True) if only is None else (lambda r: r == only)
 
     def hbm(name, nbytes, ms, extra=None):
         gbps = nbytes / (ms / 1000.0) / 1e9
@@ -144,21 +149,22 @@ def measure_other_rows(torch, kvq, workloads, x_kv8):
         res[name] = d
         log(f"{name}: {ms * 1000:.1f} us, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
 
-    # a1: fp8 encode of the 32768-row cache
-    N = x_kv8.shape[0]
-    c8 = torch.empty((N, 512), dtype=torch.uint8, device=dev)
-    s8 = torch.empty(N, dtype=torch.float32, device=dev)
-    ms = time_graph(torch, lambda: kvq.kvq_encode_fp8(x_kv8, c8, s8), 20)
-    hbm("fp8_encode_32768", N * (2048 + 516), ms, {"rows/s": N / (ms / 1000.0)})
-    # a2: TQ4 encode, the 8192-row pass and a 262144-row asymptote
     mask = torch.from_numpy(workloads.tq4_decode(T=256).sign_mask).to(dev)
-    x8k = torch.from_numpy(workloads.tq4_encode_rows(8192)).to(dev)
-    for n, xs in ((8192, x8k), (262144, gpu_latents(torch, 262144, 5))):
-        ct = torch.empty((n, 256), dtype=torch.uint8, device=dev)
-        rt = torch.empty(n, dtype=torch.float32, device=dev)
-        ms = time_graph(torch, lambda: kvq.kvq_encode_tq4(xs, mask, ct, rt), 20)
-        hbm(f"tq4_encode_{n}", n * (2048 + 260) + 64, ms, {"rows/s": n / (ms / 1000.0)})
-    del x8k
+    if want("encode"):
+        # a1: fp8 encode of the 32768-row cache
+        N = x_kv8.shape[0]
+        c8 = torch.empty((N, 512), dtype=torch.uint8, device=dev)
+        s8 = torch.empty(N, dtype=torch.float32, device=dev)
+        ms = time_graph(torch, lambda: kvq.kvq_encode_fp8(x_kv8, c8, s8), 20)
+        hbm("fp8_encode_32768", N * (2048 + 516), ms, {"rows/s": N / (ms / 1000.0)})
+        # a2: TQ4 encode, the 8192-row pass and a 262144-row asymptote
+        x8k = torch.from_numpy(workloads.tq4_encode_rows(8192)).to(dev)
+        for n, xs in ((8192, x8k), (262144, gpu_latents(torch, 262144, 5))):
+            ct = torch.empty((n, 256), dtype=torch.uint8, device=dev)
+            rt = torch.empty(n, dtype=torch.float32, device=dev)
+            ms = time_graph(torch, lambda: kvq.kvq_encode_tq4(xs, mask, ct, rt), 20)
+            hbm(f"tq4_encode_{n}", n * (2048 + 260) + 64, ms, {"rows/s": n / (ms / 1000.0)})
+        del x8k
 
     def decode(name, qmode, x, lengths, n_heads, seed, copies):
         T = x.shape[0]
@@ -208,89 +214,106 @@ def measure_other_rows(torch, kvq, workloads, x_kv8):
         log(f"{name}: attention call {ms_full * 1000:.1f} us ({T / (ms_full / 1000.0):.3g} rows/s), split kernel "
             f"{ms_split * 1000:.1f} us, {tf:.0f} TFLOP/s ({100 * tf / PEAK_T:.1f}% of MFMA)")
 
-    # a2 + a3-a8 on TQ4 rows: T = 32768, 128 heads, 16 copies
-    decode("tq4_decode_T32768_H128", 2, x_kv8, [x_kv8.shape[0]], 128, 1002, 16)
-    # ragged long-context fp8 decode: 32 sequences U[1024, 16384] + one of 131072
-    L = workloads.ragged_lengths()
-    xr = gpu_latents(torch, int(L.sum()), 1003, lengths=L)
-    decode("ragged_kv8_decode_33seq", 1, xr, L, 128, 1003, 1)
-    del xr
-    torch.cuda.empty_cache()
+    def sparse_row():
+        # sparse (DSA-style) decode: a 32768-row fp8 cache, 16 queries x 2048 selected rows, 128 heads;
+        # the selected rows are gathered into the workspace, then the dense kernels run
+        w = workloads.dsa_sparse_decode()
+        xs = torch.from_numpy(w.latent).to(dev)
+        cs = torch.empty((w.cache_rows, 512), dtype=torch.uint8, device=dev)
+        ss = torch.empty(w.cache_rows, dtype=torch.float32, device=dev)
+        kvq.kvq_encode_fp8(xs, cs, ss)
+        krs = torch.from_numpy(w.k_rope.view(np.int16)).to(dev)
+        idx = torch.from_numpy(w.row_index).to(dev)
+        outs = torch.empty((w.n_seqs, w.n_heads, 512), dtype=torch.float32, device=dev)
+        lses = torch.empty((w.n_seqs, w.n_heads), dtype=torch.float32, device=dev)
+        sa = kvq.attn_args(1, 0, torch.from_numpy(w.offsets).to(dev), w.total_rows, cs, ss, krs,
+                           torch.from_numpy(w.q_lat).to(dev), torch.from_numpy(w.q_rope).to(dev), w.sm_scale, outs, lses)
+        sws = kvq.alloc_workspace_sparse(sa)
+        ms_sp = time_graph(torch, lambda: kvq.kvq_decode_attn_sparse(sa, idx, w.cache_rows, sws), 16)
+        gc = torch.empty((w.total_rows, 512), dtype=torch.uint8, device=dev)
+        gs = torch.empty(w.total_rows, dtype=torch.float32, device=dev)
+        gr = torch.empty((w.total_rows, 64), dtype=torch.int16, device=dev)
+        ms_g = time_graph(torch, lambda: kvq.kvq_gather_rows(1, cs, ss, krs, idx, gc, gs, gr), 16)
+        n = w.total_rows
+        res["dsa_sparse_decode_T32768_q16_k2048"] = {
+            "us_per_call": ms_sp * 1000.0, "rows/s": n / (ms_sp / 1000.0), "gather_us": ms_g * 1000.0,
+            "gather_GB/s": n * (8 + 2 * 644) / (ms_g / 1000.0) / 1e9, "rows": n, "queries": w.n_seqs}
+        log(f"dsa_sparse_decode_T32768_q16_k2048: call {ms_sp * 1000:.1f} us ({n / (ms_sp / 1000.0):.3g} rows/s), "
+            f"gather {ms_g * 1000:.1f} us ({n * (8 + 2 * 644) / (ms_g / 1000.0) / 1e9:.0f} GB/s)")
+        del xs, cs, ss, krs, idx, sws, gc, gs, gr
+        torch.cuda.empty_cache()
 
-    # sparse (DSA-style) decode: a 32768-row fp8 cache, 16 queries x 2048 selected rows, 128 heads;
-    # the selected rows are gathered into the workspace, then the dense kernels run
-    w = workloads.dsa_sparse_decode()
-    xs = torch.from_numpy(w.latent).to(dev)
-    cs = torch.empty((w.cache_rows, 512), dtype=torch.uint8, device=dev)
-    ss = torch.empty(w.cache_rows, dtype=torch.float32, device=dev)
-    kvq.kvq_encode_fp8(xs, cs, ss)
-    krs = torch.from_numpy(w.k_rope.view(np.int16)).to(dev)
-    idx = torch.from_numpy(w.row_index).to(dev)
-    outs = torch.empty((w.n_seqs, w.n_heads, 512), dtype=torch.float32, device=dev)
-    lses = torch.empty((w.n_seqs, w.n_heads), dtype=torch.float32, device=dev)
-    sa = kvq.attn_args(1, 0, torch.from_numpy(w.offsets).to(dev), w.total_rows, cs, ss, krs,
-                       torch.from_numpy(w.q_lat).to(dev), torch.from_numpy(w.q_rope).to(dev), w.sm_scale, outs, lses)
-    sws = kvq.alloc_workspace_sparse(sa)
-    ms_sp = time_graph(torch, lambda: kvq.kvq_decode_attn_sparse(sa, idx, w.cache_rows, sws), 16)
-    gc = torch.empty((w.total_rows, 512), dtype=torch.uint8, device=dev)
-    gs = torch.empty(w.total_rows, dtype=torch.float32, device=dev)
-    gr = torch.empty((w.total_rows, 64), dtype=torch.int16, device=dev)
-    ms_g = time_graph(torch, lambda: kvq.kvq_gather_rows(1, cs, ss, krs, idx, gc, gs, gr), 16)
-    n = w.total_rows
-    res["dsa_sparse_decode_T32768_q16_k2048"] = {
-        "us_per_call": ms_sp * 1000.0, "rows/s": n / (ms_sp / 1000.0), "gather_us": ms_g * 1000.0,
-        "gather_GB/s": n * (8 + 2 * 644) / (ms_g / 1000.0) / 1e9, "rows": n, "queries": w.n_seqs}
-    log(f"dsa_sparse_decode_T32768_q16_k2048: call {ms_sp * 1000:.1f} us ({n / (ms_sp / 1000.0):.3g} rows/s), "
-        f"gather {ms_g * 1000:.1f} us ({n * (8 + 2 * 644) / (ms_g / 1000.0) / 1e9:.0f} GB/s)")
-    del xs, cs, ss, krs, idx, sws, gc, gs, gr
-    torch.cuda.empty_cache()
 
-    # a9 / a10: q4_0 bulk append of the 16 prefills, then the gather of everything
-    q = workloads.Q4Workload()
-    tok = int(q.prefill_off[-1])
-    kp = torch.zeros((q.n_cells, 8, 144), dtype=torch.uint8, device=dev)
-    vp = torch.zeros_like(kp)
-    cache = kvq.q4_cache(kp, vp, torch.from_numpy(q.table).to(dev), 64)
-    ks = torch.from_numpy(q.k_prefill).to(dev)
-    vs = torch.from_numpy(q.v_prefill).to(dev)
-    pos0 = torch.from_numpy(q.pos0_prefill).to(dev)
-    off = torch.from_numpy(q.prefill_off).to(dev)
-    ms = time_graph(torch, lambda: kvq.kvq_append_q4_0(cache, pos0, off, tok, ks, vs), 5)
-    hbm("q4_0_append_bulk", tok * 8 * 2 * (1024 + 144), ms, {"tokens": tok})
-    del ks, vs
-    kd = torch.empty((tok, 8, 256), dtype=torch.int16, device=dev)
-    vd = torch.empty_like(kd)
-    ms = time_graph(torch, lambda: kvq.kvq_gather_q4_0(cache, off, tok, kd, vd), 5)
-    hbm("q4_0_gather", tok * 8 * 2 * (144 + 512), ms, {"tokens": tok})
-    del kd, vd
-    # fused decode attention over the same pools: 32 query heads over the 8 KV heads, one
-    # query per sequence; three copies of the pools (3 x 131 MB) rotate past the 256 MB MALL
-    qq = torch.from_numpy(workloads.q4_queries(1007, q.n_seqs)).to(dev)
-    oq = torch.empty_like(qq)
-    lq = torch.empty(qq.shape[:2], dtype=torch.float32, device=dev)
-    tab = torch.from_numpy(q.table).to(dev)
-    caches = [cache] + [kvq.q4_cache(kp.clone(), vp.clone(), tab, 64) for _ in range(2)]
-    qa = kvq.q4_attn_args(off, tok, qq, oq, lq, workloads.Q4_SM_SCALE)
-    qws = kvq.alloc_workspace_q4(cache, qa)
-    it = [0]
+    def q4_rows(want):
+        # a9 / a10: q4_0 bulk append of the 16 prefills, then the gather of everything
+        q = workloads.Q4Workload()
+        tok = int(q.prefill_off[-1])
+        kp = torch.zeros((q.n_cells, 8, 144), dtype=torch.uint8, device=dev)
+        vp = torch.zeros_like(kp)
+        cache = kvq.q4_cache(kp, vp, torch.from_numpy(q.table).to(dev), 64)
+        ks = torch.from_numpy(q.k_prefill).to(dev)
+        vs = torch.from_numpy(q.v_prefill).to(dev)
+        pos0 = torch.from_numpy(q.pos0_prefill).to(dev)
+        off = torch.from_numpy(q.prefill_off).to(dev)
+        ms = time_graph(torch, lambda: kvq.kvq_append_q4_0(cache, pos0, off, tok, ks, vs), 5)
+        if want("q4"):
+            hbm("q4_0_append_bulk", tok * 8 * 2 * (1024 + 144), ms, {"tokens": tok})
+        del ks, vs
+        if want("q4"):
+            kd = torch.empty((tok, 8, 256), dtype=torch.int16, device=dev)
+            vd = torch.empty_like(kd)
+            ms = time_graph(torch, lambda: kvq.kvq_gather_q4_0(cache, off, tok, kd, vd), 5)
+            hbm("q4_0_gather", tok * 8 * 2 * (144 + 512), ms, {"tokens": tok})
+            del kd, vd
+        if not want("q4attn"):
+            return
+        # fused decode attention over the same pools: 32 query heads over the 8 KV heads, one
+        # query per sequence; three copies of the pools (3 x 131 MB) rotate past the 256 MB MALL
+        qq = torch.from_numpy(workloads.q4_queries(1007, q.n_seqs)).to(dev)
+        oq = torch.empty_like(qq)
+        lq = torch.empty(qq.shape[:2], dtype=torch.float32, device=dev)
+        tab = torch.from_numpy(q.table).to(dev)
+        caches = [cache] + [kvq.q4_cache(kp.clone(), vp.clone(), tab, 64) for _ in range(2)]
+        qa = kvq.q4_attn_args(off, tok, qq, oq, lq, workloads.Q4_SM_SCALE)
+        qws = kvq.alloc_workspace_q4(cache, qa)
+        it = [0]
 
-    def q4_call():
-        kvq.kvq_decode_attn_q4_0(caches[it[0] % 3], qa, qws)
-        it[0] += 1
+        def q4_call():
+            kvq.kvq_decode_attn_q4_0(caches[it[0] % 3], qa, qws)
+            it[0] += 1
 
-    ms = time_graph(torch, q4_call, 6)
-    kv_bytes = tok * 8 * 2 * 144
-    hbm("q4_0_decode_attn_g4", kv_bytes, ms, {"tokens": tok, "q_heads": 32, "kv_heads": 8,
-                                               "tokens/s": tok / (ms / 1000.0)})
-    # the same pools read by 64 query heads (8 per KV head)
-    q8 = torch.from_numpy(workloads.q4_queries(1007, q.n_seqs, n_q_heads=64)).to(dev)
-    o8 = torch.empty_like(q8)
-    qa = kvq.q4_attn_args(off, tok, q8, o8, None, workloads.Q4_SM_SCALE)
-    qws = kvq.alloc_workspace_q4(cache, qa)
-    ms = time_graph(torch, q4_call, 6)
-    hbm("q4_0_decode_attn_g8", kv_bytes, ms, {"tokens": tok, "q_heads": 64, "kv_heads": 8,
-                                               "tokens/s": tok / (ms / 1000.0)})
+        ms = time_graph(torch, q4_call, 6)
+        kv_bytes = tok * 8 * 2 * 144
+        hbm("q4_0_decode_attn_g4", kv_bytes, ms, {"tokens": tok, "q_heads": 32, "kv_heads": 8,
+                                                   "tokens/s": tok / (ms / 1000.0)})
+        # the same pools read by 64 query heads (8 per KV head)
+        q8 = torch.from_numpy(workloads.q4_queries(1007, q.n_seqs, n_q_heads=64)).to(dev)
+        o8 = torch.empty_like(q8)
+        qa = kvq.q4_attn_args(off, tok, q8, o8, None, workloads.Q4_SM_SCALE)
+        qws = kvq.alloc_workspace_q4(cache, qa)
+        ms = time_graph(torch, q4_call, 6)
+        hbm("q4_0_decode_attn_g8", kv_bytes, ms, {"tokens": tok, "q_heads": 64, "kv_heads": 8,
+                                                   "tokens/s": tok / (ms / 1000.0)})
+
+    if want("tq4"):
+        # a2 + a3-a8 on TQ4 rows: T = 32768, 128 heads, 16 copies
+        decode("tq4_decode_T32768_H128", 2, x_kv8, [x_kv8.shape[0]], 128, 1002, 16)
+    if want("ragged"):
+        # ragged long-context fp8 decode: 32 sequences U[1024, 16384] + one of 131072
+        L = workloads.ragged_lengths()
+        xr = gpu_latents(torch, int(L.sum()), 1003, lengths=L)
+        decode("ragged_kv8_decode_33seq", 1, xr, L, 128, 1003, 1)
+        del xr
+        torch.cuda.empty_cache()
+    if want("sparse"):
+        sparse_row()
+    if want("q4") or want("q4attn"):
+        q4_rows(want)
     return res
+
+    return res
+
+
 
 
 def main():
@@ -306,6 +329,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-rows", action="store_true",
                     help="skip the encoders, TQ4 decode, ragged decode and q4_0 measurements")
+    ap.add_argument("--only", choices=("fp8",) + ROWS,
+                    help="measure one row only (for a profiler run): fp8 = the decode step alone, else one of the "
+                         "other rows; prints no benchmark line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 10 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -323,6 +349,11 @@ def main():
     from quantized_kv_cache_row_amd import kvq, workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.only is not None and args.only != "fp8":
+        x = torch.from_numpy(workloads.kv8_decode().latent).to("cuda")
+        res = measure_other_rows(torch, kvq, workloads, x, only=args.only)
+        print(json.dumps({"only": args.only, "rows": res}), flush=True)
+        return
     dev = torch.device("cuda:0")
     log(f"device {torch.cuda.get_device_name(0)}")
     qmode = 1 if args.qmode == "fp8" else 2
@@ -443,6 +474,9 @@ def main():
     log(f"step {ms_per_step * 1000:.1f} us, split kernel {kern_ms * 1000:.1f} us ({reps * n_copies} launches), "
         f"{tflops:.1f} TFLOP/s, {gbps:.0f} GB/s")
 
+    if args.only == "fp8":
+        print(json.dumps({"only": "fp8", "step_us": ms_per_step * 1000.0, "split_us": kern_ms * 1000.0}), flush=True)
+        return
     other = None
     if not args.no_other_rows and qmode == 1 and args.precision == 0:
         other = measure_other_rows(torch, kvq, workloads, x)

@@ -69,7 +69,21 @@ def lib():
         L.oracle_decode_fp8_rows.restype = ctypes.c_int
         L.oracle_tq4_codebook.argtypes = [_c_f64p, _c_f32p, _c_f32p, ctypes.POINTER(ctypes.c_int)]
         L.oracle_tq4_codebook.restype = ctypes.c_int
+        L.oracle_tq_codebook.argtypes = [ctypes.c_int, _c_f64p, _c_f32p, _c_f32p, ctypes.POINTER(ctypes.c_int)]
+        L.oracle_tq_codebook.restype = ctypes.c_int
         L.oracle_quantizer_mse.argtypes = [_c_f64p, _c_f64p]
+        L.oracle_quantizer_mse_n.argtypes = [ctypes.c_int, _c_f64p, _c_f64p]
+        L.oracle_quantizer_mse_n.restype = ctypes.c_double
+        L.oracle_tq_code_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.oracle_tq_code_bytes.restype = ctypes.c_int64
+        L.oracle_encode_tq.argtypes = [ctypes.c_int, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_u8p, _c_f32p]
+        L.oracle_encode_tq.restype = ctypes.c_int
+        L.oracle_decode_tq_rows.argtypes = [ctypes.c_int, _c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p,
+                                            _c_f64p]
+        L.oracle_decode_tq_rows.restype = ctypes.c_int
+        L.oracle_tq_identity_check.argtypes = [ctypes.c_int, _c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p,
+                                               _c_f64p, _c_f64p, ctypes.c_int]
+        L.oracle_tq_identity_check.restype = ctypes.c_double
         L.oracle_quantizer_mse.restype = ctypes.c_double
         L.oracle_encode_tq4.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_u8p, _c_f32p]
         L.oracle_encode_tq4.restype = ctypes.c_int
@@ -221,6 +235,82 @@ def tq4_codebook():
     _check(lib().oracle_tq4_codebook(_p(le, _c_f64p), _p(lb, _c_f32p), _p(th, _c_f32p), ctypes.byref(it)),
            "tq4_codebook")
     return le, lb, th, it.value
+
+
+def tq_codebook(bits):
+    """Codec-1 codebook of a b-bit tier (b = 3, 4, 6): (levels_exact[2^b] f64,
+    levels_bf16[2^b] f32, thresholds[2^b - 1] f32, iterations)."""
+    n = 1 << bits
+    le = np.empty(n, np.float64)
+    lb = np.empty(n, np.float32)
+    th = np.empty(n - 1, np.float32)
+    it = ctypes.c_int(0)
+    _check(lib().oracle_tq_codebook(int(bits), _p(le, _c_f64p), _p(lb, _c_f32p), _p(th, _c_f32p),
+                                    ctypes.byref(it)), "tq_codebook")
+    return le, lb, th, it.value
+
+
+def tq_code_bytes(bits, dim):
+    """Code bytes per row of a b-bit tier, -1 where the width is refused."""
+    return lib().oracle_tq_code_bytes(int(bits), int(dim))
+
+
+def quantizer_mse_n(levels, thresholds):
+    lv = _c(levels, np.float64)
+    th = _c(thresholds, np.float64)
+    assert th.size == lv.size - 1
+    return lib().oracle_quantizer_mse_n(lv.size, _p(lv, _c_f64p), _p(th, _c_f64p))
+
+
+def encode_tq(x, sign_mask, bits):
+    """Codec-1 row encoder of a b-bit tier: (codes [n][dim*b/8] u8, radii [n] f32)."""
+    x = _c(x, np.float32)
+    m = _c(sign_mask, np.uint8)
+    n, dim = x.shape
+    cb = tq_code_bytes(bits, dim)
+    codes = np.empty((n, max(cb, 1)), np.uint8)
+    radii = np.empty(max(n, 1), np.float32)
+    rc = lib().oracle_encode_tq(int(bits), _p(x, _c_f32p), n, dim, _p(m, _c_u8p), _p(codes, _c_u8p),
+                                _p(radii, _c_f32p))
+    _check(rc, "encode_tq")
+    return codes[:, :cb], radii[:n]
+
+
+def encode_tq_rc(x, sign_mask, bits):
+    """Raw return code of the codec-1 encoder (for the refusal tests)."""
+    x = _c(x, np.float32)
+    m = _c(sign_mask, np.uint8)
+    n, dim = x.shape
+    codes = np.empty((n, max(dim, 1)), np.uint8)
+    radii = np.empty(max(n, 1), np.float32)
+    return lib().oracle_encode_tq(int(bits), _p(x, _c_f32p), n, dim, _p(m, _c_u8p), _p(codes, _c_u8p),
+                                  _p(radii, _c_f32p))
+
+
+def decode_tq(codes, radii, sign_mask, bits, dim):
+    codes = _c(codes, np.uint8)
+    radii = _c(radii, np.float32)
+    m = _c(sign_mask, np.uint8)
+    n = codes.shape[0]
+    assert codes.shape[1] == tq_code_bytes(bits, dim)
+    out = np.empty((n, dim), np.float64)
+    _check(lib().oracle_decode_tq_rows(int(bits), _p(codes, _c_u8p), _p(radii, _c_f32p), n, dim,
+                                       _p(m, _c_u8p), _p(out, _c_f64p)), "decode_tq")
+    return out
+
+
+def tq_identity_check(codes, radii, sign_mask, q, w, bits, plant=0):
+    """tq4_identity_check for a b-bit tier."""
+    codes = _c(codes, np.uint8)
+    radii = _c(radii, np.float32)
+    m = _c(sign_mask, np.uint8)
+    q = _c(q, np.float64)
+    w = _c(w, np.float64)
+    n = codes.shape[0]
+    dim = q.shape[0]
+    assert codes.shape[1] == tq_code_bytes(bits, dim)
+    return lib().oracle_tq_identity_check(int(bits), _p(codes, _c_u8p), _p(radii, _c_f32p), n, dim,
+                                          _p(m, _c_u8p), _p(q, _c_f64p), _p(w, _c_f64p), int(plant))
 
 
 def quantizer_mse(levels, thresholds):

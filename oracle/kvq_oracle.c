@@ -284,59 +284,70 @@ int oracle_decode_fp8_rows(const uint8_t* codes, const float* scales, int64_t n_
 }
 
 /* ------------------------------------------------------------------------- */
-/* TQ4 codebook: 16-level Lloyd-Max quantizer for N(0,1) ([KV8] Why int4)     */
+/* Codec-1 codebooks: 2^b-level Lloyd-Max quantizers for N(0,1), b = 3, 4, 6  */
+/* ([KV8] Why rotated-int4; the KV_TQ=4,6 tiers of the teacher-forcing table; */
+/* the "codec 1, 3-bit" tier of the .coli_kv reply)                          */
 /* ------------------------------------------------------------------------- */
 
 static double phi(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * M_PI); }
 static double Phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+static double Qtail(double x) { return 0.5 * erfc(x / sqrt(2.0)); } /* 1 - Phi(x), no cancellation */
 
-/* Lloyd-Max for N(0,1), 16 levels, in double.  Only the positive half is
- * iterated (the density is symmetric, so the optimum is symmetric with a
- * threshold at 0): thresholds are midpoints of neighbouring levels, levels are
- * the conditional means (phi(a) - phi(b)) / (Phi(b) - Phi(a)) of their cells.
- * Outputs (any may be NULL):
- *   levels_exact[16]   the converged levels, ascending;
- *   levels_bf16[16]    each level rounded to the nearest bfloat16 (reading:
- *                      the decode feeds bf16 tiles, so the stored levels are
- *                      bf16 values);
- *   thresholds[15]     fp32 midpoints of neighbouring bf16 levels (exact);
- *   iters              iterations to convergence. */
-int oracle_tq4_codebook(double* levels_exact, float* levels_bf16, float* thresholds, int* iters) {
-    double c[8], t[9];
-    for (int k = 0; k < 8; k++) c[k] = 0.25 + 0.35 * k; /* initial guess */
-    int it;
-    for (it = 0; it < 100000; it++) {
+/* Number of codebook levels of a codec-1 tier: 8 (3-bit), 16 (4-bit) or 64
+ * (6-bit); 0 for any other width. */
+static int tq_levels(int bits) { return (bits == 3 || bits == 4 || bits == 6) ? 1 << bits : 0; }
+
+/* Lloyd-Max for N(0,1) with N = 2^bits levels, in double.  Only the positive
+ * half is iterated (the density is symmetric, so the optimum is symmetric with
+ * a threshold at 0): thresholds are midpoints of neighbouring levels, levels
+ * are the conditional means (phi(a) - phi(b)) / (Q(a) - Q(b)) of their cells
+ * (Q the upper tail, Q(a) - Q(b) = Phi(b) - Phi(a)).  Once no level moves by
+ * 1e-14 it runs as many iterations again: the 64-level iteration contracts
+ * slowly (about 0.2% per step), so a small step still leaves the levels about
+ * 1e-12 from the fixed point, and its rounding noise (a few 1e-15) rules out a
+ * much smaller step bound.  Outputs (any may be NULL):
+ *   levels_exact[N]   the converged levels, ascending;
+ *   levels_bf16[N]    each level rounded to the nearest bfloat16 (reading:
+ *                     the decode feeds 16-bit tiles, so the stored levels are
+ *                     bf16 values);
+ *   thresholds[N-1]   fp32 midpoints of neighbouring bf16 levels (exact);
+ *   iters             iterations to convergence. */
+int oracle_tq_codebook(int bits, double* levels_exact, float* levels_bf16, float* thresholds, int* iters) {
+    const int N = tq_levels(bits);
+    if (!N) return ORACLE_ERR_UNSUPPORTED;
+    const int h = N / 2;
+    double c[32], t[33];
+    for (int k = 0; k < h; k++) c[k] = (k + 0.5) * 3.0 / h; /* initial guess */
+    int it, stop = -1;
+    for (it = 0; it < 2000000; it++) {
         t[0] = 0.0;
-        for (int k = 1; k < 8; k++) t[k] = 0.5 * (c[k - 1] + c[k]);
+        for (int k = 1; k < h; k++) t[k] = 0.5 * (c[k - 1] + c[k]);
         double delta = 0.0;
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < h; k++) {
             double a = t[k];
-            double b = (k == 7) ? INFINITY : t[k + 1];
-            double pa = phi(a), pb = (k == 7) ? 0.0 : phi(b);
-            double Pa = Phi(a), Pb = (k == 7) ? 1.0 : Phi(b);
-            double nc = (pa - pb) / (Pb - Pa);
+            double nc = (k == h - 1) ? phi(a) / Qtail(a)
+                                     : (phi(a) - phi(t[k + 1])) / (Qtail(a) - Qtail(t[k + 1]));
             double d = fabs(nc - c[k]);
             if (d > delta) delta = d;
             c[k] = nc;
         }
-        if (delta < 1e-15) break;
+        if (stop < 0 && delta < 1e-14) stop = 2 * it + 1;
+        if (it == stop) break;
     }
-    double full[16];
-    for (int k = 0; k < 8; k++) {
-        full[8 + k] = c[k];
-        full[7 - k] = -c[k];
+    if (stop < 0) return ORACLE_ERR_UNSUPPORTED; /* did not converge */
+    double full[64];
+    for (int k = 0; k < h; k++) {
+        full[h + k] = c[k];
+        full[h - 1 - k] = -c[k];
     }
     if (levels_exact)
-        for (int k = 0; k < 16; k++) levels_exact[k] = full[k];
-    float lb[16];
-    for (int k = 0; k < 16; k++) {
-        uint16_t b = oracle_bf16_encode(full[k]);
-        lb[k] = (float)oracle_bf16_decode(b);
-    }
+        for (int k = 0; k < N; k++) levels_exact[k] = full[k];
+    float lb[64];
+    for (int k = 0; k < N; k++) lb[k] = (float)oracle_bf16_decode(oracle_bf16_encode(full[k]));
     if (levels_bf16)
-        for (int k = 0; k < 16; k++) levels_bf16[k] = lb[k];
+        for (int k = 0; k < N; k++) levels_bf16[k] = lb[k];
     if (thresholds)
-        for (int k = 0; k < 15; k++) {
+        for (int k = 0; k < N - 1; k++) {
             double m = ((double)lb[k] + (double)lb[k + 1]) / 2.0;
             float mf = (float)m;
             if ((double)mf != m) return ORACLE_ERR_UNSUPPORTED; /* must be exact */
@@ -346,13 +357,18 @@ int oracle_tq4_codebook(double* levels_exact, float* levels_bf16, float* thresho
     return ORACLE_OK;
 }
 
-/* Mean squared error of a scalar quantizer (levels[16], cell boundaries
- * thresholds[15]) on N(0,1), closed form from the truncated moments. */
-double oracle_quantizer_mse(const double* levels, const double* thresholds) {
+int oracle_tq4_codebook(double* levels_exact, float* levels_bf16, float* thresholds, int* iters) {
+    return oracle_tq_codebook(4, levels_exact, levels_bf16, thresholds, iters);
+}
+
+/* Mean squared error of an n-level scalar quantizer (levels[n], cell
+ * boundaries thresholds[n-1]) on N(0,1), closed form from the truncated
+ * moments. */
+double oracle_quantizer_mse_n(int n, const double* levels, const double* thresholds) {
     double mse = 0.0;
-    for (int k = 0; k < 16; k++) {
+    for (int k = 0; k < n; k++) {
         double a = (k == 0) ? -INFINITY : thresholds[k - 1];
-        double b = (k == 15) ? INFINITY : thresholds[k];
+        double b = (k == n - 1) ? INFINITY : thresholds[k];
         double Pa = isinf(a) ? 0.0 : Phi(a), Pb = isinf(b) ? 1.0 : Phi(b);
         double pa = isinf(a) ? 0.0 : phi(a), pb = isinf(b) ? 0.0 : phi(b);
         double apa = isinf(a) ? 0.0 : a * pa, bpb = isinf(b) ? 0.0 : b * pb;
@@ -365,29 +381,64 @@ double oracle_quantizer_mse(const double* levels, const double* thresholds) {
     return mse;
 }
 
+double oracle_quantizer_mse(const double* levels, const double* thresholds) {
+    return oracle_quantizer_mse_n(16, levels, thresholds);
+}
+
 /* ------------------------------------------------------------------------- */
-/* a2: TQ4 row encoder ([KV8] Why rotated-int4; rebase 85852e2 refusal)       */
+/* a2: codec-1 row encoder ([KV8] Why rotated-int4; rebase 85852e2 refusal)  */
 /* ------------------------------------------------------------------------- */
 
 static int sign_bit(const uint8_t* mask, int i) { return (mask[i >> 3] >> (i & 7)) & 1; }
+
+/* Packing of b-bit indices (reading: the pages fix the index width per tier but
+ * not the byte layout; the plainest layout that is the 4-bit tier's nibble
+ * layout at b = 4): the row is a little-endian bit stream and index i occupies
+ * bits b*i .. b*i + b - 1, least significant bit first, so bit j of the stream
+ * is bit j % 8 of byte j / 8.  A row of dim indices takes dim * b / 8 bytes. */
+static void put_index(uint8_t* row, int i, int bits, unsigned v) {
+    for (int j = 0; j < bits; j++) {
+        int pos = i * bits + j;
+        if ((v >> j) & 1u) row[pos >> 3] |= (uint8_t)(1u << (pos & 7));
+    }
+}
+
+static unsigned get_index(const uint8_t* row, int i, int bits) {
+    unsigned v = 0;
+    for (int j = 0; j < bits; j++) {
+        int pos = i * bits + j;
+        v |= (unsigned)((row[pos >> 3] >> (pos & 7)) & 1) << j;
+    }
+    return v;
+}
+
+/* Code bytes per row of a b-bit tier, or -1 if dim cannot be encoded: dim must
+ * be a power of two (refusal of non-power-of-two widths) whose indices fill
+ * whole bytes. */
+int64_t oracle_tq_code_bytes(int bits, int dim) {
+    if (!tq_levels(bits) || !is_pow2(dim) || dim < 2 || (dim * bits) % 8 != 0) return -1;
+    return (int64_t)dim * bits / 8;
+}
 
 /* For each row x (dim a power of two):
  *   z_i = -x_i where sign bit i is set, else x_i;
  *   w   = FWHT(z), unnormalized, fp32 (oracle_fwht_f32 order);
  *   r   = sqrt of the pairwise-tree sum of x_i*x_i (level 0 is fl(x_i*x_i),
  *         each level adds adjacent pairs), correctly rounded;
- *   T_k = fl(t_k * r), k = 0..14 (t_k the fp32 thresholds of the codebook);
+ *   T_k = fl(t_k * r), k = 0 .. N-2 (t_k the fp32 thresholds of the codebook);
  *   idx_i = #{k : w_i > T_k}  (a value exactly on a threshold goes low);
- *   byte j = idx_{2j} | idx_{2j+1} << 4.
+ *   the indices packed as above (b = 4: byte j = idx_{2j} | idx_{2j+1} << 4).
  * The orthonormal coordinate is y = w / sqrt(n) and the scaled levels are
  * c_k r / sqrt(n), so the nearest level is found by comparing w with t_k r.
  * Non-power-of-two widths are refused. */
-int oracle_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
-                      uint8_t* codes, float* radii) {
+int oracle_encode_tq(int bits, const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
+                     uint8_t* codes, float* radii) {
     if (!x || !codes || !radii || !sign_mask || n_rows < 0) return ORACLE_ERR_ARG;
-    if (!is_pow2(dim) || dim < 2) return ORACLE_ERR_UNSUPPORTED;
-    float thr[15];
-    if (oracle_tq4_codebook(NULL, NULL, thr, NULL) != ORACLE_OK) return ORACLE_ERR_UNSUPPORTED;
+    const int64_t cb = oracle_tq_code_bytes(bits, dim);
+    if (cb < 0) return ORACLE_ERR_UNSUPPORTED;
+    const int N = tq_levels(bits);
+    float thr[63];
+    if (oracle_tq_codebook(bits, NULL, NULL, thr, NULL) != ORACLE_OK) return ORACLE_ERR_UNSUPPORTED;
     int rc = ORACLE_OK;
 #pragma omp parallel
     {
@@ -407,16 +458,15 @@ int oracle_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* si
                     for (int i = 0; i < len / 2; i++) sq[i] = sq[2 * i] + sq[2 * i + 1];
                 float rad = sqrtf(sq[0]);
                 radii[r] = rad;
-                float T[15];
-                for (int k = 0; k < 15; k++) T[k] = thr[k] * rad;
-                uint8_t* cr = codes + r * (dim / 2);
-                for (int j = 0; j < dim / 2; j++) {
-                    int i0 = 0, i1 = 0;
-                    for (int k = 0; k < 15; k++) {
-                        if (z[2 * j] > T[k]) i0++;
-                        if (z[2 * j + 1] > T[k]) i1++;
-                    }
-                    cr[j] = (uint8_t)(i0 | (i1 << 4));
+                float T[63];
+                for (int k = 0; k < N - 1; k++) T[k] = thr[k] * rad;
+                uint8_t* cr = codes + r * cb;
+                memset(cr, 0, (size_t)cb);
+                for (int i = 0; i < dim; i++) {
+                    unsigned idx = 0;
+                    for (int k = 0; k < N - 1; k++)
+                        if (z[i] > T[k]) idx++;
+                    put_index(cr, i, bits, idx);
                 }
             }
         }
@@ -426,33 +476,41 @@ int oracle_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* si
     return rc;
 }
 
+int oracle_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
+                      uint8_t* codes, float* radii) {
+    return oracle_encode_tq(4, x, n_rows, dim, sign_mask, codes, radii);
+}
+
 /* Reconstruction in double: y_i = c[idx_i] r / sqrt(n), x_hat = D H y / sqrt(n)
  * (R = H D / sqrt(n) is orthonormal, so R^-1 = R^T = D H / sqrt(n)). */
-static void decode_tq4_rows_with(const float* lv, const uint8_t* codes, const float* radii,
-                                 int64_t n_rows, int dim, const uint8_t* sign_mask, double* out) {
+static void decode_tq_rows_with(int bits, const float* lv, const uint8_t* codes, const float* radii,
+                                int64_t n_rows, int dim, const uint8_t* sign_mask, double* out) {
+    const int64_t cb = (int64_t)dim * bits / 8;
     double rs = sqrt((double)dim);
     for (int64_t r = 0; r < n_rows; r++) {
         double* o = out + r * dim;
-        const uint8_t* cr = codes + r * (dim / 2);
-        for (int i = 0; i < dim; i++) {
-            int idx = (i & 1) ? (cr[i >> 1] >> 4) : (cr[i >> 1] & 15);
-            o[i] = (double)lv[idx] * (double)radii[r] / rs;
-        }
+        const uint8_t* cr = codes + r * cb;
+        for (int i = 0; i < dim; i++) o[i] = (double)lv[get_index(cr, i, bits)] * (double)radii[r] / rs;
         fwht_f64(o, dim);
         for (int i = 0; i < dim; i++) o[i] = (sign_bit(sign_mask, i) ? -o[i] : o[i]) / rs;
     }
 }
 
-int oracle_decode_tq4_rows(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
-                           const uint8_t* sign_mask, double* out) {
-    if (!is_pow2(dim) || dim < 2) return ORACLE_ERR_UNSUPPORTED;
-    float lv[16];
-    oracle_tq4_codebook(NULL, lv, NULL, NULL);
-    decode_tq4_rows_with(lv, codes, radii, n_rows, dim, sign_mask, out);
+int oracle_decode_tq_rows(int bits, const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
+                          const uint8_t* sign_mask, double* out) {
+    if (oracle_tq_code_bytes(bits, dim) < 0) return ORACLE_ERR_UNSUPPORTED;
+    float lv[64];
+    oracle_tq_codebook(bits, NULL, lv, NULL, NULL);
+    decode_tq_rows_with(bits, lv, codes, radii, n_rows, dim, sign_mask, out);
     return ORACLE_OK;
 }
 
-/* The rotation identities of the native 4-bit consumer ([KV8] Ready for
+int oracle_decode_tq4_rows(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
+                           const uint8_t* sign_mask, double* out) {
+    return oracle_decode_tq_rows(4, codes, radii, n_rows, dim, sign_mask, out);
+}
+
+/* The rotation identities of the native codec-1 consumer ([KV8] Ready for
  * review): for a query q and weights w over rows,
  *   q . x_hat_t        == (R q) . y_t
  *   sum_t w_t x_hat_t  == R^T (sum_t w_t y_t)
@@ -464,11 +522,13 @@ int oracle_decode_tq4_rows(const uint8_t* codes, const float* radii, int64_t n_r
  * the query rotation (R q := H q / sqrt(n)); 3 drops the signs from the
  * un-rotation (R^T v := H v / sqrt(n)); 4 leaves the weighted sum unrotated
  * (R^T v := v).  Each planted mistake must show up as a large discrepancy. */
-static double tq4_identity_check_planted(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
-                                         const uint8_t* sign_mask, const double* q, const double* w, int plant) {
-    if (!is_pow2(dim) || dim < 2) return -1.0;
-    float lv[16];
-    oracle_tq4_codebook(NULL, lv, NULL, NULL);
+static double tq_identity_check_planted(int bits, const uint8_t* codes, const float* radii, int64_t n_rows,
+                                        int dim, const uint8_t* sign_mask, const double* q, const double* w,
+                                        int plant) {
+    if (oracle_tq_code_bytes(bits, dim) < 0) return -1.0;
+    const int64_t cb = (int64_t)dim * bits / 8;
+    float lv[64];
+    oracle_tq_codebook(bits, NULL, lv, NULL, NULL);
     double rs = sqrt((double)dim);
     double* xh = (double*)malloc(sizeof(double) * (size_t)dim);
     double* y = (double*)malloc(sizeof(double) * (size_t)dim);
@@ -484,12 +544,9 @@ static double tq4_identity_check_planted(const uint8_t* codes, const float* radi
         for (int i = 0; i < dim; i++) rq[i] /= rs;
     }
     for (int64_t r = 0; r < n_rows; r++) {
-        decode_tq4_rows_with(lv, codes + r * (dim / 2), radii + r, 1, dim, sign_mask, xh);
-        const uint8_t* cr = codes + r * (dim / 2);
-        for (int i = 0; i < dim; i++) {
-            int idx = (i & 1) ? (cr[i >> 1] >> 4) : (cr[i >> 1] & 15);
-            y[i] = (double)lv[idx] * (double)radii[r] / rs;
-        }
+        const uint8_t* cr = codes + r * cb;
+        decode_tq_rows_with(bits, lv, cr, radii + r, 1, dim, sign_mask, xh);
+        for (int i = 0; i < dim; i++) y[i] = (double)lv[get_index(cr, i, bits)] * (double)radii[r] / rs;
         double a = 0.0, b = 0.0, mag = 0.0;
         for (int i = 0; i < dim; i++) {
             a += q[i] * xh[i];
@@ -519,15 +576,20 @@ static double tq4_identity_check_planted(const uint8_t* codes, const float* radi
     return worst;
 }
 
+double oracle_tq_identity_check(int bits, const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
+                                const uint8_t* sign_mask, const double* q, const double* w, int plant) {
+    return tq_identity_check_planted(bits, codes, radii, n_rows, dim, sign_mask, q, w, plant);
+}
+
 double oracle_tq4_identity_check(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
                                  const uint8_t* sign_mask, const double* q, const double* w) {
-    return tq4_identity_check_planted(codes, radii, n_rows, dim, sign_mask, q, w, 0);
+    return tq_identity_check_planted(4, codes, radii, n_rows, dim, sign_mask, q, w, 0);
 }
 
 /* The same check with a planted mistake (see above); tests only. */
 double oracle_tq4_identity_check_planted(const uint8_t* codes, const float* radii, int64_t n_rows, int dim,
                                          const uint8_t* sign_mask, const double* q, const double* w, int plant) {
-    return tq4_identity_check_planted(codes, radii, n_rows, dim, sign_mask, q, w, plant);
+    return tq_identity_check_planted(4, codes, radii, n_rows, dim, sign_mask, q, w, plant);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -536,11 +598,12 @@ double oracle_tq4_identity_check_planted(const uint8_t* codes, const float* radi
 
 /* For every sequence s (rows seq_offsets[s] .. seq_offsets[s+1]-1) and head h:
  *   x_hat_t  = reconstructed latent row (fp8: e4m3(code) * scale;
- *              TQ4: oracle_decode_tq4_rows), explicitly, in double;
+ *              codec 1: oracle_decode_tq_rows), explicitly, in double;
  *   s_t      = sm_scale * (q_lat[s,h] . x_hat_t + q_rope[s,h] . k_rope_t);
  *   p        = softmax over all rows of the sequence (max subtracted);
  *   out[s,h] = sum_t p_t x_hat_t;   lse[s,h] = m + log(sum_t exp(s_t - m)).
- * qmode 1 = fp8 rows (codes [rows][dim]), 2 = TQ4 rows (codes [rows][dim/2]).
+ * qmode 1 = fp8 rows (codes [rows][dim]); codec-1 rows, codes [rows][dim*b/8]:
+ * qmode 2 = 4-bit (TQ4), 3 = 3-bit (TQ3), 4 = 6-bit (TQ6).
  * k_rope holds bfloat16 bit patterns.  A sequence with no rows gives zeros and
  * lse = -Inf.  Decode attends to every cached row (no mask). */
 int oracle_decode_attn(int qmode, int n_seqs, int n_heads, int dim, int dim_rope,
@@ -549,11 +612,12 @@ int oracle_decode_attn(int qmode, int n_seqs, int n_heads, int dim, int dim_rope
                        const float* q_rope, double sm_scale, double* out, double* lse) {
     if (n_seqs < 0 || n_heads <= 0 || dim <= 0 || dim_rope < 0 || !seq_offsets || !out)
         return ORACLE_ERR_ARG;
-    if (qmode != 1 && qmode != 2) return ORACLE_ERR_UNSUPPORTED;
-    if (qmode == 2 && (!is_pow2(dim) || !sign_mask)) return ORACLE_ERR_UNSUPPORTED;
-    int cb = (qmode == 1) ? dim : dim / 2;
-    float lv[16];
-    if (qmode == 2) oracle_tq4_codebook(NULL, lv, NULL, NULL);
+    const int bits = qmode == 2 ? 4 : qmode == 3 ? 3 : qmode == 4 ? 6 : 0;
+    if (qmode != 1 && !bits) return ORACLE_ERR_UNSUPPORTED;
+    if (bits && (oracle_tq_code_bytes(bits, dim) < 0 || !sign_mask)) return ORACLE_ERR_UNSUPPORTED;
+    const int64_t cb = (qmode == 1) ? dim : oracle_tq_code_bytes(bits, dim);
+    float lv[64];
+    if (bits) oracle_tq_codebook(bits, NULL, lv, NULL, NULL);
     for (int s = 0; s < n_seqs; s++) {
         int64_t t0 = seq_offsets[s], t1 = seq_offsets[s + 1];
         int64_t T = t1 - t0;
@@ -573,7 +637,7 @@ int oracle_decode_attn(int qmode, int n_seqs, int n_heads, int dim, int dim_rope
             if (qmode == 1)
                 oracle_decode_fp8_rows(codes + (t0 + t) * cb, row_scale + t0 + t, 1, dim, X + t * dim);
             else
-                decode_tq4_rows_with(lv, codes + (t0 + t) * cb, row_scale + t0 + t, 1, dim, sign_mask,
+                decode_tq_rows_with(bits, lv, codes + (t0 + t) * cb, row_scale + t0 + t, 1, dim, sign_mask,
                                      X + t * dim);
             for (int r = 0; r < dim_rope; r++)
                 KR[t * dim_rope + r] = oracle_bf16_decode(k_rope[(t0 + t) * dim_rope + r]);

@@ -24,9 +24,13 @@ def _attn_case(rows, q_lat, q_rope, k_rope_f32=None, qmode=1, mask=None, offsets
     if qmode == 1:
         codes, scales = oracle.encode_fp8(rows)
         xh = oracle.decode_fp8(codes, scales)
-    else:
+    elif qmode == 2:
         codes, scales = oracle.encode_tq4(rows, mask)
         xh = oracle.decode_tq4(codes, scales, mask)
+    else:
+        bits = {3: 3, 4: 6}[qmode]
+        codes, scales = oracle.encode_tq(rows, mask, bits)
+        xh = oracle.decode_tq(codes, scales, mask, bits, rows.shape[1])
     if k_rope_f32 is None:
         k_rope_f32 = np.zeros((T, 64), np.float32)
     kr = workloads.to_bf16_bits(k_rope_f32)
@@ -128,16 +132,44 @@ def test_row_permutation_invariance_and_sequences_independent():
         np.testing.assert_allclose(l1[0], lse[s], rtol=1e-13)
 
 
-def test_tq4_attention_zero_query_and_single_row():
+@pytest.mark.parametrize("qmode", [2, 3, 4])
+def test_tq4_attention_zero_query_and_single_row(qmode):
     r = _rng(7)
     mask = r.integers(0, 256, 64, dtype=np.uint8)
     x = r.standard_normal((20, 512)).astype(np.float32)
     out, lse, xh, _ = _attn_case(x, np.zeros((1, 2, 512), np.float32), np.zeros((1, 2, 64), np.float32),
-                                 qmode=2, mask=mask)
+                                 qmode=qmode, mask=mask)
     np.testing.assert_allclose(out[0, 1], xh.mean(axis=0), rtol=1e-12, atol=1e-12)
     out, lse, xh, _ = _attn_case(x[:1], r.standard_normal((1, 2, 512)).astype(np.float32),
-                                 np.zeros((1, 2, 64), np.float32), qmode=2, mask=mask)
+                                 np.zeros((1, 2, 64), np.float32), qmode=qmode, mask=mask)
     np.testing.assert_allclose(out[0, 0], xh[0], rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("qmode,bits", [(2, 4), (3, 3), (4, 6)])
+def test_codec1_attention_against_independent_decode(qmode, bits):
+    # Rows decoded outside the oracle (numpy's reading of the bit stream, scipy's
+    # Hadamard matrix, the codebook levels) and the softmax written out in numpy.
+    import scipy.linalg
+    r = _rng(70 + qmode)
+    mask = r.integers(0, 256, 64, dtype=np.uint8)
+    x = (r.standard_normal((37, 512)) * r.lognormal(0, 0.3, (37, 1))).astype(np.float32)
+    ql = (r.standard_normal((1, 3, 512)) * 0.5).astype(np.float32)
+    qr = r.standard_normal((1, 3, 64)).astype(np.float32)
+    kr = r.standard_normal((37, 64)).astype(np.float32)
+    out, lse, _, krb = _attn_case(x, ql, qr, kr, qmode=qmode, mask=mask)
+    codes, radii = oracle.encode_tq(x, mask, bits)
+    _, lv, _, _ = oracle.tq_codebook(bits)
+    b = np.unpackbits(codes, axis=1, bitorder="little").reshape(37, 512, bits)
+    idx = (b.astype(np.int64) << np.arange(bits)).sum(axis=2)
+    d = np.where(np.unpackbits(mask, bitorder="little") == 1, -1.0, 1.0)
+    R = scipy.linalg.hadamard(512) * d[None, :] / np.sqrt(512.0)
+    xh = (lv.astype(np.float64)[idx] * radii.astype(np.float64)[:, None] / np.sqrt(512.0)) @ R
+    krd = oracle.bf16_decode(krb)
+    for h in range(3):
+        s = SM * (xh @ ql[0, h].astype(np.float64) + krd @ qr[0, h].astype(np.float64))
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(out[0, h], (p / p.sum()) @ xh, rtol=0, atol=1e-12 * np.abs(xh).max())
+        assert abs(lse[0, h] - (s.max() + np.log(p.sum()))) < 1e-12 * max(1.0, abs(lse[0, h]))
 
 
 # ---- q4_0 ---------------------------------------------------------------------

@@ -127,9 +127,10 @@ def test_fp8_roundtrip_error_bounds():
 
 # ---- TQ4 codebook ----------------------------------------------------------------
 
-def test_codebook_matches_textbook_lloyd_max():
-    le, lb, th, it = oracle.tq4_codebook()
-    for kind, idx, val in read_golden("lloyd_max_gaussian16.txt"):
+@pytest.mark.parametrize("bits,golden", [(4, "lloyd_max_gaussian16.txt"), (3, "lloyd_max_gaussian8.txt")])
+def test_codebook_matches_textbook_lloyd_max(bits, golden):
+    le, lb, th, it = oracle.tq_codebook(bits)
+    for kind, idx, val in read_golden(golden):
         i, v = int(idx), float(val)
         if kind == "level":
             assert abs(le[i] - v) < 6e-4, (i, le[i], v)
@@ -138,37 +139,79 @@ def test_codebook_matches_textbook_lloyd_max():
             t = (le[i] + le[i + 1]) / 2
             assert abs(t - v) < 6e-4, (i, t, v)
         else:
-            mse = oracle.quantizer_mse(le, (le[:-1] + le[1:]) / 2)
+            mse = oracle.quantizer_mse_n(le, (le[:-1] + le[1:]) / 2)
             assert abs(mse - v) < 1e-5, (mse, v)
+    if bits == 4:  # the 4-bit entry points are the b = 4 tier
+        le4, lb4, th4, _ = oracle.tq4_codebook()
+        np.testing.assert_array_equal(le4, le)
+        np.testing.assert_array_equal(lb4, lb)
+        np.testing.assert_array_equal(th4, th)
 
 
-def test_codebook_centroid_condition_by_integration():
-    le, lb, th, it = oracle.tq4_codebook()
+@pytest.mark.parametrize("bits", [3, 4, 6])
+def test_codebook_centroid_condition_by_integration(bits):
+    le, lb, th, it = oracle.tq_codebook(bits)
+    assert le.size == 1 << bits and np.all(np.diff(le) > 0)
     t = np.concatenate([[-np.inf], (le[:-1] + le[1:]) / 2, [np.inf]])
     pdf = scipy.stats.norm.pdf
-    for k in range(16):
-        num = scipy.integrate.quad(lambda x: x * pdf(x), t[k], t[k + 1], epsabs=1e-14, epsrel=1e-13)[0]
-        den = scipy.integrate.quad(pdf, t[k], t[k + 1], epsabs=1e-14, epsrel=1e-13)[0]
+    for k in range(le.size):
+        num = scipy.integrate.quad(lambda x: x * pdf(x), t[k], t[k + 1], epsabs=1e-15, epsrel=1e-13)[0]
+        den = scipy.integrate.quad(pdf, t[k], t[k + 1], epsabs=1e-15, epsrel=1e-13)[0]
         assert abs(num / den - le[k]) < 1e-9, k
 
 
-def test_codebook_mse_by_integration_and_bf16_levels():
-    le, lb, th, it = oracle.tq4_codebook()
+def test_codebook_64_levels_near_high_resolution_limit():
+    # Panter-Dite: the optimal N-level MSE of N(0,1) tends to (sqrt(3) pi / 2) / N^2 from
+    # below; at N = 64 the optimum is within a few percent of it.  Across tiers the MSE
+    # falls by about 4x per bit, faster than the limit at small N.
+    mses = {}
+    for bits in (3, 4, 6):
+        le, _, _, _ = oracle.tq_codebook(bits)
+        mses[bits] = oracle.quantizer_mse_n(le, (le[:-1] + le[1:]) / 2)
+    pd64 = np.sqrt(3) * np.pi / 2 / 64 ** 2
+    assert 0.95 * pd64 < mses[6] < pd64, (mses[6], pd64)
+    assert 3.4 < mses[3] / mses[4] < 4.0
+    assert 3.6 * 3.6 < mses[4] / mses[6] < 16.0
+    # the exact MSE is a minimum: moving any one level changes it upward
+    le, _, _, _ = oracle.tq_codebook(6)
+    base = oracle.quantizer_mse_n(le, (le[:-1] + le[1:]) / 2)
+    for k in (0, 17, 40, 63):
+        for d in (-1e-3, 1e-3):
+            l2 = le.copy()
+            l2[k] += d
+            l2 = np.sort(l2)
+            assert oracle.quantizer_mse_n(l2, (l2[:-1] + l2[1:]) / 2) > base
+
+
+@pytest.mark.parametrize("bits,mse_bf16", [(3, 0.03455), (4, 0.0095), (6, 0.000646)])
+def test_codebook_mse_by_integration_and_bf16_levels(bits, mse_bf16):
+    le, lb, th, it = oracle.tq_codebook(bits)
+    n = 1 << bits
     pdf = scipy.stats.norm.pdf
     thr = th.astype(np.float64)
     lv = lb.astype(np.float64)
     edges = np.concatenate([[-np.inf], thr, [np.inf]])
     mse_num = sum(scipy.integrate.quad(lambda x: (x - lv[k]) ** 2 * pdf(x), edges[k], edges[k + 1],
-                                       epsabs=1e-14)[0] for k in range(16))
-    assert abs(oracle.quantizer_mse(lv, thr) - mse_num) < 1e-10
-    # levels are bfloat16 values, symmetric, thresholds their exact fp32 midpoints
-    bits = lb.view(np.uint32)
-    assert np.all(bits & 0xFFFF == 0)
+                                       epsabs=1e-15)[0] for k in range(n))
+    assert abs(oracle.quantizer_mse_n(lv, thr) - mse_num) < 1e-10
+    if bits == 4:
+        assert oracle.quantizer_mse(lv, thr) == oracle.quantizer_mse_n(lv, thr)
+    # levels are bfloat16 values (each the nearest one to its exact level), symmetric,
+    # thresholds their exact fp32 midpoints
+    ub = lb.view(np.uint32)
+    assert np.all(ub & 0xFFFF == 0)
+    for k in range(n):
+        up = np.float32(np.uint32(ub[k] + 0x10000).view(np.float32))
+        dn = np.float32(np.uint32(ub[k] - 0x10000).view(np.float32))
+        assert abs(le[k] - lv[k]) <= min(abs(le[k] - up), abs(le[k] - dn)), k
+        # the rounding is far from a tie, so the table does not hang on the last digits
+        # of the iteration
+        assert abs(abs(le[k] - lv[k]) - abs(up - lv[k]) / 2) > 1e-7, k
     np.testing.assert_array_equal(lb, -lb[::-1])
     np.testing.assert_array_equal(th.astype(np.float64), (lv[:-1] + lv[1:]) / 2)
-    assert th[7] == 0.0
-    # rounding the levels to bf16 costs little: 0.0095 -> within 1e-5
-    assert abs(oracle.quantizer_mse(lv, thr) - 0.0095) < 2e-5
+    assert th[n // 2 - 1] == 0.0
+    # rounding the levels to bf16 costs little
+    assert abs(oracle.quantizer_mse_n(lv, thr) - mse_bf16) < 2e-5 * (mse_bf16 / 0.0095)
 
 
 # ---- TQ4 encoder -----------------------------------------------------------------
@@ -267,3 +310,93 @@ def test_tq4_sign_mask_matters():
     c2, r2 = oracle.encode_tq4(x, _mask(77))
     np.testing.assert_array_equal(r1, r2)  # the radius does not see the rotation
     assert np.mean(c1 != c2) > 0.5
+
+
+# ---- the 3- and 6-bit tiers of the same codec ---------------------------------------
+
+def _unpack(codes, bits, dim):
+    """Indices of b-bit codes, read as a little-endian bit stream (numpy's unpackbits)."""
+    b = np.unpackbits(codes, axis=1, bitorder="little").reshape(codes.shape[0], dim, bits)
+    return (b.astype(np.int64) << np.arange(bits)).sum(axis=2)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6])
+def test_tq_packing_radius_and_nearest_level(bits):
+    rng = np.random.default_rng(40 + bits)
+    x = (rng.standard_normal((64, 512)) * rng.lognormal(0, 0.5, (64, 1))).astype(np.float32)
+    mask = _mask()
+    codes, radii = oracle.encode_tq(x, mask, bits)
+    assert codes.shape == (64, 512 * bits // 8) and oracle.tq_code_bytes(bits, 512) == 64 * bits
+    xd = x.astype(np.float64)
+    r = np.linalg.norm(xd, axis=1)
+    ulp = np.spacing(radii.astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(radii - r) <= 2 * ulp)
+    le, lb, th, _ = oracle.tq_codebook(bits)
+    H = scipy.linalg.hadamard(512).astype(np.float64)
+    y = (xd * _signs(mask)[None, :]) @ H.T / np.sqrt(512)
+    idx = _unpack(codes, bits, 512)
+    sc = (radii.astype(np.float64) / np.sqrt(512))[:, None, None]
+    best = np.argmin(np.abs(y[:, :, None] - lb.astype(np.float64)[None, None, :] * sc), axis=2)
+    margin = np.min(np.abs(y[:, :, None] - th.astype(np.float64)[None, None, :] * sc), axis=2)
+    clear = margin > 1e-6 * (radii[:, None] / np.sqrt(512))
+    assert np.all(idx[clear] == best[clear])
+    assert clear.mean() > 0.99
+    if bits == 4:  # the nibble layout of the 4-bit tier
+        c4, r4 = oracle.encode_tq4(x, mask)
+        np.testing.assert_array_equal(c4, codes)
+        np.testing.assert_array_equal(r4, radii)
+        np.testing.assert_array_equal(np.stack([c4 & 15, c4 >> 4], axis=2).reshape(64, 512), idx)
+
+
+@pytest.mark.parametrize("bits,mse_bf16", [(3, 0.03455), (6, 0.000646)])
+def test_tq_distortion_near_gaussian_limit(bits, mse_bf16):
+    # A Gaussian row's rotated coordinates, scaled by sqrt(n) / r, are close to N(0, 1),
+    # so the relative L2 error approaches sqrt of the codebook's MSE (4 bits: ~0.0975,
+    # next to the page's ~0.096).
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((400, 512)).astype(np.float32)
+    mask = _mask()
+    codes, radii = oracle.encode_tq(x, mask, bits)
+    xh = oracle.decode_tq(codes, radii, mask, bits, 512)
+    agg = np.sqrt(np.sum((xh - x) ** 2) / np.sum(x.astype(np.float64) ** 2))
+    assert abs(agg / np.sqrt(mse_bf16) - 1) < 0.04, agg
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_tq_rotation_identity_and_planted_mistakes(bits):
+    w = workloads.tiny_fp8_decode()
+    x = w.latent[:64]
+    mask = _mask()
+    codes, radii = oracle.encode_tq(x, mask, bits)
+    xh = oracle.decode_tq(codes, radii, mask, bits, 512)
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal(512)
+    wts = rng.uniform(0, 1, 64)
+    assert oracle.tq_identity_check(codes, radii, mask, q, wts, bits) < 1e-12
+    for plant in (1, 2, 3, 4):
+        assert oracle.tq_identity_check(codes, radii, mask, q, wts, bits, plant=plant) > 1e-3, plant
+    # the reconstruction, outside the oracle: x_hat = R^T y, R = H D / sqrt(n) from scipy's
+    # Sylvester matrix, y from numpy's reading of the bit stream
+    _, lv, _, _ = oracle.tq_codebook(bits)
+    d = np.where(np.unpackbits(mask, bitorder="little")[:512] == 1, -1.0, 1.0)
+    R = scipy.linalg.hadamard(512) * d[None, :] / np.sqrt(512.0)
+    y = lv.astype(np.float64)[_unpack(codes, bits, 512)] * radii.astype(np.float64)[:, None] / np.sqrt(512.0)
+    np.testing.assert_allclose(xh, y @ R, rtol=0, atol=1e-12 * np.max(np.abs(xh)))
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_tq_inert_rows_and_refusal(bits):
+    mask = _mask()
+    codes, radii = oracle.encode_tq(np.zeros((2, 512), np.float32), mask, bits)
+    assert np.all(radii == 0) and np.all(codes == 0)
+    # a zero row decodes to the zero row whatever its indices say
+    _, lb, _, _ = oracle.tq_codebook(bits)
+    assert np.all(oracle.decode_tq(codes, radii, mask, bits, 512) == 0)
+    for dim in (384, 500, 576):
+        assert oracle.encode_tq_rc(np.ones((1, dim), np.float32), np.zeros(dim // 8 + 1, np.uint8), bits) == 2
+    # widths whose indices do not fill whole bytes are refused too (3 bits: dim 2, 4)
+    for dim in (2, 4):
+        assert oracle.tq_code_bytes(bits, dim) == (dim * bits // 8 if dim * bits % 8 == 0 else -1)
+    assert oracle.tq_code_bytes(5, 512) == -1 and oracle.encode_tq_rc(np.ones((1, 8), np.float32),
+                                                                      np.zeros(1, np.uint8), 5) == 2
+    assert oracle.tq_code_bytes(bits, 8) == bits

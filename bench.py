@@ -46,8 +46,8 @@ def decode_flops(T, H):
 
 
 def decode_bytes(T, qmode):
-    # per row: codes (512 fp8 or 256 nibble bytes) + fp32 scale + 64 bf16 rope
-    return T * ((512 if qmode == 1 else 256) + 4 + 128)
+    # per row: codes (512 fp8 bytes, or 64 * bits for the rotated codec) + fp32 scale + 64 bf16 rope
+    return T * ({1: 512, 2: 256, 3: 192, 4: 384}[qmode] + 4 + 128)
 
 
 COPY_BYTES = 256 << 20
@@ -128,13 +128,14 @@ def time_graph(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-ROWS = ("encode", "tq4", "ragged", "sparse", "q4", "q4attn")
+ROWS = ("encode", "tq4", "tq3", "tq6", "ragged", "sparse", "q4", "q4attn")
+MALL_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 
 
 def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
-    """The other hot-path rows, each on its own workload: encoders, TQ4
-    decode, the ragged long-context decode, the sparse decode, q4_0 append and
-    gather, the fused q4_0 decode.  Inputs resident on the device; HIP events
+    """The other hot-path rows, each on its own workload: encoders, the rotated
+    codec's decode at 4, 3 and 6 bits, the ragged long-context decode, the
+    sparse decode, q4_0 append and gather, the fused q4_0 decode.  Inputs resident on the device; HIP events
     around graphs of back-to-back launches.  Rates are algorithmic bytes (or
     flops) over kernel time.  only: one of ROWS (the others are skipped)."""
     res = {}
@@ -175,20 +176,24 @@ def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
         ql = torch.randn((S, n_heads, 512), generator=g, device=dev) / math.sqrt(576.0)
         qr = torch.randn((S, n_heads, 64), generator=g, device=dev) / math.sqrt(576.0)
         kr = torch.randn((T, 64), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
-        cb = 512 if qmode == 1 else 256
+        cb = kvq.code_bytes(qmode)
+        if copies > 1:  # enough copies that the cycled caches exceed the last-level cache
+            copies = max(copies, -(-(MALL_BYTES + (64 << 20)) // decode_bytes(T, qmode)))
         sets = []
         for _ in range(copies):
             codes = torch.empty((T, cb), dtype=torch.uint8, device=dev)
             sc = torch.empty(T, dtype=torch.float32, device=dev)
             if qmode == 1:
                 kvq.kvq_encode_fp8(x, codes, sc)
-            else:
+            elif qmode == 2:
                 kvq.kvq_encode_tq4(x, mask, codes, sc)
+            else:
+                kvq.kvq_encode_tq(kvq.TQ_QMODE_BITS[qmode], x, mask, codes, sc)
             sets.append((codes, sc, kr.clone() if copies > 1 else kr))
         out = torch.empty((S, n_heads, 512), dtype=torch.float32, device=dev)
         lse = torch.empty((S, n_heads), dtype=torch.float32, device=dev)
         argsets = [kvq.attn_args(qmode, 0, offs, T, c, s_, k, ql, qr, workloads.SM_SCALE, out, lse,
-                                 sign_mask=mask if qmode == 2 else None) for (c, s_, k) in sets]
+                                 sign_mask=mask if qmode != 1 else None) for (c, s_, k) in sets]
         ws = kvq.alloc_workspace(argsets[0])
         it = [0]
 
@@ -210,7 +215,7 @@ def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
         tf = flops / (ms_split / 1000.0) / 1e12
         res[name] = {"us_per_call": ms_full * 1000.0, "rows/s": T / (ms_full / 1000.0), "split_us": ms_split * 1000.0,
                      "TFLOP/s": tf, "frac_mfma": tf / PEAK_T, "GB/s": nbytes / (ms_split / 1000.0) / 1e9,
-                     "rows": T, "seqs": S}
+                     "rows": T, "seqs": S, "copies": copies}
         log(f"{name}: attention call {ms_full * 1000:.1f} us ({T / (ms_full / 1000.0):.3g} rows/s), split kernel "
             f"{ms_split * 1000:.1f} us, {tf:.0f} TFLOP/s ({100 * tf / PEAK_T:.1f}% of MFMA)")
 
@@ -296,8 +301,21 @@ def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
                                                    "tokens/s": tok / (ms / 1000.0)})
 
     if want("tq4"):
-        # a2 + a3-a8 on TQ4 rows: T = 32768, 128 heads, 16 copies
+        # a2 + a3-a8 on TQ4 rows: T = 32768, 128 heads, copies past the last-level cache
         decode("tq4_decode_T32768_H128", 2, x_kv8, [x_kv8.shape[0]], 128, 1002, 16)
+    for bits, qm in ((3, kvq.KVQ_QMODE_TQ3), (6, kvq.KVQ_QMODE_TQ6)):
+        if not want(f"tq{bits}"):
+            continue
+        # the 3- and 6-bit tiers: the 8192-row encode pass, then the T = 32768, 128-head decode
+        n = 8192
+        x8k = torch.from_numpy(workloads.tq4_encode_rows(n)).to(dev)
+        ct = torch.empty((n, 64 * bits), dtype=torch.uint8, device=dev)
+        rt = torch.empty(n, dtype=torch.float32, device=dev)
+        ms = time_graph(torch, lambda b=bits: kvq.kvq_encode_tq(b, x8k, mask, ct, rt), 20)
+        hbm(f"tq{bits}_encode_{n}", n * (2048 + 64 * bits + 4) + 64, ms, {"rows/s": n / (ms / 1000.0)})
+        del x8k, ct, rt
+        decode(f"tq{bits}_decode_T32768_H128", qm, x_kv8, [x_kv8.shape[0]], 128, 1002, 16)
+        torch.cuda.empty_cache()
     if want("ragged"):
         # ragged long-context fp8 decode: 32 sequences U[1024, 16384] + one of 131072
         L = workloads.ragged_lengths()
@@ -309,8 +327,6 @@ def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
         sparse_row()
     if want("q4") or want("q4attn"):
         q4_rows(want)
-    return res
-
     return res
 
 

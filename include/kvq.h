@@ -14,7 +14,8 @@
  *  - Alignment (KVQ_ERR_INVALID_ARG otherwise): fp32 row inputs (x, k_src,
  *    v_src), code arrays read by the attention, pools, rope keys, outputs of
  *    the gather and of the attention: 16 bytes; fp8 codes written by the
- *    encoder: 8 bytes; TQ4 codes: 4 bytes; every other buffer: the natural
+ *    encoder: 8 bytes; codes written by the rotated-codec encoders: 4 bytes;
+ *    every other buffer: the natural
  *    alignment of its element type.
  *  - NaN and Inf in floating-point inputs are outside the contract.
  *  - Calls are thread-safe; the library holds only immutable state.
@@ -46,6 +47,8 @@ extern "C" {
 /* ---- modes ---------------------------------------------------------------- */
 #define KVQ_QMODE_FP8 1      /* e4m3 codes [rows][dim] + fp32 scale per row           */
 #define KVQ_QMODE_TQ4 2      /* 4-bit codebook indices [rows][dim/2] + fp32 radius    */
+#define KVQ_QMODE_TQ3 3      /* 3-bit indices [rows][3*dim/8] + fp32 radius           */
+#define KVQ_QMODE_TQ6 4      /* 6-bit indices [rows][6*dim/8] + fp32 radius           */
 /* KVQ_PREC_MFMA: 16-bit matrix-core contractions with fp32 accumulation,
  * softmax and per-row scales.  [KV8]'s matrix-core wording names bf16
  * operands; it is read as "16-bit operands, fp32 accumulation", and the
@@ -64,8 +67,9 @@ int kvq_abi_version(void);
 const char* kvq_status_string(int status);
 
 /* Bytes per stored row: KVQ_QMODE_FP8 -> dim + 4 (codes + scale),
- * KVQ_QMODE_TQ4 -> dim/2 + 4 (nibbles + radius).  Returns -1 for an unknown
- * mode or a dim the encoders refuse.  Host only. */
+ * KVQ_QMODE_TQ4 -> dim/2 + 4 (nibbles + radius), KVQ_QMODE_TQ3 -> 3*dim/8 + 4,
+ * KVQ_QMODE_TQ6 -> 6*dim/8 + 4.  Returns -1 for an unknown mode or a dim the
+ * encoders refuse.  Host only. */
 int64_t kvq_row_bytes(int qmode, int dim);
 
 /* The 4-bit codec's codebook ([KV8] "Why rotated-int4 for the 4-bit tier":
@@ -73,6 +77,14 @@ int64_t kvq_row_bytes(int qmode, int dim);
  * ascending, each a bfloat16 value; thresholds: host float[15], the exact
  * midpoints of neighbouring levels.  Either may be NULL.  Host only. */
 int kvq_tq4_codebook(float* levels, float* thresholds);
+
+/* The codebook of the rotated codec's b-bit tier, b = 3, 4 or 6 ([KV8]: the
+ * 4-bit tier above; the 6-bit tier of the teacher-forcing table, TQ6; the
+ * 3-bit tier of the .coli_kv reply, "codec 1, 3-bit"): the 2^b-level Lloyd-Max
+ * quantizer for N(0,1), levels rounded to bfloat16, thresholds their exact
+ * midpoints.  levels: host float[2^b]; thresholds: host float[2^b - 1]; either
+ * may be NULL.  KVQ_ERR_UNSUPPORTED for another b.  Host only. */
+int kvq_tq_codebook(int bits, float* levels, float* thresholds);
 
 /* ---- a1: fp8 e4m3 per-row encoder ([KV8] Summary, commit 1) -------------
  * For each row r of x (fp32 [n_rows][dim], row-major):
@@ -99,6 +111,16 @@ int kvq_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* codes, floa
  * dim: a power of two, 8 <= dim <= 512 (KVQ_ERR_UNSUPPORTED otherwise). */
 int kvq_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
                    uint8_t* codes, float* radii, void* stream);
+
+/* The same codec at b = 3, 4 or 6 bits (TQ3, TQ4, TQ6; codebook:
+ * kvq_tq_codebook(b)).  Identical steps with 2^b - 1 thresholds; the indices
+ * of a row form a little-endian bit stream, index i in bits b*i .. b*i + b - 1
+ * (least significant first; bit j of the stream is bit j % 8 of byte j / 8),
+ * so codes is u8 [n_rows][dim*b/8] (b = 4: the nibble layout above; b = 4
+ * gives exactly kvq_encode_tq4's output).  dim: a power of two, 8 <= dim <=
+ * 512.  KVQ_ERR_UNSUPPORTED for another b or dim. */
+int kvq_encode_tq(int bits, const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
+                  uint8_t* codes, float* radii, void* stream);
 
 /* ---- a9/a10: q4_0 paged tier ([Q4]) ---------------------------------------
  * Pools: u8 [n_cells][n_kv_heads][144]; each 144-byte head-row is 8 blocks of
@@ -148,25 +170,29 @@ int kvq_gather_q4_0(const kvq_q4_cache* cache, int n_seqs, const int64_t* dst_of
  * ([KV8] commit 6: fused decode with a 3-way qmode, score a_score8 and context
  * a_clat8 over fp8 rows; commit 2: split-T kernels; "Ready for review": the
  * native 4-bit consumer rotates q once per head, dots the codes through the
- * codebook and un-rotates the weighted sum.)
+ * codebook and un-rotates the weighted sum; the 3- and 6-bit tiers of the
+ * same codec are consumed the same way.)
  * For sequence s (rows seq_offsets[s] .. seq_offsets[s+1]-1) and head h:
- *   x_hat_t = the decoded latent row (fp8: e4m3(code)*scale; TQ4: see above);
+ *   x_hat_t = the decoded latent row (fp8: e4m3(code)*scale; TQ3/4/6: the
+ *             decode of kvq_encode_tq);
  *   s_t = sm_scale * (q_lat[s,h] . x_hat_t + q_rope[s,h] . k_rope_t);
  *   out[s,h] = sum_t softmax(s)_t x_hat_t;  lse[s,h] = log sum_t exp(s_t).
- * The latent rows are not reconstructed: fp8 codes (and TQ4 codebook levels)
+ * The latent rows are not reconstructed: fp8 codes (and codebook levels)
  * are converted exactly to fp16 matrix-core operands (KVQ_PREC_MFMA) or to
- * fp32 (KVQ_PREC_FP32), and the per-row scale is applied in fp32; TQ4 uses
- * the rotated query R q and un-rotates the merged output (R = H D / sqrt(dim)).
+ * fp32 (KVQ_PREC_FP32), and the per-row scale is applied in fp32; the rotated
+ * codec (TQ3/4/6) uses the rotated query R q and un-rotates the merged output
+ * (R = H D / sqrt(dim)).
  * A sequence with no rows gets out = 0 and lse = -Inf.
  * Tolerance against an fp64 evaluation on the same codes:
  *   max|err| / max|ref| <= 2e-3 (KVQ_PREC_MFMA), <= 1e-5 (KVQ_PREC_FP32).
  * KVQ_PREC_MFMA operands: latent codes in fp16 (exact for every e4m3 value and
- * codebook level); the latent query (TQ4: R q) scaled per head by a power of
- * two and rounded to fp16; the rope query split into two bf16 terms (k_rope is
+ * codebook level); the latent query scaled per head by a power of two and
+ * rounded to fp16 (TQ3/4/6: R q, as two fp16 terms, the rounding and its
+ * remainder); the rope query split into two bf16 terms (k_rope is
  * bf16); the probabilities p * rho_t scaled by a power of two per work item
  * and rounded to fp16; fp32 accumulation, softmax and per-row scales. */
 typedef struct kvq_attn_args {
-    int32_t qmode;              /* KVQ_QMODE_FP8 or KVQ_QMODE_TQ4                 */
+    int32_t qmode;              /* KVQ_QMODE_FP8, _TQ4, _TQ3 or _TQ6              */
     int32_t precision;          /* KVQ_PREC_MFMA or KVQ_PREC_FP32                 */
     int32_t n_seqs;             /* >= 1                                           */
     int32_t n_heads;            /* 1 .. 256                                       */
@@ -176,10 +202,11 @@ typedef struct kvq_attn_args {
     int32_t reserved0;          /* must be 0                                      */
     int64_t total_rows;         /* host copy of seq_offsets[n_seqs]               */
     const int64_t* seq_offsets; /* device int64 [n_seqs+1], ascending, [0] = 0    */
-    const uint8_t* codes;       /* device, fp8 [rows][512] or TQ4 [rows][256]     */
-    const float* row_scale;     /* device fp32 [rows]: fp8 scale or TQ4 radius    */
+    const uint8_t* codes;       /* device, fp8 [rows][512], TQ4 [rows][256],
+                                   TQ3 [rows][192] or TQ6 [rows][384]             */
+    const float* row_scale;     /* device fp32 [rows]: fp8 scale or the radius    */
     const uint16_t* k_rope;     /* device bf16 bits [rows][64]                    */
-    const uint8_t* sign_mask;   /* device u8 [64] (TQ4 only, else ignored)        */
+    const uint8_t* sign_mask;   /* device u8 [64] (TQ3/4/6; ignored for fp8)      */
     const float* q_lat;         /* device fp32 [n_seqs][n_heads][512]             */
     const float* q_rope;        /* device fp32 [n_seqs][n_heads][64]              */
     float* out;                 /* device fp32 [n_seqs][n_heads][512]             */
@@ -221,13 +248,14 @@ int kvq_decode_attn_noalloc(const kvq_attn_args* a, void* stream);
 /* One stage of kvq_decode_attn; running stages 0..2 in order on one stream is
  * exactly kvq_decode_attn.  Running a stage gives profilers and timers one
  * stage per call:
- *   KVQ_STAGE_PREP   KVQ_PREC_FP32: the per-sequence T-split prefix and, TQ4,
- *                    R q in the workspace; KVQ_PREC_MFMA, TQ4: the rotated
- *                    fp16 query operands; KVQ_PREC_MFMA, fp8: nothing (the
- *                    matrix-core split kernels plan their T-split themselves,
- *                    the fp8 one also prepares its query);
+ *   KVQ_STAGE_PREP   KVQ_PREC_FP32: the per-sequence T-split prefix and, TQ3/4/6,
+ *                    R q in the workspace; KVQ_PREC_MFMA: the fp16 query
+ *                    operands of every (sequence, head) with their per-head
+ *                    power-of-two scales (TQ3/4/6: of R q) and the rope query
+ *                    terms (the matrix-core split kernels plan their T-split
+ *                    themselves);
  *   KVQ_STAGE_SPLITS the attention over every T-split (partial softmax states);
- *   KVQ_STAGE_MERGE  merge of the splits (+ TQ4 un-rotation) into out / lse. */
+ *   KVQ_STAGE_MERGE  merge of the splits (+ un-rotation for TQ3/4/6) into out / lse. */
 #define KVQ_STAGE_PREP 0
 #define KVQ_STAGE_SPLITS 1
 #define KVQ_STAGE_MERGE 2
@@ -242,7 +270,8 @@ int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, in
  *
  * kvq_gather_rows copies rows row_index[0 .. n_index) of a quantized cache
  * (codes, row_scale, k_rope: cache_rows rows; code bytes per row: 512 for
- * KVQ_QMODE_FP8, 256 for KVQ_QMODE_TQ4) unchanged to row i of codes_out,
+ * KVQ_QMODE_FP8, 256 for KVQ_QMODE_TQ4, 192 for KVQ_QMODE_TQ3, 384 for
+ * KVQ_QMODE_TQ6) unchanged to row i of codes_out,
  * scale_out and rope_out.
  *  - row_index: device int64.  An index outside [0, cache_rows) is clamped
  *    to the nearest valid row (0 or cache_rows - 1), so the call never reads

@@ -50,7 +50,7 @@ int launch_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUN
 
 int check_attn(const kvq_attn_args* a) {
     if (!a) return KVQ_ERR_INVALID_ARG;
-    if (a->qmode != KVQ_QMODE_FP8 && a->qmode != KVQ_QMODE_TQ4) return KVQ_ERR_UNSUPPORTED;
+    if (a->qmode != KVQ_QMODE_FP8 && !kvq::qmode_rotated(a->qmode)) return KVQ_ERR_UNSUPPORTED;
     if (a->precision != KVQ_PREC_MFMA && a->precision != KVQ_PREC_FP32) return KVQ_ERR_UNSUPPORTED;
     if (a->dim_lat != 512 || a->dim_rope != 64) return KVQ_ERR_UNSUPPORTED;
     if (a->n_seqs < 1 || a->n_heads < 1 || a->total_rows < 0 || a->split_rows < 0) return KVQ_ERR_INVALID_ARG;
@@ -59,7 +59,7 @@ int check_attn(const kvq_attn_args* a) {
     if (a->split_rows > 0 && a->split_rows % 32 != 0) return KVQ_ERR_INVALID_ARG;
     if (!a->seq_offsets || !a->q_lat || !a->q_rope || !a->out) return KVQ_ERR_INVALID_ARG;
     if (a->total_rows > 0 && (!a->codes || !a->row_scale || !a->k_rope)) return KVQ_ERR_INVALID_ARG;
-    if (a->qmode == KVQ_QMODE_TQ4 && !a->sign_mask) return KVQ_ERR_INVALID_ARG;
+    if (kvq::qmode_rotated(a->qmode) && !a->sign_mask) return KVQ_ERR_INVALID_ARG;
     if (!aligned(a->seq_offsets, 8) || !aligned16(a->codes) || !aligned(a->row_scale, 4) || !aligned16(a->k_rope) ||
         !aligned(a->q_lat, 4) || !aligned(a->q_rope, 4) || !aligned16(a->out) || !aligned(a->lse, 4))
         return KVQ_ERR_INVALID_ARG;
@@ -138,13 +138,18 @@ const char* kvq_status_string(int status) {
 
 int64_t kvq_row_bytes(int qmode, int dim) {
     if (qmode == KVQ_QMODE_FP8) return (dim >= 8 && dim <= 2048 && dim % 8 == 0) ? (int64_t)dim + 4 : -1;
-    if (qmode == KVQ_QMODE_TQ4) return (pow2(dim) && dim >= 8 && dim <= 512) ? (int64_t)dim / 2 + 4 : -1;
+    const int bits = kvq::qmode_bits(qmode);
+    if (bits) return (pow2(dim) && dim >= 8 && dim <= 512) ? (int64_t)dim * bits / 8 + 4 : -1;
     return -1;
 }
 
 int kvq_tq4_codebook(float* levels, float* thresholds) {
-    kvq::host_codebook(levels, thresholds);
+    kvq::host_codebook(4, levels, thresholds);
     return KVQ_OK;
+}
+
+int kvq_tq_codebook(int bits, float* levels, float* thresholds) {
+    return kvq::host_codebook(bits, levels, thresholds) > 0 ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
 }
 
 int kvq_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* codes, float* scales, void* stream) {
@@ -158,15 +163,21 @@ int kvq_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* codes, floa
     return launch_status(kvq::launch_encode_fp8(x, n_rows, dim, codes, scales, as_stream(stream)));
 }
 
-int kvq_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask, uint8_t* codes,
-                   float* radii, void* stream) {
+int kvq_encode_tq(int bits, const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask, uint8_t* codes,
+                  float* radii, void* stream) {
+    if (bits != 3 && bits != 4 && bits != 6) return KVQ_ERR_UNSUPPORTED;
     if (n_rows < 0 || dim <= 0) return KVQ_ERR_INVALID_ARG;
     if (!pow2(dim) || dim < 8 || dim > 512) return KVQ_ERR_UNSUPPORTED;
     if (n_rows == 0) return KVQ_OK;
     if (!x || !sign_mask || !codes || !radii) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned(codes, 4) || !aligned(radii, 4)) return KVQ_ERR_INVALID_ARG;
     if (n_rows > ((int64_t)1 << 40) / dim) return KVQ_ERR_UNSUPPORTED;
-    return launch_status(kvq::launch_encode_tq4(x, n_rows, dim, sign_mask, codes, radii, as_stream(stream)));
+    return launch_status(kvq::launch_encode_tq(bits, x, n_rows, dim, sign_mask, codes, radii, as_stream(stream)));
+}
+
+int kvq_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask, uint8_t* codes,
+                   float* radii, void* stream) {
+    return kvq_encode_tq(4, x, n_rows, dim, sign_mask, codes, radii, stream);
 }
 
 int kvq_append_q4_0(const kvq_q4_cache* cache, int n_seqs, const int32_t* pos0, const int64_t* src_off,
@@ -246,7 +257,7 @@ int kvq_decode_attn_stage(const kvq_attn_args* a, int stage, void* workspace, in
 int kvq_gather_rows(int qmode, const uint8_t* codes, const float* row_scale, const uint16_t* k_rope,
                     int64_t cache_rows, const int64_t* row_index, int64_t n_index, uint8_t* codes_out,
                     float* scale_out, uint16_t* rope_out, void* stream) {
-    if (qmode != KVQ_QMODE_FP8 && qmode != KVQ_QMODE_TQ4) return KVQ_ERR_UNSUPPORTED;
+    if (qmode != KVQ_QMODE_FP8 && !kvq::qmode_rotated(qmode)) return KVQ_ERR_UNSUPPORTED;
     if (n_index < 0 || cache_rows < 0) return KVQ_ERR_INVALID_ARG;
     if (n_index == 0) return KVQ_OK;
     if (cache_rows < 1 || !codes || !row_scale || !k_rope || !row_index || !codes_out || !scale_out || !rope_out)
@@ -255,7 +266,7 @@ int kvq_gather_rows(int qmode, const uint8_t* codes, const float* row_scale, con
         !aligned(row_scale, 4) || !aligned(scale_out, 4) || !aligned(row_index, 8))
         return KVQ_ERR_INVALID_ARG;
     if (n_index > ((int64_t)1 << 33)) return KVQ_ERR_UNSUPPORTED;  // grid of n_index / 4 workgroups
-    const int cb = qmode == KVQ_QMODE_TQ4 ? 256 : 512;
+    const int cb = kvq::code_bytes_512(qmode);
     return launch_status(kvq::launch_gather_rows(cb, codes, row_scale, k_rope, cache_rows, row_index, n_index,
                                                  codes_out, scale_out, rope_out, as_stream(stream)));
 }

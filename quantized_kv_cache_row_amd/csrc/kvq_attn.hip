@@ -10,18 +10,20 @@
 //   s_t = sm * (rho_t <q, c_t> + <q_rope, k_rope_t>),  p = softmax(s),
 //   o   = sum_t p_t rho_t c_t
 //
-// where c_t is the decoded code row (fp8: e4m3 values, rho_t = scale; TQ4: the
-// codebook levels, rho_t = radius / sqrt(512), q replaced by R q, and o
-// un-rotated by R^T after the merge).  The latent rows are never rebuilt.
+// where c_t is the decoded code row (fp8: e4m3 values, rho_t = scale; the
+// rotated codec at 3, 4 or 6 bits (TQ3/TQ4/TQ6): the codebook levels, rho_t =
+// radius / sqrt(512), q replaced by R q, and o un-rotated by R^T after the
+// merge).  The latent rows are never rebuilt.
 //
 // Pipeline (all on the caller's stream, no host synchronisation):
 //   prep  -- fp32 check path: k_plan (per-sequence T-split counts -> prefix)
-//            and, TQ4, k_qrot (R q in fp32); matrix-core path, TQ4:
-//            k_qprep_tq4 (R q as fp16 operands).  The matrix-core split
-//            kernels plan their chunk themselves, the fp8 one also prepares
-//            its query;
+//            and, rotated codec, k_qrot (R q in fp32); matrix-core path:
+//            k_qprep_fp8 / k_qprep_tq4 (the query as fp16 operands, R q for
+//            the rotated codec).  The matrix-core split kernels plan their
+//            chunk themselves;
 //   split -- k_attn_*: online softmax over every T-split, partial (m, l, O);
-//   merge -- k_merge: combine the splits, TQ4 un-rotation, write out / lse.
+//   merge -- k_merge / k_merge_f8: combine the splits (un-rotation for the
+//            rotated codec), write out / lse.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_codebook.inc"
@@ -31,6 +33,8 @@ namespace kvq {
 namespace {
 
 __constant__ uint32_t c_tq4_level[16] = KVQ_TQ4_LEVEL_BITS;
+__constant__ uint32_t c_tq3_level[8] = KVQ_TQ3_LEVEL_BITS;
+__constant__ uint32_t c_tq6_level[64] = KVQ_TQ6_LEVEL_BITS;
 
 constexpr int DL = 512;  // latent width
 constexpr int DR = 64;   // rope width
@@ -42,9 +46,11 @@ constexpr int F32_HEADS = 8;      // fp32 path: heads per workgroup
 constexpr int MF_HEADS = 16;      // matrix-core path: heads per workgroup (one MFMA N block)
 constexpr int MF_WAVES = 4;       // matrix-core path: waves per workgroup, splitting the rows
 constexpr int MF_TILE = 32;       // rows per wave tile
-constexpr int TQ4_HEADS = 64;    // TQ4 matrix-core path: heads per workgroup (4 waves x 16)
-constexpr int QPACK_U4 = 80;      // TQ4: uint4 per prepared query (fp16 latent 64, rope hi 8, rope lo 8)
+constexpr int TQ_HEADS = 64;      // rotated codec, matrix-core path: heads per workgroup (4 waves x 16)
+constexpr int QPACK_U4 = 80;      // fp8: uint4 per prepared query (fp16 latent 64, rope hi 8, rope lo 8)
 constexpr int QP_RH = 64, QP_RL = 72;
+constexpr int QPACK_TQ = 144;     // rotated codec: the same, then the fp16 latent remainder (64)
+constexpr int QP_LL = 80;
 constexpr int F8_HEADS = 32;      // fp8 matrix-core path: heads per workgroup (one 32x32 MFMA N block)
 constexpr int F8_TILE = 128;      // fp8 matrix-core path: rows per workgroup tile (32 per wave)
 constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
@@ -52,8 +58,9 @@ constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators a
 
 struct Plan {
     int64_t* chunk_prefix;  // [n_seqs + 1]
-    float* q_rot;           // fp32 path, TQ4: [n_seqs][H][512]
-    uint4* q_pack;          // matrix-core paths: [n_seqs][H padded][QPACK_U4] (fp8: in operand order per group)
+    float* q_rot;           // fp32 path, rotated codec: [n_seqs][H][512]
+    uint4* q_pack;          // matrix-core paths: [n_seqs][H padded][QPACK_U4 (fp8, in operand order per
+                            // group) or QPACK_TQ]
     float* q_inv;           // matrix-core paths: [n_seqs][H padded]
     float* part_m;          // [max_chunks][H]
     float* part_l;          // [max_chunks][H]
@@ -70,10 +77,10 @@ struct Plan {
 
 int auto_split_rows(const kvq_attn_args& a) {
     if (a.precision == KVQ_PREC_FP32) return 512;
-    if (a.qmode == KVQ_QMODE_TQ4) {
+    if (qmode_rotated(a.qmode)) {
         // one workgroup per compute unit over all splits and groups of 64 heads,
         // whole tiles, at least 8 tiles per split
-        const int64_t groups = (a.n_heads + TQ4_HEADS - 1) / TQ4_HEADS;
+        const int64_t groups = (a.n_heads + TQ_HEADS - 1) / TQ_HEADS;
         int64_t split = (a.total_rows * groups + 255) / 256;
         if (split < 8 * MF_TILE) split = 8 * MF_TILE;
         split = (split + MF_TILE - 1) / MF_TILE * MF_TILE;
@@ -96,7 +103,7 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     Plan p{};
     p.split_rows = a.split_rows > 0 ? a.split_rows : auto_split_rows(a);
     const bool f32 = a.precision == KVQ_PREC_FP32;
-    p.heads_per_group = f32 ? F32_HEADS : (a.qmode == KVQ_QMODE_TQ4 ? TQ4_HEADS : F8_HEADS);
+    p.heads_per_group = f32 ? F32_HEADS : (qmode_rotated(a.qmode) ? TQ_HEADS : F8_HEADS);
     p.n_groups = (a.n_heads + p.heads_per_group - 1) / p.heads_per_group;
     p.heads_padded = p.n_groups * p.heads_per_group;
     // sum_s max(1, ceil(T_s / split)) over T_s summing to at most total_rows is at
@@ -115,10 +122,10 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
         return q;
     };
     p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
-    if (f32 && a.qmode == KVQ_QMODE_TQ4) p.q_rot = (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
+    if (f32 && qmode_rotated(a.qmode)) p.q_rot = (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
     if (!f32) {  // matrix-core paths: the prepared query operands
         const int64_t rows_q = (int64_t)a.n_seqs * p.heads_padded;
-        p.q_pack = (uint4*)take(sizeof(uint4) * rows_q * QPACK_U4);
+        p.q_pack = (uint4*)take(sizeof(uint4) * rows_q * (qmode_rotated(a.qmode) ? QPACK_TQ : QPACK_U4));
         p.q_inv = (float*)take(sizeof(float) * rows_q);
     }
     p.part_m = (float*)take(sizeof(float) * p.max_chunks * a.n_heads);
@@ -175,7 +182,7 @@ __device__ __forceinline__ int find_chunk_seq(const int64_t* __restrict__ cp, in
     return lo;
 }
 
-// ---- 1a. TQ4 query rotation (fp32 path) ----------------------------------------------------------
+// ---- 1a. query rotation of the rotated codec (fp32 path) ----------------------------------------------------------
 // One wave per (sequence, head): q~ = H (D q) / sqrt(512), 8 consecutive per lane.
 __global__ __launch_bounds__(256) void k_qrot(const float* __restrict__ q, const uint8_t* __restrict__ sign_mask,
                                              int64_t n_rows, float* __restrict__ q_rot) {
@@ -205,12 +212,23 @@ __global__ __launch_bounds__(256) void k_qrot(const float* __restrict__ q, const
     for (int i = 0; i < 8; i++) dst[i] = v[i] * INV_SQRT_DL;
 }
 
-// Decoded value of element i of a code row (fp8: e4m3 value, TQ4: codebook level).
+// Decoded value of element i of a code row (fp8: e4m3 value; rotated codec:
+// codebook level of index i, bits B*i .. B*i + B - 1 of the row's little-endian
+// bit stream).  The second byte is read only when the index crosses into it, so
+// the last index of a row reads nothing past the row.
 template <int QMODE>
 __device__ __forceinline__ float code_value(const uint8_t* __restrict__ row, int i) {
     if (QMODE == KVQ_QMODE_FP8) return e4m3_to_f32(row[i]);
-    const uint32_t b = row[i >> 1];
-    return u2f(c_tq4_level[(i & 1) ? (b >> 4) : (b & 15u)]);
+    if (QMODE == KVQ_QMODE_TQ4) {
+        const uint32_t b = row[i >> 1];
+        return u2f(c_tq4_level[(i & 1) ? (b >> 4) : (b & 15u)]);
+    }
+    constexpr int B = QMODE == KVQ_QMODE_TQ3 ? 3 : 6;
+    const int pos = B * i, sh = pos & 7;
+    uint32_t w = row[pos >> 3];
+    if (sh + B > 8) w |= (uint32_t)row[(pos >> 3) + 1] << 8;
+    const uint32_t idx = (w >> sh) & ((1u << B) - 1u);
+    return u2f(B == 3 ? c_tq3_level[idx] : c_tq6_level[idx]);
 }
 
 // ---- 2a. fp32 check path ----------------------------------------------------------------
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(kvq_attn_args a, Plan p, const
         qr_s[hh][d] = hh < nh ? a.q_rope[((int64_t)s * a.n_heads + h0 + hh) * DR + d] : 0.0f;
     }
     __syncthreads();
-    const int cb = QMODE == KVQ_QMODE_FP8 ? DL : DL / 2;  // code bytes per row
+    constexpr int cb = QMODE == KVQ_QMODE_FP8 ? DL : DL * (QMODE == KVQ_QMODE_TQ3 ? 3 : QMODE == KVQ_QMODE_TQ6 ? 6 : 4) / 8;
     const int ph = tid >> 5, pd = (tid & 31) * 16;       // PV ownership
     float m_run[F32_HEADS], l_run[F32_HEADS];
 #pragma unroll
@@ -256,7 +274,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(kvq_attn_args a, Plan p, const
         if (tid < nt) {
             const int64_t t = t0 + tid;
             rho = a.row_scale[t];
-            if (QMODE == KVQ_QMODE_TQ4) rho *= INV_SQRT_DL;
+            if (QMODE != KVQ_QMODE_FP8) rho *= INV_SQRT_DL;
             const uint8_t* row = a.codes + t * cb;
             float dot[F32_HEADS], dr[F32_HEADS];
 #pragma unroll
@@ -421,6 +439,19 @@ __device__ __forceinline__ Tq4Lut make_tq4_lut() {
     return t;
 }
 
+// The 3-bit codebook in the same form: its 4 positive levels (index 4 + m) at
+// m = 0 .. 3 (entries 4 .. 7 unused).
+__device__ __forceinline__ Tq4Lut make_tq3_lut() {
+    Tq4Lut t{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const uint32_t h = f16_bits(u2f(c_tq3_level[4 + m]));
+        t.lo03 |= (h & 0xFF) << (8 * m);
+        t.hi03 |= (h >> 8) << (8 * m);
+    }
+    return t;
+}
+
 // 8 nibble indices (element k = nibble k of x) -> 8 fp16 codebook levels.  The
 // codebook is symmetric: index i >= 8 is +level[i], index i < 8 is
 // -level[15 - i]; the magnitude comes from a byte table lookup (v_perm).
@@ -440,6 +471,34 @@ __device__ __forceinline__ uint4 tq4x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
                       __builtin_amdgcn_perm(bo, be, 0x05040100u), __builtin_amdgcn_perm(bo, be, 0x07060302u));
 }
 
+
+// 8 three-bit indices (element k = bits 3k .. 3k + 2 of x) -> 8 fp16 levels of
+// the 8-level codebook: each index i is spread to nibble k as i + 4, which
+// tq4x8_to_f16x8 reads as sign (i >= 4) and magnitude index (i - 4 or 3 - i),
+// the symmetric layout of the 8 levels.
+__device__ __forceinline__ uint4 tq3x8_to_f16x8(uint32_t x, const Tq4Lut& t) {
+    const uint32_t y = (x & 0xFFFu) | ((x & 0xFFF000u) << 4);  // elements 4..7 to the upper half
+    const uint32_t n = (y & 0x00070007u) | ((y & 0x00380038u) << 1) | ((y & 0x01C001C0u) << 2) |
+                       ((y & 0x0E000E00u) << 3);
+    return tq4x8_to_f16x8(n + 0x44444444u, t);
+}
+
+// 8 six-bit indices (element k = bits 6k .. 6k + 5 of the 48-bit x) -> 8 fp16
+// levels of the 64-level codebook: index i >= 32 is +level[i], i < 32 is
+// -level[63 - i]; the magnitude comes from lane m of tab (lane l holds the
+// fp16 bits of level 32 + l % 32) through ds_bpermute.  All 64 lanes must be
+// active.
+__device__ __forceinline__ uint4 tq6x8_to_f16x8(uint64_t x, uint32_t tab) {
+    uint32_t h[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const uint32_t i = (uint32_t)(x >> (6 * k)) & 63u;
+        const uint32_t neg = (i >> 5) ^ 1u;
+        const uint32_t m = (i & 31u) ^ (neg * 31u);
+        h[k] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(m << 2), (int)tab) | (neg << 15);
+    }
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
@@ -924,10 +983,13 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     }
 }
 
-// TQ4 query preparation: q~ = H D q / sqrt(512) for every (sequence, head),
-// scaled by a power of two qs (max |q~| * qs in [256, 512)) and rounded to
-// fp16, in the split kernel's operand layout: uint4 16 g + ks holds dims
-// 32 ks + 8 g .. + 7; the rope query (times sm_scale * log2(e)) as bf16 hi
+// Rotated-codec query preparation: q~ = H D q / sqrt(512) for every
+// (sequence, head), scaled by a power of two qs (max |q~| * qs in [256, 512))
+// and split into two fp16 terms, hi = fp16(q~ qs) and lo = fp16(q~ qs - hi)
+// (about 22 significant bits together; one fp16 term alone moves sharply
+// peaked softmaxes by up to 3e-3 of the output), in the split kernel's operand
+// layout: uint4 16 g + ks holds hi of dims 32 ks + 8 g .. + 7, uint4 QP_LL +
+// 16 g + ks their lo; the rope query (times sm_scale * log2(e)) as bf16 hi
 // (uint4 QP_RH + 2 g + k) and lo (QP_RL + 2 g + k) terms of dims 32 k + 8 g ..
 // + 7; 1 / qs in q_inv.  One wave per (sequence, head); lane l rotates dims
 // 8 l .. 8 l + 7 (three butterfly stages in registers, six across lanes).
@@ -977,9 +1039,18 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
     }
     qmax = wave_max(qmax);
     const float qs = pow2_scale_for(qmax, 8);
-    uint4* dst = p.q_pack + row * QPACK_U4;
-    dst[16 * (lane & 3) + (lane >> 2)] = make_uint4(pack_f16x2(v[0] * qs, v[1] * qs), pack_f16x2(v[2] * qs, v[3] * qs),
-                                                    pack_f16x2(v[4] * qs, v[5] * qs), pack_f16x2(v[6] * qs, v[7] * qs));
+    uint4* dst = p.q_pack + row * QPACK_TQ;
+    float hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float x = v[i] * qs;  // exact (a power of two)
+        hi[i] = (float)(_Float16)x;
+        lo[i] = x - hi[i];          // exact in fp32
+    }
+    dst[16 * (lane & 3) + (lane >> 2)] = make_uint4(pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]),
+                                                    pack_f16x2(hi[4], hi[5]), pack_f16x2(hi[6], hi[7]));
+    dst[QP_LL + 16 * (lane & 3) + (lane >> 2)] = make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                            pack_f16x2(lo[4], lo[5]), pack_f16x2(lo[6], lo[7]));
     if (lane < 8) {  // rope dims 8 lane .. + 7: k-step lane / 4, lane group lane % 4
         const float c2r = valid ? a.sm_scale * LOG2E : 0.0f;
         const float rv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
@@ -997,13 +1068,13 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
     if (lane == 0) p.q_inv[row] = 1.0f / qs;  // exact
 }
 
-// TQ4 split kernel.  Work item = (T-chunk, group of 64 heads); the items are
-// dealt to XCDs in contiguous runs so the head groups of a chunk share one
-// L2.  All 4 waves of a workgroup step through the chunk's tiles (32 rows)
-// together, wave w for heads 16 w .. 16 w + 15: the nibble codes of a tile
-// are decoded once per workgroup -- each wave decodes 8 rows into a shared,
-// double-buffered fp16 LDS tile (rope keys and row scales next to it) -- and
-// every wave then reads the whole tile:
+// Rotated-codec split kernel (BITS = 3, 4, 6).  Work item = (T-chunk, group of
+// 64 heads); the items are dealt to XCDs in contiguous runs so the head groups
+// of a chunk share one L2.  All 4 waves of a workgroup step through the
+// chunk's tiles (32 rows) together, wave w for heads 16 w .. 16 w + 15: the
+// codes of a tile are decoded once per workgroup -- each wave decodes 8 rows
+// into a shared, double-buffered fp16 LDS tile (rope keys and row scales next
+// to it) -- and every wave then reads the whole tile:
 //   score:  S^T (16 rows x 16 heads) += X(rows, k) q~^T, X from the tile
 //           (lane (g, n): row 16 rb + n, dims 32 ks + 8 g .. + 7);
 //   PV:     O^T (16 dims x 16 heads) += X^T P'^T, X^T via ds_read_b64_tr_b16
@@ -1017,7 +1088,8 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
 // partial per (chunk, head), written by the wave that owns the head.
 constexpr int XT = DL + 8;                // halfwords per fp16 tile row (rows 4 banks apart)
 constexpr int KT = DR + 8;                // halfwords per rope tile row
-__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a, Plan p) {
+template <int BITS>
+__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) uint16_t xt[2][MF_TILE][XT];  // decoded latent rows, fp16
     __shared__ __align__(16) uint16_t kt[2][MF_TILE][KT];  // rope keys, bf16
     __shared__ __align__(16) float rho_s[2][MF_TILE];      // radius / sqrt(512)
@@ -1031,42 +1103,83 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
     if (c >= p.max_chunks) return;
-    const int head = hg * TQ4_HEADS + MF_HEADS * wave + n;  // may exceed n_heads (its query is zero)
-    constexpr int CB = DL / 2;                                 // code bytes per row
+    const int head = hg * TQ_HEADS + MF_HEADS * wave + n;  // may exceed n_heads (its query is zero)
+    constexpr int CB = DL * BITS / 8;                         // code bytes per row
     int64_t r0, r1;
     int sq;
     if (!locate_chunk(a, p, c, plan_s, wave, lane, r0, r1, sq)) return;  // workgroup-uniform
     const int ntiles = (int)((r1 - r0 + MF_TILE - 1) / MF_TILE);
 
     // decode share of this wave: tile row 8 wave + lane / 8, code bytes
-    // 32 (lane % 8) .. + 31 (dims 64 (lane % 8) .. + 63), rope bytes 16 (lane % 8)
+    // 8 BITS (lane % 8) .. + 8 BITS - 1 (dims 64 (lane % 8) .. + 63), rope bytes
+    // 16 (lane % 8).  Group i of 8 dims is bits 8 BITS i .. of the lane's words.
     const int drow = 8 * wave + (lane >> 3), dq = lane & 7;
-    uint4 ca[2], cr;  // codes and rope of the tile to decode next
-    float cs;         // its row radius (scaled by 1 / sqrt(512) when it is stored)
+    uint4 cv[3];  // codes of the tile to decode next (BITS * 2 words)
+    uint4 cr;     // its rope keys
+    float cs;     // its row radius (scaled by 1 / sqrt(512) when it is stored)
     auto load_share = [&](int t) __attribute__((always_inline)) {
         const int64_t t0 = r0 + (int64_t)MF_TILE * t;
         const int64_t row = t0 + min(drow, (int)(r1 - t0) - 1);  // rows past the chunk re-read its last row
-        const uint8_t* cp = a.codes + row * CB + 32 * dq;
-        ca[0] = *reinterpret_cast<const uint4*>(cp);
-        ca[1] = *reinterpret_cast<const uint4*>(cp + 16);
+        const uint8_t* cp = a.codes + row * CB + 8 * BITS * dq;
+        if constexpr (BITS == 3) {  // 24 bytes, 8-byte aligned
+            const uint2 v0 = *reinterpret_cast<const uint2*>(cp);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(cp + 8);
+            const uint2 v2 = *reinterpret_cast<const uint2*>(cp + 16);
+            cv[0] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+            cv[1] = make_uint4(v2.x, v2.y, 0u, 0u);
+        } else {  // 32 or 48 bytes, 16-byte aligned
+            cv[0] = *reinterpret_cast<const uint4*>(cp);
+            cv[1] = *reinterpret_cast<const uint4*>(cp + 16);
+            if constexpr (BITS == 6) cv[2] = *reinterpret_cast<const uint4*>(cp + 32);
+        }
         cr = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 8 * dq);
         cs = a.row_scale[row];
     };
-    const Tq4Lut lut = make_tq4_lut();
+    const Tq4Lut lut = BITS == 3 ? make_tq3_lut() : make_tq4_lut();
+    const uint32_t tab6 = BITS == 6 ? f16_bits(u2f(c_tq6_level[32 + (lane & 31)])) : 0u;
     auto decode_share = [&](int buf) __attribute__((always_inline)) {
-        const uint32_t w[8] = {ca[0].x, ca[0].y, ca[0].z, ca[0].w, ca[1].x, ca[1].y, ca[1].z, ca[1].w};
+        uint16_t* dst = &xt[buf][drow][64 * dq];
+        auto put = [&](int i, uint4 h) __attribute__((always_inline)) {
+            *reinterpret_cast<uint4*>(dst + 8 * i) = h;
+        };
+        if constexpr (BITS == 4) {
+            const uint32_t w[8] = {cv[0].x, cv[0].y, cv[0].z, cv[0].w, cv[1].x, cv[1].y, cv[1].z, cv[1].w};
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            *reinterpret_cast<uint4*>(&xt[buf][drow][64 * dq + 8 * i]) = tq4x8_to_f16x8(w[i], lut);
+            for (int i = 0; i < 8; i++) put(i, tq4x8_to_f16x8(w[i], lut));
+        } else if constexpr (BITS == 3) {
+            // group i = bits 24 i .. 24 i + 23 of the words w0 .. w5
+            const uint32_t w0 = cv[0].x, w1 = cv[0].y, w2 = cv[0].z, w3 = cv[0].w, w4 = cv[1].x, w5 = cv[1].y;
+            put(0, tq3x8_to_f16x8(w0 & 0xFFFFFFu, lut));
+            put(1, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFFFFu, lut));
+            put(2, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w2, w1, 16) & 0xFFFFFFu, lut));
+            put(3, tq3x8_to_f16x8(w2 >> 8, lut));
+            put(4, tq3x8_to_f16x8(w3 & 0xFFFFFFu, lut));
+            put(5, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w4, w3, 24) & 0xFFFFFFu, lut));
+            put(6, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w5, w4, 16) & 0xFFFFFFu, lut));
+            put(7, tq3x8_to_f16x8(w5 >> 8, lut));
+        } else {
+            // groups 2k and 2k + 1 = bits 0 .. 47 and 48 .. 95 of words 3k .. 3k + 2
+            auto pair = [&](int k, uint32_t a0, uint32_t a1, uint32_t a2) __attribute__((always_inline)) {
+                put(2 * k, tq6x8_to_f16x8((uint64_t)a0 | ((uint64_t)(a1 & 0xFFFFu) << 32), tab6));
+                put(2 * k + 1, tq6x8_to_f16x8((uint64_t)(a1 >> 16) | ((uint64_t)a2 << 16), tab6));
+            };
+            pair(0, cv[0].x, cv[0].y, cv[0].z);
+            pair(1, cv[0].w, cv[1].x, cv[1].y);
+            pair(2, cv[1].z, cv[1].w, cv[2].x);
+            pair(3, cv[2].y, cv[2].z, cv[2].w);
+        }
         *reinterpret_cast<uint4*>(&kt[buf][drow][8 * dq]) = cr;
         rho_s[buf][drow] = cs * INV_SQRT_DL;  // the 8 lanes of a row store the same value
     };
     // ---- query operands (prepared once per sequence and head), loaded first: the
     // row-scale loop below waits for its loads, and with them for these
-    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + head) * QPACK_U4;
-    uint4 qh[16], rh[2], rl[2];
+    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + head) * QPACK_TQ;
+    uint4 qh[16], qo[16], rh[2], rl[2];
 #pragma unroll
-    for (int k = 0; k < 16; k++) qh[k] = qp[16 * g + k];
+    for (int k = 0; k < 16; k++) {
+        qh[k] = qp[16 * g + k];
+        qo[k] = qp[QP_LL + 16 * g + k];
+    }
 #pragma unroll
     for (int k = 0; k < 2; k++) {
         rh[k] = qp[QP_RH + 2 * g + k];
@@ -1123,7 +1236,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
         // ---- scores S^T (two row blocks) from the tile: four independent
         // accumulator chains (row block x even / odd k-step), reads one step ahead
         f32x4_t sl[2], sr[2], sx[2];
-        sl[0] = sl[1] = sr[0] = sr[1] = sx[0] = sx[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4_t sq[2];  // the query's fp16 remainder terms
+        sl[0] = sl[1] = sr[0] = sr[1] = sx[0] = sx[1] = sq[0] = sq[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         {
             const uint16_t* xa = &xt[buf][n][8 * g];
             const uint16_t* xb = &xt[buf][16 + n][8 * g];
@@ -1139,6 +1253,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
                 f32x4_t& s1 = (ks & 1) ? sx[1] : sl[1];
                 s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qh[ks]), s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qh[ks]), s1, 0, 0, 0);
+                sq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qo[ks]), sq[0], 0, 0, 0);
+                sq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qo[ks]), sq[1], 0, 0, 0);
             }
 #pragma unroll
             for (int rb = 0; rb < 2; rb++) {
@@ -1150,6 +1266,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
                     sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
                 }
                 sl[rb] += sx[rb];
+                sl[rb] += sq[rb];
             }
         }
         // ---- softmax: lane (g, n) holds rows 16 rb + 4 g + r of head n (no branches)
@@ -1244,7 +1361,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq4(kvq_attn_args a
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int k = 0; k < MF_HEADS; k++) {
-            const int h = hg * TQ4_HEADS + MF_HEADS * wave + k;
+            const int h = hg * TQ_HEADS + MF_HEADS * wave + k;
             if (h < a.n_heads)
                 *reinterpret_cast<float4*>(p.part_o + (c * a.n_heads + h) * DL + DL / 2 * hf + 4 * lane) =
                     *reinterpret_cast<const float4*>(stg + k * SR + 4 * lane);
@@ -1453,20 +1570,20 @@ int64_t attn_workspace_bytes(const kvq_attn_args& a) { return plan_bytes(a); }
 hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws, hipStream_t st) {
     Plan p = make_plan(a, ws, nullptr);
     const bool f32 = a.precision == KVQ_PREC_FP32;
-    const bool tq4 = a.qmode == KVQ_QMODE_TQ4;
+    const bool tq = qmode_rotated(a.qmode);
     switch (stage) {
         case KVQ_STAGE_PREP:
             // the matrix-core split kernels plan their chunk themselves; their
-            // query operands are prepared here once per head (TQ4: rotated)
+            // query operands are prepared here once per head (rotated codec: R q)
             if (!f32) {
                 const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
-                if (tq4) hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
+                if (tq) hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
                 else hipLaunchKernelGGL(k_qprep_fp8, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
                 break;
             }
             hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a.seq_offsets, a.n_seqs, p.split_rows, a.total_rows,
                                p.chunk_prefix);
-            if (tq4) {
+            if (tq) {
                 const int64_t rows = (int64_t)a.n_seqs * a.n_heads;
                 hipLaunchKernelGGL(k_qrot, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a.q_lat, a.sign_mask,
                                    rows, p.q_rot);
@@ -1475,13 +1592,21 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
         case KVQ_STAGE_SPLITS:
             if (f32) {
                 const dim3 grid((unsigned)p.max_chunks, (unsigned)p.n_groups);
-                const float* qsrc = tq4 ? p.q_rot : a.q_lat;
-                if (tq4) hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_TQ4>, grid, dim3(256), 0, st, a, p, qsrc);
-                else hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p, qsrc);
+                const float* qsrc = tq ? p.q_rot : a.q_lat;
+                switch (a.qmode) {
+                    case KVQ_QMODE_TQ4: hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_TQ4>, grid, dim3(256), 0, st, a, p, qsrc); break;
+                    case KVQ_QMODE_TQ3: hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_TQ3>, grid, dim3(256), 0, st, a, p, qsrc); break;
+                    case KVQ_QMODE_TQ6: hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_TQ6>, grid, dim3(256), 0, st, a, p, qsrc); break;
+                    default: hipLaunchKernelGGL(k_attn_f32<KVQ_QMODE_FP8>, grid, dim3(256), 0, st, a, p, qsrc); break;
+                }
             } else {
                 const dim3 grid((unsigned)(p.chunks_per_xcd * N_XCD * p.n_groups));
-                if (tq4) hipLaunchKernelGGL(k_attn_mfma_tq4, grid, dim3(MF_WAVES * 64), 0, st, a, p);
-                else hipLaunchKernelGGL(k_attn_mfma_fp8, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+                switch (a.qmode) {
+                    case KVQ_QMODE_TQ4: hipLaunchKernelGGL(k_attn_mfma_tq<4>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
+                    case KVQ_QMODE_TQ3: hipLaunchKernelGGL(k_attn_mfma_tq<3>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
+                    case KVQ_QMODE_TQ6: hipLaunchKernelGGL(k_attn_mfma_tq<6>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
+                    default: hipLaunchKernelGGL(k_attn_mfma_fp8, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
+                }
             }
             break;
         default: {
@@ -1490,7 +1615,7 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
             // a single one (one thread per float4 column) when there are few
             const bool wide = p.max_chunks >= 16 * (int64_t)a.n_seqs;
             const bool narrow = p.max_chunks <= 4 * (int64_t)a.n_seqs;
-            if (tq4) {
+            if (tq) {
                 if (!f32 && wide) hipLaunchKernelGGL((k_merge<true, true, 1024>), dim3((unsigned)items), dim3(1024), 0, st, a, p);
                 else if (!f32 && narrow) hipLaunchKernelGGL((k_merge<true, true, 128>), dim3((unsigned)items), dim3(128), 0, st, a, p);
                 else if (!f32) hipLaunchKernelGGL((k_merge<true, true, 256>), dim3((unsigned)items), dim3(256), 0, st, a, p);

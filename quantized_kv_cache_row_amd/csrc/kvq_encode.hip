@@ -5,7 +5,9 @@
 //      per row, round to nearest even.
 // TQ4: same page, "Why rotated-int4 for the 4-bit tier": random sign flips,
 //      a Walsh-Hadamard rotation, one radius per row and indices into a fixed
-//      16-level Lloyd-Max codebook scaled by radius / sqrt(n).
+//      16-level Lloyd-Max codebook scaled by radius / sqrt(n); the 3- and 6-bit
+//      tiers (TQ3, TQ6: the .coli_kv reply and the teacher-forcing table) are the
+//      same codec with the 8- and 64-level codebooks.
 //
 // fp8: one wave per row, 8 consecutive fp32 per lane loaded as two 16-byte
 // loads, codes stored as one 8-byte store per lane, so every wave instruction
@@ -24,6 +26,8 @@ namespace kvq {
 namespace {
 
 __constant__ uint32_t c_tq4_thresh[15] = KVQ_TQ4_THRESH_BITS;
+__constant__ uint32_t c_tq3_thresh[7] = KVQ_TQ3_THRESH_BITS;
+__constant__ uint32_t c_tq6_thresh[63] = KVQ_TQ6_THRESH_BITS;
 
 constexpr int ENC_WAVES = 4;  // waves per workgroup
 
@@ -94,15 +98,28 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float
     if (lane == 0) scales[row] = s;
 }
 
-// ---- TQ4 -------------------------------------------------------------------
+// ---- rotated codec, any width ------------------------------------------------------
 // L = dim/8 lanes per row (1..64), 64/L rows per wave, 8 consecutive elements
 // per lane.  FWHT stages h = 1, 2, 4 in registers, h >= 8 across lanes
 // (partner lane ^ h/8); the same (a+b, a-b) data flow as the definition, so the
 // result is bit-identical to any other evaluation in that stage order.
-__global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4(const float* __restrict__ x, int64_t n_rows,
-                                                                     int dim, const uint8_t* __restrict__ sign_mask,
-                                                                     uint8_t* __restrict__ codes,
-                                                                     float* __restrict__ radii) {
+// BITS = 4: nibbles, one 4-byte store per lane.  BITS = 3, 6: the lane's 8
+// indices are 3 or 6 bytes of the row's little-endian bit stream (index i in
+// bits BITS*i ..), found by a binary search over the 2^BITS - 1 thresholds in
+// LDS: T_k = fl(t_k * r) is ascending in k (or, for a radius of inf or NaN, the
+// comparisons w > T_k are still true for a prefix of k), so the search returns
+// #{k : w > T_k} exactly.
+template <int BITS>
+__global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq(const float* __restrict__ x, int64_t n_rows,
+                                                                    int dim, const uint8_t* __restrict__ sign_mask,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    float* __restrict__ radii) {
+    constexpr int NL = 1 << BITS;  // levels
+    __shared__ float th_s[NL];
+    if (BITS != 4) {
+        if (threadIdx.x < NL - 1) th_s[threadIdx.x] = u2f(BITS == 3 ? c_tq3_thresh[threadIdx.x] : c_tq6_thresh[threadIdx.x]);
+        __syncthreads();
+    }
     const int L = dim >> 3;
     const int lane = threadIdx.x & (KVQ_WAVE - 1);
     const int j = lane & (L - 1);                      // lane within the row
@@ -183,6 +200,32 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4(const float
             if (L > 16) stage(std::integral_constant<int, 16>{});
             if (L > 32) stage(std::integral_constant<int, 32>{});
         }
+        if constexpr (BITS != 4) {
+            uint64_t packed = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const float w = v[i];
+                uint32_t idx = 0;
+#pragma unroll
+                for (int step = NL / 2; step >= 1; step >>= 1) idx += (w > th_s[idx + step - 1] * rad) ? step : 0;
+                packed |= (uint64_t)idx << (BITS * i);
+            }
+            if (valid) {
+                uint8_t* cr = codes + row * (int64_t)(dim * BITS / 8) + BITS * j;
+                if (BITS == 3) {
+                    cr[0] = (uint8_t)packed;
+                    cr[1] = (uint8_t)(packed >> 8);
+                    cr[2] = (uint8_t)(packed >> 16);
+                } else {  // 6 bytes at an even offset
+                    uint16_t* c2 = reinterpret_cast<uint16_t*>(cr);
+                    c2[0] = (uint16_t)packed;
+                    c2[1] = (uint16_t)(packed >> 16);
+                    c2[2] = (uint16_t)(packed >> 32);
+                }
+                if (j == 0) radii[row] = rad;
+            }
+            continue;
+        }
         // bucketize against fl(t_k * r): idx = #{k : w > T_k}
         float T[15];
 #pragma unroll
@@ -212,7 +255,7 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4(const float
 }
 
 // ---- TQ4, dim 512 --------------------------------------------------------------
-// The same result as k_encode_tq4 with fewer vector instructions per row
+// The same result as k_encode_tq<4> with fewer vector instructions per row
 // (the general kernel spends about 500 per 512-wide row, so it is bound by the
 // vector ALU rather than by HBM):
 //  - 16 lanes per row, 4 rows per wave.  Lane u of a row holds column
@@ -428,13 +471,19 @@ __global__ void k_convert(int kind, const void* __restrict__ in, int64_t n, void
 
 }  // namespace
 
-void host_codebook(float* levels16, float* thresholds15) {
-    static const uint32_t lv[16] = KVQ_TQ4_LEVEL_BITS;
-    static const uint32_t th[15] = KVQ_TQ4_THRESH_BITS;
-    if (levels16)
-        for (int k = 0; k < 16; k++) std::memcpy(&levels16[k], &lv[k], 4);
-    if (thresholds15)
-        for (int k = 0; k < 15; k++) std::memcpy(&thresholds15[k], &th[k], 4);
+int host_codebook(int bits, float* levels, float* thresholds) {
+    static const uint32_t lv3[8] = KVQ_TQ3_LEVEL_BITS, th3[7] = KVQ_TQ3_THRESH_BITS;
+    static const uint32_t lv4[16] = KVQ_TQ4_LEVEL_BITS, th4[15] = KVQ_TQ4_THRESH_BITS;
+    static const uint32_t lv6[64] = KVQ_TQ6_LEVEL_BITS, th6[63] = KVQ_TQ6_THRESH_BITS;
+    const uint32_t* lv = bits == 3 ? lv3 : bits == 4 ? lv4 : bits == 6 ? lv6 : nullptr;
+    const uint32_t* th = bits == 3 ? th3 : bits == 4 ? th4 : bits == 6 ? th6 : nullptr;
+    if (!lv) return -1;
+    const int n = 1 << bits;
+    if (levels)
+        for (int k = 0; k < n; k++) std::memcpy(&levels[k], &lv[k], 4);
+    if (thresholds)
+        for (int k = 0; k < n - 1; k++) std::memcpy(&thresholds[k], &th[k], 4);
+    return n;
 }
 
 hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* codes, float* scales,
@@ -451,10 +500,10 @@ hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* c
     return hipGetLastError();
 }
 
-hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
-                             uint8_t* codes, float* radii, hipStream_t st) {
+hipError_t launch_encode_tq(int bits, const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
+                            uint8_t* codes, float* radii, hipStream_t st) {
     if (n_rows == 0) return hipSuccess;
-    if (dim == 512) {
+    if (dim == 512 && bits == 4) {
         const int64_t waves = (n_rows + D512_ROWS - 1) / D512_ROWS;
         int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;
         if (wgs > 1280) wgs = 1280;  // the resident count (5 per CU at 86 VGPRs); the kernel strides
@@ -467,7 +516,9 @@ hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int dim, const uint
     int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;
     if (wgs > 4096) wgs = 4096;  // 16 waves per CU; the kernel strides over the rest
     const dim3 grid((unsigned)wgs), block(ENC_WAVES * KVQ_WAVE);
-    hipLaunchKernelGGL(k_encode_tq4, grid, block, 0, st, x, n_rows, dim, sign_mask, codes, radii);
+    if (bits == 3) hipLaunchKernelGGL(k_encode_tq<3>, grid, block, 0, st, x, n_rows, dim, sign_mask, codes, radii);
+    else if (bits == 6) hipLaunchKernelGGL(k_encode_tq<6>, grid, block, 0, st, x, n_rows, dim, sign_mask, codes, radii);
+    else hipLaunchKernelGGL(k_encode_tq<4>, grid, block, 0, st, x, n_rows, dim, sign_mask, codes, radii);
     return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ namespace {
 // (each piece 256-byte aligned), then the dense call's workspace
 int64_t sparse_compact_bytes(const kvq_attn_args& a) {
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
-    const int64_t n = a.total_rows, cb = a.qmode == KVQ_QMODE_TQ4 ? 256 : 512;
+    const int64_t n = a.total_rows, cb = code_bytes_512(a.qmode);
     return align(n * cb) + align(n * 4) + align(n * 128);
 }
 }  // namespace
@@ -56,7 +56,7 @@ hipError_t launch_decode_attn_sparse(const kvq_attn_args& a, const int64_t* row_
                                      int64_t ws_bytes, hipStream_t st) {
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
     const int64_t n = a.total_rows;
-    const int cb = a.qmode == KVQ_QMODE_TQ4 ? 256 : 512;
+    const int cb = code_bytes_512(a.qmode);
     char* base = (char*)ws;
     uint8_t* codes_c = (uint8_t*)base;
     float* scale_c = (float*)(base + align(n * cb));

@@ -16,7 +16,9 @@ KVQ_ABI_VERSION = 1
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = 0, 1, 2, 3, 4
 KVQ_ERR_TOO_LARGE = 5
 KVQ_NOALLOC_SCRATCH_BYTES = 32 << 20
-KVQ_QMODE_FP8, KVQ_QMODE_TQ4 = 1, 2
+KVQ_QMODE_FP8, KVQ_QMODE_TQ4, KVQ_QMODE_TQ3, KVQ_QMODE_TQ6 = 1, 2, 3, 4
+TQ_QMODE_BITS = {KVQ_QMODE_TQ3: 3, KVQ_QMODE_TQ4: 4, KVQ_QMODE_TQ6: 6}
+TQ_BITS_QMODE = {b: q for q, b in TQ_QMODE_BITS.items()}
 KVQ_PREC_MFMA, KVQ_PREC_FP32 = 0, 1
 KVQ_Q4_NO_ROTATE = 1
 KVQ_STAGE_PREP, KVQ_STAGE_SPLITS, KVQ_STAGE_MERGE = 0, 1, 2
@@ -74,8 +76,10 @@ def lib():
             "kvq_status_string": ([i32], ctypes.c_char_p),
             "kvq_row_bytes": ([i32, i32], i64),
             "kvq_tq4_codebook": ([vp, vp], i32),
+            "kvq_tq_codebook": ([i32, vp, vp], i32),
             "kvq_encode_fp8": ([vp, i64, i32, vp, vp, vp], i32),
             "kvq_encode_tq4": ([vp, i64, i32, vp, vp, vp, vp], i32),
+            "kvq_encode_tq": ([i32, vp, i64, i32, vp, vp, vp, vp], i32),
             "kvq_append_q4_0": ([ctypes.POINTER(KvqQ4Cache), i32, vp, vp, i64, vp, vp, u32, vp], i32),
             "kvq_gather_q4_0": ([ctypes.POINTER(KvqQ4Cache), i32, vp, i64, vp, vp, vp], i32),
             "kvq_decode_attn_workspace_bytes": ([ctypes.POINTER(KvqAttnArgs)], i64),
@@ -104,7 +108,7 @@ def exported_symbols():
             "kvq_encode_tq4", "kvq_append_q4_0", "kvq_gather_q4_0", "kvq_decode_attn_workspace_bytes",
             "kvq_decode_attn", "kvq_decode_attn_stage", "kvq_gather_rows", "kvq_decode_attn_sparse_workspace_bytes",
             "kvq_decode_attn_sparse", "kvq_convert", "kvq_struct_layout", "kvq_decode_attn_q4_0_workspace_bytes",
-            "kvq_decode_attn_q4_0", "kvq_decode_attn_noalloc"]
+            "kvq_decode_attn_q4_0", "kvq_decode_attn_noalloc", "kvq_tq_codebook", "kvq_encode_tq"]
 
 
 # ---- host-only entry points -----------------------------------------------------
@@ -127,6 +131,21 @@ def kvq_tq4_codebook():
     _check("kvq_tq4_codebook", lib().kvq_tq4_codebook(ctypes.cast(lv, ctypes.c_void_p),
                                                       ctypes.cast(th, ctypes.c_void_p)))
     return list(lv), list(th)
+
+
+def kvq_tq_codebook(bits):
+    """Levels [2^bits] and thresholds [2^bits - 1] of the rotated codec's tier."""
+    n = 1 << int(bits) if 0 < int(bits) <= 8 else 1
+    lv = (ctypes.c_float * n)()
+    th = (ctypes.c_float * n)()
+    _check("kvq_tq_codebook", lib().kvq_tq_codebook(int(bits), ctypes.cast(lv, ctypes.c_void_p),
+                                                    ctypes.cast(th, ctypes.c_void_p)))
+    return list(lv), list(th)[:n - 1]
+
+
+def code_bytes(qmode, dim=512):
+    """Code bytes per row of a mode (fp8: dim; rotated codec: dim * bits / 8)."""
+    return dim if qmode == KVQ_QMODE_FP8 else dim * TQ_QMODE_BITS.get(qmode, 4) // 8
 
 
 def kvq_struct_layout(which):
@@ -199,6 +218,17 @@ def kvq_encode_tq4(x, sign_mask, codes, radii, stream=None):
                                                   _ptr(radii, torch.float32, "radii"), _stream(stream)))
 
 
+def kvq_encode_tq(bits, x, sign_mask, codes, radii, stream=None):
+    """x fp32 [n][dim], sign_mask u8 [dim/8] -> codes u8 [n][dim*bits/8], radii fp32 [n]."""
+    n, dim = x.shape
+    _shape(codes, (n, dim * int(bits) // 8), "codes")
+    _shape(radii, (n,), "radii")
+    _check("kvq_encode_tq", lib().kvq_encode_tq(int(bits), _ptr(x, torch.float32, "x"), n, dim,
+                                                _ptr(sign_mask, torch.uint8, "sign_mask"),
+                                                _ptr(codes, torch.uint8, "codes"),
+                                                _ptr(radii, torch.float32, "radii"), _stream(stream)))
+
+
 def q4_cache(k_pool, v_pool, block_table, page_size, head_dim=256):
     """The cache descriptor; it keeps the tensors it points to alive."""
     _shape(k_pool, (None, None, 144), "k_pool")
@@ -239,7 +269,7 @@ def attn_args(qmode, precision, seq_offsets, total_rows, codes, row_scale, k_rop
     _shape(out, (n_seqs, n_heads, dim_lat), "out")
     _shape(lse, (n_seqs, n_heads), "lse")
     _shape(seq_offsets, (n_seqs + 1,), "seq_offsets")
-    _shape(codes, (None, dim_lat if qmode == KVQ_QMODE_FP8 else dim_lat // 2), "codes")
+    _shape(codes, (None, code_bytes(qmode, dim_lat)), "codes")
     rows = codes.shape[0]
     _shape(row_scale, (rows,), "row_scale")
     _shape(k_rope, (rows, q_rope.shape[2]), "k_rope")
@@ -293,8 +323,10 @@ def kvq_decode_attn_stage(args, stage, workspace, stream=None):
 
 
 def kvq_gather_rows(qmode, codes, row_scale, k_rope, row_index, codes_out, scale_out, rope_out, stream=None):
-    """Rows row_index of the cache (codes [rows][512 or 256], row_scale [rows],
+    """Rows row_index of the cache (codes [rows][code_bytes(qmode)], row_scale [rows],
     k_rope [rows][64] bf16 bits) copied to row i of the outputs."""
+    _shape(codes, (None, code_bytes(qmode)), "codes")
+    _shape(codes_out, (row_index.numel(), code_bytes(qmode)), "codes_out")
     _check("kvq_gather_rows", lib().kvq_gather_rows(
         int(qmode), _ptr(codes, torch.uint8, "codes"), _ptr(row_scale, torch.float32, "row_scale"),
         _ptr(k_rope, (torch.uint16, torch.int16, torch.bfloat16), "k_rope"), codes.shape[0],

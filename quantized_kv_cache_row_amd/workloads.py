@@ -146,6 +146,13 @@ def tq4_decode(T=32768):
     return DecodeWorkload(f"tq4-mla-decode-T{T}-H128", 1001, [T], 128, qmode=2, sign_seed=1002)
 
 
+def tq_decode(bits, T=32768):
+    """The rotated codec's decode at 3, 4 or 6 bits (qmode 3, 2, 4): the TQ4
+    workload's latents and signs (seeds 1001 and 1002)."""
+    qmode = {3: 3, 4: 2, 6: 4}[bits]
+    return DecodeWorkload(f"tq{bits}-mla-decode-T{T}-H128", 1001, [T], 128, qmode=qmode, sign_seed=1002)
+
+
 def tq4_encode_rows(n=8192, dim=DIM_LAT):
     """The 8192 new rows of the TQ4 encode-throughput pass (seed 1002)."""
     st = streams(1002)

@@ -36,6 +36,10 @@ def test_host_calls():
     assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_FP8, 512) == 516
     assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ4, 512) == 260
     assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ4, 384) == -1
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ3, 512) == 196
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ6, 512) == 388
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ3, 8) == 7
+    assert kvq.kvq_row_bytes(kvq.KVQ_QMODE_TQ6, 768) == -1
     assert kvq.kvq_row_bytes(7, 512) == -1
 
 
@@ -49,6 +53,16 @@ def test_codebook_equals_oracle():
     _, olv, oth, _ = oracle.tq4_codebook()
     np.testing.assert_array_equal(np.array(lv, np.float32), olv)
     np.testing.assert_array_equal(np.array(th, np.float32), oth)
+    # every tier: the library's table (its own generator) equals the oracle's
+    for bits in (3, 4, 6):
+        lv, th = kvq.kvq_tq_codebook(bits)
+        _, olv, oth, _ = oracle.tq_codebook(bits)
+        assert len(lv) == 1 << bits and len(th) == (1 << bits) - 1
+        np.testing.assert_array_equal(np.array(lv, np.float32), olv)
+        np.testing.assert_array_equal(np.array(th, np.float32), oth)
+    L = kvq.lib()
+    for bits in (0, 2, 5, 8):
+        assert L.kvq_tq_codebook(bits, None, None) == kvq.KVQ_ERR_UNSUPPORTED
 
 
 def test_refusals_without_launch():
@@ -64,6 +78,12 @@ def test_refusals_without_launch():
     # TQ4: non-power-of-two widths are refused, as the pages require
     for dim in (384, 500, 576, 1024):
         assert L.kvq_encode_tq4(P(16), 4, dim, P(16), P(16), P(16), None) == kvq.KVQ_ERR_UNSUPPORTED
+        for bits in (3, 4, 6):
+            assert L.kvq_encode_tq(bits, P(16), 4, dim, P(16), P(16), P(16), None) == kvq.KVQ_ERR_UNSUPPORTED
+    for bits in (2, 5, 8):  # only the 3-, 4- and 6-bit tiers exist
+        assert L.kvq_encode_tq(bits, P(16), 4, 512, P(16), P(16), P(16), None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert L.kvq_encode_tq(6, P(16), 0, 512, None, None, None, None) == kvq.KVQ_OK  # empty is a no-op
+    assert L.kvq_encode_tq(3, P(16), 4, 512, P(16), P(18), P(16), None) == kvq.KVQ_ERR_INVALID_ARG  # misaligned
     # attention
     a = kvq.KvqAttnArgs()
     assert L.kvq_decode_attn(ctypes.byref(a), None, 0, None) == kvq.KVQ_ERR_UNSUPPORTED  # qmode 0
@@ -78,8 +98,14 @@ def test_refusals_without_launch():
     assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_UNSUPPORTED
     a.dim_lat, a.split_rows = 512, 33
     assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
-    a.split_rows, a.qmode = 0, 2  # TQ4 without a sign mask
-    assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    for qm in (2, 3, 4):  # the rotated codec without a sign mask
+        a.split_rows, a.qmode = 0, qm
+        assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_INVALID_ARG
+    a.qmode = 5
+    assert L.kvq_decode_attn(ctypes.byref(a), P(256), need, None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert L.kvq_gather_rows(5, P(256), P(256), P(256), 4, P(256), 1, P(256), P(256), P(256), None) == \
+        kvq.KVQ_ERR_UNSUPPORTED
+    a.qmode = 2
     assert L.kvq_decode_attn_noalloc(ctypes.byref(a), None) == kvq.KVQ_ERR_INVALID_ARG
     # the no-allocation entry point refuses work beyond its static scratch before any HIP call
     a.qmode, a.total_rows, a.split_rows = 1, 1 << 22, 1024

@@ -53,6 +53,18 @@ def gpu_encode_tq4(x, mask):
     return c, r
 
 
+def gpu_encode_tq(x, mask, bits):
+    xt = _t(x.astype(np.float32))
+    n, d = x.shape
+    c = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=DEV)
+    r = torch.empty(n, dtype=torch.float32, device=DEV)
+    kvq.kvq_encode_tq(bits, xt, _t(mask), c, r)
+    return c, r
+
+
+QMODES = [kvq.KVQ_QMODE_FP8, kvq.KVQ_QMODE_TQ4, kvq.KVQ_QMODE_TQ3, kvq.KVQ_QMODE_TQ6]
+
+
 def gpu_attn(w, codes, scales, precision, split_rows=0, q_lat=None, q_rope=None, heads=None):
     q_lat = w.q_lat if q_lat is None else q_lat
     q_rope = w.q_rope if q_rope is None else q_rope
@@ -60,7 +72,7 @@ def gpu_attn(w, codes, scales, precision, split_rows=0, q_lat=None, q_rope=None,
     lse = torch.empty(q_lat.shape[:2], dtype=torch.float32, device=DEV)
     args = kvq.attn_args(w.qmode, precision, _t(w.offsets), w.total_rows, codes, scales, _t(w.k_rope),
                          _t(q_lat), _t(q_rope), w.sm_scale, out, lse,
-                         sign_mask=_t(w.sign_mask) if w.qmode == 2 else None, split_rows=split_rows)
+                         sign_mask=_t(w.sign_mask) if w.qmode != 1 else None, split_rows=split_rows)
     ws = kvq.alloc_workspace(args)
     kvq.kvq_decode_attn(args, ws)
     torch.cuda.synchronize()
@@ -145,9 +157,10 @@ def test_fp8_encoder_bit_exact(case):
         np.testing.assert_array_equal(_np(c), rc)
 
 
+@pytest.mark.parametrize("bits", [4, 3, 6])
 @pytest.mark.parametrize("case", ["tq4_decode-cache", "tq4_decode-new", "dims", "extremes"])
-def test_tq4_encoder_bit_exact(case):
-    _say(f"tq4 encoder {case}")
+def test_tq4_encoder_bit_exact(case, bits):
+    _say(f"tq encoder {case} bits={bits}")
     w = workloads.tq4_decode(T=1024) if case != "tq4_decode-cache" else workloads.tq4_decode()
     if case == "tq4_decode-cache":
         xs = [(w.latent, w.sign_mask)]
@@ -184,10 +197,13 @@ def test_tq4_encoder_bit_exact(case):
             x[3] = 0
             xs.append((x, rng.integers(0, 256, d // 8, dtype=np.uint8)))
     for x, m in xs:
-        c, r = gpu_encode_tq4(x, m)
-        rc, rr = oracle.encode_tq4(x, m)
+        c, r = gpu_encode_tq4(x, m) if bits == 4 else gpu_encode_tq(x, m, bits)
+        rc, rr = oracle.encode_tq(x, m, bits)
         np.testing.assert_array_equal(_np(r).view(np.uint32), rr.view(np.uint32))
         np.testing.assert_array_equal(_np(c), rc)
+        if bits == 4:  # the width-generic entry point gives the same bytes
+            c2, r2 = gpu_encode_tq(x, m, 4)
+            np.testing.assert_array_equal(_np(c2), rc)
 
 
 # ---- decode attention --------------------------------------------------------------------
@@ -195,7 +211,9 @@ def test_tq4_encoder_bit_exact(case):
 def _encode_cache(w):
     if w.qmode == 1:
         return gpu_encode_fp8(w.latent)
-    return gpu_encode_tq4(w.latent, w.sign_mask)
+    if w.qmode == 2:
+        return gpu_encode_tq4(w.latent, w.sign_mask)
+    return gpu_encode_tq(w.latent, w.sign_mask, kvq.TQ_QMODE_BITS[w.qmode])
 
 
 _REF = {}
@@ -240,7 +258,7 @@ def test_attn_tiny_and_split_invariance(precision):
 
 
 @pytest.mark.parametrize("n_heads", [5, 20])
-@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("qmode", QMODES)
 @pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_attn_head_counts(n_heads, qmode, precision):
     """Head counts that leave part of a head group empty: 5 heads (one partial
@@ -248,16 +266,22 @@ def test_attn_head_counts(n_heads, qmode, precision):
     group for TQ4).  Two sequences of 700 and 333 rows."""
     _say(f"attn head count {n_heads} qmode={qmode} precision={precision}")
     w = workloads.DecodeWorkload(f"heads{n_heads}", 1006, [700, 333], n_heads, qmode=qmode,
-                                 sign_seed=1002 if qmode == 2 else None)
+                                 sign_seed=1002 if qmode != 1 else None)
     c, s = _encode_cache(w)
     _check_attn(w, c, s, precision, label=f"heads{n_heads}")
 
 
-@pytest.mark.parametrize("qmode", [1, 2])
+def _full(qmode, T=32768):
+    if qmode == 1:
+        return workloads.kv8_decode(T)
+    return workloads.tq_decode(kvq.TQ_QMODE_BITS[qmode], T)
+
+
+@pytest.mark.parametrize("qmode", QMODES)
 @pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_attn_full_T32768(qmode, precision):
     _say(f"attn T=32768 H=128 qmode={qmode} precision={precision}")
-    w = workloads.kv8_decode() if qmode == 1 else workloads.tq4_decode()
+    w = _full(qmode)
     c, s = _encode_cache(w)
     _check_attn(w, c, s, precision, label=w.name)
     if precision == kvq.KVQ_PREC_MFMA:  # a few explicit split sizes
@@ -265,10 +289,10 @@ def test_attn_full_T32768(qmode, precision):
             _check_attn(w, c, s, precision, sr, label=w.name)
 
 
-@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("qmode", QMODES)
 def test_attn_peaked_softmax(qmode):
     _say(f"attn peaked qmode={qmode}")
-    w = workloads.tq4_decode(T=3000) if qmode == 2 else workloads.kv8_decode(T=3000)
+    w = _full(qmode, T=3000)
     c, s = _encode_cache(w)
     ql = (w.q_lat * 50).astype(np.float32)
     qr = (w.q_rope * 50).astype(np.float32)
@@ -277,7 +301,7 @@ def test_attn_peaked_softmax(qmode):
         _check_attn(w, c, s, prec, split_rows=96, q_lat=ql, q_rope=qr, label="peaked-split96")
 
 
-@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("qmode", QMODES)
 def test_attn_rising_scores_and_scales(qmode):
     """Scores that climb along the rows (a sawtooth of period 512 in one rope
     dimension) and row gains that double every 256 rows: the split kernels'
@@ -293,9 +317,23 @@ def test_attn_rising_scores_and_scales(qmode):
     qr = w.q_rope.copy()
     qr[..., 0] = 400.0
     c, s = _encode_cache(w)
+    # Scores here reach |s| ~ 400.  An fp32 evaluation carries up to |s| 2^-24 of
+    # rounding in every exponent (a correctly rounded fp32 score already does;
+    # the summation of the 576 products adds a few such units), which moves the
+    # normalized output by the same order, about 2e-5 at this scale: the fp32
+    # path's bar is max(1e-5, 2 S 2^-24) for the largest score magnitude S.
+    if w.qmode == 1:
+        xh = oracle.decode_fp8(_np(c), _np(s))
+    else:
+        xh = oracle.decode_tq(_np(c), _np(s), w.sign_mask, kvq.TQ_QMODE_BITS[w.qmode], 512)
+    kr = oracle.bf16_decode(w.k_rope)
+    S = float(np.max(np.abs(w.sm_scale * (ql[0].astype(np.float64) @ xh.T + qr[0].astype(np.float64) @ kr.T))))
+    tol32 = max(TOL[kvq.KVQ_PREC_FP32], 2.0 * S * 2.0 ** -24)
+    _say(f"  rising: max|s| = {S:.1f}, fp32 bar {tol32:.2e}")
     for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
         for sr in (0, 4096, 96):
-            _check_attn(w, c, s, prec, sr, q_lat=ql, q_rope=qr, label="rising")
+            _check_attn(w, c, s, prec, sr, q_lat=ql, q_rope=qr, label="rising",
+                        tol=tol32 if prec == kvq.KVQ_PREC_FP32 else None)
 
 
 def test_attn_ragged_edges():
@@ -306,10 +344,12 @@ def test_attn_ragged_edges():
         for sr in (0, 32, 64):
             got = _check_attn(w, c, s, prec, sr, label="edges")
             assert np.all(got[1] == 0)  # empty sequence
-    w2 = workloads.DecodeWorkload("edges-tq4", 78, [1, 40, 0, 129], 16, qmode=2)
-    c2, s2 = _encode_cache(w2)
-    for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
-        _check_attn(w2, c2, s2, prec, 32, label="edges-tq4")
+    for qm in (2, 3, 4):
+        w2 = workloads.DecodeWorkload(f"edges-q{qm}", 78, [1, 40, 0, 129], 16, qmode=qm)
+        c2, s2 = _encode_cache(w2)
+        for prec in (kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32):
+            got = _check_attn(w2, c2, s2, prec, 32, label=f"edges-q{qm}")
+            assert np.all(got[2] == 0)
 
 
 def test_attn_ragged_full_size_all_heads():

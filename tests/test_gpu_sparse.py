@@ -43,13 +43,15 @@ def rel_err(got, ref):
 
 def _encode(w):
     x = _t(w.latent)
-    cb = 512 if w.qmode == 1 else 256
+    cb = kvq.code_bytes(w.qmode)
     codes = torch.empty((w.cache_rows, cb), dtype=torch.uint8, device=DEV)
     scales = torch.empty(w.cache_rows, dtype=torch.float32, device=DEV)
     if w.qmode == 1:
         kvq.kvq_encode_fp8(x, codes, scales)
-    else:
+    elif w.qmode == 2:
         kvq.kvq_encode_tq4(x, _t(w.sign_mask), codes, scales)
+    else:
+        kvq.kvq_encode_tq(kvq.TQ_QMODE_BITS[w.qmode], x, _t(w.sign_mask), codes, scales)
     return codes, scales
 
 
@@ -57,7 +59,7 @@ def _args(w, precision, offsets, n, codes, scales, k_rope, split_rows=0):
     out = torch.empty((w.n_seqs, w.n_heads, 512), dtype=torch.float32, device=DEV)
     lse = torch.empty((w.n_seqs, w.n_heads), dtype=torch.float32, device=DEV)
     a = kvq.attn_args(w.qmode, precision, _t(offsets), n, codes, scales, k_rope, _t(w.q_lat), _t(w.q_rope),
-                      w.sm_scale, out, lse, sign_mask=_t(w.sign_mask) if w.qmode == 2 else None, split_rows=split_rows)
+                      w.sm_scale, out, lse, sign_mask=_t(w.sign_mask) if w.qmode != 1 else None, split_rows=split_rows)
     return a, out, lse
 
 
@@ -72,14 +74,14 @@ def _sparse(w, precision, codes, scales, offsets, row_index, split_rows=0):
 def _oracle(w, codes, scales, offsets, row_index):
     return oracle.decode_attn_sparse(w.qmode, np.asarray(offsets, np.int64), np.asarray(row_index, np.int64),
                                      _np(codes), _np(scales), w.k_rope, w.q_lat, w.q_rope, w.sm_scale,
-                                     sign_mask=w.sign_mask if w.qmode == 2 else None)
+                                     sign_mask=w.sign_mask if w.qmode != 1 else None)
 
 
-@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("qmode", [1, 2, 3, 4])
 def test_gather_rows_bit_exact(qmode):
     _say(f"gather rows qmode={qmode}")
     rng = np.random.default_rng(11)
-    T, cb = 1000, (512 if qmode == 1 else 256)
+    T, cb = 1000, kvq.code_bytes(qmode)
     codes = rng.integers(0, 256, (T, cb), dtype=np.uint8)
     sc = rng.standard_normal(T).astype(np.float32)
     kr = rng.integers(0, 65536, (T, 64), dtype=np.uint16)
@@ -98,12 +100,12 @@ def test_gather_rows_bit_exact(qmode):
     assert np.array_equal(_np(ro, np.uint16), kr[ref])
 
 
-@pytest.mark.parametrize("qmode", [1, 2])
+@pytest.mark.parametrize("qmode", [1, 2, 3, 4])
 @pytest.mark.parametrize("precision", [kvq.KVQ_PREC_MFMA, kvq.KVQ_PREC_FP32])
 def test_sparse_attn_vs_oracle(qmode, precision):
     _say(f"sparse attention qmode={qmode} precision={precision}")
     w = workloads.SparseDecodeWorkload("sparse-small", 1005, 4096, [1, 37, 300, 2048], 16, qmode=qmode,
-                                       sign_seed=1002 if qmode == 2 else None)
+                                       sign_seed=1002 if qmode != 1 else None)
     codes, scales = _encode(w)
     got, glse = _sparse(w, precision, codes, scales, w.offsets, w.row_index)
     ref, rlse = _oracle(w, codes, scales, w.offsets, w.row_index)

@@ -1,10 +1,12 @@
 """Benchmark of the quantized-KV decode hot path on one MI355X.
 
 A step is one decode step of the KV8 absorbed-MLA workload (1 sequence,
-T = 32768 cached rows, 128 heads, 512-dim fp8 latent + 64-dim bf16 rope key):
-  1. fp8-encode the step's new latent row into the cache (row T-1),
-  2. decode attention over all T rows: split plan + query preparation, the
-     split kernel (the dominant kernel), the merge.
+T = 32768 cached rows, 128 heads, 512-dim fp8 latent + 64-dim bf16 rope key),
+one kvq_decode_attn_append call:
+  1. fp8-encode the step's new latent row into the cache (row T-1), in the
+     same launch as 2's query preparation,
+  2. decode attention over all T rows: query preparation, the split kernel
+     (the dominant kernel, which plans its own split), the merge.
 The steps cycle through --kv-copies independent caches (16 x 21 MB > the
 256 MB last-level cache) so every step reads its KV from HBM, as consecutive
 layers of a model do; one step per cache, in order, is captured as one HIP
@@ -407,13 +409,10 @@ def main():
         codes_c, scales_c, _ = copies[c]
         a = argsets[c]
         if stage is None:
-            row = new_rows[c:c + 1]
-            if qmode == 1:
-                kvq.kvq_encode_fp8(row, codes_c[T - 1:T], scales_c[T - 1:T])
-            else:
-                kvq.kvq_encode_tq4(row, mask, codes_c[T - 1:T], scales_c[T - 1:T])
-            for st in (kvq.KVQ_STAGE_PREP, kvq.KVQ_STAGE_SPLITS, kvq.KVQ_STAGE_MERGE):
-                kvq.kvq_decode_attn_stage(a, st, ws)
+            # the new token's row is encoded into the cache's last row and the
+            # attention runs over the whole cache, in one call (on the fp8
+            # matrix-core path the encode shares the query-preparation launch)
+            kvq.kvq_decode_attn_append(a, new_rows[c:c + 1], codes_c[T - 1:T], scales_c[T - 1:T], ws)
         else:
             kvq.kvq_decode_attn_stage(a, stage, ws)
 

@@ -226,6 +226,21 @@ int64_t kvq_decode_attn_workspace_bytes(const kvq_attn_args* a);
  * calls that share a workspace must be ordered (same stream). */
 int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, void* stream);
 
+/* Appends n_new rows and runs decode attention, in one call: the same as the
+ * row encoder of a->qmode (kvq_encode_fp8, or kvq_encode_tq with a->sign_mask)
+ * on x_new (fp32 [n_new][512]) into codes_new (u8 [n_new][code bytes]) and
+ * scale_new (fp32 [n_new]), followed by kvq_decode_attn(a, ...) -- a decode
+ * step's append of the new token's latent row and its attention over the
+ * cache ([KV8] commit 6, the fused layer decode).  codes_new and scale_new
+ * normally point at the rows the new tokens take in the cache that a->codes and
+ * a->row_scale describe; the attention reads them after the encode.  On the
+ * fp8 matrix-core path the encode runs inside the attention's query-preparation
+ * launch (one launch fewer); other modes launch the encoder first.  Results are
+ * bit-identical to the two calls.  n_new = 0 is kvq_decode_attn.  Alignment:
+ * x_new 16 bytes, codes_new 8 (fp8) or 4 bytes, scale_new 4. */
+int kvq_decode_attn_append(const kvq_attn_args* a, const float* x_new, int64_t n_new, uint8_t* codes_new,
+                           float* scale_new, void* workspace, int64_t ws_bytes, void* stream);
+
 /* ---- decode attention without allocation ----------------------------------
  * For callers that cannot allocate device memory or pass a workspace: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -234,6 +234,24 @@ int kvq_decode_attn(const kvq_attn_args* a, void* workspace, int64_t ws_bytes, v
     return launch_status(kvq::launch_decode_attn(*a, workspace, ws_bytes, as_stream(stream)));
 }
 
+int kvq_decode_attn_append(const kvq_attn_args* a, const float* x_new, int64_t n_new, uint8_t* codes_new,
+                           float* scale_new, void* workspace, int64_t ws_bytes, void* stream) {
+    int rc = check_attn(a);
+    if (rc != KVQ_OK) return rc;
+    if (n_new < 0) return KVQ_ERR_INVALID_ARG;
+    if (n_new > ((int64_t)1 << 31)) return KVQ_ERR_UNSUPPORTED;
+    if (n_new > 0) {
+        if (!x_new || !codes_new || !scale_new) return KVQ_ERR_INVALID_ARG;
+        if (!aligned16(x_new) || !aligned(codes_new, a->qmode == KVQ_QMODE_FP8 ? 8 : 4) || !aligned(scale_new, 4))
+            return KVQ_ERR_INVALID_ARG;
+    }
+    const int64_t need = kvq::attn_workspace_bytes(*a);
+    if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return KVQ_ERR_INVALID_ARG;
+    const kvq::NewRows nr{x_new, n_new, codes_new, scale_new};
+    return launch_status(kvq::launch_decode_attn_append(*a, nr, workspace, as_stream(stream)));
+}
+
 int kvq_decode_attn_noalloc(const kvq_attn_args* a, void* stream) {
     int rc = check_attn(a);
     if (rc != KVQ_OK) return rc;

@@ -624,10 +624,17 @@ __device__ __forceinline__ bool locate_chunk(const kvq_attn_args& a, const Plan&
 // .. + 7 (i < 16, j < 2, h < 2); uint4 2048 + (((i * 2 + j) * 2 + t) * 2 + h) *
 // 32 + n its rope dims 32 i + 16 h + 8 j .. + 7, term t (0: hi, 1: lo; i < 2).
 // One wave per (sequence, head); lane l converts dims 8 l .. 8 l + 7.
-__global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p) {
+__global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p, NewRows nr) {
     const int lane = threadIdx.x & 63;
+    const int64_t prep_rows = (int64_t)a.n_seqs * p.heads_padded;
+    const int64_t prep_blocks = (prep_rows + 3) / 4;
+    if ((int64_t)blockIdx.x >= prep_blocks) {  // the rows appended by this call: one wave per row
+        const int64_t r = ((int64_t)blockIdx.x - prep_blocks) * 4 + (threadIdx.x >> 6);
+        if (r < nr.n) encode_fp8_row<1>(nr.x + r * DL, DL, nr.codes + r * DL, nr.scales + r, lane);
+        return;
+    }
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + head
-    if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
+    if (row >= prep_rows) return;
     const int s = (int)(row / p.heads_padded), hd = (int)(row % p.heads_padded);
     const bool hv = hd < a.n_heads;
     const int64_t qrow = (int64_t)s * a.n_heads + min(hd, a.n_heads - 1);  // absent heads: a zero query
@@ -1567,8 +1574,9 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
 
 int64_t attn_workspace_bytes(const kvq_attn_args& a) { return plan_bytes(a); }
 
-hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws, hipStream_t st) {
+hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws, hipStream_t st, const NewRows* nr) {
     Plan p = make_plan(a, ws, nullptr);
+    const NewRows none{nullptr, 0, nullptr, nullptr};
     const bool f32 = a.precision == KVQ_PREC_FP32;
     const bool tq = qmode_rotated(a.qmode);
     switch (stage) {
@@ -1577,8 +1585,13 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
             // query operands are prepared here once per head (rotated codec: R q)
             if (!f32) {
                 const int64_t rows = (int64_t)a.n_seqs * p.heads_padded;
-                if (tq) hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
-                else hipLaunchKernelGGL(k_qprep_fp8, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
+                if (tq) {
+                    hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
+                } else {  // with the fp8 encode of the appended rows, if any, in the same launch
+                    const NewRows n = nr ? *nr : none;
+                    const int64_t blocks = (rows + 3) / 4 + (n.n + 3) / 4;
+                    hipLaunchKernelGGL(k_qprep_fp8, dim3((unsigned)blocks), dim3(256), 0, st, a, p, n);
+                }
                 break;
             }
             hipLaunchKernelGGL(k_plan, dim3(1), dim3(256), 0, st, a.seq_offsets, a.n_seqs, p.split_rows, a.total_rows,
@@ -1637,6 +1650,22 @@ hipError_t launch_decode_attn(const kvq_attn_args& a, void* ws, int64_t ws_bytes
     (void)ws_bytes;
     for (int stage = KVQ_STAGE_PREP; stage <= KVQ_STAGE_MERGE; stage++) {
         const hipError_t e = launch_decode_attn_stage(a, stage, ws, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_decode_attn_append(const kvq_attn_args& a, const NewRows& nr, void* ws, hipStream_t st) {
+    const bool fused = a.qmode == KVQ_QMODE_FP8 && a.precision == KVQ_PREC_MFMA;
+    if (!fused && nr.n > 0) {  // the encoder first, then the attention
+        const hipError_t e = a.qmode == KVQ_QMODE_FP8
+                                 ? launch_encode_fp8(nr.x, nr.n, DL, nr.codes, nr.scales, st)
+                                 : launch_encode_tq(qmode_bits(a.qmode), nr.x, nr.n, DL, a.sign_mask, nr.codes,
+                                                    nr.scales, st);
+        if (e != hipSuccess) return e;
+    }
+    for (int stage = KVQ_STAGE_PREP; stage <= KVQ_STAGE_MERGE; stage++) {
+        const hipError_t e = launch_decode_attn_stage(a, stage, ws, st, fused ? &nr : nullptr);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -111,6 +111,73 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// ---- the fp8 row encoder ---------------------------------------------------
+// One row of dim (a multiple of 8, <= 512 ITER) fp32 values, one wave (colibri
+// PR #399 "KV cache quantization: fp8 (KV8) + 4-bit TurboQuant (KV_TQ) ...",
+// Summary and commit 1: e4m3 codes with one amax/448 scale per row, round to
+// nearest even):
+//   *scale = fl(amax / 448) (0 for an all-zero row),
+//   code_i = e4m3(fl(x_i / scale)) (0 for an all-zero row).
+// Lane l holds elements 4 l .. 4 l + 3 and 256 + 4 l .. + 3 of each 512-element
+// span, so every load covers 1 KB of the row contiguously (the steps are
+// element-wise; the maximum does not depend on the order).  Codes are stored as
+// one 4-byte store per lane and span, the scale by lane 0.
+typedef float f32x4v __attribute__((ext_vector_type(4)));  // a native vector (non-temporal loads)
+
+template <int ITER>
+__device__ __forceinline__ void encode_fp8_row(const float* __restrict__ xr, int dim, uint8_t* __restrict__ cr,
+                                               float* __restrict__ scale, int lane) {
+    float v[ITER][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int it = 0; it < ITER; it++) {
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            const int base = it * 512 + 256 * hf + lane * 4;  // dim is a multiple of 8: all four or none
+            if (base < dim) {
+                const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(xr + base));
+                v[it][4 * hf + 0] = a[0]; v[it][4 * hf + 1] = a[1]; v[it][4 * hf + 2] = a[2]; v[it][4 * hf + 3] = a[3];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) v[it][4 * hf + j] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(v[it][j]));
+    }
+    amax = wave_max(amax);
+    const float s = (amax == 0.0f) ? 0.0f : amax / 448.0f;  // correctly rounded division
+    // x / s, correctly rounded: for amax >= 2^-90 from the correctly rounded
+    // reciprocal r = 1/s with one fma correction, q = q0 + (x - q0 s) r with
+    // q0 = x r (Markstein's theorem; the residual x - q0 s is exact in an fma).
+    // Smaller rows, where 1/s can overflow, divide.  Wave-uniform branch.
+    const bool recip = amax >= 0x1p-90f;
+    const float r = recip ? 1.0f / s : 0.0f;
+#pragma unroll
+    for (int it = 0; it < ITER; it++) {
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            const int base = it * 512 + 256 * hf + lane * 4;
+            if (base < dim) {
+                float qv[4];
+                if (recip) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float q0 = v[it][4 * hf + j] * r;
+                        qv[j] = __builtin_fmaf(__builtin_fmaf(-q0, s, v[it][4 * hf + j]), r, q0);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) qv[j] = (s != 0.0f) ? v[it][4 * hf + j] / s : 0.0f;
+                }
+                const uint32_t w = e4m3x2_rne(qv[0], qv[1]) | (e4m3x2_rne(qv[2], qv[3]) << 16);
+                __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(cr + base));
+            }
+        }
+    }
+    if (lane == 0) *scale = s;
+}
+
 // Cross-lane FWHT stage with partner lane^m: the lower lane keeps a + b, the
 // upper lane keeps a - b, where a is the lower lane's value and b the upper's.
 __device__ __forceinline__ float fwht_xlane(float v, int lane, int m) {

@@ -32,9 +32,7 @@ __constant__ uint32_t c_tq6_thresh[63] = KVQ_TQ6_THRESH_BITS;
 constexpr int ENC_WAVES = 4;  // waves per workgroup
 
 // ---- fp8 -------------------------------------------------------------------
-// One wave per row; ITER chunks of 512 elements (8 per lane).
-typedef float f32x4v __attribute__((ext_vector_type(4)));  // a native vector (non-temporal loads)
-
+// One wave per row (encode_fp8_row in kvq_device.h); ITER chunks of 512 elements.
 template <int ITER>
 __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float* __restrict__ x, int64_t n_rows,
                                                                      int dim, uint8_t* __restrict__ codes,
@@ -42,60 +40,7 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float
     const int lane = threadIdx.x & (KVQ_WAVE - 1);
     const int64_t row = (int64_t)blockIdx.x * ENC_WAVES + (threadIdx.x >> 6);
     if (row >= n_rows) return;  // whole wave exits together
-    const float* xr = x + row * dim;
-    // lane l holds elements 4 l .. 4 l + 3 and 256 + 4 l .. + 3 of each 512-element
-    // span, so every load covers 1 KB of the row contiguously (the steps below are
-    // element-wise; the maximum does not depend on the order)
-    float v[ITER][8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int it = 0; it < ITER; it++) {
-#pragma unroll
-        for (int hf = 0; hf < 2; hf++) {
-            const int base = it * 512 + 256 * hf + lane * 4;  // dim is a multiple of 8: all four or none
-            if (base < dim) {
-                const f32x4v a = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(xr + base));
-                v[it][4 * hf + 0] = a[0]; v[it][4 * hf + 1] = a[1]; v[it][4 * hf + 2] = a[2]; v[it][4 * hf + 3] = a[3];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; j++) v[it][4 * hf + j] = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; j++) amax = fmaxf(amax, fabsf(v[it][j]));
-    }
-    amax = wave_max(amax);
-    const float s = (amax == 0.0f) ? 0.0f : amax / 448.0f;  // correctly rounded division
-    // x / s, correctly rounded: for amax >= 2^-90 from the correctly rounded
-    // reciprocal r = 1/s with one fma correction, q = q0 + (x - q0 s) r with
-    // q0 = x r (Markstein's theorem; the residual x - q0 s is exact in an fma).
-    // Smaller rows, where 1/s can overflow, divide.  Wave-uniform branch.
-    const bool recip = amax >= 0x1p-90f;
-    const float r = recip ? 1.0f / s : 0.0f;
-    uint8_t* cr = codes + row * dim;
-#pragma unroll
-    for (int it = 0; it < ITER; it++) {
-#pragma unroll
-        for (int hf = 0; hf < 2; hf++) {
-            const int base = it * 512 + 256 * hf + lane * 4;
-            if (base < dim) {
-                float qv[4];
-                if (recip) {
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const float q0 = v[it][4 * hf + j] * r;
-                        qv[j] = __builtin_fmaf(__builtin_fmaf(-q0, s, v[it][4 * hf + j]), r, q0);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; j++) qv[j] = (s != 0.0f) ? v[it][4 * hf + j] / s : 0.0f;
-                }
-                const uint32_t w = e4m3x2_rne(qv[0], qv[1]) | (e4m3x2_rne(qv[2], qv[3]) << 16);
-                __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(cr + base));
-            }
-        }
-    }
-    if (lane == 0) scales[row] = s;
+    encode_fp8_row<ITER>(x + row * dim, dim, codes + row * dim, scales + row, lane);
 }
 
 // ---- rotated codec, any width ------------------------------------------------------

@@ -86,6 +86,7 @@ def lib():
             "kvq_decode_attn": ([ctypes.POINTER(KvqAttnArgs), vp, i64, vp], i32),
             "kvq_decode_attn_stage": ([ctypes.POINTER(KvqAttnArgs), i32, vp, i64, vp], i32),
             "kvq_decode_attn_noalloc": ([ctypes.POINTER(KvqAttnArgs), vp], i32),
+            "kvq_decode_attn_append": ([ctypes.POINTER(KvqAttnArgs), vp, i64, vp, vp, vp, i64, vp], i32),
             "kvq_convert": ([i32, vp, i64, vp, vp], i32),
             "kvq_gather_rows": ([i32, vp, vp, vp, i64, vp, i64, vp, vp, vp, vp], i32),
             "kvq_decode_attn_sparse_workspace_bytes": ([ctypes.POINTER(KvqAttnArgs)], i64),
@@ -108,7 +109,8 @@ def exported_symbols():
             "kvq_encode_tq4", "kvq_append_q4_0", "kvq_gather_q4_0", "kvq_decode_attn_workspace_bytes",
             "kvq_decode_attn", "kvq_decode_attn_stage", "kvq_gather_rows", "kvq_decode_attn_sparse_workspace_bytes",
             "kvq_decode_attn_sparse", "kvq_convert", "kvq_struct_layout", "kvq_decode_attn_q4_0_workspace_bytes",
-            "kvq_decode_attn_q4_0", "kvq_decode_attn_noalloc", "kvq_tq_codebook", "kvq_encode_tq"]
+            "kvq_decode_attn_q4_0", "kvq_decode_attn_noalloc", "kvq_tq_codebook", "kvq_encode_tq",
+            "kvq_decode_attn_append"]
 
 
 # ---- host-only entry points -----------------------------------------------------
@@ -306,6 +308,19 @@ def _cache_rows_cover(args):
     codes = args._keep[1]
     if codes is not None and codes.shape[0] < args.total_rows:
         raise ValueError(f"codes: {codes.shape[0]} rows, fewer than total_rows = {args.total_rows}")
+
+
+def kvq_decode_attn_append(args, x_new, codes_new, scale_new, workspace, stream=None):
+    """Encodes x_new (fp32 [n][512]) into codes_new / scale_new, then decode attention."""
+    n = x_new.shape[0]
+    _shape(x_new, (n, 512), "x_new")
+    _shape(codes_new, (n, code_bytes(args.qmode)), "codes_new")
+    _shape(scale_new, (n,), "scale_new")
+    _cache_rows_cover(args)
+    _check("kvq_decode_attn_append", lib().kvq_decode_attn_append(
+        ctypes.byref(args), _ptr(x_new, torch.float32, "x_new"), n, _ptr(codes_new, torch.uint8, "codes_new"),
+        _ptr(scale_new, torch.float32, "scale_new"), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))
 
 
 def kvq_decode_attn_noalloc(args, stream=None):

@@ -113,6 +113,18 @@ def test_refusals_without_launch():
     assert L.kvq_decode_attn_noalloc(ctypes.byref(a), None) == kvq.KVQ_ERR_TOO_LARGE
     assert "scratch" in kvq.kvq_status_string(kvq.KVQ_ERR_TOO_LARGE)
     a.total_rows, a.split_rows = 32768, 0
+    # decode attention with appended rows: counts, pointers, alignment, workspace
+    need = L.kvq_decode_attn_workspace_bytes(ctypes.byref(a))
+    assert L.kvq_decode_attn_append(ctypes.byref(a), P(256), -1, P(256), P(256), P(256), need, None) == \
+        kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_decode_attn_append(ctypes.byref(a), None, 1, P(256), P(256), P(256), need, None) == \
+        kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_decode_attn_append(ctypes.byref(a), P(264), 1, P(256), P(256), P(256), need, None) == \
+        kvq.KVQ_ERR_INVALID_ARG  # x_new not 16-byte aligned
+    assert L.kvq_decode_attn_append(ctypes.byref(a), P(256), 1, P(260), P(256), P(256), need, None) == \
+        kvq.KVQ_ERR_INVALID_ARG  # fp8 codes not 8-byte aligned
+    assert L.kvq_decode_attn_append(ctypes.byref(a), P(256), 1, P(256), P(256), P(256), need - 1, None) == \
+        kvq.KVQ_ERR_WORKSPACE
     # q4_0
     c = kvq.KvqQ4Cache(256, 256, 256, 64, 1, 64, 8, 128)
     assert L.kvq_append_q4_0(ctypes.byref(c), 1, P(256), P(256), 1, P(256), P(256), 0, None) == \

@@ -370,6 +370,37 @@ def test_attn_ragged_div16_all_heads():
         _check_attn(w, c, s, prec, label=w.name)
 
 
+@pytest.mark.parametrize("qmode,precision", [(1, kvq.KVQ_PREC_MFMA), (1, kvq.KVQ_PREC_FP32),
+                                             (2, kvq.KVQ_PREC_MFMA), (4, kvq.KVQ_PREC_MFMA)])
+def test_attn_append_equals_encode_then_attend(qmode, precision):
+    """kvq_decode_attn_append encodes the last rows of the cache itself (on the
+    fp8 matrix-core path inside the query-preparation launch); codes, scales and
+    the attention output are bit-identical to a separate encode followed by
+    kvq_decode_attn.  Two sequences; 1 and then 37 appended rows."""
+    _say(f"attn append qmode={qmode} precision={precision}")
+    w = workloads.DecodeWorkload(f"append-q{qmode}", 1010, [900, 1300], 24, qmode=qmode,
+                                 sign_seed=1002 if qmode != 1 else None)
+    c_ref, s_ref = _encode_cache(w)
+    ref, rlse = gpu_attn(w, c_ref, s_ref, precision)
+    for n_new in (1, 37):
+        c = c_ref.clone()
+        sc = s_ref.clone()
+        c[-n_new:] = 0
+        sc[-n_new:] = -1.0
+        out = torch.empty(w.q_lat.shape, dtype=torch.float32, device=DEV)
+        lse = torch.empty(w.q_lat.shape[:2], dtype=torch.float32, device=DEV)
+        args = kvq.attn_args(w.qmode, precision, _t(w.offsets), w.total_rows, c, sc, _t(w.k_rope), _t(w.q_lat),
+                             _t(w.q_rope), w.sm_scale, out, lse,
+                             sign_mask=_t(w.sign_mask) if w.qmode != 1 else None)
+        ws = kvq.alloc_workspace(args)
+        kvq.kvq_decode_attn_append(args, _t(w.latent[-n_new:]), c[-n_new:], sc[-n_new:], ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_np(c), _np(c_ref))
+        np.testing.assert_array_equal(_np(sc).view(np.uint32), _np(s_ref).view(np.uint32))
+        np.testing.assert_array_equal(_np(out).astype(np.float64), ref)
+        np.testing.assert_array_equal(_np(lse).astype(np.float64), rlse)
+
+
 def test_attn_deterministic():
     _say("attn determinism")
     w = workloads.kv8_decode(T=5000)

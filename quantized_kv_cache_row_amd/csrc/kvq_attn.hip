@@ -1093,11 +1093,26 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
 // the chunk's largest radius; a tile more than 2^8 above the reference raises
 // it, and the workgroup (which shares the tiles) starts its rows again.  One
 // partial per (chunk, head), written by the wave that owns the head.
-constexpr int XT = DL + 8;                // halfwords per fp16 tile row (rows 4 banks apart)
+//
+// The decoded tile: row r at DL halfwords r, its 16-byte chunk c (dims 8 c ..
+// 8 c + 7) stored at chunk c ^ tq_swz(r), tq_swz(r) = 2 (r % 4) ^ 9 bit2(r) ^
+// bit3(r) (0, 2, 4, 6, 9, 11, 13, 15, 1, 3, 5, 7, 8, 10, 12, 14 for r % 16).
+// With the decode share of lane l on row l % 8 of its wave's 8 rows, the
+// decode writes (8 or 16 lanes on 8 rows), score reads (8 or 16 consecutive
+// rows, one chunk) and transposed PV reads (4 or 8 rows x 4 half-chunks) fall
+// on distinct banks whether a read or write cycle serves 64 bytes per 8 lanes
+// (32 banks) or 128 bytes per 16 (64 banks) -- checked on the CPU.  The
+// unswizzled layout with padded rows lost ~25 % of the kernel to bank
+// conflicts (6.4 M conflict cycles per launch).
 constexpr int KT = DR + 8;                // halfwords per rope tile row
+constexpr int SR = DL / 2 + 4;            // floats per staged half row of the epilogue
+constexpr int XT_HALFWORDS = (2 * MF_TILE * DL > MF_WAVES * MF_HEADS * SR * 2) ? 2 * MF_TILE * DL
+                                                                               : MF_WAVES * MF_HEADS * SR * 2;
+__device__ __forceinline__ int tq_swz(int r) { return (2 * (r & 3)) ^ ((r & 4) ? 9 : 0) ^ ((r >> 3) & 1); }
 template <int BITS>
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a, Plan p) {
-    __shared__ __align__(16) uint16_t xt[2][MF_TILE][XT];  // decoded latent rows, fp16
+    __shared__ __align__(16) uint16_t xt_mem[XT_HALFWORDS];  // decoded latent rows, fp16 (then the epilogue's staging)
+    auto xt_row = [&](int buf, int r) __attribute__((always_inline)) { return xt_mem + (buf * MF_TILE + r) * DL; };
     __shared__ __align__(16) uint16_t kt[2][MF_TILE][KT];  // rope keys, bf16
     __shared__ __align__(16) float rho_s[2][MF_TILE];      // radius / sqrt(512)
     __shared__ float red_s[MF_WAVES];
@@ -1120,7 +1135,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
     // decode share of this wave: tile row 8 wave + lane / 8, code bytes
     // 8 BITS (lane % 8) .. + 8 BITS - 1 (dims 64 (lane % 8) .. + 63), rope bytes
     // 16 (lane % 8).  Group i of 8 dims is bits 8 BITS i .. of the lane's words.
-    const int drow = 8 * wave + (lane >> 3), dq = lane & 7;
+    const int drow = 8 * wave + (lane & 7), dq = lane >> 3;
     uint4 cv[3];  // codes of the tile to decode next (BITS * 2 words)
     uint4 cr;     // its rope keys
     float cs;     // its row radius (scaled by 1 / sqrt(512) when it is stored)
@@ -1144,10 +1159,12 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
     };
     const Tq4Lut lut = BITS == 3 ? make_tq3_lut() : make_tq4_lut();
     const uint32_t tab6 = BITS == 6 ? f16_bits(u2f(c_tq6_level[32 + (lane & 31)])) : 0u;
+    const int dswz = tq_swz(drow);
+    const int dq_off = 64 * (dq ^ (dswz >> 3)), di = dswz & 7;  // chunk 8 dq + i sits at 8 (dq ^ f / 8) + (i ^ f % 8)
     auto decode_share = [&](int buf) __attribute__((always_inline)) {
-        uint16_t* dst = &xt[buf][drow][64 * dq];
-        auto put = [&](int i, uint4 h) __attribute__((always_inline)) {
-            *reinterpret_cast<uint4*>(dst + 8 * i) = h;
+        uint16_t* dst = xt_row(buf, drow) + dq_off;
+        auto put = [&](int i, uint4 h) __attribute__((always_inline)) {  // chunk 8 dq + i of the row
+            *reinterpret_cast<uint4*>(dst + 8 * (i ^ di)) = h;
         };
         if constexpr (BITS == 4) {
             const uint32_t w[8] = {cv[0].x, cv[0].y, cv[0].z, cv[0].w, cv[1].x, cv[1].y, cv[1].z, cv[1].w};
@@ -1213,7 +1230,19 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
 
     // per-lane LDS addresses: score row 16 rb + n, dims 8 g + 32 ks; PV source
     // lane (g, n) at row 4 g + n / 4, column 4 (n % 4) (+ 16 mb, + 16 rows)
-    const int trow = 4 * g + (n >> 2), tcol = 4 * (n & 3);
+    const int trow = 4 * g + (n >> 2);
+    // score reads: chunk g + 4 ks of row n sits at 4 (ks ^ f / 4) + (g ^ f % 4), f = tq_swz(n)
+    const int fs = tq_swz(n);
+    int sro[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) sro[j] = 32 * (j ^ (fs >> 2)) + 8 * (g ^ (fs & 3));
+    // PV reads: dims 16 mb + 4 (n % 4) .. + 3 of row trow: half n % 2 of chunk 2 mb + b (b = n / 2 % 2),
+    // which sits at chunk 2 (mb ^ f / 2) + (b ^ f % 2), f = tq_swz(trow) (rows 16 + trow alike):
+    // halfword 16 (mb - mb % 8) + po[mb % 8]
+    const int fp = tq_swz(trow);
+    int po[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) po[j] = 16 * (j ^ (fp >> 1)) + 8 * (((n >> 1) & 1) ^ (fp & 1)) + 4 * (n & 1);
     f32x4_t acc_o[32];
     float m_run = -INFINITY, l_part = 0.0f;
     bool over = false;
@@ -1246,15 +1275,20 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
         f32x4_t sq[2];  // the query's fp16 remainder terms
         sl[0] = sl[1] = sr[0] = sr[1] = sx[0] = sx[1] = sq[0] = sq[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         {
-            const uint16_t* xa = &xt[buf][n][8 * g];
-            const uint16_t* xb = &xt[buf][16 + n][8 * g];
-            f16x8_t na = *reinterpret_cast<const f16x8_t*>(xa), nb = *reinterpret_cast<const f16x8_t*>(xb);
+            // chunk g + 4 ks of rows n and 16 + n (the same swizzle) sits at halfword
+            // 32 (ks - ks % 4) + sro[ks % 4]
+            const uint16_t* xa = xt_row(buf, n);
+            const uint16_t* xb = xt_row(buf, 16 + n);
+            auto sc_read = [&](const uint16_t* x, int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const f16x8_t*>(x + 32 * (ks & ~3) + sro[ks & 3]);
+            };
+            f16x8_t na = sc_read(xa, 0), nb = sc_read(xb, 0);
 #pragma unroll
             for (int ks = 0; ks < 16; ks++) {
                 const f16x8_t ca2 = na, cb2 = nb;
                 if (ks < 15) {
-                    na = *reinterpret_cast<const f16x8_t*>(xa + 32 * (ks + 1));
-                    nb = *reinterpret_cast<const f16x8_t*>(xb + 32 * (ks + 1));
+                    na = sc_read(xa, ks + 1);
+                    nb = sc_read(xb, ks + 1);
                 }
                 f32x4_t& s0 = (ks & 1) ? sx[0] : sl[0];
                 f32x4_t& s1 = (ks & 1) ? sx[1] : sl[1];
@@ -1320,10 +1354,11 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
         load_share(min(t + 2, ntiles - 1));
         // ---- PV from the tile, the transposed reads four column blocks ahead
         auto pv_read = [&](int mb) __attribute__((always_inline)) {
+            const int off = 16 * (mb & ~7) + po[mb & 7];
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)&xt[buf][trow][16 * mb + tcol]);
+                (__attribute__((address_space(3))) s16x4_t*)(xt_row(buf, trow) + off));
             const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)&xt[buf][16 + trow][16 * mb + tcol]);
+                (__attribute__((address_space(3))) s16x4_t*)(xt_row(buf, 16 + trow) + off));
             const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
             return as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
         };
@@ -1352,9 +1387,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
         p.part_m[c * a.n_heads + head] = m_run;  // log2 units
         p.part_l[c * a.n_heads + head] = l_part;
     }
-    constexpr int SR = DL / 2 + 4;  // floats per staged half row
-    static_assert(sizeof(xt) >= MF_WAVES * MF_HEADS * SR * sizeof(float), "staging fits in the tiles");
-    float* stg = reinterpret_cast<float*>(&xt[0][0][0]) + wave * (MF_HEADS * SR);
+    static_assert(sizeof(xt_mem) >= MF_WAVES * MF_HEADS * SR * sizeof(float), "staging fits in the tiles");
+    float* stg = reinterpret_cast<float*>(xt_mem) + wave * (MF_HEADS * SR);
     const float so = 1.0f / rs;  // exact (a power of two)
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {

@@ -198,7 +198,10 @@ typedef struct kvq_attn_args {
     int32_t n_heads;            /* 1 .. 256                                       */
     int32_t dim_lat;            /* must be 512                                    */
     int32_t dim_rope;           /* must be 64                                     */
-    int32_t split_rows;         /* rows per work item; 0 = automatic              */
+    int32_t split_rows;         /* rows per work item, a multiple of 32; 0 =
+                                   automatic.  fp8 matrix-core path: rounded up to
+                                   whole 128-row tiles, dealt over the sequences in
+                                   order (a work item may span several) */
     int32_t reserved0;          /* must be 0                                      */
     int64_t total_rows;         /* host copy of seq_offsets[n_seqs]               */
     const int64_t* seq_offsets; /* device int64 [n_seqs+1], ascending, [0] = 0    */
@@ -267,8 +270,9 @@ int kvq_decode_attn_noalloc(const kvq_attn_args* a, void* stream);
  *                    R q in the workspace; KVQ_PREC_MFMA: the fp16 query
  *                    operands of every (sequence, head) with their per-head
  *                    power-of-two scales (TQ3/4/6: of R q) and the rope query
- *                    terms (the matrix-core split kernels plan their T-split
- *                    themselves);
+ *                    terms, and for fp8 with several sequences the split
+ *                    kernel's tile plan (tiles per sequence, their prefix and
+ *                    the tiles per work item);
  *   KVQ_STAGE_SPLITS the attention over every T-split (partial softmax states);
  *   KVQ_STAGE_MERGE  merge of the splits (+ un-rotation for TQ3/4/6) into out / lse. */
 #define KVQ_STAGE_PREP 0

@@ -57,7 +57,7 @@ constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to
 constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators are rescaled
 
 struct Plan {
-    int64_t* chunk_prefix;  // [n_seqs + 1]
+    int64_t* chunk_prefix;  // [n_seqs + 2]: chunk prefix; fp8 matrix-core path: tile prefix, total, quota
     float* q_rot;           // fp32 path, rotated codec: [n_seqs][H][512]
     uint4* q_pack;          // matrix-core paths: [n_seqs][H padded][QPACK_U4 (fp8, in operand order per
                             // group) or QPACK_TQ]
@@ -71,6 +71,12 @@ struct Plan {
     int n_groups;
     int heads_padded;
     int64_t chunks_per_xcd; // matrix-core grid: chunk c runs on XCD c % 8, all its head groups together
+    // fp8 matrix-core path: each head group's F8_TILE-row tiles (every sequence's, in order) are
+    // dealt in runs of tile_quota to n_work work items; a work item writes one partial state per
+    // sequence it touches, in slot (work item + sequence), so max_chunks = n_work + n_seqs
+    int64_t n_work;
+    int64_t n_tiles;        // one sequence: the tile count (several: computed by the preparation)
+    int64_t tile_quota;     // 0: the preparation computes max(1, ceil(tiles / n_work))
 };
 
 // ---- workspace plan ------------------------------------------------------------
@@ -87,16 +93,7 @@ int auto_split_rows(const kvq_attn_args& a) {
         if (split > (1 << 24)) split = 1 << 24;
         return (int)split;
     }
-    // fp8: about one workgroup per compute unit over all splits and groups of
-    // 32 heads, whole 128-row tiles, at least two tiles per split; large splits
-    // keep the partial states (32 heads x 2 KB per split and group) below the
-    // KV bytes they summarize.
-    const int64_t groups = (a.n_heads + F8_HEADS - 1) / F8_HEADS;
-    int64_t split = (a.total_rows * groups + 255) / 256;
-    if (split < 2 * F8_TILE) split = 2 * F8_TILE;
-    split = (split + F8_TILE - 1) / F8_TILE * F8_TILE;
-    if (split > (1 << 24)) split = 1 << 24;
-    return (int)split;
+    return F8_TILE;  // fp8 matrix-core path: work items of whole tiles (see make_plan)
 }
 
 Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
@@ -112,7 +109,26 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     p.max_chunks = std::max<int64_t>(a.n_seqs, std::min<int64_t>(a.total_rows / p.split_rows + a.n_seqs,
                                                                   (a.total_rows + p.split_rows - 1) / p.split_rows +
                                                                       a.n_seqs - 1));
-    p.chunks_per_xcd = (p.max_chunks + N_XCD - 1) / N_XCD;
+    if (!f32 && a.qmode == KVQ_QMODE_FP8) {
+        // one work item per compute unit over the head groups (at least two tiles each), or
+        // split_rows / F8_TILE tiles each when the caller fixes it
+        const int64_t ub = (a.total_rows + F8_TILE - 1) / F8_TILE + a.n_seqs;  // >= sum_s ceil(T_s / F8_TILE)
+        if (a.split_rows > 0) {
+            p.tile_quota = (a.split_rows + F8_TILE - 1) / F8_TILE;
+            p.n_work = std::max<int64_t>(1, (ub + p.tile_quota - 1) / p.tile_quota);
+        } else {
+            p.tile_quota = 0;
+            p.n_work = std::max<int64_t>(1, std::min<int64_t>(256 / p.n_groups, (ub + 1) / 2));
+        }
+        if (a.n_seqs == 1) {
+            p.n_tiles = (a.total_rows + F8_TILE - 1) / F8_TILE;
+            if (p.tile_quota == 0) p.tile_quota = std::max<int64_t>(1, (p.n_tiles + p.n_work - 1) / p.n_work);
+        }
+        p.max_chunks = p.n_work + a.n_seqs;
+        p.chunks_per_xcd = (p.n_work + N_XCD - 1) / N_XCD;
+    } else {
+        p.chunks_per_xcd = (p.max_chunks + N_XCD - 1) / N_XCD;
+    }
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
     int64_t off = 0;
     char* base = (char*)ws;
@@ -121,7 +137,7 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
         off = align(off + bytes);
         return q;
     };
-    p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
+    p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 2));
     if (f32 && qmode_rotated(a.qmode)) p.q_rot = (float*)take(sizeof(float) * (int64_t)a.n_seqs * a.n_heads * DL);
     if (!f32) {  // matrix-core paths: the prepared query operands
         const int64_t rows_q = (int64_t)a.n_seqs * p.heads_padded;
@@ -624,10 +640,49 @@ __device__ __forceinline__ bool locate_chunk(const kvq_attn_args& a, const Plan&
 // .. + 7 (i < 16, j < 2, h < 2); uint4 2048 + (((i * 2 + j) * 2 + t) * 2 + h) *
 // 32 + n its rope dims 32 i + 16 h + 8 j .. + 7, term t (0: hi, 1: lo; i < 2).
 // One wave per (sequence, head); lane l converts dims 8 l .. 8 l + 7.
+// The split kernel's tile plan over several sequences (one workgroup): tiles of
+// sequence s = ceil(T_s / F8_TILE) (T_s clamped as in the plan), their exclusive
+// prefix, the total and the quota of tiles per work item.
+__device__ __forceinline__ void plan_tiles_fp8(const kvq_attn_args& a, const Plan& p) {
+    __shared__ int64_t wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int64_t run = 0;
+    for (int base = 0; base < a.n_seqs; base += 256) {
+        const int s = base + tid;
+        int64_t cnt = 0;
+        if (s < a.n_seqs) {
+            const int64_t lo = max(a.seq_offsets[s], (int64_t)0), hi = min(a.seq_offsets[s + 1], a.total_rows);
+            cnt = hi > lo ? (hi - lo + F8_TILE - 1) / F8_TILE : 0;
+        }
+        int64_t incl = cnt;  // inclusive scan over the wave, then over the waves
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        int64_t before = run;
+        for (int k = 0; k < wv; k++) before += wsum[k];
+        if (s < a.n_seqs) p.chunk_prefix[s] = before + incl - cnt;
+        run += (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+        __syncthreads();
+    }
+    if (tid == 0) {
+        p.chunk_prefix[a.n_seqs] = run;
+        p.chunk_prefix[a.n_seqs + 1] =
+            p.tile_quota > 0 ? p.tile_quota : max((int64_t)1, (run + p.n_work - 1) / p.n_work);
+    }
+}
+
 __global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p, NewRows nr) {
     const int lane = threadIdx.x & 63;
     const int64_t prep_rows = (int64_t)a.n_seqs * p.heads_padded;
-    const int64_t prep_blocks = (prep_rows + 3) / 4;
+    const int64_t prep_blocks = (prep_rows + 3) / 4, enc_blocks = (nr.n + 3) / 4;
+    if ((int64_t)blockIdx.x >= prep_blocks + enc_blocks) {  // the last block, several sequences: the tile plan
+        plan_tiles_fp8(a, p);
+        return;
+    }
     if ((int64_t)blockIdx.x >= prep_blocks) {  // the rows appended by this call: one wave per row
         const int64_t r = ((int64_t)blockIdx.x - prep_blocks) * 4 + (threadIdx.x >> 6);
         if (r < nr.n) encode_fp8_row<1>(nr.x + r * DL, DL, nr.codes + r * DL, nr.scales + r, lane);
@@ -694,12 +749,16 @@ __global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p, NewR
 // 16-byte chunk c stored at chunk c ^ (r % 16), which puts the rows any read
 // below serves on distinct banks (checked on the CPU).
 //
-// Softmax: one reference per head for the whole workgroup (the first tile's
-// maximum, agreed through LDS at a barrier every tile); probabilities are
-// 2^(s - m) <= 2^8, times rho * rsc (rsc a power of two with max rho * rsc < 1
-// over the chunk), rounded to fp16.  A tile whose maximum exceeds the reference
-// by more than 2^8 raises it and the workgroup starts its rows again: the
-// accumulators are never rescaled inside the loop.
+// Softmax: one reference per head for the whole workgroup, the first tile's
+// maximum, agreed through LDS at a barrier (B1) on that tile only;
+// probabilities are 2^(s - m) <= 2^8, times rho * rsc (rsc a power of two with
+// max rho * rsc < 1 over the chunk), rounded to fp16.  Every tile's maxima go
+// to LDS beside its P, and after the barrier that publishes P (B2) a tile
+// whose maximum exceeds the reference by more than 2^8 raises it and the
+// workgroup starts its rows again (its P is then discarded): the accumulators
+// are never rescaled inside the loop.  P and the maxima are double-buffered by
+// tile parity, since without a barrier between B2 of tile t and the P writes
+// of tile t + 1 a wave may still be reading P of tile t.
 constexpr int F8_WROWS = 32;                    // score rows per wave
 constexpr int F8_WBYTES = F8_WROWS * DL;        // one wave's rows in a code buffer: 16 KB
 constexpr int F8_BUF = MF_WAVES * F8_WBYTES;    // a code buffer: 64 KB
@@ -707,9 +766,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct F8Smem {
     uint8_t code[2][F8_BUF];               // raw e4m3 rows
-    uint4 p[8][2][F8_HEADS];               // P^T per k-step of 16 rows: [step][lane half][head] x 8 fp16
+    uint4 p[2][8][2][F8_HEADS];            // P^T per k-step of 16 rows: [parity][step][lane half][head] x 8 fp16
     float rho[2][MF_WAVES][64];            // each wave's row scales (lanes 32..63 hold copies)
-    float xch[MF_WAVES][F8_HEADS];         // per-wave values per head: tile maxima, then sums
+    float xch[2][MF_WAVES][F8_HEADS];      // per-wave tile maxima per head
+    float lsum[MF_WAVES][F8_HEADS];        // per-wave probability sums per head (a segment's end)
     float red[MF_WAVES];
 };
 static_assert(sizeof(F8Smem) <= 160 * 1024, "LDS");
@@ -721,20 +781,41 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(uint4 a, uint4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+template <bool ONE>  // one sequence: the tile plan is the host's, and every work item is one segment
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) F8Smem sm;
-    __shared__ int64_t plan_s[3];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int h = lane >> 5, n = lane & 31;  // lane half, head (and score row) within the group
     const int64_t local = blockIdx.x / N_XCD;
-    const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
+    const int64_t w = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);  // work item of the group
     const int hg = (int)(local % p.n_groups);
-    if (c >= p.max_chunks) return;
-    int64_t r0, r1;
-    int sq;
-    if (!locate_chunk(a, p, c, plan_s, wave, lane, r0, r1, sq)) return;  // workgroup-uniform
-    const int ntiles = (int)((r1 - r0 + F8_TILE - 1) / F8_TILE);
+    if (w >= p.n_work) return;
+    // this work item's tiles [tb, te) of the group's tile list (every sequence's tiles in order);
+    // with several sequences the prefix, the total and the quota come from the preparation launch
+    constexpr bool one = ONE;
+    const int64_t* tp = p.chunk_prefix;
+    const int64_t ntot = one ? p.n_tiles : tp[a.n_seqs];
+    const int64_t quota = one ? p.tile_quota : tp[a.n_seqs + 1];
+    const int64_t tb = w * quota, te = min(ntot, tb + quota);
+    if (tb >= te) return;  // workgroup-uniform
+    // sequence s: rows [seq_lo, seq_hi) (clamped as in the plan), tiles [seq_t0, seq_t1) of the list
+    auto seq_lo = [&](int s) { return one ? (int64_t)0 : max(a.seq_offsets[s], (int64_t)0); };
+    auto seq_hi = [&](int s) { return one ? a.total_rows : min(a.seq_offsets[s + 1], a.total_rows); };
+    auto seq_t0 = [&](int s) { return one ? (int64_t)0 : tp[s]; };
+    auto seq_t1 = [&](int s) { return one ? ntot : tp[s + 1]; };
+    auto seq_of = [&](int64_t t) {  // the sequence holding tile t: the last s with seq_t0(s) <= t
+        if (one) return 0;
+        int lo = 0, hi = a.n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tp[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    auto tile_row = [&](int64_t t, int s) { return seq_lo(s) + (int64_t)F8_TILE * (t - seq_t0(s)); };
+    int sq = seq_of(tb);
     const int head = hg * F8_HEADS + n;
 
     // ---- loaders.  The DMA of a tile brings this wave's 32 score rows: instruction
@@ -768,8 +849,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             for (int j = 0; j < 2; j++)
                 kr[i][j] = *reinterpret_cast<const uint4*>(a.k_rope + row * DR + 32 * i + 16 * h + 8 * j);
     };
-    if (ntiles > 0) {  // workgroup-uniform
-        const int64_t tw = r0 + F8_WROWS * wave;
+    {
+        const int64_t tw = tile_row(tb, sq) + F8_WROWS * wave;
 #pragma unroll
         for (int k = 0; k < 17; k++) dma_one(k, tw, 0);
         load_rope(tw);
@@ -788,13 +869,21 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             dma_lds_b128(qp + 64 * blk, 16u * lane, lq + 1024u * blk);
         }
     }
-    const float qinv = p.q_inv[(int64_t)sq * p.heads_padded + head];
-    // ---- rsc from the chunk's largest row scale (four loads in flight per thread)
+    float qinv = p.q_inv[(int64_t)sq * p.heads_padded + head];
+    // ---- rsc from the largest row scale of the work item's rows (contiguous over its
+    // sequences; four loads in flight per thread)
+    const int64_t r0 = tile_row(tb, sq);
+    int64_t r1;
+    {
+        const int sl = seq_of(te - 1);
+        r1 = min(tile_row(te - 1, sl) + F8_TILE, seq_hi(sl));
+        r1 = max(r1, r0 + 1);
+    }
     float rm = 0.0f;
     for (int64_t t = r0 + tid; t < r1; t += 4 * MF_WAVES * 64) {
         float x[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(t + u * MF_WAVES * 64, r1 - 1)];
+        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(min(t + u * MF_WAVES * 64, r1 - 1), a.total_rows - 1)];
 #pragma unroll
         for (int u = 0; u < 4; u++) rm = fmaxf(rm, fabsf(x[u]));
     }
@@ -818,7 +907,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 rl[i][j] = q4[2048 + ((i * 2 + j) * 2 + 1) * 64];
             }
     }
-    const float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
+    float k1 = a.sm_scale * LOG2E * qinv;  // latent score scale (log2 units)
     const float rsc = pow2_scale_for(fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3])), -1);
 
     // ---- per-lane LDS addresses
@@ -835,6 +924,11 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         pv_addr[b] = pv_r * 512u + (((uint32_t)(8 * wave + 2 * b + mh) ^ pv_r) << 4) + 8u * (uint32_t)(q16 & 1);
 
     f32x16_t acc_o[4];
+    int g0 = 0;  // buffer and P parity of the segment's first tile
+    int64_t t_seg = tb;
+    for (;;) {  // segments: the work item's tiles of one sequence
+    const int64_t seg_t1 = min(te, seq_t1(sq));
+    const int64_t s_t0 = seq_t0(sq), s_lo = seq_lo(sq), s_hi = seq_hi(sq);
     float m_ref = -INFINITY;  // per head (lane n), identical in every wave
     float l_part = 0.0f;
     for (;;) {
@@ -842,9 +936,14 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     for (int b = 0; b < 4; b++) acc_o[b] = f32x16_t{};
     l_part = 0.0f;
     bool again = false;
-    for (int t = 0; t < ntiles; t++) {
-        const int buf = t & 1;
-        const int64_t tw = r0 + (int64_t)F8_TILE * t + F8_WROWS * wave;  // this wave's first score row
+    // (a counted loop from 0: with a bottom-tested loop LLVM copies the accumulators
+    // between register files every tile)
+    const int ntl = (int)(seg_t1 - t_seg);
+    const bool seg_more = !ONE && seg_t1 < te;  // the work item goes on with another segment
+    for (int k = 0; k < ntl; k++) {
+        const int64_t t = t_seg + k;
+        const int buf = (g0 + k) & 1;
+        const int64_t tw = s_lo + (int64_t)F8_TILE * (t - s_t0) + F8_WROWS * wave;  // this wave's first score row
         vm_wait_all();  // this wave's rows, row scales and rope keys of the tile have landed
         // ---- scores: rope first (its keys are then free for the next tile's), latent on two chains
         f32x16_t s_r = f32x16_t{}, s_a = f32x16_t{}, s_b = f32x16_t{};
@@ -855,8 +954,11 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 s_r = mfma32_bf16(kr[i][j], rh[i][j], s_r);
                 s_r = mfma32_bf16(kr[i][j], rl[i][j], s_r);
             }
-        const bool more = t + 1 < ntiles;  // workgroup-uniform
-        if (more) load_rope(tw + F8_TILE);
+        // workgroup-uniform: a next tile, of this segment or the next (written on the loop
+        // counter: a 64-bit compare here made LLVM move the accumulators every tile)
+        const bool more = k + 1 < ntl || seg_more;
+        const int64_t ntw = (ONE || k + 1 < ntl) ? tw + F8_TILE : tile_row(t + 1, seq_of(t + 1)) + F8_WROWS * wave;
+        if (more) load_rope(ntw);
         const uint8_t* cw = &sm.code[buf][0] + sc_row;
         auto chunk = [&](int i) {
             return *reinterpret_cast<const uint4*>(cw + ((((uint32_t)(2 * i + h)) ^ sc_x) << 4));
@@ -878,7 +980,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- softmax: lane (h, n) holds rows 8 (r / 4) + 4 h + r % 4 of head n
-        const int nvw = (int)min((int64_t)F8_WROWS, r1 - tw);  // valid rows of this wave's block (may be <= 0)
+        const int nvw = (int)min((int64_t)F8_WROWS, s_hi - tw);  // valid rows of this wave's block (may be <= 0)
         float sc[16], rr[16];
         float tmax = -INFINITY;
 #pragma unroll
@@ -895,14 +997,11 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             }
         }
         tmax = fmaxf(tmax, xor_lane<32>(tmax, lane));
-        if (h == 0) sm.xch[wave][n] = tmax;
-        wg_barrier_lds();  // B1: every wave's tile maxima
-        const float mt = fmaxf(fmaxf(sm.xch[0][n], sm.xch[1][n]), fmaxf(sm.xch[2][n], sm.xch[3][n]));
-        m_ref = m_ref == -INFINITY ? mt : m_ref;  // first tile: the workgroup's maximum (finite)
-        if (__any(mt > m_ref + LAZY_LOG2)) {  // workgroup-uniform: every wave sees the same maxima
-            m_ref = fmaxf(m_ref, mt);
-            again = true;
-            break;
+        const int par = buf;
+        if (h == 0) sm.xch[par][wave][n] = tmax;
+        if (m_ref == -INFINITY) {  // the first tile (workgroup-uniform): agree on the reference
+            wg_barrier_lds();      // B1: every wave's tile maxima
+            m_ref = fmaxf(fmaxf(sm.xch[par][0][n], sm.xch[par][1][n]), fmaxf(sm.xch[par][2][n], sm.xch[par][3][n]));
         }
         float psum = 0.0f;
         uint32_t pk[8];
@@ -912,11 +1011,19 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             psum += p0 + p1;
             pk[r / 2] = pack_f16x2(p0 * (rr[r] * rsc), p1 * (rr[r + 1] * rsc));
         }
+        // (buffer par: the PV of tile t - 2 read it, and every wave was past that PV at B2 of tile t - 1)
+        sm.p[par][2 * wave][h][n] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        sm.p[par][2 * wave + 1][h][n] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        wg_barrier_lds();  // B2: P of every row, every wave's tile maxima and rows of the tile are in LDS
+        {
+            const float mt = fmaxf(fmaxf(sm.xch[par][0][n], sm.xch[par][1][n]), fmaxf(sm.xch[par][2][n], sm.xch[par][3][n]));
+            if (__any(mt > m_ref + LAZY_LOG2)) {  // workgroup-uniform: every wave sees the same maxima
+                m_ref = fmaxf(m_ref, mt);
+                again = true;
+                break;
+            }
+        }
         l_part += psum;
-        // (one buffer: the previous tile's PV read it, and every wave is past that PV at B1)
-        sm.p[2 * wave][h][n] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-        sm.p[2 * wave + 1][h][n] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-        wg_barrier_lds();  // B2: P of every row and every wave's rows of the tile are in LDS
         // ---- PV over the tile's 8 k-steps, each step's reads issued during the one
         // before; the next tile's DMA goes out between the steps
         const uint8_t* vb = &sm.code[buf][0];
@@ -924,7 +1031,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(
                 vb + (J >> 1) * F8_WBYTES + (J & 1) * 16 * 512 + pv_addr[b]));
         };
-        uint4 bp = sm.p[0][h][n];
+        uint4 bp = sm.p[par][0][h][n];
         i32x2_t tv[4];
 #pragma unroll
         for (int b = 0; b < 4; b++) tv[b] = pv_read(0, b);
@@ -935,15 +1042,15 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 #pragma unroll
             for (int b = 0; b < 4; b++) cv[b] = tv[b];
             if (J < 7) {
-                bp = sm.p[J + 1][h][n];
+                bp = sm.p[par][J + 1][h][n];
 #pragma unroll
                 for (int b = 0; b < 4; b++) tv[b] = pv_read(J + 1, b);
             }
             __builtin_amdgcn_sched_barrier(0);  // the next step's reads issue before this step's math
             if (more) {
-                dma_one(2 * J, tw + F8_TILE, buf ^ 1);
-                dma_one(2 * J + 1, tw + F8_TILE, buf ^ 1);
-                if (J == 7) dma_one(16, tw + F8_TILE, buf ^ 1);
+                dma_one(2 * J, ntw, buf ^ 1);
+                dma_one(2 * J + 1, ntw, buf ^ 1);
+                if (J == 7) dma_one(16, ntw, buf ^ 1);
             }
 #pragma unroll
             for (int b = 0; b < 4; b++) {
@@ -953,23 +1060,29 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    vm_wait_all();  // DMA and rope loads in flight (restart or epilogue)
-    if (!again) break;
+    if (!again) {
+        g0 += ntl;
+        break;
+    }
+    vm_wait_all();    // the rope loads in flight
     __syncthreads();  // every wave has read the tile maxima before they are written again
-    if (ntiles > 0) {  // start the rows again with the raised reference
-        const int64_t tw = r0 + F8_WROWS * wave;
+    {  // start the segment's rows again with the raised reference (both buffers are free)
+        g0 = 0;
+        const int64_t tw = s_lo + (int64_t)F8_TILE * (t_seg - s_t0) + F8_WROWS * wave;
 #pragma unroll
         for (int k = 0; k < 17; k++) dma_one(k, tw, 0);
         load_rope(tw);
     }
     }
 
-    // ---- epilogue: l per head over the waves, then each wave's dims of every head
+    // ---- the segment's partial state, in slot w + sq (the merge reads a sequence's slots
+    // as one run): l per head over the waves, then each wave's dims of every head.  The
+    // next segment's first tile is in flight meanwhile.
+    const int64_t c = w + sq;
     float lt = l_part + xor_lane<32>(l_part, lane);
-    __syncthreads();  // every wave is done with xch
-    if (h == 0) sm.xch[wave][n] = lt;
-    __syncthreads();
-    const float L = (sm.xch[0][n] + sm.xch[1][n]) + (sm.xch[2][n] + sm.xch[3][n]);
+    if (h == 0) sm.lsum[wave][n] = lt;
+    wg_barrier_lds();  // (LDS only: the next segment's first tile stays in flight)
+    const float L = (sm.lsum[0][n] + sm.lsum[1][n]) + (sm.lsum[2][n] + sm.lsum[3][n]);
     {
         // partial O of this (chunk, group) in the matrix cores' lane order: float4
         // ((w * 4 + b) * 4 + j) * 64 + lane holds head n = lane % 32, dims 128 w + 32 b +
@@ -987,6 +1100,28 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
             p.part_m[c * a.n_heads + head] = m_ref;  // log2 units
             p.part_l[c * a.n_heads + head] = L;
         }
+    }
+    t_seg = seg_t1;
+    if (ONE || t_seg >= te) break;
+    // ---- the next sequence: its query operands straight from the prepared pack (the
+    // staging buffer holds a tile by now)
+    sq = seq_of(t_seg);
+    {
+        const uint4* q4 = p.q_pack + ((int64_t)sq * p.heads_padded + hg * F8_HEADS) * QPACK_U4 + lane;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) qh[i][j] = q4[(i * 2 + j) * 64];
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                rh[i][j] = q4[2048 + ((i * 2 + j) * 2 + 0) * 64];
+                rl[i][j] = q4[2048 + ((i * 2 + j) * 2 + 1) * 64];
+            }
+        qinv = p.q_inv[(int64_t)sq * p.heads_padded + head];
+        k1 = a.sm_scale * LOG2E * qinv;
+    }
     }
 }
 
@@ -1549,7 +1684,19 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
     const int g = (int)(sg % p.n_groups), s = (int)(sg / p.n_groups);
     const int head = g * F8_HEADS + n;
     const int hc = min(head, a.n_heads - 1);  // a padded head reads a real one's m, l and is not written
-    const int64_t c0 = min(p.chunk_prefix[s], p.max_chunks), c1 = min(p.chunk_prefix[s + 1], p.max_chunks);
+    // sequence s's partial states: slots (work item + s) of the work items its tiles went to
+    int64_t c0 = 0, c1 = 0;
+    {
+        const bool one = a.n_seqs == 1;
+        const int64_t t0 = one ? 0 : p.chunk_prefix[s], t1 = one ? p.n_tiles : p.chunk_prefix[s + 1];
+        const int64_t q = one ? p.tile_quota : p.chunk_prefix[a.n_seqs + 1];
+        if (t1 > t0) {
+            c0 = t0 / q + s;
+            c1 = (t1 - 1) / q + s + 1;
+        }
+        c0 = min(c0, p.max_chunks);
+        c1 = min(c1, p.max_chunks);
+    }
     const float4* src = reinterpret_cast<const float4*>(p.part_o) + g * (int64_t)(F8_HEADS * DL / 4) + wbj * 64 + l;
     const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
     float m = -INFINITY, lsum = 0.0f;
@@ -1623,7 +1770,7 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
                     hipLaunchKernelGGL(k_qprep_tq4, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, p);
                 } else {  // with the fp8 encode of the appended rows, if any, in the same launch
                     const NewRows n = nr ? *nr : none;
-                    const int64_t blocks = (rows + 3) / 4 + (n.n + 3) / 4;
+                    const int64_t blocks = (rows + 3) / 4 + (n.n + 3) / 4 + (a.n_seqs > 1 ? 1 : 0);
                     hipLaunchKernelGGL(k_qprep_fp8, dim3((unsigned)blocks), dim3(256), 0, st, a, p, n);
                 }
                 break;
@@ -1652,7 +1799,10 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
                     case KVQ_QMODE_TQ4: hipLaunchKernelGGL(k_attn_mfma_tq<4>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
                     case KVQ_QMODE_TQ3: hipLaunchKernelGGL(k_attn_mfma_tq<3>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
                     case KVQ_QMODE_TQ6: hipLaunchKernelGGL(k_attn_mfma_tq<6>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
-                    default: hipLaunchKernelGGL(k_attn_mfma_fp8, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
+                    default:
+                        if (a.n_seqs == 1) hipLaunchKernelGGL(k_attn_mfma_fp8<true>, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+                        else hipLaunchKernelGGL(k_attn_mfma_fp8<false>, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+                        break;
                 }
             }
             break;

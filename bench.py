@@ -68,6 +68,20 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 10}), flush=True)
 
 
+def fp8_kernel_sha256():
+    """sha256 of the fp8 split kernel's source: kvq_attn.hip up to the end of that
+    kernel (the kernel and every helper, constant and struct it uses are defined
+    above that point), then kvq_device.h and kvq_internal.h."""
+    import hashlib
+
+    src = open(KERNEL_SOURCE, "rb").read()
+    end = src.index(b"// Rotated-codec query preparation:")
+    h = hashlib.sha256(src[:end])
+    for name in ("kvq_device.h", "kvq_internal.h"):
+        h.update(open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per split-kernel launch from the committed counter summary:
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled by
@@ -82,8 +96,7 @@ def measured_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if kv.get("source_sha256") != sha:
+    if kv.get("source_sha256") != fp8_kernel_sha256():
         return None
     fetch = float(kv["fetch_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_fetch_kib_per_dispatch"])
     write = float(kv["write_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_write_kib_per_dispatch"])

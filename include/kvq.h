@@ -307,9 +307,14 @@ int kvq_gather_rows(int qmode, const uint8_t* codes, const float* row_scale, con
  *  - a->seq_offsets partitions the index list, and a->total_rows = n_index is
  *    its host copy of seq_offsets[n_seqs].
  *  - a->codes, a->row_scale and a->k_rope describe the whole cache of
- *    cache_rows rows.
- *  - The result equals kvq_decode_attn over the gathered rows: the call gathers
- *    them into the workspace (kvq_gather_rows), then runs the same kernels.
+ *    cache_rows rows, 1 <= cache_rows < 2^32 (KVQ_ERR_INVALID_ARG otherwise;
+ *    0 is accepted when the index list is empty).  Indices are clamped as in
+ *    kvq_gather_rows.
+ *  - The result equals kvq_decode_attn over the gathered rows, bit for bit.
+ *    On the fp8 matrix-core path (KVQ_QMODE_FP8, KVQ_PREC_MFMA) the split
+ *    kernel reads the selected rows in place through the index list; the
+ *    other paths gather them into the workspace (kvq_gather_rows) and run the
+ *    dense kernels over the copy.
  *  - A repeated index counts once per occurrence.
  *  - The workspace is device memory, 256-byte aligned, of at least
  *    kvq_decode_attn_sparse_workspace_bytes(a) bytes.  That function returns

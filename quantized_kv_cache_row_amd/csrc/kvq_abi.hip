@@ -300,7 +300,7 @@ int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int
     int rc = check_attn(a);
     if (rc != KVQ_OK) return rc;
     if (a->total_rows > ((int64_t)1 << 33)) return KVQ_ERR_UNSUPPORTED;
-    if (cache_rows < 0) return KVQ_ERR_INVALID_ARG;
+    if (cache_rows < 0 || cache_rows > (int64_t)0xFFFFFFFF) return KVQ_ERR_INVALID_ARG;
     if (a->total_rows > 0 && (cache_rows < 1 || !row_index || !aligned(row_index, 8))) return KVQ_ERR_INVALID_ARG;
     const int64_t need = kvq::attn_sparse_workspace_bytes(*a);
     if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;

@@ -77,6 +77,10 @@ struct Plan {
     int64_t n_work;
     int64_t n_tiles;        // one sequence: the tile count (several: computed by the preparation)
     int64_t tile_quota;     // 0: the preparation computes max(1, ceil(tiles / n_work))
+    // sparse decode on the fp8 matrix-core path: logical row t of the index list is cache row
+    // clamp(row_index[t], 0, cache_rows - 1), read in place (null: the rows are contiguous)
+    const int64_t* row_index;
+    int64_t cache_rows;
 };
 
 // ---- workspace plan ------------------------------------------------------------
@@ -554,6 +558,13 @@ __device__ __forceinline__ void dma_lds_b32(const void* sbase, uint32_t voff, ui
                  : "v"(voff), "s"(sbase), "{m0}"(lds_base)
                  : "memory");
 }
+// Per-lane 64-bit address form (rows gathered by index: every lane its own row).
+__device__ __forceinline__ void dma_lds_b128_at(const void* vaddr, uint32_t lds_base) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(vaddr), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma_lds_b32_at(const void* vaddr, uint32_t lds_base) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" : : "v"(vaddr), "{m0}"(lds_base) : "memory");
+}
 // max over the four lanes n, n ^ 16, n ^ 32, n ^ 48 (gfx950 lane-swap
 // instructions: each pairs a lane with the one 16 or 32 lanes away).
 __device__ __forceinline__ float max_xor16_xor32(float v) {
@@ -781,7 +792,9 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(uint4 a, uint4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-template <bool ONE>  // one sequence: the tile plan is the host's, and every work item is one segment
+// ONE: one sequence (the tile plan is the host's, and every work item is one segment).
+// GATHER: sparse decode, the rows of the index list read in place (p.row_index).
+template <bool ONE, bool GATHER>
 __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a, Plan p) {
     __shared__ __align__(16) F8Smem sm;
     const int tid = threadIdx.x;
@@ -817,6 +830,14 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     auto tile_row = [&](int64_t t, int s) { return seq_lo(s) + (int64_t)F8_TILE * (t - seq_t0(s)); };
     int sq = seq_of(tb);
     const int head = hg * F8_HEADS + n;
+    // GATHER: the cache row of logical row t (t < total_rows is not required: rows past the
+    // list re-read its last entry); gp = that row for row tw + lane % 32 of the wave block
+    // whose loads are issued next
+    auto phys = [&](int64_t t) -> uint32_t {
+        const int64_t r = p.row_index[min(t, a.total_rows - 1)];
+        return (uint32_t)min(max(r, (int64_t)0), p.cache_rows - 1);
+    };
+    uint32_t gp = 0;
 
     // ---- loaders.  The DMA of a tile brings this wave's 32 score rows: instruction
     // k (0..15) fills LDS chunks 64 k .. 64 k + 63 of the wave's 16 KB, lane l the
@@ -827,6 +848,18 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     const uint32_t lds_code0 = lds_offset(&sm.code[0][0]) + (uint32_t)wave * F8_WBYTES;
     const uint32_t lds_rho0 = lds_offset(&sm.rho[0][0][0]) + (uint32_t)wave * 256u;
     auto dma_one = [&](int k, int64_t tw, int buf) __attribute__((always_inline)) {
+        if constexpr (GATHER) {  // rows 2 k + h of the block from their cache rows (gp)
+            if (k < 16) {
+                const uint32_t g0 = __builtin_amdgcn_readlane(gp, 2 * k), g1 = __builtin_amdgcn_readlane(gp, 2 * k + 1);
+                const uint32_t gr = h ? g1 : g0;
+                dma_lds_b128_at(a.codes + (uint64_t)gr * DL + ((dma_c ^ (uint32_t)((2 * k) & 15)) << 4),
+                                __builtin_amdgcn_readfirstlane(lds_code0 + (uint32_t)buf * F8_BUF + 1024u * k));
+            } else {
+                dma_lds_b32_at(a.row_scale + gp,
+                               __builtin_amdgcn_readfirstlane(lds_rho0 + (uint32_t)buf * (MF_WAVES * 256u)));
+            }
+            return;
+        }
         // tw: first row of this wave's block; the base row and the offsets stay inside the arrays
         const int64_t b = min(tw, a.total_rows - 1);
         const uint32_t lim = (uint32_t)(a.total_rows - b);  // rows from b to the end, >= 1
@@ -842,7 +875,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     // rope keys of this wave's score rows: lane (h, n) takes row n, dims 32 i + 16 h .. + 15 (i = 0, 1)
     uint4 kr[2][2];
     auto load_rope = [&](int64_t tw) __attribute__((always_inline)) {
-        const int64_t row = min(tw + n, a.total_rows - 1);
+        const int64_t row = GATHER ? (int64_t)gp : min(tw + n, a.total_rows - 1);
 #pragma unroll
         for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -851,6 +884,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     };
     {
         const int64_t tw = tile_row(tb, sq) + F8_WROWS * wave;
+        if (GATHER) gp = phys(tw + (lane & 31));
 #pragma unroll
         for (int k = 0; k < 17; k++) dma_one(k, tw, 0);
         load_rope(tw);
@@ -883,7 +917,10 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     for (int64_t t = r0 + tid; t < r1; t += 4 * MF_WAVES * 64) {
         float x[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(min(t + u * MF_WAVES * 64, r1 - 1), a.total_rows - 1)];
+        for (int u = 0; u < 4; u++) {
+            const int64_t tr = min(min(t + u * MF_WAVES * 64, r1 - 1), a.total_rows - 1);
+            x[u] = a.row_scale[GATHER ? (int64_t)phys(tr) : tr];
+        }
 #pragma unroll
         for (int u = 0; u < 4; u++) rm = fmaxf(rm, fabsf(x[u]));
     }
@@ -945,6 +982,12 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         const int buf = (g0 + k) & 1;
         const int64_t tw = s_lo + (int64_t)F8_TILE * (t - s_t0) + F8_WROWS * wave;  // this wave's first score row
         vm_wait_all();  // this wave's rows, row scales and rope keys of the tile have landed
+        if constexpr (GATHER) {  // the next tile's cache rows, used from its first DMA (in the PV below)
+            if (k + 1 < ntl || seg_more) {
+                const int64_t gtw = (ONE || k + 1 < ntl) ? tw + F8_TILE : tile_row(t + 1, seq_of(t + 1)) + F8_WROWS * wave;
+                gp = phys(gtw + (lane & 31));
+            }
+        }
         // ---- scores: rope first (its keys are then free for the next tile's), latent on two chains
         f32x16_t s_r = f32x16_t{}, s_a = f32x16_t{}, s_b = f32x16_t{};
 #pragma unroll
@@ -958,7 +1001,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
         // counter: a 64-bit compare here made LLVM move the accumulators every tile)
         const bool more = k + 1 < ntl || seg_more;
         const int64_t ntw = (ONE || k + 1 < ntl) ? tw + F8_TILE : tile_row(t + 1, seq_of(t + 1)) + F8_WROWS * wave;
-        if (more) load_rope(ntw);
+        if (!GATHER && more) load_rope(ntw);  // (GATHER: with the first DMAs, after gp has landed)
         const uint8_t* cw = &sm.code[buf][0] + sc_row;
         auto chunk = [&](int i) {
             return *reinterpret_cast<const uint4*>(cw + ((((uint32_t)(2 * i + h)) ^ sc_x) << 4));
@@ -1051,6 +1094,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
                 dma_one(2 * J, ntw, buf ^ 1);
                 dma_one(2 * J + 1, ntw, buf ^ 1);
                 if (J == 7) dma_one(16, ntw, buf ^ 1);
+                if (GATHER && J == 0) load_rope(ntw);
             }
 #pragma unroll
             for (int b = 0; b < 4; b++) {
@@ -1069,6 +1113,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     {  // start the segment's rows again with the raised reference (both buffers are free)
         g0 = 0;
         const int64_t tw = s_lo + (int64_t)F8_TILE * (t_seg - s_t0) + F8_WROWS * wave;
+        if (GATHER) gp = phys(tw + (lane & 31));
 #pragma unroll
         for (int k = 0; k < 17; k++) dma_one(k, tw, 0);
         load_rope(tw);
@@ -1751,12 +1796,7 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
     if (a.lse && wbj == 0 && h == 0) a.lse[(int64_t)s * a.n_heads + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -INFINITY;
 }
 
-}  // namespace
-
-int64_t attn_workspace_bytes(const kvq_attn_args& a) { return plan_bytes(a); }
-
-hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws, hipStream_t st, const NewRows* nr) {
-    Plan p = make_plan(a, ws, nullptr);
+hipError_t launch_stage(const kvq_attn_args& a, const Plan& p, int stage, hipStream_t st, const NewRows* nr) {
     const NewRows none{nullptr, 0, nullptr, nullptr};
     const bool f32 = a.precision == KVQ_PREC_FP32;
     const bool tq = qmode_rotated(a.qmode);
@@ -1799,10 +1839,17 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
                     case KVQ_QMODE_TQ4: hipLaunchKernelGGL(k_attn_mfma_tq<4>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
                     case KVQ_QMODE_TQ3: hipLaunchKernelGGL(k_attn_mfma_tq<3>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
                     case KVQ_QMODE_TQ6: hipLaunchKernelGGL(k_attn_mfma_tq<6>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
-                    default:
-                        if (a.n_seqs == 1) hipLaunchKernelGGL(k_attn_mfma_fp8<true>, grid, dim3(MF_WAVES * 64), 0, st, a, p);
-                        else hipLaunchKernelGGL(k_attn_mfma_fp8<false>, grid, dim3(MF_WAVES * 64), 0, st, a, p);
+                    default: {
+                        const dim3 wg(MF_WAVES * 64);
+                        if (p.row_index) {
+                            if (a.n_seqs == 1) hipLaunchKernelGGL((k_attn_mfma_fp8<true, true>), grid, wg, 0, st, a, p);
+                            else hipLaunchKernelGGL((k_attn_mfma_fp8<false, true>), grid, wg, 0, st, a, p);
+                        } else {
+                            if (a.n_seqs == 1) hipLaunchKernelGGL((k_attn_mfma_fp8<true, false>), grid, wg, 0, st, a, p);
+                            else hipLaunchKernelGGL((k_attn_mfma_fp8<false, false>), grid, wg, 0, st, a, p);
+                        }
                         break;
+                    }
                 }
             }
             break;
@@ -1828,6 +1875,26 @@ hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws,
         }
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t attn_workspace_bytes(const kvq_attn_args& a) { return plan_bytes(a); }
+
+hipError_t launch_decode_attn_stage(const kvq_attn_args& a, int stage, void* ws, hipStream_t st, const NewRows* nr) {
+    return launch_stage(a, make_plan(a, ws, nullptr), stage, st, nr);
+}
+
+hipError_t launch_decode_attn_indexed(const kvq_attn_args& a, const int64_t* row_index, int64_t cache_rows, void* ws,
+                                      hipStream_t st) {
+    Plan p = make_plan(a, ws, nullptr);
+    p.row_index = row_index;
+    p.cache_rows = cache_rows;
+    for (int stage = KVQ_STAGE_PREP; stage <= KVQ_STAGE_MERGE; stage++) {
+        const hipError_t e = launch_stage(a, p, stage, st, nullptr);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_decode_attn(const kvq_attn_args& a, void* ws, int64_t ws_bytes, hipStream_t st) {

@@ -1,7 +1,9 @@
 // kvq_sparse.hip -- sparse (DSA-style) decode: the row gather by absolute
-// index, and the call that gathers a query's selected rows into the workspace
-// and runs the dense decode kernels over them ([KV8] commit list item 2, the
-// DSA-aware gather; the rebase note on the DSA gather).
+// index, and the sparse decode call ([KV8] commit list item 2, the DSA-aware
+// gather; the rebase note on the DSA gather).  On the fp8 matrix-core path the
+// split kernel reads a query's selected rows in place through the index list;
+// the other paths gather them into the workspace and run the dense decode
+// kernels over the copy.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -50,10 +52,16 @@ int64_t sparse_compact_bytes(const kvq_attn_args& a) {
 }
 }  // namespace
 
-int64_t attn_sparse_workspace_bytes(const kvq_attn_args& a) { return sparse_compact_bytes(a) + attn_workspace_bytes(a); }
+// the fp8 matrix-core path reads the selected rows in place: no compact copy
+static bool sparse_in_place(const kvq_attn_args& a) { return a.qmode == KVQ_QMODE_FP8 && a.precision == KVQ_PREC_MFMA; }
+
+int64_t attn_sparse_workspace_bytes(const kvq_attn_args& a) {
+    return (sparse_in_place(a) ? 0 : sparse_compact_bytes(a)) + attn_workspace_bytes(a);
+}
 
 hipError_t launch_decode_attn_sparse(const kvq_attn_args& a, const int64_t* row_index, int64_t cache_rows, void* ws,
                                      int64_t ws_bytes, hipStream_t st) {
+    if (sparse_in_place(a)) return launch_decode_attn_indexed(a, row_index, cache_rows, ws, st);
     auto align = [](int64_t v) { return (v + 255) & ~(int64_t)255; };
     const int64_t n = a.total_rows;
     const int cb = code_bytes_512(a.qmode);

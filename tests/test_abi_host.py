@@ -125,6 +125,19 @@ def test_refusals_without_launch():
         kvq.KVQ_ERR_INVALID_ARG  # fp8 codes not 8-byte aligned
     assert L.kvq_decode_attn_append(ctypes.byref(a), P(256), 1, P(256), P(256), P(256), need - 1, None) == \
         kvq.KVQ_ERR_WORKSPACE
+    # sparse decode: the fp8 matrix-core path reads the listed rows in place (its workspace is
+    # the dense call's); a cache of 2^32 rows or more is refused
+    a.total_rows = 2048
+    sneed = L.kvq_decode_attn_sparse_workspace_bytes(ctypes.byref(a))
+    assert sneed == L.kvq_decode_attn_workspace_bytes(ctypes.byref(a))
+    for cache_rows in (-1, 1 << 32):
+        assert L.kvq_decode_attn_sparse(ctypes.byref(a), P(256), cache_rows, P(256), sneed, None) == \
+            kvq.KVQ_ERR_INVALID_ARG
+    assert L.kvq_decode_attn_sparse(ctypes.byref(a), P(260), 4096, P(256), sneed, None) == \
+        kvq.KVQ_ERR_INVALID_ARG  # index list not 8-byte aligned
+    a.precision = 1  # the fp32 check path gathers a compact copy first
+    assert L.kvq_decode_attn_sparse_workspace_bytes(ctypes.byref(a)) > L.kvq_decode_attn_workspace_bytes(ctypes.byref(a))
+    a.precision, a.total_rows = 0, 32768
     # q4_0
     c = kvq.KvqQ4Cache(256, 256, 256, 64, 1, 64, 8, 128)
     assert L.kvq_append_q4_0(ctypes.byref(c), 1, P(256), P(256), 1, P(256), P(256), 0, None) == \

@@ -4,7 +4,8 @@ The row gather must match numpy indexing bit for bit (clamping included).
 Sparse attention must match the oracle, on the same codes, within
 max|err| / max|ref| <= 2e-3 (matrix cores) or <= 1e-5 (fp32 check path).
 It must also equal, bit for bit, the dense kernels run over a gathered copy
-of the rows.
+of the rows (on the fp8 matrix-core path the split kernel reads the listed
+rows in place, so this compares two read paths of the same kernel).
 """
 import sys
 
@@ -130,17 +131,77 @@ def test_sparse_edge_lists():
         assert err <= TOL[kvq.KVQ_PREC_MFMA], f"split {split}: {err:.3e}"
 
 
-def test_sparse_equals_dense_on_gathered_copy():
-    _say("sparse attention == dense attention over a gathered copy")
-    w = workloads.SparseDecodeWorkload("sparse-vs-dense", 1005, 4096, [100, 700, 2048], 32)
-    codes, scales = _encode(w)
-    got, glse = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, w.offsets, w.row_index)
-    ix = torch.from_numpy(w.row_index).to(DEV)
-    a, out, lse = _args(w, kvq.KVQ_PREC_MFMA, w.offsets, len(w.row_index), codes[ix].contiguous(),
-                        scales[ix].contiguous(), _t(w.k_rope[w.row_index]))
+def _dense_on_copy(w, codes, scales, offsets, row_index, split_rows=0):
+    """kvq_decode_attn over a gathered copy of the listed rows (indices clamped)."""
+    ix = torch.from_numpy(np.clip(np.asarray(row_index, np.int64), 0, w.cache_rows - 1)).to(DEV)
+    a, out, lse = _args(w, kvq.KVQ_PREC_MFMA, offsets, len(row_index), codes[ix].contiguous(), scales[ix].contiguous(),
+                        _t(w.k_rope[ix.cpu().numpy()]), split_rows)
     kvq.kvq_decode_attn(a, kvq.alloc_workspace(a))
     torch.cuda.synchronize()
-    assert np.array_equal(_np(out).astype(np.float64), got) and np.array_equal(_np(lse).astype(np.float64), glse)
+    return _np(out).astype(np.float64), _np(lse).astype(np.float64)
+
+
+@pytest.mark.parametrize("lengths,split", [([2048], 0), ([100, 700, 2048], 0), ([100, 700, 2048], 256)])
+def test_sparse_equals_dense_on_gathered_copy(lengths, split):
+    """On the fp8 matrix-core path the split kernel reads the listed rows in place;
+    the result is bit-identical to the dense kernels over a gathered copy (one
+    sequence and several, automatic and fixed splits)."""
+    _say(f"sparse attention == dense attention over a gathered copy: lists {lengths}, split {split}")
+    w = workloads.SparseDecodeWorkload("sparse-vs-dense", 1005, 4096, lengths, 32)
+    codes, scales = _encode(w)
+    got, glse = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, w.offsets, w.row_index, split_rows=split)
+    out, lse = _dense_on_copy(w, codes, scales, w.offsets, w.row_index, split_rows=split)
+    assert np.array_equal(out, got) and np.array_equal(lse, glse)
+
+
+@pytest.mark.parametrize("n_lists", [1, 3])
+def test_sparse_clamped_indices(n_lists):
+    """Indices below 0 or past the cache read its first or last row (the rows read
+    in place, and the gather of the other paths, clamp alike)."""
+    _say(f"sparse attention: out-of-range indices clamped, {n_lists} list(s)")
+    T = 1000
+    w = workloads.SparseDecodeWorkload("sparse-clamp", 1005, T, [300] * n_lists, 16)
+    rng = np.random.default_rng(6)
+    idx = rng.integers(0, T, w.total_rows).astype(np.int64)
+    idx[::7] = -3
+    idx[3::11] = T
+    idx[5::13] = 1 << 40
+    idx[6::17] = -(1 << 40)
+    codes, scales = _encode(w)
+    ref, _ = _oracle(w, codes, scales, w.offsets, np.clip(idx, 0, T - 1))
+    got, glse = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, w.offsets, idx)
+    assert rel_err(got, ref) <= TOL[kvq.KVQ_PREC_MFMA]
+    out, lse = _dense_on_copy(w, codes, scales, w.offsets, idx)
+    assert np.array_equal(out, got) and np.array_equal(lse, glse)
+
+
+def test_sparse_rising_scores_in_place():
+    """Scores that climb along each list (a rope-key sawtooth over the list order,
+    a sharp rope query): the split kernel's first-tile reference is exceeded again
+    and again, so work items restart their rows, re-reading them through the list."""
+    _say("sparse attention: rising scores along the lists (restarts), rows read in place")
+    T = 4096
+    w = workloads.SparseDecodeWorkload("sparse-rising", 4242, T, [3000, 1000], 16)
+    rng = np.random.default_rng(4244)
+    perm = rng.permutation(T)
+    idx = np.concatenate([perm[:3000], perm[3000:4000]]).astype(np.int64)
+    rank = np.empty(T, np.int64)
+    rank[perm] = np.arange(T)
+    rope = rng.standard_normal((T, 64)).astype(np.float32)
+    rope[:, 0] = ((rank % 512) * 0.02).astype(np.float32)
+    w.k_rope = workloads.to_bf16_bits(rope)
+    w.q_lat = (w.q_lat * 1e-2).astype(np.float32)
+    w.q_rope = w.q_rope.copy()
+    w.q_rope[..., 0] = 400.0
+    codes, scales = _encode(w)
+    ref, _ = _oracle(w, codes, scales, w.offsets, idx)
+    for split in (0, 384):
+        got, glse = _sparse(w, kvq.KVQ_PREC_MFMA, codes, scales, w.offsets, idx, split_rows=split)
+        err = rel_err(got, ref)
+        _say(f"  split {split}: max|err|/max|ref| = {err:.3e}")
+        assert err <= TOL[kvq.KVQ_PREC_MFMA]
+        out, lse = _dense_on_copy(w, codes, scales, w.offsets, idx, split_rows=split)
+        assert np.array_equal(out, got) and np.array_equal(lse, glse)
 
 
 def test_sparse_full_size():

@@ -48,9 +48,9 @@ constexpr int MF_WAVES = 4;       // matrix-core path: waves per workgroup, spli
 constexpr int MF_TILE = 32;       // rows per wave tile
 constexpr int TQ_HEADS = 64;      // rotated codec, matrix-core path: heads per workgroup (4 waves x 16)
 constexpr int QPACK_U4 = 80;      // fp8: uint4 per prepared query (fp16 latent 64, rope hi 8, rope lo 8)
-constexpr int QP_RH = 64, QP_RL = 72;
 constexpr int QPACK_TQ = 144;     // rotated codec: the same, then the fp16 latent remainder (64)
-constexpr int QP_LL = 80;
+// rotated codec: slots (of 64 uint4, one per lane) of a 16-head block of the pack
+constexpr int QS_RH = 16, QS_RL = 18, QS_LL = 20;
 constexpr int F8_HEADS = 32;      // fp8 matrix-core path: heads per workgroup (one 32x32 MFMA N block)
 constexpr int F8_TILE = 128;      // fp8 matrix-core path: rows per workgroup tile (32 per wave)
 constexpr int N_XCD = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
@@ -59,8 +59,8 @@ constexpr float LAZY_LOG2 = 8.0f; // running-max slack before the accumulators a
 struct Plan {
     int64_t* chunk_prefix;  // [n_seqs + 2]: chunk prefix; fp8 matrix-core path: tile prefix, total, quota
     float* q_rot;           // fp32 path, rotated codec: [n_seqs][H][512]
-    uint4* q_pack;          // matrix-core paths: [n_seqs][H padded][QPACK_U4 (fp8, in operand order per
-                            // group) or QPACK_TQ]
+    uint4* q_pack;          // matrix-core paths: [n_seqs][H padded][QPACK_U4 or QPACK_TQ], in the split
+                            // kernel's operand order per group of 32 (fp8) or 16 (rotated codec) heads
     float* q_inv;           // matrix-core paths: [n_seqs][H padded]
     float* part_m;          // [max_chunks][H]
     float* part_l;          // [max_chunks][H]
@@ -565,6 +565,15 @@ __device__ __forceinline__ void dma_lds_b128_at(const void* vaddr, uint32_t lds_
 __device__ __forceinline__ void dma_lds_b32_at(const void* vaddr, uint32_t lds_base) {
     asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" : : "v"(vaddr), "{m0}"(lds_base) : "memory");
 }
+// max over the wave by lane swaps (no LDS round trips)
+__device__ __forceinline__ float wave_max_swap(float v, int lane) {
+    v = fmaxf(v, xor_lane<32>(v, lane));
+    v = fmaxf(v, xor_lane<16>(v, lane));
+    v = fmaxf(v, xor_lane<8>(v, lane));
+    v = fmaxf(v, xor_lane<4>(v, lane));
+    v = fmaxf(v, xor_lane<2>(v, lane));
+    return fmaxf(v, xor_lane<1>(v, lane));
+}
 // max over the four lanes n, n ^ 16, n ^ 32, n ^ 48 (gfx950 lane-swap
 // instructions: each pairs a lane with the one 16 or 32 lanes away).
 __device__ __forceinline__ float max_xor16_xor32(float v) {
@@ -924,7 +933,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 #pragma unroll
         for (int u = 0; u < 4; u++) rm = fmaxf(rm, fabsf(x[u]));
     }
-    rm = wave_max(rm);
+    rm = wave_max_swap(rm, lane);
     if (lane == 0) sm.red[wave] = rm;
 
     vm_wait_all();     // this wave's share of the pack (and the loads before it) has landed
@@ -1175,11 +1184,13 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 // and split into two fp16 terms, hi = fp16(q~ qs) and lo = fp16(q~ qs - hi)
 // (about 22 significant bits together; one fp16 term alone moves sharply
 // peaked softmaxes by up to 3e-3 of the output), in the split kernel's operand
-// layout: uint4 16 g + ks holds hi of dims 32 ks + 8 g .. + 7, uint4 QP_LL +
-// 16 g + ks their lo; the rope query (times sm_scale * log2(e)) as bf16 hi
-// (uint4 QP_RH + 2 g + k) and lo (QP_RL + 2 g + k) terms of dims 32 k + 8 g ..
-// + 7; 1 / qs in q_inv.  One wave per (sequence, head); lane l rotates dims
-// 8 l .. 8 l + 7 (three butterfly stages in registers, six across lanes).
+// order per block of 16 heads, so that a wave loads each operand register as
+// 1 KB contiguous: uint4 64 ks + 16 g + n of the block holds head n's hi of
+// dims 32 ks + 8 g .. + 7, uint4 64 (QS_LL + ks) + 16 g + n their lo; the rope
+// query (times sm_scale * log2(e)) as bf16 hi (slot QS_RH + k) and lo (slot
+// QS_RL + k) terms of dims 32 k + 8 g .. + 7; 1 / qs in q_inv.  One wave per
+// (sequence, head); lane l rotates dims 8 l .. 8 l + 7 (three butterfly stages
+// in registers, six across lanes).
 __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + h
@@ -1226,7 +1237,8 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
     }
     qmax = wave_max(qmax);
     const float qs = pow2_scale_for(qmax, 8);
-    uint4* dst = p.q_pack + row * QPACK_TQ;
+    // (heads_padded is a multiple of 16: the block of this row's 16 heads, head row % 16 in it)
+    uint4* dst = p.q_pack + (row & ~(int64_t)15) * QPACK_TQ + (row & 15);
     float hi[8], lo[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
@@ -1234,10 +1246,11 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
         hi[i] = (float)(_Float16)x;
         lo[i] = x - hi[i];          // exact in fp32
     }
-    dst[16 * (lane & 3) + (lane >> 2)] = make_uint4(pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]),
-                                                    pack_f16x2(hi[4], hi[5]), pack_f16x2(hi[6], hi[7]));
-    dst[QP_LL + 16 * (lane & 3) + (lane >> 2)] = make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
-                                                            pack_f16x2(lo[4], lo[5]), pack_f16x2(lo[6], lo[7]));
+    const int ks = lane >> 2, gq = lane & 3;  // dims 8 lane = 32 ks + 8 gq
+    dst[64 * ks + 16 * gq] = make_uint4(pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]),
+                                       pack_f16x2(hi[4], hi[5]), pack_f16x2(hi[6], hi[7]));
+    dst[64 * (QS_LL + ks) + 16 * gq] = make_uint4(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]),
+                                                 pack_f16x2(lo[4], lo[5]), pack_f16x2(lo[6], lo[7]));
     if (lane < 8) {  // rope dims 8 lane .. + 7: k-step lane / 4, lane group lane % 4
         const float c2r = valid ? a.sm_scale * LOG2E : 0.0f;
         const float rv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
@@ -1249,8 +1262,8 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
             rh[i] = pack_bf16x2(b0, b1);
             rl[i] = pack_bf16x2(f0 - b0, f1 - b1);
         }
-        dst[QP_RH + 2 * (lane & 3) + (lane >> 2)] = make_uint4(rh[0], rh[1], rh[2], rh[3]);
-        dst[QP_RL + 2 * (lane & 3) + (lane >> 2)] = make_uint4(rl[0], rl[1], rl[2], rl[3]);
+        dst[64 * (QS_RH + ks) + 16 * gq] = make_uint4(rh[0], rh[1], rh[2], rh[3]);
+        dst[64 * (QS_RL + ks) + 16 * gq] = make_uint4(rl[0], rl[1], rl[2], rl[3]);
     }
     if (lane == 0) p.q_inv[row] = 1.0f / qs;  // exact
 }
@@ -1377,17 +1390,18 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
     };
     // ---- query operands (prepared once per sequence and head), loaded first: the
     // row-scale loop below waits for its loads, and with them for these
-    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + head) * QPACK_TQ;
+    // (the wave's block of 16 heads: lane (g, n) = lane reads uint4 64 slot + lane, 1 KB per slot)
+    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + hg * TQ_HEADS + MF_HEADS * wave) * QPACK_TQ + lane;
     uint4 qh[16], qo[16], rh[2], rl[2];
 #pragma unroll
     for (int k = 0; k < 16; k++) {
-        qh[k] = qp[16 * g + k];
-        qo[k] = qp[QP_LL + 16 * g + k];
+        qh[k] = qp[64 * k];
+        qo[k] = qp[64 * (QS_LL + k)];
     }
 #pragma unroll
     for (int k = 0; k < 2; k++) {
-        rh[k] = qp[QP_RH + 2 * g + k];
-        rl[k] = qp[QP_RL + 2 * g + k];
+        rh[k] = qp[64 * (QS_RH + k)];
+        rl[k] = qp[64 * (QS_RL + k)];
     }
     const float k1 = a.sm_scale * LOG2E * p.q_inv[(int64_t)sq * p.heads_padded + head];
 
@@ -1402,7 +1416,7 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
 #pragma unroll
         for (int u = 0; u < 4; u++) rmax = fmaxf(rmax, fabsf(x[u]));
     }
-    rmax = wave_max(rmax);
+    rmax = wave_max_swap(rmax, lane);
     if (lane == 0) red_s[wave] = rmax;
     __syncthreads();
     rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));

@@ -1270,22 +1270,28 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
 
 // Rotated-codec split kernel (BITS = 3, 4, 6).  Work item = (T-chunk, group of
 // 64 heads); the items are dealt to XCDs in contiguous runs so the head groups
-// of a chunk share one L2.  All 4 waves of a workgroup step through the
-// chunk's tiles (32 rows) together, wave w for heads 16 w .. 16 w + 15: the
-// codes of a tile are decoded once per workgroup -- each wave decodes 8 rows
-// into a shared, double-buffered fp16 LDS tile (rope keys and row scales next
-// to it) -- and every wave then reads the whole tile:
-//   score:  S^T (16 rows x 16 heads) += X(rows, k) q~^T, X from the tile
-//           (lane (g, n): row 16 rb + n, dims 32 ks + 8 g .. + 7);
-//   PV:     O^T (16 dims x 16 heads) += X^T P'^T, X^T via ds_read_b64_tr_b16
+// of a chunk share one L2.  A workgroup has 8 waves in two roles, two waves on
+// each SIMD (one of each role), pipelined over the chunk's 32-row tiles:
+//   score wave w (0..3), heads 16 w .. 16 w + 15:
+//           S^T (16 rows x 16 heads) += X(rows, k) q~^T from the decoded tile
+//           (lane (g, n): row 16 rb + n, dims 32 ks + 8 g .. + 7), softmax,
+//           P'^T (the PV operand, 1 KB) to LDS;
+//   PV wave v (4..7, v - 4 = u), dims 128 u .. 128 u + 127 of all 64 heads:
+//           O^T (16 dims x 16 heads) += X^T P'^T, X^T via ds_read_b64_tr_b16
 //           (lane (g, p) gets rows 4 g .. 4 g + 3 and 16 + 4 g .. + 3 of column
-//           p, the k order the score accumulators hold P in).
-// One barrier per tile.  While a wave multiplies tile t it decodes tile t + 1
-// (its codes were loaded one tile earlier).  Softmax: fixed per-wave
-// reference (first tile's max) and probabilities times rho * rs with rs from
-// the chunk's largest radius; a tile more than 2^8 above the reference raises
-// it, and the workgroup (which shares the tiles) starts its rows again.  One
-// partial per (chunk, head), written by the wave that owns the head.
+//           p, the k order the score waves hold P in), one read per 16 dims
+//           serving the 4 head blocks; and the decode of the tile after next
+//           (each PV wave 8 rows) into the third fp16 buffer.
+// At step k the score waves take tile k and the PV waves tile k - 1; one
+// barrier per step.  The decoded tiles are triple-buffered (score, PV and
+// decode each use one), P double-buffered.  On one SIMD the matrix cores
+// alternate between the two roles' products while the other role issues its
+// LDS reads and vector work; with one wave per SIMD (score and PV in one
+// wave, the whole tile read twice per wave) a 32-row tile took about 3 us.
+// Softmax: fixed per-head reference (first tile's max) and probabilities times
+// rho * rs with rs from the chunk's largest radius; a tile more than 2^8 above
+// the reference raises it, and the workgroup (which shares the tiles) starts
+// its rows again at the next step's vote.
 //
 // The decoded tile: row r at DL halfwords r, its 16-byte chunk c (dims 8 c ..
 // 8 c + 7) stored at chunk c ^ tq_swz(r), tq_swz(r) = 2 (r % 4) ^ 9 bit2(r) ^
@@ -1294,42 +1300,41 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
 // decode writes (8 or 16 lanes on 8 rows), score reads (8 or 16 consecutive
 // rows, one chunk) and transposed PV reads (4 or 8 rows x 4 half-chunks) fall
 // on distinct banks whether a read or write cycle serves 64 bytes per 8 lanes
-// (32 banks) or 128 bytes per 16 (64 banks) -- checked on the CPU.  The
-// unswizzled layout with padded rows lost ~25 % of the kernel to bank
-// conflicts (6.4 M conflict cycles per launch).
-constexpr int KT = DR + 8;                // halfwords per rope tile row
-constexpr int SR = DL / 2 + 4;            // floats per staged half row of the epilogue
-constexpr int XT_HALFWORDS = (2 * MF_TILE * DL > MF_WAVES * MF_HEADS * SR * 2) ? 2 * MF_TILE * DL
-                                                                               : MF_WAVES * MF_HEADS * SR * 2;
+// (32 banks) or 128 bytes per 16 (64 banks) -- checked on the CPU.
+constexpr int KT = DR + 8;  // halfwords per rope tile row
+constexpr int TQ_BUFS = 3;  // decoded tiles in flight: scored, multiplied, being decoded
 __device__ __forceinline__ int tq_swz(int r) { return (2 * (r & 3)) ^ ((r & 4) ? 9 : 0) ^ ((r >> 3) & 1); }
 template <int BITS>
-__global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a, Plan p) {
-    __shared__ __align__(16) uint16_t xt_mem[XT_HALFWORDS];  // decoded latent rows, fp16 (then the epilogue's staging)
+__global__ __launch_bounds__(2 * MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a, Plan p) {
+    __shared__ __align__(16) uint16_t xt_mem[TQ_BUFS * MF_TILE * DL];  // decoded latent rows, fp16
     auto xt_row = [&](int buf, int r) __attribute__((always_inline)) { return xt_mem + (buf * MF_TILE + r) * DL; };
-    __shared__ __align__(16) uint16_t kt[2][MF_TILE][KT];  // rope keys, bf16
-    __shared__ __align__(16) float rho_s[2][MF_TILE];      // radius / sqrt(512)
-    __shared__ float red_s[MF_WAVES];
+    __shared__ __align__(16) uint16_t kt[TQ_BUFS][MF_TILE][KT];  // rope keys, bf16
+    __shared__ __align__(16) float rho_s[TQ_BUFS][MF_TILE];      // radius / sqrt(512)
+    __shared__ __align__(16) uint4 pb_s[2][MF_WAVES][64];         // P'^T of each score wave, by tile parity
+    __shared__ float red_s[2 * MF_WAVES];
     __shared__ int flag_s[2][MF_WAVES];
     __shared__ int64_t plan_s[3];
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const bool score_wave = wid < MF_WAVES;  // workgroup-uniform per wave
+    const int wave = wid & (MF_WAVES - 1);   // index within the role
     const int g = lane >> 4, n = lane & 15;
     const int64_t local = blockIdx.x / N_XCD;
     const int64_t c = (int64_t)(blockIdx.x % N_XCD) + N_XCD * (local / p.n_groups);
     const int hg = (int)(local % p.n_groups);
     if (c >= p.max_chunks) return;
-    const int head = hg * TQ_HEADS + MF_HEADS * wave + n;  // may exceed n_heads (its query is zero)
+    const int head = hg * TQ_HEADS + MF_HEADS * wave + n;  // score waves; may exceed n_heads (its query is zero)
     constexpr int CB = DL * BITS / 8;                         // code bytes per row
     int64_t r0, r1;
     int sq;
-    if (!locate_chunk(a, p, c, plan_s, wave, lane, r0, r1, sq)) return;  // workgroup-uniform
+    if (!locate_chunk(a, p, c, plan_s, wid, lane, r0, r1, sq)) return;  // workgroup-uniform
     const int ntiles = (int)((r1 - r0 + MF_TILE - 1) / MF_TILE);
 
-    // decode share of this wave: tile row 8 wave + lane / 8, code bytes
-    // 8 BITS (lane % 8) .. + 8 BITS - 1 (dims 64 (lane % 8) .. + 63), rope bytes
-    // 16 (lane % 8).  Group i of 8 dims is bits 8 BITS i .. of the lane's words.
+    // PV waves' decode share: tile row 8 wave + lane / 8, code bytes 8 BITS (lane % 8) ..
+    // + 8 BITS - 1 (dims 64 (lane % 8) .. + 63), rope bytes 16 (lane % 8).  Group i of 8
+    // dims is bits 8 BITS i .. of the lane's words.
     const int drow = 8 * wave + (lane & 7), dq = lane >> 3;
-    uint4 cv[3];  // codes of the tile to decode next (BITS * 2 words)
+    uint4 cv[3] = {};  // codes of the tile to decode next (BITS * 2 words)
     uint4 cr;     // its rope keys
     float cs;     // its row radius (scaled by 1 / sqrt(512) when it is stored)
     auto load_share = [&](int t) __attribute__((always_inline)) {
@@ -1354,256 +1359,261 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_args a,
     const uint32_t tab6 = BITS == 6 ? f16_bits(u2f(c_tq6_level[32 + (lane & 31)])) : 0u;
     const int dswz = tq_swz(drow);
     const int dq_off = 64 * (dq ^ (dswz >> 3)), di = dswz & 7;  // chunk 8 dq + i sits at 8 (dq ^ f / 8) + (i ^ f % 8)
-    auto decode_share = [&](int buf) __attribute__((always_inline)) {
-        uint16_t* dst = xt_row(buf, drow) + dq_off;
-        auto put = [&](int i, uint4 h) __attribute__((always_inline)) {  // chunk 8 dq + i of the row
-            *reinterpret_cast<uint4*>(dst + 8 * (i ^ di)) = h;
-        };
+    // group i (dims 64 dq + 8 i .. + 7) of the share, decoded into chunk 8 dq + i of the row
+    auto decode_group = [&](int buf, int i) __attribute__((always_inline)) {
+        uint4 hv;
+        const uint32_t w[12] = {cv[0].x, cv[0].y, cv[0].z, cv[0].w, cv[1].x, cv[1].y,
+                                cv[1].z, cv[1].w, cv[2].x, cv[2].y, cv[2].z, cv[2].w};
         if constexpr (BITS == 4) {
-            const uint32_t w[8] = {cv[0].x, cv[0].y, cv[0].z, cv[0].w, cv[1].x, cv[1].y, cv[1].z, cv[1].w};
-#pragma unroll
-            for (int i = 0; i < 8; i++) put(i, tq4x8_to_f16x8(w[i], lut));
+            hv = tq4x8_to_f16x8(w[i], lut);
         } else if constexpr (BITS == 3) {
             // group i = bits 24 i .. 24 i + 23 of the words w0 .. w5
-            const uint32_t w0 = cv[0].x, w1 = cv[0].y, w2 = cv[0].z, w3 = cv[0].w, w4 = cv[1].x, w5 = cv[1].y;
-            put(0, tq3x8_to_f16x8(w0 & 0xFFFFFFu, lut));
-            put(1, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFFFFu, lut));
-            put(2, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w2, w1, 16) & 0xFFFFFFu, lut));
-            put(3, tq3x8_to_f16x8(w2 >> 8, lut));
-            put(4, tq3x8_to_f16x8(w3 & 0xFFFFFFu, lut));
-            put(5, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w4, w3, 24) & 0xFFFFFFu, lut));
-            put(6, tq3x8_to_f16x8(__builtin_amdgcn_alignbit(w5, w4, 16) & 0xFFFFFFu, lut));
-            put(7, tq3x8_to_f16x8(w5 >> 8, lut));
+            const int b = 24 * i, k = b >> 5, sh = b & 31;
+            const uint32_t v = sh == 0 ? w[k] : (sh <= 8 ? (w[k] >> sh) : __builtin_amdgcn_alignbit(w[k + 1], w[k], sh));
+            hv = tq3x8_to_f16x8(v & 0xFFFFFFu, lut);
         } else {
             // groups 2k and 2k + 1 = bits 0 .. 47 and 48 .. 95 of words 3k .. 3k + 2
-            auto pair = [&](int k, uint32_t a0, uint32_t a1, uint32_t a2) __attribute__((always_inline)) {
-                put(2 * k, tq6x8_to_f16x8((uint64_t)a0 | ((uint64_t)(a1 & 0xFFFFu) << 32), tab6));
-                put(2 * k + 1, tq6x8_to_f16x8((uint64_t)(a1 >> 16) | ((uint64_t)a2 << 16), tab6));
-            };
-            pair(0, cv[0].x, cv[0].y, cv[0].z);
-            pair(1, cv[0].w, cv[1].x, cv[1].y);
-            pair(2, cv[1].z, cv[1].w, cv[2].x);
-            pair(3, cv[2].y, cv[2].z, cv[2].w);
+            const int k = i >> 1;
+            const uint32_t a0 = w[3 * k], a1 = w[3 * k + 1], a2 = w[3 * k + 2];
+            hv = (i & 1) ? tq6x8_to_f16x8((uint64_t)(a1 >> 16) | ((uint64_t)a2 << 16), tab6)
+                         : tq6x8_to_f16x8((uint64_t)a0 | ((uint64_t)(a1 & 0xFFFFu) << 32), tab6);
         }
+        *reinterpret_cast<uint4*>(xt_row(buf, drow) + dq_off + 8 * (i ^ di)) = hv;
+    };
+    auto decode_rest = [&](int buf) __attribute__((always_inline)) {  // the rope key and the radius
         *reinterpret_cast<uint4*>(&kt[buf][drow][8 * dq]) = cr;
         rho_s[buf][drow] = cs * INV_SQRT_DL;  // the 8 lanes of a row store the same value
     };
-    // ---- query operands (prepared once per sequence and head), loaded first: the
-    // row-scale loop below waits for its loads, and with them for these
-    // (the wave's block of 16 heads: lane (g, n) = lane reads uint4 64 slot + lane, 1 KB per slot)
-    const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + hg * TQ_HEADS + MF_HEADS * wave) * QPACK_TQ + lane;
-    uint4 qh[16], qo[16], rh[2], rl[2];
+    auto decode_share = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 16; k++) {
-        qh[k] = qp[64 * k];
-        qo[k] = qp[64 * (QS_LL + k)];
-    }
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        rh[k] = qp[64 * (QS_RH + k)];
-        rl[k] = qp[64 * (QS_RL + k)];
-    }
-    const float k1 = a.sm_scale * LOG2E * p.q_inv[(int64_t)sq * p.heads_padded + head];
-
-    if (ntiles > 0) load_share(0);
-
+        for (int i = 0; i < 8; i++) decode_group(buf, i);
+        decode_rest(buf);
+    };
     // ---- the chunk's largest row scale (four loads in flight per thread)
     float rmax = 0.0f;
-    for (int64_t t = r0 + tid; t < r1; t += 4 * MF_WAVES * 64) {
+    for (int64_t t = r0 + tid; t < r1; t += 8 * MF_WAVES * 64) {
         float x[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(t + u * MF_WAVES * 64, r1 - 1)];
+        for (int u = 0; u < 4; u++) x[u] = a.row_scale[min(t + u * 2 * MF_WAVES * 64, r1 - 1)];
 #pragma unroll
         for (int u = 0; u < 4; u++) rmax = fmaxf(rmax, fabsf(x[u]));
     }
     rmax = wave_max_swap(rmax, lane);
-    if (lane == 0) red_s[wave] = rmax;
+    if (lane == 0) red_s[wid] = rmax;
     __syncthreads();
-    rmax = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+#pragma unroll
+    for (int k = 0; k < 2 * MF_WAVES; k++) rmax = fmaxf(rmax, red_s[k]);
     const float rs = pow2_scale_for(rmax * INV_SQRT_DL, -1);  // max rho * rs in [0.5, 1)
 
-    // per-lane LDS addresses: score row 16 rb + n, dims 8 g + 32 ks; PV source
-    // lane (g, n) at row 4 g + n / 4, column 4 (n % 4) (+ 16 mb, + 16 rows)
-    const int trow = 4 * g + (n >> 2);
-    // score reads: chunk g + 4 ks of row n sits at 4 (ks ^ f / 4) + (g ^ f % 4), f = tq_swz(n)
-    const int fs = tq_swz(n);
-    int sro[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) sro[j] = 32 * (j ^ (fs >> 2)) + 8 * (g ^ (fs & 3));
-    // PV reads: dims 16 mb + 4 (n % 4) .. + 3 of row trow: half n % 2 of chunk 2 mb + b (b = n / 2 % 2),
-    // which sits at chunk 2 (mb ^ f / 2) + (b ^ f % 2), f = tq_swz(trow) (rows 16 + trow alike):
-    // halfword 16 (mb - mb % 8) + po[mb % 8]
-    const int fp = tq_swz(trow);
-    int po[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) po[j] = 16 * (j ^ (fp >> 1)) + 8 * (((n >> 1) & 1) ^ (fp & 1)) + 4 * (n & 1);
-    f32x4_t acc_o[32];
-    float m_run = -INFINITY, l_part = 0.0f;
     bool over = false;
-    // one vote + barrier per tile: every wave reports whether its last tile was
-    // out of range (any such vote restarts the workgroup); the barrier also
-    // publishes the tile decoded since the last one
-    auto vote = [&](int t) __attribute__((always_inline)) {
-        flag_s[t & 1][wave] = over ? 1 : 0;  // every lane stores the same value
+    // one vote + barrier per step: every score wave reports whether its tile was out of
+    // range (any such vote restarts the workgroup); the barrier also publishes the
+    // decoded tile and the P operands of the step.  The two roles run separate loops
+    // with the same votes (their registers then never overlap).
+    auto vote = [&](int k) __attribute__((always_inline)) {
+        if (score_wave) flag_s[k & 1][wave] = over ? 1 : 0;  // every lane stores the same value
         wg_barrier_lds();
-        const int4 f = *reinterpret_cast<const int4*>(&flag_s[t & 1][0]);
+        const int4 f = *reinterpret_cast<const int4*>(&flag_s[k & 1][0]);
         return (f.x | f.y | f.z | f.w) != 0;  // workgroup-uniform
     };
-    for (;;) {
+    if (score_wave) {
+        // ---- query operands (prepared once per sequence and head; the wave's block of
+        // 16 heads, lane (g, n) = lane reads uint4 64 slot + lane, 1 KB per slot)
+        const uint4* qp = p.q_pack + ((int64_t)sq * p.heads_padded + hg * TQ_HEADS + MF_HEADS * wave) * QPACK_TQ + lane;
+        uint4 qh[16], qo[16], rh[2], rl[2];
 #pragma unroll
-    for (int mb = 0; mb < 32; mb++) acc_o[mb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    l_part = 0.0f;
-    if (ntiles > 0) {
-        decode_share(0);  // its codes were loaded above (or at the restart)
-        load_share(min(1, ntiles - 1));
-    }
-    bool again = vote(0);
-    if (!again && ntiles > 0) {
-    int t = 0;
-    do {
-        const int buf = t & 1;
-        const int nt = (int)min((int64_t)MF_TILE, r1 - (r0 + (int64_t)MF_TILE * t));
-        // ---- scores S^T (two row blocks) from the tile: four independent
-        // accumulator chains (row block x even / odd k-step), reads one step ahead
-        f32x4_t sl[2], sr[2], sx[2];
-        f32x4_t sq[2];  // the query's fp16 remainder terms
-        sl[0] = sl[1] = sr[0] = sr[1] = sx[0] = sx[1] = sq[0] = sq[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        {
-            // chunk g + 4 ks of rows n and 16 + n (the same swizzle) sits at halfword
-            // 32 (ks - ks % 4) + sro[ks % 4]
-            const uint16_t* xa = xt_row(buf, n);
-            const uint16_t* xb = xt_row(buf, 16 + n);
-            auto sc_read = [&](const uint16_t* x, int ks) __attribute__((always_inline)) {
-                return *reinterpret_cast<const f16x8_t*>(x + 32 * (ks & ~3) + sro[ks & 3]);
-            };
-            f16x8_t na = sc_read(xa, 0), nb = sc_read(xb, 0);
+        for (int k = 0; k < 16; k++) {
+            qh[k] = qp[64 * k];
+            qo[k] = qp[64 * (QS_LL + k)];
+        }
 #pragma unroll
-            for (int ks = 0; ks < 16; ks++) {
-                const f16x8_t ca2 = na, cb2 = nb;
-                if (ks < 15) {
-                    na = sc_read(xa, ks + 1);
-                    nb = sc_read(xb, ks + 1);
+        for (int k = 0; k < 2; k++) {
+            rh[k] = qp[64 * (QS_RH + k)];
+            rl[k] = qp[64 * (QS_RL + k)];
+        }
+        const float k1 = a.sm_scale * LOG2E * p.q_inv[(int64_t)sq * p.heads_padded + head];
+        // score row 16 rb + n, dims 8 g + 32 ks: chunk g + 4 ks of row n sits at
+        // 4 (ks ^ f / 4) + (g ^ f % 4), f = tq_swz(n)
+        const int fs = tq_swz(n);
+        int sro[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) sro[j] = 32 * (j ^ (fs >> 2)) + 8 * (g ^ (fs & 3));
+        float m_run = -INFINITY, l_part = 0.0f;
+        for (;;) {
+            l_part = 0.0f;
+            bool again = vote(0);
+            for (int k = 0; !again && k <= ntiles; k++) {
+                if (k < ntiles) {
+                    const int buf = k % TQ_BUFS;
+                    const int nt = (int)min((int64_t)MF_TILE, r1 - (r0 + (int64_t)MF_TILE * k));
+                    // ---- scores S^T (two row blocks) from the tile: four independent
+                    // accumulator chains (row block x even / odd k-step), reads one step ahead
+                    f32x4_t sl[2], sr[2], sx[2];
+                    f32x4_t sqv[2];  // the query's fp16 remainder terms
+                    sl[0] = sl[1] = sr[0] = sr[1] = sx[0] = sx[1] = sqv[0] = sqv[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    {
+                        // chunk g + 4 ks of rows n and 16 + n (the same swizzle) sits at halfword
+                        // 32 (ks - ks % 4) + sro[ks % 4]
+                        const uint16_t* xa = xt_row(buf, n);
+                        const uint16_t* xb = xt_row(buf, 16 + n);
+                        auto sc_read = [&](const uint16_t* x, int ks) __attribute__((always_inline)) {
+                            return *reinterpret_cast<const f16x8_t*>(x + 32 * (ks & ~3) + sro[ks & 3]);
+                        };
+                        f16x8_t na = sc_read(xa, 0), nb = sc_read(xb, 0);
+#pragma unroll
+                        for (int ks = 0; ks < 16; ks++) {
+                            const f16x8_t ca2 = na, cb2 = nb;
+                            if (ks < 15) {
+                                na = sc_read(xa, ks + 1);
+                                nb = sc_read(xb, ks + 1);
+                            }
+                            f32x4_t& s0 = (ks & 1) ? sx[0] : sl[0];
+                            f32x4_t& s1 = (ks & 1) ? sx[1] : sl[1];
+                            s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qh[ks]), s0, 0, 0, 0);
+                            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qh[ks]), s1, 0, 0, 0);
+                            sqv[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qo[ks]), sqv[0], 0, 0, 0);
+                            sqv[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qo[ks]), sqv[1], 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int rb = 0; rb < 2; rb++) {
+                            const uint16_t* kr = &kt[buf][16 * rb + n][8 * g];
+#pragma unroll
+                            for (int kk = 0; kk < 2; kk++) {
+                                const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kr + 32 * kk);
+                                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rh[kk]), sr[rb], 0, 0, 0);
+                                sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rl[kk]), sr[rb], 0, 0, 0);
+                            }
+                            sl[rb] += sx[rb];
+                            sl[rb] += sqv[rb];
+                        }
+                    }
+                    // ---- softmax: lane (g, n) holds rows 16 rb + 4 g + r of head n (no branches)
+                    float sc[2][4], rr[2][4];
+                    float tmax = -INFINITY;
+#pragma unroll
+                    for (int rb = 0; rb < 2; rb++) {
+                        const float4 rq = *reinterpret_cast<const float4*>(&rho_s[buf][16 * rb + 4 * g]);
+                        const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const bool ok = 16 * rb + 4 * g + r < nt;
+                            rr[rb][r] = ok ? rv[r] : 0.0f;
+                            sc[rb][r] = ok ? fmaf(rv[r] * k1, sl[rb][r], sr[rb][r]) : -INFINITY;
+                            tmax = fmaxf(tmax, sc[rb][r]);
+                        }
+                    }
+                    tmax = max_xor16_xor32(tmax);
+                    m_run = m_run == -INFINITY ? tmax : m_run;  // first tile: row 0 is valid
+                    // a tile more than 2^8 above the reference raises it; the workgroup
+                    // restarts at the next vote
+                    const bool ov = __any(tmax > m_run + LAZY_LOG2);
+                    m_run = ov ? fmaxf(m_run, tmax) : m_run;
+                    over = over || ov;
+                    float psum = 0.0f;
+                    uint32_t pbv[4];
+#pragma unroll
+                    for (int rb = 0; rb < 2; rb++) {
+                        float pw[4];
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const float pv = __builtin_amdgcn_exp2f(sc[rb][r] - m_run);  // masked rows: 0
+                            psum += pv;
+                            pw[r] = pv * (rr[rb][r] * rs);
+                        }
+                        pbv[2 * rb] = pack_f16x2(pw[0], pw[1]);
+                        pbv[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
+                    }
+                    l_part += psum;
+                    // (buffer k % 2: the PV waves read it during step k + 1, and were past their
+                    // step k - 1 reads of it at the vote ending step k - 1)
+                    pb_s[k & 1][wave][lane] = make_uint4(pbv[0], pbv[1], pbv[2], pbv[3]);
                 }
-                f32x4_t& s0 = (ks & 1) ? sx[0] : sl[0];
-                f32x4_t& s1 = (ks & 1) ? sx[1] : sl[1];
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qh[ks]), s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qh[ks]), s1, 0, 0, 0);
-                sq[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ca2, as_f16x8(qo[ks]), sq[0], 0, 0, 0);
-                sq[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cb2, as_f16x8(qo[ks]), sq[1], 0, 0, 0);
+                again = vote(k + 1);
             }
+            if (!again) break;
+            __syncthreads();  // every wave has read the votes before the restart's first vote rewrites them
+            over = false;
+        }
+        // ---- m and l of the wave's heads
+        l_part += __shfl_xor(l_part, 16, 64);
+        l_part += __shfl_xor(l_part, 32, 64);
+        if (g == 0 && head < a.n_heads) {
+            p.part_m[c * a.n_heads + head] = m_run;  // log2 units
+            p.part_l[c * a.n_heads + head] = l_part;
+        }
+    } else {
+        // PV source lane (g, n) at row 4 g + n / 4, column 4 (n % 4) (+ 16 mb, + 16 rows):
+        // dims 16 mb + 4 (n % 4) .. + 3 of row trow are half n % 2 of chunk 2 mb + b (b =
+        // n / 2 % 2), which sits at chunk 2 (mb ^ f / 2) + (b ^ f % 2), f = tq_swz(trow)
+        // (rows 16 + trow alike): halfword 16 (mb - mb % 8) + po[mb % 8]
+        const int trow = 4 * g + (n >> 2);
+        const int fp = tq_swz(trow);
+        int po[8];
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                const uint16_t* kr = &kt[buf][16 * rb + n][8 * g];
+        for (int j = 0; j < 8; j++) po[j] = 16 * (j ^ (fp >> 1)) + 8 * (((n >> 1) & 1) ^ (fp & 1)) + 4 * (n & 1);
+        f32x4_t acc_o[8][4];  // dims 128 wave + 16 mb (mb < 8) x head block hb
+        if (ntiles > 0) load_share(0);
+        for (;;) {
 #pragma unroll
-                for (int k = 0; k < 2; k++) {
-                    const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(kr + 32 * k);
-                    sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rh[k]), sr[rb], 0, 0, 0);
-                    sr[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, as_bf16x8(rl[k]), sr[rb], 0, 0, 0);
+            for (int mb = 0; mb < 8; mb++)
+#pragma unroll
+                for (int hb = 0; hb < 4; hb++) acc_o[mb][hb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if (ntiles > 0) {
+                decode_share(0);
+                load_share(min(1, ntiles - 1));
+            }
+            bool again = vote(0);
+            for (int k = 0; !again && k <= ntiles; k++) {
+                if (k >= 1) {
+                    // ---- PV of tile k - 1: dims 128 wave + 16 mb, the transposed reads one block ahead
+                    const int buf = (k - 1) % TQ_BUFS;
+                    f16x8_t bo[4];
+#pragma unroll
+                    for (int hb = 0; hb < 4; hb++) bo[hb] = as_f16x8(pb_s[(k - 1) & 1][hb][lane]);
+                    auto pv_read = [&](int mb) __attribute__((always_inline)) {
+                        const int gm = 8 * wave + mb;  // dim block of the row
+                        const int off = 16 * (gm & ~7) + po[gm & 7];
+                        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_t*)(xt_row(buf, trow) + off));
+                        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_t*)(xt_row(buf, 16 + trow) + off));
+                        const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+                        return as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+                    };
+                    f16x8_t nxt = pv_read(0);
+#pragma unroll
+                    for (int mb = 0; mb < 8; mb++) {
+                        const f16x8_t aop = nxt;
+                        if (mb + 1 < 8) nxt = pv_read(mb + 1);
+#pragma unroll
+                        for (int hb = 0; hb < 4; hb++)
+                            acc_o[mb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bo[hb], acc_o[mb][hb], 0, 0, 0);
+                    }
                 }
-                sl[rb] += sx[rb];
-                sl[rb] += sq[rb];
+                if (k + 1 < ntiles) {  // the tile after the scored one: decoded now, its successor's codes loaded
+                    decode_share((k + 1) % TQ_BUFS);
+                    load_share(min(k + 2, ntiles - 1));
+                }
+                again = vote(k + 1);
+            }
+            if (!again) break;
+            __syncthreads();  // (the restart barrier of the score waves)
+            if (ntiles > 0) load_share(0);
+        }
+        // ---- O of dims 128 wave .. + 127 of every head of the group
+        const float so = 1.0f / rs;  // exact (a power of two)
+#pragma unroll
+        for (int hb = 0; hb < 4; hb++) {
+            const int h = hg * TQ_HEADS + MF_HEADS * hb + n;
+            if (h < a.n_heads) {
+                float* dst = p.part_o + (c * a.n_heads + h) * DL + 128 * wave + 4 * g;
+#pragma unroll
+                for (int mb = 0; mb < 8; mb++) {
+                    const f32x4_t v = acc_o[mb][hb];
+                    *reinterpret_cast<float4*>(dst + 16 * mb) = make_float4(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
+                }
             }
         }
-        // ---- softmax: lane (g, n) holds rows 16 rb + 4 g + r of head n (no branches)
-        float sc[2][4], rr[2][4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const float4 rq = *reinterpret_cast<const float4*>(&rho_s[buf][16 * rb + 4 * g]);
-            const float rv[4] = {rq.x, rq.y, rq.z, rq.w};
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const bool ok = 16 * rb + 4 * g + r < nt;
-                rr[rb][r] = ok ? rv[r] : 0.0f;
-                sc[rb][r] = ok ? fmaf(rv[r] * k1, sl[rb][r], sr[rb][r]) : -INFINITY;
-                tmax = fmaxf(tmax, sc[rb][r]);
-            }
-        }
-        tmax = max_xor16_xor32(tmax);
-        m_run = m_run == -INFINITY ? tmax : m_run;  // first tile: row 0 is valid
-        // a tile more than 2^8 above the reference raises it; the workgroup
-        // restarts at the next vote
-        const bool ov = __any(tmax > m_run + LAZY_LOG2);
-        m_run = ov ? fmaxf(m_run, tmax) : m_run;
-        over = over || ov;
-        float psum = 0.0f;
-        uint32_t pb[4];
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            float pw[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const float pv = __builtin_amdgcn_exp2f(sc[rb][r] - m_run);  // masked rows: 0
-                psum += pv;
-                pw[r] = pv * (rr[rb][r] * rs);
-            }
-            pb[2 * rb] = pack_f16x2(pw[0], pw[1]);
-            pb[2 * rb + 1] = pack_f16x2(pw[2], pw[3]);
-        }
-        l_part += psum;
-        const f16x8_t bop = as_f16x8(make_uint4(pb[0], pb[1], pb[2], pb[3]));
-        // ---- the next tile's share (after the last tile: the last one again,
-        // into the free buffer), then the loads of the one after
-        decode_share(buf ^ 1);
-        load_share(min(t + 2, ntiles - 1));
-        // ---- PV from the tile, the transposed reads four column blocks ahead
-        auto pv_read = [&](int mb) __attribute__((always_inline)) {
-            const int off = 16 * (mb & ~7) + po[mb & 7];
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(xt_row(buf, trow) + off));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(xt_row(buf, 16 + trow) + off));
-            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-            return as_f16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-        };
-        f16x8_t pvq[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) pvq[i] = pv_read(i);
-#pragma unroll
-        for (int mb = 0; mb < 32; mb++) {
-            const f16x8_t aop = pvq[mb & 3];
-            if (mb + 4 < 32) pvq[mb & 3] = pv_read(mb + 4);
-            acc_o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc_o[mb], 0, 0, 0);
-        }
-        t++;
-        again = vote(t);
-    } while (!again && t < ntiles);
-    }
-    if (!again) break;
-    over = false;
-    if (ntiles > 0) load_share(0);
-    }
-    // ---- the partials of this wave's heads, staged in LDS (the tiles are free
-    // after the last vote) half a row at a time and stored as whole rows
-    l_part += __shfl_xor(l_part, 16, 64);
-    l_part += __shfl_xor(l_part, 32, 64);
-    if (g == 0 && head < a.n_heads) {
-        p.part_m[c * a.n_heads + head] = m_run;  // log2 units
-        p.part_l[c * a.n_heads + head] = l_part;
-    }
-    static_assert(sizeof(xt_mem) >= MF_WAVES * MF_HEADS * SR * sizeof(float), "staging fits in the tiles");
-    float* stg = reinterpret_cast<float*>(xt_mem) + wave * (MF_HEADS * SR);
-    const float so = 1.0f / rs;  // exact (a power of two)
-#pragma unroll
-    for (int hf = 0; hf < 2; hf++) {
-#pragma unroll
-        for (int mb = 0; mb < 16; mb++) {
-            const f32x4_t v = acc_o[16 * hf + mb];
-            *reinterpret_cast<float4*>(stg + n * SR + 16 * mb + 4 * g) = make_float4(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int k = 0; k < MF_HEADS; k++) {
-            const int h = hg * TQ_HEADS + MF_HEADS * wave + k;
-            if (h < a.n_heads)
-                *reinterpret_cast<float4*>(p.part_o + (c * a.n_heads + h) * DL + DL / 2 * hf + 4 * lane) =
-                    *reinterpret_cast<const float4*>(stg + k * SR + 4 * lane);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -1850,9 +1860,9 @@ hipError_t launch_stage(const kvq_attn_args& a, const Plan& p, int stage, hipStr
             } else {
                 const dim3 grid((unsigned)(p.chunks_per_xcd * N_XCD * p.n_groups));
                 switch (a.qmode) {
-                    case KVQ_QMODE_TQ4: hipLaunchKernelGGL(k_attn_mfma_tq<4>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
-                    case KVQ_QMODE_TQ3: hipLaunchKernelGGL(k_attn_mfma_tq<3>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
-                    case KVQ_QMODE_TQ6: hipLaunchKernelGGL(k_attn_mfma_tq<6>, grid, dim3(MF_WAVES * 64), 0, st, a, p); break;
+                    case KVQ_QMODE_TQ4: hipLaunchKernelGGL(k_attn_mfma_tq<4>, grid, dim3(2 * MF_WAVES * 64), 0, st, a, p); break;
+                    case KVQ_QMODE_TQ3: hipLaunchKernelGGL(k_attn_mfma_tq<3>, grid, dim3(2 * MF_WAVES * 64), 0, st, a, p); break;
+                    case KVQ_QMODE_TQ6: hipLaunchKernelGGL(k_attn_mfma_tq<6>, grid, dim3(2 * MF_WAVES * 64), 0, st, a, p); break;
                     default: {
                         const dim3 wg(MF_WAVES * 64);
                         if (p.row_index) {

@@ -1820,6 +1820,80 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
     if (a.lse && wbj == 0 && h == 0) a.lse[(int64_t)s * a.n_heads + head] = L > 0.0f ? (M + log2f(L)) * LN2 : -INFINITY;
 }
 
+// Merge of the fp8 matrix-core partials when sequences have few slots each
+// (several sequences): one wave per (sequence, group of 32 heads, NB
+// consecutive 32-dim blocks), thread (h, n) owning head n's dims of those
+// blocks; the slots are merged online in order, U at a time with every load
+// in flight, and each slot's weight serves the NB blocks.  (A workgroup per
+// block with the slots dealt to several waves, combined through LDS, was
+// slower here: most of its waves had one slot or none.)
+template <int NB, int U>
+__global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
+    const int l = threadIdx.x, n = l & 31, h = l >> 5;
+    const int64_t item = blockIdx.x;
+    const int wb0 = (int)(item % (64 / NB)) * NB;  // first (w * 4 + b) * 4 + j block
+    const int64_t sg = item / (64 / NB);
+    const int g = (int)(sg % p.n_groups), s = (int)(sg / p.n_groups);
+    const int head = g * F8_HEADS + n;
+    const int hc = min(head, a.n_heads - 1);  // a padded head reads a real one's m, l and is not written
+    int64_t c0 = 0, c1 = 0;
+    {
+        const bool one = a.n_seqs == 1;
+        const int64_t t0 = one ? 0 : p.chunk_prefix[s], t1 = one ? p.n_tiles : p.chunk_prefix[s + 1];
+        const int64_t q = one ? p.tile_quota : p.chunk_prefix[a.n_seqs + 1];
+        if (t1 > t0) {
+            c0 = t0 / q + s;
+            c1 = (t1 - 1) / q + s + 1;
+        }
+        c0 = min(c0, p.max_chunks);
+        c1 = min(c1, p.max_chunks);
+    }
+    const float4* src = reinterpret_cast<const float4*>(p.part_o) + g * (int64_t)(F8_HEADS * DL / 4) + wb0 * 64 + l;
+    const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
+    float m = -INFINITY, lsum = 0.0f;
+    float4 o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) o[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int64_t cb = c0; cb < c1; cb += U) {
+        float mc[U], lc[U];
+        float4 v[U][NB];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t cc = cb + u;
+            const int64_t ch = cc < c1 ? cc : cb;
+            mc[u] = p.part_m[ch * a.n_heads + hc];
+            lc[u] = p.part_l[ch * a.n_heads + hc];
+#pragma unroll
+            for (int b = 0; b < NB; b++) v[u][b] = src[ch * cstride + b * 64];
+            if (cc >= c1) mc[u] = -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const float mn = fmaxf(m, mc[u]);
+            const float sc = m == -INFINITY ? 0.0f : exp2f(m - mn);
+            const float w = mc[u] == -INFINITY ? 0.0f : exp2f(mc[u] - mn);
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                o[b].x = o[b].x * sc + w * v[u][b].x;
+                o[b].y = o[b].y * sc + w * v[u][b].y;
+                o[b].z = o[b].z * sc + w * v[u][b].z;
+                o[b].w = o[b].w * sc + w * v[u][b].w;
+            }
+            lsum = lsum * sc + w * lc[u];
+            m = mn;
+        }
+    }
+    if (head >= a.n_heads) return;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int wbj = wb0 + b, w = wbj >> 4, bb = (wbj >> 2) & 3, j = wbj & 3;
+        *reinterpret_cast<float4*>(a.out + ((int64_t)s * a.n_heads + head) * DL + 128 * w + 32 * bb + 8 * j + 4 * h) =
+            make_float4(o[b].x * inv, o[b].y * inv, o[b].z * inv, o[b].w * inv);
+    }
+    if (a.lse && wb0 == 0 && h == 0) a.lse[(int64_t)s * a.n_heads + head] = lsum > 0.0f ? (m + log2f(lsum)) * LN2 : -INFINITY;
+}
+
 hipError_t launch_stage(const kvq_attn_args& a, const Plan& p, int stage, hipStream_t st, const NewRows* nr) {
     const NewRows none{nullptr, 0, nullptr, nullptr};
     const bool f32 = a.precision == KVQ_PREC_FP32;
@@ -1891,8 +1965,7 @@ hipError_t launch_stage(const kvq_attn_args& a, const Plan& p, int stage, hipStr
             } else {
                 const int64_t f8_items = (int64_t)a.n_seqs * p.n_groups * 64;  // (sequence, group, 32-dim block)
                 if (!f32 && wide) hipLaunchKernelGGL((k_merge_f8<8>), dim3((unsigned)f8_items), dim3(512), 0, st, a, p);
-                else if (!f32 && narrow) hipLaunchKernelGGL((k_merge_f8<1>), dim3((unsigned)f8_items), dim3(64), 0, st, a, p);
-                else if (!f32) hipLaunchKernelGGL((k_merge_f8<2>), dim3((unsigned)f8_items), dim3(128), 0, st, a, p);
+                else if (!f32) hipLaunchKernelGGL((k_merge_f8_few<2, 8>), dim3((unsigned)(f8_items / 2)), dim3(64), 0, st, a, p);
                 else hipLaunchKernelGGL((k_merge<false, false, 256>), dim3((unsigned)(2 * items)), dim3(256), 0, st, a, p);
             }
             break;

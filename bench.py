@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "KV rows/s + achieved HBM GB/s (% roofline), fp8/TQ4 MLA decode, T=32k"
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 (and bf16) matrix-core peak
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 
 
@@ -155,7 +155,7 @@ def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
     flops) over kernel time.  only: one of ROWS (the others are skipped)."""
     res = {}
     dev = "cuda"
-    PEAK_T = PEAK_BF16_TFLOPS
+    PEAK_T = PEAK_F16_TFLOPS
     want = (lambda r: True) if only is None else (lambda r: r == only)
 
     def hbm(name, nbytes, ms, extra=None):
@@ -570,8 +570,8 @@ def main():
         "config": {"workload": w.name, "seqs": 1, "T": T, "heads": H, "qmode": "fp8" if qmode == 1 else "tq4",
                    "precision": "mfma-fp16" if args.precision == 0 else "fp32", "kv_copies": args.kv_copies,
                    "parallelism": "single-gpu"},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_F16_TFLOPS,
                      "traffic": measured_traffic() if (qmode == 1 and args.precision == 0) else None},
         "hbm": {"achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
                 "bytes_per_launch": nbytes},

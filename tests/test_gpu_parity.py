@@ -2,7 +2,7 @@
 
 Encoders, conversions and the q4_0 tier must match bit for bit; decode
 attention must match the oracle's fp64 evaluation on the same codes within
-max|err| / max|ref| <= 2e-3 (bf16 matrix cores) or <= 1e-5 (fp32 check path).
+max|err| / max|ref| <= 2e-3 (fp16 matrix-core path) or <= 1e-5 (fp32 check path).
 """
 import sys
 

@@ -123,9 +123,12 @@ def gpu_latents(torch, n_rows, seed, lengths=None, dim=512):
     return x
 
 
-def time_graph(torch, fn, reps):
+def time_graph(torch, fn, reps, warm_s=0.03, timed=3):
     """Average duration (ms) of fn() over reps back-to-back launches captured
-    in one HIP graph, by HIP events on the replay stream."""
+    in one HIP graph, by HIP events on the replay stream: the median of
+    `timed` replays after untimed ones for at least warm_s seconds (the first
+    few milliseconds of a new load run measurably slower, e.g. about 25% for a
+    600 MB streaming pass)."""
     fn()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -133,14 +136,20 @@ def time_graph(torch, fn, reps):
     with torch.cuda.graph(g, stream=side):
         for _ in range(reps):
             fn()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    t0, n = time.perf_counter(), 0
+    while n < 3 or time.perf_counter() - t0 < warm_s:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
+    times = []
+    for _ in range(timed):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    return sorted(times)[len(times) // 2]
 
 
 ROWS = ("encode", "tq4", "tq3", "tq6", "ragged", "sparse", "q4", "q4attn")

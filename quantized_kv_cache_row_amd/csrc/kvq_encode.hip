@@ -12,8 +12,8 @@
 // fp8: one wave per row, 8 consecutive fp32 per lane loaded as two 16-byte
 // loads, codes stored as one 8-byte store per lane, so every wave instruction
 // touches one contiguous span.  TQ4: a general kernel (dim/8 lanes per row) and
-// one for dim 512 that spends half the vector instructions per row (the TQ4
-// encoder is bound by the vector ALU, not by HBM).
+// one for dim 512 with well under half the vector instructions per row, which
+// streams its input at close to the rate of a plain copy.
 #include <cstring>
 #include <type_traits>
 
@@ -201,30 +201,39 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq(const float*
 
 // ---- TQ4, dim 512 --------------------------------------------------------------
 // The same result as k_encode_tq<4> with fewer vector instructions per row
-// (the general kernel spends about 500 per 512-wide row, so it is bound by the
-// vector ALU rather than by HBM):
-//  - 16 lanes per row, 4 rows per wave.  Lane u of a row holds column
-//    q = u ^ 3 bit2(u), i.e. the 32 elements p = j + 4 q + 64 k (j = 0..3,
-//    k = 0..7), loaded as eight 16-byte loads (load k covers 256 contiguous
-//    bytes per row).  FWHT stages in the definition's order: h = 1, 2 in
-//    registers (bits of j), h = 4, 8, 16, 32 across lanes (bits of q: partner
-//    lane u ^ 1, u ^ 2, u ^ 7, u ^ 8, each a single DPP pattern inside a 16-lane
-//    row), h = 64, 128, 256 in registers (bits of k).
+// (the general kernel spends about 500 per 512-wide row):
+//  - 16 lanes per row, 4 rows per wave.  Lane u of a row has the lane-stage
+//    index q = u ^ 3 bit2(u) and loads column group g = q ^ 15, i.e. the 32
+//    elements p = j + 4 g + 64 k (j = 0..3, k = 0..7), as eight 16-byte loads
+//    (load k covers 256 contiguous bytes per row).  FWHT stages in the
+//    definition's order: h = 1, 2 in registers (bits of j), h = 4, 8, 16, 32
+//    across lanes (bits of q: partner lane u ^ 1, u ^ 2, u ^ 7, u ^ 8, each a
+//    single DPP pattern inside a 16-lane row), h = 64, 128, 256 in registers
+//    (bits of k).
 //  - Each cross-lane stage is one fma with the partner's value as the DPP
 //    operand: y + c * y_partner with c = +1 in the lower lane and -1 in the
-//    upper.  The upper lane then holds -(a - b) instead of a - b (the sum is
-//    rounded once either way, and rounding to nearest is symmetric), so after
-//    the four stages lane q holds (-1)^popcount(q) times the transform; that
-//    sign is put back in the bucketing step.
-//  - Bucketing uses the codebook's symmetry (t_{14-k} = -t_k, t_7 = 0, hence
-//    T_{14-k} = -T_k exactly): for w > 0, idx = 8 + #{k >= 8 : w > T_k}; for
-//    w <= 0, idx = 7 - #{k >= 8 : |w| >= T_k}.  Both counts are one 3-level
-//    search over the 7 positive thresholds on integer keys (the bits of |w|,
-//    plus 1 for w <= 0, which turns >= into >); the bits of nonnegative floats
-//    order like the values.  A row whose radius is not finite takes the
-//    defining comparisons against all 15 thresholds instead.
-constexpr int D512_ROWS = 4;  // rows per wave
-
+//    upper.  The upper lane then holds -(a - b) instead of a - b (rounded once
+//    either way; rounding to nearest is symmetric), so the four stages compute
+//    (-1)^popcount(q) times the 16-point transform of what the lanes hold.
+//    That sign pattern is a Walsh character: multiplying the transform's output
+//    by it equals transforming the input with its lane index xor-ed by 15.  The
+//    lanes load group q ^ 15 for that reason, and lane q ends with the
+//    transform's value for group q itself, sign included, from the same
+//    pairwise sums.
+//  - Bucketing: idx = #{k : w > T_k} with T_k = fl(t_k * r).  The cell
+//    c = clamp(floor(a w / r + 7.5), 0, 14) with a = D512_CELL_SCALE puts its
+//    lower edges (c - 7.5) / a strictly between consecutive thresholds,
+//    (c - 7.5) / a in (t_{c-1}, t_c) for c = 1..14, at least 0.05 from both, so
+//    the cell holds no threshold but t_c and idx = c + [w > T_c] exactly
+//    (rounding in a w / r is below 1e-6 relative; the clamp covers any |w| / r).
+//    T_c comes from lane c of the row, which holds T_u = fl(t_u * r) for its
+//    own u, through ds_bpermute.  A zero radius needs no special case (see
+//    the code); a row whose r^2 is inf or NaN takes the defining comparisons
+//    against all 15 thresholds.
+//  - Inputs are read once, codes written once: both with non-temporal hints.
+constexpr int D512_ROWS = 4;                // rows per wave
+constexpr float D512_CELL_SCALE = 3.35f;    // a above; any a in (3.18, 3.53) separates the thresholds
+constexpr int64_t D512_MAX_WGS = 1 << 24;   // grid cap; the kernel strides over the rest
 
 __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const float* __restrict__ x,
                                                                           int64_t n_rows,
@@ -232,21 +241,21 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const 
                                                                           uint8_t* __restrict__ codes,
                                                                           float* __restrict__ radii) {
     constexpr int D = 512;
+    typedef float f4v __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & (KVQ_WAVE - 1);
     const int slot = lane >> 4, u = lane & 15;
     const int q = u ^ (((u >> 2) & 1) * 3);
-    // sign flip of element (j, k): bit j + 4 (q & 1) of mask byte 8 k + q / 2, gathered
+    const int g = q ^ 15;  // column group this lane loads
+    // sign flip of element (j, k): bit j + 4 (g & 1) of mask byte 8 k + g / 2, gathered
     // into bit 4 k + j of one word
     uint32_t sbits = 0;
 #pragma unroll
     for (int k = 0; k < 8; k++)
-        sbits |= (((uint32_t)sign_mask[8 * k + (q >> 1)] >> (4 * (q & 1))) & 15u) << (4 * k);
+        sbits |= (((uint32_t)sign_mask[8 * k + (g >> 1)] >> (4 * (g & 1))) & 15u) << (4 * k);
     const float c0 = (q & 1) ? -1.0f : 1.0f, c1 = (q & 2) ? -1.0f : 1.0f;
     const float c2 = (q & 4) ? -1.0f : 1.0f, c3 = (q & 8) ? -1.0f : 1.0f;
-    const uint32_t lane_sign = (uint32_t)(__builtin_popcount(q) & 1) << 31;
-    // value classes (v_cmp_class bits) of y where w = (-1)^popcount(q) y is <= 0:
-    // -inf, -normal, -denormal, -0, +0, or their mirror images
-    const int nonpos_class = lane_sign ? 0x3E0 : 0x07C;
+    const float t_own = u2f(c_tq4_thresh[min(u, 14)]);  // lane u of a row provides T_u (lane 15: unused)
+    const int perm_row = 64 * slot;                       // ds_bpermute byte address of the row's lane 0
     const bool qodd = q & 1;
     const uint32_t sel_lo = qodd ? 0x01000504u : 0x05040100u;  // own 16 bits low (even q) or high (odd q)
     const uint32_t sel_hi = qodd ? 0x03020706u : 0x07060302u;
@@ -257,21 +266,20 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const 
     // copy of the last row
     auto load = [&](int64_t base, float4 (&v)[8]) __attribute__((always_inline)) {
         const int64_t row = min(base + slot, n_rows - 1);
-        const float* xr = x + row * D + 4 * q;
+        const float* xr = x + row * D + 4 * g;
 #pragma unroll
-        for (int k = 0; k < 8; k++) v[k] = *reinterpret_cast<const float4*>(xr + 64 * k);
+        for (int k = 0; k < 8; k++) {
+            const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(xr + 64 * k));
+            v[k] = make_float4(t.x, t.y, t.z, t.w);
+        }
     };
-    // No prefetch: at 4 rows per wave and about 1100 vector instructions per
-    // iteration, the other resident waves cover a wave's load latency.
+    float4 nv[8];
+    load(first, nv);
     for (int64_t base = first; base < n_rows; base += stride) {
         float v[32];
-        {
-            float4 nv[8];
-            load(base, nv);
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                v[4 * k + 0] = nv[k].x; v[4 * k + 1] = nv[k].y; v[4 * k + 2] = nv[k].z; v[4 * k + 3] = nv[k].w;
-            }
+        for (int k = 0; k < 8; k++) {
+            v[4 * k + 0] = nv[k].x; v[4 * k + 1] = nv[k].y; v[4 * k + 2] = nv[k].z; v[4 * k + 3] = nv[k].w;
         }
         const int64_t row = base + slot;  // rows past the end hold a copy of the last row
         // radius^2: the pairwise tree over p (bits 0, 1 here, 2..5 across lanes, 6..8 here)
@@ -325,30 +333,39 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const 
                     v[i + h] = a - b;
                 }
         // bucketing; nibble of element (j, k) -> bit 4 j + 16 bit1(k) of word P[2 (k & 1) + k / 4]
-        uint32_t tb[7];
-#pragma unroll
-        for (int i = 0; i < 7; i++) tb[i] = f2u(u2f(c_tq4_thresh[8 + i]) * rad);
+        // a zero radius gives inv_a = +inf: cell 14 for w > 0, cell 0 for w < 0 and, through
+        // NaN, for w = +-0, where T_0 = -0 and T_14 = +0 make idx 15 and 0 as the definition
+        // does; a radius of inf or NaN leaves every cell in [0, 14] and the row is redone below
+        const bool redo = !(r2 <= 3.40282347e38f);
+        const float inv_a = D512_CELL_SCALE * __builtin_amdgcn_rcpf(rad);
+        const int t_me = (int)f2u(t_own * rad);
         uint32_t P[4] = {0u, 0u, 0u, 0u};
+        // 16 elements at a time: their cells, then their 16 lane reads in flight together,
+        // then the comparisons
 #pragma unroll
-        for (int k = 0; k < 8; k++)
+        for (int h = 0; h < 32; h += 16) {
+            uint32_t c[16];
+            float tc[16];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float y = v[4 * k + j];
-                const bool neg = __builtin_amdgcn_classf(y, nonpos_class);  // w = +-y <= 0
-                const uint32_t key = (f2u(y) & 0x7FFFFFFFu) + (neg ? 1u : 0u);
-                const bool b2 = key > tb[3];
-                const bool b1 = key > (b2 ? tb[5] : tb[1]);
-                const uint32_t ta = b2 ? tb[6] : tb[2], tc = b2 ? tb[4] : tb[0];
-                const bool b0 = key > (b1 ? ta : tc);
-                // idx = 8 + m (w > 0) or 7 - m (w <= 0), m = 4 b2 + 2 b1 + b0: the bits of 7 - m are
-                // those of m flipped, so idx = 8 (w > 0) + the three bits, each xor neg
-                uint32_t idx = neg ? 0u : 1u;
-                idx = 2u * idx + ((b2 != neg) ? 1u : 0u);
-                idx = 2u * idx + ((b1 != neg) ? 1u : 0u);
-                idx = 2u * idx + ((b0 != neg) ? 1u : 0u);
+            for (int i = 0; i < 16; i++) {
+                const float cf = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[h + i], inv_a, 7.5f), 0.0f, 14.5f);
+                // v_med3 returns the smaller bound or NaN for a NaN input; v_cvt_u32_f32,
+                // written out, turns NaN into 0
+                asm("v_cvt_u32_f32 %0, %1" : "=v"(c[i]) : "v"(cf));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                tc[i] = u2f((uint32_t)__builtin_amdgcn_ds_bpermute(perm_row + 4 * (int)c[i], t_me));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int e = h + i, k = e >> 2, j = e & 3;
+                const uint32_t idx = c[i] + ((v[e] > tc[i]) ? 1u : 0u);
                 P[2 * (k & 1) + (k >> 2)] |= idx << (4 * j + 16 * ((k >> 1) & 1));
             }
-        if (__builtin_amdgcn_ballot_w64(!(r2 <= 3.40282347e38f)) != 0 && !(r2 <= 3.40282347e38f)) {
+        }
+        if (__builtin_amdgcn_ballot_w64(redo) != 0 && redo) {
             // radius inf or NaN (wave-uniform test first: the common path has no select of it;
             // the empty volatile block keeps the compiler from evaluating this path speculatively)
             asm volatile("" ::: "memory");
@@ -361,7 +378,7 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const 
             for (int k = 0; k < 8; k++)
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    const float w = u2f(f2u(v[4 * k + j]) ^ lane_sign);
+                    const float w = v[4 * k + j];
                     uint32_t idx = 0;
 #pragma unroll
                     for (int t = 0; t < 15; t++) idx += (w > T[t]) ? 1u : 0u;
@@ -378,12 +395,14 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const 
         // and writes that row's bytes again (identical values), and all 16 lanes of a
         // row store its radius.
         const int64_t srow = min(row, n_rows - 1);
-        uint8_t* cr = codes + srow * (D / 2) + 2 * (q & 14) + 32 * (qodd ? 1 : 0);
-        *reinterpret_cast<uint32_t*>(cr) = __builtin_amdgcn_perm(r0, keep0, sel_lo);        // k = 0 / 1
-        *reinterpret_cast<uint32_t*>(cr + 64) = __builtin_amdgcn_perm(r0, keep0, sel_hi);   // k = 2 / 3
-        *reinterpret_cast<uint32_t*>(cr + 128) = __builtin_amdgcn_perm(r1, keep1, sel_lo);  // k = 4 / 5
-        *reinterpret_cast<uint32_t*>(cr + 192) = __builtin_amdgcn_perm(r1, keep1, sel_hi);  // k = 6 / 7
-        radii[srow] = rad;
+        uint32_t* cr = reinterpret_cast<uint32_t*>(codes + srow * (D / 2) + 2 * (q & 14) + 32 * (qodd ? 1 : 0));
+        __builtin_nontemporal_store(__builtin_amdgcn_perm(r0, keep0, sel_lo), cr);       // k = 0 / 1
+        __builtin_nontemporal_store(__builtin_amdgcn_perm(r0, keep0, sel_hi), cr + 16);  // k = 2 / 3
+        __builtin_nontemporal_store(__builtin_amdgcn_perm(r1, keep1, sel_lo), cr + 32);  // k = 4 / 5
+        __builtin_nontemporal_store(__builtin_amdgcn_perm(r1, keep1, sel_hi), cr + 48);  // k = 6 / 7
+        __builtin_nontemporal_store(rad, radii + srow);
+        // wave-uniform test: a wave's last iteration issues no load it would wait on at the end
+        if (base + stride < n_rows) load(base + stride, nv);
     }
 }
 
@@ -451,7 +470,7 @@ hipError_t launch_encode_tq(int bits, const float* x, int64_t n_rows, int dim, c
     if (dim == 512 && bits == 4) {
         const int64_t waves = (n_rows + D512_ROWS - 1) / D512_ROWS;
         int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;
-        if (wgs > 1280) wgs = 1280;  // the resident count (5 per CU at 86 VGPRs); the kernel strides
+        if (wgs > D512_MAX_WGS) wgs = D512_MAX_WGS;
         hipLaunchKernelGGL(k_encode_tq4_d512, dim3((unsigned)wgs), dim3(ENC_WAVES * KVQ_WAVE), 0, st, x, n_rows,
                            sign_mask, codes, radii);
         return hipGetLastError();

@@ -28,6 +28,7 @@ namespace {
 __constant__ uint32_t c_tq4_thresh[15] = KVQ_TQ4_THRESH_BITS;
 __constant__ uint32_t c_tq3_thresh[7] = KVQ_TQ3_THRESH_BITS;
 __constant__ uint32_t c_tq6_thresh[63] = KVQ_TQ6_THRESH_BITS;
+__constant__ uint8_t c_tq6_cell[KVQ_TQ6_CELLS] = KVQ_TQ6_CELL_TABLE;
 
 constexpr int ENC_WAVES = 4;  // waves per workgroup
 
@@ -50,19 +51,37 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_fp8(const float
 // result is bit-identical to any other evaluation in that stage order.
 // BITS = 4: nibbles, one 4-byte store per lane.  BITS = 3, 6: the lane's 8
 // indices are 3 or 6 bytes of the row's little-endian bit stream (index i in
-// bits BITS*i ..), found by a binary search over the 2^BITS - 1 thresholds in
-// LDS: T_k = fl(t_k * r) is ascending in k (or, for a radius of inf or NaN, the
-// comparisons w > T_k are still true for a prefix of k), so the search returns
-// #{k : w > T_k} exactly.
+// bits BITS*i ..).  Their index #{k : w > T_k}, T_k = fl(t_k * r), comes from a
+// cell: v = clamp(A w / r + OFF, 0, N - 1/2) and cell floor(v), where every
+// threshold lies inside a cell, at least 0.05 cell widths from its edges, and
+// no cell holds two (the generator of the cell constants asserts both; 3 bits:
+// 7 cells of width 1/1.9, one per threshold; 6 bits: 173 cells of width
+// 1/23.75, narrower than the closest pair of thresholds).  A cell's table entry
+// is c, the number of thresholds below its lower edge, and t_c, the next one
+// up, so idx = c + [w > fl(t_c r)] exactly (the rounding in A w / r is below
+// 1e-3 cell widths).  A zero radius needs no special case (as in the dim-512
+// TQ4 kernel below); a row whose r^2 is inf or NaN takes a binary search over
+// all thresholds instead: T_k is ascending in k (or, for a radius of inf or
+// NaN, w > T_k still holds for a prefix of k), so it returns the count exactly.
 template <int BITS>
 __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq(const float* __restrict__ x, int64_t n_rows,
                                                                     int dim, const uint8_t* __restrict__ sign_mask,
                                                                     uint8_t* __restrict__ codes,
                                                                     float* __restrict__ radii) {
     constexpr int NL = 1 << BITS;  // levels
+    constexpr int NC = BITS == 3 ? KVQ_TQ3_CELLS : BITS == 6 ? KVQ_TQ6_CELLS : 1;  // cells
+    constexpr float CELL_A = BITS == 3 ? KVQ_TQ3_CELL_A : BITS == 6 ? KVQ_TQ6_CELL_A : 0.0f;
+    constexpr float CELL_OFF = BITS == 3 ? KVQ_TQ3_CELL_OFF : BITS == 6 ? KVQ_TQ6_CELL_OFF : 0.0f;
+    static_assert(NC <= ENC_WAVES * KVQ_WAVE, "one cell entry per thread");
     __shared__ float th_s[NL];
+    __shared__ uint2 cell_s[NC];  // (bits of t_c, c)
     if (BITS != 4) {
-        if (threadIdx.x < NL - 1) th_s[threadIdx.x] = u2f(BITS == 3 ? c_tq3_thresh[threadIdx.x] : c_tq6_thresh[threadIdx.x]);
+        const int t = threadIdx.x;
+        if (t < NL - 1) th_s[t] = u2f(BITS == 3 ? c_tq3_thresh[t] : c_tq6_thresh[t]);
+        if (t < NC) {
+            const uint32_t c = BITS == 3 ? (uint32_t)t : (uint32_t)c_tq6_cell[t];
+            cell_s[t] = make_uint2(BITS == 3 ? c_tq3_thresh[c] : c_tq6_thresh[c], c);
+        }
         __syncthreads();
     }
     const int L = dim >> 3;
@@ -146,14 +165,32 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq(const float*
             if (L > 32) stage(std::integral_constant<int, 32>{});
         }
         if constexpr (BITS != 4) {
+            const bool redo = !(r2 <= 3.40282347e38f);
+            const float inv_a = CELL_A * __builtin_amdgcn_rcpf(rad);  // +inf for a zero radius
             uint64_t packed = 0;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const float w = v[i];
-                uint32_t idx = 0;
-#pragma unroll
-                for (int step = NL / 2; step >= 1; step >>= 1) idx += (w > th_s[idx + step - 1] * rad) ? step : 0;
+                // v_med3 returns the smaller bound or NaN for a NaN input (w = 0 with a zero
+                // radius); v_cvt_u32_f32, written out, turns NaN into cell 0
+                const float cf = __builtin_amdgcn_fmed3f(__builtin_fmaf(w, inv_a, CELL_OFF), 0.0f, NC - 0.5f);
+                uint32_t ci;
+                asm("v_cvt_u32_f32 %0, %1" : "=v"(ci) : "v"(cf));
+                const uint2 e = cell_s[ci];
+                const uint32_t idx = e.y + ((w > u2f(e.x) * rad) ? 1u : 0u);
                 packed |= (uint64_t)idx << (BITS * i);
+            }
+            if (__builtin_amdgcn_ballot_w64(redo) != 0 && redo) {
+                asm volatile("" ::: "memory");  // not evaluated speculatively
+                packed = 0;
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const float w = v[i];
+                    uint32_t idx = 0;
+#pragma unroll
+                    for (int step = NL / 2; step >= 1; step >>= 1) idx += (w > th_s[idx + step - 1] * rad) ? step : 0;
+                    packed |= (uint64_t)idx << (BITS * i);
+                }
             }
             if (valid) {
                 uint8_t* cr = codes + row * (int64_t)(dim * BITS / 8) + BITS * j;

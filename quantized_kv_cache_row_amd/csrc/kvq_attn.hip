@@ -64,7 +64,9 @@ struct Plan {
     float* q_inv;           // matrix-core paths: [n_seqs][H padded]
     float* part_m;          // [max_chunks][H]
     float* part_l;          // [max_chunks][H]
-    float* part_o;          // [max_chunks][H][512]
+    float* part_o;          // fp32 path: f32 [max_chunks][H][512]
+    uint16_t* part_h;       // matrix-core paths: fp16 O * 2^k, same order as part_o would be
+    float* part_s;          // matrix-core paths: [max_chunks][4][H], 2^-k of each 128-dim quarter
     int64_t max_chunks;
     int split_rows;
     int heads_per_group;
@@ -152,7 +154,12 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
     p.part_l = (float*)take(sizeof(float) * p.max_chunks * a.n_heads);
     // (fp8 matrix-core partials are stored per group of 32 heads, the last one padded)
     const int64_t ph = (!f32 && a.qmode == KVQ_QMODE_FP8) ? p.heads_padded : a.n_heads;
-    p.part_o = (float*)take(sizeof(float) * p.max_chunks * ph * DL);
+    if (f32) {
+        p.part_o = (float*)take(sizeof(float) * p.max_chunks * ph * DL);
+    } else {
+        p.part_h = (uint16_t*)take(sizeof(uint16_t) * p.max_chunks * ph * DL);
+        p.part_s = (float*)take(sizeof(float) * p.max_chunks * 4 * a.n_heads);
+    }
     if (bytes_out) *bytes_out = off;
     return p;
 }
@@ -428,6 +435,32 @@ __device__ __forceinline__ float pow2_scale_for(float max_abs, int log2_target) 
     if (k > 127) k = 127;
     if (k < -126) k = -126;
     return u2f((uint32_t)(k + 127) << 23);
+}
+
+// Scale of a partial O stored as fp16: 2^k with max_abs * 2^k in [2^14, 2^15) (below the
+// fp16 maximum 65504 after rounding), k in [-126, 126] (1 if max_abs == 0); *inv = 2^-k.
+__device__ __forceinline__ float f16_store_scale(float max_abs, float* inv) {
+    const uint32_t eb = min(f2u(pow2_scale_for(max_abs, 14)), 253u << 23);  // (k + 127) << 23
+    *inv = u2f((254u << 23) - eb);
+    return u2f(eb);
+}
+
+// Non-temporal 8-byte store and load (the fp8 path's partial states: written once in
+// whole 512-byte runs per wave, read once by the merge).
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_nt(uint2* p, uint2 v) {
+    __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+// Four fp16 of a stored partial O times its 2^-k (exact unless the product leaves the
+// normal range, as O itself would have).
+__device__ __forceinline__ float4 f16x4_scaled(uint2 v, float s) {
+    const f16x2_t a = __builtin_bit_cast(f16x2_t, v.x), b = __builtin_bit_cast(f16x2_t, v.y);
+    return make_float4((float)a[0] * s, (float)a[1] * s, (float)b[0] * s, (float)b[1] * s);
 }
 
 // Two e4m3 codes (byte pair HI of w) -> two fp16, exact (hardware conversion, scale 1).
@@ -1138,21 +1171,34 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
     wg_barrier_lds();  // (LDS only: the next segment's first tile stays in flight)
     const float L = (sm.lsum[0][n] + sm.lsum[1][n]) + (sm.lsum[2][n] + sm.lsum[3][n]);
     {
-        // partial O of this (chunk, group) in the matrix cores' lane order: float4
-        // ((w * 4 + b) * 4 + j) * 64 + lane holds head n = lane % 32, dims 128 w + 32 b +
-        // 8 j + 4 (lane / 32) .. + 3 (k_merge_f8 reads it in the same order)
+        // partial O of this (chunk, group) in the matrix cores' lane order, as fp16 O * 2^k
+        // with one k per head and wave (128 dims) putting the largest |O| * 2^k in
+        // [2^14, 2^15): uint2 ((w * 4 + b) * 4 + j) * 64 + lane holds head n = lane % 32,
+        // dims 128 w + 32 b + 8 j + 4 (lane / 32) .. + 3 (k_merge_f8 reads it in the same
+        // order); 2^-k in part_s
+        float am = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) am = fmaxf(am, fabsf(acc_o[b][e]));
+        am = fmaxf(am, xor_lane<32>(am, lane));
         const float so = 1.0f / rsc;  // exact (a power of two)
-        float4* dst = reinterpret_cast<float4*>(p.part_o) + (c * p.n_groups + hg) * (int64_t)(F8_HEADS * DL / 4) +
-                      wave * 16 * 64 + lane;
+        float sk_inv;
+        const float f = so * f16_store_scale(am * so, &sk_inv);  // exact: amax(acc) * f is near 2^14
+        uint2* dst = reinterpret_cast<uint2*>(p.part_h) + (c * p.n_groups + hg) * (int64_t)(F8_HEADS * DL / 4) +
+                     wave * 16 * 64 + lane;
 #pragma unroll
         for (int b = 0; b < 4; b++)
 #pragma unroll
             for (int j = 0; j < 4; j++)
-                dst[(b * 4 + j) * 64] = make_float4(acc_o[b][4 * j] * so, acc_o[b][4 * j + 1] * so,
-                                                    acc_o[b][4 * j + 2] * so, acc_o[b][4 * j + 3] * so);
-        if (wave == 0 && h == 0 && head < a.n_heads) {
-            p.part_m[c * a.n_heads + head] = m_ref;  // log2 units
-            p.part_l[c * a.n_heads + head] = L;
+                st_nt(dst + (b * 4 + j) * 64, make_uint2(pack_f16x2(acc_o[b][4 * j] * f, acc_o[b][4 * j + 1] * f),
+                                                         pack_f16x2(acc_o[b][4 * j + 2] * f, acc_o[b][4 * j + 3] * f)));
+        if (h == 0 && head < a.n_heads) {
+            __builtin_nontemporal_store(sk_inv, &p.part_s[(c * 4 + wave) * a.n_heads + head]);
+            if (wave == 0) {
+                __builtin_nontemporal_store(m_ref, &p.part_m[c * a.n_heads + head]);  // log2 units
+                __builtin_nontemporal_store(L, &p.part_l[c * a.n_heads + head]);
+            }
         }
     }
     t_seg = seg_t1;
@@ -1600,18 +1646,29 @@ __global__ __launch_bounds__(2 * MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_arg
             __syncthreads();  // (the restart barrier of the score waves)
             if (ntiles > 0) load_share(0);
         }
-        // ---- O of dims 128 wave .. + 127 of every head of the group
+        // ---- O of dims 128 wave .. + 127 of every head of the group, as fp16 O * 2^k with
+        // one k per head and wave putting the largest |O| * 2^k in [2^14, 2^15); 2^-k in part_s
         const float so = 1.0f / rs;  // exact (a power of two)
 #pragma unroll
         for (int hb = 0; hb < 4; hb++) {
             const int h = hg * TQ_HEADS + MF_HEADS * hb + n;
+            float am = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 8; mb++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) am = fmaxf(am, fabsf(acc_o[mb][hb][i]));
+            am = fmaxf(am, __shfl_xor(am, 16, 64));
+            am = fmaxf(am, __shfl_xor(am, 32, 64));
+            float sk_inv;
+            const float f = so * f16_store_scale(am * so, &sk_inv);  // exact: amax(acc) * f is near 2^14
             if (h < a.n_heads) {
-                float* dst = p.part_o + (c * a.n_heads + h) * DL + 128 * wave + 4 * g;
+                uint2* dst = reinterpret_cast<uint2*>(p.part_h + (c * a.n_heads + h) * DL + 128 * wave + 4 * g);
 #pragma unroll
                 for (int mb = 0; mb < 8; mb++) {
                     const f32x4_t v = acc_o[mb][hb];
-                    *reinterpret_cast<float4*>(dst + 16 * mb) = make_float4(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
+                    dst[4 * mb] = make_uint2(pack_f16x2(v[0] * f, v[1] * f), pack_f16x2(v[2] * f, v[3] * f));
                 }
+                if (g == 0) p.part_s[(c * 4 + wave) * a.n_heads + h] = sk_inv;
             }
         }
     }
@@ -1621,9 +1678,11 @@ __global__ __launch_bounds__(2 * MF_WAVES * 64) void k_attn_mfma_tq(kvq_attn_arg
 // NDH workgroups per (sequence, head), each over DL / NDH output dims (TQ4: the
 // whole row, which the un-rotation needs).  A thread owns one float4 column and
 // every NGRP-th split; it merges its splits online (running max, rescaled sums),
-// then the NGRP groups are combined through LDS.
+// then the NGRP groups are combined through LDS.  LOG2: the matrix-core
+// partials (log2 units, O as scaled fp16); otherwise the fp32 path's.
 template <bool TQ4, bool LOG2, int NT>
 __global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
+    constexpr bool F16 = LOG2;
     constexpr int NDH = TQ4 ? 1 : 2;
     constexpr int DW = DL / NDH;       // dims per workgroup
     constexpr int COLS = DW / 4;       // float4 columns
@@ -1644,19 +1703,28 @@ __global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
     // batches of U splits: all loads first (no branch between them), then the
     // online update with selects
     for (int64_t cb = c0 + grp; cb < c1; cb += U * NGRP) {
-        float mc[U], lc[U];
+        float mc[U], lc[U], sk[U];
         float4 v[U];
+        uint2 vh[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int64_t c = cb + u * NGRP;
-            const int64_t ch = (c < c1 ? c : cb) * a.n_heads + h;
+            const int64_t ci = c < c1 ? c : cb, ch = ci * a.n_heads + h;
             mc[u] = p.part_m[ch];
             lc[u] = p.part_l[ch];
-            v[u] = *reinterpret_cast<const float4*>(p.part_o + ch * DL + part * DW + 4 * col);
-            if (c >= c1) mc[u] = -INFINITY;
+            if (F16) {
+                const int d = part * DW + 4 * col;
+                vh[u] = *reinterpret_cast<const uint2*>(p.part_h + ch * DL + d);
+                sk[u] = p.part_s[(ci * 4 + (d >> 7)) * a.n_heads + h];
+            } else {
+                v[u] = *reinterpret_cast<const float4*>(p.part_o + ch * DL + part * DW + 4 * col);
+            }
         }
+        // (every load above is issued before any is used: a split past the end is masked here)
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            if (F16) v[u] = f16x4_scaled(vh[u], sk[u]);
+            if (cb + u * NGRP >= c1) mc[u] = -INFINITY;
             const float mn = fmaxf(m, mc[u]);
             const float sc = m == -INFINITY ? 0.0f : ex(m - mn);
             const float w = mc[u] == -INFINITY ? 0.0f : ex(mc[u] - mn);
@@ -1766,31 +1834,35 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
         c0 = min(c0, p.max_chunks);
         c1 = min(c1, p.max_chunks);
     }
-    const float4* src = reinterpret_cast<const float4*>(p.part_o) + g * (int64_t)(F8_HEADS * DL / 4) + wbj * 64 + l;
+    const uint2* src = reinterpret_cast<const uint2*>(p.part_h) + g * (int64_t)(F8_HEADS * DL / 4) + wbj * 64 + l;
+    const float* ssrc = p.part_s + (wbj >> 4) * a.n_heads + hc;  // 2^-k of quarter w of the head
     const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
     float m = -INFINITY, lsum = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int64_t cb = c0 + grp; cb < c1; cb += U * NG) {
-        float mc[U], lc[U];
-        float4 v[U];
+        float mc[U], lc[U], sk[U];
+        uint2 vh[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int64_t cc = cb + u * NG;
             const int64_t ch = cc < c1 ? cc : cb;
             mc[u] = p.part_m[ch * a.n_heads + hc];
             lc[u] = p.part_l[ch * a.n_heads + hc];
-            v[u] = src[ch * cstride];
-            if (cc >= c1) mc[u] = -INFINITY;
+            vh[u] = ld_nt(src + ch * cstride);
+            sk[u] = ssrc[ch * 4 * a.n_heads];
         }
+        // (every load above is issued before any is used: a slot past the end is masked here)
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            const float4 vu = f16x4_scaled(vh[u], sk[u]);
+            if (cb + u * NG >= c1) mc[u] = -INFINITY;
             const float mn = fmaxf(m, mc[u]);
             const float sc = m == -INFINITY ? 0.0f : exp2f(m - mn);
             const float w = mc[u] == -INFINITY ? 0.0f : exp2f(mc[u] - mn);
-            o.x = o.x * sc + w * v[u].x;
-            o.y = o.y * sc + w * v[u].y;
-            o.z = o.z * sc + w * v[u].z;
-            o.w = o.w * sc + w * v[u].w;
+            o.x = o.x * sc + w * vu.x;
+            o.y = o.y * sc + w * vu.y;
+            o.z = o.z * sc + w * vu.z;
+            o.w = o.w * sc + w * vu.w;
             lsum = lsum * sc + w * lc[u];
             m = mn;
         }
@@ -1848,36 +1920,43 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
         c0 = min(c0, p.max_chunks);
         c1 = min(c1, p.max_chunks);
     }
-    const float4* src = reinterpret_cast<const float4*>(p.part_o) + g * (int64_t)(F8_HEADS * DL / 4) + wb0 * 64 + l;
+    static_assert(16 % NB == 0, "the NB blocks lie in one 128-dim quarter");
+    const uint2* src = reinterpret_cast<const uint2*>(p.part_h) + g * (int64_t)(F8_HEADS * DL / 4) + wb0 * 64 + l;
+    const float* ssrc = p.part_s + (wb0 >> 4) * a.n_heads + hc;  // 2^-k of quarter w of the head
     const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
     float m = -INFINITY, lsum = 0.0f;
     float4 o[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) o[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int64_t cb = c0; cb < c1; cb += U) {
-        float mc[U], lc[U];
-        float4 v[U][NB];
+        float mc[U], lc[U], sk[U];
+        uint2 vh[U][NB];
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int64_t cc = cb + u;
             const int64_t ch = cc < c1 ? cc : cb;
             mc[u] = p.part_m[ch * a.n_heads + hc];
             lc[u] = p.part_l[ch * a.n_heads + hc];
+            sk[u] = ssrc[ch * 4 * a.n_heads];
 #pragma unroll
-            for (int b = 0; b < NB; b++) v[u][b] = src[ch * cstride + b * 64];
-            if (cc >= c1) mc[u] = -INFINITY;
+            for (int b = 0; b < NB; b++) vh[u][b] = ld_nt(src + ch * cstride + b * 64);
         }
+        // (every load above is issued before any is used: a slot past the end is masked here)
 #pragma unroll
         for (int u = 0; u < U; u++) {
+            if (cb + u >= c1) mc[u] = -INFINITY;
+            float4 v[NB];
+#pragma unroll
+            for (int b = 0; b < NB; b++) v[b] = f16x4_scaled(vh[u][b], sk[u]);
             const float mn = fmaxf(m, mc[u]);
             const float sc = m == -INFINITY ? 0.0f : exp2f(m - mn);
             const float w = mc[u] == -INFINITY ? 0.0f : exp2f(mc[u] - mn);
 #pragma unroll
             for (int b = 0; b < NB; b++) {
-                o[b].x = o[b].x * sc + w * v[u][b].x;
-                o[b].y = o[b].y * sc + w * v[u][b].y;
-                o[b].z = o[b].z * sc + w * v[u][b].z;
-                o[b].w = o[b].w * sc + w * v[u][b].w;
+                o[b].x = o[b].x * sc + w * v[b].x;
+                o[b].y = o[b].y * sc + w * v[b].y;
+                o[b].z = o[b].z * sc + w * v[b].z;
+                o[b].w = o[b].w * sc + w * v[b].w;
             }
             lsum = lsum * sc + w * lc[u];
             m = mn;

@@ -79,6 +79,7 @@ struct Plan {
     int64_t n_work;
     int64_t n_tiles;        // one sequence: the tile count (several: computed by the preparation)
     int64_t tile_quota;     // 0: the preparation computes max(1, ceil(tiles / n_work))
+    int64_t one_slots;      // one sequence: its partial-state slots, ceil(n_tiles / tile_quota)
     // sparse decode on the fp8 matrix-core path: logical row t of the index list is cache row
     // clamp(row_index[t], 0, cache_rows - 1), read in place (null: the rows are contiguous)
     const int64_t* row_index;
@@ -129,6 +130,7 @@ Plan make_plan(const kvq_attn_args& a, void* ws, int64_t* bytes_out) {
         if (a.n_seqs == 1) {
             p.n_tiles = (a.total_rows + F8_TILE - 1) / F8_TILE;
             if (p.tile_quota == 0) p.tile_quota = std::max<int64_t>(1, (p.n_tiles + p.n_work - 1) / p.n_work);
+            p.one_slots = (p.n_tiles + p.tile_quota - 1) / p.tile_quota;
         }
         p.max_chunks = p.n_work + a.n_seqs;
         p.chunks_per_xcd = (p.n_work + N_XCD - 1) / N_XCD;
@@ -1823,10 +1825,10 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
     const int hc = min(head, a.n_heads - 1);  // a padded head reads a real one's m, l and is not written
     // sequence s's partial states: slots (work item + s) of the work items its tiles went to
     int64_t c0 = 0, c1 = 0;
-    {
-        const bool one = a.n_seqs == 1;
-        const int64_t t0 = one ? 0 : p.chunk_prefix[s], t1 = one ? p.n_tiles : p.chunk_prefix[s + 1];
-        const int64_t q = one ? p.tile_quota : p.chunk_prefix[a.n_seqs + 1];
+    if (a.n_seqs == 1) {
+        c1 = min(p.one_slots, p.max_chunks);
+    } else {
+        const int64_t t0 = p.chunk_prefix[s], t1 = p.chunk_prefix[s + 1], q = p.chunk_prefix[a.n_seqs + 1];
         if (t1 > t0) {
             c0 = t0 / q + s;
             c1 = (t1 - 1) / q + s + 1;
@@ -1834,22 +1836,25 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
         c0 = min(c0, p.max_chunks);
         c1 = min(c1, p.max_chunks);
     }
+    const int64_t nh = a.n_heads, cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
     const uint2* src = reinterpret_cast<const uint2*>(p.part_h) + g * (int64_t)(F8_HEADS * DL / 4) + wbj * 64 + l;
-    const float* ssrc = p.part_s + (wbj >> 4) * a.n_heads + hc;  // 2^-k of quarter w of the head
-    const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
+    const float* ssrc = p.part_s + (wbj >> 4) * nh + hc;  // 2^-k of quarter w of the head
     float m = -INFINITY, lsum = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int64_t cb = c0 + grp; cb < c1; cb += U * NG) {
         float mc[U], lc[U], sk[U];
         uint2 vh[U];
+        const uint2* vb = src + cb * cstride;
+        const float* mb = p.part_m + cb * nh + hc;
+        const float* lb = p.part_l + cb * nh + hc;
+        const float* sb = ssrc + cb * 4 * nh;
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t cc = cb + u * NG;
-            const int64_t ch = cc < c1 ? cc : cb;
-            mc[u] = p.part_m[ch * a.n_heads + hc];
-            lc[u] = p.part_l[ch * a.n_heads + hc];
-            vh[u] = ld_nt(src + ch * cstride);
-            sk[u] = ssrc[ch * 4 * a.n_heads];
+            const int64_t du = cb + u * NG < c1 ? u * NG : 0;  // a slot past the end reads slot cb
+            mc[u] = mb[du * nh];
+            lc[u] = lb[du * nh];
+            vh[u] = ld_nt(vb + du * cstride);
+            sk[u] = sb[du * 4 * nh];
         }
         // (every load above is issued before any is used: a slot past the end is masked here)
 #pragma unroll
@@ -1857,8 +1862,8 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
             const float4 vu = f16x4_scaled(vh[u], sk[u]);
             if (cb + u * NG >= c1) mc[u] = -INFINITY;
             const float mn = fmaxf(m, mc[u]);
-            const float sc = m == -INFINITY ? 0.0f : exp2f(m - mn);
-            const float w = mc[u] == -INFINITY ? 0.0f : exp2f(mc[u] - mn);
+            const float sc = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+            const float w = mc[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[u] - mn);
             o.x = o.x * sc + w * vu.x;
             o.y = o.y * sc + w * vu.y;
             o.z = o.z * sc + w * vu.z;
@@ -1879,7 +1884,7 @@ __global__ __launch_bounds__(64 * NG) void k_merge_f8(kvq_attn_args a, Plan p) {
     float4 r = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
     for (int k = 0; k < NG; k++) {
-        const float wk = m_s[k][l] == -INFINITY ? 0.0f : exp2f(m_s[k][l] - M);
+        const float wk = m_s[k][l] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_s[k][l] - M);
         L += wk * l_s[k][l];
         const float4 u = o_s[k][l];
         r.x += wk * u.x; r.y += wk * u.y; r.z += wk * u.z; r.w += wk * u.w;
@@ -1909,10 +1914,10 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
     const int head = g * F8_HEADS + n;
     const int hc = min(head, a.n_heads - 1);  // a padded head reads a real one's m, l and is not written
     int64_t c0 = 0, c1 = 0;
-    {
-        const bool one = a.n_seqs == 1;
-        const int64_t t0 = one ? 0 : p.chunk_prefix[s], t1 = one ? p.n_tiles : p.chunk_prefix[s + 1];
-        const int64_t q = one ? p.tile_quota : p.chunk_prefix[a.n_seqs + 1];
+    if (a.n_seqs == 1) {
+        c1 = min(p.one_slots, p.max_chunks);
+    } else {
+        const int64_t t0 = p.chunk_prefix[s], t1 = p.chunk_prefix[s + 1], q = p.chunk_prefix[a.n_seqs + 1];
         if (t1 > t0) {
             c0 = t0 / q + s;
             c1 = (t1 - 1) / q + s + 1;
@@ -1921,9 +1926,9 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
         c1 = min(c1, p.max_chunks);
     }
     static_assert(16 % NB == 0, "the NB blocks lie in one 128-dim quarter");
+    const int64_t nh = a.n_heads, cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
     const uint2* src = reinterpret_cast<const uint2*>(p.part_h) + g * (int64_t)(F8_HEADS * DL / 4) + wb0 * 64 + l;
-    const float* ssrc = p.part_s + (wb0 >> 4) * a.n_heads + hc;  // 2^-k of quarter w of the head
-    const int64_t cstride = (int64_t)p.n_groups * (F8_HEADS * DL / 4);
+    const float* ssrc = p.part_s + (wb0 >> 4) * nh + hc;  // 2^-k of quarter w of the head
     float m = -INFINITY, lsum = 0.0f;
     float4 o[NB];
 #pragma unroll
@@ -1931,15 +1936,18 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
     for (int64_t cb = c0; cb < c1; cb += U) {
         float mc[U], lc[U], sk[U];
         uint2 vh[U][NB];
+        const uint2* vb = src + cb * cstride;
+        const float* mb = p.part_m + cb * nh + hc;
+        const float* lb = p.part_l + cb * nh + hc;
+        const float* sb = ssrc + cb * 4 * nh;
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t cc = cb + u;
-            const int64_t ch = cc < c1 ? cc : cb;
-            mc[u] = p.part_m[ch * a.n_heads + hc];
-            lc[u] = p.part_l[ch * a.n_heads + hc];
-            sk[u] = ssrc[ch * 4 * a.n_heads];
+            const int64_t du = cb + u < c1 ? u : 0;  // a slot past the end reads slot cb
+            mc[u] = mb[du * nh];
+            lc[u] = lb[du * nh];
+            sk[u] = sb[du * 4 * nh];
 #pragma unroll
-            for (int b = 0; b < NB; b++) vh[u][b] = ld_nt(src + ch * cstride + b * 64);
+            for (int b = 0; b < NB; b++) vh[u][b] = ld_nt(vb + du * cstride + b * 64);
         }
         // (every load above is issued before any is used: a slot past the end is masked here)
 #pragma unroll
@@ -1949,8 +1957,8 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
 #pragma unroll
             for (int b = 0; b < NB; b++) v[b] = f16x4_scaled(vh[u][b], sk[u]);
             const float mn = fmaxf(m, mc[u]);
-            const float sc = m == -INFINITY ? 0.0f : exp2f(m - mn);
-            const float w = mc[u] == -INFINITY ? 0.0f : exp2f(mc[u] - mn);
+            const float sc = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+            const float w = mc[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[u] - mn);
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 o[b].x = o[b].x * sc + w * v[b].x;

@@ -743,7 +743,8 @@ __global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p, NewR
         if (r < nr.n) encode_fp8_row<1>(nr.x + r * DL, DL, nr.codes + r * DL, nr.scales + r, lane);
         return;
     }
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + head
+    // wave-uniform (scalar) row and its division
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = s * heads_padded + head
     if (row >= prep_rows) return;
     const int s = (int)(row / p.heads_padded), hd = (int)(row % p.heads_padded);
     const bool hv = hd < a.n_heads;
@@ -1241,7 +1242,8 @@ __global__ __launch_bounds__(MF_WAVES * 64) void k_attn_mfma_fp8(kvq_attn_args a
 // in registers, six across lanes).
 __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // = s * heads_padded + h
+    // wave-uniform (scalar) row and its division
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = s * heads_padded + h
     if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
     const int s = (int)(row / p.heads_padded), h = (int)(row % p.heads_padded);
     const bool valid = h < a.n_heads;
@@ -1699,27 +1701,31 @@ __global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
     const int s = (int)(item / a.n_heads), h = (int)(item % a.n_heads);
     const int64_t c0 = min(p.chunk_prefix[s], p.max_chunks), c1 = min(p.chunk_prefix[s + 1], p.max_chunks);
     const int col = tid % COLS, grp = tid / COLS;
-    auto ex = [](float x) { return LOG2 ? exp2f(x) : expf(x); };
+    // (the matrix-core paths: the hardware exp2; the fp32 path: the library's exp)
+    auto ex = [](float x) { return LOG2 ? __builtin_amdgcn_exp2f(x) : expf(x); };
     float m = -INFINITY, l = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int64_t nh = a.n_heads;
+    const int d = part * DW + 4 * col;
     // batches of U splits: all loads first (no branch between them), then the
     // online update with selects
     for (int64_t cb = c0 + grp; cb < c1; cb += U * NGRP) {
         float mc[U], lc[U], sk[U];
         float4 v[U];
         uint2 vh[U];
+        // split cb's entries, and uniform offsets from them (a split past the end reads cb's)
+        const float* mb = p.part_m + cb * nh + h;
+        const float* lb = p.part_l + cb * nh + h;
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t c = cb + u * NGRP;
-            const int64_t ci = c < c1 ? c : cb, ch = ci * a.n_heads + h;
-            mc[u] = p.part_m[ch];
-            lc[u] = p.part_l[ch];
+            const int64_t du = cb + u * NGRP < c1 ? u * NGRP : 0;
+            mc[u] = mb[du * nh];
+            lc[u] = lb[du * nh];
             if (F16) {
-                const int d = part * DW + 4 * col;
-                vh[u] = *reinterpret_cast<const uint2*>(p.part_h + ch * DL + d);
-                sk[u] = p.part_s[(ci * 4 + (d >> 7)) * a.n_heads + h];
+                vh[u] = *reinterpret_cast<const uint2*>(p.part_h + (cb * nh + h) * DL + d + du * nh * DL);
+                sk[u] = p.part_s[(cb * 4 + (d >> 7)) * nh + h + du * 4 * nh];
             } else {
-                v[u] = *reinterpret_cast<const float4*>(p.part_o + ch * DL + part * DW + 4 * col);
+                v[u] = *reinterpret_cast<const float4*>(p.part_o + (cb * nh + h) * DL + d + du * nh * DL);
             }
         }
         // (every load above is issued before any is used: a split past the end is masked here)
@@ -1783,9 +1789,15 @@ __global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
                         v[i + hh] = x - y;
                     }
 #pragma unroll
-            for (int mm = 1; mm < 64; mm <<= 1)
-#pragma unroll
-                for (int i = 0; i < 8; i++) v[i] = fwht_xlane(v[i], lane, mm);
+            for (int i = 0; i < 8; i++) {
+                float x = v[i];
+                x = fwht_xlane_c<1>(x, lane);
+                x = fwht_xlane_c<2>(x, lane);
+                x = fwht_xlane_c<4>(x, lane);
+                x = fwht_xlane_c<8>(x, lane);
+                x = fwht_xlane_c<16>(x, lane);
+                v[i] = fwht_xlane_c<32>(x, lane);
+            }
             const uint32_t sm = a.sign_mask[lane];
 #pragma unroll
             for (int i = 0; i < 8; i++) {

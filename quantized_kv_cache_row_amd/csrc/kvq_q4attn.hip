@@ -9,35 +9,34 @@
 // Three launches on the caller's stream:
 //   prep   workgroup 0 writes the T-split prefix; every other wave rotates one
 //          query row (4 values per lane, stages 1-2 in registers, 4-128 across
-//          lanes), folds sm_scale * log2(e) into it and writes the 8 block sums;
-//   attn   one workgroup per (T-split, KV head), XCD-grouped so that the KV
-//          heads of one split (adjacent 144-byte head-rows of the same cells)
-//          share an L2; four waves take contiguous quarters of the split in
-//          tiles of 64 positions; partial (m, l, O) per query head;
+//          lanes), folds sm_scale * log2(e) into it and writes the score
+//          products' fp16 operands (three terms per head, in lane order);
+//   attn   one workgroup per (T-split, KV head, group of up to 4 query heads),
+//          XCD-grouped so that the KV heads of one split (adjacent 144-byte
+//          head-rows of the same cells) share an L2; four waves take contiguous
+//          quarters of the split in tiles of 32 positions; partial (m, l, O)
+//          per query head;
 //   merge  one wave per (sequence, query head): combine the splits, divide,
 //          rotate back, write out and lse.
 //
-// attn, per 64-position tile of a wave:
-//   * lane = position: page-table lookup, the K and V head-rows (nine 16-byte
-//     loads each) for the next tile are issued before this tile's arithmetic;
-//   * scores, lane = position: per block, sum_j nibble_j * q~_j over the 32
-//     elements with q~ broadcast from LDS, then d * (sum - 8 * sum_j q~_j), so
-//     each element costs one byte-to-float conversion and G fmas;
-//   * online softmax in the log2 domain per query head;
-//   * values: the tile's V head-rows go to the wave's LDS slice regrouped so
-//     that every read is aligned (nibble bytes of block b at 16b, scales at
-//     128); a lane owns 8 output elements (4 nibble bytes of one block) over
-//     the positions of one parity, O += (p d) * nibble with p from LDS, plus a
-//     per-head sum of p d for the -8 term, folded into O at the end of every
-//     tile (so the offset codes' large, nearly cancelling sums never span more
-//     than one tile's 32 positions per lane); the two parities are added
-//     across the wave halves.
-// The arithmetic stays on the vector ALU: about 9 * G + 12 wave64
-// instructions per position and KV head (scores 4 * G + 5.6, values
-// 5 * G + 6.5), which at G = 4 query heads per KV head outweighs the 288 HBM
-// bytes of the two head-rows; the matrix cores (a K = 32 step per block for
-// the scores, a V operand transposed through LDS for the values) are the way
-// past that bound.
+// attn, per 32-position tile of a wave (kernel k_q4_attn_mx, on the gfx950
+// matrix cores, v_mfma_f32_16x16x32_f16; the pages' fp32 arithmetic kept to
+// fp32 accuracy by exact fp16 operands and fp16 term splits):
+//   * lanes 0-31 carry the tile's K head-rows, lanes 32-63 its V head-rows
+//     (nine 16-byte loads, issued a tile ahead), staged into LDS regrouped so
+//     that every read is aligned (nibble bytes of block b at 16b), the block
+//     scales by block and position;
+//   * scores: per block, a K = 32 step with the codes minus 8 (exact in fp16)
+//     against three fp16 terms of the power-of-two scaled rotated query of
+//     each head (one column per head and term), then d times the result in
+//     fp32;
+//   * online softmax in the log2 domain per query head (lane = position);
+//   * values: O^T += V^T P with V^T read transposed from the staged rows
+//     (ds_read_b64_tr_b8) as (code - 8) * d * vs in two exact fp16 terms (vs a
+//     power of two that keeps the products in range) and two fp16 terms of p
+//     per head; the accumulators hold O * vs.
+// Four waves per workgroup take contiguous quarters of the split; their
+// (m, l, O) are combined through LDS into one partial per (split, query head).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -46,7 +45,7 @@ namespace kvq {
 namespace {
 
 constexpr int QA_WAVES = 4;
-constexpr int QA_TILE = 64;   // positions per wave tile (one per lane)
+constexpr int QA_TILE = 64;   // split granularity: QA_TILE * QA_WAVES positions
 constexpr int QA_HD = 256;    // head_dim
 constexpr int QA_RB = 144;    // bytes per head-row: 8 blocks of 18
 constexpr int QA_NXCD = 8;
@@ -60,8 +59,8 @@ constexpr float QA_LN2 = 0.6931471805599453f;
 
 struct Q4Plan {
     int64_t* chunk_prefix;  // [n_seqs + 1]
-    float* q_rot;           // [n_seqs][n_q][256]: H q / 16 * sm_scale * log2(e)
-    float* q_bsum;          // [n_seqs][n_q][8]: block sums of q_rot
+    uint4* q_mx;            // [n_seqs][n_kv][sub][8 blocks][64 lanes]: the score products' fp16 operands
+    float* q_inv;           // [n_seqs][n_q]: 1 / qs of each head's operands
     float* part_m;          // [max_chunks][n_q] (log2 domain)
     float* part_l;          // [max_chunks][n_q]
     float* part_o;          // [max_chunks][n_q][256] (rotated domain, unnormalized)
@@ -100,8 +99,8 @@ Q4Plan q4_make_plan(const kvq_q4_cache& c, const kvq_q4_attn_args& a, void* ws, 
     };
     const int64_t rows_q = (int64_t)a.n_seqs * a.n_q_heads;
     p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
-    p.q_rot = (float*)take(sizeof(float) * rows_q * QA_HD);
-    p.q_bsum = (float*)take(sizeof(float) * rows_q * 8);
+    p.q_mx = (uint4*)take(sizeof(uint4) * (int64_t)a.n_seqs * c.n_kv_heads * p.sub * 8 * 64);
+    p.q_inv = (float*)take(sizeof(float) * rows_q);
     p.part_m = (float*)take(sizeof(float) * p.max_chunks * a.n_q_heads);
     p.part_l = (float*)take(sizeof(float) * p.max_chunks * a.n_q_heads);
     p.part_o = (float*)take(sizeof(float) * p.max_chunks * a.n_q_heads * QA_HD);
@@ -138,6 +137,17 @@ __device__ __forceinline__ void fwht256_wave(float (&x)[4], int lane) {
     }
 }
 
+// Power of two 2^k with max_abs * 2^k in [2^t, 2^(t+1)) for normal max_abs; 1 for 0.
+__device__ __forceinline__ float q4_pow2_scale(float max_abs, int t) {
+    if (!(max_abs > 0.0f)) return 1.0f;
+    int e = (int)((f2u(max_abs) >> 23) & 255u) - 127;
+    if (e < -126) e = -126;
+    int k = t - e;
+    if (k > 127) k = 127;
+    if (k < -126) k = -126;
+    return u2f((uint32_t)(k + 127) << 23);
+}
+
 // ---- prep -------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
     const int tid = threadIdx.x;
@@ -169,7 +179,8 @@ __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
         return;
     }
     const int lane = tid & 63;
-    const int64_t row = (int64_t)(blockIdx.x - 1) * 4 + (tid >> 6);
+    // wave-uniform (scalar) row and its divisions
+    const int64_t row = (int64_t)(blockIdx.x - 1) * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
     if (row >= (int64_t)a.n_seqs * a.n_q_heads) return;
     const float4 v = reinterpret_cast<const float4*>(a.q + row * QA_HD)[lane];
     float x[4] = {v.x, v.y, v.z, v.w};
@@ -177,13 +188,39 @@ __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
     const float sc = a.sm_scale * QA_LOG2E;
 #pragma unroll
     for (int i = 0; i < 4; i++) x[i] *= sc;
-    reinterpret_cast<float4*>(p.q_rot + row * QA_HD)[lane] = make_float4(x[0], x[1], x[2], x[3]);
-    // block b = elements 32b .. 32b+31 = lanes 8b .. 8b+7
-    float bs = (x[0] + x[1]) + (x[2] + x[3]);
-    bs += shfl_xor_f(bs, 1);
-    bs += shfl_xor_f(bs, 2);
-    bs += shfl_xor_f(bs, 4);
-    if ((lane & 7) == 0) p.q_bsum[row * 8 + (lane >> 3)] = bs;
+    // The score products' B operands (v_mfma_f32_16x16x32_f16, one K = 32 step per block),
+    // x = H q / 16 * sm_scale * log2(e):
+    // x * qs (qs a power of two, max |x| qs in [2^14, 2^15)) as three fp16 terms, about
+    // 33 significant bits together.  Column n = h + 4 t holds term t of head h of the
+    // workgroup's 4; lane (g, n) holds k = 8 g + e, which is block element 4 g + e for
+    // e < 4 and 16 + 4 g + e - 4 for e >= 4 (the low and high nibbles of bytes 4 g ..
+    // 4 g + 3).  This lane's elements 4 (lane % 8) .. + 3 of block lane / 8 are
+    // k = 8 g + 4 hf + {0..3} with g = lane % 4, hf = (lane / 4) % 2.
+    float qmax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    qmax = wave_max(qmax);
+    const float qs = q4_pow2_scale(qmax, 14);
+    const int64_t sq = row / a.n_q_heads;
+    const int hq = (int)(row - sq * a.n_q_heads), kv = hq / p.group, hl = hq - kv * p.group;
+    const int part = hl / QA_GMAX, hh = hl % QA_GMAX;
+    const int64_t nkv = a.n_q_heads / p.group;
+    uint2* qm = reinterpret_cast<uint2*>(p.q_mx + (((sq * nkv + kv) * p.sub + part) * 8 + (lane >> 3)) * 64);
+    const int gk = lane & 3, hf = (lane >> 2) & 1;
+    float r[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) r[i] = x[i] * qs;  // exact
+#pragma unroll
+    for (int t = 0; t < 3; t++) {
+        float tv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            tv[i] = (float)(_Float16)r[i];  // round to nearest even
+            r[i] -= tv[i];                  // exact
+        }
+        qm[2 * (16 * gk + hh + 4 * t) + hf] =
+            make_uint2(f32_to_f16_rne(tv[0]) | (f32_to_f16_rne(tv[1]) << 16),
+                       f32_to_f16_rne(tv[2]) | (f32_to_f16_rne(tv[3]) << 16));
+    }
+    if (lane == 0) p.q_inv[row] = 1.0f / qs;  // exact
 }
 
 // ---- attn -------------------------------------------------------------------------
@@ -202,60 +239,6 @@ __device__ __forceinline__ uint32_t row_dw(const uint32_t (&r)[36]) {
         const uint64_t pair = ((uint64_t)r[OFF / 4 + 1] << 32) | r[OFF / 4];
         return (uint32_t)(pair >> (8 * (OFF % 4)));
     }
-}
-
-template <int G>
-struct Q4AttnShared {
-    float q[G][QA_HD];
-    float qb[G][8];
-    uint8_t v[QA_WAVES][QA_TILE][QA_RB];
-    float pr[QA_WAVES][QA_TILE][G];
-    float m[QA_WAVES][G];
-    float l[QA_WAVES][G];
-};
-
-// Bytes 4W .. 4W+3 of block B's nibbles: elements 4W .. 4W+3 (low nibbles) and
-// 16 + 4W .. 16 + 4W + 3 (high nibbles) against the broadcast rotated queries.
-template <int G, int B, int W>
-__device__ __forceinline__ void qk_word(const uint32_t (&k)[36], const Q4AttnShared<G>& sh, float (&acc)[G]) {
-    const uint32_t x = row_dw<18 * B + 2 + 4 * W>(k);
-    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-    float nl[4], nh[4];
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        nl[e] = (float)((lo >> (8 * e)) & 0xFFu);
-        nh[e] = (float)((hi >> (8 * e)) & 0xFFu);
-    }
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        const float4 ql = *reinterpret_cast<const float4*>(&sh.q[h][32 * B + 4 * W]);
-        const float4 qh = *reinterpret_cast<const float4*>(&sh.q[h][32 * B + 16 + 4 * W]);
-        float t = acc[h];
-        t = __builtin_fmaf(nl[0], ql.x, t);
-        t = __builtin_fmaf(nl[1], ql.y, t);
-        t = __builtin_fmaf(nl[2], ql.z, t);
-        t = __builtin_fmaf(nl[3], ql.w, t);
-        t = __builtin_fmaf(nh[0], qh.x, t);
-        t = __builtin_fmaf(nh[1], qh.y, t);
-        t = __builtin_fmaf(nh[2], qh.z, t);
-        t = __builtin_fmaf(nh[3], qh.w, t);
-        acc[h] = t;
-    }
-}
-
-// Block B of the K head-row: sc += d * (sum_j nibble_j q~_j - 8 sum_j q~_j).
-template <int G, int B>
-__device__ __forceinline__ void qk_block(const uint32_t (&k)[36], const Q4AttnShared<G>& sh, float (&sc)[G]) {
-    const float d = half_bits_to_f32(row_dw<18 * B>(k));
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) acc[h] = 0.0f;
-    qk_word<G, B, 0>(k, sh, acc);
-    qk_word<G, B, 1>(k, sh, acc);
-    qk_word<G, B, 2>(k, sh, acc);
-    qk_word<G, B, 3>(k, sh, acc);
-#pragma unroll
-    for (int h = 0; h < G; h++) sc[h] = __builtin_fmaf(d, __builtin_fmaf(-8.0f, sh.qb[h][B], acc[h]), sc[h]);
 }
 
 // A V head-row into the wave's LDS slice, blocks regrouped so that every read
@@ -281,9 +264,94 @@ __device__ __forceinline__ void stage_v_row(const uint32_t (&r)[36], uint8_t* ds
                    sc2(row_dw<72>(r), row_dw<90>(r)), sc2(row_dw<108>(r), row_dw<126>(r)));
 }
 
+// ---- attn on the matrix cores ------------------------------------------------------
+// v_mfma_f32_16x16x32_f16 (lane (g, n) = (l / 16, l % 16) holds A[n][8 g + e] and
+// B[8 g + e][n], e < 8, and D[4 g + i][n], i < 4).  Per 64-position tile of a wave:
+//   * scores: for 16 positions and block b, A = the codes minus 8 (exact in fp16),
+//     K index 8 g + e = block element 4 g + e (e < 4) or 16 + 4 g + e - 4 (the
+//     low and high nibbles of bytes 4 g .. 4 g + 3), B = three fp16 terms of
+//     q~ * qs per head (column h + 4 t), C = 0; then s += d_b * D in fp32, the
+//     terms summed across lanes, times 1 / qs;
+//   * online softmax per head, lane = position, through LDS;
+//   * values: O^T (dims x columns) += A B over 32 positions: A = (code - 8) *
+//     d * vs as two exact fp16 terms (the product has at most 14 significant
+//     bits; vs a power of two per tile putting 8 max |d| vs in [2^14, 2^15)),
+//     read transposed from the staged rows (ds_read_b64_tr_b8: the 16 lanes
+//     of group g receive byte n of block b from positions 8 g .. 8 g + 7), B =
+//     two fp16 terms of p per head (column h + 4 t); the accumulators hold O * vs
+//     and are rescaled by alpha * vs_new / vs per tile.
+typedef _Float16 q4h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 q4h8_t __attribute__((ext_vector_type(8)));
+typedef float q4f4_t __attribute__((ext_vector_type(4)));
+typedef int q4i2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t h2_add(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(q4h2_t, a) + __builtin_bit_cast(q4h2_t, b));
+}
+__device__ __forceinline__ uint32_t h2_mul(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(q4h2_t, a) * __builtin_bit_cast(q4h2_t, b));
+}
+// a * b + c with one rounding
+__device__ __forceinline__ uint32_t h2_fma(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(q4h2_t, a),
+                                                                  __builtin_bit_cast(q4h2_t, b),
+                                                                  __builtin_bit_cast(q4h2_t, c)));
+}
+// Eight bytes b (each 0 .. 15: bytes 0..3 of w0, then of w1) -> eight fp16 b - 8, exact:
+// the byte under 0x64 is the binary16 1024 + b, then 1032 is subtracted.
+__device__ __forceinline__ uint4 q4_nib_f16(uint32_t w0, uint32_t w1) {
+    const uint32_t c = 0x64646464u, m = 0xE408E408u;  // m = (-1032, -1032)
+    return make_uint4(h2_add(__builtin_amdgcn_perm(c, w0, 0x04010400u), m),
+                      h2_add(__builtin_amdgcn_perm(c, w0, 0x04030402u), m),
+                      h2_add(__builtin_amdgcn_perm(c, w1, 0x04010400u), m),
+                      h2_add(__builtin_amdgcn_perm(c, w1, 0x04030402u), m));
+}
+__device__ __forceinline__ q4f4_t q4_mfma(uint4 a, uint4 b, q4f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(q4h8_t, a), __builtin_bit_cast(q4h8_t, b), c,
+                                                  0, 0, 0);
+}
+// The value of lane + K within the 16-lane row (0 past its end).
+template <int K>
+__device__ __forceinline__ float row_from_above(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xF, 0xF, true));
+}
+
+constexpr int QM_TILE = 32;  // positions per wave tile: lanes 0-31 carry their K head-rows, 32-63 their V head-rows
+
+// Maximum over the wave, on DPP and lane swaps (every lane gets it).
+__device__ __forceinline__ float q4_wave_max(float v, int lane) {
+    v = fmaxf(v, xor_lane<1>(v, lane));
+    v = fmaxf(v, xor_lane<2>(v, lane));
+    v = fmaxf(v, xor_lane<4>(v, lane));
+    v = fmaxf(v, xor_lane<8>(v, lane));
+    v = fmaxf(v, xor_lane<16>(v, lane));
+    return fmaxf(v, xor_lane<32>(v, lane));
+}
+
+struct Q4MxShared {
+    uint8_t k[QA_WAVES][QM_TILE][QA_RB];  // the tile's K head-rows, regrouped as stage_v_row does
+    uint8_t v[QA_WAVES][QM_TILE][QA_RB];  // the V head-rows, the same
+    uint16_t dk[QA_WAVES][8][QM_TILE];    // K block scales (binary16) by block, then position
+    uint16_t dv[QA_WAVES][8][QM_TILE];    // V block scales times vs (binary16), the same
+    float sc[QA_WAVES][QM_TILE][4];       // scores (log2 units) by position, then head
+    float pr[QA_WAVES][4][QM_TILE];       // probabilities by head, then position
+    float m[QA_WAVES][4];
+    float l[QA_WAVES][4];
+};
+
+template <int B>
+__device__ __forceinline__ void stage_scale(const uint32_t (&r)[36], bool is_v, float vs, uint16_t* dst) {
+    const uint32_t bits = row_dw<18 * B>(r) & 0xFFFFu;
+    dst[B * QM_TILE] = (uint16_t)(is_v ? f32_to_f16_rne(half_bits_to_f32(bits) * vs) : bits);  // exact when normal
+}
+template <int B>
+__device__ __forceinline__ float row_dabs(const uint32_t (&r)[36]) {
+    return fabsf(half_bits_to_f32(row_dw<18 * B>(r)));
+}
+
 template <int G>
-__global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q4_attn_args a, Q4Plan p) {
-    __shared__ __align__(16) Q4AttnShared<G> sh;
+__global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c, kvq_q4_attn_args a, Q4Plan p) {
+    __shared__ __align__(16) Q4MxShared sh;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t n_items = p.max_chunks * c.n_kv_heads * p.sub;
@@ -309,154 +377,203 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
     const int hq0 = g * p.group + part * G;
     const int64_t qrow0 = (int64_t)s * a.n_q_heads + hq0;
 
-    // rotated queries of the G heads and their block sums
-    for (int i = tid; i < G * QA_HD / 4; i += QA_WAVES * 64)
-        reinterpret_cast<float4*>(&sh.q[0][0])[i] = reinterpret_cast<const float4*>(p.q_rot + qrow0 * QA_HD)[i];
-    if (tid < G * 8) (&sh.qb[0][0])[tid] = p.q_bsum[qrow0 * 8 + tid];
-    __syncthreads();
+    // MFMA lane (gq, nq); the score operands of this workgroup's heads (columns of absent
+    // heads and of t = 3 are zero) and 1 / qs of head nq
+    const int gq = lane >> 4, nq = lane & 15;
+    uint4 qb[8];
+    {
+        const bool col = nq < 12 && (nq & 3) < G;
+        const uint4* qsrc = p.q_mx + (((int64_t)s * c.n_kv_heads + g) * p.sub + part) * (8 * 64) + lane;
+#pragma unroll
+        for (int b = 0; b < 8; b++) {
+            const uint4 v = qsrc[b * 64];
+            qb[b] = col ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    const float qinv = p.q_inv[qrow0 + min(nq & 3, G - 1)];
 
-    const int64_t quarter = ((r1 - r0 + QA_WAVES - 1) / QA_WAVES + QA_TILE - 1) / QA_TILE * QA_TILE;
+    const int64_t quarter = ((r1 - r0 + QA_WAVES - 1) / QA_WAVES + QM_TILE - 1) / QM_TILE * QM_TILE;
     const int64_t w0 = r0 + wave * quarter;
     const int64_t w1 = min(r1, w0 + quarter);
 
-    // position -> cell; false where the page column, entry or cell is missing
+    // lane l carries position l % 32 of the tile: its K head-row (l < 32) or V head-row
+    const bool is_v = lane >= 32;
+    const int pl = lane & 31;
     const int64_t cap = (int64_t)c.max_pages * c.page_size;
     const int32_t* __restrict__ tab = c.block_table + (int64_t)s * c.max_pages;
-    auto cell_of = [&](int64_t pos, int64_t& cell) {
-        if (pos >= cap) return false;
-        const int64_t col = pos / c.page_size;
-        const int32_t pg = tab[col];
-        cell = (int64_t)pg * c.page_size + (pos - col * c.page_size);
-        return pg >= 0 && cell < c.n_cells;
-    };
-    auto load_rows = [&](int64_t t0, uint4 (&kr)[9], uint4 (&vr)[9]) {
-        const int64_t pos = t0 + lane;
+    const uint8_t* __restrict__ pool = is_v ? c.v_pool : c.k_pool;
+    // (the row is masked where it is used, a tile later: a mask applied here would make the
+    // compiler wait for the loads at once)
+    auto load_row = [&](int64_t t0, uint4 (&rr)[9]) {
+        const int64_t pos = t0 + pl;
+        bool ok = pos < w1 && pos < cap;
         int64_t cell = 0;
-        const bool ok = pos < w1 && cell_of(pos, cell);
-        const int64_t off = ((ok ? cell : 0) * c.n_kv_heads + g) * QA_RB;
-        const uint4* kp = reinterpret_cast<const uint4*>(c.k_pool + off);
-        const uint4* vp = reinterpret_cast<const uint4*>(c.v_pool + off);
-        const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;  // a missing position reads as zeros
-#pragma unroll
-        for (int i = 0; i < 9; i++) {
-            const uint4 kv = kp[i], vv = vp[i];
-            kr[i] = make_uint4(kv.x & keep, kv.y & keep, kv.z & keep, kv.w & keep);
-            vr[i] = make_uint4(vv.x & keep, vv.y & keep, vv.z & keep, vv.w & keep);
+        if (ok) {
+            const int64_t col = pos / c.page_size;
+            const int32_t pg = tab[col];
+            cell = (int64_t)pg * c.page_size + (pos - col * c.page_size);
+            ok = pg >= 0 && cell < c.n_cells;
         }
+        const uint4* rp = reinterpret_cast<const uint4*>(pool + ((ok ? cell : 0) * c.n_kv_heads + g) * QA_RB);
+#pragma unroll
+        for (int i = 0; i < 9; i++) rr[i] = rp[i];
         return ok;
     };
 
-    float m[G], lp[G], o[G][8];
+    float m[G], lp[G];
 #pragma unroll
     for (int h = 0; h < G; h++) {
         m[h] = -INFINITY;
         lp[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; e++) o[h][e] = 0.0f;
     }
-    const bool any_cells = c.n_cells > 0;
-    uint4 kn[9], vn[9];
+    q4f4_t acc[8][2];  // O^T * vs: dims 32 b + 16 half + 4 gq + i, column nq
 #pragma unroll
-    for (int i = 0; i < 9; i++) kn[i] = vn[i] = make_uint4(0, 0, 0, 0);  // no cells: every row reads as zeros
+    for (int b = 0; b < 8; b++) acc[b][0] = acc[b][1] = q4f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float vs = 1.0f;
+    const bool any_cells = c.n_cells > 0;
+    uint4 rn[9];
+#pragma unroll
+    for (int i = 0; i < 9; i++) rn[i] = make_uint4(0, 0, 0, 0);
     bool okn = false;
-    if (w0 < w1 && any_cells) okn = load_rows(w0, kn, vn);
-    // value lane: positions of parity vh, block vb, nibble bytes 4 vk .. 4 vk + 3
-    const int vh = lane >> 5, vb = (lane & 31) >> 2, vk = lane & 3;
-    for (int64_t t0 = w0; t0 < w1; t0 += QA_TILE) {
-        const int nt = (int)min((int64_t)QA_TILE, w1 - t0);
-        uint32_t k[36], vw[36];
+    if (w0 < w1 && any_cells) okn = load_row(w0, rn);
+    const q4f4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t t0 = w0; t0 < w1; t0 += QM_TILE) {
+        uint32_t r[36];
+        const uint32_t keep = okn ? 0xFFFFFFFFu : 0u;  // a missing position reads as zeros
 #pragma unroll
         for (int i = 0; i < 9; i++) {
-            k[4 * i] = kn[i].x;
-            k[4 * i + 1] = kn[i].y;
-            k[4 * i + 2] = kn[i].z;
-            k[4 * i + 3] = kn[i].w;
-            vw[4 * i] = vn[i].x;
-            vw[4 * i + 1] = vn[i].y;
-            vw[4 * i + 2] = vn[i].z;
-            vw[4 * i + 3] = vn[i].w;
+            r[4 * i] = rn[i].x & keep;
+            r[4 * i + 1] = rn[i].y & keep;
+            r[4 * i + 2] = rn[i].z & keep;
+            r[4 * i + 3] = rn[i].w & keep;
         }
-        stage_v_row(vw, &sh.v[wave][lane][0]);
         const bool ok = okn;
-        if (t0 + QA_TILE < w1 && any_cells) okn = load_rows(t0 + QA_TILE, kn, vn);
+        // the V scale: kept while 8 max |d| vs stays in [2^10, 2^15) (the products then stay
+        // exact down to 2^-24 of that bound), else chosen again with 8 max |d| vs in [2^14, 2^15)
+        float dm = fmaxf(fmaxf(fmaxf(row_dabs<0>(r), row_dabs<1>(r)), fmaxf(row_dabs<2>(r), row_dabs<3>(r))),
+                         fmaxf(fmaxf(row_dabs<4>(r), row_dabs<5>(r)), fmaxf(row_dabs<6>(r), row_dabs<7>(r))));
+        dm = q4_wave_max(is_v ? dm : 0.0f, lane);
+        const float span = 8.0f * dm * vs;
+        const float vs_new = (span < 32768.0f && (span >= 1024.0f || dm == 0.0f)) ? vs : q4_pow2_scale(8.0f * dm, 14);
+        stage_v_row(r, is_v ? &sh.v[wave][pl][0] : &sh.k[wave][pl][0]);
+        {
+            uint16_t* sd = is_v ? &sh.dv[wave][0][pl] : &sh.dk[wave][0][pl];
+            stage_scale<0>(r, is_v, vs_new, sd);
+            stage_scale<1>(r, is_v, vs_new, sd);
+            stage_scale<2>(r, is_v, vs_new, sd);
+            stage_scale<3>(r, is_v, vs_new, sd);
+            stage_scale<4>(r, is_v, vs_new, sd);
+            stage_scale<5>(r, is_v, vs_new, sd);
+            stage_scale<6>(r, is_v, vs_new, sd);
+            stage_scale<7>(r, is_v, vs_new, sd);
+        }
+        if (t0 + QM_TILE < w1 && any_cells) okn = load_row(t0 + QM_TILE, rn);
 
-        // scores (log2 domain), lane = position
-        float sc[G];
+        // ---- scores: positions 16 P + 4 gq + i, column nq
 #pragma unroll
-        for (int h = 0; h < G; h++) sc[h] = 0.0f;
-        qk_block<G, 0>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 1>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 2>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 3>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 4>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 5>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 6>(k, sh, sc);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_block<G, 7>(k, sh, sc);
+        for (int P = 0; P < 2; P++) {
+            float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int b = 0; b < 8; b++) {
+                const uint32_t x = *reinterpret_cast<const uint32_t*>(&sh.k[wave][16 * P + nq][16 * b + 4 * gq]);
+                const q4f4_t cb = q4_mfma(q4_nib_f16(x & 0x0F0F0F0Fu, (x >> 4) & 0x0F0F0F0Fu), qb[b], zero4);
+                const uint2 dd = *reinterpret_cast<const uint2*>(&sh.dk[wave][b][16 * P + 4 * gq]);
+                sp[0] = __builtin_fmaf(half_bits_to_f32(dd.x), cb[0], sp[0]);
+                sp[1] = __builtin_fmaf(half_bits_to_f32(dd.x >> 16), cb[1], sp[1]);
+                sp[2] = __builtin_fmaf(half_bits_to_f32(dd.y), cb[2], sp[2]);
+                sp[3] = __builtin_fmaf(half_bits_to_f32(dd.y >> 16), cb[3], sp[3]);
+            }
+            // the three terms of column h + 4 t: lanes nq < 4 get head nq's sum
+            float tp[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float v = sp[i];
+                tp[i] = ((v + row_from_above<4>(v)) + row_from_above<8>(v)) * qinv;
+            }
+            if (nq < G) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) sh.sc[wave][16 * P + 4 * gq + i][nq] = tp[i];
+            }
+        }
 
-        // online softmax per head; p to LDS
+        // ---- online softmax per head, lane = position (lanes 0-31)
+        const float4 s4 = *reinterpret_cast<const float4*>(&sh.sc[wave][pl][0]);
+        const float sl[4] = {s4.x, s4.y, s4.z, s4.w};
+        float alpha[G];
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            const float sv = ok ? sc[h] : -INFINITY;
-            const float mn = fmaxf(m[h], wave_max(sv));
-            float pv = 0.0f, alpha = 1.0f;
+            const float sv = (ok && !is_v) ? sl[h] : -INFINITY;
+            const float mn = fmaxf(m[h], q4_wave_max(sv, lane));
+            float pv = 0.0f, al = 1.0f;
             if (mn != -INFINITY) {  // wave-uniform
-                alpha = exp2f(m[h] - mn);
+                al = exp2f(m[h] - mn);
                 pv = exp2f(sv - mn);
             }
             m[h] = mn;
-            lp[h] = __builtin_fmaf(lp[h], alpha, pv);
+            lp[h] = __builtin_fmaf(lp[h], al, pv);
+            alpha[h] = al;
+            if (!is_v) sh.pr[wave][h][pl] = pv;
+        }
+        {  // rescale (wave-uniform test: after the first tiles the maxima and vs rarely move):
+           // column nq belongs to head nq % 4
+            bool same = vs_new == vs;
 #pragma unroll
-            for (int e = 0; e < 8; e++) o[h][e] *= alpha;
-            sh.pr[wave][lane][h] = pv;
+            for (int h = 0; h < G; h++) same = same && alpha[h] == 1.0f;
+            if (!same) {
+                float f = alpha[0];
+#pragma unroll
+                for (int h = 1; h < G; h++) f = (nq & 3) == h ? alpha[h] : f;
+                f *= vs_new / vs;  // powers of two: exact
+#pragma unroll
+                for (int b = 0; b < 8; b++) {
+                    acc[b][0] *= f;
+                    acc[b][1] *= f;
+                }
+                vs = vs_new;
+            }
         }
 
-        // values: lane = elements 32 vb + 4 vk + {0..3} and 32 vb + 16 + 4 vk + {0..3} over the
-        // positions of parity vh (rows past nt are zero with p = 0, so the pair loop may read one);
-        // cs = this tile's sum of p d, the weight of the -8 offset, folded in below
-        float cs[G];
+        // ---- values over the tile's 32 positions
+        uint4 pb;  // B: term nq / 4 of p of head nq % 4 at positions 8 gq + e
+        {
+            const int hs = min(nq & 3, G - 1);
+            const float4 pa = *reinterpret_cast<const float4*>(&sh.pr[wave][hs][8 * gq]);
+            const float4 pc = *reinterpret_cast<const float4*>(&sh.pr[wave][hs][8 * gq + 4]);
+            const float pe[8] = {pa.x, pa.y, pa.z, pa.w, pc.x, pc.y, pc.z, pc.w};
+            const bool second = nq >= 4;
+            uint32_t w[4];
 #pragma unroll
-        for (int h = 0; h < G; h++) cs[h] = 0.0f;
-#pragma unroll 4
-        for (int tt = 0; tt < nt; tt += 2) {
-            const int t = tt + vh;
-            const uint8_t* vrow = &sh.v[wave][t][0];
-            const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + 16 * vb + 4 * vk);
-            const float d = half_bits_to_f32(*reinterpret_cast<const uint16_t*>(vrow + 128 + 2 * vb));
-            const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-            float n[8];
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                n[e] = (float)((lo >> (8 * e)) & 0xFFu);
-                n[4 + e] = (float)((hi >> (8 * e)) & 0xFFu);
+            for (int j = 0; j < 4; j++) {
+                const float x0 = pe[2 * j], x1 = pe[2 * j + 1];
+                const float a0 = (float)(_Float16)x0, a1 = (float)(_Float16)x1;
+                w[j] = f32_to_f16_rne(second ? x0 - a0 : a0) | (f32_to_f16_rne(second ? x1 - a1 : a1) << 16);
             }
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                const float wgt = sh.pr[wave][t][h] * d;
-#pragma unroll
-                for (int e = 0; e < 8; e++) o[h][e] = __builtin_fmaf(wgt, n[e], o[h][e]);
-                cs[h] += wgt;
-            }
+            const bool col = nq < 8 && (nq & 3) < G;
+            pb = col ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0u, 0u, 0u, 0u);
         }
-        // sum p d (nibble - 8) = sum p d nibble - 8 sum p d, once per tile
+        const int prow = 8 * gq + (nq >> 1);  // the row this lane's address names
 #pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int e = 0; e < 8; e++) o[h][e] = __builtin_fmaf(-8.0f, cs[h], o[h][e]);
+        for (int b = 0; b < 8; b++) {
+            const q4i2_t xv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) q4i2_t*)(&sh.v[wave][prow][16 * b + 8 * (nq & 1)]));
+            const uint32_t x0 = (uint32_t)xv[0], x1 = (uint32_t)xv[1];
+            const uint4 ds = *reinterpret_cast<const uint4*>(&sh.dv[wave][b][8 * gq]);
+            const uint4 nl = q4_nib_f16(x0 & 0x0F0F0F0Fu, x1 & 0x0F0F0F0Fu);
+            const uint4 nh = q4_nib_f16((x0 >> 4) & 0x0F0F0F0Fu, (x1 >> 4) & 0x0F0F0F0Fu);
+            const uint4 lhi = make_uint4(h2_mul(nl.x, ds.x), h2_mul(nl.y, ds.y), h2_mul(nl.z, ds.z), h2_mul(nl.w, ds.w));
+            const uint4 llo = make_uint4(h2_fma(nl.x, ds.x, lhi.x ^ 0x80008000u), h2_fma(nl.y, ds.y, lhi.y ^ 0x80008000u),
+                                         h2_fma(nl.z, ds.z, lhi.z ^ 0x80008000u), h2_fma(nl.w, ds.w, lhi.w ^ 0x80008000u));
+            const uint4 hhi = make_uint4(h2_mul(nh.x, ds.x), h2_mul(nh.y, ds.y), h2_mul(nh.z, ds.z), h2_mul(nh.w, ds.w));
+            const uint4 hlo = make_uint4(h2_fma(nh.x, ds.x, hhi.x ^ 0x80008000u), h2_fma(nh.y, ds.y, hhi.y ^ 0x80008000u),
+                                         h2_fma(nh.z, ds.z, hhi.z ^ 0x80008000u), h2_fma(nh.w, ds.w, hhi.w ^ 0x80008000u));
+            acc[b][0] = q4_mfma(lhi, pb, acc[b][0]);
+            acc[b][0] = q4_mfma(llo, pb, acc[b][0]);
+            acc[b][1] = q4_mfma(hhi, pb, acc[b][1]);
+            acc[b][1] = q4_mfma(hlo, pb, acc[b][1]);
+        }
     }
-    // the two position parities
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) o[h][e] += xor_lane<32>(o[h][e], lane);
 
-    // wave states -> LDS, then combine the four waves per query head
+    // ---- the wave's (m, l, O): O = acc / vs, the two terms of column h + 4 t added
 #pragma unroll
     for (int h = 0; h < G; h++) {
         const float l = wave_sum(lp[h]);
@@ -465,43 +582,42 @@ __global__ __launch_bounds__(QA_WAVES * 64) void k_q4_attn(kvq_q4_cache c, kvq_q
             sh.l[wave][h] = l;
         }
     }
-    __syncthreads();  // every wave is past its last read of sh.v and sh.pr
-    float* ob = reinterpret_cast<float*>(&sh.v[0][0][0]);  // [QA_WAVES][G][256] when it fits
-    constexpr int HB = (int)(sizeof(sh.v) / (sizeof(float) * QA_WAVES * QA_HD));  // heads that fit per pass
-    constexpr int HPASS = G <= 8 ? G : 8;                                          // heads per exchange pass
-    static_assert(HPASS <= HB && G % HPASS == 0, "exchange buffer");
-    const int e0 = 32 * vb + 4 * vk;
-    for (int hb = 0; hb < G; hb += HPASS) {
-        if (vh == 0) {
+    const float vinv = 1.0f / vs;  // exact
+    __syncthreads();  // every wave is past its last read of the staged rows
+    float* ob = reinterpret_cast<float*>(&sh.k[0][0][0]);  // [QA_WAVES][G][256]
+    static_assert(sizeof(sh.k) + sizeof(sh.v) >= sizeof(float) * QA_WAVES * 4 * QA_HD, "exchange buffer");
 #pragma unroll
-            for (int hh = 0; hh < HPASS; hh++) {
-                const int h = hb + hh;
-                float* dst = ob + ((int64_t)wave * HPASS + hh) * QA_HD;
-                *reinterpret_cast<float4*>(dst + e0) = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-                *reinterpret_cast<float4*>(dst + e0 + 16) = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+    for (int b = 0; b < 8; b++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            float o4[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float v = acc[b][hf][i];
+                o4[i] = (v + row_from_above<4>(v)) * vinv;
             }
+            if (nq < G)
+                *reinterpret_cast<float4*>(ob + ((int64_t)wave * G + nq) * QA_HD + 32 * b + 16 * hf + 4 * gq) =
+                    make_float4(o4[0], o4[1], o4[2], o4[3]);
         }
-        __syncthreads();
-        for (int hh = 0; hh < HPASS; hh++) {
-            const int h = hb + hh;
-            float mx = -INFINITY;
+    __syncthreads();
+    for (int h = 0; h < G; h++) {
+        float mx = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < QA_WAVES; w++) mx = fmaxf(mx, sh.m[w][h]);
-            float L = 0.0f, O = 0.0f;
+        for (int w = 0; w < QA_WAVES; w++) mx = fmaxf(mx, sh.m[w][h]);
+        float L = 0.0f, O = 0.0f;
 #pragma unroll
-            for (int w = 0; w < QA_WAVES; w++) {
-                const float f = mx == -INFINITY ? 0.0f : exp2f(sh.m[w][h] - mx);
-                L = __builtin_fmaf(sh.l[w][h], f, L);
-                O = __builtin_fmaf(ob[((int64_t)w * HPASS + hh) * QA_HD + tid], f, O);
-            }
-            const int64_t prow = ch * a.n_q_heads + hq0 + h;
-            p.part_o[prow * QA_HD + tid] = O;
-            if (tid == 0) {
-                p.part_m[prow] = mx;
-                p.part_l[prow] = L;
-            }
+        for (int w = 0; w < QA_WAVES; w++) {
+            const float f = mx == -INFINITY ? 0.0f : exp2f(sh.m[w][h] - mx);
+            L = __builtin_fmaf(sh.l[w][h], f, L);
+            O = __builtin_fmaf(ob[((int64_t)w * G + h) * QA_HD + tid], f, O);
         }
-        __syncthreads();
+        const int64_t prow = ch * a.n_q_heads + hq0 + h;
+        p.part_o[prow * QA_HD + tid] = O;
+        if (tid == 0) {
+            p.part_m[prow] = mx;
+            p.part_l[prow] = L;
+        }
     }
 }
 
@@ -566,7 +682,7 @@ __global__ __launch_bounds__(256) void k_q4_merge(kvq_q4_attn_args a, Q4Plan p) 
 template <int G>
 hipError_t launch_attn_g(const kvq_q4_cache& c, const kvq_q4_attn_args& a, const Q4Plan& p, hipStream_t st) {
     const int64_t grid = p.items_per_xcd * QA_NXCD;
-    hipLaunchKernelGGL(k_q4_attn<G>, dim3((unsigned)grid), dim3(QA_WAVES * 64), 0, st, c, a, p);
+    hipLaunchKernelGGL(k_q4_attn_mx<G>, dim3((unsigned)grid), dim3(QA_WAVES * 64), 0, st, c, a, p);
     return hipGetLastError();
 }
 

@@ -49,11 +49,11 @@ constexpr int QA_TILE = 64;   // split granularity: QA_TILE * QA_WAVES positions
 constexpr int QA_HD = 256;    // head_dim
 constexpr int QA_RB = 144;    // bytes per head-row: 8 blocks of 18
 constexpr int QA_NXCD = 8;
-// Query heads per workgroup at most: larger groups split over workgroups that
-// read the same head-rows (neighbouring items, so from the same L2).  Eight
-// heads per workgroup fill all 256 registers and took 1.5 x the time of two
-// workgroups of four.
-constexpr int QA_GMAX = 4;
+// Query heads per workgroup at most: 16 heads per KV head split over two
+// workgroups that read the same head-rows (neighbouring items, so from the same
+// L2).  With 8 heads the value products use all 16 columns of the matrix-core
+// tile (two terms of p per head).
+constexpr int QA_GMAX = 8;
 constexpr float QA_LOG2E = 1.4426950408889634f;
 constexpr float QA_LN2 = 0.6931471805599453f;
 
@@ -99,7 +99,7 @@ Q4Plan q4_make_plan(const kvq_q4_cache& c, const kvq_q4_attn_args& a, void* ws, 
     };
     const int64_t rows_q = (int64_t)a.n_seqs * a.n_q_heads;
     p.chunk_prefix = (int64_t*)take(sizeof(int64_t) * (a.n_seqs + 1));
-    p.q_mx = (uint4*)take(sizeof(uint4) * (int64_t)a.n_seqs * c.n_kv_heads * p.sub * 8 * 64);
+    p.q_mx = (uint4*)take(sizeof(uint4) * (int64_t)a.n_seqs * c.n_kv_heads * p.sub * 2 * 8 * 64);
     p.q_inv = (float*)take(sizeof(float) * rows_q);
     p.part_m = (float*)take(sizeof(float) * p.max_chunks * a.n_q_heads);
     p.part_l = (float*)take(sizeof(float) * p.max_chunks * a.n_q_heads);
@@ -189,21 +189,23 @@ __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
 #pragma unroll
     for (int i = 0; i < 4; i++) x[i] *= sc;
     // The score products' B operands (v_mfma_f32_16x16x32_f16, one K = 32 step per block),
-    // x = H q / 16 * sm_scale * log2(e):
-    // x * qs (qs a power of two, max |x| qs in [2^14, 2^15)) as three fp16 terms, about
-    // 33 significant bits together.  Column n = h + 4 t holds term t of head h of the
-    // workgroup's 4; lane (g, n) holds k = 8 g + e, which is block element 4 g + e for
-    // e < 4 and 16 + 4 g + e - 4 for e >= 4 (the low and high nibbles of bytes 4 g ..
-    // 4 g + 3).  This lane's elements 4 (lane % 8) .. + 3 of block lane / 8 are
-    // k = 8 g + 4 hf + {0..3} with g = lane % 4, hf = (lane / 4) % 2.
+    // x = H q / 16 * sm_scale * log2(e): x * qs (qs a power of two, max |x| qs in
+    // [2^14, 2^15)) as three fp16 terms, about 33 significant bits together.  Up to 4 heads
+    // per workgroup: column h + 4 t of column tile 0 holds term t of head h; 8 heads:
+    // column h + 8 t of tile 0 holds terms 0 and 1, column h of tile 1 term 2.  Lane (g, n)
+    // holds k = 8 g + e, which is block element 4 g + e for e < 4 and 16 + 4 g + e - 4 for
+    // e >= 4 (the low and high nibbles of bytes 4 g .. 4 g + 3).  This lane's elements
+    // 4 (lane % 8) .. + 3 of block lane / 8 are k = 8 g + 4 hf + {0..3} with g = lane % 4,
+    // hf = (lane / 4) % 2.
     float qmax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
     qmax = wave_max(qmax);
     const float qs = q4_pow2_scale(qmax, 14);
     const int64_t sq = row / a.n_q_heads;
     const int hq = (int)(row - sq * a.n_q_heads), kv = hq / p.group, hl = hq - kv * p.group;
     const int part = hl / QA_GMAX, hh = hl % QA_GMAX;
+    const bool eight = p.group >= 8;
     const int64_t nkv = a.n_q_heads / p.group;
-    uint2* qm = reinterpret_cast<uint2*>(p.q_mx + (((sq * nkv + kv) * p.sub + part) * 8 + (lane >> 3)) * 64);
+    uint2* qm = reinterpret_cast<uint2*>(p.q_mx + (((sq * nkv + kv) * p.sub + part) * 16 + (lane >> 3)) * 64);
     const int gk = lane & 3, hf = (lane >> 2) & 1;
     float r[4];
 #pragma unroll
@@ -216,7 +218,9 @@ __global__ __launch_bounds__(256) void k_q4_prep(kvq_q4_attn_args a, Q4Plan p) {
             tv[i] = (float)(_Float16)r[i];  // round to nearest even
             r[i] -= tv[i];                  // exact
         }
-        qm[2 * (16 * gk + hh + 4 * t) + hf] =
+        const int tile = eight && t == 2 ? 1 : 0;
+        const int colm = eight ? hh + 8 * (t & 1) * (t < 2 ? 1 : 0) : hh + 4 * t;
+        qm[tile * (8 * 64 * 2) + 2 * (16 * gk + colm) + hf] =
             make_uint2(f32_to_f16_rne(tv[0]) | (f32_to_f16_rne(tv[1]) << 16),
                        f32_to_f16_rne(tv[2]) | (f32_to_f16_rne(tv[3]) << 16));
     }
@@ -328,15 +332,17 @@ __device__ __forceinline__ float q4_wave_max(float v, int lane) {
     return fmaxf(v, xor_lane<32>(v, lane));
 }
 
+template <int G>
 struct Q4MxShared {
+    uint4 qmx[G == 8 ? 2 : 1][8][64];     // 8 heads: the score operands (in registers for fewer)
     uint8_t k[QA_WAVES][QM_TILE][QA_RB];  // the tile's K head-rows, regrouped as stage_v_row does
     uint8_t v[QA_WAVES][QM_TILE][QA_RB];  // the V head-rows, the same
     uint16_t dk[QA_WAVES][8][QM_TILE];    // K block scales (binary16) by block, then position
     uint16_t dv[QA_WAVES][8][QM_TILE];    // V block scales times vs (binary16), the same
-    float sc[QA_WAVES][QM_TILE][4];       // scores (log2 units) by position, then head
-    float pr[QA_WAVES][4][QM_TILE];       // probabilities by head, then position
-    float m[QA_WAVES][4];
-    float l[QA_WAVES][4];
+    float sc[QA_WAVES][QM_TILE][8];       // scores (log2 units) by position, then head
+    float pr[QA_WAVES][8][QM_TILE];       // probabilities by head, then position
+    float m[QA_WAVES][8];
+    float l[QA_WAVES][8];
 };
 
 template <int B>
@@ -351,7 +357,7 @@ __device__ __forceinline__ float row_dabs(const uint32_t (&r)[36]) {
 
 template <int G>
 __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c, kvq_q4_attn_args a, Q4Plan p) {
-    __shared__ __align__(16) Q4MxShared sh;
+    __shared__ __align__(16) Q4MxShared<G> sh;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t n_items = p.max_chunks * c.n_kv_heads * p.sub;
@@ -377,20 +383,36 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
     const int hq0 = g * p.group + part * G;
     const int64_t qrow0 = (int64_t)s * a.n_q_heads + hq0;
 
-    // MFMA lane (gq, nq); the score operands of this workgroup's heads (columns of absent
-    // heads and of t = 3 are zero) and 1 / qs of head nq
-    const int gq = lane >> 4, nq = lane & 15;
-    uint4 qb[8];
+    // MFMA lane (gq, nq).  Column nq is (head nq % HS, term nq / HS); with 8 heads the
+    // third query term is a second column tile.  The score operands of this workgroup's
+    // heads (columns of absent heads and terms are zero) and 1 / qs of head nq % HS.
+    constexpr int HS = G == 8 ? 8 : 4;
+    constexpr int KT = G == 8 ? 2 : 1;
+    const int gq = lane >> 4, nq = lane & 15, hn = nq % HS;
+    // (8 heads: 16 operand registers per lane would not fit beside the rest; they go to
+    // LDS and are read there per step)
+    constexpr int KR = G == 8 ? 1 : 8;
+    uint4 qb[KR];
     {
-        const bool col = nq < 12 && (nq & 3) < G;
-        const uint4* qsrc = p.q_mx + (((int64_t)s * c.n_kv_heads + g) * p.sub + part) * (8 * 64) + lane;
+        const uint4* qsrc = p.q_mx + (((int64_t)s * c.n_kv_heads + g) * p.sub + part) * (16 * 64);
+        if constexpr (G == 8) {
 #pragma unroll
-        for (int b = 0; b < 8; b++) {
-            const uint4 v = qsrc[b * 64];
-            qb[b] = col ? v : make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < 4; i++) {
+                const int e = tid + 256 * i;  // (tile, block, lane)
+                const uint4 v = qsrc[e];
+                (&sh.qmx[0][0][0])[e] = ((e >> 9) == 0 || (e & 15) < 8) ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
+            __syncthreads();
+        } else {
+            const bool col = nq < 12 && hn < G;
+#pragma unroll
+            for (int b = 0; b < 8; b++) {
+                const uint4 v = qsrc[b * 64 + lane];
+                qb[b] = col ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
         }
     }
-    const float qinv = p.q_inv[qrow0 + min(nq & 3, G - 1)];
+    const float qinv = p.q_inv[qrow0 + min(hn, G - 1)];
 
     const int64_t quarter = ((r1 - r0 + QA_WAVES - 1) / QA_WAVES + QM_TILE - 1) / QM_TILE * QM_TILE;
     const int64_t w0 = r0 + wave * quarter;
@@ -472,23 +494,32 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
         // ---- scores: positions 16 P + 4 gq + i, column nq
 #pragma unroll
         for (int P = 0; P < 2; P++) {
-            float sp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float sp[KT][4];
+#pragma unroll
+            for (int kt = 0; kt < KT; kt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) sp[kt][i] = 0.0f;
 #pragma unroll
             for (int b = 0; b < 8; b++) {
                 const uint32_t x = *reinterpret_cast<const uint32_t*>(&sh.k[wave][16 * P + nq][16 * b + 4 * gq]);
-                const q4f4_t cb = q4_mfma(q4_nib_f16(x & 0x0F0F0F0Fu, (x >> 4) & 0x0F0F0F0Fu), qb[b], zero4);
+                const uint4 av = q4_nib_f16(x & 0x0F0F0F0Fu, (x >> 4) & 0x0F0F0F0Fu);
                 const uint2 dd = *reinterpret_cast<const uint2*>(&sh.dk[wave][b][16 * P + 4 * gq]);
-                sp[0] = __builtin_fmaf(half_bits_to_f32(dd.x), cb[0], sp[0]);
-                sp[1] = __builtin_fmaf(half_bits_to_f32(dd.x >> 16), cb[1], sp[1]);
-                sp[2] = __builtin_fmaf(half_bits_to_f32(dd.y), cb[2], sp[2]);
-                sp[3] = __builtin_fmaf(half_bits_to_f32(dd.y >> 16), cb[3], sp[3]);
+                const float d4[4] = {half_bits_to_f32(dd.x), half_bits_to_f32(dd.x >> 16), half_bits_to_f32(dd.y),
+                                     half_bits_to_f32(dd.y >> 16)};
+#pragma unroll
+                for (int kt = 0; kt < KT; kt++) {
+                    const q4f4_t cb = q4_mfma(av, G == 8 ? sh.qmx[kt][b][lane] : qb[b % KR], zero4);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) sp[kt][i] = __builtin_fmaf(d4[i], cb[i], sp[kt][i]);
+                }
             }
-            // the three terms of column h + 4 t: lanes nq < 4 get head nq's sum
+            // the three terms of each head summed: lanes nq < HS get head nq's score
             float tp[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const float v = sp[i];
-                tp[i] = ((v + row_from_above<4>(v)) + row_from_above<8>(v)) * qinv;
+                const float v = sp[0][i];
+                if constexpr (G == 8) tp[i] = ((v + row_from_above<8>(v)) + sp[KT - 1][i]) * qinv;
+                else tp[i] = ((v + row_from_above<4>(v)) + row_from_above<8>(v)) * qinv;
             }
             if (nq < G) {
 #pragma unroll
@@ -497,8 +528,15 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
         }
 
         // ---- online softmax per head, lane = position (lanes 0-31)
-        const float4 s4 = *reinterpret_cast<const float4*>(&sh.sc[wave][pl][0]);
-        const float sl[4] = {s4.x, s4.y, s4.z, s4.w};
+        float sl[8];
+        {
+            const float4 s4 = *reinterpret_cast<const float4*>(&sh.sc[wave][pl][0]);
+            sl[0] = s4.x; sl[1] = s4.y; sl[2] = s4.z; sl[3] = s4.w;
+            if constexpr (G == 8) {
+                const float4 s8 = *reinterpret_cast<const float4*>(&sh.sc[wave][pl][4]);
+                sl[4] = s8.x; sl[5] = s8.y; sl[6] = s8.z; sl[7] = s8.w;
+            }
+        }
         float alpha[G];
 #pragma unroll
         for (int h = 0; h < G; h++) {
@@ -522,7 +560,7 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
             if (!same) {
                 float f = alpha[0];
 #pragma unroll
-                for (int h = 1; h < G; h++) f = (nq & 3) == h ? alpha[h] : f;
+                for (int h = 1; h < G; h++) f = hn == h ? alpha[h] : f;
                 f *= vs_new / vs;  // powers of two: exact
 #pragma unroll
                 for (int b = 0; b < 8; b++) {
@@ -534,13 +572,13 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
         }
 
         // ---- values over the tile's 32 positions
-        uint4 pb;  // B: term nq / 4 of p of head nq % 4 at positions 8 gq + e
+        uint4 pb;  // B: term nq / HS of p of head nq % HS at positions 8 gq + e
         {
-            const int hs = min(nq & 3, G - 1);
+            const int hs = min(hn, G - 1);
             const float4 pa = *reinterpret_cast<const float4*>(&sh.pr[wave][hs][8 * gq]);
             const float4 pc = *reinterpret_cast<const float4*>(&sh.pr[wave][hs][8 * gq + 4]);
             const float pe[8] = {pa.x, pa.y, pa.z, pa.w, pc.x, pc.y, pc.z, pc.w};
-            const bool second = nq >= 4;
+            const bool second = nq >= HS;
             uint32_t w[4];
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -548,7 +586,7 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
                 const float a0 = (float)(_Float16)x0, a1 = (float)(_Float16)x1;
                 w[j] = f32_to_f16_rne(second ? x0 - a0 : a0) | (f32_to_f16_rne(second ? x1 - a1 : a1) << 16);
             }
-            const bool col = nq < 8 && (nq & 3) < G;
+            const bool col = nq < 2 * HS && hn < G;
             pb = col ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0u, 0u, 0u, 0u);
         }
         const int prow = 8 * gq + (nq >> 1);  // the row this lane's address names
@@ -573,7 +611,7 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
         }
     }
 
-    // ---- the wave's (m, l, O): O = acc / vs, the two terms of column h + 4 t added
+    // ---- the wave's (m, l, O): O = acc / vs, the two terms of each head added
 #pragma unroll
     for (int h = 0; h < G; h++) {
         const float l = wave_sum(lp[h]);
@@ -585,7 +623,7 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
     const float vinv = 1.0f / vs;  // exact
     __syncthreads();  // every wave is past its last read of the staged rows
     float* ob = reinterpret_cast<float*>(&sh.k[0][0][0]);  // [QA_WAVES][G][256]
-    static_assert(sizeof(sh.k) + sizeof(sh.v) >= sizeof(float) * QA_WAVES * 4 * QA_HD, "exchange buffer");
+    static_assert(sizeof(sh.k) + sizeof(sh.v) >= sizeof(float) * QA_WAVES * G * QA_HD, "exchange buffer");
 #pragma unroll
     for (int b = 0; b < 8; b++)
 #pragma unroll
@@ -594,7 +632,7 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const float v = acc[b][hf][i];
-                o4[i] = (v + row_from_above<4>(v)) * vinv;
+                o4[i] = (v + row_from_above<HS>(v)) * vinv;
             }
             if (nq < G)
                 *reinterpret_cast<float4*>(ob + ((int64_t)wave * G + nq) * QA_HD + 32 * b + 16 * hf + 4 * gq) =
@@ -703,7 +741,7 @@ hipError_t launch_decode_attn_q4_0(const kvq_q4_cache& c, const kvq_q4_attn_args
     switch (p.group) {
         case 1: e = launch_attn_g<1>(c, a, p, st); break;
         case 2: e = launch_attn_g<2>(c, a, p, st); break;
-        case 4:
+        case 4: e = launch_attn_g<4>(c, a, p, st); break;
         case 8:
         case 16: e = launch_attn_g<QA_GMAX>(c, a, p, st); break;
         default: return hipErrorInvalidValue;

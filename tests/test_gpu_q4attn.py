@@ -216,3 +216,41 @@ def test_q4_attn_long_flat_sequence(split_rows):
     ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, table, page, off, q, SM)
     out, lse = _run(kp, vp, table, off, q, split_rows=split_rows)
     _check(out, lse, ref_o, ref_l, f"long flat split {split_rows}")
+
+
+def test_q4_attn_peaked_scores_and_wide_value_scales():
+    """A peaked softmax (the query times 8) over value rows whose binary16 block
+    scales span 2^-20 .. 2^10 (subnormal ones included, both signs) and jump
+    from one 32-position stretch to the next, K scales 2^-3 .. 2^3: the three
+    query terms of the scores, the two exact terms of the value products and
+    their per-tile power-of-two range must keep the fp32 result.  Two KV heads,
+    8 query heads each (one workgroup of 8 heads), and 4 each."""
+    _say("q4 attn peaked scores, wide value scales")
+    rng = np.random.default_rng(1016)
+    n, page, n_kv = 4096, 64, 2
+    table = rng.permutation(n // page).astype(np.int32)[None, :]
+    kp = rng.integers(0, 256, (n, n_kv, 144), dtype=np.uint8)
+    vp = rng.integers(0, 256, (n, n_kv, 144), dtype=np.uint8)
+    stretch = np.repeat(rng.uniform(-20.0, 10.0, n // 32), 32)[:, None, None]  # per 32 positions
+    for pool, lo, hi, base in ((kp, -3.0, 3.0, 0.0), (vp, -4.0, 0.0, stretch)):
+        e = base + rng.uniform(lo, hi, (n, n_kv, 8))
+        d = (np.exp2(e) * rng.choice([-1.0, 1.0], (n, n_kv, 8))).astype(np.float16)
+        b = d.view(np.uint16)
+        for blk in range(8):
+            pool[:, :, 18 * blk] = (b[:, :, blk] & 0xFF).astype(np.uint8)
+            pool[:, :, 18 * blk + 1] = (b[:, :, blk] >> 8).astype(np.uint8)
+    off = np.array([0, n], np.int64)
+    for group in (8, 4):
+        q = (workloads.q4_queries(1017, 1, n_q_heads=n_kv * group) * 8.0).astype(np.float32)
+        ref_o, ref_l = oracle.decode_attn_q4_0(kp, vp, table, page, off, q, SM)
+        out, lse = _run(kp, vp, table, off, q)
+        assert np.all(np.isfinite(out))
+        # fp32 evaluation of scores up to S (natural-log units) moves the weights by about S 2^-24
+        S = float(np.max(np.abs(ref_l)))
+        tol = max(TOL, 4.0 * S * 2.0 ** -24)
+        _say(f"  group {group}: max |lse| {S:.1f}, bar {tol:.2e}")
+        e = np.max(np.abs(out - ref_o)) / np.max(np.abs(ref_o))
+        d = np.max(np.abs(lse - ref_l) / np.maximum(1.0, np.abs(ref_l)))
+        _say(f"  group {group}: max|err|/max|ref| {e:.2e}, lse {d:.2e}")
+        assert e <= tol, f"group {group}: rel err {e:.3e}"
+        assert d <= tol, f"group {group}: lse err {d:.3e}"

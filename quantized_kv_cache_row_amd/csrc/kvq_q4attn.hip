@@ -334,15 +334,16 @@ __device__ __forceinline__ float q4_wave_max(float v, int lane) {
 
 template <int G>
 struct Q4MxShared {
-    uint4 qmx[G == 8 ? 2 : 1][8][64];     // 8 heads: the score operands (in registers for fewer)
+    static constexpr int NH = G == 8 ? 8 : 4;
+    uint4 qmx[G == 8 ? 2 : 1][8][64];     // the score operands
     uint8_t k[QA_WAVES][QM_TILE][QA_RB];  // the tile's K head-rows, regrouped as stage_v_row does
     uint8_t v[QA_WAVES][QM_TILE][QA_RB];  // the V head-rows, the same
     uint16_t dk[QA_WAVES][8][QM_TILE];    // K block scales (binary16) by block, then position
     uint16_t dv[QA_WAVES][8][QM_TILE];    // V block scales times vs (binary16), the same
-    float sc[QA_WAVES][QM_TILE][8];       // scores (log2 units) by position, then head
-    float pr[QA_WAVES][8][QM_TILE];       // probabilities by head, then position
-    float m[QA_WAVES][8];
-    float l[QA_WAVES][8];
+    float sc[QA_WAVES][QM_TILE][NH];      // scores (log2 units) by position, then head
+    float pr[QA_WAVES][NH][QM_TILE];      // probabilities by head, then position
+    float m[QA_WAVES][NH];
+    float l[QA_WAVES][NH];
 };
 
 template <int B>
@@ -356,7 +357,7 @@ __device__ __forceinline__ float row_dabs(const uint32_t (&r)[36]) {
 }
 
 template <int G>
-__global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c, kvq_q4_attn_args a, Q4Plan p) {
+__global__ __launch_bounds__(QA_WAVES * 64, G == 8 ? 2 : 3) void k_q4_attn_mx(kvq_q4_cache c, kvq_q4_attn_args a, Q4Plan p) {
     __shared__ __align__(16) Q4MxShared<G> sh;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -389,28 +390,18 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
     constexpr int HS = G == 8 ? 8 : 4;
     constexpr int KT = G == 8 ? 2 : 1;
     const int gq = lane >> 4, nq = lane & 15, hn = nq % HS;
-    // (8 heads: 16 operand registers per lane would not fit beside the rest; they go to
-    // LDS and are read there per step)
-    constexpr int KR = G == 8 ? 1 : 8;
-    uint4 qb[KR];
+    // (in LDS and read there per step: registers are the occupancy limit)
     {
         const uint4* qsrc = p.q_mx + (((int64_t)s * c.n_kv_heads + g) * p.sub + part) * (16 * 64);
-        if constexpr (G == 8) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int e = tid + 256 * i;  // (tile, block, lane)
-                const uint4 v = qsrc[e];
-                (&sh.qmx[0][0][0])[e] = ((e >> 9) == 0 || (e & 15) < 8) ? v : make_uint4(0u, 0u, 0u, 0u);
-            }
-            __syncthreads();
-        } else {
-            const bool col = nq < 12 && hn < G;
-#pragma unroll
-            for (int b = 0; b < 8; b++) {
-                const uint4 v = qsrc[b * 64 + lane];
-                qb[b] = col ? v : make_uint4(0u, 0u, 0u, 0u);
-            }
+        for (int i = 0; i < 2 * KT; i++) {
+            const int e = tid + 256 * i;  // (tile, block, lane)
+            const int en = e & 15;
+            const bool col = G == 8 ? ((e >> 9) == 0 || en < 8) : (en < 12 && en % 4 < G);
+            const uint4 v = qsrc[e];
+            (&sh.qmx[0][0][0])[e] = col ? v : make_uint4(0u, 0u, 0u, 0u);
         }
+        __syncthreads();
     }
     const float qinv = p.q_inv[qrow0 + min(hn, G - 1)];
 
@@ -508,7 +499,7 @@ __global__ __launch_bounds__(QA_WAVES * 64, 2) void k_q4_attn_mx(kvq_q4_cache c,
                                      half_bits_to_f32(dd.y >> 16)};
 #pragma unroll
                 for (int kt = 0; kt < KT; kt++) {
-                    const q4f4_t cb = q4_mfma(av, G == 8 ? sh.qmx[kt][b][lane] : qb[b % KR], zero4);
+                    const q4f4_t cb = q4_mfma(av, sh.qmx[kt][b][lane], zero4);
 #pragma unroll
                     for (int i = 0; i < 4; i++) sp[kt][i] = __builtin_fmaf(d4[i], cb[i], sp[kt][i]);
                 }

@@ -340,9 +340,12 @@ int kvq_decode_attn_sparse(const kvq_attn_args* a, const int64_t* row_index, int
  * is negative or whose cell is past n_cells take no part.  A sequence with no
  * position gets out = 0 and lse = -Inf.  The sigmoid gate that follows in the
  * pages' model is the caller's.
- * Arithmetic: fp32 throughout (scores as d * (sum nibble * q~ - 8 * sum q~)
- * per block, sm_scale * log2(e) folded into q~, exp2); tolerance against an
- * fp64 evaluation on the same pool bytes: max|err| / max|ref| <= 1e-5. */
+ * Arithmetic: fp32 accuracy on the matrix cores -- exact fp16 products of the
+ * codes minus 8 with three fp16 terms of q~ (times a power of two) summed in
+ * fp32 and multiplied by d in fp32; the value sum from (nibble - 8) * d as two
+ * exact fp16 terms times p as two fp16 terms; sm_scale * log2(e) folded into
+ * q~, exp2.  Tolerance against an fp64 evaluation on the same pool bytes:
+ * max|err| / max|ref| <= 1e-5. */
 typedef struct kvq_q4_attn_args {
     int32_t n_seqs;             /* >= 1                                              */
     int32_t n_q_heads;          /* n_kv_heads * G with G in {1, 2, 4, 8, 16}          */

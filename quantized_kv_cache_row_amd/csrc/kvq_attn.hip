@@ -1945,32 +1945,41 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
     float4 o[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) o[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int64_t cb = c0; cb < c1; cb += U) {
-        float mc[U], lc[U], sk[U];
-        uint2 vh[U][NB];
-        const uint2* vb = src + cb * cstride;
-        const float* mb = p.part_m + cb * nh + hc;
-        const float* lb = p.part_l + cb * nh + hc;
-        const float* sb = ssrc + cb * 4 * nh;
+    // batches of U slots in two register sets, each batch's loads issued before the one
+    // ahead of it is used (a long sequence's slots then cost about one load latency, not one
+    // per batch).  The loads are unconditional, so that the waits are the same on every path:
+    // a batch past the end reads slot c1 - 1 again and is masked.
+    struct Batch {
+        float m[U], l[U], s[U];
+        uint2 v[U][NB];
+    };
+    Batch A, B;
+    auto load_batch = [&](Batch& t, int64_t cb) __attribute__((always_inline)) {
+        const int64_t base = min(cb, c1 - 1);
+        const uint2* vb = src + base * cstride;
+        const float* mb = p.part_m + base * nh + hc;
+        const float* lb = p.part_l + base * nh + hc;
+        const float* sb = ssrc + base * 4 * nh;
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t du = cb + u < c1 ? u : 0;  // a slot past the end reads slot cb
-            mc[u] = mb[du * nh];
-            lc[u] = lb[du * nh];
-            sk[u] = sb[du * 4 * nh];
+            const int64_t du = base + u < c1 ? u : 0;  // a slot past the end reads slot base
+            t.m[u] = mb[du * nh];
+            t.l[u] = lb[du * nh];
+            t.s[u] = sb[du * 4 * nh];
 #pragma unroll
-            for (int b = 0; b < NB; b++) vh[u][b] = ld_nt(vb + du * cstride + b * 64);
+            for (int b = 0; b < NB; b++) t.v[u][b] = ld_nt(vb + du * cstride + b * 64);
         }
-        // (every load above is issued before any is used: a slot past the end is masked here)
+    };
+    auto use_batch = [&](Batch& t, int64_t cb) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            if (cb + u >= c1) mc[u] = -INFINITY;
+            const float mu = cb + u < c1 ? t.m[u] : -INFINITY;  // a slot past the end is masked
             float4 v[NB];
 #pragma unroll
-            for (int b = 0; b < NB; b++) v[b] = f16x4_scaled(vh[u][b], sk[u]);
-            const float mn = fmaxf(m, mc[u]);
+            for (int b = 0; b < NB; b++) v[b] = f16x4_scaled(t.v[u][b], t.s[u]);
+            const float mn = fmaxf(m, mu);
             const float sc = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
-            const float w = mc[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mc[u] - mn);
+            const float w = mu == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mu - mn);
 #pragma unroll
             for (int b = 0; b < NB; b++) {
                 o[b].x = o[b].x * sc + w * v[b].x;
@@ -1978,8 +1987,19 @@ __global__ __launch_bounds__(64) void k_merge_f8_few(kvq_attn_args a, Plan p) {
                 o[b].z = o[b].z * sc + w * v[b].z;
                 o[b].w = o[b].w * sc + w * v[b].w;
             }
-            lsum = lsum * sc + w * lc[u];
+            lsum = lsum * sc + w * t.l[u];
             m = mn;
+        }
+    };
+    if (c0 < c1) {
+        load_batch(A, c0);
+        for (int64_t cb = c0;; cb += 2 * U) {
+            load_batch(B, cb + U);
+            use_batch(A, cb);
+            if (cb + U >= c1) break;  // (wave-uniform)
+            load_batch(A, cb + 2 * U);
+            use_batch(B, cb + U);
+            if (cb + 2 * U >= c1) break;
         }
     }
     if (head >= a.n_heads) return;

@@ -601,6 +601,23 @@ __device__ __forceinline__ void dma_lds_b32_at(const void* vaddr, uint32_t lds_b
     asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" : : "v"(vaddr), "{m0}"(lds_base) : "memory");
 }
 // max over the wave by lane swaps (no LDS round trips)
+// (sequence, head) of a query-preparation row s * hp + head, wave-uniform: no
+// division for one sequence, a 32-bit one below 2^32 rows (a 64-bit division
+// is a long dependent instruction chain on the GPU).
+__device__ __forceinline__ void seq_head_of(int64_t row, int n_seqs, int64_t hp, int& s, int& hd) {
+    if (n_seqs == 1) {
+        s = 0;
+        hd = (int)row;
+    } else if ((uint64_t)n_seqs * (uint64_t)hp <= 0xFFFFFFFFull) {
+        const uint32_t q = (uint32_t)row / (uint32_t)hp;
+        s = (int)q;
+        hd = (int)((uint32_t)row - q * (uint32_t)hp);
+    } else {
+        s = (int)(row / hp);
+        hd = (int)(row % hp);
+    }
+}
+
 __device__ __forceinline__ float wave_max_swap(float v, int lane) {
     v = fmaxf(v, xor_lane<32>(v, lane));
     v = fmaxf(v, xor_lane<16>(v, lane));
@@ -746,7 +763,8 @@ __global__ __launch_bounds__(256) void k_qprep_fp8(kvq_attn_args a, Plan p, NewR
     // wave-uniform (scalar) row and its division
     const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = s * heads_padded + head
     if (row >= prep_rows) return;
-    const int s = (int)(row / p.heads_padded), hd = (int)(row % p.heads_padded);
+    int s, hd;
+    seq_head_of(row, a.n_seqs, p.heads_padded, s, hd);
     const bool hv = hd < a.n_heads;
     const int64_t qrow = (int64_t)s * a.n_heads + min(hd, a.n_heads - 1);  // absent heads: a zero query
     const float4 x0 = *reinterpret_cast<const float4*>(a.q_lat + qrow * DL + 8 * lane);
@@ -1245,7 +1263,8 @@ __global__ __launch_bounds__(256) void k_qprep_tq4(kvq_attn_args a, Plan p) {
     // wave-uniform (scalar) row and its division
     const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // = s * heads_padded + h
     if (row >= (int64_t)a.n_seqs * p.heads_padded) return;
-    const int s = (int)(row / p.heads_padded), h = (int)(row % p.heads_padded);
+    int s, h;
+    seq_head_of(row, a.n_seqs, p.heads_padded, s, h);
     const bool valid = h < a.n_heads;
     // unconditional loads (a clamped head; a guarded load would wait for every load in flight)
     const float* src = a.q_lat + ((int64_t)s * a.n_heads + min(h, a.n_heads - 1)) * DL + 8 * lane;

@@ -99,11 +99,8 @@ __device__ __forceinline__ uint32_t shfl_xor_u(uint32_t v, int m) {
     return (uint32_t)__shfl_xor((int)v, m, KVQ_WAVE);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
-    return v;
-}
+// max over the wave (defined below, after the lane-exchange helpers it uses)
+__device__ __forceinline__ float wave_max(float v);
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -211,6 +208,18 @@ __device__ __forceinline__ float xor_lane(float v, int lane) {
         r = (int)((lane & 32) ? p[0] : p[1]);
     }
     return __int_as_float(r);
+}
+
+// Max over the wave by lane swaps and DPP moves (no LDS crossbar round trips:
+// six short dependent steps).  The max is exact, so the order does not matter.
+__device__ __forceinline__ float wave_max(float v) {
+    const int lane = (int)__lane_id();
+    v = fmaxf(v, xor_lane<32>(v, lane));
+    v = fmaxf(v, xor_lane<16>(v, lane));
+    v = fmaxf(v, xor_lane<8>(v, lane));
+    v = fmaxf(v, xor_lane<4>(v, lane));
+    v = fmaxf(v, xor_lane<2>(v, lane));
+    return fmaxf(v, xor_lane<1>(v, lane));
 }
 
 // FWHT stage with partner lane ^ M (as fwht_xlane, M a compile-time constant).

@@ -348,14 +348,16 @@ def measure_other_rows(torch, kvq, workloads, x_kv8, only=None):
     for bits, qm in ((3, kvq.KVQ_QMODE_TQ3), (6, kvq.KVQ_QMODE_TQ6)):
         if not want(f"tq{bits}"):
             continue
-        # the 3- and 6-bit tiers: the 8192-row encode pass, then the T = 32768, 128-head decode
-        n = 8192
-        x8k = torch.from_numpy(workloads.tq4_encode_rows(n)).to(dev)
-        ct = torch.empty((n, 64 * bits), dtype=torch.uint8, device=dev)
-        rt = torch.empty(n, dtype=torch.float32, device=dev)
-        ms = time_graph(torch, lambda b=bits: kvq.kvq_encode_tq(b, x8k, mask, ct, rt), 20)
-        hbm(f"tq{bits}_encode_{n}", n * (2048 + 64 * bits + 4) + 64, ms, {"rows/s": n / (ms / 1000.0)})
-        del x8k, ct, rt
+        # the 3- and 6-bit tiers: the 8192-row encode pass and a 262144-row asymptote, then
+        # the T = 32768, 128-head decode
+        for n in (8192, 262144):
+            xe = (torch.from_numpy(workloads.tq4_encode_rows(n)).to(dev) if n == 8192
+                  else gpu_latents(torch, n, 5))
+            ct = torch.empty((n, 64 * bits), dtype=torch.uint8, device=dev)
+            rt = torch.empty(n, dtype=torch.float32, device=dev)
+            ms = time_graph(torch, lambda b=bits, xe=xe, ct=ct, rt=rt: kvq.kvq_encode_tq(b, xe, mask, ct, rt), 20)
+            hbm(f"tq{bits}_encode_{n}", n * (2048 + 64 * bits + 4) + 64, ms, {"rows/s": n / (ms / 1000.0)})
+            del xe, ct, rt
         decode(f"tq{bits}_decode_T32768_H128", qm, x_kv8, [x_kv8.shape[0]], 128, 1002, 16)
         torch.cuda.empty_cache()
     if want("ragged"):

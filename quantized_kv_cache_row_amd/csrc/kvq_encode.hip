@@ -272,12 +272,39 @@ constexpr int D512_ROWS = 4;                // rows per wave
 constexpr float D512_CELL_SCALE = 3.35f;    // a above; any a in (3.18, 3.53) separates the thresholds
 constexpr int64_t D512_MAX_WGS = 1 << 24;   // grid cap; the kernel strides over the rest
 
-__global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const float* __restrict__ x,
-                                                                          int64_t n_rows,
-                                                                          const uint8_t* __restrict__ sign_mask,
-                                                                          uint8_t* __restrict__ codes,
-                                                                          float* __restrict__ radii) {
+//  - BITS = 3 and 6 (k_encode_tq_d512<3/6>) share the load, radius, signs and
+//    transform, so their values are the general kernel's bit for bit; the
+//    bucketing is the general kernel's cell table, and the codes go through a
+//    per-wave LDS row: lane q holds the indices of elements 4 q + 64 k + j, for
+//    each k a 24-bit piece (6 bits: its own four, at byte 3 q + 48 k; 3 bits:
+//    an even lane's four and its odd partner's, at byte 3 (q / 2) + 24 k),
+//    written as a 16-bit and an 8-bit LDS store, then read back as 24 (12)
+//    contiguous bytes per lane and stored with 8-byte (4-byte) stores.
+template <int BITS>
+__global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq_d512(const float* __restrict__ x,
+                                                                         int64_t n_rows,
+                                                                         const uint8_t* __restrict__ sign_mask,
+                                                                         uint8_t* __restrict__ codes,
+                                                                         float* __restrict__ radii) {
     constexpr int D = 512;
+    constexpr int NL = 1 << BITS;  // levels
+    constexpr int NC = BITS == 3 ? KVQ_TQ3_CELLS : BITS == 6 ? KVQ_TQ6_CELLS : 1;  // cells
+    constexpr float CELL_A = BITS == 3 ? KVQ_TQ3_CELL_A : BITS == 6 ? KVQ_TQ6_CELL_A : 0.0f;
+    constexpr float CELL_OFF = BITS == 3 ? KVQ_TQ3_CELL_OFF : BITS == 6 ? KVQ_TQ6_CELL_OFF : 0.0f;
+    constexpr int RB = D * BITS / 8;  // code bytes per row
+    static_assert(NC <= ENC_WAVES * KVQ_WAVE, "one cell entry per thread");
+    __shared__ float th_s[NL];
+    __shared__ uint2 cell_s[NC];                                       // (bits of t_c, c)
+    __shared__ __align__(16) uint8_t row_s[ENC_WAVES][D512_ROWS][BITS == 4 ? 16 : RB];  // BITS 3, 6
+    if constexpr (BITS != 4) {
+        const int t = threadIdx.x;
+        if (t < NL - 1) th_s[t] = u2f(BITS == 3 ? c_tq3_thresh[t] : c_tq6_thresh[t]);
+        if (t < NC) {
+            const uint32_t c = BITS == 3 ? (uint32_t)t : (uint32_t)c_tq6_cell[t];
+            cell_s[t] = make_uint2(BITS == 3 ? c_tq3_thresh[c] : c_tq6_thresh[c], c);
+        }
+        __syncthreads();
+    }
     typedef float f4v __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & (KVQ_WAVE - 1);
     const int slot = lane >> 4, u = lane & 15;
@@ -369,6 +396,87 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq4_d512(const 
                     v[i] = a + b;
                     v[i + h] = a - b;
                 }
+        if constexpr (BITS != 4) {
+            // lane q holds elements p = j + 4 q + 64 k (v[4 k + j]); cells as in k_encode_tq
+            const bool redo = !(r2 <= 3.40282347e38f);
+            const float inv_a = CELL_A * __builtin_amdgcn_rcpf(rad);  // +inf for a zero radius
+            uint32_t V[8];  // the indices of elements 4 q + 64 k + j, BITS j bits up, for each k
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                V[k] = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float w = v[4 * k + j];
+                    // v_med3 returns the smaller bound or NaN for a NaN input; v_cvt_u32_f32,
+                    // written out, turns NaN into cell 0
+                    const float cf = __builtin_amdgcn_fmed3f(__builtin_fmaf(w, inv_a, CELL_OFF), 0.0f, NC - 0.5f);
+                    uint32_t ci;
+                    asm("v_cvt_u32_f32 %0, %1" : "=v"(ci) : "v"(cf));
+                    const uint2 e = cell_s[ci];
+                    V[k] |= (e.y + ((w > u2f(e.x) * rad) ? 1u : 0u)) << (BITS * j);
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(redo) != 0 && redo) {
+                asm volatile("" ::: "memory");  // not evaluated speculatively
+#pragma unroll
+                for (int k = 0; k < 8; k++) {
+                    V[k] = 0u;
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float w = v[4 * k + j];
+                        uint32_t idx = 0;
+#pragma unroll
+                        for (int st = NL / 2; st >= 1; st >>= 1) idx += (w > th_s[idx + st - 1] * rad) ? st : 0;
+                        V[k] |= idx << (BITS * j);
+                    }
+                }
+            }
+            // the row's code bytes in LDS (this wave's own rows: its LDS operations run in order)
+            uint8_t* rs = &row_s[threadIdx.x >> 6][slot][0];
+            const bool writer = BITS == 6 || !qodd;
+            uint32_t off = BITS == 6 ? 3u * (uint32_t)q : 3u * (uint32_t)(q >> 1);
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                uint32_t w24 = V[k];
+                if constexpr (BITS == 3)  // the odd partner's 12 bits above the even lane's
+                    w24 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)V[k], DPP_XOR1, 0xF, 0xF, false) << 12;
+                const uint32_t o = off + (uint32_t)(k * (RB / 8));
+                if (writer) {
+                    if (o & 1u) {
+                        rs[o] = (uint8_t)w24;
+                        *reinterpret_cast<uint16_t*>(rs + o + 1) = (uint16_t)(w24 >> 8);
+                    } else {
+                        *reinterpret_cast<uint16_t*>(rs + o) = (uint16_t)w24;
+                        rs[o + 2] = (uint8_t)(w24 >> 16);
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const int64_t srow = min(row, n_rows - 1);  // a slot past the end rewrites the last row
+            if constexpr (BITS == 6) {  // lane u: bytes 24 u .. 24 u + 23
+                const uint2* src2 = reinterpret_cast<const uint2*>(rs + 24 * u);
+                uint2* dst2 = reinterpret_cast<uint2*>(codes + srow * RB + 24 * u);
+                const uint2 w0 = src2[0], w1 = src2[1], w2 = src2[2];
+                __builtin_nontemporal_store(w0.x, &dst2[0].x);
+                __builtin_nontemporal_store(w0.y, &dst2[0].y);
+                __builtin_nontemporal_store(w1.x, &dst2[1].x);
+                __builtin_nontemporal_store(w1.y, &dst2[1].y);
+                __builtin_nontemporal_store(w2.x, &dst2[2].x);
+                __builtin_nontemporal_store(w2.y, &dst2[2].y);
+            } else {  // lane u: bytes 12 u .. 12 u + 11
+                const uint32_t* src1 = reinterpret_cast<const uint32_t*>(rs + 12 * u);
+                uint32_t* dst1 = reinterpret_cast<uint32_t*>(codes + srow * RB + 12 * u);
+                const uint32_t w0 = src1[0], w1 = src1[1], w2 = src1[2];
+                __builtin_nontemporal_store(w0, dst1);
+                __builtin_nontemporal_store(w1, dst1 + 1);
+                __builtin_nontemporal_store(w2, dst1 + 2);
+            }
+            __builtin_nontemporal_store(rad, radii + srow);
+            // every lane has read the row before the next iteration writes it
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            if (base + stride < n_rows) load(base + stride, nv);
+            continue;
+        }
         // bucketing; nibble of element (j, k) -> bit 4 j + 16 bit1(k) of word P[2 (k & 1) + k / 4]
         // a zero radius gives inv_a = +inf: cell 14 for w > 0, cell 0 for w < 0 and, through
         // NaN, for w = +-0, where T_0 = -0 and T_14 = +0 make idx 15 and 0 as the definition
@@ -504,12 +612,16 @@ hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int dim, uint8_t* c
 hipError_t launch_encode_tq(int bits, const float* x, int64_t n_rows, int dim, const uint8_t* sign_mask,
                             uint8_t* codes, float* radii, hipStream_t st) {
     if (n_rows == 0) return hipSuccess;
-    if (dim == 512 && bits == 4) {
+    // the 512-wide kernel's stores need 8-byte (6 bits) or 4-byte (3, 4 bits) aligned rows
+    const uintptr_t calign = bits == 6 ? 7u : 3u;
+    if (dim == 512 && (bits == 3 || bits == 4 || bits == 6) && ((uintptr_t)codes & calign) == 0) {
         const int64_t waves = (n_rows + D512_ROWS - 1) / D512_ROWS;
         int64_t wgs = (waves + ENC_WAVES - 1) / ENC_WAVES;
         if (wgs > D512_MAX_WGS) wgs = D512_MAX_WGS;
-        hipLaunchKernelGGL(k_encode_tq4_d512, dim3((unsigned)wgs), dim3(ENC_WAVES * KVQ_WAVE), 0, st, x, n_rows,
-                           sign_mask, codes, radii);
+        const dim3 grid((unsigned)wgs), block(ENC_WAVES * KVQ_WAVE);
+        if (bits == 3) hipLaunchKernelGGL(k_encode_tq_d512<3>, grid, block, 0, st, x, n_rows, sign_mask, codes, radii);
+        else if (bits == 6) hipLaunchKernelGGL(k_encode_tq_d512<6>, grid, block, 0, st, x, n_rows, sign_mask, codes, radii);
+        else hipLaunchKernelGGL(k_encode_tq_d512<4>, grid, block, 0, st, x, n_rows, sign_mask, codes, radii);
         return hipGetLastError();
     }
     const int64_t rows_per_wave = KVQ_WAVE / (dim / 8);

@@ -236,7 +236,7 @@ __global__ __launch_bounds__(ENC_WAVES * KVQ_WAVE) void k_encode_tq(const float*
     }
 }
 
-// ---- TQ4, dim 512 --------------------------------------------------------------
+// ---- rotated codec, dim 512 ------------------------------------------------------
 // The same result as k_encode_tq<4> with fewer vector instructions per row
 // (the general kernel spends about 500 per 512-wide row):
 //  - 16 lanes per row, 4 rows per wave.  Lane u of a row has the lane-stage

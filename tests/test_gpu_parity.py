@@ -206,6 +206,28 @@ def test_tq4_encoder_bit_exact(case, bits):
             np.testing.assert_array_equal(_np(c2), rc)
 
 
+def test_tq_encoder_unaligned_codes():
+    """6-bit codes of 512-wide rows into a buffer 4 bytes past an 8-byte boundary (the
+    interface's 4-byte minimum, below the 512-wide kernel's 8-byte stores): the general
+    kernel takes the rows and the bytes are the definition's; 2 bytes past is refused."""
+    _say("tq encoder unaligned codes")
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((37, 512)) * rng.lognormal(0, 1, (37, 1))).astype(np.float32)
+    x[4] = 0
+    m = rng.integers(0, 256, 64, dtype=np.uint8)
+    rb = 512 * 6 // 8
+    buf = torch.zeros(37 * rb + 16, dtype=torch.uint8, device=DEV)
+    c = buf[4:4 + 37 * rb].view(37, rb)
+    r = torch.empty(37, dtype=torch.float32, device=DEV)
+    kvq.kvq_encode_tq(6, _t(x), _t(m), c, r)
+    rc, rr = oracle.encode_tq(x, m, 6)
+    np.testing.assert_array_equal(_np(r).view(np.uint32), rr.view(np.uint32))
+    np.testing.assert_array_equal(_np(c), rc)
+    assert not _np(buf[:4]).any() and not _np(buf[4 + 37 * rb:]).any()  # nothing outside the rows
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_encode_tq(6, _t(x), _t(m), buf[2:2 + 37 * rb].view(37, rb), r)
+
+
 # ---- decode attention --------------------------------------------------------------------
 
 def _encode_cache(w):

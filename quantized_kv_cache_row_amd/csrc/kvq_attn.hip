@@ -1741,7 +1741,7 @@ __global__ __launch_bounds__(NT) void k_merge(kvq_attn_args a, Plan p) {
             mc[u] = mb[du * nh];
             lc[u] = lb[du * nh];
             if (F16) {
-                vh[u] = *reinterpret_cast<const uint2*>(p.part_h + (cb * nh + h) * DL + d + du * nh * DL);
+                vh[u] = ld_nt(reinterpret_cast<const uint2*>(p.part_h + (cb * nh + h) * DL + d + du * nh * DL));
                 sk[u] = p.part_s[(cb * 4 + (d >> 7)) * nh + h + du * 4 * nh];
             } else {
                 v[u] = *reinterpret_cast<const float4*>(p.part_o + (cb * nh + h) * DL + d + du * nh * DL);
